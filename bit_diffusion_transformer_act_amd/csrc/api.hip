@@ -1,0 +1,139 @@
+// Host side of the C ABI: argument validation, the gfx950 capability check
+// and dispatch. Nothing here allocates or synchronizes.
+//
+// The capability check mirrors the pages' loader, which validates the GPU
+// at load time and raises a clear error instead of producing wrong output
+// (dothoosh.com "How Nunchaku Lite halves diffusion-model VRAM",
+// hardware-support paragraph).
+#include <atomic>
+#include <cstdlib>
+#include <cstring>
+
+#include "launch.hpp"
+#include "svdq.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool arch_is_gfx950(const char* name) { return name && std::strncmp(name, "gfx950", 6) == 0; }
+
+int check_device(int dev) {
+  const char* force = std::getenv("SVDQ_FORCE_ARCH");
+  if (force && *force) return arch_is_gfx950(force) ? SVDQ_OK : SVDQ_ERR_UNSUPPORTED_DEVICE;
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || dev < 0 || dev >= count) {
+    (void)hipGetLastError();
+    return SVDQ_ERR_UNSUPPORTED_DEVICE;
+  }
+  if (dev < kMaxDevices) {
+    const int c = g_arch_ok[dev].load(std::memory_order_acquire);
+    if (c == 1) return SVDQ_OK;
+    if (c == 2) return SVDQ_ERR_UNSUPPORTED_DEVICE;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return SVDQ_ERR_UNSUPPORTED_DEVICE;
+  }
+  const bool ok = arch_is_gfx950(prop.gcnArchName);
+  if (dev < kMaxDevices) g_arch_ok[dev].store(ok ? 1 : 2, std::memory_order_release);
+  return ok ? SVDQ_OK : SVDQ_ERR_UNSUPPORTED_DEVICE;
+}
+
+int check_current_device() {
+  const char* force = std::getenv("SVDQ_FORCE_ARCH");
+  if (force && *force) return arch_is_gfx950(force) ? SVDQ_OK : SVDQ_ERR_UNSUPPORTED_DEVICE;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return SVDQ_ERR_UNSUPPORTED_DEVICE;
+  }
+  return check_device(dev);
+}
+
+int finish(hipError_t e) { return e == hipSuccess ? SVDQ_OK : SVDQ_ERR_HIP; }
+
+bool rank_ok(int r) { return r >= 0 && r <= 128 && (r % 16) == 0; }
+bool k_ok(int K) { return K >= 128 && K <= 65536 && (K % 128) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int svdq_version(void) { return 10000 * 0 + 100 * 1 + 0; }
+
+const char* svdq_status_str(int status) {
+  switch (status) {
+    case SVDQ_OK: return "ok";
+    case SVDQ_ERR_INVALID_ARG: return "invalid argument (null pointer or bad enum value)";
+    case SVDQ_ERR_SHAPE: return "unsupported shape";
+    case SVDQ_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case SVDQ_ERR_UNSUPPORTED_DEVICE: return "no HIP device, or the device is not gfx950 (MI355X)";
+    case SVDQ_ERR_HIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+int svdq_device_check(int hip_device) { return check_device(hip_device); }
+
+int svdq_quantize_act(int fmt, int M, int K, int r, const void* X, const float* smooth_inv,
+                      const void* lora_down, uint8_t* act_codes, void* act_scales, float* lora_act,
+                      void* stream) {
+  if (fmt != SVDQ_INT4_G64 && fmt != SVDQ_FP4_E2M1_B32) return SVDQ_ERR_INVALID_ARG;
+  if (M < 0 || !k_ok(K) || !rank_ok(r)) return SVDQ_ERR_SHAPE;
+  if (M == 0) return SVDQ_OK;
+  if (!X || !smooth_inv || !act_codes || !act_scales) return SVDQ_ERR_INVALID_ARG;
+  if (r > 0 && (!lora_down || !lora_act)) return SVDQ_ERR_INVALID_ARG;
+  if (!aligned16(X) || !aligned16(smooth_inv) || !aligned16(act_codes) || !aligned16(act_scales))
+    return SVDQ_ERR_ALIGN;
+  if (r > 0 && (!aligned16(lora_down) || !aligned16(lora_act))) return SVDQ_ERR_ALIGN;
+  const int dc = check_current_device();
+  if (dc != SVDQ_OK) return dc;
+  (void)hipGetLastError();
+  return finish(svdq::launch_quantize_act(fmt, M, K, r, X, smooth_inv, lora_down, act_codes,
+                                          act_scales, lora_act, (hipStream_t)stream));
+}
+
+int svdq_gemm_w4a4(int fmt, int M, int N, int K, int r, const uint8_t* act_codes,
+                   const void* act_scales, const float* lora_act, const uint8_t* w_codes,
+                   const void* w_scales, const void* lora_up, const void* bias, int epi, void* Y,
+                   void* stream) {
+  if (fmt != SVDQ_INT4_G64 && fmt != SVDQ_FP4_E2M1_B32) return SVDQ_ERR_INVALID_ARG;
+  if (epi != SVDQ_EPI_NONE && epi != SVDQ_EPI_GELU_TANH) return SVDQ_ERR_INVALID_ARG;
+  if (M < 0 || M > (1 << 23) || N < 128 || N > 65536 || (N % 128) != 0 || !k_ok(K) || !rank_ok(r))
+    return SVDQ_ERR_SHAPE;
+  if (M == 0) return SVDQ_OK;
+  if (!act_codes || !act_scales || !w_codes || !w_scales || !Y) return SVDQ_ERR_INVALID_ARG;
+  if (r > 0 && (!lora_act || !lora_up)) return SVDQ_ERR_INVALID_ARG;
+  if (!aligned16(act_codes) || !aligned16(act_scales) || !aligned16(w_codes) ||
+      !aligned16(w_scales) || !aligned16(Y) || (bias && !aligned16(bias)))
+    return SVDQ_ERR_ALIGN;
+  if (r > 0 && (!aligned16(lora_act) || !aligned16(lora_up))) return SVDQ_ERR_ALIGN;
+  const int dc = check_current_device();
+  if (dc != SVDQ_OK) return dc;
+  (void)hipGetLastError();
+  return finish(svdq::launch_gemm_w4a4(fmt, M, N, K, r, act_codes, act_scales, lora_act, w_codes,
+                                       w_scales, lora_up, bias, epi, Y, (hipStream_t)stream));
+}
+
+int awq_gemv_w4a16(int M, int N, int K, int group, const void* x, const uint8_t* w_codes,
+                   const void* scales, const void* zeros, void* y, void* stream) {
+  if (group != 64) return SVDQ_ERR_SHAPE;
+  if (M < 0 || M > 8 || N < 1 || N > (1 << 20) || K < 64 || (K % 64) != 0 || M * K > 32768)
+    return SVDQ_ERR_SHAPE;
+  if (M == 0) return SVDQ_OK;
+  if (!x || !w_codes || !scales || !zeros || !y) return SVDQ_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_codes) || !aligned16(scales) || !aligned16(zeros) ||
+      !aligned16(y))
+    return SVDQ_ERR_ALIGN;
+  const int dc = check_current_device();
+  if (dc != SVDQ_OK) return dc;
+  (void)hipGetLastError();
+  return finish(svdq::launch_awq_gemv(M, N, K, x, w_codes, scales, zeros, y, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,222 @@
+"""Python binding of the C ABI in include/svdq.h (ctypes).
+
+Argument marshalling only: tensors are checked (device, dtype, shape,
+contiguity), outputs are allocated with torch on the input's device, and the
+call goes to the HIP library on torch's current stream. Every step of the
+layer runs in the library's kernels; there is no fallback of any kind, and a
+missing library is an error.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+from .build import LIB_PATH
+
+INT4_G64 = 0
+FP4_E2M1_B32 = 1
+FORMATS = {"int4_g64": INT4_G64, "fp4_b32": FP4_E2M1_B32}
+EPI_NONE = 0
+EPI_GELU_TANH = 1
+EPILOGUES = {"none": EPI_NONE, "gelu_tanh": EPI_GELU_TANH}
+
+SVDQ_OK = 0
+SVDQ_ERR_INVALID_ARG = -1
+SVDQ_ERR_SHAPE = -2
+SVDQ_ERR_ALIGN = -3
+SVDQ_ERR_UNSUPPORTED_DEVICE = -4
+SVDQ_ERR_HIP = -5
+
+EXPORTED_SYMBOLS = ("svdq_device_check", "svdq_status_str", "svdq_version",
+                    "svdq_quantize_act", "svdq_gemm_w4a4", "awq_gemv_w4a16")
+
+_lock = threading.Lock()
+_handle = None
+
+
+class SvdqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {svdq_status_str(status)} (status {status})")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libsvdq_mi355x.so (after torch, so both share one HIP runtime)."""
+    global _handle
+    with _lock:
+        if _handle is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(
+                    f"HIP library {LIB_PATH} is not built; run "
+                    "`python -c 'import __graft_entry__ as g; g.build()'` (hipcc, gfx950)")
+            h = ctypes.CDLL(LIB_PATH)
+            vp, i32 = ctypes.c_void_p, ctypes.c_int
+            h.svdq_device_check.argtypes = [i32]
+            h.svdq_device_check.restype = i32
+            h.svdq_status_str.argtypes = [i32]
+            h.svdq_status_str.restype = ctypes.c_char_p
+            h.svdq_version.argtypes = []
+            h.svdq_version.restype = i32
+            h.svdq_quantize_act.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
+            h.svdq_quantize_act.restype = i32
+            h.svdq_gemm_w4a4.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp]
+            h.svdq_gemm_w4a4.restype = i32
+            h.awq_gemv_w4a16.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]
+            h.awq_gemv_w4a16.restype = i32
+            _handle = h
+        return _handle
+
+
+def svdq_status_str(status: int) -> str:
+    return lib().svdq_status_str(int(status)).decode()
+
+
+def svdq_version() -> int:
+    return lib().svdq_version()
+
+
+def svdq_device_check(device: int = 0) -> int:
+    return lib().svdq_device_check(int(device))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _check(t: torch.Tensor, name: str, dtype, shape, dev):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, expected {dev}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _fmt(fmt) -> int:
+    if isinstance(fmt, str):
+        if fmt not in FORMATS:
+            raise ValueError(f"unknown format {fmt!r}")
+        return FORMATS[fmt]
+    return int(fmt)
+
+
+def _scale_spec(fmt: int, rows: int, K: int):
+    if fmt == INT4_G64:
+        return torch.float16, (rows, K // 64)
+    return torch.uint8, (rows, K // 32)
+
+
+def svdq_quantize_act(X: torch.Tensor, smooth_inv: torch.Tensor, lora_down, fmt="int4_g64",
+                      act_codes=None, act_scales=None, lora_act=None):
+    """Smoothing + low-rank down-projection + 4-bit activation quantization.
+
+    X fp16 [M][K]; smooth_inv fp32 [K]; lora_down fp16 [r][K] or None.
+    Returns (act_codes u8 [M][K/2], act_scales fp16 [M][K/64] | u8 [M][K/32],
+    lora_act fp32 [M][r] or None). Output tensors may be passed in.
+    """
+    f = _fmt(fmt)
+    dev = X.device
+    if dev.type != "cuda":
+        raise ValueError("X must be a HIP device tensor")
+    M, K = X.shape
+    r = 0 if lora_down is None else lora_down.shape[0]
+    _check(X, "X", torch.float16, (M, K), dev)
+    _check(smooth_inv, "smooth_inv", torch.float32, (K,), dev)
+    if lora_down is not None:
+        _check(lora_down, "lora_down", torch.float16, (r, K), dev)
+    sdt, sshape = _scale_spec(f, M, K)
+    if act_codes is None:
+        act_codes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    if act_scales is None:
+        act_scales = torch.empty(sshape, dtype=sdt, device=dev)
+    if r > 0 and lora_act is None:
+        lora_act = torch.empty((M, r), dtype=torch.float32, device=dev)
+    _check(act_codes, "act_codes", torch.uint8, (M, K // 2), dev)
+    _check(act_scales, "act_scales", sdt, sshape, dev)
+    if r > 0:
+        _check(lora_act, "lora_act", torch.float32, (M, r), dev)
+    with torch.cuda.device(dev):
+        st = lib().svdq_quantize_act(f, M, K, r, _ptr(X), _ptr(smooth_inv), _ptr(lora_down),
+                                     _ptr(act_codes), _ptr(act_scales),
+                                     _ptr(lora_act) if r > 0 else None, _stream(dev))
+    if st != SVDQ_OK:
+        raise SvdqError(st, "svdq_quantize_act")
+    return act_codes, act_scales, (lora_act if r > 0 else None)
+
+
+def svdq_gemm_w4a4(act_codes, act_scales, lora_act, w_codes, w_scales, lora_up, bias,
+                   fmt="int4_g64", epilogue="none", out=None):
+    """Fused 4-bit GEMM + low-rank up-projection + bias (+ GELU) -> Y fp16 [M][N]."""
+    f = _fmt(fmt)
+    e = EPILOGUES[epilogue] if isinstance(epilogue, str) else int(epilogue)
+    dev = act_codes.device
+    if dev.type != "cuda":
+        raise ValueError("act_codes must be a HIP device tensor")
+    M, KB = act_codes.shape
+    K = 2 * KB
+    N = w_codes.shape[0]
+    r = 0 if lora_up is None else lora_up.shape[1]
+    sdt, sa_shape = _scale_spec(f, M, K)
+    _, sw_shape = _scale_spec(f, N, K)
+    _check(act_codes, "act_codes", torch.uint8, (M, KB), dev)
+    _check(act_scales, "act_scales", sdt, sa_shape, dev)
+    _check(w_codes, "w_codes", torch.uint8, (N, KB), dev)
+    _check(w_scales, "w_scales", sdt, sw_shape, dev)
+    if r > 0:
+        _check(lora_act, "lora_act", torch.float32, (M, r), dev)
+        _check(lora_up, "lora_up", torch.float16, (N, r), dev)
+    if bias is not None:
+        _check(bias, "bias", torch.float16, (N,), dev)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=dev)
+    _check(out, "out", torch.float16, (M, N), dev)
+    with torch.cuda.device(dev):
+        st = lib().svdq_gemm_w4a4(f, M, N, K, r, _ptr(act_codes), _ptr(act_scales),
+                                  _ptr(lora_act) if r > 0 else None, _ptr(w_codes), _ptr(w_scales),
+                                  _ptr(lora_up) if r > 0 else None, _ptr(bias), e, _ptr(out),
+                                  _stream(dev))
+    if st != SVDQ_OK:
+        raise SvdqError(st, "svdq_gemm_w4a4")
+    return out
+
+
+def awq_gemv_w4a16(x, w_codes, scales, zeros, group: int = 64, out=None):
+    """AWQ W4A16 GEMV: y[m,n] = sum_k x[m,k] (q[n,k] - z) s -> fp16 [M][N]."""
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("x must be a HIP device tensor")
+    M, K = x.shape
+    N = w_codes.shape[0]
+    _check(x, "x", torch.float16, (M, K), dev)
+    _check(w_codes, "w_codes", torch.uint8, (N, K // 2), dev)
+    _check(scales, "scales", torch.float16, (N, K // group), dev)
+    _check(zeros, "zeros", torch.float16, (N, K // group), dev)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=dev)
+    _check(out, "out", torch.float16, (M, N), dev)
+    with torch.cuda.device(dev):
+        st = lib().awq_gemv_w4a16(M, N, K, group, _ptr(x), _ptr(w_codes), _ptr(scales),
+                                  _ptr(zeros), _ptr(out), _stream(dev))
+    if st != SVDQ_OK:
+        raise SvdqError(st, "awq_gemv_w4a16")
+    return out
+
+
+def svdq_linear(X, layer: dict, bias=None, epilogue: str = "none"):
+    """One SVDQ W4A4 linear layer: the two fused calls back to back.
+    layer holds device tensors smooth_inv, lora_down, w_codes, w_scales,
+    lora_up and the format name under "fmt"."""
+    codes, scales, la = svdq_quantize_act(X, layer["smooth_inv"], layer.get("lora_down"), layer["fmt"])
+    return svdq_gemm_w4a4(codes, scales, la, layer["w_codes"], layer["w_scales"],
+                          layer.get("lora_up"), bias, layer["fmt"], epilogue)

@@ -1,0 +1,190 @@
+/*
+ * svdq.h -- C ABI of the MI355X (gfx950) SVDQuant W4A4 + AWQ W4A16 library.
+ *
+ * The layer this library runs is the SVDQuant linear layer: activation
+ * outliers migrated into the weights by a per-channel smoothing, a small
+ * 16-bit low-rank branch holding the hardest part of the weight, and the
+ * residual quantized to 4 bits, so the main product runs with 4-bit weights
+ * AND 4-bit activations (dothoosh.com "How Nunchaku Lite halves
+ * diffusion-model VRAM", SVDQuant paragraph; nextgz.net "Hugging Face brings
+ * Nunchaku Lite to Diffusers", section "Why W4A4 differs from weight-only
+ * backends"). As on the pages' fused kernels, the low-rank down-projection
+ * is fused with the activation quantizer and the up-projection with the
+ * 4-bit GEMM (dothoosh.com article, fused-kernel paragraph), giving two
+ * calls per layer:
+ *
+ *     svdq_quantize_act:  X -> (act_codes, act_scales, lora_act = X . lora_down^T)
+ *     svdq_gemm_w4a4:     Y = act(lora_act . lora_up^T + dequant(act) dequant(W)^T + bias)
+ *
+ * plus the AWQ W4A16 GEMV of the modulation / adaptive-norm projections
+ * (dothoosh.com article, kernel-family list, the awq_w4a16 entry).
+ *
+ * Conventions for every entry point:
+ *   - Ownership: the caller owns every buffer; all pointers are DEVICE
+ *     pointers (HIP device memory) unless stated. The library allocates
+ *     nothing, keeps no per-call state and only uses the pointers for the
+ *     work it enqueues.
+ *   - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL is the
+ *     null stream) and the call returns without synchronizing.
+ *   - Errors: arguments are checked on the host BEFORE anything is enqueued;
+ *     the call returns an svdq_status and never aborts or prints. Order of
+ *     checks: enum values, sizes (SVDQ_ERR_SHAPE), null pointers
+ *     (SVDQ_ERR_INVALID_ARG), 16-byte alignment of every pointer
+ *     (SVDQ_ERR_ALIGN), then the device (SVDQ_ERR_UNSUPPORTED_DEVICE: the
+ *     current HIP device is not gfx950, or there is none), then the launch
+ *     (SVDQ_ERR_HIP). A call with M == 0 validates and returns SVDQ_OK
+ *     without enqueuing work (pointers may then be NULL).
+ *   - Layouts are row-major and K-contiguous: X [M][K], W [N][K]
+ *     (nn.Linear layout), Y [M][N]. 4-bit codes are packed two per byte,
+ *     the even-k code in the low nibble. INT4 codes are two's complement
+ *     (the quantizers produce -7..7; -8 is accepted).
+ *   - Thread safety: calls may be made concurrently from several threads;
+ *     the only global state is a per-device architecture cache.
+ */
+#ifndef SVDQ_MI355X_H
+#define SVDQ_MI355X_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SVDQ_OK = 0,
+  SVDQ_ERR_INVALID_ARG = -1,       /* NULL pointer or bad enum value */
+  SVDQ_ERR_SHAPE = -2,             /* size outside what the kernels support */
+  SVDQ_ERR_ALIGN = -3,             /* a pointer is not 16-byte aligned */
+  SVDQ_ERR_UNSUPPORTED_DEVICE = -4,/* no HIP device, or not gfx950 */
+  SVDQ_ERR_HIP = -5                /* the HIP runtime reported a launch error */
+} svdq_status;
+
+/* 4-bit formats. The pages ship INT4 and a 4-bit float (NVFP4, group 16)
+ * (dothoosh.com article, kernel-family list and quantization_config block).
+ * SVDQ_INT4_G64: symmetric INT4, one fp16 scale per 64 values along K.
+ * SVDQ_FP4_E2M1_B32: OCP E2M1 codes, one E8M0 (power-of-two) scale byte per
+ *   32 values along K -- the block-scaled form CDNA4's matrix cores consume. */
+typedef enum { SVDQ_INT4_G64 = 0, SVDQ_FP4_E2M1_B32 = 1 } svdq_format;
+
+/* Epilogue applied after the bias: identity, or GELU in its tanh form
+ * y/2 (1 + tanh(sqrt(2/pi) (y + 0.044715 y^3))) for MLP up-projections
+ * (the GELU/MLP fusion of the full engine, dothoosh.com article, paragraph on
+ * model-specific fused paths). */
+typedef enum { SVDQ_EPI_NONE = 0, SVDQ_EPI_GELU_TANH = 1 } svdq_epilogue;
+
+/* Returns SVDQ_OK iff HIP device `hip_device` exists and is a gfx950 part.
+ * This is the library's capability check: a clear error instead of wrong
+ * output on hardware the kernels were not built for (dothoosh.com article,
+ * hardware-support paragraph). Result is cached per device. */
+int svdq_device_check(int hip_device);
+
+/* Static string for a status code (never NULL). */
+const char* svdq_status_str(int status);
+
+/* Library version as 10000*major + 100*minor + patch. */
+int svdq_version(void);
+
+/*
+ * svdq_quantize_act -- fused activation smoothing, low-rank down-projection
+ * and per-group 4-bit activation quantization (one pass over X).
+ *
+ *   x_hat[m,k]   = fl32(fp32(X[m,k]) * smooth_inv[k])          (IEEE multiply)
+ *   lora_act[m,j]= sum_k X[m,k] * lora_down[j,k]   (fp16 inputs, fp32 accumulate)
+ *   INT4_G64, per row m and group g of 64 along K:
+ *     amax = max |x_hat|;  s = fp16_rne(min(fl32(amax / 7), 65504));
+ *     q = s == 0 ? 0 : clamp(rint_even(fl32(x_hat / s)), -7, 7)   (IEEE division)
+ *   FP4_E2M1_B32, per row m and block of 32 along K:
+ *     amax == 0 -> scale byte 0, codes 0; else e = min integer with
+ *     6 * 2^e >= amax, clamped to [-127, 127]; scale byte = e + 127;
+ *     code = E2M1 nearest to x_hat / 2^e (ties to even mantissa), sign bit
+ *     from x_hat's sign.
+ * Codes and scales are bit-exact functions of (X, smooth_inv); lora_act is a
+ * float result (summation order unspecified).
+ *
+ * Arguments:
+ *   fmt         svdq_format.
+ *   M           rows (tokens), M >= 0.
+ *   K           input channels; K % 128 == 0, 128 <= K <= 65536.
+ *   r           low-rank width; r % 16 == 0, 0 <= r <= 128.
+ *   X           fp16 [M][K].
+ *   smooth_inv  fp32 [K], the smoothing multiplier (1/lambda).
+ *   lora_down   fp16 [r][K] (carries diag(smooth_inv)); may be NULL iff r == 0.
+ *   act_codes   out, u8 [M][K/2].
+ *   act_scales  out, fp16 [M][K/64] (INT4_G64) or u8 [M][K/32] (FP4_E2M1_B32).
+ *   lora_act    out, fp32 [M][r]; may be NULL iff r == 0.
+ *   stream      hipStream_t.
+ */
+int svdq_quantize_act(int fmt, int M, int K, int r,
+                      const void* X, const float* smooth_inv, const void* lora_down,
+                      uint8_t* act_codes, void* act_scales, float* lora_act,
+                      void* stream);
+
+/*
+ * svdq_gemm_w4a4 -- the 4-bit GEMM with the low-rank up-projection, scale
+ * dequantization, bias and epilogue fused:
+ *
+ *   Y[m,n] = act( sum_j lora_act[m,j] lora_up[n,j]
+ *               + sum_g s_x[m,g] s_w[n,g] sum_{k in g} q_x[m,k] q_w[n,k]
+ *               + bias[n] )                                 -> fp16 (RNE)
+ *
+ * INT4_G64 multiplies the codes exactly (int8 matrix cores, int32 per
+ * group) and applies s_x s_w in fp32; FP4_E2M1_B32 uses the block-scaled
+ * FP4 matrix instruction with the E8M0 scales applied in hardware and fp32
+ * accumulation. lora_act is rounded to fp16 for the low-rank product
+ * (fp32 accumulation).
+ *
+ * Arguments:
+ *   fmt         svdq_format.
+ *   M           rows, 0 <= M <= 2^23 (any value; tails are masked).
+ *   N           output channels; N % 128 == 0, N <= 65536.
+ *   K           input channels; K % 128 == 0, 128 <= K <= 65536.
+ *   r           low-rank width; r % 16 == 0, 0 <= r <= 128.
+ *   act_codes   u8 [M][K/2] (from svdq_quantize_act).
+ *   act_scales  fp16 [M][K/64] or u8 [M][K/32].
+ *   lora_act    fp32 [M][r]; may be NULL iff r == 0.
+ *   w_codes     u8 [N][K/2].
+ *   w_scales    fp16 [N][K/64] or u8 [N][K/32].
+ *   lora_up     fp16 [N][r]; may be NULL iff r == 0.
+ *   bias        fp16 [N], or NULL for no bias.
+ *   epi         svdq_epilogue.
+ *   Y           out, fp16 [M][N].
+ *   stream      hipStream_t.
+ */
+int svdq_gemm_w4a4(int fmt, int M, int N, int K, int r,
+                   const uint8_t* act_codes, const void* act_scales, const float* lora_act,
+                   const uint8_t* w_codes, const void* w_scales, const void* lora_up,
+                   const void* bias, int epi, void* Y, void* stream);
+
+/*
+ * awq_gemv_w4a16 -- 4-bit weights, 16-bit activations, memory-bound GEMV for
+ * the modulation / adaptive-norm projections (dothoosh.com article,
+ * kernel-family list: awq_w4a16; quantization_config block: int4, group 64):
+ *
+ *   y[m,n] = sum_k x[m,k] * (q[n,k] - z[n,k/G]) * s[n,k/G]   -> fp16 (RNE)
+ *
+ * with fp32 accumulation.
+ *
+ * Arguments:
+ *   M       rows of x, 0 <= M <= 8.
+ *   N       output channels, 1 <= N <= 2^20.
+ *   K       input channels; K % 64 == 0, K >= 64, M * K <= 32768 (x is staged
+ *           in LDS).
+ *   group   group size along K; must be 64.
+ *   x       fp16 [M][K].
+ *   w_codes u8 [N][K/2], unsigned nibbles, even k in the low nibble.
+ *   scales  fp16 [N][K/64].
+ *   zeros   fp16 [N][K/64], in code units; must hold integers 0..15 (a
+ *           non-integer zero is rounded to an integer by the packed fp16
+ *           dequantization).
+ *   y       out, fp16 [M][N].
+ *   stream  hipStream_t.
+ */
+int awq_gemv_w4a16(int M, int N, int K, int group,
+                   const void* x, const uint8_t* w_codes, const void* scales,
+                   const void* zeros, void* y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SVDQ_MI355X_H */

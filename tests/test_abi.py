@@ -1,0 +1,131 @@
+"""The C ABI library on the CPU: it loads, exports every symbol include/svdq.h
+declares, and rejects bad arguments with the documented status before it
+touches a device. No kernel is launched here (there is no GPU in this test;
+the device check itself reports SVDQ_ERR_UNSUPPORTED_DEVICE).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import bit_diffusion_transformer_act_amd as P
+from bit_diffusion_transformer_act_amd import ops
+from bit_diffusion_transformer_act_amd.build import LIB_PATH
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "svdq.h")
+
+A = 4096  # a 16-byte aligned, never dereferenced fake device address
+U = 4099  # unaligned fake address
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(ops.EXPORTED_SYMBOLS)
+    lib = P.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB_PATH], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert set(names) <= exported
+
+
+def test_status_strings_and_version():
+    for st in (0, -1, -2, -3, -4, -5):
+        assert P.svdq_status_str(st)
+    assert "unknown" in P.svdq_status_str(17)
+    assert P.svdq_version() == 100
+
+
+def q(fmt=0, M=4, K=128, r=16, X=A, si=A, ld=A, codes=A, scales=A, la=A):
+    return P.lib().svdq_quantize_act(fmt, M, K, r, X, si, ld, codes, scales, la, None)
+
+
+def g(fmt=0, M=4, N=128, K=128, r=16, ac=A, sa=A, la=A, wc=A, ws=A, lu=A, b=None, epi=0, Y=A):
+    return P.lib().svdq_gemm_w4a4(fmt, M, N, K, r, ac, sa, la, wc, ws, lu, b, epi, Y, None)
+
+
+def v(M=1, N=64, K=128, G=64, x=A, c=A, s=A, z=A, y=A):
+    return P.lib().awq_gemv_w4a16(M, N, K, G, x, c, s, z, y, None)
+
+
+def test_quantize_act_argument_errors():
+    assert q(fmt=2) == ops.SVDQ_ERR_INVALID_ARG
+    assert q(K=64) == ops.SVDQ_ERR_SHAPE
+    assert q(K=192) == ops.SVDQ_ERR_SHAPE
+    assert q(r=8) == ops.SVDQ_ERR_SHAPE
+    assert q(r=144) == ops.SVDQ_ERR_SHAPE
+    assert q(M=-1) == ops.SVDQ_ERR_SHAPE
+    assert q(M=0, X=None, si=None, ld=None, codes=None, scales=None, la=None) == ops.SVDQ_OK
+    assert q(X=None) == ops.SVDQ_ERR_INVALID_ARG
+    assert q(la=None) == ops.SVDQ_ERR_INVALID_ARG
+    assert q(r=0, ld=None, la=None) == ops.SVDQ_ERR_UNSUPPORTED_DEVICE
+    assert q(codes=U) == ops.SVDQ_ERR_ALIGN
+    assert q(si=U) == ops.SVDQ_ERR_ALIGN
+    # valid arguments reach the device check, which fails without a gfx950
+    assert q() == ops.SVDQ_ERR_UNSUPPORTED_DEVICE
+
+
+def test_gemm_argument_errors():
+    assert g(fmt=5) == ops.SVDQ_ERR_INVALID_ARG
+    assert g(epi=3) == ops.SVDQ_ERR_INVALID_ARG
+    assert g(N=192) == ops.SVDQ_ERR_SHAPE
+    assert g(N=0) == ops.SVDQ_ERR_SHAPE
+    assert g(K=320) == ops.SVDQ_ERR_SHAPE
+    assert g(r=40) == ops.SVDQ_ERR_SHAPE
+    assert g(M=(1 << 23) + 1) == ops.SVDQ_ERR_SHAPE
+    assert g(M=0, ac=None, sa=None, la=None, wc=None, ws=None, lu=None, Y=None) == ops.SVDQ_OK
+    assert g(wc=None) == ops.SVDQ_ERR_INVALID_ARG
+    assert g(lu=None) == ops.SVDQ_ERR_INVALID_ARG
+    assert g(r=0, la=None, lu=None) == ops.SVDQ_ERR_UNSUPPORTED_DEVICE
+    assert g(Y=U) == ops.SVDQ_ERR_ALIGN
+    assert g(b=U) == ops.SVDQ_ERR_ALIGN
+    assert g() == ops.SVDQ_ERR_UNSUPPORTED_DEVICE
+
+
+def test_gemv_argument_errors():
+    assert v(G=32) == ops.SVDQ_ERR_SHAPE
+    assert v(M=9) == ops.SVDQ_ERR_SHAPE
+    assert v(K=96) == ops.SVDQ_ERR_SHAPE
+    assert v(M=2, K=32768) == ops.SVDQ_ERR_SHAPE
+    assert v(N=0) == ops.SVDQ_ERR_SHAPE
+    assert v(M=0, x=None, c=None, s=None, z=None, y=None) == ops.SVDQ_OK
+    assert v(z=None) == ops.SVDQ_ERR_INVALID_ARG
+    assert v(y=U) == ops.SVDQ_ERR_ALIGN
+    assert v() == ops.SVDQ_ERR_UNSUPPORTED_DEVICE
+
+
+def test_device_check_without_gpu():
+    assert P.svdq_device_check(0) == ops.SVDQ_ERR_UNSUPPORTED_DEVICE
+    assert P.svdq_device_check(-1) == ops.SVDQ_ERR_UNSUPPORTED_DEVICE
+
+
+def test_forced_arch_override(monkeypatch):
+    monkeypatch.setenv("SVDQ_FORCE_ARCH", "gfx942")
+    assert q() == ops.SVDQ_ERR_UNSUPPORTED_DEVICE
+    assert P.svdq_device_check(0) == ops.SVDQ_ERR_UNSUPPORTED_DEVICE
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    X = torch.zeros((4, 128), dtype=torch.float16)
+    with pytest.raises(ValueError):
+        P.svdq_quantize_act(X, torch.ones(128), None)
+
+
+def test_product_path_does_not_import_the_oracle():
+    pkg_dir = os.path.join(ROOT, "bit_diffusion_transformer_act_amd")
+    for dirpath, _, files in os.walk(pkg_dir):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+                assert "oracle/" not in text, f
