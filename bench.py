@@ -1,0 +1,299 @@
+#!/usr/bin/env python3
+"""Benchmark of the SVDQuant W4A4 + low-rank linear layer and the AWQ W4A16
+GEMV on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+svdq_quantize_act (smoothing + low-rank down + 4-bit activation quantizer),
+svdq_gemm_w4a4 (4-bit GEMM + low-rank up + scales + bias [+ GELU]) on the
+DiT QKV projection (M=4096 tokens, K=3072, N=9216, rank 32, INT4 group 64),
+then awq_gemv_w4a16 on the modulation projection (M=1, K=3072, N=18432,
+group 64). Inputs are resident in HBM before the timed region; R sets of
+inputs and outputs are rotated so the working set (> 512 MB) cannot live in
+the 256 MB Infinity Cache.
+
+Prints ONE JSON line (rank 0). `value` is the layer's effective throughput
+2*M*N*K / step time in TOPS (the GEMV's time is inside the step).
+Per-kernel durations come from HIP events recorded on the launch stream
+around every launch in the timed region.
+
+Options: --gpus N (only 1 is supported: one GPU), --steps K, --warmup W,
+--workload {qkv,mlp_up,mlp_down,mlp_down_m1024,attn_out,mlp_up_int4,block},
+--no-cpu-baseline, --warm (no buffer rotation).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "W4A4+lowrank GEMM effective TOPS & % MFMA peak; W4A16 GEMV HBM GB/s"
+PEAK_TOPS = {"int4_g64": 5000.0, "fp4_b32": 10100.0}   # int8 / MXFP4 dense MFMA peaks
+PEAK_HBM_GBS = 8000.0
+ROTATE_BYTES = 600 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="qkv",
+                    choices=["qkv", "mlp_up", "mlp_down", "mlp_down_m1024", "attn_out",
+                             "mlp_up_int4", "block"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--warm", action="store_true", help="no buffer rotation (cache-warm)")
+    ap.add_argument("--rank", type=int, default=None, help="override the low-rank width")
+    return ap.parse_args()
+
+
+def layer_bytes(cfg, r):
+    M, K, N = cfg.M, cfg.K, cfg.N
+    sbytes = (K // 64) * 2 if cfg.fmt == "int4_g64" else K // 32
+    q = M * K * 2 + K * 4 + r * K * 2 + M * K // 2 + M * sbytes + M * r * 4
+    g = (M * K // 2 + M * sbytes + M * r * 4 + N * K // 2 + N * sbytes + N * r * 2 + N * 2
+         + M * N * 2)
+    return q, g
+
+
+def gemv_bytes(g, M=1):
+    return g.N * g.K // 2 + 2 * g.N * (g.K // g.group) * 2 + M * g.K * 2 + M * g.N * 2
+
+
+def kernel_source_hash(name):
+    p = os.path.join(ROOT, "bit_diffusion_transformer_act_amd", "csrc", name)
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def stored_traffic(kernel_file, workload):
+    """HBM bytes per launch from committed rocprofv3 --pmc counters, only if the
+    kernel source is unchanged since they were taken."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+    except (OSError, ValueError):
+        return None
+    if d.get("source_sha") != kernel_source_hash(kernel_file):
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build runs the layer on a single MI355X "
+              "(token-parallel sharding across GPUs is described in DESIGN.md, not run). "
+              "Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import bit_diffusion_transformer_act_amd as P
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if P.svdq_device_check(0) != 0:
+        print("cuda:0 is not a gfx950 (MI355X) device", file=sys.stderr)
+        sys.exit(3)
+
+    names = list(synth.BLOCK_STREAM) if args.workload == "block" else [args.workload]
+    cfgs = [synth.CONFIGS[n] for n in names]
+    gcfg = synth.CONFIGS["gemv"]
+
+    def t(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    # ---- one input set (host generation once), replicated on the device
+    host_sets = []
+    for cfg in cfgs:
+        p = synth.random_quantized_layer(cfg, seed=0)
+        r = cfg.rank if args.rank is None else args.rank
+        host_sets.append((cfg, r, p))
+    gp = synth.random_awq_layer(gcfg, seed=0)
+
+    per_set = 0
+    for cfg, r, _ in host_sets:
+        qb, gb = layer_bytes(cfg, r)
+        per_set += qb + gb
+    per_set += gemv_bytes(gcfg)
+    nsets = 1 if args.warm else max(2, -(-ROTATE_BYTES // per_set))
+
+    sets = []
+    for _ in range(nsets):
+        layers = []
+        for cfg, r, p in host_sets:
+            L = {"cfg": cfg, "r": r, "X": t(p["X"]), "smooth_inv": t(p["smooth_inv"]),
+                 "lora_down": t(p["lora_down"][:r]) if r else None,
+                 "w_codes": t(p["w_codes"]), "w_scales": t(p["w_scales"]),
+                 "lora_up": t(np.ascontiguousarray(p["lora_up"][:, :r])) if r else None,
+                 "bias": t(p["bias"])}
+            sdt = torch.float16 if cfg.fmt == "int4_g64" else torch.uint8
+            scols = cfg.K // 64 if cfg.fmt == "int4_g64" else cfg.K // 32
+            L["codes"] = torch.empty((cfg.M, cfg.K // 2), dtype=torch.uint8, device=dev)
+            L["scales"] = torch.empty((cfg.M, scols), dtype=sdt, device=dev)
+            L["lora_act"] = torch.empty((cfg.M, r), dtype=torch.float32, device=dev) if r else None
+            L["Y"] = torch.empty((cfg.M, cfg.N), dtype=torch.float16, device=dev)
+            layers.append(L)
+        G = {"x": t(gp["x"]), "codes": t(gp["codes"]), "scales": t(gp["scales"]),
+             "zeros": t(gp["zeros"]), "y": torch.empty((1, gcfg.N), dtype=torch.float16, device=dev)}
+        sets.append((layers, G))
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    nk = sum(2 for _ in cfgs) + 1   # launches per step
+
+    def step(i, events=None):
+        layers, G = sets[i % nsets]
+        j = 0
+        for L in layers:
+            cfg = L["cfg"]
+            if events is not None:
+                events[j].record(stream)
+            P.svdq_quantize_act(L["X"], L["smooth_inv"], L["lora_down"], cfg.fmt,
+                                L["codes"], L["scales"], L["lora_act"])
+            if events is not None:
+                events[j + 1].record(stream)
+            P.svdq_gemm_w4a4(L["codes"], L["scales"], L["lora_act"], L["w_codes"], L["w_scales"],
+                             L["lora_up"], L["bias"], cfg.fmt, cfg.epilogue, out=L["Y"])
+            j += 2
+        if events is not None:
+            events[j].record(stream)
+        P.awq_gemv_w4a16(G["x"], G["codes"], G["scales"], G["zeros"], out=G["y"])
+        if events is not None:
+            events[j + 1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # event pairs per launch: quantize_l, gemm_l ..., gemv
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(args.warmup + s, evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # per-launch durations (ms): launch k spans events[k] -> events[k+1]
+    durs = np.zeros((args.steps, nk))
+    for s in range(args.steps):
+        e = evs[s]
+        for k in range(nk):
+            durs[s, k] = e[k].elapsed_time(e[k + 1])
+    mean_ms = durs.mean(axis=0)
+    med_ms = np.median(durs, axis=0)
+    ms_per_step = wall * 1e3 / args.steps
+
+    total_ops = sum(2.0 * c.M * c.N * c.K for c in cfgs)
+    value = total_ops / (ms_per_step * 1e-3) / 1e12
+
+    kernels = {}
+    gemm_ms_sum = 0.0
+    dominant = None
+    for li, (cfg, r, _) in enumerate(host_sets):
+        qb, gb = layer_bytes(cfg, r)
+        qms, gms = mean_ms[2 * li], mean_ms[2 * li + 1]
+        gemm_ms_sum += gms
+        ops = 2.0 * cfg.M * cfg.N * cfg.K
+        kernels[f"{cfg.name}.svdq_quantize_act"] = {
+            "avg_us": round(qms * 1e3, 2), "median_us": round(med_ms[2 * li] * 1e3, 2),
+            "alg_bytes": qb, "GB/s": round(qb / (qms * 1e-3) / 1e9, 1),
+            "frac_hbm": round(qb / (qms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        tops = ops / (gms * 1e-3) / 1e12
+        kernels[f"{cfg.name}.svdq_gemm_w4a4"] = {
+            "avg_us": round(gms * 1e3, 2), "median_us": round(med_ms[2 * li + 1] * 1e3, 2),
+            "alg_ops": ops, "lowrank_ops": 2.0 * cfg.M * cfg.N * r + 2.0 * cfg.M * cfg.K * r,
+            "TOPS": round(tops, 1), "frac_peak": round(tops / PEAK_TOPS[cfg.fmt], 4),
+            "format": cfg.fmt, "epilogue": cfg.epilogue, "rank": r}
+        if dominant is None or gms > dominant[1]:
+            dominant = (cfg, gms, ops, r)
+    gvb = gemv_bytes(gcfg)
+    gvms = mean_ms[-1]
+    kernels["gemv.awq_gemv_w4a16"] = {
+        "avg_us": round(gvms * 1e3, 2), "median_us": round(med_ms[-1] * 1e3, 2),
+        "alg_bytes": gvb, "GB/s": round(gvb / (gvms * 1e-3) / 1e9, 1),
+        "frac_hbm": round(gvb / (gvms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+
+    dcfg, dms, dops, dr = dominant
+    achieved = dops / (dms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": "svdq_gemm_w4a4", "workload": dcfg.name,
+                "achieved": round(achieved, 1), "peak": PEAK_TOPS[dcfg.fmt], "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_TOPS[dcfg.fmt], 4),
+                "traffic": stored_traffic("gemm_w4a4.hip", dcfg.name),
+                "ops_per_launch": dops,
+                "note": "INT4 runs on int8 MFMA: tera-ops against the 5.0 POP/s int8 peak"
+                        if dcfg.fmt == "int4_g64" else "FP4 against the 10.1 PFLOP/s MXFP4 peak"}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfgs[0], gcfg, host_sets[0][2], gp, host_sets[0][1])
+
+    wl = ("DiT block linear stream (QKV, out-proj, MLP-up GELU, MLP-down; all W4A4 INT4 g64 r32)"
+          if args.workload == "block" else
+          f"SVDQ W4A4 {cfgs[0].name} M={cfgs[0].M} K={cfgs[0].K} N={cfgs[0].N} r={host_sets[0][1]} "
+          f"{cfgs[0].fmt} epilogue={cfgs[0].epilogue}")
+    wl += f" + AWQ W4A16 modulation GEMV M=1 K={gcfg.K} N={gcfg.N} g{gcfg.group}"
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "TOPS", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int8" if all(c.fmt == "int4_g64" for c in cfgs) else "fp4",
+        "data": "synthetic",
+        "config": {"workload": wl, "layers": names, "rotating_sets": nsets,
+                   "cache": "warm" if args.warm else "cold (rotated > Infinity Cache)"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "gemm_TOPS": round(sum(2.0 * c.M * c.N * c.K for c in cfgs) / (gemm_ms_sum * 1e-3) / 1e12, 1),
+        "gemv_GBps": kernels["gemv.awq_gemv_w4a16"]["GB/s"],
+        "device": torch.cuda.get_device_properties(dev).gcnArchName,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(cfg, gcfg, p, gp, r):
+    """The oracle's run-time steps, as they stand, on a bounded sample of the
+    same workload: quantizer + fp64 group-scaled GEMM + low-rank + bias on the
+    first `rows` tokens, and the fp64 AWQ GEMV. Scaled to TOPS over the
+    sample's own 2*rows*N*K."""
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    rows = min(cfg.M, 2048)
+    X = p["X"][:rows]
+    t0 = time.perf_counter()
+    codes_u, _, scales = oracle.quantize_act_ref(X, p["smooth_inv"], cfg.fmt)
+    la = oracle.lora_act_ref(X, p["lora_down"][:r])
+    wu = oracle.unpack_nibbles(p["w_codes"], signed=(cfg.fmt == "int4_g64"))
+    oracle.gemm_ref(codes_u, scales, la, wu, p["w_scales"], p["lora_up"][:, :r], p["bias"], cfg.fmt,
+                    cfg.epilogue)
+    t_layer = time.perf_counter() - t0
+    t1 = time.perf_counter()
+    oracle.gemv_ref(gp["x"], gp["codes"], gp["scales"], gp["zeros"], gcfg.group)
+    t_gemv = time.perf_counter() - t1
+    ops = 2.0 * rows * cfg.N * cfg.K
+    return {"value": round(ops / t_layer / 1e12, 5), "unit": "TOPS", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{rows} of {cfg.M} tokens of the {cfg.name} layer (quantizer + fp64 forward), "
+                      f"{t_layer:.2f} s; full AWQ GEMV fp64 {t_gemv * 1e3:.0f} ms "
+                      f"({gemv_bytes(gcfg) / t_gemv / 1e9:.2f} GB/s)"}
+
+
+if __name__ == "__main__":
+    main()

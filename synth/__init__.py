@@ -5,6 +5,7 @@ quantization method's arithmetic (no smoothing, no SVD, no quantizer, no
 forward). Both sides receive the same arrays from here.
 """
 from .inputs import (  # noqa: F401
+    BLOCK_STREAM,
     CONFIGS,
     LayerConfig,
     GemvConfig,
