@@ -26,6 +26,9 @@ HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result",
+    # MFMA results stay in VGPRs: the INT4 path converts every group partial
+    # with VALU ops, and AGPR copies would add one VALU op per element.
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

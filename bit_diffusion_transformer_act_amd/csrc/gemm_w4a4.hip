@@ -6,31 +6,61 @@
 // article, SVDQuant paragraph, and nextgz.net "Hugging Face brings Nunchaku
 // Lite to Diffusers", section "Why W4A4 differs from weight-only backends").
 //
-// Tiling: 128 x 128 output tile per workgroup of 4 waves (2 x 2, 64 x 64
-// per wave = 2 x 2 blocks of 32 x 32), K step 128 codes (64 packed bytes per
-// row) double-buffered in LDS with a 16-byte row pad.
+// Tiling: a workgroup of 4 waves (2 x 2) owns a BM x BN output tile, each wave
+// (32 WM) x (32 WN) built from 32 x 32 MFMA blocks. The K loop walks steps of
+// 128 codes (64 packed bytes per row). Each step (A codes, B codes and both
+// operands' scale words) is brought into an LDS ring of STAGES buffers by
+// LDS-DMA loads (global_load_lds_dwordx4 / _dword): no register staging, and
+// the loads for step ks + STAGES - 1 are in flight while step ks computes.
+// One barrier per step. Code rows are 64 bytes with the four 16-byte chunks
+// XOR-swizzled by (row >> 1) & 3 so the ds_read_b128 of 32 consecutive rows
+// spread over the banks.
+//
+// Blocks are remapped so that each of the 8 XCDs (round-robin dispatch)
+// works on a contiguous range of tiles, M-tile fastest, which keeps the A
+// rows of concurrently running tiles in that XCD's L2.
 //
 // Accumulators start from the low-rank product: lora_act (fp32 -> fp16) times
 // lora_up on v_mfma_f32_32x32x16_f16, 16 ranks per instruction.
 //
-// INT4_G64: each lane reads 16 packed bytes (32 codes) per 32-row block
-// and group; nibbles become int8 bytes holding 16 q with two ALU ops per
-// word (hi = w & 0xF0F0F0F0, lo = (w << 4) & 0xF0F0F0F0), so an int32 result
-// is 256 sum q_x q_w exactly. Two v_mfma_i32_32x32x32_i8 give one group's
-// partial; the group's scales s_x 2^-8 and s_w are applied in fp32. A and B
-// use the same permutation of k inside the instruction, which a dot product
-// does not see.
+// INT4_G64: each lane reads 16 packed bytes (32 codes) per 32-row block and
+// group; nibbles become int8 bytes holding 16 q with two ALU ops per word
+// (hi = w & 0xF0F0F0F0, lo = (w << 4) & 0xF0F0F0F0), so the int32 result is
+// 256 sum q_x q_w exactly. Two v_mfma_i32_32x32x32_i8 give one group's
+// partial, converted and scaled by s_x s_w 2^-8 in fp32. A and B use the same
+// permutation of k inside the instruction, which a dot product does not see.
 //
 // FP4_E2M1_B32: the packed codes are the operands of
 // v_mfma_scale_f32_32x32x64_f8f6f4 as they are (lane l: row l%32, k
 // 32 (l/32) .. +32), with the E8M0 byte of (row, 32-block) as the lane's
 // scale; the hardware applies both scales and accumulates in fp32.
+#include <atomic>
+
 #include "common.hpp"
 
 namespace svdq {
 
-constexpr int GBM = 128, GBN = 128;
-constexpr int GROWB = 80;  // LDS row stride (64 data bytes + 16 pad)
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// LDS-DMA loads: lane l's bytes land at lds_base + l * size. The LDS base is
+// wave-uniform (M0); the instruction has no destination register. Completion
+// is tracked with vmcnt by the caller (waitvm) before the barrier that
+// publishes the data.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_base)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds_base)
+               : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void waitvm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
 
 // 16 packed INT4 codes (two words) -> one int8 MFMA operand of 16 bytes:
 // [even codes of w0, odd codes of w0, even of w1, odd of w1], each byte 16 q.
@@ -39,43 +69,112 @@ __device__ __forceinline__ v4i unpack_i4x16(uint32_t w0, uint32_t w1) {
              (int)((w1 << 4) & 0xF0F0F0F0u), (int)(w1 & 0xF0F0F0F0u)};
 }
 
-template <int FMT, int EPI>
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 3; }
+
+template <int WM, int WN, int STAGES>
+struct GemmShape {
+  static constexpr int BM = 64 * WM, BN = 64 * WN;
+  static constexpr int A_BYTES = BM * 64, B_BYTES = BN * 64;
+  static constexpr int SC_INSTR = (BM + BN + 255) / 256;     // scale DMAs per wave per step
+  static constexpr int SC_ROWS = SC_INSTR * 256;
+  static constexpr int STAGE = A_BYTES + B_BYTES + SC_ROWS * 4;
+  static constexpr int LDS = STAGES * STAGE;
+  static constexpr int DMA_PER_STEP = BM / 64 + BN / 64 + SC_INSTR;  // per thread
+};
+
+template <int FMT, int EPI, int WM, int WN, int STAGES>
 __global__ __launch_bounds__(256)
 void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restrict__ act_scales,
                       const float* __restrict__ lora_act, const uint8_t* __restrict__ w_codes,
                       const void* __restrict__ w_scales, const __half* __restrict__ lora_up,
                       const __half* __restrict__ bias, __half* __restrict__ Y,
                       int M, int N, int K, int r) {
-  __shared__ __attribute__((aligned(16))) uint8_t sA[2][GBM * GROWB];
-  __shared__ __attribute__((aligned(16))) uint8_t sB[2][GBN * GROWB];
-  // INT4: fp32 scales [buf][group in step][row]; FP4: E8M0 bytes, one dword per row
-  __shared__ __attribute__((aligned(16))) float sSA[2][2][GBM];
-  __shared__ __attribute__((aligned(16))) float sSB[2][2][GBN];
+  using S = GemmShape<WM, WN, STAGES>;
+  constexpr int BM = S::BM, BN = S::BN;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int n0 = blockIdx.x * GBN;
-  const int m0 = blockIdx.y * GBM;
-  const int nk = K >> 7;
-  const int KB = K >> 1;  // bytes per packed row
   const int l32 = lane & 31, lh = lane >> 5;
 
+  // ---- tile index, XCD-aware
+  const int ntm = (M + BM - 1) / BM;
+  const int ntiles = ntm * (N / BN);
+  int pid = blockIdx.x;
+  if ((ntiles & 7) == 0) pid = (pid & 7) * (ntiles >> 3) + (pid >> 3);
+  const int m0 = (pid % ntm) * BM;
+  const int n0 = (pid / ntm) * BN;
+  const int nk = K >> 7;
+  const int KB = K >> 1;  // bytes per packed row
+  const int sstride = (FMT == 0) ? (K >> 6) * 2 : (K >> 5);  // scale bytes per row
+
+  // ---- DMA source pointers (per lane) for step 0; advance by 64 B (codes) / 4 B (scales)
+  const uint8_t* ga[BM / 64];
+  const uint8_t* gb[BN / 64];
+  const uint8_t* gs[S::SC_INSTR];
+  uint32_t la_off[BM / 64], lb_off[BN / 64], ls_off[S::SC_INSTR];
+  const uint32_t lds0 = lds_addr(smem);
+#pragma unroll
+  for (int i = 0; i < BM / 64; ++i) {
+    // wave w, instruction i: 16 rows starting at w*(BM/4) + 16 i; lane -> (row, slot)
+    const int rloc = wave * (BM / 4) + 16 * i;
+    const int row = rloc + (lane >> 2);
+    const int chunk = (lane & 3) ^ swz(row);
+    const int grow = min(m0 + row, M - 1);
+    ga[i] = act_codes + (size_t)grow * KB + chunk * 16;
+    la_off[i] = rloc * 64;
+  }
+#pragma unroll
+  for (int i = 0; i < BN / 64; ++i) {
+    const int rloc = wave * (BN / 4) + 16 * i;
+    const int row = rloc + (lane >> 2);
+    const int chunk = (lane & 3) ^ swz(row);
+    gb[i] = w_codes + (size_t)(n0 + row) * KB + chunk * 16;
+    lb_off[i] = S::A_BYTES + rloc * 64;
+  }
+#pragma unroll
+  for (int i = 0; i < S::SC_INSTR; ++i) {
+    const int rloc = (wave * S::SC_INSTR + i) * 64;
+    const int row = rloc + lane;   // rows [0, BM) are A, [BM, BM + BN) are B, beyond: padding
+    const uint8_t* p;
+    if (row < BM) p = reinterpret_cast<const uint8_t*>(act_scales) + (size_t)min(m0 + row, M - 1) * sstride;
+    else if (row < BM + BN) p = reinterpret_cast<const uint8_t*>(w_scales) + (size_t)(n0 + row - BM) * sstride;
+    else p = reinterpret_cast<const uint8_t*>(w_scales) + (size_t)n0 * sstride;
+    gs[i] = p;
+    ls_off[i] = S::A_BYTES + S::B_BYTES + rloc * 4;
+  }
+
+  auto issue = [&](int ks) {
+    const uint32_t base = lds0 + (uint32_t)((ks % STAGES) * S::STAGE);
+#pragma unroll
+    for (int i = 0; i < BM / 64; ++i) dma16(ga[i] + ks * 64, base + la_off[i]);
+#pragma unroll
+    for (int i = 0; i < BN / 64; ++i) dma16(gb[i] + ks * 64, base + lb_off[i]);
+#pragma unroll
+    for (int i = 0; i < S::SC_INSTR; ++i) dma4(gs[i] + ks * 4, base + ls_off[i]);
+  };
+
+  // prologue loads go out before the low-rank product so they overlap it
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < nk) issue(s);
+
   // ---- low-rank up-projection initialises the accumulators
-  v16f acc[2][2];
+  v16f acc[WM][WN];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < WM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < WN; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
   for (int j0 = 0; j0 < r; j0 += 16) {
-    v8h a[2], b[2];
+    v8h a[WM], b[WN];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const int m = m0 + wm * 64 + rb * 32 + l32;
+    for (int rb = 0; rb < WM; ++rb) {
+      const int m = m0 + wm * 32 * WM + rb * 32 + l32;
       if (m < M) {
         const float4* p = reinterpret_cast<const float4*>(lora_act + (size_t)m * r + j0 + lh * 8);
         const float4 u = p[0], w = p[1];
@@ -86,163 +185,134 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restr
       }
     }
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      const int n = n0 + wn * 64 + cb * 32 + l32;
+    for (int cb = 0; cb < WN; ++cb) {
+      const int n = n0 + wn * 32 * WN + cb * 32 + l32;
       b[cb] = __builtin_bit_cast(v8h, *reinterpret_cast<const uint4*>(lora_up + (size_t)n * r + j0 + lh * 8));
     }
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < WM; ++rb)
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
+      for (int cb = 0; cb < WN; ++cb)
         acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[rb], b[cb], acc[rb][cb], 0, 0, 0);
   }
 
-  // ---- global -> register staging for one K step
-  // thread t: rows t/4 and 64 + t/4 of each tile, 16-byte chunk t%4
-  const int ld_row = tid >> 2, ld_chk = tid & 3;
-  uint4 ra[2], rbv[2];
-  uint32_t rsa = 0, rsb = 0;  // scale words (2 fp16 or 4 E8M0 bytes)
-
-  auto gload = [&](int ks) {
+  // LDS read offsets (within a stage) of this lane's operand rows
+  int arow[WM], brow[WN];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int ar = m0 + ld_row + 64 * h;
-      ra[h] = (ar < M) ? *reinterpret_cast<const uint4*>(act_codes + (size_t)ar * KB + ks * 64 + ld_chk * 16)
-                       : make_uint4(0, 0, 0, 0);
-      const int br = n0 + ld_row + 64 * h;
-      rbv[h] = *reinterpret_cast<const uint4*>(w_codes + (size_t)br * KB + ks * 64 + ld_chk * 16);
-    }
-    if (tid < GBM) {
-      const int ar = m0 + tid;
-      if (FMT == 0)
-        rsa = (ar < M) ? *reinterpret_cast<const uint32_t*>(reinterpret_cast<const __half*>(act_scales) + (size_t)ar * (K >> 6) + 2 * ks) : 0u;
-      else
-        rsa = (ar < M) ? *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(act_scales) + (size_t)ar * (K >> 5) + 4 * ks) : 0u;
-    } else {
-      const int br = n0 + tid - GBM;
-      if (FMT == 0)
-        rsb = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const __half*>(w_scales) + (size_t)br * (K >> 6) + 2 * ks);
-      else
-        rsb = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(w_scales) + (size_t)br * (K >> 5) + 4 * ks);
-    }
-  };
-  auto sstore = [&](int buf) {
+  for (int rb = 0; rb < WM; ++rb) arow[rb] = wm * 32 * WM + rb * 32 + l32;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      *reinterpret_cast<uint4*>(&sA[buf][(ld_row + 64 * h) * GROWB + ld_chk * 16]) = ra[h];
-      *reinterpret_cast<uint4*>(&sB[buf][(ld_row + 64 * h) * GROWB + ld_chk * 16]) = rbv[h];
-    }
-    if (tid < GBM) {
-      if (FMT == 0) {
-        const __half2 hv = __builtin_bit_cast(__half2, rsa);
-        sSA[buf][0][tid] = __low2float(hv) * 0.00390625f;   // fold the 16 x 16 nibble shift
-        sSA[buf][1][tid] = __high2float(hv) * 0.00390625f;
-      } else {
-        reinterpret_cast<uint32_t*>(&sSA[buf][0][0])[tid] = rsa;
-      }
-    } else {
-      const int t = tid - GBM;
-      if (FMT == 0) {
-        const __half2 hv = __builtin_bit_cast(__half2, rsb);
-        sSB[buf][0][t] = __low2float(hv);
-        sSB[buf][1][t] = __high2float(hv);
-      } else {
-        reinterpret_cast<uint32_t*>(&sSB[buf][0][0])[t] = rsb;
-      }
-    }
-  };
-
-  gload(0);
-  sstore(0);
-  __syncthreads();
+  for (int cb = 0; cb < WN; ++cb) brow[cb] = wn * 32 * WN + cb * 32 + l32;
 
   for (int ks = 0; ks < nk; ++ks) {
-    const int buf = ks & 1;
-    if (ks + 1 < nk) gload(ks + 1);
+    if (ks + STAGES - 2 < nk) waitvm<S::DMA_PER_STEP * (STAGES - 2)>();
+    else waitvm<0>();
+    __syncthreads();
+    if (ks + STAGES - 1 < nk) issue(ks + STAGES - 1);
 
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      uint4 ap[2], bp[2];
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-        ap[rb] = *reinterpret_cast<const uint4*>(&sA[buf][(wm * 64 + rb * 32 + l32) * GROWB + g * 32 + lh * 16]);
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
-        bp[cb] = *reinterpret_cast<const uint4*>(&sB[buf][(wn * 64 + cb * 32 + l32) * GROWB + g * 32 + lh * 16]);
+    const uint8_t* st = smem + (ks % STAGES) * S::STAGE;
+    const uint8_t* sA = st;
+    const uint8_t* sB = st + S::A_BYTES;
+    const uint32_t* sS = reinterpret_cast<const uint32_t*>(st + S::A_BYTES + S::B_BYTES);
 
-      if constexpr (FMT == 0) {
-        v4i a0[2], a1[2], b0[2], b1[2];
+    if constexpr (FMT == 0) {
+      // scale words of this step: 2 fp16 per row (groups 2 ks, 2 ks + 1)
+      // lane rows in block rb: (v/4)*8 + lh*4 + v%4 -> four 16-byte reads
+      uint4 sxw[WM][4];
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          a0[rb] = unpack_i4x16(ap[rb].x, ap[rb].y);
-          a1[rb] = unpack_i4x16(ap[rb].z, ap[rb].w);
+      for (int rb = 0; rb < WM; ++rb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          sxw[rb][q] = *reinterpret_cast<const uint4*>(sS + wm * 32 * WM + rb * 32 + q * 8 + lh * 4);
+      float sw[WN][2];
+#pragma unroll
+      for (int cb = 0; cb < WN; ++cb) {
+        const __half2 h = __builtin_bit_cast(__half2, sS[BM + brow[cb]]);
+        sw[cb][0] = __low2float(h) * 0.00390625f;   // 16 x 16 nibble shift folded here
+        sw[cb][1] = __high2float(h) * 0.00390625f;
+      }
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        v4i a0[WM], a1[WM], b0[WN], b1[WN];
+#pragma unroll
+        for (int rb = 0; rb < WM; ++rb) {
+          const int rr = arow[rb];
+          const uint4 ap = *reinterpret_cast<const uint4*>(sA + rr * 64 + (((g * 2 + lh) ^ swz(rr)) << 4));
+          a0[rb] = unpack_i4x16(ap.x, ap.y);
+          a1[rb] = unpack_i4x16(ap.z, ap.w);
         }
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-          b0[cb] = unpack_i4x16(bp[cb].x, bp[cb].y);
-          b1[cb] = unpack_i4x16(bp[cb].z, bp[cb].w);
+        for (int cb = 0; cb < WN; ++cb) {
+          const int rr = brow[cb];
+          const uint4 bp = *reinterpret_cast<const uint4*>(sB + rr * 64 + (((g * 2 + lh) ^ swz(rr)) << 4));
+          b0[cb] = unpack_i4x16(bp.x, bp.y);
+          b1[cb] = unpack_i4x16(bp.z, bp.w);
         }
-        float sw[2];
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb) sw[cb] = sSB[buf][g][wn * 64 + cb * 32 + l32];
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          // rows of this lane in block rb: (v/4)*8 + lh*4 + v%4
+        for (int rb = 0; rb < WM; ++rb) {
           float sx[16];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const float4 t4 = *reinterpret_cast<const float4*>(&sSA[buf][g][wm * 64 + rb * 32 + q * 8 + lh * 4]);
-            sx[4 * q + 0] = t4.x; sx[4 * q + 1] = t4.y; sx[4 * q + 2] = t4.z; sx[4 * q + 3] = t4.w;
+            const uint32_t wv[4] = {sxw[rb][q].x, sxw[rb][q].y, sxw[rb][q].z, sxw[rb][q].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const __half2 h = __builtin_bit_cast(__half2, wv[e]);
+              sx[4 * q + e] = g ? __high2float(h) : __low2float(h);
+            }
           }
 #pragma unroll
-          for (int cb = 0; cb < 2; ++cb) {
+          for (int cb = 0; cb < WN; ++cb) {
             v16i p = {};
             p = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0[rb], b0[cb], p, 0, 0, 0);
             p = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1[rb], b1[cb], p, 0, 0, 0);
 #pragma unroll
             for (int v = 0; v < 16; ++v)
-              acc[rb][cb][v] = fmaf((float)p[v], sx[v] * sw[cb], acc[rb][cb][v]);
+              acc[rb][cb][v] = fmaf((float)p[v], sx[v] * sw[cb][g], acc[rb][cb][v]);
           }
         }
-      } else {
-        const uint32_t* ea = reinterpret_cast<const uint32_t*>(&sSA[buf][0][0]);
-        const uint32_t* eb = reinterpret_cast<const uint32_t*>(&sSB[buf][0][0]);
+      }
+    } else {
+      uint32_t ea[WM], eb[WN];
+#pragma unroll
+      for (int rb = 0; rb < WM; ++rb) ea[rb] = sS[arow[rb]];
+#pragma unroll
+      for (int cb = 0; cb < WN; ++cb) eb[cb] = sS[BM + brow[cb]];
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
         const int sh = 8 * (2 * g + lh);
-        int sa[2], sb[2];
-        v8i av[2], bv[2];
+        v8i av[WM], bv[WN];
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          sa[rb] = (int)((ea[wm * 64 + rb * 32 + l32] >> sh) & 0xFFu);
-          av[rb] = v8i{(int)ap[rb].x, (int)ap[rb].y, (int)ap[rb].z, (int)ap[rb].w, 0, 0, 0, 0};
+        for (int rb = 0; rb < WM; ++rb) {
+          const int rr = arow[rb];
+          const uint4 ap = *reinterpret_cast<const uint4*>(sA + rr * 64 + (((g * 2 + lh) ^ swz(rr)) << 4));
+          av[rb] = v8i{(int)ap.x, (int)ap.y, (int)ap.z, (int)ap.w, 0, 0, 0, 0};
         }
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-          sb[cb] = (int)((eb[wn * 64 + cb * 32 + l32] >> sh) & 0xFFu);
-          bv[cb] = v8i{(int)bp[cb].x, (int)bp[cb].y, (int)bp[cb].z, (int)bp[cb].w, 0, 0, 0, 0};
+        for (int cb = 0; cb < WN; ++cb) {
+          const int rr = brow[cb];
+          const uint4 bp = *reinterpret_cast<const uint4*>(sB + rr * 64 + (((g * 2 + lh) ^ swz(rr)) << 4));
+          bv[cb] = v8i{(int)bp.x, (int)bp.y, (int)bp.z, (int)bp.w, 0, 0, 0, 0};
         }
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
+        for (int rb = 0; rb < WM; ++rb)
 #pragma unroll
-          for (int cb = 0; cb < 2; ++cb)
+          for (int cb = 0; cb < WN; ++cb)
             acc[rb][cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                av[rb], bv[cb], acc[rb][cb], 4, 4, 0, sa[rb], 0, sb[cb]);
+                av[rb], bv[cb], acc[rb][cb], 4, 4, 0, (int)((ea[rb] >> sh) & 0xFFu), 0,
+                (int)((eb[cb] >> sh) & 0xFFu));
       }
     }
-
-    if (ks + 1 < nk) sstore(buf ^ 1);
-    __syncthreads();
   }
 
   // ---- epilogue: bias, activation, fp16 store
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    const int n = n0 + wn * 64 + cb * 32 + l32;
+  for (int cb = 0; cb < WN; ++cb) {
+    const int n = n0 + brow[cb];
     const float bn = bias ? __half2float(bias[n]) : 0.f;
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < WM; ++rb) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int m = m0 + wm * 64 + rb * 32 + (v >> 2) * 8 + lh * 4 + (v & 3);
+        const int m = m0 + wm * 32 * WM + rb * 32 + (v >> 2) * 8 + lh * 4 + (v & 3);
         if (m < M) {
           float yv = acc[rb][cb][v] + bn;
           if (EPI == 1) yv = gelu_tanh_f32(yv);
@@ -253,20 +323,38 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restr
   }
 }
 
+template <int FMT, int EPI, int WM, int WN, int STAGES>
+static hipError_t launch_cfg(int M, int N, int K, int r, const uint8_t* ac, const void* as,
+                             const float* la, const uint8_t* wc, const void* ws, const void* lu,
+                             const void* bias, void* Y, hipStream_t st) {
+  using S = GemmShape<WM, WN, STAGES>;
+  auto kern = gemm_w4a4_kernel<FMT, EPI, WM, WN, STAGES>;
+  if (S::LDS > 65536) {
+    static std::atomic<int> raised{0};
+    if (!raised.load(std::memory_order_acquire)) {
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS);
+      if (e != hipSuccess) return e;
+      raised.store(1, std::memory_order_release);
+    }
+  }
+  const int ntiles = ((M + S::BM - 1) / S::BM) * (N / S::BN);
+  hipLaunchKernelGGL(kern, dim3(ntiles), dim3(256), S::LDS, st, ac, as, la, wc, ws,
+                     (const __half*)lu, (const __half*)bias, (__half*)Y, M, N, K, r);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_w4a4(int fmt, int M, int N, int K, int r, const uint8_t* ac, const void* as,
                             const float* la, const uint8_t* wc, const void* ws, const void* lu,
                             const void* bias, int epi, void* Y, hipStream_t st) {
-  const dim3 grid(N / GBN, (M + GBM - 1) / GBM), block(256);
-#define SVDQ_LAUNCH(F, E)                                                                   \
-  hipLaunchKernelGGL((gemm_w4a4_kernel<F, E>), grid, block, 0, st, ac, as, la, wc, ws,      \
-                     (const __half*)lu, (const __half*)bias, (__half*)Y, M, N, K, r)
+#define SVDQ_GO(F, E, WM_, WN_, ST_) \
+  return launch_cfg<F, E, WM_, WN_, ST_>(M, N, K, r, ac, as, la, wc, ws, lu, bias, Y, st)
   if (fmt == 0) {
-    if (epi == 0) SVDQ_LAUNCH(0, 0); else SVDQ_LAUNCH(0, 1);
+    if (epi == 0) SVDQ_GO(0, 0, 2, 2, 4); else SVDQ_GO(0, 1, 2, 2, 4);
   } else {
-    if (epi == 0) SVDQ_LAUNCH(1, 0); else SVDQ_LAUNCH(1, 1);
+    if (epi == 0) SVDQ_GO(1, 0, 2, 2, 4); else SVDQ_GO(1, 1, 2, 2, 4);
   }
-#undef SVDQ_LAUNCH
-  return hipGetLastError();
+#undef SVDQ_GO
 }
 
 }  // namespace svdq
