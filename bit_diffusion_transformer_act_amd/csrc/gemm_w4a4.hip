@@ -27,7 +27,11 @@
 // group; nibbles become int8 bytes holding 16 q with two ALU ops per word
 // (hi = w & 0xF0F0F0F0, lo = (w << 4) & 0xF0F0F0F0), so the int32 result is
 // 256 sum q_x q_w exactly. Two v_mfma_i32_32x32x32_i8 give one group's
-// partial, converted and scaled by s_x s_w 2^-8 in fp32. A and B use the same
+// partial P. The int32 accumulation starts from the bit pattern of 1.5 * 2^23,
+// so the result read as fp32 is exactly 1.5*2^23 + 256 P; one fma with
+// s_w 2^-8 and the exact constant -1.5*2^23 s_w 2^-8 yields fl(P s_w) with no
+// int-to-float convert, and a second fma adds s_x times that to the fp32
+// accumulator: two VALU ops per output and group. A and B use the same
 // permutation of k inside the instruction, which a dot product does not see.
 //
 // FP4_E2M1_B32: the packed codes are the operands of
@@ -70,6 +74,13 @@ __device__ __forceinline__ v4i unpack_i4x16(uint32_t w0, uint32_t w1) {
 }
 
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 3; }
+
+// 0x4B400000 is 1.5 * 2^23 as fp32: integers added to it stay exact in the
+// mantissa while |x| < 2^22.
+constexpr int kMagicBits = 0x4B400000;
+#define SVDQ_M16 kMagicBits, kMagicBits, kMagicBits, kMagicBits
+__device__ constexpr v16i kMagic16 = {SVDQ_M16, SVDQ_M16, SVDQ_M16, SVDQ_M16};
+#undef SVDQ_M16
 
 template <int WM, int WN, int STAGES>
 struct GemmShape {
@@ -223,12 +234,16 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restr
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           sxw[rb][q] = *reinterpret_cast<const uint4*>(sS + wm * 32 * WM + rb * 32 + q * 8 + lh * 4);
-      float sw[WN][2];
+      // sw' = s_w 2^-8 (the 16 x 16 nibble shift) and -1.5*2^23 sw' (exact:
+      // s_w has 11 significant bits, 3 s_w at most 13)
+      float swp[WN][2], swm[WN][2];
 #pragma unroll
       for (int cb = 0; cb < WN; ++cb) {
         const __half2 h = __builtin_bit_cast(__half2, sS[BM + brow[cb]]);
-        sw[cb][0] = __low2float(h) * 0.00390625f;   // 16 x 16 nibble shift folded here
-        sw[cb][1] = __high2float(h) * 0.00390625f;
+        swp[cb][0] = __low2float(h) * 0.00390625f;
+        swp[cb][1] = __high2float(h) * 0.00390625f;
+        swm[cb][0] = swp[cb][0] * -12582912.0f;
+        swm[cb][1] = swp[cb][1] * -12582912.0f;
       }
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
@@ -249,24 +264,29 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restr
         }
 #pragma unroll
         for (int rb = 0; rb < WM; ++rb) {
-          float sx[16];
+          _Float16 sx[16];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const uint32_t wv[4] = {sxw[rb][q].x, sxw[rb][q].y, sxw[rb][q].z, sxw[rb][q].w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const __half2 h = __builtin_bit_cast(__half2, wv[e]);
-              sx[4 * q + e] = g ? __high2float(h) : __low2float(h);
+              const v2h h = __builtin_bit_cast(v2h, wv[e]);
+              sx[4 * q + e] = h[g];
             }
           }
 #pragma unroll
           for (int cb = 0; cb < WN; ++cb) {
-            v16i p = {};
+            // int32 accumulation starts at the bit pattern of 1.5 * 2^23, so the
+            // result read as fp32 is exactly 1.5 * 2^23 + 256 P (|256 P| < 2^22)
+            v16i p = kMagic16;
             p = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0[rb], b0[cb], p, 0, 0, 0);
             p = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1[rb], b1[cb], p, 0, 0, 0);
 #pragma unroll
-            for (int v = 0; v < 16; ++v)
-              acc[rb][cb][v] = fmaf((float)p[v], sx[v] * sw[cb][g], acc[rb][cb][v]);
+            for (int v = 0; v < 16; ++v) {
+              // t = fl(P s_w): one rounding of the exact (1.5*2^23 + 256 P) sw' - 1.5*2^23 sw'
+              const float t = fmaf(__int_as_float(p[v]), swp[cb][g], swm[cb][g]);
+              acc[rb][cb][v] = fmaf(t, (float)sx[v], acc[rb][cb][v]);
+            }
           }
         }
       }
