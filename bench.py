@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--warm", action="store_true", help="no buffer rotation (cache-warm)")
     ap.add_argument("--rank", type=int, default=None, help="override the low-rank width")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after the timed region, run one plain device copy of this many MiB "
+                         "(the reference kernel for scaling HBM byte counters)")
     return ap.parse_args()
 
 
@@ -184,6 +187,14 @@ def main():
         step(args.warmup + s, evs[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)     # writes n bytes
+        torch.cuda.synchronize()
+        dst = torch.add(src, 1)                                 # reads n, writes n bytes
+        torch.cuda.synchronize()
+        del src, dst
 
     # per-launch durations (ms): launch k spans events[k] -> events[k+1]
     durs = np.zeros((args.steps, nk))

@@ -17,8 +17,8 @@
 // spread over the banks.
 //
 // Blocks are remapped so that each of the 8 XCDs (round-robin dispatch)
-// works on a contiguous range of tiles, M-tile fastest, which keeps the A
-// rows of concurrently running tiles in that XCD's L2.
+// works on a contiguous range of tiles in 8-M-tile groups, which keeps the A
+// and B rows of concurrently running tiles in that XCD's L2.
 //
 // Accumulators start from the low-rank product: lora_act (fp32 -> fp16) times
 // lora_up on v_mfma_f32_32x32x16_f16, 16 ranks per instruction.
@@ -110,13 +110,21 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restr
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, lh = lane >> 5;
 
-  // ---- tile index, XCD-aware
+  // ---- tile index, XCD-aware: XCD x (blocks x, x+8, ...) takes the x-th
+  // contiguous eighth of the logical tiles, which run in groups of 8 M-tiles
+  // with N outer, so the ~64 tiles resident on one XCD form an 8 x 8 patch and
+  // share A and B rows through that XCD's L2.
   const int ntm = (M + BM - 1) / BM;
-  const int ntiles = ntm * (N / BN);
+  const int ntn = N / BN;
+  const int ntiles = ntm * ntn;
   int pid = blockIdx.x;
   if ((ntiles & 7) == 0) pid = (pid & 7) * (ntiles >> 3) + (pid >> 3);
-  const int m0 = (pid % ntm) * BM;
-  const int n0 = (pid / ntm) * BN;
+  constexpr int GROUP_M = 8;
+  const int gsz = GROUP_M * ntn;
+  const int first_m = (pid / gsz) * GROUP_M;
+  const int gm = min(ntm - first_m, GROUP_M);
+  const int m0 = (first_m + (pid % gsz) % gm) * BM;
+  const int n0 = ((pid % gsz) / gm) * BN;
   const int nk = K >> 7;
   const int KB = K >> 1;  // bytes per packed row
   const int sstride = (FMT == 0) ? (K >> 6) * 2 : (K >> 5);  // scale bytes per row

@@ -50,22 +50,30 @@ void quantize_act_kernel(const __half* __restrict__ X, const float* __restrict__
 #pragma unroll
   for (int c = 0; c < (NCB > 0 ? NCB : 1); ++c) lacc[c] = v4f{0.f, 0.f, 0.f, 0.f};
 
+  // X for the wave's first step; each iteration prefetches the next step's
+  // X before working on the current one.
+  uint4 xa = make_uint4(0, 0, 0, 0), xb = make_uint4(0, 0, 0, 0);
+  if (row_ok && wave < steps) {
+    const uint4* p = reinterpret_cast<const uint4*>(X + xrow + wave * 64 + q4 * 16);
+    xa = p[0];
+    xb = p[1];
+  }
   for (int s = wave; s < steps; s += kWaves) {
     const int k0 = s * 64 + q4 * 16;
-    uint4 xa = make_uint4(0, 0, 0, 0), xb = make_uint4(0, 0, 0, 0);
-    if (row_ok) {
-      const uint4* p = reinterpret_cast<const uint4*>(X + xrow + k0);
+    const uint4 ca = xa, cb = xb;
+    if (row_ok && s + kWaves < steps) {
+      const uint4* p = reinterpret_cast<const uint4*>(X + xrow + k0 + kWaves * 64);
       xa = p[0];
       xb = p[1];
     }
     if constexpr (NCB > 0) {
-      v8h a0 = __builtin_bit_cast(v8h, xa);
-      v8h a1 = __builtin_bit_cast(v8h, xb);
+      const v8h a0 = __builtin_bit_cast(v8h, ca);
+      const v8h a1 = __builtin_bit_cast(v8h, cb);
 #pragma unroll
       for (int c = 0; c < NCB; ++c) {
         const uint4* pb = reinterpret_cast<const uint4*>(lora_down + (size_t)(c * 16 + (lane & 15)) * K + k0);
-        v8h b0 = __builtin_bit_cast(v8h, pb[0]);
-        v8h b1 = __builtin_bit_cast(v8h, pb[1]);
+        const v8h b0 = __builtin_bit_cast(v8h, pb[0]);
+        const v8h b1 = __builtin_bit_cast(v8h, pb[1]);
         lacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b0, lacc[c], 0, 0, 0);
         lacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b1, lacc[c], 0, 0, 0);
       }
@@ -74,11 +82,11 @@ void quantize_act_kernel(const __half* __restrict__ X, const float* __restrict__
     float xh[16];
     {
       const float4* ps = reinterpret_cast<const float4*>(smooth_inv + k0);
-      const __half* ha = reinterpret_cast<const __half*>(&xa);
-      const __half* hb = reinterpret_cast<const __half*>(&xb);
+      const __half* ha = reinterpret_cast<const __half*>(&ca);
+      const __half* hb = reinterpret_cast<const __half*>(&cb);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float4 sv = ps[i];
+        const float4 sv = ps[i];
         const __half* hs = (i < 2) ? ha + 4 * i : hb + 4 * (i - 2);
         xh[4 * i + 0] = __half2float(hs[0]) * sv.x;
         xh[4 * i + 1] = __half2float(hs[1]) * sv.y;
@@ -99,12 +107,35 @@ void quantize_act_kernel(const __half* __restrict__ X, const float* __restrict__
       const __half s16 = __float2half_rn(fminf(s32, 65504.0f));
       const float sf = __half2float(s16);
       if (sf != 0.0f) {
+        // q = clamp(rint(fl32(x_hat / s)), -7, 7) without a division per value:
+        // y = x_hat * rcp(s) is within 2^-19 |y| of fl32(x_hat / s) (rcp and the
+        // multiply are each within an ulp), so the two round to the same integer
+        // unless y lies within 2^-16 of a half-integer; only such values are
+        // recomputed with the IEEE division. Clamping first is harmless: every
+        // value beyond +-7 maps to +-7 either way. Rounding is the add/subtract
+        // of 1.5 * 2^23, whose low mantissa bits are then the two's-complement
+        // code.
+        const float rs = __builtin_amdgcn_rcpf(sf);
+        bool near_tie = false;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          float q = rintf(xh[i] / sf);                  // IEEE division, ties to even
-          q = fminf(fmaxf(q, -7.0f), 7.0f);
-          const uint32_t nib = (uint32_t)((int)q) & 0xFu;
+          const float c = __builtin_amdgcn_fmed3f(xh[i] * rs, -7.0f, 7.0f);
+          const float yv = c + 12582912.0f;
+          const float rv = yv - 12582912.0f;
+          near_tie |= fabsf(c - rv) > 0.4999847412109375f;   // 0.5 - 2^-16
+          const uint32_t nib = __float_as_uint(yv) & 0xFu;
           if (i < 8) w0 |= nib << (4 * i); else w1 |= nib << (4 * (i - 8));
+        }
+        if (near_tie) {
+          w0 = 0;
+          w1 = 0;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            float q = rintf(xh[i] / sf);                // IEEE division, ties to even
+            q = fminf(fmaxf(q, -7.0f), 7.0f);
+            const uint32_t nib = (uint32_t)((int)q) & 0xFu;
+            if (i < 8) w0 |= nib << (4 * i); else w1 |= nib << (4 * (i - 8));
+          }
         }
       }
       if (row_ok) {
@@ -122,14 +153,18 @@ void quantize_act_kernel(const __half* __restrict__ X, const float* __restrict__
         e = min(max(e, -127), 127);
         sc = (uint32_t)(e + 127);
         const float p = ldexpf(1.0f, -e);               // exact power of two
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float u = fabsf(xh[i] * p);
-          uint32_t mag = (u > 0.25f) + (u >= 0.75f) + (u > 1.25f) + (u >= 1.75f) +
-                         (u > 2.5f) + (u >= 3.5f) + (u > 5.0f);
-          const uint32_t nib = mag | (signbit(xh[i]) ? 8u : 0u);
-          if (i < 8) w0 |= nib << (4 * i); else w1 |= nib << (4 * (i - 8));
-        }
+        // u = fl32(x_hat / 2^e) = x_hat * 2^-e; v_cvt_scalef32_pk_fp4_f32 with
+        // scale 1 rounds two values to E2M1 (nearest, ties to even mantissa,
+        // saturating at 6, sign kept, first value in the low nibble) and writes
+        // the byte selected by its last operand.
+        w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, xh[0] * p, xh[1] * p, 1.0f, 0);
+        w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, xh[2] * p, xh[3] * p, 1.0f, 1);
+        w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, xh[4] * p, xh[5] * p, 1.0f, 2);
+        w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, xh[6] * p, xh[7] * p, 1.0f, 3);
+        w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, xh[8] * p, xh[9] * p, 1.0f, 0);
+        w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, xh[10] * p, xh[11] * p, 1.0f, 1);
+        w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, xh[12] * p, xh[13] * p, 1.0f, 2);
+        w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, xh[14] * p, xh[15] * p, 1.0f, 3);
       }
       if (row_ok) {
         *reinterpret_cast<uint2*>(codes + (size_t)row * (K >> 1) + s * 32 + q4 * 8) = make_uint2(w0, w1);

@@ -173,9 +173,7 @@ int svdq_gemm_w4a4(int fmt, int M, int N, int K, int r,
  *   x       fp16 [M][K].
  *   w_codes u8 [N][K/2], unsigned nibbles, even k in the low nibble.
  *   scales  fp16 [N][K/64].
- *   zeros   fp16 [N][K/64], in code units; must hold integers 0..15 (a
- *           non-integer zero is rounded to an integer by the packed fp16
- *           dequantization).
+ *   zeros   fp16 [N][K/64], in code units (any fp16 value).
  *   y       out, fp16 [M][N].
  *   stream  hipStream_t.
  */

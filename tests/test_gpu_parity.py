@@ -216,11 +216,25 @@ def test_awq_gemv(P, M, N):
     assert rel_l2(host(y), y_ref) <= Y_TOL
 
 
-def test_awq_gemv_random_params_other_k(P):
-    g = synth.GemvConfig("gemv_k4096", 40, 1, 4096, 512, 64)
-    p = synth.random_awq_layer(g, seed=5, M=4)
+@pytest.mark.parametrize("M,K,N", [(4, 4096, 512), (1, 12288, 3072), (2, 16384, 300),
+                                   (1, 16448, 77), (8, 4096, 130), (1, 64, 5)])
+def test_awq_gemv_random_params_other_k(P, M, K, N):
+    """Both kernel paths (x in registers for M * ceil(K/4096) <= 4, x in LDS
+    otherwise), ragged N, K not a multiple of 4096."""
+    g = synth.GemvConfig(f"gemv_k{K}", 40, 1, K, N, 64)
+    p = synth.random_awq_layer(g, seed=5, M=M)
     y_ref = oracle.gemv_ref(p["x"], p["codes"], p["scales"], p["zeros"])
     y = P.awq_gemv_w4a16(dev(p["x"]), dev(p["codes"]), dev(p["scales"]), dev(p["zeros"]))
+    assert rel_l2(host(y), y_ref) <= Y_TOL
+
+
+@pytest.mark.parametrize("M", [1, 8])
+def test_awq_gemv_fractional_zeros(P, M):
+    g = synth.GemvConfig("gemv_fz", 41, 1, 1024, 256, 64)
+    p = synth.random_awq_layer(g, seed=6, M=M)
+    z = (p["zeros"].astype(np.float32) + np.random.default_rng(1).uniform(-0.5, 0.5, p["zeros"].shape)).astype(np.float16)
+    y_ref = oracle.gemv_ref(p["x"], p["codes"], p["scales"], z)
+    y = P.awq_gemv_w4a16(dev(p["x"]), dev(p["codes"]), dev(p["scales"]), dev(z))
     assert rel_l2(host(y), y_ref) <= Y_TOL
 
 
