@@ -1,0 +1,102 @@
+#!/usr/bin/env python3
+"""HBM traffic per launch from rocprofv3 counter passes, for bench.py's
+roofline `traffic` field.
+
+Input: the counter_collection.csv of one `rocprofv3 --pmc FETCH_SIZE` pass and
+one `--pmc WRITE_SIZE` pass over the same `bench.py --calib-copy-mib N` command.
+The calibration kernels that command runs after its timed region (a torch fill
+that writes N MiB, then a torch add that reads N MiB and writes N MiB) give the
+counter-to-bytes factors: fetch factor = add's FETCH_SIZE / N MiB, write factor
+= fill's WRITE_SIZE / N MiB. Each library kernel's average counters are divided
+by those factors.
+
+Writes profiles/traffic_<workload>.json (read by bench.py, which reports the
+figure only while the GEMM source hash recorded here still matches) and prints
+a short text summary.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import hashlib
+import json
+import os
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+KERNELS = {"svdq_gemm_w4a4": ("gemm_w4a4_kernel", "gemm_w4a4.hip"),
+           "svdq_quantize_act": ("quantize_act_kernel", "quantize_act.hip"),
+           "awq_gemv_w4a16": ("awq_gemv", "awq_gemv.hip")}
+
+
+def source_sha(fname: str) -> str:
+    p = os.path.join(ROOT, "bit_diffusion_transformer_act_amd", "csrc", fname)
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def per_dispatch(path: str, counter: str):
+    """[(kernel name, value KiB)] in dispatch order."""
+    rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+    acc = collections.OrderedDict()
+    for r in rows:
+        key = int(r["Dispatch_Id"])
+        name, v = acc.get(key, (r["Kernel_Name"], 0.0))
+        acc[key] = (name, v + float(r["Counter_Value"]))
+    return list(acc.values())
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--workload", required=True)
+    ap.add_argument("--fetch", required=True, help="counter_collection.csv of the FETCH_SIZE pass")
+    ap.add_argument("--write", required=True, help="counter_collection.csv of the WRITE_SIZE pass")
+    ap.add_argument("--calib-mib", type=int, required=True)
+    ap.add_argument("--command", default="", help="the profiled command, recorded verbatim")
+    args = ap.parse_args()
+
+    fetch = per_dispatch(args.fetch, "FETCH_SIZE")
+    write = per_dispatch(args.write, "WRITE_SIZE")
+    calib_kib = args.calib_mib * 1024.0
+
+    elem_f = [v for n, v in fetch if "elementwise" in n]
+    elem_w = [v for n, v in write if "elementwise" in n]
+    if len(elem_f) < 2 or len(elem_w) < 2:
+        raise SystemExit("calibration kernels not found (run bench.py with --calib-copy-mib)")
+    # the add reads N MiB (largest fetch); the fill and the add each write N MiB
+    f_factor = max(elem_f) / calib_kib
+    w_factor = sorted(elem_w)[-1] / calib_kib
+
+    out = {"workload": args.workload, "calib_mib": args.calib_mib,
+           "fetch_factor": round(f_factor, 4), "write_factor": round(w_factor, 4),
+           "command": args.command, "kernels": {}}
+    lines = [f"# HBM traffic per launch, workload {args.workload}",
+             f"command: {args.command}",
+             f"calibration: fetch factor {f_factor:.4f}, write factor {w_factor:.4f} "
+             f"(torch add / fill of {args.calib_mib} MiB)", "",
+             "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM read MB | HBM write MB | total MB |",
+             "|---|---|---|---|---|---|"]
+    for api, (sub, src) in KERNELS.items():
+        fv = [v for n, v in fetch if sub in n]
+        wv = [v for n, v in write if sub in n]
+        if not fv or not wv:
+            continue
+        fk, wk = sum(fv) / len(fv), sum(wv) / len(wv)
+        rd, wr = fk / f_factor * 1024, wk / w_factor * 1024
+        out["kernels"][api] = {"fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
+                               "hbm_read_bytes": round(rd), "hbm_write_bytes": round(wr),
+                               "hbm_bytes_per_launch": round(rd + wr),
+                               "launches": len(fv), "source_sha": source_sha(src)}
+        lines.append(f"| {api} | {fk:.0f} | {wk:.0f} | {rd / 1e6:.1f} | {wr / 1e6:.1f} | "
+                     f"{(rd + wr) / 1e6:.1f} |")
+    g = out["kernels"].get("svdq_gemm_w4a4")
+    if g:
+        out["source_sha"] = g["source_sha"]
+        out["hbm_bytes_per_launch"] = g["hbm_bytes_per_launch"]
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", f"traffic_{args.workload}.json"), "w") as f:
+        json.dump(out, f, indent=1)
+    print("\n".join(lines))
+
+
+if __name__ == "__main__":
+    main()

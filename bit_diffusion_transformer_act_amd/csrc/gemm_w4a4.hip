@@ -13,8 +13,8 @@
 // LDS-DMA loads (global_load_lds_dwordx4 / _dword): no register staging, and
 // the loads for step ks + STAGES - 1 are in flight while step ks computes.
 // One barrier per step. Code rows are 64 bytes with the four 16-byte chunks
-// XOR-swizzled by (row >> 1) & 3 so the ds_read_b128 of 32 consecutive rows
-// spread over the banks.
+// XOR-swizzled by (row >> 2) & 3, so 16 consecutive rows read at one chunk
+// index touch 16 distinct 16-byte bank slots.
 //
 // Blocks are remapped so that each of the 8 XCDs (round-robin dispatch)
 // works on a contiguous range of tiles in 8-M-tile groups, which keeps the A
@@ -73,13 +73,13 @@ __device__ __forceinline__ v4i unpack_i4x16(uint32_t w0, uint32_t w1) {
              (int)((w1 << 4) & 0xF0F0F0F0u), (int)(w1 & 0xF0F0F0F0u)};
 }
 
-__device__ __forceinline__ int swz(int row) { return (row >> 1) & 3; }
+__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
 
 // 0x4B400000 is 1.5 * 2^23 as fp32: integers added to it stay exact in the
 // mantissa while |x| < 2^22.
 constexpr int kMagicBits = 0x4B400000;
 #define SVDQ_M16 kMagicBits, kMagicBits, kMagicBits, kMagicBits
-__device__ constexpr v16i kMagic16 = {SVDQ_M16, SVDQ_M16, SVDQ_M16, SVDQ_M16};
+__device__ constexpr v4i kMagic4 = {SVDQ_M16};
 #undef SVDQ_M16
 
 template <int WM, int WN, int STAGES>
@@ -180,39 +180,76 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restr
   for (int s = 0; s < STAGES - 1; ++s)
     if (s < nk) issue(s);
 
-  // ---- low-rank up-projection initialises the accumulators
-  v16f acc[WM][WN];
+  // ---- low-rank up-projection initialises the accumulators. INT4 keeps 16 x 16
+  // blocks (acc4), FP4 32 x 32 blocks (acc); only one of the two is live.
+  constexpr int RB4 = (FMT == 0) ? 2 * WM : 1, CB4 = (FMT == 0) ? 2 * WN : 1;
+  constexpr int RB32 = (FMT == 0) ? 1 : WM, CB32 = (FMT == 0) ? 1 : WN;
+  v4f acc4[RB4][CB4];
+  v16f acc[RB32][CB32];
 #pragma unroll
-  for (int i = 0; i < WM; ++i)
+  for (int i = 0; i < RB4; ++i)
 #pragma unroll
-    for (int j = 0; j < WN; ++j)
+    for (int j = 0; j < CB4; ++j) acc4[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < RB32; ++i)
+#pragma unroll
+    for (int j = 0; j < CB32; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  for (int j0 = 0; j0 < r; j0 += 16) {
-    v8h a[WM], b[WN];
+  if constexpr (FMT == 0) {
+    // v_mfma_f32_16x16x16_f16: lane l supplies row l%16, ranks j0 + 4 (l/16) .. +4
+    const int l16 = lane & 15, lq = lane >> 4;
+    for (int j0 = 0; j0 < r; j0 += 16) {
+      v4h a[RB4], b[CB4];
 #pragma unroll
-    for (int rb = 0; rb < WM; ++rb) {
-      const int m = m0 + wm * 32 * WM + rb * 32 + l32;
-      if (m < M) {
-        const float4* p = reinterpret_cast<const float4*>(lora_act + (size_t)m * r + j0 + lh * 8);
-        const float4 u = p[0], w = p[1];
-        a[rb] = v8h{(_Float16)u.x, (_Float16)u.y, (_Float16)u.z, (_Float16)u.w,
-                    (_Float16)w.x, (_Float16)w.y, (_Float16)w.z, (_Float16)w.w};
-      } else {
-        a[rb] = v8h{0, 0, 0, 0, 0, 0, 0, 0};
+      for (int rb = 0; rb < RB4; ++rb) {
+        const int m = m0 + wm * 32 * WM + rb * 16 + l16;
+        if (m < M) {
+          const float4 u = *reinterpret_cast<const float4*>(lora_act + (size_t)m * r + j0 + lq * 4);
+          a[rb] = v4h{(_Float16)u.x, (_Float16)u.y, (_Float16)u.z, (_Float16)u.w};
+        } else {
+          a[rb] = v4h{0, 0, 0, 0};
+        }
       }
+#pragma unroll
+      for (int cb = 0; cb < CB4; ++cb) {
+        const int n = n0 + wn * 32 * WN + cb * 16 + l16;
+        b[cb] = __builtin_bit_cast(v4h, *reinterpret_cast<const uint2*>(lora_up + (size_t)n * r + j0 + lq * 4));
+      }
+#pragma unroll
+      for (int rb = 0; rb < RB4; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < CB4; ++cb)
+          acc4[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x16f16(a[rb], b[cb], acc4[rb][cb], 0, 0, 0);
     }
+  } else {
+    // v_mfma_f32_32x32x16_f16: lane l supplies row l%32, ranks j0 + 8 (l/32) .. +8
+    for (int j0 = 0; j0 < r; j0 += 16) {
+      v8h a[RB32], b[CB32];
 #pragma unroll
-    for (int cb = 0; cb < WN; ++cb) {
-      const int n = n0 + wn * 32 * WN + cb * 32 + l32;
-      b[cb] = __builtin_bit_cast(v8h, *reinterpret_cast<const uint4*>(lora_up + (size_t)n * r + j0 + lh * 8));
+      for (int rb = 0; rb < RB32; ++rb) {
+        const int m = m0 + wm * 32 * WM + rb * 32 + l32;
+        if (m < M) {
+          const float4* p = reinterpret_cast<const float4*>(lora_act + (size_t)m * r + j0 + lh * 8);
+          const float4 u = p[0], w = p[1];
+          a[rb] = v8h{(_Float16)u.x, (_Float16)u.y, (_Float16)u.z, (_Float16)u.w,
+                      (_Float16)w.x, (_Float16)w.y, (_Float16)w.z, (_Float16)w.w};
+        } else {
+          a[rb] = v8h{0, 0, 0, 0, 0, 0, 0, 0};
+        }
+      }
+#pragma unroll
+      for (int cb = 0; cb < CB32; ++cb) {
+        const int n = n0 + wn * 32 * WN + cb * 32 + l32;
+        b[cb] = __builtin_bit_cast(v8h, *reinterpret_cast<const uint4*>(lora_up + (size_t)n * r + j0 + lh * 8));
+      }
+#pragma unroll
+      for (int rb = 0; rb < RB32; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < CB32; ++cb)
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[rb], b[cb], acc[rb][cb], 0, 0, 0);
     }
-#pragma unroll
-    for (int rb = 0; rb < WM; ++rb)
-#pragma unroll
-      for (int cb = 0; cb < WN; ++cb)
-        acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[rb], b[cb], acc[rb][cb], 0, 0, 0);
   }
 
   // LDS read offsets (within a stage) of this lane's operand rows
@@ -234,66 +271,56 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restr
     const uint32_t* sS = reinterpret_cast<const uint32_t*>(st + S::A_BYTES + S::B_BYTES);
 
     if constexpr (FMT == 0) {
-      // scale words of this step: 2 fp16 per row (groups 2 ks, 2 ks + 1)
-      // lane rows in block rb: (v/4)*8 + lh*4 + v%4 -> four 16-byte reads
-      uint4 sxw[WM][4];
+      // INT4 on v_mfma_i32_16x16x64_i8: the wave tile is (2 WM) x (2 WN) blocks
+      // of 16 x 16, one MFMA per block and 64-group. Lane l supplies row l%16
+      // and 16 codes (8 packed bytes at 8 (l/16) within the group's 32 bytes);
+      // its results are rows 4 (l/16) + i, column l%16 of the block.
+      constexpr int RB = 2 * WM, CB = 2 * WN;
+      const int l16 = lane & 15, lq = lane >> 4;
+      // scale words: 2 fp16 per row (groups 2 ks, 2 ks + 1); 4 rows per 16-byte read
+      uint4 sxw[RB];
 #pragma unroll
-      for (int rb = 0; rb < WM; ++rb)
+      for (int rb = 0; rb < RB; ++rb)
+        sxw[rb] = *reinterpret_cast<const uint4*>(sS + wm * 32 * WM + rb * 16 + lq * 4);
+      uint32_t sww[CB];
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          sxw[rb][q] = *reinterpret_cast<const uint4*>(sS + wm * 32 * WM + rb * 32 + q * 8 + lh * 4);
-      // sw' = s_w 2^-8 (the 16 x 16 nibble shift) and -1.5*2^23 sw' (exact:
-      // s_w has 11 significant bits, 3 s_w at most 13)
-      float swp[WN][2], swm[WN][2];
-#pragma unroll
-      for (int cb = 0; cb < WN; ++cb) {
-        const __half2 h = __builtin_bit_cast(__half2, sS[BM + brow[cb]]);
-        swp[cb][0] = __low2float(h) * 0.00390625f;
-        swp[cb][1] = __high2float(h) * 0.00390625f;
-        swm[cb][0] = swp[cb][0] * -12582912.0f;
-        swm[cb][1] = swp[cb][1] * -12582912.0f;
-      }
+      for (int cb = 0; cb < CB; ++cb) sww[cb] = sS[BM + wn * 32 * WN + cb * 16 + l16];
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
-        v4i a0[WM], a1[WM], b0[WN], b1[WN];
+        v4i av[RB], bv[CB];
 #pragma unroll
-        for (int rb = 0; rb < WM; ++rb) {
-          const int rr = arow[rb];
-          const uint4 ap = *reinterpret_cast<const uint4*>(sA + rr * 64 + (((g * 2 + lh) ^ swz(rr)) << 4));
-          a0[rb] = unpack_i4x16(ap.x, ap.y);
-          a1[rb] = unpack_i4x16(ap.z, ap.w);
+        for (int rb = 0; rb < RB; ++rb) {
+          const int rr = wm * 32 * WM + rb * 16 + l16;
+          const uint2 ap = *reinterpret_cast<const uint2*>(
+              sA + rr * 64 + (((g * 2 + (lq >> 1)) ^ swz(rr)) << 4) + (lq & 1) * 8);
+          av[rb] = unpack_i4x16(ap.x, ap.y);
         }
 #pragma unroll
-        for (int cb = 0; cb < WN; ++cb) {
-          const int rr = brow[cb];
-          const uint4 bp = *reinterpret_cast<const uint4*>(sB + rr * 64 + (((g * 2 + lh) ^ swz(rr)) << 4));
-          b0[cb] = unpack_i4x16(bp.x, bp.y);
-          b1[cb] = unpack_i4x16(bp.z, bp.w);
+        for (int cb = 0; cb < CB; ++cb) {
+          const int rr = wn * 32 * WN + cb * 16 + l16;
+          const uint2 bp = *reinterpret_cast<const uint2*>(
+              sB + rr * 64 + (((g * 2 + (lq >> 1)) ^ swz(rr)) << 4) + (lq & 1) * 8);
+          bv[cb] = unpack_i4x16(bp.x, bp.y);
         }
 #pragma unroll
-        for (int rb = 0; rb < WM; ++rb) {
-          _Float16 sx[16];
+        for (int cb = 0; cb < CB; ++cb) {
+          // sw' = s_w 2^-8 (the 16 x 16 nibble shift) and -1.5*2^23 sw' (exact:
+          // s_w has 11 significant bits, 3 s_w at most 13)
+          const v2h hw = __builtin_bit_cast(v2h, sww[cb]);
+          const float swp = (float)hw[g] * 0.00390625f;
+          const float swm = swp * -12582912.0f;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint32_t wv[4] = {sxw[rb][q].x, sxw[rb][q].y, sxw[rb][q].z, sxw[rb][q].w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const v2h h = __builtin_bit_cast(v2h, wv[e]);
-              sx[4 * q + e] = h[g];
-            }
-          }
-#pragma unroll
-          for (int cb = 0; cb < WN; ++cb) {
+          for (int rb = 0; rb < RB; ++rb) {
             // int32 accumulation starts at the bit pattern of 1.5 * 2^23, so the
             // result read as fp32 is exactly 1.5 * 2^23 + 256 P (|256 P| < 2^22)
-            v16i p = kMagic16;
-            p = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0[rb], b0[cb], p, 0, 0, 0);
-            p = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1[rb], b1[cb], p, 0, 0, 0);
+            const v4i p = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[rb], bv[cb], kMagic4, 0, 0, 0);
+            const uint32_t wx[4] = {sxw[rb].x, sxw[rb].y, sxw[rb].z, sxw[rb].w};
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              // t = fl(P s_w): one rounding of the exact (1.5*2^23 + 256 P) sw' - 1.5*2^23 sw'
-              const float t = fmaf(__int_as_float(p[v]), swp[cb][g], swm[cb][g]);
-              acc[rb][cb][v] = fmaf(t, (float)sx[v], acc[rb][cb][v]);
+            for (int i = 0; i < 4; ++i) {
+              // t = fl(P s_w): one rounding of (1.5*2^23 + 256 P) sw' - 1.5*2^23 sw'
+              const float t = fmaf(__int_as_float(p[i]), swp, swm);
+              const v2h hx = __builtin_bit_cast(v2h, wx[i]);
+              acc4[rb][cb][i] = fmaf(t, (float)hx[g], acc4[rb][cb][i]);
             }
           }
         }
@@ -332,21 +359,40 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restr
   }
 
   // ---- epilogue: bias, activation, fp16 store
+  if constexpr (FMT == 0) {
+    const int l16 = lane & 15, lq = lane >> 4;
 #pragma unroll
-  for (int cb = 0; cb < WN; ++cb) {
-    const int n = n0 + brow[cb];
-    const float bn = bias ? __half2float(bias[n]) : 0.f;
+    for (int cb = 0; cb < CB4; ++cb) {
+      const int n = n0 + wn * 32 * WN + cb * 16 + l16;
+      const float bn = bias ? __half2float(bias[n]) : 0.f;
 #pragma unroll
-    for (int rb = 0; rb < WM; ++rb) {
+      for (int rb = 0; rb < RB4; ++rb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int m = m0 + wm * 32 * WM + rb * 32 + (v >> 2) * 8 + lh * 4 + (v & 3);
-        if (m < M) {
-          float yv = acc[rb][cb][v] + bn;
-          if (EPI == 1) yv = gelu_tanh_f32(yv);
-          Y[(size_t)m * N + n] = __float2half_rn(yv);
+        for (int i = 0; i < 4; ++i) {
+          const int m = m0 + wm * 32 * WM + rb * 16 + lq * 4 + i;
+          if (m < M) {
+            float yv = acc4[rb][cb][i] + bn;
+            if (EPI == 1) yv = gelu_tanh_f32(yv);
+            Y[(size_t)m * N + n] = __float2half_rn(yv);
+          }
         }
-      }
+    }
+  } else {
+#pragma unroll
+    for (int cb = 0; cb < CB32; ++cb) {
+      const int n = n0 + brow[cb];
+      const float bn = bias ? __half2float(bias[n]) : 0.f;
+#pragma unroll
+      for (int rb = 0; rb < RB32; ++rb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int m = m0 + wm * 32 * WM + rb * 32 + (v >> 2) * 8 + lh * 4 + (v & 3);
+          if (m < M) {
+            float yv = acc[rb][cb][v] + bn;
+            if (EPI == 1) yv = gelu_tanh_f32(yv);
+            Y[(size_t)m * N + n] = __float2half_rn(yv);
+          }
+        }
     }
   }
 }
@@ -378,7 +424,7 @@ hipError_t launch_gemm_w4a4(int fmt, int M, int N, int K, int r, const uint8_t* 
 #define SVDQ_GO(F, E, WM_, WN_, ST_) \
   return launch_cfg<F, E, WM_, WN_, ST_>(M, N, K, r, ac, as, la, wc, ws, lu, bias, Y, st)
   if (fmt == 0) {
-    if (epi == 0) SVDQ_GO(0, 0, 2, 2, 4); else SVDQ_GO(0, 1, 2, 2, 4);
+    if (epi == 0) SVDQ_GO(0, 0, 2, 2, 3); else SVDQ_GO(0, 1, 2, 2, 3);
   } else {
     if (epi == 0) SVDQ_GO(1, 0, 2, 2, 4); else SVDQ_GO(1, 1, 2, 2, 4);
   }
