@@ -59,8 +59,8 @@ def parse():
 def layer_bytes(cfg, r):
     M, K, N = cfg.M, cfg.K, cfg.N
     sbytes = (K // 64) * 2 if cfg.fmt == "int4_g64" else K // 32
-    q = M * K * 2 + K * 4 + r * K * 2 + M * K // 2 + M * sbytes + M * r * 4
-    g = (M * K // 2 + M * sbytes + M * r * 4 + N * K // 2 + N * sbytes + N * r * 2 + N * 2
+    q = M * K * 2 + K * 4 + r * K * 2 + M * K // 2 + M * sbytes + M * r * 2
+    g = (M * K // 2 + M * sbytes + M * r * 2 + N * K // 2 + N * sbytes + N * r * 2 + N * 2
          + M * N * 2)
     return q, g
 
@@ -144,7 +144,7 @@ def main():
             scols = cfg.K // 64 if cfg.fmt == "int4_g64" else cfg.K // 32
             L["codes"] = torch.empty((cfg.M, cfg.K // 2), dtype=torch.uint8, device=dev)
             L["scales"] = torch.empty((cfg.M, scols), dtype=sdt, device=dev)
-            L["lora_act"] = torch.empty((cfg.M, r), dtype=torch.float32, device=dev) if r else None
+            L["lora_act"] = torch.empty((cfg.M, r), dtype=torch.float16, device=dev) if r else None
             L["Y"] = torch.empty((cfg.M, cfg.N), dtype=torch.float16, device=dev)
             layers.append(L)
         G = {"x": t(gp["x"]), "codes": t(gp["codes"]), "scales": t(gp["scales"]),

@@ -20,15 +20,17 @@ LIB_NAME = "libsvdq_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["api.hip", "quantize_act.hip", "gemm_w4a4.hip", "awq_gemv.hip"]
+# MFMA results stay in VGPRs where VALU post-processes every partial (the INT4
+# group scaling would otherwise pay one AGPR copy per element); the FP4 large
+# tile keeps its 256 accumulators per lane in AGPRs, so it is built without.
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+SOURCES = {"api.hip": [], "quantize_act.hip": VGPR_FORM, "gemm_w4a4.hip": VGPR_FORM,
+           "gemm_fp4.hip": [], "awq_gemv.hip": VGPR_FORM}
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result",
-    # MFMA results stay in VGPRs: the INT4 path converts every group partial
-    # with VALU ops, and AGPR copies would add one VALU op per element.
-    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 
@@ -41,7 +43,8 @@ def hipcc() -> str:
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *HIPCC_FLAGS, *SOURCES[src], "-I", INCLUDE, "-I", CSRC, "-c",
+           os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -54,7 +57,7 @@ def build(verbose: bool = False) -> str:
     """Compile every HIP source for gfx950 and link the shared library."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+        objs = list(ex.map(lambda s: _compile(s, verbose), list(SOURCES)))
     tmp = LIB_PATH + ".tmp"
     cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:

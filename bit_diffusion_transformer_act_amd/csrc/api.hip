@@ -81,7 +81,7 @@ const char* svdq_status_str(int status) {
 int svdq_device_check(int hip_device) { return check_device(hip_device); }
 
 int svdq_quantize_act(int fmt, int M, int K, int r, const void* X, const float* smooth_inv,
-                      const void* lora_down, uint8_t* act_codes, void* act_scales, float* lora_act,
+                      const void* lora_down, uint8_t* act_codes, void* act_scales, void* lora_act,
                       void* stream) {
   if (fmt != SVDQ_INT4_G64 && fmt != SVDQ_FP4_E2M1_B32) return SVDQ_ERR_INVALID_ARG;
   if (M < 0 || !k_ok(K) || !rank_ok(r)) return SVDQ_ERR_SHAPE;
@@ -99,7 +99,7 @@ int svdq_quantize_act(int fmt, int M, int K, int r, const void* X, const float* 
 }
 
 int svdq_gemm_w4a4(int fmt, int M, int N, int K, int r, const uint8_t* act_codes,
-                   const void* act_scales, const float* lora_act, const uint8_t* w_codes,
+                   const void* act_scales, const void* lora_act, const uint8_t* w_codes,
                    const void* w_scales, const void* lora_up, const void* bias, int epi, void* Y,
                    void* stream) {
   if (fmt != SVDQ_INT4_G64 && fmt != SVDQ_FP4_E2M1_B32) return SVDQ_ERR_INVALID_ARG;

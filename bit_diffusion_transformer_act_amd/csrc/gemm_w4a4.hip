@@ -20,8 +20,8 @@
 // works on a contiguous range of tiles in 8-M-tile groups, which keeps the A
 // and B rows of concurrently running tiles in that XCD's L2.
 //
-// Accumulators start from the low-rank product: lora_act (fp32 -> fp16) times
-// lora_up on v_mfma_f32_32x32x16_f16, 16 ranks per instruction.
+// Accumulators start from the low-rank product: lora_act (fp16) times lora_up
+// on fp16 MFMAs (16 ranks per instruction), loads for 32 ranks in one batch.
 //
 // INT4_G64: each lane reads 16 packed bytes (32 codes) per 32-row block and
 // group; nibbles become int8 bytes holding 16 q with two ALU ops per word
@@ -41,30 +41,10 @@
 #include <atomic>
 
 #include "common.hpp"
+#include "launch.hpp"
+#include "pipeline.hpp"
 
 namespace svdq {
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-// LDS-DMA loads: lane l's bytes land at lds_base + l * size. The LDS base is
-// wave-uniform (M0); the instruction has no destination register. Completion
-// is tracked with vmcnt by the caller (waitvm) before the barrier that
-// publishes the data.
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_base)
-               : "memory", "m0");
-}
-__device__ __forceinline__ void dma4(const void* g, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds_base)
-               : "memory", "m0");
-}
-template <int N>
-__device__ __forceinline__ void waitvm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
-}
 
 // 16 packed INT4 codes (two words) -> one int8 MFMA operand of 16 bytes:
 // [even codes of w0, odd codes of w0, even of w1, odd of w1], each byte 16 q.
@@ -73,7 +53,6 @@ __device__ __forceinline__ v4i unpack_i4x16(uint32_t w0, uint32_t w1) {
              (int)((w1 << 4) & 0xF0F0F0F0u), (int)(w1 & 0xF0F0F0F0u)};
 }
 
-__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
 
 // 0x4B400000 is 1.5 * 2^23 as fp32: integers added to it stay exact in the
 // mantissa while |x| < 2^22.
@@ -93,10 +72,12 @@ struct GemmShape {
   static constexpr int DMA_PER_STEP = BM / 64 + BN / 64 + SC_INSTR;  // per thread
 };
 
+// 3 waves per SIMD (at most 168 VGPRs): the INT4 inner loop is VALU-bound and
+// needs the extra wave to cover LDS and MFMA latencies.
 template <int FMT, int EPI, int WM, int WN, int STAGES>
-__global__ __launch_bounds__(256)
+__global__ __launch_bounds__(256, 3)
 void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restrict__ act_scales,
-                      const float* __restrict__ lora_act, const uint8_t* __restrict__ w_codes,
+                      const __half* __restrict__ lora_act, const uint8_t* __restrict__ w_codes,
                       const void* __restrict__ w_scales, const __half* __restrict__ lora_up,
                       const __half* __restrict__ bias, __half* __restrict__ Y,
                       int M, int N, int K, int r) {
@@ -198,57 +179,63 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restr
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
   if constexpr (FMT == 0) {
-    // v_mfma_f32_16x16x16_f16: lane l supplies row l%16, ranks j0 + 4 (l/16) .. +4
+    // v_mfma_f32_16x16x16_f16: lane l supplies row l%16, ranks j0 + 4 (l/16) .. +4.
+    // Loads for 16 ranks go out together (more would raise the register peak).
     const int l16 = lane & 15, lq = lane >> 4;
     for (int j0 = 0; j0 < r; j0 += 16) {
-      v4h a[RB4], b[CB4];
+      uint2 ua[RB4], ub[CB4];
+      {
 #pragma unroll
-      for (int rb = 0; rb < RB4; ++rb) {
-        const int m = m0 + wm * 32 * WM + rb * 16 + l16;
-        if (m < M) {
-          const float4 u = *reinterpret_cast<const float4*>(lora_act + (size_t)m * r + j0 + lq * 4);
-          a[rb] = v4h{(_Float16)u.x, (_Float16)u.y, (_Float16)u.z, (_Float16)u.w};
-        } else {
-          a[rb] = v4h{0, 0, 0, 0};
+        for (int rb = 0; rb < RB4; ++rb) {
+          const int m = m0 + wm * 32 * WM + rb * 16 + l16;
+          ua[rb] = (m < M) ? *reinterpret_cast<const uint2*>(lora_act + (size_t)m * r + j0 + lq * 4)
+                           : make_uint2(0, 0);
         }
-      }
 #pragma unroll
-      for (int cb = 0; cb < CB4; ++cb) {
-        const int n = n0 + wn * 32 * WN + cb * 16 + l16;
-        b[cb] = __builtin_bit_cast(v4h, *reinterpret_cast<const uint2*>(lora_up + (size_t)n * r + j0 + lq * 4));
+        for (int cb = 0; cb < CB4; ++cb) {
+          const int n = n0 + wn * 32 * WN + cb * 16 + l16;
+          ub[cb] = *reinterpret_cast<const uint2*>(lora_up + (size_t)n * r + j0 + lq * 4);
+        }
       }
 #pragma unroll
       for (int rb = 0; rb < RB4; ++rb)
 #pragma unroll
         for (int cb = 0; cb < CB4; ++cb)
-          acc4[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x16f16(a[rb], b[cb], acc4[rb][cb], 0, 0, 0);
+          acc4[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(v4h, ua[rb]),
+                                                               __builtin_bit_cast(v4h, ub[cb]),
+                                                               acc4[rb][cb], 0, 0, 0);
     }
   } else {
-    // v_mfma_f32_32x32x16_f16: lane l supplies row l%32, ranks j0 + 8 (l/32) .. +8
-    for (int j0 = 0; j0 < r; j0 += 16) {
-      v8h a[RB32], b[CB32];
+    // v_mfma_f32_32x32x16_f16: lane l supplies row l%32, ranks j0 + 8 (l/32) .. +8.
+    // Loads for 32 ranks are issued together so a tile pays one round trip.
+    for (int j0 = 0; j0 < r; j0 += 32) {
+      const int nj = min(r - j0, 32) >> 4;
+      uint4 ua[RB32][2], ub[CB32][2];
 #pragma unroll
-      for (int rb = 0; rb < RB32; ++rb) {
-        const int m = m0 + wm * 32 * WM + rb * 32 + l32;
-        if (m < M) {
-          const float4* p = reinterpret_cast<const float4*>(lora_act + (size_t)m * r + j0 + lh * 8);
-          const float4 u = p[0], w = p[1];
-          a[rb] = v8h{(_Float16)u.x, (_Float16)u.y, (_Float16)u.z, (_Float16)u.w,
-                      (_Float16)w.x, (_Float16)w.y, (_Float16)w.z, (_Float16)w.w};
-        } else {
-          a[rb] = v8h{0, 0, 0, 0, 0, 0, 0, 0};
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int rb = 0; rb < RB32; ++rb) {
+          const int m = m0 + wm * 32 * WM + rb * 32 + l32;
+          ua[rb][h] = (m < M && h < nj)
+                          ? *reinterpret_cast<const uint4*>(lora_act + (size_t)m * r + j0 + 16 * h + lh * 8)
+                          : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int cb = 0; cb < CB32; ++cb) {
+          const int n = n0 + wn * 32 * WN + cb * 32 + l32;
+          ub[cb][h] = (h < nj) ? *reinterpret_cast<const uint4*>(lora_up + (size_t)n * r + j0 + 16 * h + lh * 8)
+                               : make_uint4(0, 0, 0, 0);
         }
       }
 #pragma unroll
-      for (int cb = 0; cb < CB32; ++cb) {
-        const int n = n0 + wn * 32 * WN + cb * 32 + l32;
-        b[cb] = __builtin_bit_cast(v8h, *reinterpret_cast<const uint4*>(lora_up + (size_t)n * r + j0 + lh * 8));
-      }
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int rb = 0; rb < RB32; ++rb)
+        for (int rb = 0; rb < RB32; ++rb)
 #pragma unroll
-        for (int cb = 0; cb < CB32; ++cb)
-          acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[rb], b[cb], acc[rb][cb], 0, 0, 0);
+          for (int cb = 0; cb < CB32; ++cb)
+            acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, ua[rb][h]),
+                                                                 __builtin_bit_cast(v8h, ub[cb][h]),
+                                                                 acc[rb][cb], 0, 0, 0);
     }
   }
 
@@ -358,48 +345,54 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restr
     }
   }
 
-  // ---- epilogue: bias, activation, fp16 store
+  // ---- epilogue: bias and activation, then the tile goes through LDS (the ring
+  // is free now) so that Y is written as whole rows with 16-byte stores.
+  constexpr int TP = BN + 8;   // padded row (halves) of the staging tile
+  static_assert(BM * TP * 2 <= S::LDS, "staging tile must fit in the ring");
+  __syncthreads();
+  __half* tile = reinterpret_cast<__half*>(smem);
   if constexpr (FMT == 0) {
     const int l16 = lane & 15, lq = lane >> 4;
 #pragma unroll
     for (int cb = 0; cb < CB4; ++cb) {
-      const int n = n0 + wn * 32 * WN + cb * 16 + l16;
-      const float bn = bias ? __half2float(bias[n]) : 0.f;
+      const int nl = wn * 32 * WN + cb * 16 + l16;
+      const float bn = bias ? __half2float(bias[n0 + nl]) : 0.f;
 #pragma unroll
       for (int rb = 0; rb < RB4; ++rb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int m = m0 + wm * 32 * WM + rb * 16 + lq * 4 + i;
-          if (m < M) {
-            float yv = acc4[rb][cb][i] + bn;
-            if (EPI == 1) yv = gelu_tanh_f32(yv);
-            Y[(size_t)m * N + n] = __float2half_rn(yv);
-          }
+          float yv = acc4[rb][cb][i] + bn;
+          if (EPI == 1) yv = gelu_tanh_f32(yv);
+          tile[(wm * 32 * WM + rb * 16 + lq * 4 + i) * TP + nl] = __float2half_rn(yv);
         }
     }
   } else {
 #pragma unroll
     for (int cb = 0; cb < CB32; ++cb) {
-      const int n = n0 + brow[cb];
-      const float bn = bias ? __half2float(bias[n]) : 0.f;
+      const int nl = brow[cb];
+      const float bn = bias ? __half2float(bias[n0 + nl]) : 0.f;
 #pragma unroll
       for (int rb = 0; rb < RB32; ++rb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int m = m0 + wm * 32 * WM + rb * 32 + (v >> 2) * 8 + lh * 4 + (v & 3);
-          if (m < M) {
-            float yv = acc[rb][cb][v] + bn;
-            if (EPI == 1) yv = gelu_tanh_f32(yv);
-            Y[(size_t)m * N + n] = __float2half_rn(yv);
-          }
+          float yv = acc[rb][cb][v] + bn;
+          if (EPI == 1) yv = gelu_tanh_f32(yv);
+          tile[(wm * 32 * WM + rb * 32 + (v >> 2) * 8 + lh * 4 + (v & 3)) * TP + nl] = __float2half_rn(yv);
         }
     }
+  }
+  __syncthreads();
+  for (int c = tid; c < BM * (BN / 8); c += 256) {
+    const int row = c / (BN / 8), c8 = c - row * (BN / 8);
+    if (m0 + row < M)
+      *reinterpret_cast<uint4*>(Y + (size_t)(m0 + row) * N + n0 + c8 * 8) =
+          *reinterpret_cast<const uint4*>(tile + row * TP + c8 * 8);
   }
 }
 
 template <int FMT, int EPI, int WM, int WN, int STAGES>
 static hipError_t launch_cfg(int M, int N, int K, int r, const uint8_t* ac, const void* as,
-                             const float* la, const uint8_t* wc, const void* ws, const void* lu,
+                             const void* la, const uint8_t* wc, const void* ws, const void* lu,
                              const void* bias, void* Y, hipStream_t st) {
   using S = GemmShape<WM, WN, STAGES>;
   auto kern = gemm_w4a4_kernel<FMT, EPI, WM, WN, STAGES>;
@@ -413,19 +406,21 @@ static hipError_t launch_cfg(int M, int N, int K, int r, const uint8_t* ac, cons
     }
   }
   const int ntiles = ((M + S::BM - 1) / S::BM) * (N / S::BN);
-  hipLaunchKernelGGL(kern, dim3(ntiles), dim3(256), S::LDS, st, ac, as, la, wc, ws,
+  hipLaunchKernelGGL(kern, dim3(ntiles), dim3(256), S::LDS, st, ac, as, (const __half*)la, wc, ws,
                      (const __half*)lu, (const __half*)bias, (__half*)Y, M, N, K, r);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_w4a4(int fmt, int M, int N, int K, int r, const uint8_t* ac, const void* as,
-                            const float* la, const uint8_t* wc, const void* ws, const void* lu,
+                            const void* la, const uint8_t* wc, const void* ws, const void* lu,
                             const void* bias, int epi, void* Y, hipStream_t st) {
 #define SVDQ_GO(F, E, WM_, WN_, ST_) \
   return launch_cfg<F, E, WM_, WN_, ST_>(M, N, K, r, ac, as, la, wc, ws, lu, bias, Y, st)
   if (fmt == 0) {
     if (epi == 0) SVDQ_GO(0, 0, 2, 2, 3); else SVDQ_GO(0, 1, 2, 2, 3);
   } else {
+    const hipError_t e = launch_gemm_fp4_big(M, N, K, r, ac, as, la, wc, ws, lu, bias, epi, Y, st);
+    if (e != hipErrorNotSupported) return e;
     if (epi == 0) SVDQ_GO(1, 0, 2, 2, 4); else SVDQ_GO(1, 1, 2, 2, 4);
   }
 #undef SVDQ_GO

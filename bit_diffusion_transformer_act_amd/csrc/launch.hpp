@@ -7,13 +7,18 @@
 namespace svdq {
 
 hipError_t launch_quantize_act(int fmt, int M, int K, int r, const void* X, const float* smooth_inv,
-                               const void* lora_down, uint8_t* codes, void* scales, float* lora_act,
+                               const void* lora_down, uint8_t* codes, void* scales, void* lora_act,
                                hipStream_t stream);
 
 hipError_t launch_gemm_w4a4(int fmt, int M, int N, int K, int r, const uint8_t* act_codes,
-                            const void* act_scales, const float* lora_act, const uint8_t* w_codes,
+                            const void* act_scales, const void* lora_act, const uint8_t* w_codes,
                             const void* w_scales, const void* lora_up, const void* bias, int epi,
                             void* Y, hipStream_t stream);
+
+hipError_t launch_gemm_fp4_big(int M, int N, int K, int r, const uint8_t* act_codes,
+                               const void* act_scales, const void* lora_act, const uint8_t* w_codes,
+                               const void* w_scales, const void* lora_up, const void* bias, int epi,
+                               void* Y, hipStream_t stream);
 
 hipError_t launch_awq_gemv(int M, int N, int K, const void* x, const uint8_t* codes,
                            const void* scales, const void* zeros, void* y, hipStream_t stream);

@@ -20,7 +20,7 @@
 //     of an FP4 block (lanes l, l^16), whose amax is a two-/one-step xor
 //     shuffle reduction.
 // Partial low-rank sums of the 16 waves meet in LDS and are added in a fixed
-// order, so lora_act is deterministic.
+// order, so lora_act (stored as fp16) is deterministic.
 #include <atomic>
 
 #include "common.hpp"
@@ -31,7 +31,7 @@ template <int FMT, int NCB>
 __global__ __launch_bounds__(1024)
 void quantize_act_kernel(const __half* __restrict__ X, const float* __restrict__ smooth_inv,
                          const __half* __restrict__ lora_down, uint8_t* __restrict__ codes,
-                         void* __restrict__ scales, float* __restrict__ lora_act,
+                         void* __restrict__ scales, __half* __restrict__ lora_act,
                          int M, int K) {
 #pragma clang fp contract(off)
   extern __shared__ float red[];  // [16 waves][16 rows][16 * NCB]
@@ -186,14 +186,14 @@ void quantize_act_kernel(const __half* __restrict__ X, const float* __restrict__
       float sum = 0.f;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) sum += red[(w * 16 + rr) * R + cc];
-      if (m0 + rr < M) lora_act[(size_t)(m0 + rr) * R + cc] = sum;
+      if (m0 + rr < M) lora_act[(size_t)(m0 + rr) * R + cc] = __float2half_rn(sum);
     }
   }
 }
 
 template <int FMT, int NCB>
 static hipError_t launch_q(int M, int K, const void* X, const float* si, const void* ld,
-                           uint8_t* codes, void* scales, float* la, hipStream_t st) {
+                           uint8_t* codes, void* scales, void* la, hipStream_t st) {
   const dim3 grid((M + 15) / 16), block(1024);
   const size_t lds = NCB > 0 ? (size_t)16 * 16 * 16 * NCB * sizeof(float) : 0;
   if (lds > 65536) {
@@ -207,13 +207,13 @@ static hipError_t launch_q(int M, int K, const void* X, const float* si, const v
     }
   }
   hipLaunchKernelGGL((quantize_act_kernel<FMT, NCB>), grid, block, lds, st,
-                     (const __half*)X, si, (const __half*)ld, codes, scales, la, M, K);
+                     (const __half*)X, si, (const __half*)ld, codes, scales, (__half*)la, M, K);
   return hipGetLastError();
 }
 
 template <int FMT>
 static hipError_t launch_q_r(int M, int K, int r, const void* X, const float* si, const void* ld,
-                             uint8_t* codes, void* scales, float* la, hipStream_t st) {
+                             uint8_t* codes, void* scales, void* la, hipStream_t st) {
   switch (r / 16) {
     case 0: return launch_q<FMT, 0>(M, K, X, si, ld, codes, scales, la, st);
     case 1: return launch_q<FMT, 1>(M, K, X, si, ld, codes, scales, la, st);
@@ -228,7 +228,7 @@ static hipError_t launch_q_r(int M, int K, int r, const void* X, const float* si
 }
 
 hipError_t launch_quantize_act(int fmt, int M, int K, int r, const void* X, const float* si,
-                               const void* ld, uint8_t* codes, void* scales, float* la,
+                               const void* ld, uint8_t* codes, void* scales, void* la,
                                hipStream_t st) {
   if (fmt == 0) return launch_q_r<0>(M, K, r, X, si, ld, codes, scales, la, st);
   return launch_q_r<1>(M, K, r, X, si, ld, codes, scales, la, st);

@@ -123,7 +123,7 @@ def svdq_quantize_act(X: torch.Tensor, smooth_inv: torch.Tensor, lora_down, fmt=
 
     X fp16 [M][K]; smooth_inv fp32 [K]; lora_down fp16 [r][K] or None.
     Returns (act_codes u8 [M][K/2], act_scales fp16 [M][K/64] | u8 [M][K/32],
-    lora_act fp32 [M][r] or None). Output tensors may be passed in.
+    lora_act fp16 [M][r] or None). Output tensors may be passed in.
     """
     f = _fmt(fmt)
     dev = X.device
@@ -141,11 +141,11 @@ def svdq_quantize_act(X: torch.Tensor, smooth_inv: torch.Tensor, lora_down, fmt=
     if act_scales is None:
         act_scales = torch.empty(sshape, dtype=sdt, device=dev)
     if r > 0 and lora_act is None:
-        lora_act = torch.empty((M, r), dtype=torch.float32, device=dev)
+        lora_act = torch.empty((M, r), dtype=torch.float16, device=dev)
     _check(act_codes, "act_codes", torch.uint8, (M, K // 2), dev)
     _check(act_scales, "act_scales", sdt, sshape, dev)
     if r > 0:
-        _check(lora_act, "lora_act", torch.float32, (M, r), dev)
+        _check(lora_act, "lora_act", torch.float16, (M, r), dev)
     with torch.cuda.device(dev):
         st = lib().svdq_quantize_act(f, M, K, r, _ptr(X), _ptr(smooth_inv), _ptr(lora_down),
                                      _ptr(act_codes), _ptr(act_scales),
@@ -174,7 +174,7 @@ def svdq_gemm_w4a4(act_codes, act_scales, lora_act, w_codes, w_scales, lora_up, 
     _check(w_codes, "w_codes", torch.uint8, (N, KB), dev)
     _check(w_scales, "w_scales", sdt, sw_shape, dev)
     if r > 0:
-        _check(lora_act, "lora_act", torch.float32, (M, r), dev)
+        _check(lora_act, "lora_act", torch.float16, (M, r), dev)
         _check(lora_up, "lora_up", torch.float16, (N, r), dev)
     if bias is not None:
         _check(bias, "bias", torch.float16, (N,), dev)

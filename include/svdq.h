@@ -89,7 +89,7 @@ int svdq_version(void);
  * and per-group 4-bit activation quantization (one pass over X).
  *
  *   x_hat[m,k]   = fl32(fp32(X[m,k]) * smooth_inv[k])          (IEEE multiply)
- *   lora_act[m,j]= sum_k X[m,k] * lora_down[j,k]   (fp16 inputs, fp32 accumulate)
+ *   lora_act[m,j]= fp16_rne(sum_k X[m,k] * lora_down[j,k])   (fp16 inputs, fp32 accumulate)
  *   INT4_G64, per row m and group g of 64 along K:
  *     amax = max |x_hat|;  s = fp16_rne(min(fl32(amax / 7), 65504));
  *     q = s == 0 ? 0 : clamp(rint_even(fl32(x_hat / s)), -7, 7)   (IEEE division)
@@ -99,7 +99,8 @@ int svdq_version(void);
  *     code = E2M1 nearest to x_hat / 2^e (ties to even mantissa), sign bit
  *     from x_hat's sign.
  * Codes and scales are bit-exact functions of (X, smooth_inv); lora_act is a
- * float result (summation order unspecified).
+ * float result (fp32 accumulation in unspecified order, stored as fp16 -- the
+ * 16-bit low-rank branch -- which is what the GEMM's fp16 matrix product takes).
  *
  * Arguments:
  *   fmt         svdq_format.
@@ -111,12 +112,12 @@ int svdq_version(void);
  *   lora_down   fp16 [r][K] (carries diag(smooth_inv)); may be NULL iff r == 0.
  *   act_codes   out, u8 [M][K/2].
  *   act_scales  out, fp16 [M][K/64] (INT4_G64) or u8 [M][K/32] (FP4_E2M1_B32).
- *   lora_act    out, fp32 [M][r]; may be NULL iff r == 0.
+ *   lora_act    out, fp16 [M][r]; may be NULL iff r == 0.
  *   stream      hipStream_t.
  */
 int svdq_quantize_act(int fmt, int M, int K, int r,
                       const void* X, const float* smooth_inv, const void* lora_down,
-                      uint8_t* act_codes, void* act_scales, float* lora_act,
+                      uint8_t* act_codes, void* act_scales, void* lora_act,
                       void* stream);
 
 /*
@@ -141,7 +142,7 @@ int svdq_quantize_act(int fmt, int M, int K, int r,
  *   r           low-rank width; r % 16 == 0, 0 <= r <= 128.
  *   act_codes   u8 [M][K/2] (from svdq_quantize_act).
  *   act_scales  fp16 [M][K/64] or u8 [M][K/32].
- *   lora_act    fp32 [M][r]; may be NULL iff r == 0.
+ *   lora_act    fp16 [M][r]; may be NULL iff r == 0.
  *   w_codes     u8 [N][K/2].
  *   w_scales    fp16 [N][K/64] or u8 [N][K/32].
  *   lora_up     fp16 [N][r]; may be NULL iff r == 0.
@@ -151,7 +152,7 @@ int svdq_quantize_act(int fmt, int M, int K, int r,
  *   stream      hipStream_t.
  */
 int svdq_gemm_w4a4(int fmt, int M, int N, int K, int r,
-                   const uint8_t* act_codes, const void* act_scales, const float* lora_act,
+                   const uint8_t* act_codes, const void* act_scales, const void* lora_act,
                    const uint8_t* w_codes, const void* w_scales, const void* lora_up,
                    const void* bias, int epi, void* Y, void* stream);
 

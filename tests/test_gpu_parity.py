@@ -2,7 +2,7 @@
 
 Bar: activation codes and scales bit-exact; layer / GEMM / GEMV outputs
 within relative L2 2e-3 of the oracle's float64 result on the same codes;
-lora_act within 1e-3 of the float64 low-rank down-projection. Every oracle
+lora_act (fp16) within 1e-3 of the float64 low-rank down-projection. Every oracle
 input comes from the seeded generators or from the oracle itself, never from
 the GPU.
 """
@@ -157,7 +157,7 @@ def test_gemm_tiny(P, fmt, M, rank, use_bias, epi):
     cfg, d, si, layer = tiny_layer(fmt, rank)
     X = d["X"][:M]
     codes_u, packed, scales = oracle.quantize_act_ref(X, si, fmt)
-    la = oracle.lora_act_ref(X, layer["lora_down"]).astype(np.float32)
+    la = oracle.lora_act_ref(X, layer["lora_down"]).astype(np.float16)
     bias = d["bias"] if use_bias else None
     wu = layer["w_codes_unpacked"]
     y_ref = oracle.gemm_ref(codes_u, scales, la, wu, layer["w_scales"], layer["lora_up"], bias, fmt, epi)
@@ -191,7 +191,7 @@ def test_gemm_full_size_sampled(P, name):
     fmt = cfg.fmt
     p = synth.random_quantized_layer(cfg, seed=2)
     codes_u, packed, scales = oracle.quantize_act_ref(p["X"], p["smooth_inv"], fmt)
-    la = oracle.lora_act_ref(p["X"], p["lora_down"]).astype(np.float32)
+    la = oracle.lora_act_ref(p["X"], p["lora_down"]).astype(np.float16)
     Y = P.svdq_gemm_w4a4(dev(packed), dev(scales), dev(la), dev(p["w_codes"]), dev(p["w_scales"]),
                          dev(p["lora_up"]), dev(p["bias"]), fmt, cfg.epilogue)
     y = host(Y)
