@@ -29,11 +29,12 @@ __device__ __forceinline__ float lane_sum_xor(float v, int mask) {
 // GELU, tanh form, in fp32: y/2 * (1 + tanh(u)), u = sqrt(2/pi) (y + 0.044715 y^3).
 // Uses 1 + tanh(u) = 2 / (1 + exp(-2u)), so the value is y / (1 + 2^(-2u log2 e))
 // with the hardware exp2 and reciprocal (about 1 ulp each): far below the fp16
-// rounding of the result. Large |y| saturates to y or -0 exactly.
+// rounding of the result. The exponent -2u log2 e is formed as y (c0 + c1 y^2).
+// Large |y| saturates to y or -0 exactly.
 __device__ __forceinline__ float gelu_tanh_f32(float y) {
-  const float k0 = -2.0f * 0.7978845608028654f * 1.4426950408889634f;  // -2 sqrt(2/pi) log2(e)
-  const float k1 = 0.044715f;
-  const float e = __builtin_amdgcn_exp2f(k0 * fmaf(k1 * y, y * y, y));
+  const float c0 = -2.0f * 0.7978845608028654f * 1.4426950408889634f;  // -2 sqrt(2/pi) log2(e)
+  const float c1 = c0 * 0.044715f;
+  const float e = __builtin_amdgcn_exp2f(y * fmaf(c1, y * y, c0));
   return y * __builtin_amdgcn_rcpf(1.0f + e);
 }
 

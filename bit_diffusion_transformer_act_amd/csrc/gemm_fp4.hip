@@ -10,14 +10,20 @@
 //
 // With no VALU work the bound is the matrix core, so the tile is sized for
 // operand reuse: 256 x 256 per workgroup, 4 waves of 128 x 128 (4 x 4 blocks
-// of 32 x 32, 256 fp32 accumulators per lane held in AGPRs). Per K step of 128
-// codes a workgroup moves 34 KB into LDS for 8.4 M MACs (about 33 B/clk per CU
-// at the MXFP4 rate, half of what a 128 x 128 tile would need). The ring has 4
-// stages of 34 KB (one workgroup per CU); loads are LDS-DMA as in the INT4
-// kernel, one barrier per step. This file is built with MFMA results in AGPRs
-// (no VGPR-form flag): the accumulators are only touched by MFMAs until the
-// epilogue.
+// of 32 x 32, 256 fp32 accumulators per lane held in AGPRs), one workgroup per
+// CU. Operands reach LDS by LDS-DMA in units that keep the memory pipeline's
+// request count low (each request costs about as much as the bytes it moves):
+//  - codes in stage pairs of 256 codes: whole 128-byte row lines, 8 rows per
+//    instruction, two 64 KB pair slots (the pair in use and the next one);
+//  - scales in groups of 4 steps: 16 bytes per row, two 8 KB group slots.
+// The 16 MFMAs of each half-step (64 codes) run while the next half-step's
+// operands are read from LDS; the DMA of the pair after next is threaded
+// between the MFMAs of the last half-step of a pair, after the one barrier per
+// pair. The low-rank up-projection is added after the main loop, so its global
+// loads never wait behind the DMA. Built with MFMA results in AGPRs (no
+// VGPR-form flag): the accumulators are only touched by MFMAs until the epilogue.
 #include <atomic>
+#include <type_traits>
 
 #include "common.hpp"
 #include "pipeline.hpp"
@@ -27,13 +33,18 @@ namespace svdq {
 namespace fp4big {
 constexpr int BM = 256, BN = 256;
 constexpr int RB = 4, CB = 4;                 // 32 x 32 blocks per wave
-constexpr int A_BYTES = BM * 64, B_BYTES = BN * 64;
-constexpr int SC_ROWS = BM + BN;              // one scale word (4 E8M0 bytes) per row
-constexpr int STAGE = A_BYTES + B_BYTES + SC_ROWS * 4;
-constexpr int STAGES = 4;
-constexpr int LDS = STAGES * STAGE;
-constexpr int DMA_PER_STEP = BM / 64 + BN / 64 + SC_ROWS / 256;   // per thread
+constexpr int ROW = 128;                      // bytes of a code row per stage pair
+constexpr int PAIR = (BM + BN) * ROW;         // 64 KB pair slot: A rows, then B rows
+constexpr int SROW = 16;                      // bytes of a scale row per group of 4 steps
+constexpr int SGRP = (BM + BN) * SROW;        // 8 KB group slot
+constexpr int LDS = 2 * PAIR + 2 * SGRP;      // 144 KB
+static_assert(PAIR / 4096 == 16 && SGRP / 4096 == 2, "DMA plan: 16 + 2 instructions per thread");
 }  // namespace fp4big
+
+// The eight 16-byte chunks of a 128-byte code row are XOR-swizzled with
+// (row >> 1) & 7, so the 16 rows that one ds_read_b128 serves per pass (same
+// logical chunk) land in 16 distinct 16-byte bank slots.
+__device__ __forceinline__ int swz8(int row) { return (row >> 1) & 7; }
 
 template <int EPI>
 __global__ __launch_bounds__(256, 1)
@@ -64,54 +75,43 @@ void gemm_fp4_big_kernel(const uint8_t* __restrict__ act_codes, const uint8_t* _
   const int gm = min(ntm - first_m, GROUP_M);
   const int m0 = (first_m + (pid % gsz) % gm) * BM;
   const int n0 = ((pid % gsz) / gm) * BN;
-  const int nk = K >> 7;
+  const int nk = K >> 7;          // steps of 128 codes, a multiple of 4
+  const int np = nk >> 1;         // stage pairs
+  const int ng = nk >> 2;         // scale groups
   const int KB = K >> 1;
-  const int sstride = K >> 5;
+  const int SK = K >> 5;          // scale bytes per row
 
-  // ---- DMA sources: wave w fills rows [64 w, 64 w + 64) of A and of B
-  const uint8_t* ga[BM / 64];
-  const uint8_t* gb[BN / 64];
-  const uint8_t* gs[SC_ROWS / 256];
-  uint32_t la_off[BM / 64], lb_off[BN / 64], ls_off[SC_ROWS / 256];
+  // ---- DMA plan. Code instruction j (0..15) of wave w fills slot rows
+  // 32 j + 8 w .. +8 (j < 8: A, else B); lane L takes row + L/8 and chunk L%8.
+  // Scale instruction j (0: A, 1: B) of wave w fills rows 64 w + L of its half.
+  const uint8_t* tA = act_codes + (size_t)m0 * KB;
+  const uint8_t* tB = w_codes + (size_t)n0 * KB;
+  const uint8_t* tsA = act_scales + (size_t)m0 * SK;
+  const uint8_t* tsB = w_scales + (size_t)n0 * SK;
+  const int alast = M - 1 - m0;                 // rows past M re-read the last row
+  const int rl = 8 * wave + (lane >> 3);
+  const int coff = ((lane & 7) ^ swz8(rl)) * 16;  // swz8(32 j + rl) == swz8(rl)
+  uint32_t aoff[8], boff[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    aoff[j] = (uint32_t)min(32 * j + rl, alast) * (uint32_t)KB + (uint32_t)coff;
+    boff[j] = (uint32_t)(32 * j + rl) * (uint32_t)KB + (uint32_t)coff;
+  }
+  const uint32_t saoff = (uint32_t)min(64 * wave + lane, alast) * (uint32_t)SK;
+  const uint32_t sboff = (uint32_t)(64 * wave + lane) * (uint32_t)SK;
   const uint32_t lds0 = lds_addr(smem);
-#pragma unroll
-  for (int i = 0; i < BM / 64; ++i) {
-    const int rloc = wave * (BM / 4) + 16 * i;
-    const int row = rloc + (lane >> 2);
-    const int chunk = (lane & 3) ^ swz(row);
-    ga[i] = act_codes + (size_t)min(m0 + row, M - 1) * KB + chunk * 16;
-    la_off[i] = rloc * 64;
-  }
-#pragma unroll
-  for (int i = 0; i < BN / 64; ++i) {
-    const int rloc = wave * (BN / 4) + 16 * i;
-    const int row = rloc + (lane >> 2);
-    const int chunk = (lane & 3) ^ swz(row);
-    gb[i] = w_codes + (size_t)(n0 + row) * KB + chunk * 16;
-    lb_off[i] = A_BYTES + rloc * 64;
-  }
-#pragma unroll
-  for (int i = 0; i < SC_ROWS / 256; ++i) {
-    const int rloc = (wave * (SC_ROWS / 256) + i) * 64;
-    const int row = rloc + lane;
-    gs[i] = (row < BM) ? act_scales + (size_t)min(m0 + row, M - 1) * sstride
-                       : w_scales + (size_t)(n0 + row - BM) * sstride;
-    ls_off[i] = A_BYTES + B_BYTES + rloc * 4;
-  }
-  auto issue = [&](int ks) {
-    const uint32_t base = lds0 + (uint32_t)((ks % STAGES) * STAGE);
-#pragma unroll
-    for (int i = 0; i < BM / 64; ++i) dma16(ga[i] + ks * 64, base + la_off[i]);
-#pragma unroll
-    for (int i = 0; i < BN / 64; ++i) dma16(gb[i] + ks * 64, base + lb_off[i]);
-#pragma unroll
-    for (int i = 0; i < SC_ROWS / 256; ++i) dma4(gs[i] + ks * 4, base + ls_off[i]);
-  };
-#pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
-    if (s < nk) issue(s);
 
-  // ---- low-rank up-projection initialises the accumulators
+  auto code_dma = [&](int pp, int j) {   // pair pp, instruction j (constant)
+    const uint32_t lds = lds0 + (uint32_t)((pp & 1) * PAIR + (32 * j + 8 * wave) * ROW);
+    if (j < 8) dma16_so(tA, aoff[j] + (uint32_t)(pp * ROW), lds);
+    else dma16_so(tB, boff[j - 8] + (uint32_t)(pp * ROW), lds);
+  };
+  auto scale_dma = [&](int q, int j) {   // scale group q, instruction j (constant)
+    const uint32_t lds = lds0 + (uint32_t)(2 * PAIR + (q & 1) * SGRP + (256 * j + 64 * wave) * SROW);
+    if (j == 0) dma16_so(tsA, saoff + (uint32_t)(q * SROW), lds);
+    else dma16_so(tsB, sboff + (uint32_t)(q * SROW), lds);
+  };
+
   v16f acc[RB][CB];
 #pragma unroll
   for (int i = 0; i < RB; ++i)
@@ -119,28 +119,139 @@ void gemm_fp4_big_kernel(const uint8_t* __restrict__ act_codes, const uint8_t* _
     for (int j = 0; j < CB; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-  // loads for 32 ranks are issued together so a tile pays one round trip
-  for (int j0 = 0; j0 < r; j0 += 32) {
-    const int nj = min(r - j0, 32) >> 4;
-    uint4 ua[RB][2], ub[CB][2];
+
+  int arow[RB], brow[CB];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+  for (int rb = 0; rb < RB; ++rb) arow[rb] = wm * 128 + rb * 32 + l32;
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) brow[cb] = wn * 128 + cb * 32 + l32;
+  const int s8 = swz8(l32);   // == swz8(arow[rb]) == swz8(brow[cb])
+
+  // operands of half-step hs (0..3) of pair pp: step 2 pp + hs / 2, K half hs % 2
+  struct Ops { uint4 a[RB], b[CB]; };
+  auto load_ops = [&](Ops& o, int pp, int hs) {
+    const uint8_t* st = smem + (pp & 1) * PAIR;
+    const int ch = ((2 * hs + lh) ^ s8) << 4;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) o.a[rb] = *reinterpret_cast<const uint4*>(st + arow[rb] * ROW + ch);
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+      o.b[cb] = *reinterpret_cast<const uint4*>(st + (BM + brow[cb]) * ROW + ch);
+  };
+  struct Sc { uint32_t a[RB], b[CB]; };
+  auto load_sc = [&](Sc& e, int ks) {   // the 4 E8M0 bytes of step ks for this lane's rows
+    const uint8_t* sS = smem + 2 * PAIR + ((ks >> 2) & 1) * SGRP + (ks & 3) * 4;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) e.a[rb] = *reinterpret_cast<const uint32_t*>(sS + arow[rb] * SROW);
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+      e.b[cb] = *reinterpret_cast<const uint32_t*>(sS + (BM + brow[cb]) * SROW);
+  };
+  // lane l < 32 holds K block 0 of the half-step, lane l + 32 block 1
+  auto mfma = [&](const Ops& o, const Sc& e, int g, int rb, int cb) {
+    const int sh = 8 * (2 * g + lh);
+    const v8i av = v8i{(int)o.a[rb].x, (int)o.a[rb].y, (int)o.a[rb].z, (int)o.a[rb].w, 0, 0, 0, 0};
+    const v8i bv = v8i{(int)o.b[cb].x, (int)o.b[cb].y, (int)o.b[cb].z, (int)o.b[cb].w, 0, 0, 0, 0};
+    acc[rb][cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+        av, bv, acc[rb][cb], 4, 4, 0, (int)((e.a[rb] >> sh) & 0xFFu), 0, (int)((e.b[cb] >> sh) & 0xFFu));
+  };
+  auto mma = [&](const Ops& o, const Sc& e, int g) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) mfma(o, e, g, rb, cb);
+  };
+  // the same 16 MFMAs with the DMA of pair dp (and scale group dq) threaded
+  // between them, so that issuing loads never holds up the matrix core of a
+  // SIMD that has one wave
+  auto mma_dma = [&](const Ops& o, const Sc& e, int g, int dp, int dq, auto with_scales) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        mfma(o, e, g, rb, cb);
+        const int i = rb * CB + cb;
+        code_dma(dp, i);
+        if constexpr (decltype(with_scales)::value) {
+          if (i < 2) scale_dma(dq, i);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  };
+
+  Ops P0, P1;
+  Sc E0, E1;
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  // one stage pair. On entry P0 holds its half-step 0 and E0 the scales of its
+  // first step. MORE: a pair follows (published at the end of this one); DMA:
+  // the pair after that (and, for SDMA, the next scale group) is loaded now.
+  // All three are compile-time, so the body is straight-line code.
+  auto pair = [&](int pp, auto more, auto dma, auto sdma) {
+    load_ops(P1, pp, 1);
+    mma(P0, E0, 0);
+    load_ops(P0, pp, 2);
+    load_sc(E1, 2 * pp + 1);
+    mma(P1, E0, 1);
+    load_ops(P1, pp, 3);
+    mma(P0, E1, 0);
+    if constexpr (decltype(more)::value) {
+      // every LDS read of this pair has completed, and so has the DMA of the next
+      // pair and scale group; past the barrier no wave reads this pair's slot (nor
+      // the previous scale group's), which the DMA reuses
+      waitvm_lgkm0<0>();
+      __syncthreads();
+      load_ops(P0, pp + 1, 0);
+      load_sc(E0, 2 * pp + 2);
+    }
+    if constexpr (decltype(dma)::value) mma_dma(P1, E1, 1, pp + 2, (pp >> 1) + 1, sdma);
+    else mma(P1, E1, 1);
+  };
+
+  // prologue: pair 0, scale group 0, pair 1 (nk >= 4, so np >= 2)
+#pragma unroll
+  for (int j = 0; j < 16; ++j) code_dma(0, j);
+  scale_dma(0, 0);
+  scale_dma(0, 1);
+#pragma unroll
+  for (int j = 0; j < 16; ++j) code_dma(1, j);
+  waitvm<16>();   // pair 0 and scale group 0 have landed
+  __syncthreads();
+  load_ops(P0, 0, 0);
+  load_sc(E0, 0);
+  int q = 0;
+  for (; q + 1 < ng; ++q) {
+    pair(2 * q, T_{}, T_{}, T_{});       // loads pair 2q + 2 and scale group q + 1
+    pair(2 * q + 1, T_{}, T_{}, F_{});   // loads pair 2q + 3
+  }
+  pair(2 * q, T_{}, F_{}, F_{});
+
+  // ---- low-rank up-projection: lora_act (fp16) times lora_up (fp16) into the
+  // same accumulators, v_mfma_f32_32x32x16_f16 (lane l: row l%32, ranks
+  // j0 + 8 (l/32) .. +8). The loads go out before the last pair's MFMAs.
+  constexpr int LR = 2;   // 16-rank blocks per round trip
+  auto lora_load = [&](uint4 (&ua)[RB][LR], uint4 (&ub)[CB][LR], int j0) {
+    const int nj = min(r - j0, 16 * LR) >> 4;
+#pragma unroll
+    for (int h = 0; h < LR; ++h) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        const int m = m0 + wm * 128 + rb * 32 + l32;
+        const int m = m0 + arow[rb];
         ua[rb][h] = (m < M && h < nj)
                         ? *reinterpret_cast<const uint4*>(lora_act + (size_t)m * r + j0 + 16 * h + lh * 8)
                         : make_uint4(0, 0, 0, 0);
       }
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
-        const int n = n0 + wn * 128 + cb * 32 + l32;
+        const int n = n0 + brow[cb];
         ub[cb][h] = (h < nj) ? *reinterpret_cast<const uint4*>(lora_up + (size_t)n * r + j0 + 16 * h + lh * 8)
                              : make_uint4(0, 0, 0, 0);
       }
     }
+  };
+  auto lora_mma = [&](const uint4 (&ua)[RB][LR], const uint4 (&ub)[CB][LR]) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < LR; ++h)
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -148,52 +259,15 @@ void gemm_fp4_big_kernel(const uint8_t* __restrict__ act_codes, const uint8_t* _
           acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, ua[rb][h]),
                                                                __builtin_bit_cast(v8h, ub[cb][h]),
                                                                acc[rb][cb], 0, 0, 0);
-  }
-
-  int arow[RB], brow[CB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) arow[rb] = wm * 128 + rb * 32 + l32;
-#pragma unroll
-  for (int cb = 0; cb < CB; ++cb) brow[cb] = wn * 128 + cb * 32 + l32;
-
-  for (int ks = 0; ks < nk; ++ks) {
-    if (ks + STAGES - 2 < nk) waitvm<DMA_PER_STEP * (STAGES - 2)>();
-    else waitvm<0>();
-    __syncthreads();
-    if (ks + STAGES - 1 < nk) issue(ks + STAGES - 1);
-
-    const uint8_t* st = smem + (ks % STAGES) * STAGE;
-    const uint8_t* sA = st;
-    const uint8_t* sB = st + A_BYTES;
-    const uint32_t* sS = reinterpret_cast<const uint32_t*>(st + A_BYTES + B_BYTES);
-    uint32_t ea[RB], eb[CB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) ea[rb] = sS[arow[rb]];
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) eb[cb] = sS[BM + brow[cb]];
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      const int sh = 8 * (2 * g + lh);
-      v8i av[RB], bv[CB];
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const int rr = arow[rb];
-        const uint4 ap = *reinterpret_cast<const uint4*>(sA + rr * 64 + (((g * 2 + lh) ^ swz(rr)) << 4));
-        av[rb] = v8i{(int)ap.x, (int)ap.y, (int)ap.z, (int)ap.w, 0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        const int rr = brow[cb];
-        const uint4 bp = *reinterpret_cast<const uint4*>(sB + rr * 64 + (((g * 2 + lh) ^ swz(rr)) << 4));
-        bv[cb] = v8i{(int)bp.x, (int)bp.y, (int)bp.z, (int)bp.w, 0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
-          acc[rb][cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              av[rb], bv[cb], acc[rb][cb], 4, 4, 0, (int)((ea[rb] >> sh) & 0xFFu), 0,
-              (int)((eb[cb] >> sh) & 0xFFu));
+  };
+  uint4 ua[RB][LR], ub[CB][LR];
+  if (r > 0) lora_load(ua, ub, 0);
+  pair(2 * q + 1, F_{}, F_{}, F_{});
+  if (r > 0) {
+    lora_mma(ua, ub);
+    for (int j0 = 16 * LR; j0 < r; j0 += 16 * LR) {
+      lora_load(ua, ub, j0);
+      lora_mma(ua, ub);
     }
   }
 
@@ -201,6 +275,7 @@ void gemm_fp4_big_kernel(const uint8_t* __restrict__ act_codes, const uint8_t* _
   // is free now) so that Y is written as whole rows with 16-byte stores.
   constexpr int TP = BN + 8;   // padded row (halves) of the staging tile
   static_assert(BM * TP * 2 <= LDS, "staging tile must fit in the ring");
+  waitvm<0>();   // no DMA outstanding
   __syncthreads();
   __half* tile = reinterpret_cast<__half*>(smem);
 #pragma unroll
@@ -231,7 +306,7 @@ hipError_t launch_gemm_fp4_big(int M, int N, int K, int r, const uint8_t* ac, co
                                const void* la, const uint8_t* wc, const void* ws, const void* lu,
                                const void* bias, int epi, void* Y, hipStream_t st) {
   using namespace fp4big;
-  if (N % BN != 0) return hipErrorNotSupported;
+  if (N % BN != 0 || K % 512 != 0) return hipErrorNotSupported;   // whole scale groups
   const int ntiles = ((M + BM - 1) / BM) * (N / BN);
   if (ntiles < 256) return hipErrorNotSupported;   // too few tiles to fill 256 CUs
   auto kern = epi ? gemm_fp4_big_kernel<1> : gemm_fp4_big_kernel<0>;
