@@ -74,17 +74,17 @@ def kernel_source_hash(name):
     return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
 
 
-def stored_traffic(kernel_file, workload):
-    """HBM bytes per launch from committed rocprofv3 --pmc counters, only if the
-    kernel source is unchanged since they were taken."""
+def stored_traffic(workload):
+    """HBM bytes per launch of the GEMM from committed rocprofv3 --pmc counters,
+    only if the kernel's source file is unchanged since they were taken."""
     p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(p):
         return None
     try:
         d = json.load(open(p))
-    except (OSError, ValueError):
-        return None
-    if d.get("source_sha") != kernel_source_hash(kernel_file):
+        if d.get("source_sha") != kernel_source_hash(d["source"]):
+            return None
+    except (OSError, ValueError, KeyError):
         return None
     return d.get("hbm_bytes_per_launch")
 
@@ -241,7 +241,7 @@ def main():
     roofline = {"bound": "mfma", "kernel": "svdq_gemm_w4a4", "workload": dcfg.name,
                 "achieved": round(achieved, 1), "peak": PEAK_TOPS[dcfg.fmt], "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_TOPS[dcfg.fmt], 4),
-                "traffic": stored_traffic("gemm_w4a4.hip", dcfg.name),
+                "traffic": stored_traffic(dcfg.name),
                 "ops_per_launch": dops,
                 "note": "INT4 runs on int8 MFMA: tera-ops against the 5.0 POP/s int8 peak"
                         if dcfg.fmt == "int4_g64" else "FP4 against the 10.1 PFLOP/s MXFP4 peak"}

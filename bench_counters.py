@@ -24,9 +24,11 @@ import json
 import os
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-KERNELS = {"svdq_gemm_w4a4": ("gemm_w4a4_kernel", "gemm_w4a4.hip"),
-           "svdq_quantize_act": ("quantize_act_kernel", "quantize_act.hip"),
-           "awq_gemv_w4a16": ("awq_gemv", "awq_gemv.hip")}
+# entry point -> [(kernel-name substring, source file)]; the first that matches wins
+KERNELS = {"svdq_gemm_w4a4": [("gemm_fp4_big_kernel", "gemm_fp4.hip"),
+                              ("gemm_w4a4_kernel", "gemm_w4a4.hip")],
+           "svdq_quantize_act": [("quantize_act_kernel", "quantize_act.hip")],
+           "awq_gemv_w4a16": [("awq_gemv", "awq_gemv.hip")]}
 
 
 def source_sha(fname: str) -> str:
@@ -75,21 +77,26 @@ def main():
              f"(torch add / fill of {args.calib_mib} MiB)", "",
              "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM read MB | HBM write MB | total MB |",
              "|---|---|---|---|---|---|"]
-    for api, (sub, src) in KERNELS.items():
-        fv = [v for n, v in fetch if sub in n]
-        wv = [v for n, v in write if sub in n]
-        if not fv or not wv:
+    for api, cands in KERNELS.items():
+        for sub, src in cands:
+            fv = [v for n, v in fetch if sub in n]
+            wv = [v for n, v in write if sub in n]
+            if fv and wv:
+                break
+        else:
             continue
         fk, wk = sum(fv) / len(fv), sum(wv) / len(wv)
         rd, wr = fk / f_factor * 1024, wk / w_factor * 1024
         out["kernels"][api] = {"fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
                                "hbm_read_bytes": round(rd), "hbm_write_bytes": round(wr),
                                "hbm_bytes_per_launch": round(rd + wr),
-                               "launches": len(fv), "source_sha": source_sha(src)}
+                               "launches": len(fv), "kernel": sub, "source": src,
+                               "source_sha": source_sha(src)}
         lines.append(f"| {api} | {fk:.0f} | {wk:.0f} | {rd / 1e6:.1f} | {wr / 1e6:.1f} | "
                      f"{(rd + wr) / 1e6:.1f} |")
     g = out["kernels"].get("svdq_gemm_w4a4")
     if g:
+        out["source"] = g["source"]
         out["source_sha"] = g["source_sha"]
         out["hbm_bytes_per_launch"] = g["hbm_bytes_per_launch"]
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
