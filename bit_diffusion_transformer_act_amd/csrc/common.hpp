@@ -26,6 +26,20 @@ __device__ __forceinline__ float lane_sum_xor(float v, int mask) {
   return v + __shfl_xor(v, mask, kWave);
 }
 
+// max over lanes l and l ^ 32, and over lanes l and l ^ 16, with gfx950's lane
+// swaps: v_permlane32_swap exchanges the upper 32 lanes of its first operand
+// with the lower 32 of its second (so with two copies of v each lane ends up
+// holding v[l] and v[l ^ 32]); v_permlane16_swap does the same between the odd
+// and even 16-lane rows (v[l] and v[l ^ 16]). All 64 lanes must be active.
+__device__ __forceinline__ float lane_max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float lane_max_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // GELU, tanh form, in fp32: y/2 * (1 + tanh(u)), u = sqrt(2/pi) (y + 0.044715 y^3).
 // Uses 1 + tanh(u) = 2 / (1 + exp(-2u)), so the value is y / (1 + 2^(-2u log2 e))
 // with the hardware exp2 and reciprocal (about 1 ulp each): far below the fp16

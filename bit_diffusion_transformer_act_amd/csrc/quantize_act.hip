@@ -7,36 +7,55 @@
 // paragraph; nextgz.net "Hugging Face brings Nunchaku Lite to Diffusers",
 // section "Why W4A4 differs from weight-only backends").
 //
-// Work split (gfx950, wave64): a workgroup of 16 waves owns 16 rows of X and
-// all of K; wave w handles 64-wide K steps w, w+16, w+32, ... In a step,
-// lane l holds row (l % 16) and the 16 contiguous channels
-// [64 s + 16 (l / 16), +16): two 16-byte loads. That register tile is at the
-// same time
-//   - the A operand of two v_mfma_f32_16x16x32_f16 against lora_down (the
-//     MFMA k index (l/16)*8 + j is mapped to channel 64 s + 16 (l/16) + 8 h + j
-//     for call h = 0, 1; B uses the same map, so the dot product is exact
-//     over the permuted k), and
-//   - one quarter of an INT4 group (lanes l, l^16, l^32, l^48) or one half
-//     of an FP4 block (lanes l, l^16), whose amax is a two-/one-step xor
+// Work split (gfx950, wave64): a workgroup of W waves (4, 8 or 16) owns 16 rows
+// of X and all of K; wave w handles 64-wide K steps w, w+W, w+2W, ..., with the
+// loads of its next one or two steps in flight. In a step, lane l holds row
+// (l % 16) and two 8-channel chunks: q*8 .. +8 and 32 + q*8 .. +8 of the step
+// (q = l / 16), so each load instruction reads 16 rows x 64 contiguous bytes
+// (the vector memory unit's cost grows with the number of 64-byte sectors an
+// instruction touches). That register tile is at the same time
+//   - the A operands of two v_mfma_f32_16x16x32_f16 against lora_down, in the
+//     instruction's own layout (lane l: row l % 16, k 8 (l / 16) .. +8), one
+//     call per 32-channel half, and
+//   - a quarter of an INT4 group (lanes l, l^16, l^32, l^48), or a quarter of
+//     each of the two FP4 blocks of the step, whose amax is a two-step xor
 //     shuffle reduction.
-// Partial low-rank sums of the 16 waves meet in LDS and are added in a fixed
-// order, so lora_act (stored as fp16) is deterministic.
+// smooth_inv is staged in LDS once per workgroup (a global-load variant serves
+// K beyond the LDS budget). Partial low-rank sums of the W waves meet in LDS
+// and are added in a fixed order, so lora_act (stored as fp16) is
+// deterministic.
 #include <atomic>
 
 #include "common.hpp"
 
 namespace svdq {
 
-template <int FMT, int NCB>
-__global__ __launch_bounds__(1024)
+constexpr int kQuantLdsMax = 144 * 1024;   // LDS budget per workgroup (gfx950 has 160 KB)
+
+// LDS bytes besides smooth_inv: two round buffers and the low-rank partials
+template <int WAVES>
+constexpr size_t quant_lds_bytes(int ncb) {
+  return 2 * (size_t)(16 * (WAVES * 32 + 16) + 16 * WAVES * 2) + (size_t)WAVES * 16 * 16 * ncb * sizeof(float);
+}
+
+template <int FMT, int NCB, int WAVES, bool SLDS>
+__global__ __launch_bounds__(64 * WAVES)
 void quantize_act_kernel(const __half* __restrict__ X, const float* __restrict__ smooth_inv,
                          const __half* __restrict__ lora_down, uint8_t* __restrict__ codes,
                          void* __restrict__ scales, __half* __restrict__ lora_act,
                          int M, int K) {
 #pragma clang fp contract(off)
-  extern __shared__ float red[];  // [16 waves][16 rows][16 * NCB]
-  constexpr int kWaves = 16;
+  // LDS: two round buffers (codes, then scales, of 16 rows x WAVES steps),
+  // [WAVES][16 rows][16 * NCB] low-rank partials, then smooth_inv[K] if SLDS
+  extern __shared__ float lds_f[];
   constexpr int R = 16 * NCB;
+  constexpr int NL = NCB > 0 ? NCB : 1;
+  constexpr int CROW = WAVES * 32 + 16;         // padded code row of a round (bytes)
+  constexpr int SROW = WAVES * 2;               // scale row of a round (bytes)
+  constexpr int RBUF = 16 * CROW + 16 * SROW;   // one round buffer (bytes, multiple of 16)
+  uint8_t* rbuf = reinterpret_cast<uint8_t*>(lds_f);
+  float* red = lds_f + 2 * RBUF / 4;
+  float* s_si = red + WAVES * 16 * R;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int m0 = blockIdx.x * 16;
@@ -44,132 +63,246 @@ void quantize_act_kernel(const __half* __restrict__ X, const float* __restrict__
   const int q4 = lane >> 4;
   const bool row_ok = row < M;
   const int steps = K >> 6;
-  const size_t xrow = (size_t)row * (size_t)K;
+  // rows past M read row M - 1 (never stored; rows are independent in the
+  // MFMA and in the amax groups). An unconditional load matters: a select on
+  // the load's destination would make every prefetch wait for the previous one.
+  const size_t xrow = (size_t)min(row, M - 1) * (size_t)K;
 
-  v4f lacc[NCB > 0 ? NCB : 1];
-#pragma unroll
-  for (int c = 0; c < (NCB > 0 ? NCB : 1); ++c) lacc[c] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  // X for the wave's first step; each iteration prefetches the next step's
-  // X before working on the current one.
-  uint4 xa = make_uint4(0, 0, 0, 0), xb = make_uint4(0, 0, 0, 0);
-  if (row_ok && wave < steps) {
-    const uint4* p = reinterpret_cast<const uint4*>(X + xrow + wave * 64 + q4 * 16);
-    xa = p[0];
-    xb = p[1];
+  if constexpr (SLDS) {
+    for (int i = threadIdx.x * 4; i < K; i += 64 * WAVES * 4)
+      *reinterpret_cast<float4*>(s_si + i) = *reinterpret_cast<const float4*>(smooth_inv + i);
+    __syncthreads();
   }
-  for (int s = wave; s < steps; s += kWaves) {
-    const int k0 = s * 64 + q4 * 16;
-    const uint4 ca = xa, cb = xb;
-    if (row_ok && s + kWaves < steps) {
-      const uint4* p = reinterpret_cast<const uint4*>(X + xrow + k0 + kWaves * 64);
-      xa = p[0];
-      xb = p[1];
-    }
+
+  v4f lacc[NL];
+#pragma unroll
+  for (int c = 0; c < NL; ++c) lacc[c] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // One step's loads: this lane's two 8-channel chunks of X and the matching
+  // lora_down operands. Register sets rotate so that the loads of the next one
+  // or two steps of the wave are in flight while a step is processed.
+  struct Step {
+    uint4 xa, xb;
+    uint4 lb[NL][2];
+  };
+  // Loads are unconditional (past the last step they re-read it, and the step
+  // is never processed): a branch around them would leave the compiler's
+  // vmcnt bookkeeping unsure how many are in flight, and every use would then
+  // wait for all of them.
+  auto load = [&](Step& d, int s) {
+    const int k0 = min(s, steps - 1) * 64 + q4 * 8;
+    d.xa = *reinterpret_cast<const uint4*>(X + xrow + k0);
+    d.xb = *reinterpret_cast<const uint4*>(X + xrow + k0 + 32);
     if constexpr (NCB > 0) {
-      const v8h a0 = __builtin_bit_cast(v8h, ca);
-      const v8h a1 = __builtin_bit_cast(v8h, cb);
 #pragma unroll
       for (int c = 0; c < NCB; ++c) {
-        const uint4* pb = reinterpret_cast<const uint4*>(lora_down + (size_t)(c * 16 + (lane & 15)) * K + k0);
-        const v8h b0 = __builtin_bit_cast(v8h, pb[0]);
-        const v8h b1 = __builtin_bit_cast(v8h, pb[1]);
-        lacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b0, lacc[c], 0, 0, 0);
-        lacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b1, lacc[c], 0, 0, 0);
+        const __half* pb = lora_down + (size_t)(c * 16 + (lane & 15)) * K + k0;
+        d.lb[c][0] = *reinterpret_cast<const uint4*>(pb);
+        d.lb[c][1] = *reinterpret_cast<const uint4*>(pb + 32);
       }
     }
-    // smoothing: x_hat = fl32(fp32(x) * smooth_inv), a plain IEEE multiply
+  };
+
+  // INT4 codes of 8 values against scale sf (nonzero), rs = rcp(sf); sets
+  // near_tie when a value may round differently from the IEEE quotient.
+  // y = v * rs is formed exactly inside fma(v, rs, 1.5 * 2^23), which rounds it
+  // to an integer (ties to even) in the low mantissa bits; the clamp to +-7 is
+  // a med3 in that domain, and fma(v, rs, -q) is y - q with one rounding. The
+  // low byte of the clamped value is q as a two's-complement int8, and byte
+  // permutes gather the eight low nibbles (even k in the low nibble).
+  auto int4_codes = [&](const float* v, float rs, bool& near_tie) {
+    constexpr float kM = 12582912.0f;   // 1.5 * 2^23
+    uint32_t b[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float yv = __builtin_amdgcn_fmed3f(fmaf(v[i], rs, kM), kM - 7.0f, kM + 7.0f);
+      const float t = fmaf(v[i], rs, -(yv - kM));
+      near_tie |= fabsf(t) > 0.4999847412109375f;   // 0.5 - 2^-16
+      b[i] = __float_as_uint(yv);
+    }
+    const uint32_t e = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[6], b[4], 0x0c0c0400u),
+                                             __builtin_amdgcn_perm(b[2], b[0], 0x0c0c0400u), 0x05040100u);
+    const uint32_t o = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[7], b[5], 0x0c0c0400u),
+                                             __builtin_amdgcn_perm(b[3], b[1], 0x0c0c0400u), 0x05040100u);
+    return (e & 0x0F0F0F0Fu) | ((o << 4) & 0xF0F0F0F0u);
+  };
+  auto int4_codes_exact = [&](const float* v, float sf) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float q = rintf(v[i] / sf);                           // IEEE division, ties to even
+      q = fminf(fmaxf(q, -7.0f), 7.0f);
+      w |= ((uint32_t)((int)q) & 0xFu) << (4 * i);
+    }
+    return w;
+  };
+  // FP4 E2M1 block: scale byte and the codes of this lane's 8 values
+  auto fp4_block = [&](const float* v, float amax, uint32_t& w) {
+    uint32_t sc = 0;
+    w = 0;
+    if (amax != 0.0f) {
+      int ex;
+      const float mant = frexpf(amax, &ex);           // amax = mant * 2^ex, mant in [0.5, 1)
+      int e = (mant <= 0.75f) ? ex - 3 : ex - 2;      // smallest e with 6 * 2^e >= amax
+      e = min(max(e, -127), 127);
+      sc = (uint32_t)(e + 127);
+      const float p = ldexpf(1.0f, -e);               // exact power of two
+      // u = fl32(x_hat / 2^e) = x_hat * 2^-e; v_cvt_scalef32_pk_fp4_f32 with
+      // scale 1 rounds two values to E2M1 (nearest, ties to even mantissa,
+      // saturating at 6, sign kept, first value in the low nibble) and writes
+      // the byte selected by its last operand.
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0] * p, v[1] * p, 1.0f, 0);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2] * p, v[3] * p, 1.0f, 1);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4] * p, v[5] * p, 1.0f, 2);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6] * p, v[7] * p, 1.0f, 3);
+    }
+    return sc;
+  };
+
+  // process step s into round buffer rb (its column is this wave's index)
+  auto process = [&](const Step& d, int s, uint8_t* rb) {
+    const int k0 = s * 64 + q4 * 8;
+    if constexpr (NCB > 0) {
+      const v8h a0 = __builtin_bit_cast(v8h, d.xa);
+      const v8h a1 = __builtin_bit_cast(v8h, d.xb);
+#pragma unroll
+      for (int c = 0; c < NCB; ++c) {
+        lacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, __builtin_bit_cast(v8h, d.lb[c][0]), lacc[c], 0, 0, 0);
+        lacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, __builtin_bit_cast(v8h, d.lb[c][1]), lacc[c], 0, 0, 0);
+      }
+    }
+    // smoothing: x_hat = fl32(fp32(x) * smooth_inv), a plain IEEE multiply.
+    // xh[0..7]: channels k0 .. k0+7, xh[8..15]: channels k0+32 .. k0+39.
     float xh[16];
     {
-      const float4* ps = reinterpret_cast<const float4*>(smooth_inv + k0);
-      const __half* ha = reinterpret_cast<const __half*>(&ca);
-      const __half* hb = reinterpret_cast<const __half*>(&cb);
+      float sv[16];
+      const float* ps = SLDS ? s_si : smooth_inv;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float4 sv = ps[i];
-        const __half* hs = (i < 2) ? ha + 4 * i : hb + 4 * (i - 2);
-        xh[4 * i + 0] = __half2float(hs[0]) * sv.x;
-        xh[4 * i + 1] = __half2float(hs[1]) * sv.y;
-        xh[4 * i + 2] = __half2float(hs[2]) * sv.z;
-        xh[4 * i + 3] = __half2float(hs[3]) * sv.w;
+      for (int h = 0; h < 2; ++h) {
+        const float4 u0 = *reinterpret_cast<const float4*>(ps + k0 + 32 * h);
+        const float4 u1 = *reinterpret_cast<const float4*>(ps + k0 + 32 * h + 4);
+        sv[8 * h + 0] = u0.x; sv[8 * h + 1] = u0.y; sv[8 * h + 2] = u0.z; sv[8 * h + 3] = u0.w;
+        sv[8 * h + 4] = u1.x; sv[8 * h + 5] = u1.y; sv[8 * h + 6] = u1.z; sv[8 * h + 7] = u1.w;
+      }
+      // one fma with a -0 addend: the product rounded once, sign of zero kept
+      const __half* ha = reinterpret_cast<const __half*>(&d.xa);
+      const __half* hb = reinterpret_cast<const __half*>(&d.xb);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        xh[i] = fmaf(__half2float(ha[i]), sv[i], -0.0f);
+        xh[8 + i] = fmaf(__half2float(hb[i]), sv[8 + i], -0.0f);
       }
     }
-    float amax = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(xh[i]));
-
-    uint32_t w0 = 0, w1 = 0;
+    uint8_t* crow = rb + (lane & 15) * CROW + wave * 32 + q4 * 4;
+    uint8_t* srow = rb + 16 * CROW + (lane & 15) * SROW + wave * 2;
     if constexpr (FMT == 0) {
       // INT4, group 64 = this step: reduce over the four lanes of the row.
-      amax = lane_max_xor(amax, 16);
-      amax = lane_max_xor(amax, 32);
+      float amax = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(xh[i]));
+      amax = lane_max_xor16(amax);
+      amax = lane_max_xor32(amax);
       const float s32 = amax / 7.0f;                    // IEEE division
       const __half s16 = __float2half_rn(fminf(s32, 65504.0f));
       const float sf = __half2float(s16);
+      uint32_t w0 = 0, w1 = 0;
       if (sf != 0.0f) {
         // q = clamp(rint(fl32(x_hat / s)), -7, 7) without a division per value:
-        // y = x_hat * rcp(s) is within 2^-19 |y| of fl32(x_hat / s) (rcp and the
-        // multiply are each within an ulp), so the two round to the same integer
-        // unless y lies within 2^-16 of a half-integer; only such values are
-        // recomputed with the IEEE division. Clamping first is harmless: every
-        // value beyond +-7 maps to +-7 either way. Rounding is the add/subtract
-        // of 1.5 * 2^23, whose low mantissa bits are then the two's-complement
-        // code.
+        // y = x_hat * rcp(s) is within 2^-19 |y| of fl32(x_hat / s) (rcp is within
+        // an ulp), so the two round to the same integer unless y lies within
+        // 2^-16 of a half-integer; only such groups are recomputed with the IEEE
+        // division. Clamping the rounded value equals rounding the clamped one,
+        // and a value beyond +-7.5 (possible only with a saturated scale) is
+        // flagged and recomputed.
         const float rs = __builtin_amdgcn_rcpf(sf);
         bool near_tie = false;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float c = __builtin_amdgcn_fmed3f(xh[i] * rs, -7.0f, 7.0f);
-          const float yv = c + 12582912.0f;
-          const float rv = yv - 12582912.0f;
-          near_tie |= fabsf(c - rv) > 0.4999847412109375f;   // 0.5 - 2^-16
-          const uint32_t nib = __float_as_uint(yv) & 0xFu;
-          if (i < 8) w0 |= nib << (4 * i); else w1 |= nib << (4 * (i - 8));
-        }
+        w0 = int4_codes(xh, rs, near_tie);
+        w1 = int4_codes(xh + 8, rs, near_tie);
         if (near_tie) {
-          w0 = 0;
-          w1 = 0;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            float q = rintf(xh[i] / sf);                // IEEE division, ties to even
-            q = fminf(fmaxf(q, -7.0f), 7.0f);
-            const uint32_t nib = (uint32_t)((int)q) & 0xFu;
-            if (i < 8) w0 |= nib << (4 * i); else w1 |= nib << (4 * (i - 8));
-          }
+          w0 = int4_codes_exact(xh, sf);
+          w1 = int4_codes_exact(xh + 8, sf);
         }
       }
-      if (row_ok) {
-        *reinterpret_cast<uint2*>(codes + (size_t)row * (K >> 1) + s * 32 + q4 * 8) = make_uint2(w0, w1);
-        if (q4 == 0) reinterpret_cast<__half*>(scales)[(size_t)row * (K >> 6) + s] = s16;
-      }
+      *reinterpret_cast<uint32_t*>(crow) = w0;
+      *reinterpret_cast<uint32_t*>(crow + 16) = w1;
+      if (q4 == 0) *reinterpret_cast<__half*>(srow) = s16;
     } else {
-      // FP4 E2M1, block 32 = half a step: reduce over the lane pair.
-      amax = lane_max_xor(amax, 16);
-      uint32_t sc = 0;
-      if (amax != 0.0f) {
-        int ex;
-        const float mant = frexpf(amax, &ex);           // amax = mant * 2^ex, mant in [0.5, 1)
-        int e = (mant <= 0.75f) ? ex - 3 : ex - 2;      // smallest e with 6 * 2^e >= amax
-        e = min(max(e, -127), 127);
-        sc = (uint32_t)(e + 127);
-        const float p = ldexpf(1.0f, -e);               // exact power of two
-        // u = fl32(x_hat / 2^e) = x_hat * 2^-e; v_cvt_scalef32_pk_fp4_f32 with
-        // scale 1 rounds two values to E2M1 (nearest, ties to even mantissa,
-        // saturating at 6, sign kept, first value in the low nibble) and writes
-        // the byte selected by its last operand.
-        w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, xh[0] * p, xh[1] * p, 1.0f, 0);
-        w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, xh[2] * p, xh[3] * p, 1.0f, 1);
-        w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, xh[4] * p, xh[5] * p, 1.0f, 2);
-        w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w0, xh[6] * p, xh[7] * p, 1.0f, 3);
-        w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, xh[8] * p, xh[9] * p, 1.0f, 0);
-        w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, xh[10] * p, xh[11] * p, 1.0f, 1);
-        w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, xh[12] * p, xh[13] * p, 1.0f, 2);
-        w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w1, xh[14] * p, xh[15] * p, 1.0f, 3);
+      // FP4 E2M1, block 32 = half a step: xh[0..7] belong to block 2s, xh[8..15]
+      // to block 2s + 1; each block is reduced over the four lanes of the row.
+      float am0 = 0.f, am1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        am0 = fmaxf(am0, fabsf(xh[i]));
+        am1 = fmaxf(am1, fabsf(xh[8 + i]));
       }
-      if (row_ok) {
-        *reinterpret_cast<uint2*>(codes + (size_t)row * (K >> 1) + s * 32 + q4 * 8) = make_uint2(w0, w1);
-        if ((q4 & 1) == 0) reinterpret_cast<uint8_t*>(scales)[(size_t)row * (K >> 5) + 2 * s + (q4 >> 1)] = (uint8_t)sc;
-      }
+      am0 = lane_max_xor32(lane_max_xor16(am0));
+      am1 = lane_max_xor32(lane_max_xor16(am1));
+      uint32_t w0, w1;
+      const uint32_t sc0 = fp4_block(xh, am0, w0);
+      const uint32_t sc1 = fp4_block(xh + 8, am1, w1);
+      *reinterpret_cast<uint32_t*>(crow) = w0;
+      *reinterpret_cast<uint32_t*>(crow + 16) = w1;
+      if (q4 == 0) *reinterpret_cast<uint16_t*>(srow) = (uint16_t)(sc0 | (sc1 << 8));
+    }
+  };
+
+  // The waves advance in rounds: in round p wave w processes step p W + w and
+  // leaves its codes and scales in the round buffer; after a barrier the
+  // workgroup writes the round out as whole 16-byte pieces of each row (codes:
+  // 32 W contiguous bytes per row, scales: 2 W), so each store instruction
+  // covers full lines instead of one 16-byte piece per row and step. The
+  // barriers wait for LDS only, so the loads of later rounds stay in flight.
+  const int nrounds = (steps + WAVES - 1) / WAVES;
+  auto round = [&](const Step& d, int p) {
+    uint8_t* rb = rbuf + (p & 1) * RBUF;
+    const int s = p * WAVES + wave;
+    if (s < steps) process(d, s, rb);
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS writes are done
+    __builtin_amdgcn_s_barrier();
+    const int vs = min(WAVES, steps - p * WAVES);   // steps in this round
+    for (int c = threadIdx.x; c < 16 * 2 * WAVES; c += 64 * WAVES) {
+      const int rl = c / (2 * WAVES), ch = c - rl * (2 * WAVES);
+      if (ch < 2 * vs && m0 + rl < M)
+        *reinterpret_cast<uint4*>(codes + (size_t)(m0 + rl) * (K >> 1) + p * WAVES * 32 + ch * 16) =
+            *reinterpret_cast<const uint4*>(rb + rl * CROW + ch * 16);
+    }
+    for (int c = threadIdx.x; c < 16 * WAVES; c += 64 * WAVES) {
+      const int rl = c / WAVES, j = c - rl * WAVES;
+      if (j < vs && m0 + rl < M)
+        *reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(scales) + (size_t)(m0 + rl) * (K >> 5) +
+                                     (size_t)(p * WAVES + j) * 2) =
+            *reinterpret_cast<const uint16_t*>(rb + 16 * CROW + rl * SROW + j * 2);
+    }
+    // the buffer is rewritten two rounds later, after the next round's barrier,
+    // by which time every wave has finished reading it here
+  };
+
+  // D register sets in flight: three where the register budget allows
+  // (64 * WAVES threads leave 512 / (WAVES / 4) VGPRs per lane), else two.
+  constexpr int D = (WAVES == 4) ? 3 : (WAVES == 8) ? (NCB <= 3 ? 3 : 2) : (NCB == 0 ? 3 : 2);
+  if constexpr (D == 3) {
+    Step d0, d1, d2;
+    load(d0, wave);
+    load(d1, wave + WAVES);
+    for (int p = 0; p < nrounds; p += 3) {
+      load(d2, (p + 2) * WAVES + wave);
+      round(d0, p);
+      if (p + 1 >= nrounds) break;
+      load(d0, (p + 3) * WAVES + wave);
+      round(d1, p + 1);
+      if (p + 2 >= nrounds) break;
+      load(d1, (p + 4) * WAVES + wave);
+      round(d2, p + 2);
+    }
+  } else {
+    Step d0, d1;
+    load(d0, wave);
+    for (int p = 0; p < nrounds; p += 2) {
+      load(d1, (p + 1) * WAVES + wave);
+      round(d0, p);
+      if (p + 1 >= nrounds) break;
+      load(d0, (p + 2) * WAVES + wave);
+      round(d1, p + 1);
     }
   }
 
@@ -185,30 +318,58 @@ void quantize_act_kernel(const __half* __restrict__ X, const float* __restrict__
       const int rr = t / R, cc = t - rr * R;
       float sum = 0.f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) sum += red[(w * 16 + rr) * R + cc];
+      for (int w = 0; w < WAVES; ++w) sum += red[(w * 16 + rr) * R + cc];
       if (m0 + rr < M) lora_act[(size_t)(m0 + rr) * R + cc] = __float2half_rn(sum);
     }
   }
 }
 
-template <int FMT, int NCB>
-static hipError_t launch_q(int M, int K, const void* X, const float* si, const void* ld,
-                           uint8_t* codes, void* scales, void* la, hipStream_t st) {
-  const dim3 grid((M + 15) / 16), block(1024);
-  const size_t lds = NCB > 0 ? (size_t)16 * 16 * 16 * NCB * sizeof(float) : 0;
+template <int FMT, int NCB, int WAVES, bool SLDS>
+static hipError_t launch_qws(int M, int K, const void* X, const float* si, const void* ld,
+                             uint8_t* codes, void* scales, void* la, hipStream_t st) {
+  const dim3 grid((M + 15) / 16), block(64 * WAVES);
+  const size_t lds = quant_lds_bytes<WAVES>(NCB) + (SLDS ? (size_t)K * sizeof(float) : 0);
   if (lds > 65536) {
+    // the attribute is raised once per instantiation to the largest size it may need
     static std::atomic<int> raised{0};
     if (!raised.load(std::memory_order_acquire)) {
       const hipError_t e = hipFuncSetAttribute(
-          reinterpret_cast<const void*>(&quantize_act_kernel<FMT, NCB>),
-          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+          reinterpret_cast<const void*>(&quantize_act_kernel<FMT, NCB, WAVES, SLDS>),
+          hipFuncAttributeMaxDynamicSharedMemorySize, kQuantLdsMax);
       if (e != hipSuccess) return e;
       raised.store(1, std::memory_order_release);
     }
   }
-  hipLaunchKernelGGL((quantize_act_kernel<FMT, NCB>), grid, block, lds, st,
+  hipLaunchKernelGGL((quantize_act_kernel<FMT, NCB, WAVES, SLDS>), grid, block, lds, st,
                      (const __half*)X, si, (const __half*)ld, codes, scales, (__half*)la, M, K);
   return hipGetLastError();
+}
+
+// smooth_inv goes to LDS when it fits beside the low-rank partials
+template <int FMT, int NCB, int WAVES>
+static hipError_t launch_qw(int M, int K, const void* X, const float* si, const void* ld,
+                            uint8_t* codes, void* scales, void* la, hipStream_t st) {
+  if (quant_lds_bytes<WAVES>(NCB) + (size_t)K * sizeof(float) <= (size_t)kQuantLdsMax)
+    return launch_qws<FMT, NCB, WAVES, true>(M, K, X, si, ld, codes, scales, la, st);
+  return launch_qws<FMT, NCB, WAVES, false>(M, K, X, si, ld, codes, scales, la, st);
+}
+
+// 16 rows per workgroup. With at least one workgroup per CU, 8 waves (2 per
+// SIMD, up to 256 VGPRs for the load ring); with fewer workgroups than CUs and
+// a small rank, 16 waves so that each busy CU keeps more loads in flight; for
+// ranks of 112 and more, 4 waves (the lora_down operands of a step take
+// 8 * r / 16 VGPRs per set).
+template <int FMT, int NCB>
+static hipError_t launch_q(int M, int K, const void* X, const float* si, const void* ld,
+                           uint8_t* codes, void* scales, void* la, hipStream_t st) {
+  if constexpr (NCB >= 7) {
+    return launch_qw<FMT, NCB, 4>(M, K, X, si, ld, codes, scales, la, st);
+  } else if constexpr (NCB > 2) {
+    return launch_qw<FMT, NCB, 8>(M, K, X, si, ld, codes, scales, la, st);
+  } else {
+    if ((M + 15) / 16 >= 256) return launch_qw<FMT, NCB, 8>(M, K, X, si, ld, codes, scales, la, st);
+    return launch_qw<FMT, NCB, 16>(M, K, X, si, ld, codes, scales, la, st);
+  }
 }
 
 template <int FMT>

@@ -94,6 +94,25 @@ def test_quantize_act_full_size(P, name, fmt):
     assert rel_l2(host(la), oracle.lora_act_ref(p["X"], p["lora_down"])) <= LORA_TOL
 
 
+@pytest.mark.parametrize("fmt", ["int4_g64", "fp4_b32"])
+@pytest.mark.parametrize("M,K,r", [
+    (48, 40960, 32),    # smooth_inv beyond the LDS budget: the global-load variant
+    (37, 2048, 128),    # rank 128: the 4-wave variant, ragged rows
+    (300, 1024, 48),    # rank 48: 8 waves, ragged last workgroup
+    (4096, 512, 16),    # 256 workgroups: 8 waves per workgroup
+])
+def test_quantize_act_shapes(P, fmt, M, K, r):
+    rng = np.random.default_rng(11)
+    X = (rng.standard_normal((M, K)) * 2.0).astype(np.float16)
+    si = np.exp(rng.normal(0.0, 0.3, K)).astype(np.float32)
+    ld = (rng.standard_normal((r, K)) * 0.02).astype(np.float16)
+    _, packed_ref, scales_ref = oracle.quantize_act_ref(X, si, fmt)
+    codes, scales, la = P.svdq_quantize_act(dev(X), dev(si), dev(ld), fmt)
+    assert np.array_equal(host(codes), packed_ref)
+    assert scales_equal(host(scales), scales_ref, fmt)
+    assert rel_l2(host(la), oracle.lora_act_ref(X, ld)) <= LORA_TOL
+
+
 def _adversarial_x(fmt, K=512, M=64, seed=3):
     """Rows built to hit the quantizer's edge cases exactly."""
     rng = np.random.default_rng(seed)
