@@ -18,7 +18,9 @@ around every launch in the timed region.
 
 Options: --gpus N (only 1 is supported: one GPU), --steps K, --warmup W,
 --workload {qkv,mlp_up,mlp_down,mlp_down_m1024,attn_out,mlp_up_int4,block},
---no-cpu-baseline, --warm (no buffer rotation).
+--no-cpu-baseline, --warm (no buffer rotation), --prewarm-ms T (untimed steps
+for T ms before the W warm-up steps, default 150: after idle the clocks need
+tens of ms of load to settle, and a short warm-up would time the ramp).
 """
 from __future__ import annotations
 
@@ -50,6 +52,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--warm", action="store_true", help="no buffer rotation (cache-warm)")
     ap.add_argument("--rank", type=int, default=None, help="override the low-rank width")
+    ap.add_argument("--prewarm-ms", type=float, default=150.0,
+                    help="untimed steps for this long before the warm-up steps: the GPU's clocks "
+                         "take tens of ms of sustained load to settle after idle")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the timed region, run one plain device copy of this many MiB "
                          "(the reference kernel for scaling HBM byte counters)")
@@ -175,6 +180,16 @@ def main():
         if events is not None:
             events[j + 1].record(stream)
 
+    # clocks ramp for tens of ms under load after idle: run untimed steps for
+    # --prewarm-ms of wall time (synchronizing every 8 steps so the host clock
+    # follows the GPU), then the W warm-up steps
+    t_end = time.perf_counter() + args.prewarm_ms * 1e-3
+    i = 0
+    while time.perf_counter() < t_end:
+        step(i)
+        i += 1
+        if i % 8 == 0:
+            torch.cuda.synchronize()
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()

@@ -28,11 +28,14 @@
 // (hi = w & 0xF0F0F0F0, lo = (w << 4) & 0xF0F0F0F0), so the int32 result is
 // 256 sum q_x q_w exactly. Two v_mfma_i32_32x32x32_i8 give one group's
 // partial P. The int32 accumulation starts from the bit pattern of 1.5 * 2^23,
-// so the result read as fp32 is exactly 1.5*2^23 + 256 P; one fma with
-// s_w 2^-8 and the exact constant -1.5*2^23 s_w 2^-8 yields fl(P s_w) with no
-// int-to-float convert, and a second fma adds s_x times that to the fp32
-// accumulator: two VALU ops per output and group. A and B use the same
-// permutation of k inside the instruction, which a dot product does not see.
+// so the result read as fp32 is exactly 1.5*2^23 + 256 P; one fma with the
+// fp16 s_w (read as is by v_fma_mix) and the exact constant -1.5*2^23 s_w
+// yields fl(256 P s_w) = 256 fl(P s_w) with no int-to-float convert, and a
+// second fma adds s_x times that to the fp32 accumulator: two VALU ops per
+// output and group. The accumulators therefore hold 256 times the sum (the
+// low-rank start is scaled to match); the epilogue's multiply by 2^-8 is exact.
+// A and B use the same permutation of k inside the instruction, which a dot
+// product does not see.
 //
 // FP4_E2M1_B32: the packed codes are the operands of
 // v_mfma_scale_f32_32x32x64_f8f6f4 as they are (lane l: row l%32, k
@@ -239,6 +242,14 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restr
     }
   }
 
+  if constexpr (FMT == 0) {
+    // the INT4 main loop accumulates 256 times the sum (exact power of two)
+#pragma unroll
+    for (int i = 0; i < RB4; ++i)
+#pragma unroll
+      for (int j = 0; j < CB4; ++j) acc4[i][j] *= 256.0f;
+  }
+
   // LDS read offsets (within a stage) of this lane's operand rows
   int arow[WM], brow[WN];
 #pragma unroll
@@ -291,11 +302,9 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restr
         }
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
-          // sw' = s_w 2^-8 (the 16 x 16 nibble shift) and -1.5*2^23 sw' (exact:
-          // s_w has 11 significant bits, 3 s_w at most 13)
+          // -1.5*2^23 s_w is exact: s_w has 11 significant bits, 3 s_w at most 13
           const v2h hw = __builtin_bit_cast(v2h, sww[cb]);
-          const float swp = (float)hw[g] * 0.00390625f;
-          const float swm = swp * -12582912.0f;
+          const float swm = (float)hw[g] * -12582912.0f;
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb) {
             // int32 accumulation starts at the bit pattern of 1.5 * 2^23, so the
@@ -304,8 +313,8 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restr
             const uint32_t wx[4] = {sxw[rb].x, sxw[rb].y, sxw[rb].z, sxw[rb].w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              // t = fl(P s_w): one rounding of (1.5*2^23 + 256 P) sw' - 1.5*2^23 sw'
-              const float t = fmaf(__int_as_float(p[i]), swp, swm);
+              // t = fl(256 P s_w): one rounding of (1.5*2^23 + 256 P) s_w - 1.5*2^23 s_w
+              const float t = fmaf(__int_as_float(p[i]), (float)hw[g], swm);
               const v2h hx = __builtin_bit_cast(v2h, wx[i]);
               acc4[rb][cb][i] = fmaf(t, (float)hx[g], acc4[rb][cb][i]);
             }
@@ -361,7 +370,7 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restr
       for (int rb = 0; rb < RB4; ++rb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float yv = acc4[rb][cb][i] + bn;
+          float yv = fmaf(acc4[rb][cb][i], 0.00390625f, bn);   // exact 2^-8, then + bias
           if (EPI == 1) yv = gelu_tanh_f32(yv);
           tile[(wm * 32 * WM + rb * 16 + lq * 4 + i) * TP + nl] = __float2half_rn(yv);
         }
