@@ -8,236 +8,201 @@
 // HBM-bound: every weight byte is read once. Dequantization uses the fp16
 // bit trick: (word >> 4j) & 0x000F000F | 0x64006400 is the packed fp16 pair
 // (1024 + q_j, 1024 + q_{j+4}), exact, and v_dot2_f32_f16 accumulates
-// x (1024 + q) in fp32 against x stored as pairs (x_j, x_{j+4}). Per group,
-//   sum x (q - z) = sum x (1024 + q) - (1024 + z) sum x,
-// with the second term one fma from the precomputed sum of x, so any fp16
-// zero point works.
+// x (1024 + q) in fp32 against x stored as pairs (x_j, x_{j+4}). Per 32-code
+// chunk, sum x (q - z) = sum x (1024 + q) - (1024 + z) sum x, with the second
+// term one fma from the precomputed chunk sum of x, so any fp16 zero point
+// works.
 //
-// Main kernel (M * ceil(K / 4096) <= 4): one lane owns one 64-wide group of
-// every row it visits (two 16-byte code loads, one scale, one zero); its
-// x values stay in registers for the whole kernel; a wave handles 8 rows and
-// issues all their loads before any arithmetic. Fallback kernel for larger
-// M * K: x staged in LDS, a lane owns 16-code chunks.
+// Work split: one 8-wave workgroup per CU; wave w of the grid owns the
+// contiguous rows [w N / W, (w + 1) N / W) (W waves in all), so every CU streams
+// the same number of bytes. The rows of a wave are contiguous in memory and
+// are read as a stream of units of 64 chunks of 16 bytes (lane l takes chunk
+// l of the unit): each load instruction covers 1 KB of whole cache lines, and
+// a ring of units keeps several in flight. x and its chunk sums sit in LDS. A
+// row's lane partials are summed with lane swaps and DPP at its last unit.
+#include <atomic>
+
 #include "common.hpp"
 
 namespace svdq {
 
-constexpr int kGemvWaves = 4;
+constexpr int kGemvWaves = 8;   // waves per workgroup
+constexpr int kGemvRing = 6;    // units in flight per wave
 
-// ----------------------------------------------------------------- main --
-template <int MR, int GPL, int RPW>
-__global__ __launch_bounds__(256)
-void awq_gemv_reg_kernel(const __half* __restrict__ x, const uint8_t* __restrict__ codes,
-                         const __half* __restrict__ scales, const __half* __restrict__ zeros,
-                         __half* __restrict__ y, int N, int K) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int G = K >> 6;
-  const int nbase = (blockIdx.x * kGemvWaves + wave) * RPW;
-
-  // issue every weight load of the wave's rows first
-  uint4 cw[RPW][GPL][2];
-  float sv[RPW][GPL], zv[RPW][GPL];
-#pragma unroll
-  for (int rr = 0; rr < RPW; ++rr)
-#pragma unroll
-    for (int j = 0; j < GPL; ++j) {
-      const int n = nbase + rr, g = lane + 64 * j;
-      if (n < N && g < G) {
-        const uint4* pc = reinterpret_cast<const uint4*>(codes + (size_t)n * (K >> 1) + g * 32);
-        cw[rr][j][0] = pc[0];
-        cw[rr][j][1] = pc[1];
-        sv[rr][j] = __half2float(scales[(size_t)n * G + g]);
-        zv[rr][j] = __half2float(zeros[(size_t)n * G + g]);
-      } else {
-        cw[rr][j][0] = make_uint4(0, 0, 0, 0);
-        cw[rr][j][1] = make_uint4(0, 0, 0, 0);
-        sv[rr][j] = 0.f;
-        zv[rr][j] = 0.f;
-      }
-    }
-
-  // x of this lane's groups as (x_j, x_{j+4}) pairs, and their sums
-  uint32_t xp[MR][GPL][32];
-  float xsum[MR][GPL];
-#pragma unroll
-  for (int m = 0; m < MR; ++m)
-#pragma unroll
-    for (int j = 0; j < GPL; ++j) {
-      const int g = lane + 64 * j;
-      float sum = 0.f;
-#pragma unroll
-      for (int seg = 0; seg < 8; ++seg) {
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (g < G) v = reinterpret_cast<const uint4*>(x + (size_t)m * K + g * 64)[seg];
-        xp[m][j][seg * 4 + 0] = (v.x & 0xFFFFu) | (v.z << 16);
-        xp[m][j][seg * 4 + 1] = (v.x >> 16) | (v.z & 0xFFFF0000u);
-        xp[m][j][seg * 4 + 2] = (v.y & 0xFFFFu) | (v.w << 16);
-        xp[m][j][seg * 4 + 3] = (v.y >> 16) | (v.w & 0xFFFF0000u);
-        const v2h one = {(_Float16)1.0f, (_Float16)1.0f};
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          sum = __builtin_amdgcn_fdot2(__builtin_bit_cast(v2h, xp[m][j][seg * 4 + e]), one, sum, false);
-      }
-      xsum[m][j] = sum;
-    }
-
-#pragma unroll
-  for (int rr = 0; rr < RPW; ++rr) {
-    float acc[MR];
-#pragma unroll
-    for (int m = 0; m < MR; ++m) acc[m] = 0.f;
-#pragma unroll
-    for (int j = 0; j < GPL; ++j) {
-      const uint32_t w[8] = {cw[rr][j][0].x, cw[rr][j][0].y, cw[rr][j][0].z, cw[rr][j][0].w,
-                             cw[rr][j][1].x, cw[rr][j][1].y, cw[rr][j][1].z, cw[rr][j][1].w};
-      float part[MR];
-#pragma unroll
-      for (int m = 0; m < MR; ++m) part[m] = 0.f;
-#pragma unroll
-      for (int wi = 0; wi < 8; ++wi)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const uint32_t hb = ((w[wi] >> (4 * jj)) & 0x000F000Fu) | 0x64006400u;
-#pragma unroll
-          for (int m = 0; m < MR; ++m)
-            part[m] = __builtin_amdgcn_fdot2(__builtin_bit_cast(v2h, hb),
-                                             __builtin_bit_cast(v2h, xp[m][j][wi * 4 + jj]), part[m], false);
-        }
-#pragma unroll
-      for (int m = 0; m < MR; ++m)
-        acc[m] = fmaf(sv[rr][j], fmaf(-(1024.0f + zv[rr][j]), xsum[m][j], part[m]), acc[m]);
-    }
-    const int n = nbase + rr;
-#pragma unroll
-    for (int m = 0; m < MR; ++m) {
-      float v = acc[m];
-      v = lane_sum_xor(v, 32);
-      v = lane_sum_xor(v, 16);
-      v = lane_sum_xor(v, 8);
-      v = lane_sum_xor(v, 4);
-      v = lane_sum_xor(v, 2);
-      v = lane_sum_xor(v, 1);
-      if (lane == 0 && n < N) y[(size_t)m * N + n] = __float2half_rn(v);
-    }
-  }
+// Sum over the 64 lanes; every lane gets the same total (a fixed order: the
+// xor-32 and xor-16 partners via v_permlane32/16_swap, then within each 16-lane
+// row the mirror, half-mirror and two quad permutations of DPP).
+__device__ __forceinline__ float wave_sum(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));  // row_mirror
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+  return v;
 }
 
-// ------------------------------------------------------------- fallback --
-constexpr int kRowsPerWave = 4;
-
 template <int MR>
-__global__ __launch_bounds__(256)
+__global__ __launch_bounds__(64 * kGemvWaves)
 void awq_gemv_kernel(const __half* __restrict__ x, const uint8_t* __restrict__ codes,
                      const __half* __restrict__ scales, const __half* __restrict__ zeros,
                      __half* __restrict__ y, int N, int K) {
-  extern __shared__ uint32_t xs[];  // [MR][K/8 segments][4 pairs]
-  const int segs = K >> 3;
-  for (int idx = threadIdx.x; idx < MR * segs; idx += blockDim.x) {
-    const int m = idx / segs, sg = idx - m * segs;
-    const uint4 v = *reinterpret_cast<const uint4*>(x + (size_t)m * K + sg * 8);
-    uint32_t* o = xs + (size_t)idx * 4;
-    o[0] = (v.x & 0xFFFFu) | (v.z << 16);
-    o[1] = (v.x >> 16) | (v.z & 0xFFFF0000u);
-    o[2] = (v.y & 0xFFFFu) | (v.w << 16);
-    o[3] = (v.y >> 16) | (v.w & 0xFFFF0000u);
+  // LDS: x pairs as [m][4 segments of a chunk][chunk][4 pairs] (for a fixed
+  // segment, consecutive chunks are 16 bytes apart: conflict-free reads), then
+  // the chunk sums of x [m][chunk]
+  extern __shared__ uint32_t lds[];
+  const int nch = K >> 5;                 // 32-code chunks per row (16 bytes each)
+  const int G = K >> 6;
+  uint32_t* xs = lds;
+  float* xc = reinterpret_cast<float*>(lds + (size_t)MR * nch * 16);
+  const int tid = threadIdx.x;
+  for (int idx = tid; idx < MR * nch * 4; idx += 64 * kGemvWaves) {
+    // idx = (m nch + c) 4 + e: segment e of chunk c = channels 32 c + 8 e .. +8
+    const int e = idx & 3, mc = idx >> 2;
+    const int m = mc / nch, c = mc - m * nch;
+    const uint4 v = *reinterpret_cast<const uint4*>(x + (size_t)m * K + (size_t)c * 32 + e * 8);
+    uint32_t* o = xs + (((size_t)m * 4 + e) * nch + c) * 4;
+    o[0] = (v.x & 0xFFFFu) | (v.z << 16);          // (x_0, x_4)
+    o[1] = (v.x >> 16) | (v.z & 0xFFFF0000u);      // (x_1, x_5)
+    o[2] = (v.y & 0xFFFFu) | (v.w << 16);          // (x_2, x_6)
+    o[3] = (v.y >> 16) | (v.w & 0xFFFF0000u);      // (x_3, x_7)
+  }
+  __syncthreads();
+  const v2h one = {(_Float16)1.0f, (_Float16)1.0f};
+  for (int mc = tid; mc < MR * nch; mc += 64 * kGemvWaves) {
+    const int m = mc / nch, c = mc - m * nch;
+    float sum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        sum = __builtin_amdgcn_fdot2(__builtin_bit_cast(v2h, xs[(((size_t)m * 4 + e) * nch + c) * 4 + j]), one,
+                                     sum, false);
+    xc[mc] = sum;
   }
   __syncthreads();
 
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int nbase = (blockIdx.x * kGemvWaves + wave) * kRowsPerWave;
-  const int chunks = K >> 4;        // 16 codes (8 bytes) per chunk
-  const int gstride = K >> 6;
-  const v2h one = {(_Float16)1.0f, (_Float16)1.0f};
+  const int lane = tid & 63, wave = tid >> 6;
+  const long long W = (long long)gridDim.x * kGemvWaves;
+  const long long wg = (long long)blockIdx.x * kGemvWaves + wave;
+  const int r0 = (int)(wg * N / W), r1 = (int)((wg + 1) * N / W);
+  if (r1 <= r0) return;
+  const int nseg = (nch + 63) >> 6;       // units per row
+  const int nunits = (r1 - r0) * nseg;
 
-  for (int rr = 0; rr < kRowsPerWave; ++rr) {
-    const int n = nbase + rr;
-    if (n >= N) break;
-    const uint8_t* crow = codes + (size_t)n * (K >> 1);
-    float acc[MR];
+  struct Unit {
+    uint4 w;
+    __half s, z;
+  };
+  // Loads are unconditional: past the wave's last unit they re-read it (never
+  // processed), so the compiler's count of loads in flight stays exact.
+  int lrow = r0, lseg = 0;
+  auto load_next = [&](Unit& d) {
+    const int row = min(lrow, r1 - 1);
+    const int c = min(lseg * 64 + lane, nch - 1);
+    d.w = *reinterpret_cast<const uint4*>(codes + (size_t)row * (K >> 1) + (size_t)c * 16);
+    d.s = scales[(size_t)row * G + (c >> 1)];
+    d.z = zeros[(size_t)row * G + (c >> 1)];
+    if (++lseg == nseg) {
+      lseg = 0;
+      ++lrow;
+    }
+  };
+
+  // Row totals are collected in registers (row i of the wave in lane i; the
+  // grid gives no wave more than 64 rows) and written after the loop: a store
+  // on one path only would leave the compiler unsure how many loads are in
+  // flight and drain the ring at every row.
+  float acc[MR], out[MR];
 #pragma unroll
-    for (int m = 0; m < MR; ++m) acc[m] = 0.f;
-    for (int c = lane; c < chunks; c += 64) {
-      const uint2 w = *reinterpret_cast<const uint2*>(crow + (size_t)c * 8);
-      const int g = c >> 2;
-      const float s = __half2float(scales[(size_t)n * gstride + g]);
-      const float zb = 1024.0f + __half2float(zeros[(size_t)n * gstride + g]);
-      float part[MR], sum[MR];
+  for (int m = 0; m < MR; ++m) acc[m] = out[m] = 0.f;
+  int prow = r0, pseg = 0;
+  auto process = [&](const Unit& d) {
+    const int c = pseg * 64 + lane;
+    if (c < nch) {
+      const uint32_t w[4] = {d.w.x, d.w.y, d.w.z, d.w.w};
+      const float s = __half2float(d.s);
+      const float zb = 1024.0f + __half2float(d.z);
 #pragma unroll
-      for (int m = 0; m < MR; ++m) part[m] = sum[m] = 0.f;
+      for (int m = 0; m < MR; ++m) {
+        float part = 0.f;
 #pragma unroll
-      for (int d = 0; d < 2; ++d) {
-        const uint32_t word = d ? w.y : w.x;
-        const int sg = 2 * c + d;
+        for (int e = 0; e < 4; ++e) {
+          const uint4 xp = *reinterpret_cast<const uint4*>(xs + (((size_t)m * 4 + e) * nch + c) * 4);
+          const uint32_t xv[4] = {xp.x, xp.y, xp.z, xp.w};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t hb = ((word >> (4 * j)) & 0x000F000Fu) | 0x64006400u;
-#pragma unroll
-          for (int m = 0; m < MR; ++m) {
-            const v2h xp = __builtin_bit_cast(v2h, xs[((size_t)m * segs + sg) * 4 + j]);
-            part[m] = __builtin_amdgcn_fdot2(__builtin_bit_cast(v2h, hb), xp, part[m], false);
-            sum[m] = __builtin_amdgcn_fdot2(one, xp, sum[m], false);
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t hb = ((w[e] >> (4 * j)) & 0x000F000Fu) | 0x64006400u;
+            part = __builtin_amdgcn_fdot2(__builtin_bit_cast(v2h, hb), __builtin_bit_cast(v2h, xv[j]), part, false);
           }
         }
+        acc[m] = fmaf(s, fmaf(-zb, xc[m * nch + c], part), acc[m]);
       }
-#pragma unroll
-      for (int m = 0; m < MR; ++m) acc[m] = fmaf(s, fmaf(-zb, sum[m], part[m]), acc[m]);
     }
+    if (++pseg == nseg) {   // the row is complete
+      const int slot = prow - r0;
 #pragma unroll
-    for (int m = 0; m < MR; ++m) {
-      float v = acc[m];
-      v = lane_sum_xor(v, 32);
-      v = lane_sum_xor(v, 16);
-      v = lane_sum_xor(v, 8);
-      v = lane_sum_xor(v, 4);
-      v = lane_sum_xor(v, 2);
-      v = lane_sum_xor(v, 1);
-      if (lane == 0) y[(size_t)m * N + n] = __float2half_rn(v);
+      for (int m = 0; m < MR; ++m) {
+        const float t = wave_sum(acc[m]);
+        out[m] = (lane == slot) ? t : out[m];
+        acc[m] = 0.f;
+      }
+      pseg = 0;
+      ++prow;
     }
+  };
+
+  Unit d[kGemvRing];
+#pragma unroll
+  for (int i = 0; i < kGemvRing - 1; ++i) load_next(d[i]);
+  for (int u0 = 0; u0 < nunits; u0 += kGemvRing) {
+#pragma unroll
+    for (int i = 0; i < kGemvRing; ++i) {
+      load_next(d[(i + kGemvRing - 1) % kGemvRing]);
+      if (u0 + i < nunits) process(d[i]);
+    }
+  }
+  if (lane < r1 - r0) {
+#pragma unroll
+    for (int m = 0; m < MR; ++m) y[(size_t)m * N + r0 + lane] = __float2half_rn(out[m]);
   }
 }
 
-template <int MR, int GPL>
-static hipError_t launch_reg(int N, int K, const void* x, const uint8_t* q, const void* s,
-                             const void* z, void* y, hipStream_t st) {
-  constexpr int RPW = 8;
-  const int rows_per_block = kGemvWaves * RPW;
-  const dim3 grid((N + rows_per_block - 1) / rows_per_block), block(64 * kGemvWaves);
-  hipLaunchKernelGGL((awq_gemv_reg_kernel<MR, GPL, RPW>), grid, block, 0, st, (const __half*)x, q,
-                     (const __half*)s, (const __half*)z, (__half*)y, N, K);
-  return hipGetLastError();
-}
-
 template <int MR>
-static hipError_t launch_lds(int N, int K, const void* x, const uint8_t* q, const void* s,
-                             const void* z, void* y, hipStream_t st) {
-  const int rows_per_block = kGemvWaves * kRowsPerWave;
-  const dim3 grid((N + rows_per_block - 1) / rows_per_block), block(64 * kGemvWaves);
-  const size_t lds = (size_t)MR * K * sizeof(__half);
-  hipLaunchKernelGGL((awq_gemv_kernel<MR>), grid, block, lds, st, (const __half*)x, q,
+static hipError_t launch_mr(int N, int K, const void* x, const uint8_t* q, const void* s,
+                            const void* z, void* y, hipStream_t st) {
+  // about one workgroup per CU for large N, at least ~4 rows per wave for small
+  // N, and never more than 64 rows per wave (the kernel keeps one row per lane)
+  const int rows_cap = kGemvWaves * 64;
+  const int grid = max(max(1, min(256, (N + 8 * 4 - 1) / (8 * 4))), (N + rows_cap - 1) / rows_cap);
+  const size_t lds = (size_t)MR * (K >> 5) * 16 * sizeof(uint32_t) + (size_t)MR * (K >> 5) * sizeof(float);
+  if (lds > 65536) {   // M K = 32768 needs 68 KB
+    static std::atomic<int> raised{0};
+    if (!raised.load(std::memory_order_acquire)) {
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&awq_gemv_kernel<MR>),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, 72 * 1024);
+      if (e != hipSuccess) return e;
+      raised.store(1, std::memory_order_release);
+    }
+  }
+  hipLaunchKernelGGL((awq_gemv_kernel<MR>), dim3(grid), dim3(64 * kGemvWaves), lds, st, (const __half*)x, q,
                      (const __half*)s, (const __half*)z, (__half*)y, N, K);
   return hipGetLastError();
 }
 
 hipError_t launch_awq_gemv(int M, int N, int K, const void* x, const uint8_t* q, const void* s,
                            const void* z, void* y, hipStream_t st) {
-  const int gpl = ((K >> 6) + 63) / 64;
-  if (M * gpl <= 4) {
-#define SVDQ_REG(MR_, GPL_) if (M == MR_ && gpl == GPL_) return launch_reg<MR_, GPL_>(N, K, x, q, s, z, y, st)
-    SVDQ_REG(1, 1); SVDQ_REG(1, 2); SVDQ_REG(1, 3); SVDQ_REG(1, 4);
-    SVDQ_REG(2, 1); SVDQ_REG(2, 2); SVDQ_REG(3, 1); SVDQ_REG(4, 1);
-#undef SVDQ_REG
-  }
   switch (M) {
-    case 1: return launch_lds<1>(N, K, x, q, s, z, y, st);
-    case 2: return launch_lds<2>(N, K, x, q, s, z, y, st);
-    case 3: return launch_lds<3>(N, K, x, q, s, z, y, st);
-    case 4: return launch_lds<4>(N, K, x, q, s, z, y, st);
-    case 5: return launch_lds<5>(N, K, x, q, s, z, y, st);
-    case 6: return launch_lds<6>(N, K, x, q, s, z, y, st);
-    case 7: return launch_lds<7>(N, K, x, q, s, z, y, st);
-    default: return launch_lds<8>(N, K, x, q, s, z, y, st);
+    case 1: return launch_mr<1>(N, K, x, q, s, z, y, st);
+    case 2: return launch_mr<2>(N, K, x, q, s, z, y, st);
+    case 3: return launch_mr<3>(N, K, x, q, s, z, y, st);
+    case 4: return launch_mr<4>(N, K, x, q, s, z, y, st);
+    case 5: return launch_mr<5>(N, K, x, q, s, z, y, st);
+    case 6: return launch_mr<6>(N, K, x, q, s, z, y, st);
+    case 7: return launch_mr<7>(N, K, x, q, s, z, y, st);
+    default: return launch_mr<8>(N, K, x, q, s, z, y, st);
   }
 }
 
