@@ -42,3 +42,4 @@ from .svdq import (  # noqa: F401
     dense_ref,
 )
 from .awq import awq_prep, awq_dequantize, gemv_ref  # noqa: F401
+from .qkv import rms_norm_heads, rope_pairs, qkv_epilogue_ref  # noqa: F401
