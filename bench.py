@@ -17,7 +17,7 @@ Per-kernel durations come from HIP events recorded on the launch stream
 around every launch in the timed region.
 
 Options: --gpus N (only 1 is supported: one GPU), --steps K, --warmup W,
---workload {qkv,mlp_up,mlp_down,mlp_down_m1024,attn_out,mlp_up_int4,block},
+--workload {qkv,qkv_normrope,mlp_up,mlp_down,mlp_down_m1024,attn_out,mlp_up_int4,block},
 --no-cpu-baseline, --warm (no buffer rotation), --prewarm-ms T (untimed steps
 for T ms before the W warm-up steps, default 150: after idle the clocks need
 tens of ms of load to settle, and a short warm-up would time the ramp).
@@ -47,8 +47,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="qkv",
-                    choices=["qkv", "mlp_up", "mlp_down", "mlp_down_m1024", "attn_out",
-                             "mlp_up_int4", "block"])
+                    choices=["qkv", "qkv_normrope", "mlp_up", "mlp_down", "mlp_down_m1024",
+                             "attn_out", "mlp_up_int4", "block"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--warm", action="store_true", help="no buffer rotation (cache-warm)")
     ap.add_argument("--rank", type=int, default=None, help="override the low-rank width")
@@ -151,6 +151,9 @@ def main():
             L["scales"] = torch.empty((cfg.M, scols), dtype=sdt, device=dev)
             L["lora_act"] = torch.empty((cfg.M, r), dtype=torch.float16, device=dev) if r else None
             L["Y"] = torch.empty((cfg.M, cfg.N), dtype=torch.float16, device=dev)
+            if cfg.epilogue == "qkv_norm_rope":
+                e = synth.qkv_epilogue_inputs(cfg.M, seed=0)
+                L["qk_norm_w"], L["rope"], L["eps"] = t(e["qk_norm_w"]), t(e["rope"]), e["eps"]
             layers.append(L)
         G = {"x": t(gp["x"]), "codes": t(gp["codes"]), "scales": t(gp["scales"]),
              "zeros": t(gp["zeros"]), "y": torch.empty((1, gcfg.N), dtype=torch.float16, device=dev)}
@@ -171,8 +174,13 @@ def main():
                                 L["codes"], L["scales"], L["lora_act"])
             if events is not None:
                 events[j + 1].record(stream)
-            P.svdq_gemm_w4a4(L["codes"], L["scales"], L["lora_act"], L["w_codes"], L["w_scales"],
-                             L["lora_up"], L["bias"], cfg.fmt, cfg.epilogue, out=L["Y"])
+            if cfg.epilogue == "qkv_norm_rope":
+                P.svdq_gemm_w4a4_qkv(L["codes"], L["scales"], L["lora_act"], L["w_codes"], L["w_scales"],
+                                     L["lora_up"], L["bias"], L["qk_norm_w"], L["rope"], L["eps"],
+                                     out=L["Y"])
+            else:
+                P.svdq_gemm_w4a4(L["codes"], L["scales"], L["lora_act"], L["w_codes"], L["w_scales"],
+                                 L["lora_up"], L["bias"], cfg.fmt, cfg.epilogue, out=L["Y"])
             j += 2
         if events is not None:
             events[j].record(stream)
@@ -237,7 +245,8 @@ def main():
             "alg_bytes": qb, "GB/s": round(qb / (qms * 1e-3) / 1e9, 1),
             "frac_hbm": round(qb / (qms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
         tops = ops / (gms * 1e-3) / 1e12
-        kernels[f"{cfg.name}.svdq_gemm_w4a4"] = {
+        gname = "svdq_gemm_w4a4_qkv" if cfg.epilogue == "qkv_norm_rope" else "svdq_gemm_w4a4"
+        kernels[f"{cfg.name}.{gname}"] = {
             "avg_us": round(gms * 1e3, 2), "median_us": round(med_ms[2 * li + 1] * 1e3, 2),
             "alg_ops": ops, "lowrank_ops": 2.0 * cfg.M * cfg.N * r + 2.0 * cfg.M * cfg.K * r,
             "TOPS": round(tops, 1), "frac_peak": round(tops / PEAK_TOPS[cfg.fmt], 4),

@@ -13,6 +13,7 @@ from .ops import (  # noqa: F401
     lib,
     svdq_device_check,
     svdq_gemm_w4a4,
+    svdq_gemm_w4a4_qkv,
     svdq_linear,
     svdq_quantize_act,
     svdq_status_str,

@@ -120,6 +120,31 @@ int svdq_gemm_w4a4(int fmt, int M, int N, int K, int r, const uint8_t* act_codes
                                        w_scales, lora_up, bias, epi, Y, (hipStream_t)stream));
 }
 
+int svdq_gemm_w4a4_qkv(int fmt, int M, int N, int K, int r, const uint8_t* act_codes,
+                       const void* act_scales, const void* lora_act, const uint8_t* w_codes,
+                       const void* w_scales, const void* lora_up, const void* bias,
+                       const void* qk_norm_w, const float* rope, float eps, void* Y, void* stream) {
+  if (fmt != SVDQ_INT4_G64) return SVDQ_ERR_INVALID_ARG;
+  if (!(eps >= 0.0f) || eps > 1.0f) return SVDQ_ERR_INVALID_ARG;   // also rejects NaN
+  if (M < 0 || M > (1 << 23) || N < 384 || N > 65536 || (N % 384) != 0 || !k_ok(K) || !rank_ok(r))
+    return SVDQ_ERR_SHAPE;
+  if (M == 0) return SVDQ_OK;
+  if (!act_codes || !act_scales || !w_codes || !w_scales || !Y || !qk_norm_w || !rope)
+    return SVDQ_ERR_INVALID_ARG;
+  if (r > 0 && (!lora_act || !lora_up)) return SVDQ_ERR_INVALID_ARG;
+  if (!aligned16(act_codes) || !aligned16(act_scales) || !aligned16(w_codes) ||
+      !aligned16(w_scales) || !aligned16(Y) || (bias && !aligned16(bias)) ||
+      !aligned16(qk_norm_w) || !aligned16(rope))
+    return SVDQ_ERR_ALIGN;
+  if (r > 0 && (!aligned16(lora_act) || !aligned16(lora_up))) return SVDQ_ERR_ALIGN;
+  const int dc = check_current_device();
+  if (dc != SVDQ_OK) return dc;
+  (void)hipGetLastError();
+  const svdq::QkvEpilogue qe{qk_norm_w, rope, eps, N / 384};
+  return finish(svdq::launch_gemm_w4a4(fmt, M, N, K, r, act_codes, act_scales, lora_act, w_codes,
+                                       w_scales, lora_up, bias, 2, Y, (hipStream_t)stream, &qe));
+}
+
 int awq_gemv_w4a16(int M, int N, int K, int group, const void* x, const uint8_t* w_codes,
                    const void* scales, const void* zeros, void* y, void* stream) {
   if (group != 64) return SVDQ_ERR_SHAPE;

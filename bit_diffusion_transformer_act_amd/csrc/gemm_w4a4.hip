@@ -83,7 +83,7 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restr
                       const __half* __restrict__ lora_act, const uint8_t* __restrict__ w_codes,
                       const void* __restrict__ w_scales, const __half* __restrict__ lora_up,
                       const __half* __restrict__ bias, __half* __restrict__ Y,
-                      int M, int N, int K, int r) {
+                      int M, int N, int K, int r, QkvEpilogue qe) {
   using S = GemmShape<WM, WN, STAGES>;
   constexpr int BM = S::BM, BN = S::BN;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -362,6 +362,14 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restr
   __half* tile = reinterpret_cast<__half*>(smem);
   if constexpr (FMT == 0) {
     const int l16 = lane & 15, lq = lane >> 4;
+    // the fused QKV epilogue applies to the Q and K thirds (a tile is one head:
+    // BN == 128); the block-uniform test keeps every barrier below uniform
+    bool normrope = false;
+    if constexpr (EPI == 2) {
+      static_assert(BN == 128, "the QKV epilogue needs one 128-channel head per tile");
+      normrope = (n0 / BN) < 2 * qe.heads;
+    }
+    float yv[RB4][CB4][4];
 #pragma unroll
     for (int cb = 0; cb < CB4; ++cb) {
       const int nl = wn * 32 * WN + cb * 16 + l16;
@@ -370,10 +378,60 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restr
       for (int rb = 0; rb < RB4; ++rb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float yv = fmaf(acc4[rb][cb][i], 0.00390625f, bn);   // exact 2^-8, then + bias
-          if (EPI == 1) yv = gelu_tanh_f32(yv);
-          tile[(wm * 32 * WM + rb * 16 + lq * 4 + i) * TP + nl] = __float2half_rn(yv);
+          float v = fmaf(acc4[rb][cb][i], 0.00390625f, bn);   // exact 2^-8, then + bias
+          if (EPI == 1) v = gelu_tanh_f32(v);
+          yv[rb][cb][i] = v;
         }
+    }
+    if constexpr (EPI == 2) {
+      if (normrope) {
+        // RMSNorm over the head's 128 channels: this lane's 4 columns, then the
+        // 16 lanes of its 16-lane row (DPP), then the two waves of the row pair
+        // through LDS (summed in a fixed order, so both see the same total)
+        float* red = reinterpret_cast<float*>(smem + BM * TP * 2);   // [WM][2 waves][64 rows]
+#pragma unroll
+        for (int rb = 0; rb < RB4; ++rb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float ss = 0.f;
+#pragma unroll
+            for (int cb = 0; cb < CB4; ++cb) ss = fmaf(yv[rb][cb][i], yv[rb][cb][i], ss);
+            ss = row16_sum(ss);
+            if (l16 == 0) red[(wm * 2 + wn) * 64 + rb * 16 + lq * 4 + i] = ss;
+          }
+        __syncthreads();
+        const int part = (n0 / BN) / qe.heads;   // 0: Q, 1: K
+        const __half* nw = reinterpret_cast<const __half*>(qe.qk_norm_w) + part * BN;
+#pragma unroll
+        for (int rb = 0; rb < RB4; ++rb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int rl = rb * 16 + lq * 4 + i;
+            const float tot = red[(wm * 2 + 0) * 64 + rl] + red[(wm * 2 + 1) * 64 + rl];
+            const float inv = __builtin_amdgcn_rsqf(fmaf(tot, 1.0f / 128.0f, qe.eps));
+            const int m = min(m0 + wm * 32 * WM + rl, M - 1);
+#pragma unroll
+            for (int cb = 0; cb < CB4; ++cb) {
+              const int d = wn * 32 * WN + cb * 16 + l16;   // channel within the head
+              const float v = yv[rb][cb][i] * inv * __half2float(nw[d]);
+              // partner channel d ^ 1 sits in lane ^ 1 (columns are lanes)
+              const float pv = __int_as_float(
+                  __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+              const float2 cs = *reinterpret_cast<const float2*>(qe.rope + ((size_t)m * 64 + (d >> 1)) * 2);
+              // (a, b) -> (a cos - b sin, a sin + b cos)
+              yv[rb][cb][i] = (d & 1) ? fmaf(pv, cs.y, v * cs.x) : fmaf(-pv, cs.y, v * cs.x);
+            }
+          }
+      }
+    }
+#pragma unroll
+    for (int cb = 0; cb < CB4; ++cb) {
+      const int nl = wn * 32 * WN + cb * 16 + l16;
+#pragma unroll
+      for (int rb = 0; rb < RB4; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          tile[(wm * 32 * WM + rb * 16 + lq * 4 + i) * TP + nl] = __float2half_rn(yv[rb][cb][i]);
     }
   } else {
 #pragma unroll
@@ -402,7 +460,7 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restr
 template <int FMT, int EPI, int WM, int WN, int STAGES>
 static hipError_t launch_cfg(int M, int N, int K, int r, const uint8_t* ac, const void* as,
                              const void* la, const uint8_t* wc, const void* ws, const void* lu,
-                             const void* bias, void* Y, hipStream_t st) {
+                             const void* bias, void* Y, hipStream_t st, const QkvEpilogue& qe) {
   using S = GemmShape<WM, WN, STAGES>;
   auto kern = gemm_w4a4_kernel<FMT, EPI, WM, WN, STAGES>;
   if (S::LDS > 65536) {
@@ -416,15 +474,20 @@ static hipError_t launch_cfg(int M, int N, int K, int r, const uint8_t* ac, cons
   }
   const int ntiles = ((M + S::BM - 1) / S::BM) * (N / S::BN);
   hipLaunchKernelGGL(kern, dim3(ntiles), dim3(256), S::LDS, st, ac, as, (const __half*)la, wc, ws,
-                     (const __half*)lu, (const __half*)bias, (__half*)Y, M, N, K, r);
+                     (const __half*)lu, (const __half*)bias, (__half*)Y, M, N, K, r, qe);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_w4a4(int fmt, int M, int N, int K, int r, const uint8_t* ac, const void* as,
                             const void* la, const uint8_t* wc, const void* ws, const void* lu,
-                            const void* bias, int epi, void* Y, hipStream_t st) {
+                            const void* bias, int epi, void* Y, hipStream_t st, const QkvEpilogue* qkv) {
+  const QkvEpilogue qe = qkv ? *qkv : QkvEpilogue{nullptr, nullptr, 0.f, 1};
 #define SVDQ_GO(F, E, WM_, WN_, ST_) \
-  return launch_cfg<F, E, WM_, WN_, ST_>(M, N, K, r, ac, as, la, wc, ws, lu, bias, Y, st)
+  return launch_cfg<F, E, WM_, WN_, ST_>(M, N, K, r, ac, as, la, wc, ws, lu, bias, Y, st, qe)
+  if (epi == 2) {   // fused QKV epilogue: INT4 only
+    if (fmt != 0 || !qkv) return hipErrorInvalidValue;
+    SVDQ_GO(0, 2, 2, 2, 3);
+  }
   if (fmt == 0) {
     if (epi == 0) SVDQ_GO(0, 0, 2, 2, 3); else SVDQ_GO(0, 1, 2, 2, 3);
   } else {

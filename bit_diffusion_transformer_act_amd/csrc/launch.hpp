@@ -10,10 +10,21 @@ hipError_t launch_quantize_act(int fmt, int M, int K, int r, const void* X, cons
                                const void* lora_down, uint8_t* codes, void* scales, void* lora_act,
                                hipStream_t stream);
 
+// Parameters of the fused QKV epilogue (epi == 2): per-head RMSNorm of the Q
+// and K thirds of the output (heads of 128 channels, `heads` per third) with
+// weights qk_norm_w fp16 [2][128] and epsilon eps, then the rotation of channel
+// pairs (2i, 2i+1) by rope fp32 [M][64][2] (cos, sin per token and pair).
+struct QkvEpilogue {
+  const void* qk_norm_w;
+  const float* rope;
+  float eps;
+  int heads;
+};
+
 hipError_t launch_gemm_w4a4(int fmt, int M, int N, int K, int r, const uint8_t* act_codes,
                             const void* act_scales, const void* lora_act, const uint8_t* w_codes,
                             const void* w_scales, const void* lora_up, const void* bias, int epi,
-                            void* Y, hipStream_t stream);
+                            void* Y, hipStream_t stream, const QkvEpilogue* qkv = nullptr);
 
 hipError_t launch_gemm_fp4_big(int M, int N, int K, int r, const uint8_t* act_codes,
                                const void* act_scales, const void* lora_act, const uint8_t* w_codes,

@@ -31,7 +31,7 @@ SVDQ_ERR_UNSUPPORTED_DEVICE = -4
 SVDQ_ERR_HIP = -5
 
 EXPORTED_SYMBOLS = ("svdq_device_check", "svdq_status_str", "svdq_version",
-                    "svdq_quantize_act", "svdq_gemm_w4a4", "awq_gemv_w4a16")
+                    "svdq_quantize_act", "svdq_gemm_w4a4", "svdq_gemm_w4a4_qkv", "awq_gemv_w4a16")
 
 _lock = threading.Lock()
 _handle = None
@@ -64,6 +64,9 @@ def lib() -> ctypes.CDLL:
             h.svdq_quantize_act.restype = i32
             h.svdq_gemm_w4a4.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp]
             h.svdq_gemm_w4a4.restype = i32
+            h.svdq_gemm_w4a4_qkv.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                             ctypes.c_float, vp, vp]
+            h.svdq_gemm_w4a4_qkv.restype = i32
             h.awq_gemv_w4a16.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]
             h.awq_gemv_w4a16.restype = i32
             _handle = h
@@ -188,6 +191,45 @@ def svdq_gemm_w4a4(act_codes, act_scales, lora_act, w_codes, w_scales, lora_up, 
                                   _stream(dev))
     if st != SVDQ_OK:
         raise SvdqError(st, "svdq_gemm_w4a4")
+    return out
+
+
+def svdq_gemm_w4a4_qkv(act_codes, act_scales, lora_act, w_codes, w_scales, lora_up, bias,
+                       qk_norm_w, rope, eps: float = 1e-6, fmt="int4_g64", out=None):
+    """Fused Q|K|V projection: the 4-bit GEMM, then per-head (128-channel)
+    RMSNorm of the Q and K thirds and the rotation of channel pairs by rope
+    (fp32 [M][64][2] cos, sin); V unchanged -> Y fp16 [M][N], N % 384 == 0."""
+    f = _fmt(fmt)
+    dev = act_codes.device
+    if dev.type != "cuda":
+        raise ValueError("act_codes must be a HIP device tensor")
+    M, KB = act_codes.shape
+    K = 2 * KB
+    N = w_codes.shape[0]
+    r = 0 if lora_up is None else lora_up.shape[1]
+    sdt, sa_shape = _scale_spec(f, M, K)
+    _, sw_shape = _scale_spec(f, N, K)
+    _check(act_codes, "act_codes", torch.uint8, (M, KB), dev)
+    _check(act_scales, "act_scales", sdt, sa_shape, dev)
+    _check(w_codes, "w_codes", torch.uint8, (N, KB), dev)
+    _check(w_scales, "w_scales", sdt, sw_shape, dev)
+    if r > 0:
+        _check(lora_act, "lora_act", torch.float16, (M, r), dev)
+        _check(lora_up, "lora_up", torch.float16, (N, r), dev)
+    if bias is not None:
+        _check(bias, "bias", torch.float16, (N,), dev)
+    _check(qk_norm_w, "qk_norm_w", torch.float16, (2, 128), dev)
+    _check(rope, "rope", torch.float32, (M, 64, 2), dev)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=dev)
+    _check(out, "out", torch.float16, (M, N), dev)
+    with torch.cuda.device(dev):
+        st = lib().svdq_gemm_w4a4_qkv(f, M, N, K, r, _ptr(act_codes), _ptr(act_scales),
+                                      _ptr(lora_act) if r > 0 else None, _ptr(w_codes), _ptr(w_scales),
+                                      _ptr(lora_up) if r > 0 else None, _ptr(bias), _ptr(qk_norm_w),
+                                      _ptr(rope), ctypes.c_float(eps), _ptr(out), _stream(dev))
+    if st != SVDQ_OK:
+        raise SvdqError(st, "svdq_gemm_w4a4_qkv")
     return out
 
 

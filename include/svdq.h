@@ -157,6 +157,37 @@ int svdq_gemm_w4a4(int fmt, int M, int N, int K, int r,
                    const void* bias, int epi, void* Y, void* stream);
 
 /*
+ * svdq_gemm_w4a4_qkv -- svdq_gemm_w4a4 for a fused Q|K|V projection, with the
+ * per-head RMSNorm of Q and K and the rotary position embedding applied in the
+ * same epilogue (the pages' structural rewrite that fuses the QKV projection
+ * with the Q/K norm and the rotary embedding: dothoosh.com article,
+ * structural-rewrites paragraph). With lin[m,n] the svdq_gemm_w4a4 result
+ * before rounding (bias included, no activation), heads of D = 128 channels
+ * and H = N / 384 heads per third:
+ *
+ *   V third   (n >= 2 H D):  Y = lin
+ *   Q, K      (per head):    u[d] = lin[d] / sqrt(mean_d lin^2 + eps) * w[d]
+ *                            Y[2i]   = u[2i] cos[m,i] - u[2i+1] sin[m,i]
+ *                            Y[2i+1] = u[2i] sin[m,i] + u[2i+1] cos[m,i]
+ *                                                         -> fp16 (RNE)
+ *
+ * Float results (fp32 arithmetic, hardware rsqrt); INT4_G64 only.
+ *
+ * Arguments as svdq_gemm_w4a4 (fmt must be SVDQ_INT4_G64, no activation), and
+ *   N           output channels; N % 384 == 0 (Q, K, V thirds of 128-channel heads).
+ *   qk_norm_w   fp16 [2][128]: the RMSNorm weights of Q, then of K.
+ *   rope        fp32 [M][64][2]: (cos, sin) of token m for channel pair i.
+ *   eps         RMSNorm epsilon, 0 <= eps <= 1.
+ * Errors: SVDQ_ERR_INVALID_ARG for another format, a bad eps or a NULL
+ * qk_norm_w / rope; otherwise as svdq_gemm_w4a4.
+ */
+int svdq_gemm_w4a4_qkv(int fmt, int M, int N, int K, int r,
+                       const uint8_t* act_codes, const void* act_scales, const void* lora_act,
+                       const uint8_t* w_codes, const void* w_scales, const void* lora_up,
+                       const void* bias, const void* qk_norm_w, const float* rope, float eps,
+                       void* Y, void* stream);
+
+/*
  * awq_gemv_w4a16 -- 4-bit weights, 16-bit activations, memory-bound GEMV for
  * the modulation / adaptive-norm projections (dothoosh.com article,
  * kernel-family list: awq_w4a16; quantization_config block: int4, group 64):

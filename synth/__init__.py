@@ -15,4 +15,5 @@ from .inputs import (  # noqa: F401
     make_gemv_inputs,
     random_quantized_layer,
     random_awq_layer,
+    qkv_epilogue_inputs,
 )

@@ -10,8 +10,8 @@ diffusion-model VRAM", paragraph on why outliers make 4-bit hard).
 
 Every array comes from numpy's PCG64 seeded with SeedSequence([seed, cfg_id,
 stream]); streams: 0 = X, 1 = W, 2 = bias, 3 = outlier-channel choice,
-4 = calibration X, 5 = GEMV x, 6 = GEMV W, 7.. = synthetic quantized
-parameters for timing runs.
+4 = calibration X, 5 = GEMV x, 6 = GEMV W, 7 = synthetic quantized
+parameters for timing runs, 8 = Q/K norm weights of the fused QKV epilogue.
 
 Nothing here computes the method: no smoothing, no SVD, no quantization and
 no forward pass.
@@ -24,7 +24,7 @@ from dataclasses import dataclass
 import numpy as np
 
 STREAM_X, STREAM_W, STREAM_BIAS, STREAM_OUTLIERS, STREAM_XCAL = 0, 1, 2, 3, 4
-STREAM_GEMV_X, STREAM_GEMV_W, STREAM_QPARAMS = 5, 6, 7
+STREAM_GEMV_X, STREAM_GEMV_W, STREAM_QPARAMS, STREAM_QKV_EPI = 5, 6, 7, 8
 
 
 @dataclass(frozen=True)
@@ -37,7 +37,7 @@ class LayerConfig:
     N: int
     rank: int
     fmt: str            # "int4_g64" or "fp4_b32"
-    epilogue: str       # "none" or "gelu_tanh"
+    epilogue: str       # "none", "gelu_tanh" or "qkv_norm_rope"
     x_dist: str         # "normal" or "gelu_normal"
     outlier_frac: float
     outlier_scale: float
@@ -69,6 +69,10 @@ CONFIGS = {
     # DiT attention QKV projection, Q,K,V concatenated along the output dim.
     "qkv": LayerConfig("qkv", 1, 4096, 3072, 9216, 32, "int4_g64", "none",
                        "normal", 0.005, 30.0),
+    # The same projection with the per-head Q/K RMSNorm and rotary embedding fused
+    # into its epilogue (24 heads of 128 per third).
+    "qkv_normrope": LayerConfig("qkv_normrope", 11, 4096, 3072, 9216, 32, "int4_g64",
+                                "qkv_norm_rope", "normal", 0.005, 30.0),
     # DiT MLP up-projection in FP4 E2M1 with block-32 E8M0 scales, GELU(tanh).
     "mlp_up": LayerConfig("mlp_up", 2, 4096, 3072, 12288, 32, "fp4_b32",
                           "gelu_tanh", "normal", 0.005, 30.0),
@@ -190,3 +194,25 @@ def random_awq_layer(cfg: GemvConfig, seed: int = 0, M: int | None = None) -> di
     scales = g.uniform(0.004, 0.01, (cfg.N, cfg.K // cfg.group)).astype(np.float16)
     zeros = g.integers(0, 16, (cfg.N, cfg.K // cfg.group)).astype(np.float16)
     return {"x": x, "codes": _nibble_bytes(lo, hi), "scales": scales, "zeros": zeros}
+
+
+def qkv_epilogue_inputs(M: int, seed: int = 0, head_dim: int = 128) -> dict:
+    """Inputs of the fused QKV epilogue: RMSNorm weights of Q and K (fp16, near
+    1) and rotary tables for M image tokens. The tokens are taken as a
+    ceil(sqrt(M))-wide grid in row-major order; the first half of the channel
+    pairs rotate with the token's row, the second half with its column
+    (per-axis rotary embedding of image DiTs), frequencies 10000^(-j/(P/2)) for
+    pair j of each half (P = head_dim / 2 pairs). rope is fp32 [M][P][2] (cos, sin);
+    eps is the RMSNorm epsilon."""
+    g = rng_for(seed, 0, STREAM_QKV_EPI)
+    q_w = (1.0 + 0.1 * g.standard_normal(head_dim)).astype(np.float16)
+    k_w = (1.0 + 0.1 * g.standard_normal(head_dim)).astype(np.float16)
+    P = head_dim // 2
+    side = int(math.ceil(math.sqrt(max(M, 1))))
+    m = np.arange(M)
+    row, col = (m // side).astype(np.float64), (m % side).astype(np.float64)
+    half = P // 2
+    freq = 10000.0 ** (-np.arange(half) / half)
+    theta = np.concatenate([row[:, None] * freq[None, :], col[:, None] * freq[None, :]], axis=1)
+    rope = np.stack([np.cos(theta), np.sin(theta)], axis=-1).astype(np.float32)
+    return {"qk_norm_w": np.stack([q_w, k_w]), "rope": np.ascontiguousarray(rope), "eps": 1e-6}

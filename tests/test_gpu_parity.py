@@ -223,6 +223,76 @@ def test_gemm_full_size_sampled(P, name):
     assert np.isfinite(y).all()
 
 
+# ------------------------------------------------ fused QKV epilogue --
+
+def _qkv_case(P, cfg, seed, rows=None):
+    p = synth.random_quantized_layer(cfg, seed=seed)
+    e = synth.qkv_epilogue_inputs(cfg.M, seed=seed)
+    codes_u, packed, scales = oracle.quantize_act_ref(p["X"], p["smooth_inv"], "int4_g64")
+    la = oracle.lora_act_ref(p["X"], p["lora_down"]).astype(np.float16)
+    args = (dev(packed), dev(scales), dev(la), dev(p["w_codes"]), dev(p["w_scales"]), dev(p["lora_up"]),
+            dev(p["bias"]))
+    Y = P.svdq_gemm_w4a4_qkv(*args, dev(e["qk_norm_w"]), dev(e["rope"]), e["eps"])
+    Y_plain = P.svdq_gemm_w4a4(*args, "int4_g64", "none")
+    wu = oracle.unpack_nibbles(p["w_codes"], signed=True)
+    sel = np.arange(cfg.M) if rows is None else rows
+    y_lin = oracle.gemm_ref(codes_u, scales, la, wu, p["w_scales"], p["lora_up"], p["bias"], "int4_g64",
+                            "none", rows=sel)
+    rope = e["rope"][sel]
+    y_ref = oracle.qkv_epilogue_ref(y_lin, 128, e["qk_norm_w"][0], e["qk_norm_w"][1], rope[..., 0],
+                                    rope[..., 1], e["eps"])
+    return host(Y), host(Y_plain), y_ref, sel
+
+
+def _within_one_ulp(a, b):
+    """fp16 arrays equal up to one unit in the last place (the plain GEMM may
+    round acc * 2^-8 + bias to fp16 in one step, v_fma_mixlo_f16, where the
+    QKV variant rounds to fp32 first)."""
+    ia = a.view(np.int16).astype(np.int32)
+    ib = b.view(np.int16).astype(np.int32)
+    return int(np.abs(ia - ib).max()) <= 1 and np.mean(ia != ib) < 1e-4
+
+
+def test_gemm_qkv_epilogue_small(P):
+    """Ragged M, two heads per third: Q and K normalised and rotated, V equal
+    to the plain GEMM's output (to one fp16 ulp)."""
+    cfg = synth.LayerConfig("qkv_small", 51, 200, 512, 768, 16, "int4_g64", "none", "normal", 0.005, 30.0)
+    y, y_plain, y_ref, _ = _qkv_case(P, cfg, seed=6)
+    n3 = cfg.N // 3
+    assert rel_l2(y[:, :n3], y_ref[:, :n3]) <= Y_TOL
+    assert rel_l2(y[:, n3:2 * n3], y_ref[:, n3:2 * n3]) <= Y_TOL
+    assert _within_one_ulp(y[:, 2 * n3:], y_plain[:, 2 * n3:])
+    assert rel_l2(y[:, 2 * n3:], y_ref[:, 2 * n3:]) <= Y_TOL
+
+
+def test_gemm_qkv_epilogue_full_size_sampled(P):
+    """The DiT QKV projection (24 heads of 128 per third) in the benchmark's
+    launch configuration, checked on sampled rows."""
+    cfg = synth.CONFIGS["qkv"]
+    rng = np.random.default_rng(12)
+    rows = np.unique(np.concatenate([rng.choice(cfg.M, 24, replace=False), [0, cfg.M - 1]]))
+    y, y_plain, y_ref, sel = _qkv_case(P, cfg, seed=3, rows=rows)
+    assert rel_l2(y[sel], y_ref) <= Y_TOL
+    n3 = cfg.N // 3
+    assert _within_one_ulp(y[:, 2 * n3:], y_plain[:, 2 * n3:])
+    assert np.isfinite(y).all()
+
+
+def test_gemm_qkv_epilogue_errors(P):
+    z = lambda *s, dt=torch.uint8: torch.zeros(s, dtype=dt, device="cuda")
+    M, K = 16, 256
+    ac, asc = z(M, K // 2), z(M, K // 64, dt=torch.float16)
+    nw, rope = z(2, 128, dt=torch.float16), z(M, 64, 2, dt=torch.float32)
+    with pytest.raises(P.SvdqError) as e:   # N not a multiple of 384
+        P.svdq_gemm_w4a4_qkv(ac, asc, None, z(512, K // 2), z(512, K // 64, dt=torch.float16), None, None,
+                             nw, rope)
+    assert e.value.status == -2
+    with pytest.raises(P.SvdqError) as e:   # FP4 is not supported by this entry point
+        P.svdq_gemm_w4a4_qkv(ac, z(M, K // 32), None, z(384, K // 2), z(384, K // 32), None, None,
+                             nw, rope, fmt="fp4_b32")
+    assert e.value.status == -1
+
+
 # ------------------------------------------------------------------ GEMV --
 
 @pytest.mark.parametrize("M,N", [(1, 18432), (2, 1000), (8, 96), (3, 17)])
@@ -238,8 +308,8 @@ def test_awq_gemv(P, M, N):
 @pytest.mark.parametrize("M,K,N", [(4, 4096, 512), (1, 12288, 3072), (2, 16384, 300),
                                    (1, 16448, 77), (8, 4096, 130), (1, 64, 5)])
 def test_awq_gemv_random_params_other_k(P, M, K, N):
-    """Both kernel paths (x in registers for M * ceil(K/4096) <= 4, x in LDS
-    otherwise), ragged N, K not a multiple of 4096."""
+    """Batched x (M up to 8), ragged N (including fewer rows than waves), K
+    not a multiple of 64 chunks per unit, up to the LDS limit M K = 32768."""
     g = synth.GemvConfig(f"gemv_k{K}", 40, 1, K, N, 64)
     p = synth.random_awq_layer(g, seed=5, M=M)
     y_ref = oracle.gemv_ref(p["x"], p["codes"], p["scales"], p["zeros"])
