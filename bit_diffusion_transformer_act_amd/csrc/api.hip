@@ -146,19 +146,20 @@ int svdq_gemm_w4a4_qkv(int fmt, int M, int N, int K, int r, const uint8_t* act_c
 }
 
 int awq_gemv_w4a16(int M, int N, int K, int group, const void* x, const uint8_t* w_codes,
-                   const void* scales, const void* zeros, void* y, void* stream) {
+                   const void* scales, const void* zeros, const void* bias, void* y, void* stream) {
   if (group != 64) return SVDQ_ERR_SHAPE;
   if (M < 0 || M > 8 || N < 1 || N > (1 << 20) || K < 64 || (K % 64) != 0 || M * K > 32768)
     return SVDQ_ERR_SHAPE;
   if (M == 0) return SVDQ_OK;
   if (!x || !w_codes || !scales || !zeros || !y) return SVDQ_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(w_codes) || !aligned16(scales) || !aligned16(zeros) ||
-      !aligned16(y))
+      !aligned16(y) || !aligned16(bias))
     return SVDQ_ERR_ALIGN;
   const int dc = check_current_device();
   if (dc != SVDQ_OK) return dc;
   (void)hipGetLastError();
-  return finish(svdq::launch_awq_gemv(M, N, K, x, w_codes, scales, zeros, y, (hipStream_t)stream));
+  return finish(svdq::launch_awq_gemv(M, N, K, x, w_codes, scales, zeros, bias, y,
+                                      (hipStream_t)stream));
 }
 
 }  // extern "C"

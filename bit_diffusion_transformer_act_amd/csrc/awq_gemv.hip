@@ -48,7 +48,7 @@ template <int MR>
 __global__ __launch_bounds__(64 * kGemvWaves)
 void awq_gemv_kernel(const __half* __restrict__ x, const uint8_t* __restrict__ codes,
                      const __half* __restrict__ scales, const __half* __restrict__ zeros,
-                     __half* __restrict__ y, int N, int K) {
+                     const __half* __restrict__ bias, __half* __restrict__ y, int N, int K) {
   // LDS: x pairs as [m][4 segments of a chunk][chunk][4 pairs] (for a fixed
   // segment, consecutive chunks are 16 bytes apart: conflict-free reads), then
   // the chunk sums of x [m][chunk]
@@ -165,14 +165,15 @@ void awq_gemv_kernel(const __half* __restrict__ x, const uint8_t* __restrict__ c
     }
   }
   if (lane < r1 - r0) {
+    const float b = bias ? __half2float(bias[r0 + lane]) : 0.f;
 #pragma unroll
-    for (int m = 0; m < MR; ++m) y[(size_t)m * N + r0 + lane] = __float2half_rn(out[m]);
+    for (int m = 0; m < MR; ++m) y[(size_t)m * N + r0 + lane] = __float2half_rn(out[m] + b);
   }
 }
 
 template <int MR>
 static hipError_t launch_mr(int N, int K, const void* x, const uint8_t* q, const void* s,
-                            const void* z, void* y, hipStream_t st) {
+                            const void* z, const void* b, void* y, hipStream_t st) {
   // about one workgroup per CU for large N, at least ~4 rows per wave for small
   // N, and never more than 64 rows per wave (the kernel keeps one row per lane)
   const int rows_cap = kGemvWaves * 64;
@@ -188,21 +189,21 @@ static hipError_t launch_mr(int N, int K, const void* x, const uint8_t* q, const
     }
   }
   hipLaunchKernelGGL((awq_gemv_kernel<MR>), dim3(grid), dim3(64 * kGemvWaves), lds, st, (const __half*)x, q,
-                     (const __half*)s, (const __half*)z, (__half*)y, N, K);
+                     (const __half*)s, (const __half*)z, (const __half*)b, (__half*)y, N, K);
   return hipGetLastError();
 }
 
 hipError_t launch_awq_gemv(int M, int N, int K, const void* x, const uint8_t* q, const void* s,
-                           const void* z, void* y, hipStream_t st) {
+                           const void* z, const void* b, void* y, hipStream_t st) {
   switch (M) {
-    case 1: return launch_mr<1>(N, K, x, q, s, z, y, st);
-    case 2: return launch_mr<2>(N, K, x, q, s, z, y, st);
-    case 3: return launch_mr<3>(N, K, x, q, s, z, y, st);
-    case 4: return launch_mr<4>(N, K, x, q, s, z, y, st);
-    case 5: return launch_mr<5>(N, K, x, q, s, z, y, st);
-    case 6: return launch_mr<6>(N, K, x, q, s, z, y, st);
-    case 7: return launch_mr<7>(N, K, x, q, s, z, y, st);
-    default: return launch_mr<8>(N, K, x, q, s, z, y, st);
+    case 1: return launch_mr<1>(N, K, x, q, s, z, b, y, st);
+    case 2: return launch_mr<2>(N, K, x, q, s, z, b, y, st);
+    case 3: return launch_mr<3>(N, K, x, q, s, z, b, y, st);
+    case 4: return launch_mr<4>(N, K, x, q, s, z, b, y, st);
+    case 5: return launch_mr<5>(N, K, x, q, s, z, b, y, st);
+    case 6: return launch_mr<6>(N, K, x, q, s, z, b, y, st);
+    case 7: return launch_mr<7>(N, K, x, q, s, z, b, y, st);
+    default: return launch_mr<8>(N, K, x, q, s, z, b, y, st);
   }
 }
 

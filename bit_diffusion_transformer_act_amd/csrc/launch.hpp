@@ -32,6 +32,7 @@ hipError_t launch_gemm_fp4_big(int M, int N, int K, int r, const uint8_t* act_co
                                void* Y, hipStream_t stream);
 
 hipError_t launch_awq_gemv(int M, int N, int K, const void* x, const uint8_t* codes,
-                           const void* scales, const void* zeros, void* y, hipStream_t stream);
+                           const void* scales, const void* zeros, const void* bias, void* y,
+                           hipStream_t stream);
 
 }  // namespace svdq

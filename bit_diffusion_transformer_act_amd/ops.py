@@ -67,7 +67,7 @@ def lib() -> ctypes.CDLL:
             h.svdq_gemm_w4a4_qkv.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                              ctypes.c_float, vp, vp]
             h.svdq_gemm_w4a4_qkv.restype = i32
-            h.awq_gemv_w4a16.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]
+            h.awq_gemv_w4a16.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
             h.awq_gemv_w4a16.restype = i32
             _handle = h
         return _handle
@@ -233,8 +233,8 @@ def svdq_gemm_w4a4_qkv(act_codes, act_scales, lora_act, w_codes, w_scales, lora_
     return out
 
 
-def awq_gemv_w4a16(x, w_codes, scales, zeros, group: int = 64, out=None):
-    """AWQ W4A16 GEMV: y[m,n] = sum_k x[m,k] (q[n,k] - z) s -> fp16 [M][N]."""
+def awq_gemv_w4a16(x, w_codes, scales, zeros, group: int = 64, out=None, bias=None):
+    """AWQ W4A16 GEMV: y[m,n] = sum_k x[m,k] (q[n,k] - z) s + bias[n] -> fp16 [M][N]."""
     dev = x.device
     if dev.type != "cuda":
         raise ValueError("x must be a HIP device tensor")
@@ -244,12 +244,14 @@ def awq_gemv_w4a16(x, w_codes, scales, zeros, group: int = 64, out=None):
     _check(w_codes, "w_codes", torch.uint8, (N, K // 2), dev)
     _check(scales, "scales", torch.float16, (N, K // group), dev)
     _check(zeros, "zeros", torch.float16, (N, K // group), dev)
+    if bias is not None:
+        _check(bias, "bias", torch.float16, (N,), dev)
     if out is None:
         out = torch.empty((M, N), dtype=torch.float16, device=dev)
     _check(out, "out", torch.float16, (M, N), dev)
     with torch.cuda.device(dev):
         st = lib().awq_gemv_w4a16(M, N, K, group, _ptr(x), _ptr(w_codes), _ptr(scales),
-                                  _ptr(zeros), _ptr(out), _stream(dev))
+                                  _ptr(zeros), _ptr(bias), _ptr(out), _stream(dev))
     if st != SVDQ_OK:
         raise SvdqError(st, "awq_gemv_w4a16")
     return out

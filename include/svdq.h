@@ -192,9 +192,10 @@ int svdq_gemm_w4a4_qkv(int fmt, int M, int N, int K, int r,
  * the modulation / adaptive-norm projections (dothoosh.com article,
  * kernel-family list: awq_w4a16; quantization_config block: int4, group 64):
  *
- *   y[m,n] = sum_k x[m,k] * (q[n,k] - z[n,k/G]) * s[n,k/G]   -> fp16 (RNE)
+ *   y[m,n] = sum_k x[m,k] * (q[n,k] - z[n,k/G]) * s[n,k/G] + bias[n]   -> fp16 (RNE)
  *
- * with fp32 accumulation.
+ * with fp32 accumulation; the bias is added to the fp32 total before the one
+ * rounding to fp16.
  *
  * Arguments:
  *   M       rows of x, 0 <= M <= 8.
@@ -206,12 +207,13 @@ int svdq_gemm_w4a4_qkv(int fmt, int M, int N, int K, int r,
  *   w_codes u8 [N][K/2], unsigned nibbles, even k in the low nibble.
  *   scales  fp16 [N][K/64].
  *   zeros   fp16 [N][K/64], in code units (any fp16 value).
+ *   bias    fp16 [N], or NULL for none.
  *   y       out, fp16 [M][N].
  *   stream  hipStream_t.
  */
 int awq_gemv_w4a16(int M, int N, int K, int group,
                    const void* x, const uint8_t* w_codes, const void* scales,
-                   const void* zeros, void* y, void* stream);
+                   const void* zeros, const void* bias, void* y, void* stream);
 
 #ifdef __cplusplus
 }

@@ -52,7 +52,10 @@ def awq_dequantize(codes_packed: np.ndarray, scales: np.ndarray, zeros: np.ndarr
 
 
 def gemv_ref(x16: np.ndarray, codes_packed: np.ndarray, scales: np.ndarray,
-             zeros: np.ndarray, group: int = 64) -> np.ndarray:
-    """y[m,n] = sum_k x[m,k] (q[n,k] - z[n,k/G]) s[n,k/G], float64 [M][N]."""
+             zeros: np.ndarray, group: int = 64, bias=None) -> np.ndarray:
+    """y[m,n] = sum_k x[m,k] (q[n,k] - z[n,k/G]) s[n,k/G] (+ bias[n]), float64 [M][N]."""
     Wd = awq_dequantize(codes_packed, scales, zeros, group)
-    return np.asarray(x16, dtype=np.float64) @ Wd.T
+    y = np.asarray(x16, dtype=np.float64) @ Wd.T
+    if bias is not None:
+        y = y + np.asarray(bias, dtype=np.float64)[None, :]
+    return y

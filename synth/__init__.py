@@ -16,4 +16,6 @@ from .inputs import (  # noqa: F401
     random_quantized_layer,
     random_awq_layer,
     qkv_epilogue_inputs,
+    dit_block_params,
+    dit_block_inputs,
 )

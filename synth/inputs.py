@@ -11,7 +11,8 @@ diffusion-model VRAM", paragraph on why outliers make 4-bit hard).
 Every array comes from numpy's PCG64 seeded with SeedSequence([seed, cfg_id,
 stream]); streams: 0 = X, 1 = W, 2 = bias, 3 = outlier-channel choice,
 4 = calibration X, 5 = GEMV x, 6 = GEMV W, 7 = synthetic quantized
-parameters for timing runs, 8 = Q/K norm weights of the fused QKV epilogue.
+parameters for timing runs, 8 = Q/K norm weights of the fused QKV epilogue,
+9 = dense weights of the synthetic DiT block, 10 = its inputs.
 
 Nothing here computes the method: no smoothing, no SVD, no quantization and
 no forward pass.
@@ -25,6 +26,8 @@ import numpy as np
 
 STREAM_X, STREAM_W, STREAM_BIAS, STREAM_OUTLIERS, STREAM_XCAL = 0, 1, 2, 3, 4
 STREAM_GEMV_X, STREAM_GEMV_W, STREAM_QPARAMS, STREAM_QKV_EPI = 5, 6, 7, 8
+STREAM_DIT_W, STREAM_DIT_X = 9, 10
+DIT_CFG_ID = 20
 
 
 @dataclass(frozen=True)
@@ -216,3 +219,41 @@ def qkv_epilogue_inputs(M: int, seed: int = 0, head_dim: int = 128) -> dict:
     theta = np.concatenate([row[:, None] * freq[None, :], col[:, None] * freq[None, :]], axis=1)
     rope = np.stack([np.cos(theta), np.sin(theta)], axis=-1).astype(np.float32)
     return {"qk_norm_w": np.stack([q_w, k_w]), "rope": np.ascontiguousarray(rope), "eps": 1e-6}
+
+
+def dit_block_params(dim: int, cond_dim: int | None = None, mlp_ratio: int = 4,
+                     seed: int = 0) -> dict:
+    """Dense weights of one synthetic DiT block, fp16 numpy arrays keyed by the
+    torch parameter names (nn.Linear layout [out][in]): linears N(0, 1/in),
+    biases N(0, 0.02^2), RMSNorm weights near 1, and a modulation projection
+    scaled so that shift, scale and gate come out around 0.2."""
+    cond_dim = cond_dim or dim
+    g = rng_for(seed, DIT_CFG_ID, STREAM_DIT_W)
+    hid = mlp_ratio * dim
+    shapes = {"self_attention.to_q": (dim, dim), "self_attention.to_k": (dim, dim),
+              "self_attention.to_v": (dim, dim), "self_attention.to_out": (dim, dim),
+              "mlp.0": (hid, dim), "mlp.2": (dim, hid)}
+    out = {}
+    for name, (n, k) in shapes.items():
+        out[name + ".weight"] = (g.standard_normal((n, k)) / math.sqrt(k)).astype(np.float16)
+        out[name + ".bias"] = (g.standard_normal(n) * 0.02).astype(np.float16)
+    for name in ("self_attention.norm_q", "self_attention.norm_k"):
+        out[name + ".weight"] = (1.0 + 0.1 * g.standard_normal(128)).astype(np.float16)
+    out["adaLN_modulation.1.weight"] = (g.standard_normal((6 * dim, cond_dim)) * 0.01).astype(np.float16)
+    out["adaLN_modulation.1.bias"] = (g.standard_normal(6 * dim) * 0.02).astype(np.float16)
+    return out
+
+
+def dit_block_inputs(B: int, T: int, dim: int, cond_dim: int | None = None, seed: int = 0,
+                     outlier_frac: float = 0.01, outlier_scale: float = 20.0) -> dict:
+    """x fp16 [B][T][dim]: N(0, 1) with a few channels scaled up (outliers
+    that survive LayerNorm); c fp16 [B][cond_dim] ~ N(0, 1); rope fp32
+    [T][64][2] from qkv_epilogue_inputs over a grid of T tokens."""
+    cond_dim = cond_dim or dim
+    g = rng_for(seed, DIT_CFG_ID, STREAM_DIT_X)
+    outl = outlier_channels(dim, outlier_frac, g)
+    x = g.standard_normal((B, T, dim))
+    x[..., outl] *= outlier_scale
+    c = g.standard_normal((B, cond_dim))
+    rope = qkv_epilogue_inputs(T, seed)["rope"]
+    return {"x": x.astype(np.float16), "c": c.astype(np.float16), "rope": rope}

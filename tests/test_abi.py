@@ -53,8 +53,8 @@ def g(fmt=0, M=4, N=128, K=128, r=16, ac=A, sa=A, la=A, wc=A, ws=A, lu=A, b=None
     return P.lib().svdq_gemm_w4a4(fmt, M, N, K, r, ac, sa, la, wc, ws, lu, b, epi, Y, None)
 
 
-def v(M=1, N=64, K=128, G=64, x=A, c=A, s=A, z=A, y=A):
-    return P.lib().awq_gemv_w4a16(M, N, K, G, x, c, s, z, y, None)
+def v(M=1, N=64, K=128, G=64, x=A, c=A, s=A, z=A, b=None, y=A):
+    return P.lib().awq_gemv_w4a16(M, N, K, G, x, c, s, z, b, y, None)
 
 
 def test_quantize_act_argument_errors():
@@ -100,7 +100,9 @@ def test_gemv_argument_errors():
     assert v(M=0, x=None, c=None, s=None, z=None, y=None) == ops.SVDQ_OK
     assert v(z=None) == ops.SVDQ_ERR_INVALID_ARG
     assert v(y=U) == ops.SVDQ_ERR_ALIGN
+    assert v(b=U) == ops.SVDQ_ERR_ALIGN
     assert v() == ops.SVDQ_ERR_UNSUPPORTED_DEVICE
+    assert v(b=A) == ops.SVDQ_ERR_UNSUPPORTED_DEVICE
 
 
 def test_device_check_without_gpu():

@@ -1,0 +1,156 @@
+"""The torch modules on the GPU against the oracle: one SVDQLinear /
+AWQLinear at a time, and the synthetic DiT block with every linear patched
+to the 4-bit kernels.
+
+Bars. A module: the layer bar (relative L2 2e-3 against the oracle's float64
+layer on the module's own fp16 input). The block, in three parts:
+  - each 4-bit layer on the input the GPU block actually fed it: the layer bar;
+  - the composition: the oracle block's float64 arithmetic around the layers
+    (modulation, LayerNorm, Q/K norm and rotation when unfused, attention,
+    residuals), run on the GPU's own layer outputs, must give every layer
+    input and the block output within GLUE_TOL (fp16 storage of the GPU's
+    values, relative L2 about 1.4e-4, plus its fp32 arithmetic);
+  - free running, GPU block against oracle block from the same x, c, rope:
+    4-bit activation quantization is not continuous at fp16 resolution (a
+    last-bit change of a layer input moves a code by a whole step), so the
+    two drift apart by as much as the oracle drifts from itself when its
+    layer outputs carry relative noise of 1e-5; that drift, measured here,
+    bounds the GPU's (times 2, plus 1e-3).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import oracle.block
+import synth
+from bit_diffusion_transformer_act_amd.dit import DiTBlock
+from bit_diffusion_transformer_act_amd.modules import (AWQLinear, SVDQLinear, SVDQLinearQKV,
+                                                       fuse_qkv_norm_rope, quantize_model)
+from oracle.block import linear as oracle_linear
+from tests.dit_support import dense_params, quant_config, quantized_params, to_torch
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+Y_TOL = 2e-3
+GLUE_TOL = 1e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    import bit_diffusion_transformer_act_amd as pkg
+    assert pkg.svdq_device_check(0) == 0, "cuda:0 is not gfx950"
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.detach().cpu().numpy()
+
+
+@pytest.mark.parametrize("fmt,epi", [("int4_g64", "none"), ("fp4_b32", "gelu_tanh"), ("int4_g64", "gelu_tanh")])
+def test_svdq_linear_module(fmt, epi):
+    cfg = synth.CONFIGS["tiny"]
+    d = synth.make_layer_inputs(cfg, seed=0)
+    si = oracle.smoothing_factors(d["X_cal"], d["W"], cfg.alpha)
+    layer = oracle.prep_svdq_layer(d["W"], si, cfg.rank, fmt)
+    m = SVDQLinear(cfg.K, cfg.N, cfg.rank, fmt, bias=True, epilogue=epi, device=DEV)
+    m.load_state_dict(to_torch({"smooth_inv": si, "lora_down": layer["lora_down"], "lora_up": layer["lora_up"],
+                                "w_codes": layer["w_codes"], "w_scales": layer["w_scales"], "bias": d["bias"]}, DEV))
+    X = d["X"][:150]
+    y = m(torch.from_numpy(X.reshape(3, 50, cfg.K)).to(DEV))
+    assert tuple(y.shape) == (3, 50, cfg.N) and y.dtype == torch.float16
+    ref = oracle_linear(X, {"kind": "svdq", "layer": layer, "b": d["bias"], "epilogue": epi})
+    assert rel_l2(host(y).reshape(150, cfg.N), ref) <= Y_TOL
+
+
+@pytest.mark.parametrize("M", [1, 11])
+def test_awq_linear_module(M):
+    g = synth.GemvConfig("gemv_mod", 43, 1, 1024, 768, 64)
+    x = synth.make_gemv_inputs(g, seed=8, M=M)["x"]
+    W = synth.make_gemv_inputs(g, seed=8, M=1)["W"]
+    b = (np.random.default_rng(3).standard_normal(g.N) * 0.5).astype(np.float16)
+    a = oracle.awq_prep(W)
+    m = AWQLinear(g.K, g.N, device=DEV)
+    m.load_state_dict(to_torch({"w_codes": a["codes"], "scales": a["scales"], "zeros": a["zeros"], "bias": b}, DEV))
+    y = m(torch.from_numpy(x).to(DEV))
+    ref = oracle.gemv_ref(x, a["codes"], a["scales"], a["zeros"], bias=b)
+    assert rel_l2(host(y), ref) <= Y_TOL
+
+
+def _run_block(fmt, fuse, D=1024, C=768, B=2, T=200, rank=32):
+    w = synth.dit_block_params(D, C, seed=11)
+    cal = synth.dit_block_inputs(2, 256, D, C, seed=12)
+    inp = synth.dit_block_inputs(B, T, D, C, seed=13)
+    P, sd = quantized_params(w, cal, fmt=fmt, rank=rank, fuse_qkv=fuse)
+    blk = DiTBlock(D, C)
+    quantize_model(blk, quant_config(fmt, rank), device=DEV)
+    if fuse:
+        assert fuse_qkv_norm_rope(blk) == ["self_attention"]
+    blk.load_state_dict(to_torch(sd, DEV), strict=True)
+    blk.to(DEV)
+    seen = {}
+
+    def hook(name):
+        def f(mod, args, out):
+            y = torch.cat(out, -1) if isinstance(out, tuple) else out
+            seen[name] = (host(args[0]).reshape(-1, args[0].shape[-1]), host(y).reshape(-1, y.shape[-1]))
+        return f
+    for name, mod in blk.named_modules():
+        if isinstance(mod, (SVDQLinear, AWQLinear)):
+            mod.register_forward_hook(hook(name))
+    x = torch.from_numpy(inp["x"]).to(DEV)
+    with torch.no_grad():
+        out = blk(x, torch.from_numpy(inp["c"]).to(DEV), torch.from_numpy(inp["rope"]).to(DEV))
+    return w, inp, P, seen, host(out)
+
+
+@pytest.mark.parametrize("fmt,fuse", [("int4_g64", True), ("fp4_b32", False)])
+def test_dit_block_end_to_end(fmt, fuse, monkeypatch):
+    w, inp, P, seen, out = _run_block(fmt, fuse)
+    expect = {"adaLN_modulation.1", "self_attention.to_out", "mlp.0", "mlp.2"} | (
+        {"self_attention.to_qkv"} if fuse else {f"self_attention.to_{p}" for p in "qkv"})
+    assert set(seen) == expect
+    T = inp["x"].shape[1]
+    rope_rows = np.tile(inp["rope"].astype(np.float64), (inp["x"].shape[0], 1, 1))
+    for name, (xin, y) in seen.items():
+        ref = oracle_linear(xin, P[name], rope=rope_rows if name.endswith("to_qkv") else None)
+        err = rel_l2(y, ref)
+        print(f"{fmt} {name}: rows {xin.shape[0]} rel_l2 {err:.2e}")
+        assert err <= Y_TOL, name
+    # composition: the oracle's block arithmetic on the GPU's layer outputs
+    fcap = {}
+    forced = oracle.dit_block_ref(inp["x"], inp["c"], inp["rope"], P, capture=fcap,
+                                  outputs={n: y for n, (_, y) in seen.items()})
+    for name, (xin, _) in seen.items():
+        err = rel_l2(xin, fcap[name][0])
+        print(f"{fmt} input of {name}: rel_l2 vs oracle glue {err:.2e}")
+        assert err <= GLUE_TOL, name
+    err = rel_l2(out, forced)
+    print(f"{fmt} block output, teacher-forced: rel_l2 {err:.2e}")
+    assert np.isfinite(out).all() and err <= GLUE_TOL
+
+    # free running, against the oracle's own sensitivity
+    x64 = inp["x"].astype(np.float64)
+    ref = oracle.dit_block_ref(inp["x"], inp["c"], inp["rope"], P)
+    err = rel_l2(out - x64, ref - x64)
+    rng = np.random.default_rng(17)
+
+    def noisy(xr, e, rope=None):
+        y = oracle_linear(xr, e, rope)
+        return (y * (1 + 1e-5 * rng.standard_normal(y.shape))).astype(np.float16).astype(np.float64)
+    monkeypatch.setattr(oracle.block, "linear", noisy)
+    floor = rel_l2(oracle.dit_block_ref(inp["x"], inp["c"], inp["rope"], P) - x64, ref - x64)
+    monkeypatch.undo()
+    dense = oracle.dit_block_ref(inp["x"], inp["c"], inp["rope"], dense_params(w))
+    qerr = rel_l2(ref - x64, dense - x64)
+    print(f"{fmt} block increment: GPU vs oracle {err:.2e}, oracle vs itself under 1e-5 noise "
+          f"{floor:.2e}, 4-bit vs dense {qerr:.2e} (T={T})")
+    assert err <= 2 * floor + 1e-3

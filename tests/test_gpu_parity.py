@@ -327,6 +327,17 @@ def test_awq_gemv_fractional_zeros(P, M):
     assert rel_l2(host(y), y_ref) <= Y_TOL
 
 
+@pytest.mark.parametrize("M,K,N", [(1, 3072, 18432), (5, 2048, 333)])
+def test_awq_gemv_bias(P, M, K, N):
+    """The bias joins the fp32 total before the one fp16 rounding."""
+    g = synth.GemvConfig(f"gemv_b{K}", 42, 1, K, N, 64)
+    p = synth.random_awq_layer(g, seed=7, M=M)
+    b = np.random.default_rng(2).normal(0, 2.0, N).astype(np.float16)
+    y_ref = oracle.gemv_ref(p["x"], p["codes"], p["scales"], p["zeros"], bias=b)
+    y = P.awq_gemv_w4a16(dev(p["x"]), dev(p["codes"]), dev(p["scales"]), dev(p["zeros"]), bias=dev(b))
+    assert rel_l2(host(y), y_ref) <= Y_TOL
+
+
 # ------------------------------------------------------------ semantics --
 
 def test_deterministic_and_stream(P):

@@ -130,6 +130,10 @@ def test_awq_golden():
     x2[0, 0::2] = 1
     assert oracle.gemv_ref(x1, codes, s, z)[0, 0] == float(g["y_all_ones"][0][0])
     assert oracle.gemv_ref(x2, codes, s, z)[0, 0] == float(g["y_even_ones"][0][0])
+    # the bias is a plain per-channel offset: alone when x is zero, added otherwise
+    b = np.array([-2.25], np.float16)
+    assert oracle.gemv_ref(np.zeros((1, 64), np.float16), codes, s, z, bias=b)[0, 0] == -2.25
+    assert oracle.gemv_ref(x1, codes, s, z, bias=b)[0, 0] == float(g["y_all_ones"][0][0]) - 2.25
 
 
 def test_awq_integer_special_case_and_rational():
