@@ -32,6 +32,12 @@ from .svdq import (  # noqa: F401
     smooth_act,
     quantize_int4_g64,
     quantize_fp4_b32,
+    quantize_nvfp4_g16,
+    e2m1_encode,
+    e4m3_value,
+    e4m3_rne,
+    nvfp4_global_scale,
+    nvfp4_act_global_scale,
     quantize,
     quantize_act_ref,
     lora_act_ref,

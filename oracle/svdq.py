@@ -32,7 +32,10 @@ FP16_MAX = 65504.0
 # OCP E2M1 magnitudes by 3-bit code (exponent bits << 1 | mantissa bit).
 E2M1_VALUES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
 
-FORMATS = ("int4_g64", "fp4_b32")
+FORMATS = ("int4_g64", "fp4_b32", "nvfp4_g16")
+
+# 6 * 448: the largest E2M1 magnitude times the largest E4M3 value.
+NVFP4_RANGE = 2688.0
 
 
 def _group(fmt: str) -> int:
@@ -40,6 +43,8 @@ def _group(fmt: str) -> int:
         return 64
     if fmt == "fp4_b32":
         return 32
+    if fmt == "nvfp4_g16":
+        return 16
     raise ValueError(f"unknown format {fmt!r}")
 
 
@@ -103,7 +108,8 @@ def lowrank_factors(W_hat_kn: np.ndarray, rank: int):
     return L1, L2, S
 
 
-def prep_svdq_layer(W: np.ndarray, smooth_inv: np.ndarray, rank: int, fmt: str) -> dict:
+def prep_svdq_layer(W: np.ndarray, smooth_inv: np.ndarray, rank: int, fmt: str,
+                    act_gscale=None) -> dict:
     """Offline preparation of one SVDQ W4A4 layer.
 
     W fp16 [N][K]; smooth_inv fp32 [K]. Steps (each a reading of the pages'
@@ -115,7 +121,10 @@ def prep_svdq_layer(W: np.ndarray, smooth_inv: np.ndarray, rank: int, fmt: str) 
          consumes the caller's X directly; lora_up = fp16(L2^T) [N][r].
       4. Residual with the rounded factors: R = W_hat - diag(lambda') lora_down^T lora_up^T,
          so the 16-bit rounding of the factors is absorbed by the 4-bit part.
-      5. Quantize R^T (N x K) along K with the same rule the activations use.
+      5. Quantize R^T (N x K) along K with the same rule the activations use;
+         for NVFP4 with the per-tensor scale nvfp4_global_scale(max |R|), and
+         the activations' per-tensor scale act_gscale (from calibration,
+         nvfp4_act_global_scale) is stored with the layer.
     """
     if fmt not in FORMATS:
         raise ValueError(fmt)
@@ -134,8 +143,17 @@ def prep_svdq_layer(W: np.ndarray, smooth_inv: np.ndarray, rank: int, fmt: str) 
         lora_up = np.zeros((N, 0), np.float16)
         low = 0.0
     R = W_hat - low                                                # K x N
-    codes, scales = quantize(np.ascontiguousarray(R.T).astype(np.float32), fmt)
+    Rt = np.ascontiguousarray(R.T).astype(np.float32)
+    w_gscale = None
+    if fmt == "nvfp4_g16":
+        if act_gscale is None:
+            raise ValueError("nvfp4_g16 needs the activations' per-tensor scale")
+        w_gscale = nvfp4_global_scale(np.max(np.abs(Rt)))
+        act_gscale = np.float32(act_gscale)
+    codes, scales = quantize(Rt, fmt, w_gscale)
     return {
+        "act_gscale": act_gscale,
+        "w_gscale": w_gscale,
         "fmt": fmt,
         "rank": rank,
         "smooth_inv": np.asarray(smooth_inv, dtype=np.float32),
@@ -219,26 +237,117 @@ def quantize_fp4_b32(v: np.ndarray):
     e = np.clip(_e8m0_exponent(np.where(zero, F32(1.0), amax)), -127, 127)
     scale_code = np.where(zero, 0, e + 127).astype(np.uint8)
     pow2 = np.ldexp(F32(1.0), e.astype(np.int32)).astype(np.float32)[:, :, None]
-    u = np.abs(g / pow2)
-    mag = ((u > 0.25).astype(np.uint8) + (u >= 0.75) + (u > 1.25) + (u >= 1.75)
-           + (u > 2.5) + (u >= 3.5) + (u > 5.0)).astype(np.uint8)
-    code = mag | (np.signbit(g).astype(np.uint8) << 3)
+    code = e2m1_encode(g / pow2)
     code = np.where(zero[:, :, None], 0, code).astype(np.uint8)
     return code.reshape(rows, K), scale_code
 
 
-def quantize(v: np.ndarray, fmt: str):
+def e2m1_encode(u: np.ndarray) -> np.ndarray:
+    """fp32 values -> OCP E2M1 nibbles: magnitude = nearest of
+    {0, .5, 1, 1.5, 2, 3, 4, 6}, ties to the even mantissa bit, saturating
+    at 6; sign bit = signbit(u)."""
+    a = np.abs(np.asarray(u, dtype=np.float32))
+    mag = ((a > 0.25).astype(np.uint8) + (a >= 0.75) + (a > 1.25) + (a >= 1.75)
+           + (a > 2.5) + (a >= 3.5) + (a > 5.0)).astype(np.uint8)
+    return (mag | (np.signbit(u).astype(np.uint8) << 3)).astype(np.uint8)
+
+
+# --------------------------------------------------------------------------
+# NVFP4: E2M1 codes, one E4M3 scale per 16 values, one fp32 scale per tensor.
+# --------------------------------------------------------------------------
+
+def e4m3_value(code) -> np.ndarray:
+    """OCP FP8 E4M3 (bias 7, no infinities, S.1111.111 is NaN) byte -> float64."""
+    c = np.asarray(code, dtype=np.int64)
+    sgn = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 7
+    val = np.where(e == 0, m * 2.0 ** -9, (8 + m) * np.ldexp(1.0, e - 10))
+    return np.where((c & 0x7F) == 0x7F, np.nan, sgn * val)
+
+
+def e4m3_rne(a: np.ndarray) -> np.ndarray:
+    """Non-negative fp32 values -> E4M3 byte by round-to-nearest-even,
+    saturating at 448 (0x7E). Quantum 2^(e-3) in binade [2^e, 2^(e+1)),
+    e >= -6, and 2^-9 below 2^-6; a carry into the next binade is exact."""
+    a = np.asarray(a, dtype=np.float32).astype(np.float64)
+    if (a < 0).any() or np.isnan(a).any():
+        raise ValueError("e4m3_rne takes non-negative numbers")
+    _, ex = np.frexp(np.where(a > 0, a, 1.0))
+    e = np.maximum(ex.astype(np.int64) - 1, -6)
+    q = np.ldexp(1.0, e - 3)
+    r = np.rint(a / q) * q                          # exact: a / q is a scaled fp32
+    r = np.minimum(r, 448.0)
+    # encode r (a representable value) to its byte
+    _, er = np.frexp(np.where(r > 0, r, 1.0))
+    er = er.astype(np.int64) - 1
+    normal = r >= 2.0 ** -6
+    code_n = ((er + 7) << 3) | np.rint(r / np.ldexp(1.0, er) * 8 - 8).astype(np.int64)
+    code_s = np.rint(r / 2.0 ** -9).astype(np.int64)
+    return np.where(normal, code_n, code_s).astype(np.uint8)
+
+
+def nvfp4_global_scale(amax) -> np.float32:
+    """Per-tensor fp32 scale g = fl32(amax / 2688) so that the largest block
+    scale lands on the largest E4M3 value [reading: the pages give NVFP4's
+    name and group size only; this is the usual two-level recipe]. 1 when
+    amax is 0."""
+    a = np.float32(amax)
+    return np.float32(1.0) if a == 0 else np.float32(a / np.float32(NVFP4_RANGE))
+
+
+def nvfp4_act_global_scale(X_cal16: np.ndarray, smooth_inv: np.ndarray) -> np.float32:
+    """The activations' per-tensor scale, fixed offline from calibration rows
+    (the kernels have no whole-tensor pass): g_x = nvfp4_global_scale of the
+    largest smoothed calibration value."""
+    return nvfp4_global_scale(np.max(np.abs(smooth_act(X_cal16, smooth_inv))))
+
+
+def quantize_nvfp4_g16(v: np.ndarray, gscale):
+    """NVFP4 per block of 16 along the last axis with per-tensor scale g.
+
+    Rule [reading; dothoosh.com article, quantization_config block: precision
+    nvfp4, group size 16]:
+      amax = max |v| over the block;
+      s = E4M3_rne(fl32(amax / fl32(6 g))), saturating at 448;
+      d = fl32(E4M3(s) * g); codes = E2M1_rne(fl32(v / d)) (IEEE division),
+      all codes 0 where d == 0.
+    Value of a code: E2M1(code) * E4M3(s) * g.
+    Returns (codes uint8 [rows][K] in 0..15, scales uint8 [rows][K/16]).
+    """
+    v = np.asarray(v, dtype=np.float32)
+    rows, K = v.shape
+    if K % 16:
+        raise ValueError("K must be a multiple of 16")
+    g = np.float32(gscale)
+    blk = v.reshape(rows, K // 16, 16)
+    amax = np.max(np.abs(blk), axis=2)
+    d6 = np.float32(np.float32(6.0) * g)
+    sf = (amax / d6).astype(np.float32)
+    scode = e4m3_rne(sf)
+    d = (e4m3_value(scode).astype(np.float32) * g).astype(np.float32)[:, :, None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        u = (blk / d).astype(np.float32)
+    code = np.where(d == 0, 0, e2m1_encode(np.where(d == 0, 0, u))).astype(np.uint8)
+    return code.reshape(rows, K), scode
+
+
+def quantize(v: np.ndarray, fmt: str, gscale=None):
     if fmt == "int4_g64":
         return quantize_int4_g64(v)
     if fmt == "fp4_b32":
         return quantize_fp4_b32(v)
+    if fmt == "nvfp4_g16":
+        if gscale is None:
+            raise ValueError("nvfp4_g16 needs the per-tensor scale")
+        return quantize_nvfp4_g16(v, gscale)
     raise ValueError(fmt)
 
 
-def quantize_act_ref(X16: np.ndarray, smooth_inv: np.ndarray, fmt: str):
+def quantize_act_ref(X16: np.ndarray, smooth_inv: np.ndarray, fmt: str, gscale=None):
     """Smoothing + 4-bit activation quantization. Returns (codes unpacked,
-    packed codes u8 [M][K/2], scales)."""
-    codes, scales = quantize(smooth_act(X16, smooth_inv), fmt)
+    packed codes u8 [M][K/2], scales). gscale: NVFP4's per-tensor scale."""
+    codes, scales = quantize(smooth_act(X16, smooth_inv), fmt, gscale)
     return codes, pack_nibbles(codes), scales
 
 
@@ -249,8 +358,9 @@ def lora_act_ref(X16: np.ndarray, lora_down: np.ndarray) -> np.ndarray:
     return np.asarray(X16, dtype=np.float64) @ np.asarray(lora_down, dtype=np.float64).T
 
 
-def dequantize(codes: np.ndarray, scales: np.ndarray, fmt: str) -> np.ndarray:
-    """Unpacked codes [rows][K] and scales -> float64 values (exact)."""
+def dequantize(codes: np.ndarray, scales: np.ndarray, fmt: str, gscale=None) -> np.ndarray:
+    """Unpacked codes [rows][K] and scales -> float64 values (exact).
+    gscale: NVFP4's per-tensor scale."""
     codes = np.asarray(codes)
     rows, K = codes.shape
     G = _group(fmt)
@@ -260,7 +370,10 @@ def dequantize(codes: np.ndarray, scales: np.ndarray, fmt: str) -> np.ndarray:
     c = codes.astype(np.int64)
     mag = E2M1_VALUES[c & 7]
     val = np.where(c & 8, -mag, mag)
-    p = np.ldexp(1.0, np.asarray(scales, dtype=np.int64) - 127)
+    if fmt == "nvfp4_g16":
+        p = e4m3_value(scales) * float(np.float32(gscale))
+    else:
+        p = np.ldexp(1.0, np.asarray(scales, dtype=np.int64) - 127)
     return (val.reshape(rows, K // G, G) * p[:, :, None]).reshape(rows, K)
 
 
@@ -281,13 +394,15 @@ def _finish(y: np.ndarray, bias, epilogue: str) -> np.ndarray:
 
 
 def gemm_ref(act_codes, act_scales, lora_act, w_codes, w_scales, lora_up, bias,
-             fmt: str, epilogue: str = "none", rows=None, cols=None) -> np.ndarray:
+             fmt: str, epilogue: str = "none", rows=None, cols=None,
+             act_gscale=None, w_gscale=None) -> np.ndarray:
     """The fused 4-bit GEMM entry point's contract, float64:
     Y = act(lora_act . lora_up^T + sum_g s_x[m,g] s_w[n,g] (q_x[m,g,:] . q_w[n,g,:]) + bias).
 
     act_codes / w_codes are unpacked ([M][K], [N][K]); lora_act [M][r] is the
     value handed to the GEMM (the quantizer's fp16 output). rows / cols pick a
-    subset of outputs for spot checks at full size.
+    subset of outputs for spot checks at full size. act_gscale / w_gscale are
+    NVFP4's per-tensor scales (each dequantized value carries its own).
     """
     ac = np.asarray(act_codes)
     ascl = np.asarray(act_scales)
@@ -301,8 +416,8 @@ def gemm_ref(act_codes, act_scales, lora_act, w_codes, w_scales, lora_up, bias,
     if cols is not None:
         wc, wscl, lu = wc[cols], wscl[cols], lu[cols]
         b = None if b is None else b[cols]
-    Xq = dequantize(ac, ascl, fmt)
-    Wq = dequantize(wc, wscl, fmt)
+    Xq = dequantize(ac, ascl, fmt, act_gscale)
+    Wq = dequantize(wc, wscl, fmt, w_gscale)
     y = la @ lu.T + Xq @ Wq.T
     return _finish(y, b, epilogue)
 
@@ -321,7 +436,8 @@ def forward_ref(X16, layer: dict, act_codes, act_scales, bias, epilogue: str = "
     return gemm_ref(act_codes if rows is None else np.asarray(act_codes)[rows],
                     act_scales if rows is None else np.asarray(act_scales)[rows],
                     la, wc, layer["w_scales"], layer["lora_up"], bias, layer["fmt"],
-                    epilogue, rows=None, cols=cols)
+                    epilogue, rows=None, cols=cols, act_gscale=layer.get("act_gscale"),
+                    w_gscale=layer.get("w_gscale"))
 
 
 def dense_ref(X16, W16, bias, epilogue: str = "none") -> np.ndarray:

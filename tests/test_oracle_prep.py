@@ -82,14 +82,15 @@ def test_residual_identity_and_quantization_error(tiny):
 
 
 def _layer_error(d, si, rank, fmt):
-    layer = oracle.prep_svdq_layer(d["W"], si, rank, fmt)
-    codes, _, scales = oracle.quantize_act_ref(d["X"], si, fmt)
+    ga = oracle.nvfp4_act_global_scale(d["X_cal"], si) if fmt == "nvfp4_g16" else None
+    layer = oracle.prep_svdq_layer(d["W"], si, rank, fmt, act_gscale=ga)
+    codes, _, scales = oracle.quantize_act_ref(d["X"], si, fmt, ga)
     y = oracle.forward_ref(d["X"], layer, codes, scales, d["bias"])
     y_ref = oracle.dense_ref(d["X"], d["W"], d["bias"])
     return np.linalg.norm(y - y_ref) / np.linalg.norm(y_ref)
 
 
-@pytest.mark.parametrize("fmt", ["int4_g64", "fp4_b32"])
+@pytest.mark.parametrize("fmt", ["int4_g64", "fp4_b32", "nvfp4_g16"])
 def test_method_beats_plain_w4a4(tiny, fmt):
     """The pages' claim (outliers migrate to the weights, a 16-bit low-rank
     branch takes the hardest part, the residual goes to 4 bits) must make
@@ -109,3 +110,19 @@ def test_rank_sweep_reported(tiny):
     errs = [_layer_error(d, si, r, "int4_g64") for r in (0, 8, 16, 32)]
     print("rank 0/8/16/32 rel err:", ["%.4e" % e for e in errs])
     assert errs[-1] < errs[0]
+
+
+def test_nvfp4_residual_within_half_step(tiny):
+    """NVFP4 prep: every dequantized residual weight is within half an E2M1
+    step (at most one unit of the block divisor, the 4-to-6 gap) of R, or
+    clipped at the block's top code; the per-tensor scale is the amax rule."""
+    d, si = tiny
+    ga = oracle.nvfp4_act_global_scale(d["X_cal"], si)
+    layer = oracle.prep_svdq_layer(d["W"], si, TINY.rank, "nvfp4_g16", act_gscale=ga)
+    R = layer["residual_kn"].T.astype(np.float32).astype(np.float64)
+    assert layer["w_gscale"] == np.float32(np.max(np.abs(R)) / np.float32(2688.0))
+    deq = oracle.dequantize(layer["w_codes_unpacked"], layer["w_scales"], "nvfp4_g16", layer["w_gscale"])
+    unit = np.repeat(oracle.e4m3_value(layer["w_scales"]) * float(layer["w_gscale"]), 16, axis=1)
+    err = np.abs(deq - R)
+    assert (err <= unit + 1e-6 * np.abs(R)).all()
+    assert np.linalg.norm(deq - R) / np.linalg.norm(R) < 0.15
