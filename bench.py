@@ -36,7 +36,14 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "W4A4+lowrank GEMM effective TOPS & % MFMA peak; W4A16 GEMV HBM GB/s"
-PEAK_TOPS = {"int4_g64": 5000.0, "fp4_b32": 10100.0}   # int8 / MXFP4 dense MFMA peaks
+# dense MFMA peak of the contraction each format runs on: int8 (INT4 codes),
+# MXFP4 (block-scaled FP4), fp16 (NVFP4 operands dequantized exactly to fp16)
+PEAK_TOPS = {"int4_g64": 5000.0, "fp4_b32": 10100.0, "nvfp4_g16": 2500.0}
+PEAK_NOTE = {"int4_g64": "INT4 runs on int8 MFMA: tera-ops against the 5.0 POP/s int8 peak",
+             "fp4_b32": "FP4 against the 10.1 PFLOP/s MXFP4 peak",
+             "nvfp4_g16": "NVFP4 operands dequantized exactly to fp16: against the 2.5 PFLOP/s fp16 peak"}
+SCALE_BYTES_PER_ROW = {"int4_g64": lambda K: (K // 64) * 2, "fp4_b32": lambda K: K // 32,
+                       "nvfp4_g16": lambda K: K // 16}
 PEAK_HBM_GBS = 8000.0
 ROTATE_BYTES = 600 << 20
 
@@ -47,8 +54,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="qkv",
-                    choices=["qkv", "qkv_normrope", "mlp_up", "mlp_down", "mlp_down_m1024",
-                             "attn_out", "mlp_up_int4", "block"])
+                    choices=["qkv", "qkv_normrope", "mlp_up", "mlp_up_nvfp4", "mlp_down",
+                             "mlp_down_m1024", "attn_out", "mlp_up_int4", "block"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--warm", action="store_true", help="no buffer rotation (cache-warm)")
     ap.add_argument("--rank", type=int, default=None, help="override the low-rank width")
@@ -63,7 +70,7 @@ def parse():
 
 def layer_bytes(cfg, r):
     M, K, N = cfg.M, cfg.K, cfg.N
-    sbytes = (K // 64) * 2 if cfg.fmt == "int4_g64" else K // 32
+    sbytes = SCALE_BYTES_PER_ROW[cfg.fmt](K)
     q = M * K * 2 + K * 4 + r * K * 2 + M * K // 2 + M * sbytes + M * r * 2
     g = (M * K // 2 + M * sbytes + M * r * 2 + N * K // 2 + N * sbytes + N * r * 2 + N * 2
          + M * N * 2)
@@ -146,7 +153,10 @@ def main():
                  "lora_up": t(np.ascontiguousarray(p["lora_up"][:, :r])) if r else None,
                  "bias": t(p["bias"])}
             sdt = torch.float16 if cfg.fmt == "int4_g64" else torch.uint8
-            scols = cfg.K // 64 if cfg.fmt == "int4_g64" else cfg.K // 32
+            scols = SCALE_BYTES_PER_ROW[cfg.fmt](cfg.K) // (2 if cfg.fmt == "int4_g64" else 1)
+            if cfg.fmt == "nvfp4_g16":
+                L["act_gscale"] = float(p["act_gscale"])
+                L["alpha"] = float(np.float32(p["act_gscale"]) * np.float32(p["w_gscale"]))
             L["codes"] = torch.empty((cfg.M, cfg.K // 2), dtype=torch.uint8, device=dev)
             L["scales"] = torch.empty((cfg.M, scols), dtype=sdt, device=dev)
             L["lora_act"] = torch.empty((cfg.M, r), dtype=torch.float16, device=dev) if r else None
@@ -170,11 +180,18 @@ def main():
             cfg = L["cfg"]
             if events is not None:
                 events[j].record(stream)
-            P.svdq_quantize_act(L["X"], L["smooth_inv"], L["lora_down"], cfg.fmt,
-                                L["codes"], L["scales"], L["lora_act"])
+            if cfg.fmt == "nvfp4_g16":
+                P.svdq_quantize_act_nvfp4(L["X"], L["smooth_inv"], L["lora_down"], L["act_gscale"],
+                                          L["codes"], L["scales"], L["lora_act"])
+            else:
+                P.svdq_quantize_act(L["X"], L["smooth_inv"], L["lora_down"], cfg.fmt,
+                                    L["codes"], L["scales"], L["lora_act"])
             if events is not None:
                 events[j + 1].record(stream)
-            if cfg.epilogue == "qkv_norm_rope":
+            if cfg.fmt == "nvfp4_g16":
+                P.svdq_gemm_nvfp4(L["codes"], L["scales"], L["lora_act"], L["w_codes"], L["w_scales"],
+                                  L["lora_up"], L["bias"], L["alpha"], cfg.epilogue, out=L["Y"])
+            elif cfg.epilogue == "qkv_norm_rope":
                 P.svdq_gemm_w4a4_qkv(L["codes"], L["scales"], L["lora_act"], L["w_codes"], L["w_scales"],
                                      L["lora_up"], L["bias"], L["qk_norm_w"], L["rope"], L["eps"],
                                      out=L["Y"])
@@ -245,7 +262,7 @@ def main():
             "alg_bytes": qb, "GB/s": round(qb / (qms * 1e-3) / 1e9, 1),
             "frac_hbm": round(qb / (qms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
         tops = ops / (gms * 1e-3) / 1e12
-        gname = "svdq_gemm_w4a4_qkv" if cfg.epilogue == "qkv_norm_rope" else "svdq_gemm_w4a4"
+        gname = gemm_name(cfg)
         kernels[f"{cfg.name}.{gname}"] = {
             "avg_us": round(gms * 1e3, 2), "median_us": round(med_ms[2 * li + 1] * 1e3, 2),
             "alg_ops": ops, "lowrank_ops": 2.0 * cfg.M * cfg.N * r + 2.0 * cfg.M * cfg.K * r,
@@ -262,13 +279,12 @@ def main():
 
     dcfg, dms, dops, dr = dominant
     achieved = dops / (dms * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "kernel": "svdq_gemm_w4a4", "workload": dcfg.name,
+    roofline = {"bound": "mfma", "kernel": gemm_name(dcfg), "workload": dcfg.name,
                 "achieved": round(achieved, 1), "peak": PEAK_TOPS[dcfg.fmt], "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_TOPS[dcfg.fmt], 4),
                 "traffic": stored_traffic(dcfg.name),
                 "ops_per_launch": dops,
-                "note": "INT4 runs on int8 MFMA: tera-ops against the 5.0 POP/s int8 peak"
-                        if dcfg.fmt == "int4_g64" else "FP4 against the 10.1 PFLOP/s MXFP4 peak"}
+                "note": PEAK_NOTE[dcfg.fmt]}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -283,7 +299,7 @@ def main():
         "metric": METRIC, "value": round(value, 1), "unit": "TOPS", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "int8" if all(c.fmt == "int4_g64" for c in cfgs) else "fp4",
+        "dtype": "+".join(sorted({MFMA_DTYPE[c.fmt] for c in cfgs})),
         "data": "synthetic",
         "config": {"workload": wl, "layers": names, "rotating_sets": nsets,
                    "cache": "warm" if args.warm else "cold (rotated > Infinity Cache)"},
@@ -295,6 +311,15 @@ def main():
         "device": torch.cuda.get_device_properties(dev).gcnArchName,
     }
     print(json.dumps(out), flush=True)
+
+
+MFMA_DTYPE = {"int4_g64": "int8", "fp4_b32": "fp4", "nvfp4_g16": "f16"}
+
+
+def gemm_name(cfg):
+    if cfg.fmt == "nvfp4_g16":
+        return "svdq_gemm_nvfp4"
+    return "svdq_gemm_w4a4_qkv" if cfg.epilogue == "qkv_norm_rope" else "svdq_gemm_w4a4"
 
 
 def cpu_baseline(cfg, gcfg, p, gp, r):
@@ -313,11 +338,11 @@ def cpu_baseline(cfg, gcfg, p, gp, r):
     rows = min(cfg.M, 2048)
     X = p["X"][:rows]
     t0 = time.perf_counter()
-    codes_u, _, scales = oracle.quantize_act_ref(X, p["smooth_inv"], cfg.fmt)
+    codes_u, _, scales = oracle.quantize_act_ref(X, p["smooth_inv"], cfg.fmt, p.get("act_gscale"))
     la = oracle.lora_act_ref(X, p["lora_down"][:r])
     wu = oracle.unpack_nibbles(p["w_codes"], signed=(cfg.fmt == "int4_g64"))
     oracle.gemm_ref(codes_u, scales, la, wu, p["w_scales"], p["lora_up"][:, :r], p["bias"], cfg.fmt,
-                    cfg.epilogue)
+                    cfg.epilogue, act_gscale=p.get("act_gscale"), w_gscale=p.get("w_gscale"))
     t_layer = time.perf_counter() - t0
     t1 = time.perf_counter()
     oracle.gemv_ref(gp["x"], gp["codes"], gp["scales"], gp["zeros"], gcfg.group)

@@ -27,6 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 # entry point -> [(kernel-name substring, source file)]; the first that matches wins
 KERNELS = {"svdq_gemm_w4a4": [("gemm_fp4_big_kernel", "gemm_fp4.hip"),
                               ("gemm_w4a4_kernel", "gemm_w4a4.hip")],
+           "svdq_gemm_nvfp4": [("gemm_nvfp4_kernel", "gemm_nvfp4.hip")],
            "svdq_quantize_act": [("quantize_act_kernel", "quantize_act.hip")],
            "awq_gemv_w4a16": [("awq_gemv", "awq_gemv.hip")]}
 

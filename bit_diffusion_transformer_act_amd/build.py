@@ -25,7 +25,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 # tile keeps its 256 accumulators per lane in AGPRs, so it is built without.
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 SOURCES = {"api.hip": [], "quantize_act.hip": VGPR_FORM, "gemm_w4a4.hip": VGPR_FORM,
-           "gemm_fp4.hip": [], "awq_gemv.hip": VGPR_FORM}
+           "gemm_fp4.hip": [], "gemm_nvfp4.hip": [], "awq_gemv.hip": VGPR_FORM}
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -10,14 +10,15 @@ modulation / adaptive-norm projections). This module parses and validates
 that block against what the MI355X library implements:
 
   svdq_w4a4 precision "int4" with group_size 64  -> INT4, fp16 scale per 64
+  svdq_w4a4 precision "nvfp4" with group_size 16 -> NVFP4: E2M1, E4M3 scale per
+                                                    16, fp32 scale per tensor
   svdq_w4a4 precision "mxfp4" with group_size 32 -> FP4 E2M1, E8M0 scale per 32
   awq_w4a16 precision "int4" with group_size 64  -> the AWQ GEMV
   compute_dtype "float16"
 
-The pages' own example uses precision "nvfp4" with group_size 16 and
-compute_dtype "bfloat16"; the gfx950 block-scaled matrix instruction takes an
-E8M0 scale per 32 values, and the kernels take fp16 activations, so those two
-settings are rejected with an explicit message rather than silently mapped.
+The pages' own example sets compute_dtype "bfloat16"; the kernels take fp16
+activations and write fp16 outputs, so that setting is rejected with an
+explicit message rather than silently mapped.
 Target entries are module names; "..." entries (an elision in the pages'
 example) are ignored, and shell-style wildcards are accepted.
 """
@@ -34,7 +35,7 @@ class UnsupportedQuantConfig(ValueError):
 
 @dataclass(frozen=True)
 class SvdqSpec:
-    fmt: str                  # "int4_g64" or "fp4_b32"
+    fmt: str                  # "int4_g64", "fp4_b32" or "nvfp4_g16"
     rank: int
     targets: tuple
 
@@ -89,13 +90,10 @@ def parse_quantization_config(cfg) -> QuantConfig:
         prec, gs, rank = b.get("precision"), b.get("group_size"), b.get("rank", 32)
         if prec == "int4" and gs == 64:
             fmt = "int4_g64"
+        elif prec == "nvfp4" and gs == 16:
+            fmt = "nvfp4_g16"
         elif prec == "mxfp4" and gs == 32:
             fmt = "fp4_b32"
-        elif prec == "nvfp4":
-            raise UnsupportedQuantConfig(
-                "svdq_w4a4 precision nvfp4 (group 16, non-power-of-two scales): the gfx950 "
-                "block-scaled FP4 instruction takes one E8M0 scale per 32 values; use precision "
-                "'mxfp4' with group_size 32, or 'int4' with group_size 64")
         else:
             raise UnsupportedQuantConfig(f"svdq_w4a4 precision {prec!r} with group_size {gs!r}")
         if not isinstance(rank, int) or rank < 0 or rank > 128 or rank % 16:

@@ -6,6 +6,7 @@
 // (dothoosh.com "How Nunchaku Lite halves diffusion-model VRAM",
 // hardware-support paragraph).
 #include <atomic>
+#include <cmath>
 #include <cstdlib>
 #include <cstring>
 
@@ -59,6 +60,8 @@ int finish(hipError_t e) { return e == hipSuccess ? SVDQ_OK : SVDQ_ERR_HIP; }
 
 bool rank_ok(int r) { return r >= 0 && r <= 128 && (r % 16) == 0; }
 bool k_ok(int K) { return K >= 128 && K <= 65536 && (K % 128) == 0; }
+bool k_nv_ok(int K) { return K >= 256 && K <= 65536 && (K % 256) == 0; }
+bool positive_finite(float v) { return std::isfinite(v) && v > 0.0f; }
 
 }  // namespace
 
@@ -143,6 +146,45 @@ int svdq_gemm_w4a4_qkv(int fmt, int M, int N, int K, int r, const uint8_t* act_c
   const svdq::QkvEpilogue qe{qk_norm_w, rope, eps, N / 384};
   return finish(svdq::launch_gemm_w4a4(fmt, M, N, K, r, act_codes, act_scales, lora_act, w_codes,
                                        w_scales, lora_up, bias, 2, Y, (hipStream_t)stream, &qe));
+}
+
+int svdq_quantize_act_nvfp4(int M, int K, int r, const void* X, const float* smooth_inv,
+                            const void* lora_down, float act_gscale, uint8_t* act_codes,
+                            uint8_t* act_scales, void* lora_act, void* stream) {
+  if (M < 0 || !k_nv_ok(K) || !rank_ok(r)) return SVDQ_ERR_SHAPE;
+  if (!positive_finite(act_gscale) || !positive_finite(6.0f * act_gscale)) return SVDQ_ERR_INVALID_ARG;
+  if (M == 0) return SVDQ_OK;
+  if (!X || !smooth_inv || !act_codes || !act_scales) return SVDQ_ERR_INVALID_ARG;
+  if (r > 0 && (!lora_down || !lora_act)) return SVDQ_ERR_INVALID_ARG;
+  if (!aligned16(X) || !aligned16(smooth_inv) || !aligned16(act_codes) || !aligned16(act_scales))
+    return SVDQ_ERR_ALIGN;
+  if (r > 0 && (!aligned16(lora_down) || !aligned16(lora_act))) return SVDQ_ERR_ALIGN;
+  const int dc = check_current_device();
+  if (dc != SVDQ_OK) return dc;
+  (void)hipGetLastError();
+  return finish(svdq::launch_quantize_act(SVDQ_NVFP4_G16, M, K, r, X, smooth_inv, lora_down, act_codes,
+                                          act_scales, lora_act, (hipStream_t)stream, act_gscale));
+}
+
+int svdq_gemm_nvfp4(int M, int N, int K, int r, const uint8_t* act_codes, const uint8_t* act_scales,
+                    const void* lora_act, const uint8_t* w_codes, const uint8_t* w_scales,
+                    const void* lora_up, const void* bias, float alpha, int epilogue, void* Y,
+                    void* stream) {
+  if (epilogue != SVDQ_EPI_NONE && epilogue != SVDQ_EPI_GELU_TANH) return SVDQ_ERR_INVALID_ARG;
+  if (!std::isfinite(alpha)) return SVDQ_ERR_INVALID_ARG;
+  if (M < 0 || N < 128 || N > 65536 || (N % 128) != 0 || !k_nv_ok(K) || !rank_ok(r)) return SVDQ_ERR_SHAPE;
+  if (M == 0) return SVDQ_OK;
+  if (!act_codes || !act_scales || !w_codes || !w_scales || !Y) return SVDQ_ERR_INVALID_ARG;
+  if (r > 0 && (!lora_act || !lora_up)) return SVDQ_ERR_INVALID_ARG;
+  if (!aligned16(act_codes) || !aligned16(act_scales) || !aligned16(w_codes) || !aligned16(w_scales) ||
+      !aligned16(Y) || (bias && !aligned16(bias)))
+    return SVDQ_ERR_ALIGN;
+  if (r > 0 && (!aligned16(lora_act) || !aligned16(lora_up))) return SVDQ_ERR_ALIGN;
+  const int dc = check_current_device();
+  if (dc != SVDQ_OK) return dc;
+  (void)hipGetLastError();
+  return finish(svdq::launch_gemm_nvfp4(M, N, K, r, act_codes, act_scales, lora_act, w_codes, w_scales,
+                                        lora_up, bias, alpha, epilogue, Y, (hipStream_t)stream));
 }
 
 int awq_gemv_w4a16(int M, int N, int K, int group, const void* x, const uint8_t* w_codes,

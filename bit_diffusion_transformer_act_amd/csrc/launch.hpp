@@ -6,9 +6,10 @@
 
 namespace svdq {
 
+// fmt 0 INT4 g64, 1 FP4 E2M1 b32, 2 NVFP4 (gscale: the per-tensor scale)
 hipError_t launch_quantize_act(int fmt, int M, int K, int r, const void* X, const float* smooth_inv,
                                const void* lora_down, uint8_t* codes, void* scales, void* lora_act,
-                               hipStream_t stream);
+                               hipStream_t stream, float gscale = 1.0f);
 
 // Parameters of the fused QKV epilogue (epi == 2): per-head RMSNorm of the Q
 // and K thirds of the output (heads of 128 channels, `heads` per third) with
@@ -30,6 +31,12 @@ hipError_t launch_gemm_fp4_big(int M, int N, int K, int r, const uint8_t* act_co
                                const void* act_scales, const void* lora_act, const uint8_t* w_codes,
                                const void* w_scales, const void* lora_up, const void* bias, int epi,
                                void* Y, hipStream_t stream);
+
+// NVFP4 GEMM: Y = act(alpha * sum (q_x s_x)(q_w s_w) + lora_act lora_up^T + bias)
+hipError_t launch_gemm_nvfp4(int M, int N, int K, int r, const uint8_t* act_codes,
+                             const uint8_t* act_scales, const void* lora_act, const uint8_t* w_codes,
+                             const uint8_t* w_scales, const void* lora_up, const void* bias, float alpha,
+                             int epi, void* Y, hipStream_t stream);
 
 hipError_t launch_awq_gemv(int M, int N, int K, const void* x, const uint8_t* codes,
                            const void* scales, const void* zeros, const void* bias, void* y,

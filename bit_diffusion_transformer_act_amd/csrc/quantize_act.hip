@@ -32,10 +32,28 @@ namespace svdq {
 
 constexpr int kQuantLdsMax = 144 * 1024;   // LDS budget per workgroup (gfx950 has 160 KB)
 
-// LDS bytes besides smooth_inv: two round buffers and the low-rank partials
+// LDS bytes besides smooth_inv: two round buffers (sized for the 4 scale
+// bytes per step of NVFP4) and the low-rank partials
 template <int WAVES>
 constexpr size_t quant_lds_bytes(int ncb) {
-  return 2 * (size_t)(16 * (WAVES * 32 + 16) + 16 * WAVES * 2) + (size_t)WAVES * 16 * 16 * ncb * sizeof(float);
+  return 2 * (size_t)(16 * (WAVES * 32 + 16) + 16 * WAVES * 4) + (size_t)WAVES * 16 * 16 * ncb * sizeof(float);
+}
+
+// E4M3 (OCP FP8, bias 7) byte of a non-negative fp32 value: round to nearest,
+// ties to the even mantissa, saturating at 448 (0x7E). Below 2^-6 the quantum
+// is 2^-9 (a * 512 is exact); above, the fp32 mantissa is rounded to 3 bits in
+// the integer domain (a carry moves into the exponent, as it should).
+__device__ __forceinline__ uint32_t e4m3_rne_byte(float a) {
+  if (!(a < 448.0f)) return 0x7Eu;
+  if (a < 0.015625f) return (uint32_t)__builtin_rintf(a * 512.0f);
+  uint32_t b = __float_as_uint(a);
+  b += 0x7FFFFu + ((b >> 20) & 1u);
+  return min((b >> 20) - ((127u - 7u) << 3), 0x7Eu);
+}
+
+// value of an E4M3 byte below 0x7F (exact in fp32)
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  return c < 8u ? (float)c * 0.001953125f : __uint_as_float((((c >> 3) + 120u) << 23) | ((c & 7u) << 20));
 }
 
 template <int FMT, int NCB, int WAVES, bool SLDS>
@@ -43,7 +61,7 @@ __global__ __launch_bounds__(64 * WAVES)
 void quantize_act_kernel(const __half* __restrict__ X, const float* __restrict__ smooth_inv,
                          const __half* __restrict__ lora_down, uint8_t* __restrict__ codes,
                          void* __restrict__ scales, __half* __restrict__ lora_act,
-                         int M, int K) {
+                         int M, int K, float gs, float gs6) {
 #pragma clang fp contract(off)
   // LDS: two round buffers (codes, then scales, of 16 rows x WAVES steps),
   // [WAVES][16 rows][16 * NCB] low-rank partials, then smooth_inv[K] if SLDS
@@ -51,7 +69,8 @@ void quantize_act_kernel(const __half* __restrict__ X, const float* __restrict__
   constexpr int R = 16 * NCB;
   constexpr int NL = NCB > 0 ? NCB : 1;
   constexpr int CROW = WAVES * 32 + 16;         // padded code row of a round (bytes)
-  constexpr int SROW = WAVES * 2;               // scale row of a round (bytes)
+  constexpr int SB = FMT == 2 ? 4 : 2;          // scale bytes per row and step
+  constexpr int SROW = WAVES * SB;              // scale row of a round (bytes)
   constexpr int RBUF = 16 * CROW + 16 * SROW;   // one round buffer (bytes, multiple of 16)
   uint8_t* rbuf = reinterpret_cast<uint8_t*>(lds_f);
   float* red = lds_f + 2 * RBUF / 4;
@@ -194,7 +213,7 @@ void quantize_act_kernel(const __half* __restrict__ X, const float* __restrict__
       }
     }
     uint8_t* crow = rb + (lane & 15) * CROW + wave * 32 + q4 * 4;
-    uint8_t* srow = rb + 16 * CROW + (lane & 15) * SROW + wave * 2;
+    uint8_t* srow = rb + 16 * CROW + (lane & 15) * SROW + wave * SB;
     if constexpr (FMT == 0) {
       // INT4, group 64 = this step: reduce over the four lanes of the row.
       float amax = 0.f;
@@ -226,6 +245,41 @@ void quantize_act_kernel(const __half* __restrict__ X, const float* __restrict__
       *reinterpret_cast<uint32_t*>(crow) = w0;
       *reinterpret_cast<uint32_t*>(crow + 16) = w1;
       if (q4 == 0) *reinterpret_cast<__half*>(srow) = s16;
+    } else if constexpr (FMT == 2) {
+      // NVFP4, block 16 = a quarter step: xh[0..7] and lane l ^ 16's xh[0..7]
+      // form block 4s + q4 / 2, xh[8..15] likewise block 4s + 2 + q4 / 2.
+      // s = E4M3(fl32(amax / fl32(6 g))), divisor d = fl32(E4M3(s) g), codes
+      // E2M1(fl32(x_hat / d)) with the IEEE division; the convert (scale 1)
+      // rounds to nearest, ties to even, saturates at 6 and keeps the sign.
+      float am0 = 0.f, am1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        am0 = fmaxf(am0, fabsf(xh[i]));
+        am1 = fmaxf(am1, fabsf(xh[8 + i]));
+      }
+      am0 = lane_max_xor16(am0);
+      am1 = lane_max_xor16(am1);
+      uint32_t w[2], sc[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float* v = xh + 8 * h;
+        sc[h] = e4m3_rne_byte((h ? am1 : am0) / gs6);
+        const float d = e4m3_to_f32(sc[h]) * gs;
+        w[h] = 0;
+        if (d != 0.0f) {
+          w[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[h], v[0] / d, v[1] / d, 1.0f, 0);
+          w[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[h], v[2] / d, v[3] / d, 1.0f, 1);
+          w[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[h], v[4] / d, v[5] / d, 1.0f, 2);
+          w[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[h], v[6] / d, v[7] / d, 1.0f, 3);
+        }
+      }
+      *reinterpret_cast<uint32_t*>(crow) = w[0];
+      *reinterpret_cast<uint32_t*>(crow + 16) = w[1];
+      // scale bytes of the step: [block 0, 1, 2, 3] = lanes q4 0 / 2 (xh[0..7]) and (xh[8..15])
+      if ((q4 & 1) == 0) {
+        srow[q4 >> 1] = (uint8_t)sc[0];
+        srow[2 + (q4 >> 1)] = (uint8_t)sc[1];
+      }
     } else {
       // FP4 E2M1, block 32 = half a step: xh[0..7] belong to block 2s, xh[8..15]
       // to block 2s + 1; each block is reduced over the four lanes of the row.
@@ -268,10 +322,15 @@ void quantize_act_kernel(const __half* __restrict__ X, const float* __restrict__
     }
     for (int c = threadIdx.x; c < 16 * WAVES; c += 64 * WAVES) {
       const int rl = c / WAVES, j = c - rl * WAVES;
-      if (j < vs && m0 + rl < M)
-        *reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(scales) + (size_t)(m0 + rl) * (K >> 5) +
-                                     (size_t)(p * WAVES + j) * 2) =
-            *reinterpret_cast<const uint16_t*>(rb + 16 * CROW + rl * SROW + j * 2);
+      if (j < vs && m0 + rl < M) {
+        // a row holds SB scale bytes per 64-channel step
+        uint8_t* dst = reinterpret_cast<uint8_t*>(scales) + (size_t)(m0 + rl) * (size_t)((K >> 6) * SB) +
+                       (size_t)(p * WAVES + j) * SB;
+        if constexpr (SB == 4)
+          *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(rb + 16 * CROW + rl * SROW + j * 4);
+        else
+          *reinterpret_cast<uint16_t*>(dst) = *reinterpret_cast<const uint16_t*>(rb + 16 * CROW + rl * SROW + j * 2);
+      }
     }
     // the buffer is rewritten two rounds later, after the next round's barrier,
     // by which time every wave has finished reading it here
@@ -326,7 +385,7 @@ void quantize_act_kernel(const __half* __restrict__ X, const float* __restrict__
 
 template <int FMT, int NCB, int WAVES, bool SLDS>
 static hipError_t launch_qws(int M, int K, const void* X, const float* si, const void* ld,
-                             uint8_t* codes, void* scales, void* la, hipStream_t st) {
+                             uint8_t* codes, void* scales, void* la, float gs, hipStream_t st) {
   const dim3 grid((M + 15) / 16), block(64 * WAVES);
   const size_t lds = quant_lds_bytes<WAVES>(NCB) + (SLDS ? (size_t)K * sizeof(float) : 0);
   if (lds > 65536) {
@@ -341,17 +400,18 @@ static hipError_t launch_qws(int M, int K, const void* X, const float* si, const
     }
   }
   hipLaunchKernelGGL((quantize_act_kernel<FMT, NCB, WAVES, SLDS>), grid, block, lds, st,
-                     (const __half*)X, si, (const __half*)ld, codes, scales, (__half*)la, M, K);
+                     (const __half*)X, si, (const __half*)ld, codes, scales, (__half*)la, M, K, gs,
+                     6.0f * gs);
   return hipGetLastError();
 }
 
 // smooth_inv goes to LDS when it fits beside the low-rank partials
 template <int FMT, int NCB, int WAVES>
 static hipError_t launch_qw(int M, int K, const void* X, const float* si, const void* ld,
-                            uint8_t* codes, void* scales, void* la, hipStream_t st) {
+                            uint8_t* codes, void* scales, void* la, float gs, hipStream_t st) {
   if (quant_lds_bytes<WAVES>(NCB) + (size_t)K * sizeof(float) <= (size_t)kQuantLdsMax)
-    return launch_qws<FMT, NCB, WAVES, true>(M, K, X, si, ld, codes, scales, la, st);
-  return launch_qws<FMT, NCB, WAVES, false>(M, K, X, si, ld, codes, scales, la, st);
+    return launch_qws<FMT, NCB, WAVES, true>(M, K, X, si, ld, codes, scales, la, gs, st);
+  return launch_qws<FMT, NCB, WAVES, false>(M, K, X, si, ld, codes, scales, la, gs, st);
 }
 
 // 16 rows per workgroup. With at least one workgroup per CU, 8 waves (2 per
@@ -361,38 +421,39 @@ static hipError_t launch_qw(int M, int K, const void* X, const float* si, const 
 // 8 * r / 16 VGPRs per set).
 template <int FMT, int NCB>
 static hipError_t launch_q(int M, int K, const void* X, const float* si, const void* ld,
-                           uint8_t* codes, void* scales, void* la, hipStream_t st) {
+                           uint8_t* codes, void* scales, void* la, float gs, hipStream_t st) {
   if constexpr (NCB >= 7) {
-    return launch_qw<FMT, NCB, 4>(M, K, X, si, ld, codes, scales, la, st);
+    return launch_qw<FMT, NCB, 4>(M, K, X, si, ld, codes, scales, la, gs, st);
   } else if constexpr (NCB > 2) {
-    return launch_qw<FMT, NCB, 8>(M, K, X, si, ld, codes, scales, la, st);
+    return launch_qw<FMT, NCB, 8>(M, K, X, si, ld, codes, scales, la, gs, st);
   } else {
-    if ((M + 15) / 16 >= 256) return launch_qw<FMT, NCB, 8>(M, K, X, si, ld, codes, scales, la, st);
-    return launch_qw<FMT, NCB, 16>(M, K, X, si, ld, codes, scales, la, st);
+    if ((M + 15) / 16 >= 256) return launch_qw<FMT, NCB, 8>(M, K, X, si, ld, codes, scales, la, gs, st);
+    return launch_qw<FMT, NCB, 16>(M, K, X, si, ld, codes, scales, la, gs, st);
   }
 }
 
 template <int FMT>
 static hipError_t launch_q_r(int M, int K, int r, const void* X, const float* si, const void* ld,
-                             uint8_t* codes, void* scales, void* la, hipStream_t st) {
+                             uint8_t* codes, void* scales, void* la, float gs, hipStream_t st) {
   switch (r / 16) {
-    case 0: return launch_q<FMT, 0>(M, K, X, si, ld, codes, scales, la, st);
-    case 1: return launch_q<FMT, 1>(M, K, X, si, ld, codes, scales, la, st);
-    case 2: return launch_q<FMT, 2>(M, K, X, si, ld, codes, scales, la, st);
-    case 3: return launch_q<FMT, 3>(M, K, X, si, ld, codes, scales, la, st);
-    case 4: return launch_q<FMT, 4>(M, K, X, si, ld, codes, scales, la, st);
-    case 5: return launch_q<FMT, 5>(M, K, X, si, ld, codes, scales, la, st);
-    case 6: return launch_q<FMT, 6>(M, K, X, si, ld, codes, scales, la, st);
-    case 7: return launch_q<FMT, 7>(M, K, X, si, ld, codes, scales, la, st);
-    default: return launch_q<FMT, 8>(M, K, X, si, ld, codes, scales, la, st);
+    case 0: return launch_q<FMT, 0>(M, K, X, si, ld, codes, scales, la, gs, st);
+    case 1: return launch_q<FMT, 1>(M, K, X, si, ld, codes, scales, la, gs, st);
+    case 2: return launch_q<FMT, 2>(M, K, X, si, ld, codes, scales, la, gs, st);
+    case 3: return launch_q<FMT, 3>(M, K, X, si, ld, codes, scales, la, gs, st);
+    case 4: return launch_q<FMT, 4>(M, K, X, si, ld, codes, scales, la, gs, st);
+    case 5: return launch_q<FMT, 5>(M, K, X, si, ld, codes, scales, la, gs, st);
+    case 6: return launch_q<FMT, 6>(M, K, X, si, ld, codes, scales, la, gs, st);
+    case 7: return launch_q<FMT, 7>(M, K, X, si, ld, codes, scales, la, gs, st);
+    default: return launch_q<FMT, 8>(M, K, X, si, ld, codes, scales, la, gs, st);
   }
 }
 
 hipError_t launch_quantize_act(int fmt, int M, int K, int r, const void* X, const float* si,
                                const void* ld, uint8_t* codes, void* scales, void* la,
-                               hipStream_t st) {
-  if (fmt == 0) return launch_q_r<0>(M, K, r, X, si, ld, codes, scales, la, st);
-  return launch_q_r<1>(M, K, r, X, si, ld, codes, scales, la, st);
+                               hipStream_t st, float gscale) {
+  if (fmt == 0) return launch_q_r<0>(M, K, r, X, si, ld, codes, scales, la, 1.0f, st);
+  if (fmt == 2) return launch_q_r<2>(M, K, r, X, si, ld, codes, scales, la, gscale, st);
+  return launch_q_r<1>(M, K, r, X, si, ld, codes, scales, la, 1.0f, st);
 }
 
 }  // namespace svdq

@@ -17,6 +17,7 @@ dequantize-to-dense fallback, and a module on a CPU tensor raises.
 """
 from __future__ import annotations
 
+import numpy as np
 import torch
 from torch import nn
 
@@ -40,8 +41,11 @@ class SVDQLinear(nn.Module):
     Buffers (the layout the C ABI takes, N = out_features, K = in_features):
       smooth_inv fp32 [K]; lora_down fp16 [r][K]; lora_up fp16 [N][r];
       w_codes u8 [N][K/2] (even-k code in the low nibble);
-      w_scales fp16 [N][K/64] (int4_g64) or E8M0 u8 [N][K/32] (fp4_b32);
-      bias fp16 [N] when bias=True.
+      w_scales fp16 [N][K/64] (int4_g64), E8M0 u8 [N][K/32] (fp4_b32) or
+      E4M3 u8 [N][K/16] (nvfp4_g16);
+      bias fp16 [N] when bias=True;
+      nvfp4_g16 only: act_gscale and w_gscale, fp32 scalars (the per-tensor
+      scales of the activations, fixed from calibration, and of the weight).
     epilogue "gelu_tanh" applies the tanh-approximated GELU inside the GEMM.
     """
 
@@ -49,18 +53,21 @@ class SVDQLinear(nn.Module):
                  fmt: str = "int4_g64", bias: bool = True, epilogue: str = "none",
                  device=None):
         super().__init__()
-        if fmt not in ops.FORMATS:
+        if fmt not in ops.ALL_FORMATS:
             raise ValueError(f"unknown format {fmt!r}")
         if epilogue not in ops.EPILOGUES:
             raise ValueError(f"unknown epilogue {epilogue!r}")
         if in_features % 128 or out_features % 128:
             raise ValueError("SVDQLinear needs in_features and out_features divisible by 128")
+        if fmt == "nvfp4_g16" and in_features % 256:
+            raise ValueError("nvfp4_g16 needs in_features divisible by 256")
         if rank % 16 or not 0 <= rank <= 128:
             raise ValueError("rank must be a multiple of 16 in [0, 128]")
         K, N = in_features, out_features
         self.in_features, self.out_features, self.rank = K, N, rank
         self.fmt, self.epilogue = fmt, epilogue
-        sdt, sg = (torch.float16, 64) if fmt == "int4_g64" else (torch.uint8, 32)
+        sdt, sg = {"int4_g64": (torch.float16, 64), "fp4_b32": (torch.uint8, 32),
+                   "nvfp4_g16": (torch.uint8, 16)}[fmt]
         kw = {"device": device}
         self.register_buffer("smooth_inv", torch.ones(K, dtype=torch.float32, **kw))
         self.register_buffer("lora_down", torch.zeros(rank, K, dtype=torch.float16, **kw))
@@ -71,6 +78,27 @@ class SVDQLinear(nn.Module):
             self.register_buffer("bias", torch.zeros(N, dtype=torch.float16, **kw))
         else:
             self.bias = None
+        if fmt == "nvfp4_g16":
+            # fp32 scalars kept on the host: the kernels take them by value, and
+            # reading a device scalar would synchronize every call
+            self.register_buffer("act_gscale", torch.ones((), dtype=torch.float32))
+            self.register_buffer("w_gscale", torch.ones((), dtype=torch.float32))
+            self._gs, self._alpha = (1.0, 1.0), 1.0
+            self.register_load_state_dict_post_hook(SVDQLinear._cache_gscales)
+
+    @staticmethod
+    def _cache_gscales(module, incompatible_keys):
+        a, w = np.float32(module.act_gscale.cpu()), np.float32(module.w_gscale.cpu())
+        module._gs = (float(a), float(w))
+        module._alpha = float(a * w)        # the fp32 product the GEMM scales its 4-bit sum by
+
+    def _apply(self, fn, *args, **kwargs):
+        # the per-tensor scales stay on the host whatever device the module moves to
+        out = super()._apply(fn, *args, **kwargs)
+        if self.fmt == "nvfp4_g16":
+            self.act_gscale = self.act_gscale.cpu()
+            self.w_gscale = self.w_gscale.cpu()
+        return out
 
     def extra_repr(self) -> str:
         return (f"in_features={self.in_features}, out_features={self.out_features}, "
@@ -79,14 +107,20 @@ class SVDQLinear(nn.Module):
     def quantize_input(self, x: torch.Tensor):
         """The first fused call: 4-bit codes, scales and the low-rank activation."""
         X = _as_rows(x, self.in_features, "SVDQLinear")
-        return ops.svdq_quantize_act(X, self.smooth_inv, self.lora_down if self.rank else None,
-                                     self.fmt)
+        ld = self.lora_down if self.rank else None
+        if self.fmt == "nvfp4_g16":
+            return ops.svdq_quantize_act_nvfp4(X, self.smooth_inv, ld, self._gs[0])
+        return ops.svdq_quantize_act(X, self.smooth_inv, ld, self.fmt)
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         codes, scales, la = self.quantize_input(x)
-        y = ops.svdq_gemm_w4a4(codes, scales, la, self.w_codes, self.w_scales,
-                               self.lora_up if self.rank else None, self.bias, self.fmt,
-                               self.epilogue)
+        lu = self.lora_up if self.rank else None
+        if self.fmt == "nvfp4_g16":
+            y = ops.svdq_gemm_nvfp4(codes, scales, la, self.w_codes, self.w_scales, lu, self.bias,
+                                    self._alpha, self.epilogue)
+        else:
+            y = ops.svdq_gemm_w4a4(codes, scales, la, self.w_codes, self.w_scales, lu, self.bias,
+                                   self.fmt, self.epilogue)
         return y.reshape(*x.shape[:-1], self.out_features)
 
 

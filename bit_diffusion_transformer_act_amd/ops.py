@@ -18,7 +18,10 @@ from .build import LIB_PATH
 
 INT4_G64 = 0
 FP4_E2M1_B32 = 1
+NVFP4_G16 = 2
+# formats of svdq_quantize_act / svdq_gemm_w4a4; NVFP4 has entry points of its own
 FORMATS = {"int4_g64": INT4_G64, "fp4_b32": FP4_E2M1_B32}
+ALL_FORMATS = ("int4_g64", "fp4_b32", "nvfp4_g16")
 EPI_NONE = 0
 EPI_GELU_TANH = 1
 EPILOGUES = {"none": EPI_NONE, "gelu_tanh": EPI_GELU_TANH}
@@ -31,7 +34,8 @@ SVDQ_ERR_UNSUPPORTED_DEVICE = -4
 SVDQ_ERR_HIP = -5
 
 EXPORTED_SYMBOLS = ("svdq_device_check", "svdq_status_str", "svdq_version",
-                    "svdq_quantize_act", "svdq_gemm_w4a4", "svdq_gemm_w4a4_qkv", "awq_gemv_w4a16")
+                    "svdq_quantize_act", "svdq_gemm_w4a4", "svdq_gemm_w4a4_qkv",
+                    "svdq_quantize_act_nvfp4", "svdq_gemm_nvfp4", "awq_gemv_w4a16")
 
 _lock = threading.Lock()
 _handle = None
@@ -67,6 +71,11 @@ def lib() -> ctypes.CDLL:
             h.svdq_gemm_w4a4_qkv.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                              ctypes.c_float, vp, vp]
             h.svdq_gemm_w4a4_qkv.restype = i32
+            f32 = ctypes.c_float
+            h.svdq_quantize_act_nvfp4.argtypes = [i32, i32, i32, vp, vp, vp, f32, vp, vp, vp, vp]
+            h.svdq_quantize_act_nvfp4.restype = i32
+            h.svdq_gemm_nvfp4.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, f32, i32, vp, vp]
+            h.svdq_gemm_nvfp4.restype = i32
             h.awq_gemv_w4a16.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
             h.awq_gemv_w4a16.restype = i32
             _handle = h
@@ -230,6 +239,73 @@ def svdq_gemm_w4a4_qkv(act_codes, act_scales, lora_act, w_codes, w_scales, lora_
                                       _ptr(rope), ctypes.c_float(eps), _ptr(out), _stream(dev))
     if st != SVDQ_OK:
         raise SvdqError(st, "svdq_gemm_w4a4_qkv")
+    return out
+
+
+def svdq_quantize_act_nvfp4(X: torch.Tensor, smooth_inv: torch.Tensor, lora_down, act_gscale: float,
+                            act_codes=None, act_scales=None, lora_act=None):
+    """NVFP4 activation quantizer (E2M1 codes, E4M3 scale per 16, per-tensor
+    scale act_gscale) + smoothing + low-rank down-projection.
+    Returns (act_codes u8 [M][K/2], act_scales u8 [M][K/16], lora_act fp16 [M][r] or None)."""
+    dev = X.device
+    if dev.type != "cuda":
+        raise ValueError("X must be a HIP device tensor")
+    M, K = X.shape
+    r = 0 if lora_down is None else lora_down.shape[0]
+    _check(X, "X", torch.float16, (M, K), dev)
+    _check(smooth_inv, "smooth_inv", torch.float32, (K,), dev)
+    if lora_down is not None:
+        _check(lora_down, "lora_down", torch.float16, (r, K), dev)
+    if act_codes is None:
+        act_codes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    if act_scales is None:
+        act_scales = torch.empty((M, K // 16), dtype=torch.uint8, device=dev)
+    if r > 0 and lora_act is None:
+        lora_act = torch.empty((M, r), dtype=torch.float16, device=dev)
+    _check(act_codes, "act_codes", torch.uint8, (M, K // 2), dev)
+    _check(act_scales, "act_scales", torch.uint8, (M, K // 16), dev)
+    if r > 0:
+        _check(lora_act, "lora_act", torch.float16, (M, r), dev)
+    with torch.cuda.device(dev):
+        st = lib().svdq_quantize_act_nvfp4(M, K, r, _ptr(X), _ptr(smooth_inv), _ptr(lora_down),
+                                           ctypes.c_float(act_gscale), _ptr(act_codes), _ptr(act_scales),
+                                           _ptr(lora_act) if r > 0 else None, _stream(dev))
+    if st != SVDQ_OK:
+        raise SvdqError(st, "svdq_quantize_act_nvfp4")
+    return act_codes, act_scales, (lora_act if r > 0 else None)
+
+
+def svdq_gemm_nvfp4(act_codes, act_scales, lora_act, w_codes, w_scales, lora_up, bias, alpha: float,
+                    epilogue="none", out=None):
+    """NVFP4 GEMM + low-rank up-projection + bias (+ GELU) -> Y fp16 [M][N];
+    alpha = act_gscale * w_gscale scales the 4-bit sum."""
+    e = EPILOGUES[epilogue] if isinstance(epilogue, str) else int(epilogue)
+    dev = act_codes.device
+    if dev.type != "cuda":
+        raise ValueError("act_codes must be a HIP device tensor")
+    M, KB = act_codes.shape
+    K = 2 * KB
+    N = w_codes.shape[0]
+    r = 0 if lora_up is None else lora_up.shape[1]
+    _check(act_codes, "act_codes", torch.uint8, (M, KB), dev)
+    _check(act_scales, "act_scales", torch.uint8, (M, K // 16), dev)
+    _check(w_codes, "w_codes", torch.uint8, (N, KB), dev)
+    _check(w_scales, "w_scales", torch.uint8, (N, K // 16), dev)
+    if r > 0:
+        _check(lora_act, "lora_act", torch.float16, (M, r), dev)
+        _check(lora_up, "lora_up", torch.float16, (N, r), dev)
+    if bias is not None:
+        _check(bias, "bias", torch.float16, (N,), dev)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=dev)
+    _check(out, "out", torch.float16, (M, N), dev)
+    with torch.cuda.device(dev):
+        st = lib().svdq_gemm_nvfp4(M, N, K, r, _ptr(act_codes), _ptr(act_scales),
+                                   _ptr(lora_act) if r > 0 else None, _ptr(w_codes), _ptr(w_scales),
+                                   _ptr(lora_up) if r > 0 else None, _ptr(bias), ctypes.c_float(alpha), e,
+                                   _ptr(out), _stream(dev))
+    if st != SVDQ_OK:
+        raise SvdqError(st, "svdq_gemm_nvfp4")
     return out
 
 

@@ -63,8 +63,12 @@ typedef enum {
  * (dothoosh.com article, kernel-family list and quantization_config block).
  * SVDQ_INT4_G64: symmetric INT4, one fp16 scale per 64 values along K.
  * SVDQ_FP4_E2M1_B32: OCP E2M1 codes, one E8M0 (power-of-two) scale byte per
- *   32 values along K -- the block-scaled form CDNA4's matrix cores consume. */
-typedef enum { SVDQ_INT4_G64 = 0, SVDQ_FP4_E2M1_B32 = 1 } svdq_format;
+ *   32 values along K -- the block-scaled form CDNA4's matrix cores consume.
+ * SVDQ_NVFP4_G16: the pages' own float format: OCP E2M1 codes, one OCP FP8
+ *   E4M3 scale byte per 16 values along K and one fp32 scale per tensor; it
+ *   has entry points of its own (svdq_quantize_act_nvfp4, svdq_gemm_nvfp4),
+ *   which carry the per-tensor scales. */
+typedef enum { SVDQ_INT4_G64 = 0, SVDQ_FP4_E2M1_B32 = 1, SVDQ_NVFP4_G16 = 2 } svdq_format;
 
 /* Epilogue applied after the bias: identity, or GELU in its tanh form
  * y/2 (1 + tanh(sqrt(2/pi) (y + 0.044715 y^3))) for MLP up-projections
@@ -186,6 +190,54 @@ int svdq_gemm_w4a4_qkv(int fmt, int M, int N, int K, int r,
                        const uint8_t* w_codes, const void* w_scales, const void* lora_up,
                        const void* bias, const void* qk_norm_w, const float* rope, float eps,
                        void* Y, void* stream);
+
+/*
+ * svdq_quantize_act_nvfp4 -- svdq_quantize_act for NVFP4 (the pages' svdq_w4a4
+ * precision "nvfp4" with group size 16: dothoosh.com article,
+ * quantization_config block). Smoothing and the low-rank down-projection as
+ * in svdq_quantize_act; then, per block of 16 values of x_hat along K, with
+ * the activations' per-tensor scale g (fixed offline from calibration data):
+ *
+ *   s    = E4M3_rne( fl32( amax / fl32(6 g) ) )   saturating at 448 (0x7E);
+ *   d    = fl32( E4M3(s) * g );
+ *   code = E2M1_rne( fl32( x_hat / d ) )          (IEEE division; nearest,
+ *          ties to even mantissa, saturating at 6, sign from x_hat; all codes
+ *          0 where d == 0).
+ *
+ * A value is E2M1(code) * E4M3(s) * g. Codes and scales are bit-exact.
+ *
+ * Arguments as svdq_quantize_act, except:
+ *   K           K % 256 == 0, 256 <= K <= 65536.
+ *   act_gscale  g, finite and > 0 (else SVDQ_ERR_INVALID_ARG).
+ *   act_scales  out, u8 [M][K/16] E4M3 bytes (sign bit 0).
+ */
+int svdq_quantize_act_nvfp4(int M, int K, int r,
+                            const void* X, const float* smooth_inv, const void* lora_down,
+                            float act_gscale, uint8_t* act_codes, uint8_t* act_scales,
+                            void* lora_act, void* stream);
+
+/*
+ * svdq_gemm_nvfp4 -- svdq_gemm_w4a4 for NVFP4 operands:
+ *
+ *   Y[m,n] = act( alpha * sum_k (E2M1(q_x[m,k]) E4M3(s_x[m,k/16]))
+ *                               (E2M1(q_w[n,k]) E4M3(s_w[n,k/16]))
+ *               + sum_j lora_act[m,j] lora_up[n,j] + bias[n] )     -> fp16 (RNE)
+ *
+ * with alpha = act_gscale * w_gscale (the two per-tensor scales; the caller
+ * forms the product). gfx950 has no matrix instruction for E4M3 scales per
+ * 16, so both operands are dequantized exactly to fp16 and multiplied on the
+ * fp16 matrix cores with fp32 accumulation.
+ *
+ * Arguments as svdq_gemm_w4a4, except:
+ *   K           K % 256 == 0, 256 <= K <= 65536.
+ *   act_scales  u8 [M][K/16], w_scales u8 [N][K/16]: E4M3 bytes; the sign bit
+ *               is ignored (scales are magnitudes).
+ *   alpha       finite (else SVDQ_ERR_INVALID_ARG).
+ */
+int svdq_gemm_nvfp4(int M, int N, int K, int r,
+                    const uint8_t* act_codes, const uint8_t* act_scales, const void* lora_act,
+                    const uint8_t* w_codes, const uint8_t* w_scales, const void* lora_up,
+                    const void* bias, float alpha, int epilogue, void* Y, void* stream);
 
 /*
  * awq_gemv_w4a16 -- 4-bit weights, 16-bit activations, memory-bound GEMV for

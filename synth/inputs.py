@@ -39,7 +39,7 @@ class LayerConfig:
     K: int
     N: int
     rank: int
-    fmt: str            # "int4_g64" or "fp4_b32"
+    fmt: str            # "int4_g64", "fp4_b32" or "nvfp4_g16"
     epilogue: str       # "none", "gelu_tanh" or "qkv_norm_rope"
     x_dist: str         # "normal" or "gelu_normal"
     outlier_frac: float
@@ -50,7 +50,7 @@ class LayerConfig:
 
     @property
     def group(self) -> int:
-        return 64 if self.fmt == "int4_g64" else 32
+        return {"int4_g64": 64, "fp4_b32": 32, "nvfp4_g16": 16}[self.fmt]
 
 
 @dataclass(frozen=True)
@@ -90,6 +90,10 @@ CONFIGS = {
                             "none", "normal", 0.005, 30.0),
     "mlp_up_int4": LayerConfig("mlp_up_int4", 42, 4096, 3072, 12288, 32,
                                "int4_g64", "gelu_tanh", "normal", 0.005, 30.0),
+    # The MLP up-projection in the pages' own float format: NVFP4 (E2M1, E4M3
+    # scale per 16, fp32 scale per tensor), GELU(tanh).
+    "mlp_up_nvfp4": LayerConfig("mlp_up_nvfp4", 43, 4096, 3072, 12288, 32,
+                                "nvfp4_g16", "gelu_tanh", "normal", 0.005, 30.0),
     # Modulation projection of a DiT block: six 3072-wide vectors at M = 1.
     "gemv": GemvConfig("gemv", 4, 1, 3072, 18432, 64),
 }
@@ -178,11 +182,22 @@ def random_quantized_layer(cfg: LayerConfig, seed: int = 0, M: int | None = None
         lo = g.integers(0, 16, (N, K // 2))
         hi = g.integers(0, 16, (N, K // 2))
         w_scales = g.integers(119, 123, (N, K // 32)).astype(np.uint8)
+    elif cfg.fmt == "nvfp4_g16":
+        # E4M3 block scales spread over the upper binades (the per-tensor scale
+        # puts the largest block near 448), per-tensor scales of an N(0, 0.02^2)
+        # weight and of activations whose largest smoothed value is about 50
+        lo = g.integers(0, 16, (N, K // 2))
+        hi = g.integers(0, 16, (N, K // 2))
+        w_scales = g.integers(0x50, 0x7F, (N, K // 16)).astype(np.uint8)
     else:
         raise ValueError(cfg.fmt)
-    return {"X": X, "smooth_inv": smooth_inv, "lora_down": lora_down,
-            "w_codes": _nibble_bytes(lo, hi), "w_scales": w_scales,
-            "lora_up": lora_up, "bias": bias}
+    out = {"X": X, "smooth_inv": smooth_inv, "lora_down": lora_down,
+           "w_codes": _nibble_bytes(lo, hi), "w_scales": w_scales,
+           "lora_up": lora_up, "bias": bias}
+    if cfg.fmt == "nvfp4_g16":
+        out["w_gscale"] = np.float32(0.1 / 2688.0)
+        out["act_gscale"] = np.float32(50.0 / 2688.0)
+    return out
 
 
 def random_awq_layer(cfg: GemvConfig, seed: int = 0, M: int | None = None) -> dict:

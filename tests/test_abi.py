@@ -105,6 +105,40 @@ def test_gemv_argument_errors():
     assert v(b=A) == ops.SVDQ_ERR_UNSUPPORTED_DEVICE
 
 
+def qn(M=4, K=256, r=16, X=A, si=A, ld=A, g=0.5, codes=A, scales=A, la=A):
+    return P.lib().svdq_quantize_act_nvfp4(M, K, r, X, si, ld, ctypes.c_float(g), codes, scales, la, None)
+
+
+def gn(M=4, N=128, K=256, r=16, ac=A, sa=A, la=A, wc=A, ws=A, lu=A, b=None, alpha=1.0, epi=0, Y=A):
+    return P.lib().svdq_gemm_nvfp4(M, N, K, r, ac, sa, la, wc, ws, lu, b, ctypes.c_float(alpha), epi, Y, None)
+
+
+def test_nvfp4_argument_errors():
+    assert qn(K=128) == ops.SVDQ_ERR_SHAPE          # K % 256
+    assert qn(K=384) == ops.SVDQ_ERR_SHAPE
+    assert qn(r=8) == ops.SVDQ_ERR_SHAPE
+    assert qn(g=0.0) == ops.SVDQ_ERR_INVALID_ARG
+    assert qn(g=-1.0) == ops.SVDQ_ERR_INVALID_ARG
+    assert qn(g=float("inf")) == ops.SVDQ_ERR_INVALID_ARG
+    assert qn(g=1e38) == ops.SVDQ_ERR_INVALID_ARG     # 6 g overflows fp32
+    assert qn(M=0, X=None, si=None, ld=None, codes=None, scales=None, la=None) == ops.SVDQ_OK
+    assert qn(X=None) == ops.SVDQ_ERR_INVALID_ARG
+    assert qn(scales=U) == ops.SVDQ_ERR_ALIGN
+    assert qn() == ops.SVDQ_ERR_UNSUPPORTED_DEVICE
+    assert gn(epi=2) == ops.SVDQ_ERR_INVALID_ARG
+    assert gn(alpha=float("nan")) == ops.SVDQ_ERR_INVALID_ARG
+    assert gn(K=128) == ops.SVDQ_ERR_SHAPE
+    assert gn(N=64) == ops.SVDQ_ERR_SHAPE
+    assert gn(N=200) == ops.SVDQ_ERR_SHAPE
+    assert gn(r=144) == ops.SVDQ_ERR_SHAPE
+    assert gn(M=0, ac=None, sa=None, la=None, wc=None, ws=None, lu=None, Y=None) == ops.SVDQ_OK
+    assert gn(ws=None) == ops.SVDQ_ERR_INVALID_ARG
+    assert gn(lu=None) == ops.SVDQ_ERR_INVALID_ARG
+    assert gn(Y=U) == ops.SVDQ_ERR_ALIGN
+    assert gn(b=U) == ops.SVDQ_ERR_ALIGN
+    assert gn() == ops.SVDQ_ERR_UNSUPPORTED_DEVICE
+
+
 def test_device_check_without_gpu():
     assert P.svdq_device_check(0) == ops.SVDQ_ERR_UNSUPPORTED_DEVICE
     assert P.svdq_device_check(-1) == ops.SVDQ_ERR_UNSUPPORTED_DEVICE

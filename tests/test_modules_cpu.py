@@ -25,15 +25,15 @@ PAGES_EXAMPLE = {
 }
 
 
-def test_pages_example_is_rejected_with_a_reason():
+def test_pages_example_compute_dtype_is_rejected_with_a_reason():
     with pytest.raises(UnsupportedQuantConfig, match="bfloat16"):
         parse_quantization_config({"quantization_config": PAGES_EXAMPLE})
-    fp16 = dict(PAGES_EXAMPLE, compute_dtype="float16")
-    with pytest.raises(UnsupportedQuantConfig, match="nvfp4"):
-        parse_quantization_config(fp16)
+    q = parse_quantization_config(dict(PAGES_EXAMPLE, compute_dtype="float16"))
+    assert q.svdq.fmt == "nvfp4_g16" and q.svdq.rank == 32
 
 
-@pytest.mark.parametrize("prec,gs,fmt", [("int4", 64, "int4_g64"), ("mxfp4", 32, "fp4_b32")])
+@pytest.mark.parametrize("prec,gs,fmt", [("int4", 64, "int4_g64"), ("mxfp4", 32, "fp4_b32"),
+                                         ("nvfp4", 16, "nvfp4_g16")])
 def test_supported_precisions(prec, gs, fmt):
     cfg = copy.deepcopy(dict(PAGES_EXAMPLE, compute_dtype="float16"))
     cfg["svdq_w4a4"].update(precision=prec, group_size=gs)
@@ -54,6 +54,7 @@ def test_config_errors_and_wildcards():
     for bad, exc in [({"quant_method": "gptq"}, ValueError),
                      ({"compute_dtype": "float8"}, ValueError),
                      ({"svdq_w4a4": {"precision": "int4", "group_size": 128, "rank": 32}}, UnsupportedQuantConfig),
+                     ({"svdq_w4a4": {"precision": "nvfp4", "group_size": 32, "rank": 32}}, UnsupportedQuantConfig),
                      ({"svdq_w4a4": {"precision": "int4", "group_size": 64, "rank": 20}}, UnsupportedQuantConfig),
                      ({"svdq_w4a4": {"precision": "int4", "group_size": 64, "rank": 256}}, UnsupportedQuantConfig),
                      ({"svdq_w4a4": {"precision": "int4", "group_size": 64, "targets": "mlp.0"}}, ValueError)]:
@@ -120,3 +121,13 @@ def test_module_shape_checks():
     assert m.w_scales.dtype == torch.uint8 and tuple(m.w_scales.shape) == (384, 8)
     with pytest.raises(RuntimeError):
         m(torch.zeros(3, 256, dtype=torch.float16))
+    with pytest.raises(ValueError):
+        SVDQLinear(384, 256, fmt="nvfp4_g16")
+    n = SVDQLinear(512, 256, rank=16, fmt="nvfp4_g16")
+    assert tuple(n.w_scales.shape) == (256, 32)
+    sd = n.state_dict()
+    sd["act_gscale"] = torch.tensor(0.25)
+    sd["w_gscale"] = torch.tensor(3.0)
+    n.load_state_dict(sd)
+    assert n._gs == (0.25, 3.0) and n._alpha == 0.75
+    assert n.act_gscale.device.type == "cpu"
