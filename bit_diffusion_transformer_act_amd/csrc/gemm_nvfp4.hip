@@ -167,36 +167,61 @@ void gemm_nvfp4_kernel(const uint8_t* __restrict__ act_codes, const uint8_t* __r
       o.sb[cb] = *reinterpret_cast<const uint16_t*>(st + CODES + (256 + brow[cb]) * SROW + so);
     }
   };
-  // one half-step: K block j (8 codes per lane half) uses dword j of the
-  // fragment and scale byte j / 2
-  auto mma = [&](const Ops& o) {
-    uint32_t pa[RB][2], pb[CB][2];
+  // Dequantization runs one K block ahead of the MFMAs: while the 16 MFMAs of
+  // block j execute, the VALU turns block j + 1 (or the next half-step's block
+  // 0) into fp16 operands, 1 MFMA : 4 VALU in the issue order. K block j of a
+  // half-step uses dword j of each fragment and scale byte j / 2.
+  v8h A0[RB], B0[CB], A1[RB], B1[CB];
+  uint32_t pa[RB][2], pb[CB][2];
+  auto pairs = [&](const Ops& o) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) nv_scale_pairs(o.sa[rb], pa[rb][0], pa[rb][1]);
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) nv_scale_pairs(o.sb[cb], pb[cb][0], pb[cb][1]);
+  };
+  auto deq = [&](v8h (&A)[RB], v8h (&B)[CB], const Ops& o, int j) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      v8h av[RB], bv[CB];
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const uint32_t w = j == 0 ? o.a[rb].x : j == 1 ? o.a[rb].y : j == 2 ? o.a[rb].z : o.a[rb].w;
-        av[rb] = nv_dequant8(w, pa[rb][j >> 1]);
-      }
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        const uint32_t w = j == 0 ? o.b[cb].x : j == 1 ? o.b[cb].y : j == 2 ? o.b[cb].z : o.b[cb].w;
-        bv[cb] = nv_dequant8(w, pb[cb][j >> 1]);
-      }
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
-          acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[rb], bv[cb], acc[rb][cb], 0, 0, 0);
-      // keep the four K blocks in order: hoisting later blocks' dequantization
-      // ahead would hold their operands in registers for no gain
-      __builtin_amdgcn_sched_barrier(0);
+    for (int rb = 0; rb < RB; ++rb) {
+      const uint32_t w = j == 0 ? o.a[rb].x : j == 1 ? o.a[rb].y : j == 2 ? o.a[rb].z : o.a[rb].w;
+      A[rb] = nv_dequant8(w, pa[rb][j >> 1]);
     }
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const uint32_t w = j == 0 ? o.b[cb].x : j == 1 ? o.b[cb].y : j == 2 ? o.b[cb].z : o.b[cb].w;
+      B[cb] = nv_dequant8(w, pb[cb][j >> 1]);
+    }
+  };
+  auto mm = [&](const v8h (&A)[RB], const v8h (&B)[CB]) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+        acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[rb], B[cb], acc[rb][cb], 0, 0, 0);
+  };
+  auto interleave = [&]() {
+#pragma unroll
+    for (int i = 0; i < RB * CB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // four VALU
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // one half-step: on entry A0 / B0 hold K block 0 of cur and pa / pb its scale
+  // pairs; on exit they hold block 0 of nxt (whose LDS reads were issued earlier)
+  auto half = [&](const Ops& cur, const Ops& nxt) {
+    deq(A1, B1, cur, 1);
+    mm(A0, B0);
+    interleave();
+    deq(A0, B0, cur, 2);
+    mm(A1, B1);
+    interleave();
+    deq(A1, B1, cur, 3);
+    mm(A0, B0);
+    interleave();
+    pairs(nxt);
+    deq(A0, B0, nxt, 0);
+    mm(A1, B1);
+    interleave();
   };
 
   Ops P0, P1;
@@ -210,22 +235,24 @@ void gemm_nvfp4_kernel(const uint8_t* __restrict__ act_codes, const uint8_t* __r
   }
   __syncthreads();
   load_ops(P0, 0, 0);
+  pairs(P0);
+  deq(A0, B0, P0, 0);
   for (int pp = 0; pp < np; ++pp) {
     load_ops(P1, pp, 1);
-    mma(P0);
+    half(P0, P1);
     load_ops(P0, pp, 2);
-    mma(P1);
+    half(P1, P0);
     load_ops(P1, pp, 3);
-    mma(P0);
+    half(P0, P1);
     if (pp + 1 < np) {
-      // pair pp + 1 has landed (the only DMA in flight); after the barrier no
-      // wave reads pair pp's slot, which pair pp + 2 reuses
+      // pair pp + 1 has landed (the only DMA in flight), and every read of pair
+      // pp is done; after the barrier pair pp's slot is free for pair pp + 2
       waitvm_lgkm0<0>();
       __syncthreads();
       load_ops(P0, pp + 1, 0);
       if (pp + 2 < np) dma_pair(pp + 2);
     }
-    mma(P1);
+    half(P1, P0);   // on the last pair, the look-ahead block is never used
   }
 
   // ---- per-tensor scales, then the low-rank up-projection into the same
