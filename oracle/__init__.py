@@ -30,6 +30,8 @@ from .svdq import (  # noqa: F401
     lowrank_factors,
     prep_svdq_layer,
     smooth_act,
+    bf16_round,
+    as_f32_16bit,
     quantize_int4_g64,
     quantize_fp4_b32,
     quantize_nvfp4_g16,

@@ -109,7 +109,7 @@ def lowrank_factors(W_hat_kn: np.ndarray, rank: int):
 
 
 def prep_svdq_layer(W: np.ndarray, smooth_inv: np.ndarray, rank: int, fmt: str,
-                    act_gscale=None) -> dict:
+                    act_gscale=None, dtype: str = "float16") -> dict:
     """Offline preparation of one SVDQ W4A4 layer.
 
     W fp16 [N][K]; smooth_inv fp32 [K]. Steps (each a reading of the pages'
@@ -117,8 +117,9 @@ def prep_svdq_layer(W: np.ndarray, smooth_inv: np.ndarray, rank: int, fmt: str,
       1. lambda'_k = 1 / float64(smooth_inv_k) exactly, W_hat = diag(lambda') W_kn,
          so X_hat W_hat = X W holds in real arithmetic.
       2. L1, L2 = rank-r SVD split of W_hat.
-      3. lora_down = fp16((diag(smooth_inv) L1)^T) [r][K] -- the low-rank branch
-         consumes the caller's X directly; lora_up = fp16(L2^T) [N][r].
+      3. lora_down = h16((diag(smooth_inv) L1)^T) [r][K] -- the low-rank branch
+         consumes the caller's X directly; lora_up = h16(L2^T) [N][r], with h16
+         the compute dtype: fp16, or bf16 (stored as float32 holding bf16 values).
       4. Residual with the rounded factors: R = W_hat - diag(lambda') lora_down^T lora_up^T,
          so the 16-bit rounding of the factors is absorbed by the 4-bit part.
       5. Quantize R^T (N x K) along K with the same rule the activations use;
@@ -128,6 +129,10 @@ def prep_svdq_layer(W: np.ndarray, smooth_inv: np.ndarray, rank: int, fmt: str,
     """
     if fmt not in FORMATS:
         raise ValueError(fmt)
+    if dtype not in ("float16", "bfloat16"):
+        raise ValueError(dtype)
+    h16 = (lambda a: a.astype(np.float16)) if dtype == "float16" else \
+          (lambda a: bf16_round(a.astype(np.float32)))
     W = np.asarray(W)
     N, K = W.shape
     si64 = np.asarray(smooth_inv, dtype=np.float32).astype(np.float64)
@@ -135,12 +140,12 @@ def prep_svdq_layer(W: np.ndarray, smooth_inv: np.ndarray, rank: int, fmt: str,
     W_hat = W.astype(np.float64).T * lam[:, None]                 # K x N
     if rank > 0:
         L1, L2, _ = lowrank_factors(W_hat, rank)
-        lora_down = (L1 * si64[:, None]).T.astype(np.float16)      # r x K
-        lora_up = np.ascontiguousarray(L2.T).astype(np.float16)    # N x r
+        lora_down = h16((L1 * si64[:, None]).T)                    # r x K
+        lora_up = h16(np.ascontiguousarray(L2.T))                  # N x r
         low = (lam[:, None] * lora_down.T.astype(np.float64)) @ lora_up.T.astype(np.float64)
     else:
-        lora_down = np.zeros((0, K), np.float16)
-        lora_up = np.zeros((N, 0), np.float16)
+        lora_down = h16(np.zeros((0, K)))
+        lora_up = h16(np.zeros((N, 0)))
         low = 0.0
     R = W_hat - low                                                # K x N
     Rt = np.ascontiguousarray(R.T).astype(np.float32)
@@ -170,10 +175,35 @@ def prep_svdq_layer(W: np.ndarray, smooth_inv: np.ndarray, rank: int, fmt: str,
 # Run-time reference: what the GPU must reproduce.
 # --------------------------------------------------------------------------
 
+def bf16_round(x) -> np.ndarray:
+    """Round to bfloat16 (8 significant bits, fp32's exponent range) to
+    nearest, ties to the even mantissa; returns the values as float32.
+    Worked from the fp32 bit pattern: adding 0x7FFF plus the lowest kept bit
+    and dropping the low 16 bits is round-half-even on the discarded half
+    (a carry moves into the exponent, up to infinity). NaN stays NaN."""
+    f = np.asarray(x, dtype=np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    out = r.astype(np.uint32).view(np.float32)
+    return np.where(np.isnan(f), f, out).astype(np.float32)
+
+
+def as_f32_16bit(X16) -> np.ndarray:
+    """A 16-bit input (fp16 array, or float32 array holding bf16 values) as float32."""
+    X = np.asarray(X16)
+    if X.dtype == np.float16:
+        return X.astype(np.float32)
+    X = X.astype(np.float32)
+    if (X.view(np.uint32) & 0xFFFF).any():
+        raise ValueError("a float32 16-bit input must hold bfloat16 values")
+    return X
+
+
 def smooth_act(X16: np.ndarray, smooth_inv: np.ndarray) -> np.ndarray:
     """x_hat = fl32(fp32(x) * smooth_inv[k]): one IEEE fp32 multiply, never
-    fused with anything (runtime half of outlier migration)."""
-    return np.asarray(X16, dtype=np.float16).astype(np.float32) * np.asarray(smooth_inv, dtype=np.float32)[None, :]
+    fused with anything (runtime half of outlier migration). X16: fp16, or
+    float32 holding bf16 values (the bfloat16 compute dtype)."""
+    return as_f32_16bit(X16) * np.asarray(smooth_inv, dtype=np.float32)[None, :]
 
 
 def quantize_int4_g64(v: np.ndarray):
