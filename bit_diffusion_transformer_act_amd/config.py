@@ -14,11 +14,9 @@ that block against what the MI355X library implements:
                                                     16, fp32 scale per tensor
   svdq_w4a4 precision "mxfp4" with group_size 32 -> FP4 E2M1, E8M0 scale per 32
   awq_w4a16 precision "int4" with group_size 64  -> the AWQ GEMV
-  compute_dtype "float16"
-
-The pages' own example sets compute_dtype "bfloat16"; the kernels take fp16
-activations and write fp16 outputs, so that setting is rejected with an
-explicit message rather than silently mapped.
+  compute_dtype "float16" or "bfloat16"           -> the 16-bit type of the
+                                                    activations, the low-rank
+                                                    branch, biases and outputs
 Target entries are module names; "..." entries (an elision in the pages'
 example) are ignored, and shell-style wildcards are accepted.
 """
@@ -79,9 +77,10 @@ def parse_quantization_config(cfg) -> QuantConfig:
         raise ValueError(f"quant_method must be 'nunchaku_lite', got {q.get('quant_method')!r}")
     cdt = q.get("compute_dtype", "float16")
     if cdt in ("bfloat16", "bf16"):
-        raise UnsupportedQuantConfig("compute_dtype bfloat16: the kernels take fp16 activations and "
-                                     "write fp16 outputs; use compute_dtype 'float16'")
-    if cdt not in ("float16", "fp16", "half"):
+        cdt = "bfloat16"
+    elif cdt in ("float16", "fp16", "half"):
+        cdt = "float16"
+    else:
         raise ValueError(f"unknown compute_dtype {cdt!r}")
 
     svdq = None
@@ -108,4 +107,4 @@ def parse_quantization_config(cfg) -> QuantConfig:
         awq = AwqSpec(64, _targets(b, "awq_w4a16"))
     if svdq is None and awq is None:
         raise ValueError("quantization_config has neither svdq_w4a4 nor awq_w4a16")
-    return QuantConfig("float16", svdq, awq)
+    return QuantConfig(cdt, svdq, awq)

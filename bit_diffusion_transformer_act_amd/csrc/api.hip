@@ -62,12 +62,13 @@ bool rank_ok(int r) { return r >= 0 && r <= 128 && (r % 16) == 0; }
 bool k_ok(int K) { return K >= 128 && K <= 65536 && (K % 128) == 0; }
 bool k_nv_ok(int K) { return K >= 256 && K <= 65536 && (K % 256) == 0; }
 bool positive_finite(float v) { return std::isfinite(v) && v > 0.0f; }
+bool dtype_ok(int d) { return d == SVDQ_F16 || d == SVDQ_BF16; }
 
 }  // namespace
 
 extern "C" {
 
-int svdq_version(void) { return 10000 * 0 + 100 * 1 + 0; }
+int svdq_version(void) { return 10000 * 0 + 100 * 2 + 0; }
 
 const char* svdq_status_str(int status) {
   switch (status) {
@@ -83,10 +84,11 @@ const char* svdq_status_str(int status) {
 
 int svdq_device_check(int hip_device) { return check_device(hip_device); }
 
-int svdq_quantize_act(int fmt, int M, int K, int r, const void* X, const float* smooth_inv,
+int svdq_quantize_act(int fmt, int dtype, int M, int K, int r, const void* X, const float* smooth_inv,
                       const void* lora_down, uint8_t* act_codes, void* act_scales, void* lora_act,
                       void* stream) {
   if (fmt != SVDQ_INT4_G64 && fmt != SVDQ_FP4_E2M1_B32) return SVDQ_ERR_INVALID_ARG;
+  if (!dtype_ok(dtype)) return SVDQ_ERR_INVALID_ARG;
   if (M < 0 || !k_ok(K) || !rank_ok(r)) return SVDQ_ERR_SHAPE;
   if (M == 0) return SVDQ_OK;
   if (!X || !smooth_inv || !act_codes || !act_scales) return SVDQ_ERR_INVALID_ARG;
@@ -97,15 +99,16 @@ int svdq_quantize_act(int fmt, int M, int K, int r, const void* X, const float* 
   const int dc = check_current_device();
   if (dc != SVDQ_OK) return dc;
   (void)hipGetLastError();
-  return finish(svdq::launch_quantize_act(fmt, M, K, r, X, smooth_inv, lora_down, act_codes,
+  return finish(svdq::launch_quantize_act(fmt, dtype, M, K, r, X, smooth_inv, lora_down, act_codes,
                                           act_scales, lora_act, (hipStream_t)stream));
 }
 
-int svdq_gemm_w4a4(int fmt, int M, int N, int K, int r, const uint8_t* act_codes,
+int svdq_gemm_w4a4(int fmt, int dtype, int M, int N, int K, int r, const uint8_t* act_codes,
                    const void* act_scales, const void* lora_act, const uint8_t* w_codes,
                    const void* w_scales, const void* lora_up, const void* bias, int epi, void* Y,
                    void* stream) {
   if (fmt != SVDQ_INT4_G64 && fmt != SVDQ_FP4_E2M1_B32) return SVDQ_ERR_INVALID_ARG;
+  if (!dtype_ok(dtype)) return SVDQ_ERR_INVALID_ARG;
   if (epi != SVDQ_EPI_NONE && epi != SVDQ_EPI_GELU_TANH) return SVDQ_ERR_INVALID_ARG;
   if (M < 0 || M > (1 << 23) || N < 128 || N > 65536 || (N % 128) != 0 || !k_ok(K) || !rank_ok(r))
     return SVDQ_ERR_SHAPE;
@@ -119,15 +122,16 @@ int svdq_gemm_w4a4(int fmt, int M, int N, int K, int r, const uint8_t* act_codes
   const int dc = check_current_device();
   if (dc != SVDQ_OK) return dc;
   (void)hipGetLastError();
-  return finish(svdq::launch_gemm_w4a4(fmt, M, N, K, r, act_codes, act_scales, lora_act, w_codes,
+  return finish(svdq::launch_gemm_w4a4(fmt, dtype, M, N, K, r, act_codes, act_scales, lora_act, w_codes,
                                        w_scales, lora_up, bias, epi, Y, (hipStream_t)stream));
 }
 
-int svdq_gemm_w4a4_qkv(int fmt, int M, int N, int K, int r, const uint8_t* act_codes,
+int svdq_gemm_w4a4_qkv(int fmt, int dtype, int M, int N, int K, int r, const uint8_t* act_codes,
                        const void* act_scales, const void* lora_act, const uint8_t* w_codes,
                        const void* w_scales, const void* lora_up, const void* bias,
                        const void* qk_norm_w, const float* rope, float eps, void* Y, void* stream) {
   if (fmt != SVDQ_INT4_G64) return SVDQ_ERR_INVALID_ARG;
+  if (!dtype_ok(dtype)) return SVDQ_ERR_INVALID_ARG;
   if (!(eps >= 0.0f) || eps > 1.0f) return SVDQ_ERR_INVALID_ARG;   // also rejects NaN
   if (M < 0 || M > (1 << 23) || N < 384 || N > 65536 || (N % 384) != 0 || !k_ok(K) || !rank_ok(r))
     return SVDQ_ERR_SHAPE;
@@ -144,13 +148,14 @@ int svdq_gemm_w4a4_qkv(int fmt, int M, int N, int K, int r, const uint8_t* act_c
   if (dc != SVDQ_OK) return dc;
   (void)hipGetLastError();
   const svdq::QkvEpilogue qe{qk_norm_w, rope, eps, N / 384};
-  return finish(svdq::launch_gemm_w4a4(fmt, M, N, K, r, act_codes, act_scales, lora_act, w_codes,
+  return finish(svdq::launch_gemm_w4a4(fmt, dtype, M, N, K, r, act_codes, act_scales, lora_act, w_codes,
                                        w_scales, lora_up, bias, 2, Y, (hipStream_t)stream, &qe));
 }
 
-int svdq_quantize_act_nvfp4(int M, int K, int r, const void* X, const float* smooth_inv,
+int svdq_quantize_act_nvfp4(int dtype, int M, int K, int r, const void* X, const float* smooth_inv,
                             const void* lora_down, float act_gscale, uint8_t* act_codes,
                             uint8_t* act_scales, void* lora_act, void* stream) {
+  if (!dtype_ok(dtype)) return SVDQ_ERR_INVALID_ARG;
   if (M < 0 || !k_nv_ok(K) || !rank_ok(r)) return SVDQ_ERR_SHAPE;
   if (!positive_finite(act_gscale) || !positive_finite(6.0f * act_gscale)) return SVDQ_ERR_INVALID_ARG;
   if (M == 0) return SVDQ_OK;
@@ -162,14 +167,15 @@ int svdq_quantize_act_nvfp4(int M, int K, int r, const void* X, const float* smo
   const int dc = check_current_device();
   if (dc != SVDQ_OK) return dc;
   (void)hipGetLastError();
-  return finish(svdq::launch_quantize_act(SVDQ_NVFP4_G16, M, K, r, X, smooth_inv, lora_down, act_codes,
+  return finish(svdq::launch_quantize_act(SVDQ_NVFP4_G16, dtype, M, K, r, X, smooth_inv, lora_down, act_codes,
                                           act_scales, lora_act, (hipStream_t)stream, act_gscale));
 }
 
-int svdq_gemm_nvfp4(int M, int N, int K, int r, const uint8_t* act_codes, const uint8_t* act_scales,
-                    const void* lora_act, const uint8_t* w_codes, const uint8_t* w_scales,
-                    const void* lora_up, const void* bias, float alpha, int epilogue, void* Y,
-                    void* stream) {
+int svdq_gemm_nvfp4(int dtype, int M, int N, int K, int r, const uint8_t* act_codes,
+                    const uint8_t* act_scales, const void* lora_act, const uint8_t* w_codes,
+                    const uint8_t* w_scales, const void* lora_up, const void* bias, float alpha,
+                    int epilogue, void* Y, void* stream) {
+  if (!dtype_ok(dtype)) return SVDQ_ERR_INVALID_ARG;
   if (epilogue != SVDQ_EPI_NONE && epilogue != SVDQ_EPI_GELU_TANH) return SVDQ_ERR_INVALID_ARG;
   if (!std::isfinite(alpha)) return SVDQ_ERR_INVALID_ARG;
   if (M < 0 || N < 128 || N > 65536 || (N % 128) != 0 || !k_nv_ok(K) || !rank_ok(r)) return SVDQ_ERR_SHAPE;
@@ -183,12 +189,13 @@ int svdq_gemm_nvfp4(int M, int N, int K, int r, const uint8_t* act_codes, const 
   const int dc = check_current_device();
   if (dc != SVDQ_OK) return dc;
   (void)hipGetLastError();
-  return finish(svdq::launch_gemm_nvfp4(M, N, K, r, act_codes, act_scales, lora_act, w_codes, w_scales,
+  return finish(svdq::launch_gemm_nvfp4(dtype, M, N, K, r, act_codes, act_scales, lora_act, w_codes, w_scales,
                                         lora_up, bias, alpha, epilogue, Y, (hipStream_t)stream));
 }
 
-int awq_gemv_w4a16(int M, int N, int K, int group, const void* x, const uint8_t* w_codes,
+int awq_gemv_w4a16(int dtype, int M, int N, int K, int group, const void* x, const uint8_t* w_codes,
                    const void* scales, const void* zeros, const void* bias, void* y, void* stream) {
+  if (!dtype_ok(dtype)) return SVDQ_ERR_INVALID_ARG;
   if (group != 64) return SVDQ_ERR_SHAPE;
   if (M < 0 || M > 8 || N < 1 || N > (1 << 20) || K < 64 || (K % 64) != 0 || M * K > 32768)
     return SVDQ_ERR_SHAPE;
@@ -200,7 +207,7 @@ int awq_gemv_w4a16(int M, int N, int K, int group, const void* x, const uint8_t*
   const int dc = check_current_device();
   if (dc != SVDQ_OK) return dc;
   (void)hipGetLastError();
-  return finish(svdq::launch_awq_gemv(M, N, K, x, w_codes, scales, zeros, bias, y,
+  return finish(svdq::launch_awq_gemv(dtype, M, N, K, x, w_codes, scales, zeros, bias, y,
                                       (hipStream_t)stream));
 }
 

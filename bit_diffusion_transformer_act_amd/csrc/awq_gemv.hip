@@ -5,13 +5,14 @@
 //
 //   y[m,n] = sum_k x[m,k] (q[n,k] - z[n,g]) s[n,g],  g = k / 64
 //
-// HBM-bound: every weight byte is read once. Dequantization uses the fp16
-// bit trick: (word >> 4j) & 0x000F000F | 0x64006400 is the packed fp16 pair
-// (1024 + q_j, 1024 + q_{j+4}), exact, and v_dot2_f32_f16 accumulates
-// x (1024 + q) in fp32 against x stored as pairs (x_j, x_{j+4}). Per 32-code
-// chunk, sum x (q - z) = sum x (1024 + q) - (1024 + z) sum x, with the second
+// HBM-bound: every weight byte is read once. Dequantization uses a bit trick
+// in the activations' 16-bit type: (word >> 4j) & 0x000F000F | 0x64006400 is
+// the packed fp16 pair (1024 + q_j, 1024 + q_{j+4}) and | 0x43004300 the bf16
+// pair (128 + q_j, 128 + q_{j+4}), both exact, and v_dot2_f32_f16 / _bf16
+// accumulates x (B + q) in fp32 against x stored as pairs (x_j, x_{j+4}). Per
+// 32-code chunk, sum x (q - z) = sum x (B + q) - (B + z) sum x, with the second
 // term one fma from the precomputed chunk sum of x, so any fp16 zero point
-// works.
+// works. Scales and zero points are fp16 in both cases (the stored format).
 //
 // Work split: one 8-wave workgroup per CU; wave w of the grid owns the
 // contiguous rows [w N / W, (w + 1) N / W) (W waves in all), so every CU streams
@@ -44,11 +45,24 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-template <int MR>
+// dot2 of packed 16-bit pairs in the activations' type, fp32 accumulation
+template <int IO>
+__device__ __forceinline__ float dot2_io(uint32_t a, uint32_t b, float c) {
+  if constexpr (IO == 1)
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, a), __builtin_bit_cast(v2bf, b), c, false);
+  else
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(v2h, a), __builtin_bit_cast(v2h, b), c, false);
+}
+
+template <int IO, int MR>
 __global__ __launch_bounds__(64 * kGemvWaves)
-void awq_gemv_kernel(const __half* __restrict__ x, const uint8_t* __restrict__ codes,
+void awq_gemv_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
                      const __half* __restrict__ scales, const __half* __restrict__ zeros,
-                     const __half* __restrict__ bias, __half* __restrict__ y, int N, int K) {
+                     const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int N, int K) {
+  // 1.0 as a pair, and the exact offset B of the dequantization trick with its bit pattern
+  constexpr uint32_t kOne = IO == 1 ? 0x3F803F80u : 0x3C003C00u;
+  constexpr uint32_t kMagic = IO == 1 ? 0x43004300u : 0x64006400u;
+  constexpr float kB = IO == 1 ? 128.0f : 1024.0f;
   // LDS: x pairs as [m][4 segments of a chunk][chunk][4 pairs] (for a fixed
   // segment, consecutive chunks are 16 bytes apart: conflict-free reads), then
   // the chunk sums of x [m][chunk]
@@ -70,7 +84,6 @@ void awq_gemv_kernel(const __half* __restrict__ x, const uint8_t* __restrict__ c
     o[3] = (v.y >> 16) | (v.w & 0xFFFF0000u);      // (x_3, x_7)
   }
   __syncthreads();
-  const v2h one = {(_Float16)1.0f, (_Float16)1.0f};
   for (int mc = tid; mc < MR * nch; mc += 64 * kGemvWaves) {
     const int m = mc / nch, c = mc - m * nch;
     float sum = 0.f;
@@ -78,8 +91,7 @@ void awq_gemv_kernel(const __half* __restrict__ x, const uint8_t* __restrict__ c
     for (int e = 0; e < 4; ++e)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        sum = __builtin_amdgcn_fdot2(__builtin_bit_cast(v2h, xs[(((size_t)m * 4 + e) * nch + c) * 4 + j]), one,
-                                     sum, false);
+        sum = dot2_io<IO>(xs[(((size_t)m * 4 + e) * nch + c) * 4 + j], kOne, sum);
     xc[mc] = sum;
   }
   __syncthreads();
@@ -124,7 +136,7 @@ void awq_gemv_kernel(const __half* __restrict__ x, const uint8_t* __restrict__ c
     if (c < nch) {
       const uint32_t w[4] = {d.w.x, d.w.y, d.w.z, d.w.w};
       const float s = __half2float(d.s);
-      const float zb = 1024.0f + __half2float(d.z);
+      const float zb = kB + __half2float(d.z);
 #pragma unroll
       for (int m = 0; m < MR; ++m) {
         float part = 0.f;
@@ -134,8 +146,8 @@ void awq_gemv_kernel(const __half* __restrict__ x, const uint8_t* __restrict__ c
           const uint32_t xv[4] = {xp.x, xp.y, xp.z, xp.w};
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const uint32_t hb = ((w[e] >> (4 * j)) & 0x000F000Fu) | 0x64006400u;
-            part = __builtin_amdgcn_fdot2(__builtin_bit_cast(v2h, hb), __builtin_bit_cast(v2h, xv[j]), part, false);
+            const uint32_t hb = ((w[e] >> (4 * j)) & 0x000F000Fu) | kMagic;
+            part = dot2_io<IO>(hb, xv[j], part);
           }
         }
         acc[m] = fmaf(s, fmaf(-zb, xc[m * nch + c], part), acc[m]);
@@ -165,13 +177,13 @@ void awq_gemv_kernel(const __half* __restrict__ x, const uint8_t* __restrict__ c
     }
   }
   if (lane < r1 - r0) {
-    const float b = bias ? __half2float(bias[r0 + lane]) : 0.f;
+    const float b = bias ? Io<IO>::to_f(bias[r0 + lane]) : 0.f;
 #pragma unroll
-    for (int m = 0; m < MR; ++m) y[(size_t)m * N + r0 + lane] = __float2half_rn(out[m] + b);
+    for (int m = 0; m < MR; ++m) y[(size_t)m * N + r0 + lane] = Io<IO>::from_f(out[m] + b);
   }
 }
 
-template <int MR>
+template <int IO, int MR>
 static hipError_t launch_mr(int N, int K, const void* x, const uint8_t* q, const void* s,
                             const void* z, const void* b, void* y, hipStream_t st) {
   // about one workgroup per CU for large N, at least ~4 rows per wave for small
@@ -182,29 +194,36 @@ static hipError_t launch_mr(int N, int K, const void* x, const uint8_t* q, const
   if (lds > 65536) {   // M K = 32768 needs 68 KB
     static std::atomic<int> raised{0};
     if (!raised.load(std::memory_order_acquire)) {
-      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&awq_gemv_kernel<MR>),
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&awq_gemv_kernel<IO, MR>),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, 72 * 1024);
       if (e != hipSuccess) return e;
       raised.store(1, std::memory_order_release);
     }
   }
-  hipLaunchKernelGGL((awq_gemv_kernel<MR>), dim3(grid), dim3(64 * kGemvWaves), lds, st, (const __half*)x, q,
-                     (const __half*)s, (const __half*)z, (const __half*)b, (__half*)y, N, K);
+  hipLaunchKernelGGL((awq_gemv_kernel<IO, MR>), dim3(grid), dim3(64 * kGemvWaves), lds, st, (const uint16_t*)x, q,
+                     (const __half*)s, (const __half*)z, (const uint16_t*)b, (uint16_t*)y, N, K);
   return hipGetLastError();
 }
 
-hipError_t launch_awq_gemv(int M, int N, int K, const void* x, const uint8_t* q, const void* s,
-                           const void* z, const void* b, void* y, hipStream_t st) {
+template <int IO>
+static hipError_t launch_gemv_io(int M, int N, int K, const void* x, const uint8_t* q, const void* s,
+                                 const void* z, const void* b, void* y, hipStream_t st) {
   switch (M) {
-    case 1: return launch_mr<1>(N, K, x, q, s, z, b, y, st);
-    case 2: return launch_mr<2>(N, K, x, q, s, z, b, y, st);
-    case 3: return launch_mr<3>(N, K, x, q, s, z, b, y, st);
-    case 4: return launch_mr<4>(N, K, x, q, s, z, b, y, st);
-    case 5: return launch_mr<5>(N, K, x, q, s, z, b, y, st);
-    case 6: return launch_mr<6>(N, K, x, q, s, z, b, y, st);
-    case 7: return launch_mr<7>(N, K, x, q, s, z, b, y, st);
-    default: return launch_mr<8>(N, K, x, q, s, z, b, y, st);
+    case 1: return launch_mr<IO, 1>(N, K, x, q, s, z, b, y, st);
+    case 2: return launch_mr<IO, 2>(N, K, x, q, s, z, b, y, st);
+    case 3: return launch_mr<IO, 3>(N, K, x, q, s, z, b, y, st);
+    case 4: return launch_mr<IO, 4>(N, K, x, q, s, z, b, y, st);
+    case 5: return launch_mr<IO, 5>(N, K, x, q, s, z, b, y, st);
+    case 6: return launch_mr<IO, 6>(N, K, x, q, s, z, b, y, st);
+    case 7: return launch_mr<IO, 7>(N, K, x, q, s, z, b, y, st);
+    default: return launch_mr<IO, 8>(N, K, x, q, s, z, b, y, st);
   }
+}
+
+hipError_t launch_awq_gemv(int io, int M, int N, int K, const void* x, const uint8_t* q, const void* s,
+                           const void* z, const void* b, void* y, hipStream_t st) {
+  if (io == 1) return launch_gemv_io<1>(M, N, K, x, q, s, z, b, y, st);
+  return launch_gemv_io<0>(M, N, K, x, q, s, z, b, y, st);
 }
 
 }  // namespace svdq

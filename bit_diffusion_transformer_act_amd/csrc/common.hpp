@@ -15,6 +15,45 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+// The 16-bit type of activations, the low-rank branch, biases, norm weights and
+// outputs (the layer's compute dtype): IO 0 = fp16, IO 1 = bf16. Conversions to
+// 16 bits round to nearest, ties to even; the low-rank products run on the
+// matching MFMA with fp32 accumulation. Operands are passed as raw bits.
+template <int IO> struct Io;
+template <> struct Io<0> {
+  static __device__ __forceinline__ float to_f(uint16_t b) { return __half2float(__ushort_as_half(b)); }
+  static __device__ __forceinline__ uint16_t from_f(float v) { return __half_as_ushort(__float2half_rn(v)); }
+  static __device__ __forceinline__ v4f mma16x16x16(uint2 a, uint2 b, v4f c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(v4h, a), __builtin_bit_cast(v4h, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ v4f mma16x16x32(uint4 a, uint4 b, v4f c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, a), __builtin_bit_cast(v8h, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ v16f mma32x32x16(uint4 a, uint4 b, v16f c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, a), __builtin_bit_cast(v8h, b), c, 0, 0, 0);
+  }
+};
+template <> struct Io<1> {
+  static __device__ __forceinline__ float to_f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+  static __device__ __forceinline__ uint16_t from_f(float v) {
+    const uint32_t u = __float_as_uint(v);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);   // NaN stays NaN
+    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+  }
+  static __device__ __forceinline__ v4f mma16x16x16(uint2 a, uint2 b, v4f c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4s, a), __builtin_bit_cast(v4s, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ v4f mma16x16x32(uint4 a, uint4 b, v4f c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ v16f mma32x32x16(uint4 a, uint4 b, v16f c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
+  }
+};
 
 constexpr int kWave = 64;
 

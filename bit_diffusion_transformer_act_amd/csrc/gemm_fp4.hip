@@ -46,12 +46,12 @@ static_assert(PAIR / 4096 == 16 && SGRP / 4096 == 2, "DMA plan: 16 + 2 instructi
 // logical chunk) land in 16 distinct 16-byte bank slots.
 __device__ __forceinline__ int swz8(int row) { return (row >> 1) & 7; }
 
-template <int EPI>
+template <int IO, int EPI>
 __global__ __launch_bounds__(256, 1)
 void gemm_fp4_big_kernel(const uint8_t* __restrict__ act_codes, const uint8_t* __restrict__ act_scales,
-                         const __half* __restrict__ lora_act, const uint8_t* __restrict__ w_codes,
-                         const uint8_t* __restrict__ w_scales, const __half* __restrict__ lora_up,
-                         const __half* __restrict__ bias, __half* __restrict__ Y,
+                         const uint16_t* __restrict__ lora_act, const uint8_t* __restrict__ w_codes,
+                         const uint8_t* __restrict__ w_scales, const uint16_t* __restrict__ lora_up,
+                         const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y,
                          int M, int N, int K, int r) {
   using namespace fp4big;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -256,9 +256,7 @@ void gemm_fp4_big_kernel(const uint8_t* __restrict__ act_codes, const uint8_t* _
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
-          acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, ua[rb][h]),
-                                                               __builtin_bit_cast(v8h, ub[cb][h]),
-                                                               acc[rb][cb], 0, 0, 0);
+          acc[rb][cb] = Io<IO>::mma32x32x16(ua[rb][h], ub[cb][h], acc[rb][cb]);
   };
   uint4 ua[RB][LR], ub[CB][LR];
   if (r > 0) lora_load(ua, ub, 0);
@@ -277,18 +275,18 @@ void gemm_fp4_big_kernel(const uint8_t* __restrict__ act_codes, const uint8_t* _
   static_assert(BM * TP * 2 <= LDS, "staging tile must fit in the ring");
   waitvm<0>();   // no DMA outstanding
   __syncthreads();
-  __half* tile = reinterpret_cast<__half*>(smem);
+  uint16_t* tile = reinterpret_cast<uint16_t*>(smem);
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
     const int nl = brow[cb];
-    const float bn = bias ? __half2float(bias[n0 + nl]) : 0.f;
+    const float bn = bias ? Io<IO>::to_f(bias[n0 + nl]) : 0.f;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         float yv = acc[rb][cb][v] + bn;
         if (EPI == 1) yv = gelu_tanh_f32(yv);
-        tile[(wm * 128 + rb * 32 + (v >> 2) * 8 + lh * 4 + (v & 3)) * TP + nl] = __float2half_rn(yv);
+        tile[(wm * 128 + rb * 32 + (v >> 2) * 8 + lh * 4 + (v & 3)) * TP + nl] = Io<IO>::from_f(yv);
       }
   }
   __syncthreads();
@@ -302,23 +300,25 @@ void gemm_fp4_big_kernel(const uint8_t* __restrict__ act_codes, const uint8_t* _
 
 // Large-tile FP4 launch; returns hipErrorNotSupported (without launching) when
 // the shape does not suit it, so the caller can fall back to the 128 x 128 kernel.
-hipError_t launch_gemm_fp4_big(int M, int N, int K, int r, const uint8_t* ac, const void* as,
+hipError_t launch_gemm_fp4_big(int io, int M, int N, int K, int r, const uint8_t* ac, const void* as,
                                const void* la, const uint8_t* wc, const void* ws, const void* lu,
                                const void* bias, int epi, void* Y, hipStream_t st) {
   using namespace fp4big;
   if (N % BN != 0 || K % 512 != 0) return hipErrorNotSupported;   // whole scale groups
   const int ntiles = ((M + BM - 1) / BM) * (N / BN);
   if (ntiles < 256) return hipErrorNotSupported;   // too few tiles to fill 256 CUs
-  auto kern = epi ? gemm_fp4_big_kernel<1> : gemm_fp4_big_kernel<0>;
-  static std::atomic<int> raised[2] = {0, 0};
-  if (!raised[epi].load(std::memory_order_acquire)) {
+  const int v = 2 * (io == 1) + (epi != 0);
+  auto kern = v == 3 ? gemm_fp4_big_kernel<1, 1> : v == 2 ? gemm_fp4_big_kernel<1, 0>
+            : v == 1 ? gemm_fp4_big_kernel<0, 1> : gemm_fp4_big_kernel<0, 0>;
+  static std::atomic<int> raised[4] = {0, 0, 0, 0};
+  if (!raised[v].load(std::memory_order_acquire)) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
     if (e != hipSuccess) return e;
-    raised[epi].store(1, std::memory_order_release);
+    raised[v].store(1, std::memory_order_release);
   }
-  hipLaunchKernelGGL(kern, dim3(ntiles), dim3(256), LDS, st, ac, (const uint8_t*)as, (const __half*)la, wc,
-                     (const uint8_t*)ws, (const __half*)lu, (const __half*)bias, (__half*)Y, M, N, K, r);
+  hipLaunchKernelGGL(kern, dim3(ntiles), dim3(256), LDS, st, ac, (const uint8_t*)as, (const uint16_t*)la, wc,
+                     (const uint8_t*)ws, (const uint16_t*)lu, (const uint16_t*)bias, (uint16_t*)Y, M, N, K, r);
   return hipGetLastError();
 }
 

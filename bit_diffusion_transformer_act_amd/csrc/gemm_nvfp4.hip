@@ -67,12 +67,12 @@ __device__ __forceinline__ v8h nv_dequant8(uint32_t w, uint32_t spair) {
   return v8h{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
 }
 
-template <int EPI, int BN>
+template <int IO, int EPI, int BN>
 __global__ __launch_bounds__(256, 1)
 void gemm_nvfp4_kernel(const uint8_t* __restrict__ act_codes, const uint8_t* __restrict__ act_scales,
-                       const __half* __restrict__ lora_act, const uint8_t* __restrict__ w_codes,
-                       const uint8_t* __restrict__ w_scales, const __half* __restrict__ lora_up,
-                       const __half* __restrict__ bias, __half* __restrict__ Y, float alpha,
+                       const uint16_t* __restrict__ lora_act, const uint8_t* __restrict__ w_codes,
+                       const uint8_t* __restrict__ w_scales, const uint16_t* __restrict__ lora_up,
+                       const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, float alpha,
                        int M, int N, int K, int r) {
   using namespace nvfp4;
   constexpr int CB = BN / 64;                    // 32-column blocks per wave
@@ -275,9 +275,7 @@ void gemm_nvfp4_kernel(const uint8_t* __restrict__ act_codes, const uint8_t* __r
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb)
-        acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, ua[rb]),
-                                                             __builtin_bit_cast(v8h, ub[cb]),
-                                                             acc[rb][cb], 0, 0, 0);
+        acc[rb][cb] = Io<IO>::mma32x32x16(ua[rb], ub[cb], acc[rb][cb]);
   }
 
   // ---- epilogue: bias and activation, staged through LDS so that Y is written
@@ -286,18 +284,18 @@ void gemm_nvfp4_kernel(const uint8_t* __restrict__ act_codes, const uint8_t* __r
   static_assert(BM * TP * 2 <= LDS, "staging tile must fit in the ring");
   waitvm<0>();
   __syncthreads();
-  __half* tile = reinterpret_cast<__half*>(smem);
+  uint16_t* tile = reinterpret_cast<uint16_t*>(smem);
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
     const int nl = brow[cb];
-    const float bn = bias ? __half2float(bias[n0 + nl]) : 0.f;
+    const float bn = bias ? Io<IO>::to_f(bias[n0 + nl]) : 0.f;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         float yv = acc[rb][cb][v] + bn;
         if (EPI == 1) yv = gelu_tanh_f32(yv);
-        tile[(wm * 128 + rb * 32 + (v >> 2) * 8 + lh * 4 + (v & 3)) * TP + nl] = __float2half_rn(yv);
+        tile[(wm * 128 + rb * 32 + (v >> 2) * 8 + lh * 4 + (v & 3)) * TP + nl] = Io<IO>::from_f(yv);
       }
   }
   __syncthreads();
@@ -309,12 +307,12 @@ void gemm_nvfp4_kernel(const uint8_t* __restrict__ act_codes, const uint8_t* __r
   }
 }
 
-template <int EPI, int BN>
+template <int IO, int EPI, int BN>
 static hipError_t launch_nv(int M, int N, int K, int r, const uint8_t* ac, const uint8_t* as,
                             const void* la, const uint8_t* wc, const uint8_t* ws, const void* lu,
                             const void* bias, float alpha, void* Y, hipStream_t st) {
   using namespace nvfp4;
-  auto kern = gemm_nvfp4_kernel<EPI, BN>;
+  auto kern = gemm_nvfp4_kernel<IO, EPI, BN>;
   static std::atomic<int> raised{0};
   if (!raised.load(std::memory_order_acquire)) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -323,20 +321,28 @@ static hipError_t launch_nv(int M, int N, int K, int r, const uint8_t* ac, const
     raised.store(1, std::memory_order_release);
   }
   const int ntiles = ((M + BM - 1) / BM) * (N / BN);
-  hipLaunchKernelGGL(kern, dim3(ntiles), dim3(256), LDS, st, ac, as, (const __half*)la, wc, ws,
-                     (const __half*)lu, (const __half*)bias, (__half*)Y, alpha, M, N, K, r);
+  hipLaunchKernelGGL(kern, dim3(ntiles), dim3(256), LDS, st, ac, as, (const uint16_t*)la, wc, ws,
+                     (const uint16_t*)lu, (const uint16_t*)bias, (uint16_t*)Y, alpha, M, N, K, r);
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_nvfp4(int M, int N, int K, int r, const uint8_t* ac, const uint8_t* as,
+template <int IO>
+static hipError_t launch_nv_io(int M, int N, int K, int r, const uint8_t* ac, const uint8_t* as,
+                               const void* la, const uint8_t* wc, const uint8_t* ws, const void* lu,
+                               const void* bias, float alpha, int epi, void* Y, hipStream_t st) {
+  if (N % 256 == 0) {
+    return epi ? launch_nv<IO, 1, 256>(M, N, K, r, ac, as, la, wc, ws, lu, bias, alpha, Y, st)
+               : launch_nv<IO, 0, 256>(M, N, K, r, ac, as, la, wc, ws, lu, bias, alpha, Y, st);
+  }
+  return epi ? launch_nv<IO, 1, 128>(M, N, K, r, ac, as, la, wc, ws, lu, bias, alpha, Y, st)
+             : launch_nv<IO, 0, 128>(M, N, K, r, ac, as, la, wc, ws, lu, bias, alpha, Y, st);
+}
+
+hipError_t launch_gemm_nvfp4(int io, int M, int N, int K, int r, const uint8_t* ac, const uint8_t* as,
                              const void* la, const uint8_t* wc, const uint8_t* ws, const void* lu,
                              const void* bias, float alpha, int epi, void* Y, hipStream_t st) {
-  if (N % 256 == 0) {
-    return epi ? launch_nv<1, 256>(M, N, K, r, ac, as, la, wc, ws, lu, bias, alpha, Y, st)
-               : launch_nv<0, 256>(M, N, K, r, ac, as, la, wc, ws, lu, bias, alpha, Y, st);
-  }
-  return epi ? launch_nv<1, 128>(M, N, K, r, ac, as, la, wc, ws, lu, bias, alpha, Y, st)
-             : launch_nv<0, 128>(M, N, K, r, ac, as, la, wc, ws, lu, bias, alpha, Y, st);
+  if (io == 1) return launch_nv_io<1>(M, N, K, r, ac, as, la, wc, ws, lu, bias, alpha, epi, Y, st);
+  return launch_nv_io<0>(M, N, K, r, ac, as, la, wc, ws, lu, bias, alpha, epi, Y, st);
 }
 
 }  // namespace svdq

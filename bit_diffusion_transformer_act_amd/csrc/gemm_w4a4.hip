@@ -77,12 +77,12 @@ struct GemmShape {
 
 // 3 waves per SIMD (at most 168 VGPRs): the INT4 inner loop is VALU-bound and
 // needs the extra wave to cover LDS and MFMA latencies.
-template <int FMT, int EPI, int WM, int WN, int STAGES>
+template <int IO, int FMT, int EPI, int WM, int WN, int STAGES>
 __global__ __launch_bounds__(256, 3)
 void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restrict__ act_scales,
-                      const __half* __restrict__ lora_act, const uint8_t* __restrict__ w_codes,
-                      const void* __restrict__ w_scales, const __half* __restrict__ lora_up,
-                      const __half* __restrict__ bias, __half* __restrict__ Y,
+                      const uint16_t* __restrict__ lora_act, const uint8_t* __restrict__ w_codes,
+                      const void* __restrict__ w_scales, const uint16_t* __restrict__ lora_up,
+                      const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y,
                       int M, int N, int K, int r, QkvEpilogue qe) {
   using S = GemmShape<WM, WN, STAGES>;
   constexpr int BM = S::BM, BN = S::BN;
@@ -204,9 +204,7 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restr
       for (int rb = 0; rb < RB4; ++rb)
 #pragma unroll
         for (int cb = 0; cb < CB4; ++cb)
-          acc4[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(v4h, ua[rb]),
-                                                               __builtin_bit_cast(v4h, ub[cb]),
-                                                               acc4[rb][cb], 0, 0, 0);
+          acc4[rb][cb] = Io<IO>::mma16x16x16(ua[rb], ub[cb], acc4[rb][cb]);
     }
   } else {
     // v_mfma_f32_32x32x16_f16: lane l supplies row l%32, ranks j0 + 8 (l/32) .. +8.
@@ -236,9 +234,7 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restr
         for (int rb = 0; rb < RB32; ++rb)
 #pragma unroll
           for (int cb = 0; cb < CB32; ++cb)
-            acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, ua[rb][h]),
-                                                                 __builtin_bit_cast(v8h, ub[cb][h]),
-                                                                 acc[rb][cb], 0, 0, 0);
+            acc[rb][cb] = Io<IO>::mma32x32x16(ua[rb][h], ub[cb][h], acc[rb][cb]);
     }
   }
 
@@ -359,7 +355,7 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restr
   constexpr int TP = BN + 8;   // padded row (halves) of the staging tile
   static_assert(BM * TP * 2 <= S::LDS, "staging tile must fit in the ring");
   __syncthreads();
-  __half* tile = reinterpret_cast<__half*>(smem);
+  uint16_t* tile = reinterpret_cast<uint16_t*>(smem);
   if constexpr (FMT == 0) {
     const int l16 = lane & 15, lq = lane >> 4;
     // the fused QKV epilogue applies to the Q and K thirds (a tile is one head:
@@ -373,7 +369,7 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restr
 #pragma unroll
     for (int cb = 0; cb < CB4; ++cb) {
       const int nl = wn * 32 * WN + cb * 16 + l16;
-      const float bn = bias ? __half2float(bias[n0 + nl]) : 0.f;
+      const float bn = bias ? Io<IO>::to_f(bias[n0 + nl]) : 0.f;
 #pragma unroll
       for (int rb = 0; rb < RB4; ++rb)
 #pragma unroll
@@ -401,7 +397,7 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restr
           }
         __syncthreads();
         const int part = (n0 / BN) / qe.heads;   // 0: Q, 1: K
-        const __half* nw = reinterpret_cast<const __half*>(qe.qk_norm_w) + part * BN;
+        const uint16_t* nw = reinterpret_cast<const uint16_t*>(qe.qk_norm_w) + part * BN;
 #pragma unroll
         for (int rb = 0; rb < RB4; ++rb)
 #pragma unroll
@@ -413,7 +409,7 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restr
 #pragma unroll
             for (int cb = 0; cb < CB4; ++cb) {
               const int d = wn * 32 * WN + cb * 16 + l16;   // channel within the head
-              const float v = yv[rb][cb][i] * inv * __half2float(nw[d]);
+              const float v = yv[rb][cb][i] * inv * Io<IO>::to_f(nw[d]);
               // partner channel d ^ 1 sits in lane ^ 1 (columns are lanes)
               const float pv = __int_as_float(
                   __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
@@ -431,20 +427,20 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restr
       for (int rb = 0; rb < RB4; ++rb)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          tile[(wm * 32 * WM + rb * 16 + lq * 4 + i) * TP + nl] = __float2half_rn(yv[rb][cb][i]);
+          tile[(wm * 32 * WM + rb * 16 + lq * 4 + i) * TP + nl] = Io<IO>::from_f(yv[rb][cb][i]);
     }
   } else {
 #pragma unroll
     for (int cb = 0; cb < CB32; ++cb) {
       const int nl = brow[cb];
-      const float bn = bias ? __half2float(bias[n0 + nl]) : 0.f;
+      const float bn = bias ? Io<IO>::to_f(bias[n0 + nl]) : 0.f;
 #pragma unroll
       for (int rb = 0; rb < RB32; ++rb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           float yv = acc[rb][cb][v] + bn;
           if (EPI == 1) yv = gelu_tanh_f32(yv);
-          tile[(wm * 32 * WM + rb * 32 + (v >> 2) * 8 + lh * 4 + (v & 3)) * TP + nl] = __float2half_rn(yv);
+          tile[(wm * 32 * WM + rb * 32 + (v >> 2) * 8 + lh * 4 + (v & 3)) * TP + nl] = Io<IO>::from_f(yv);
         }
     }
   }
@@ -457,12 +453,12 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restr
   }
 }
 
-template <int FMT, int EPI, int WM, int WN, int STAGES>
+template <int IO, int FMT, int EPI, int WM, int WN, int STAGES>
 static hipError_t launch_cfg(int M, int N, int K, int r, const uint8_t* ac, const void* as,
                              const void* la, const uint8_t* wc, const void* ws, const void* lu,
                              const void* bias, void* Y, hipStream_t st, const QkvEpilogue& qe) {
   using S = GemmShape<WM, WN, STAGES>;
-  auto kern = gemm_w4a4_kernel<FMT, EPI, WM, WN, STAGES>;
+  auto kern = gemm_w4a4_kernel<IO, FMT, EPI, WM, WN, STAGES>;
   if (S::LDS > 65536) {
     static std::atomic<int> raised{0};
     if (!raised.load(std::memory_order_acquire)) {
@@ -473,17 +469,19 @@ static hipError_t launch_cfg(int M, int N, int K, int r, const uint8_t* ac, cons
     }
   }
   const int ntiles = ((M + S::BM - 1) / S::BM) * (N / S::BN);
-  hipLaunchKernelGGL(kern, dim3(ntiles), dim3(256), S::LDS, st, ac, as, (const __half*)la, wc, ws,
-                     (const __half*)lu, (const __half*)bias, (__half*)Y, M, N, K, r, qe);
+  hipLaunchKernelGGL(kern, dim3(ntiles), dim3(256), S::LDS, st, ac, as, (const uint16_t*)la, wc, ws,
+                     (const uint16_t*)lu, (const uint16_t*)bias, (uint16_t*)Y, M, N, K, r, qe);
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_w4a4(int fmt, int M, int N, int K, int r, const uint8_t* ac, const void* as,
-                            const void* la, const uint8_t* wc, const void* ws, const void* lu,
-                            const void* bias, int epi, void* Y, hipStream_t st, const QkvEpilogue* qkv) {
+template <int IO>
+static hipError_t launch_gemm_io(int fmt, int M, int N, int K, int r, const uint8_t* ac, const void* as,
+                                 const void* la, const uint8_t* wc, const void* ws, const void* lu,
+                                 const void* bias, int epi, void* Y, hipStream_t st,
+                                 const QkvEpilogue* qkv) {
   const QkvEpilogue qe = qkv ? *qkv : QkvEpilogue{nullptr, nullptr, 0.f, 1};
 #define SVDQ_GO(F, E, WM_, WN_, ST_) \
-  return launch_cfg<F, E, WM_, WN_, ST_>(M, N, K, r, ac, as, la, wc, ws, lu, bias, Y, st, qe)
+  return launch_cfg<IO, F, E, WM_, WN_, ST_>(M, N, K, r, ac, as, la, wc, ws, lu, bias, Y, st, qe)
   if (epi == 2) {   // fused QKV epilogue: INT4 only
     if (fmt != 0 || !qkv) return hipErrorInvalidValue;
     SVDQ_GO(0, 2, 2, 2, 3);
@@ -491,11 +489,18 @@ hipError_t launch_gemm_w4a4(int fmt, int M, int N, int K, int r, const uint8_t* 
   if (fmt == 0) {
     if (epi == 0) SVDQ_GO(0, 0, 2, 2, 3); else SVDQ_GO(0, 1, 2, 2, 3);
   } else {
-    const hipError_t e = launch_gemm_fp4_big(M, N, K, r, ac, as, la, wc, ws, lu, bias, epi, Y, st);
+    const hipError_t e = launch_gemm_fp4_big(IO, M, N, K, r, ac, as, la, wc, ws, lu, bias, epi, Y, st);
     if (e != hipErrorNotSupported) return e;
     if (epi == 0) SVDQ_GO(1, 0, 2, 2, 4); else SVDQ_GO(1, 1, 2, 2, 4);
   }
 #undef SVDQ_GO
+}
+
+hipError_t launch_gemm_w4a4(int fmt, int io, int M, int N, int K, int r, const uint8_t* ac, const void* as,
+                            const void* la, const uint8_t* wc, const void* ws, const void* lu,
+                            const void* bias, int epi, void* Y, hipStream_t st, const QkvEpilogue* qkv) {
+  if (io == 1) return launch_gemm_io<1>(fmt, M, N, K, r, ac, as, la, wc, ws, lu, bias, epi, Y, st, qkv);
+  return launch_gemm_io<0>(fmt, M, N, K, r, ac, as, la, wc, ws, lu, bias, epi, Y, st, qkv);
 }
 
 }  // namespace svdq

@@ -6,8 +6,9 @@
 
 namespace svdq {
 
+// io: 16-bit type of activations, low-rank branch, biases and outputs (0 fp16, 1 bf16)
 // fmt 0 INT4 g64, 1 FP4 E2M1 b32, 2 NVFP4 (gscale: the per-tensor scale)
-hipError_t launch_quantize_act(int fmt, int M, int K, int r, const void* X, const float* smooth_inv,
+hipError_t launch_quantize_act(int fmt, int io, int M, int K, int r, const void* X, const float* smooth_inv,
                                const void* lora_down, uint8_t* codes, void* scales, void* lora_act,
                                hipStream_t stream, float gscale = 1.0f);
 
@@ -22,23 +23,23 @@ struct QkvEpilogue {
   int heads;
 };
 
-hipError_t launch_gemm_w4a4(int fmt, int M, int N, int K, int r, const uint8_t* act_codes,
+hipError_t launch_gemm_w4a4(int fmt, int io, int M, int N, int K, int r, const uint8_t* act_codes,
                             const void* act_scales, const void* lora_act, const uint8_t* w_codes,
                             const void* w_scales, const void* lora_up, const void* bias, int epi,
                             void* Y, hipStream_t stream, const QkvEpilogue* qkv = nullptr);
 
-hipError_t launch_gemm_fp4_big(int M, int N, int K, int r, const uint8_t* act_codes,
+hipError_t launch_gemm_fp4_big(int io, int M, int N, int K, int r, const uint8_t* act_codes,
                                const void* act_scales, const void* lora_act, const uint8_t* w_codes,
                                const void* w_scales, const void* lora_up, const void* bias, int epi,
                                void* Y, hipStream_t stream);
 
 // NVFP4 GEMM: Y = act(alpha * sum (q_x s_x)(q_w s_w) + lora_act lora_up^T + bias)
-hipError_t launch_gemm_nvfp4(int M, int N, int K, int r, const uint8_t* act_codes,
+hipError_t launch_gemm_nvfp4(int io, int M, int N, int K, int r, const uint8_t* act_codes,
                              const uint8_t* act_scales, const void* lora_act, const uint8_t* w_codes,
                              const uint8_t* w_scales, const void* lora_up, const void* bias, float alpha,
                              int epi, void* Y, hipStream_t stream);
 
-hipError_t launch_awq_gemv(int M, int N, int K, const void* x, const uint8_t* codes,
+hipError_t launch_awq_gemv(int io, int M, int N, int K, const void* x, const uint8_t* codes,
                            const void* scales, const void* zeros, const void* bias, void* y,
                            hipStream_t stream);
 

@@ -56,11 +56,11 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
   return c < 8u ? (float)c * 0.001953125f : __uint_as_float((((c >> 3) + 120u) << 23) | ((c & 7u) << 20));
 }
 
-template <int FMT, int NCB, int WAVES, bool SLDS>
+template <int IO, int FMT, int NCB, int WAVES, bool SLDS>
 __global__ __launch_bounds__(64 * WAVES)
-void quantize_act_kernel(const __half* __restrict__ X, const float* __restrict__ smooth_inv,
-                         const __half* __restrict__ lora_down, uint8_t* __restrict__ codes,
-                         void* __restrict__ scales, __half* __restrict__ lora_act,
+void quantize_act_kernel(const uint16_t* __restrict__ X, const float* __restrict__ smooth_inv,
+                         const uint16_t* __restrict__ lora_down, uint8_t* __restrict__ codes,
+                         void* __restrict__ scales, uint16_t* __restrict__ lora_act,
                          int M, int K, float gs, float gs6) {
 #pragma clang fp contract(off)
   // LDS: two round buffers (codes, then scales, of 16 rows x WAVES steps),
@@ -115,7 +115,7 @@ void quantize_act_kernel(const __half* __restrict__ X, const float* __restrict__
     if constexpr (NCB > 0) {
 #pragma unroll
       for (int c = 0; c < NCB; ++c) {
-        const __half* pb = lora_down + (size_t)(c * 16 + (lane & 15)) * K + k0;
+        const uint16_t* pb = lora_down + (size_t)(c * 16 + (lane & 15)) * K + k0;
         d.lb[c][0] = *reinterpret_cast<const uint4*>(pb);
         d.lb[c][1] = *reinterpret_cast<const uint4*>(pb + 32);
       }
@@ -182,12 +182,10 @@ void quantize_act_kernel(const __half* __restrict__ X, const float* __restrict__
   auto process = [&](const Step& d, int s, uint8_t* rb) {
     const int k0 = s * 64 + q4 * 8;
     if constexpr (NCB > 0) {
-      const v8h a0 = __builtin_bit_cast(v8h, d.xa);
-      const v8h a1 = __builtin_bit_cast(v8h, d.xb);
 #pragma unroll
       for (int c = 0; c < NCB; ++c) {
-        lacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, __builtin_bit_cast(v8h, d.lb[c][0]), lacc[c], 0, 0, 0);
-        lacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, __builtin_bit_cast(v8h, d.lb[c][1]), lacc[c], 0, 0, 0);
+        lacc[c] = Io<IO>::mma16x16x32(d.xa, d.lb[c][0], lacc[c]);
+        lacc[c] = Io<IO>::mma16x16x32(d.xb, d.lb[c][1], lacc[c]);
       }
     }
     // smoothing: x_hat = fl32(fp32(x) * smooth_inv), a plain IEEE multiply.
@@ -204,12 +202,12 @@ void quantize_act_kernel(const __half* __restrict__ X, const float* __restrict__
         sv[8 * h + 4] = u1.x; sv[8 * h + 5] = u1.y; sv[8 * h + 6] = u1.z; sv[8 * h + 7] = u1.w;
       }
       // one fma with a -0 addend: the product rounded once, sign of zero kept
-      const __half* ha = reinterpret_cast<const __half*>(&d.xa);
-      const __half* hb = reinterpret_cast<const __half*>(&d.xb);
+      const uint16_t* ha = reinterpret_cast<const uint16_t*>(&d.xa);
+      const uint16_t* hb = reinterpret_cast<const uint16_t*>(&d.xb);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        xh[i] = fmaf(__half2float(ha[i]), sv[i], -0.0f);
-        xh[8 + i] = fmaf(__half2float(hb[i]), sv[8 + i], -0.0f);
+        xh[i] = fmaf(Io<IO>::to_f(ha[i]), sv[i], -0.0f);
+        xh[8 + i] = fmaf(Io<IO>::to_f(hb[i]), sv[8 + i], -0.0f);
       }
     }
     uint8_t* crow = rb + (lane & 15) * CROW + wave * 32 + q4 * 4;
@@ -378,12 +376,12 @@ void quantize_act_kernel(const __half* __restrict__ X, const float* __restrict__
       float sum = 0.f;
 #pragma unroll
       for (int w = 0; w < WAVES; ++w) sum += red[(w * 16 + rr) * R + cc];
-      if (m0 + rr < M) lora_act[(size_t)(m0 + rr) * R + cc] = __float2half_rn(sum);
+      if (m0 + rr < M) lora_act[(size_t)(m0 + rr) * R + cc] = Io<IO>::from_f(sum);
     }
   }
 }
 
-template <int FMT, int NCB, int WAVES, bool SLDS>
+template <int IO, int FMT, int NCB, int WAVES, bool SLDS>
 static hipError_t launch_qws(int M, int K, const void* X, const float* si, const void* ld,
                              uint8_t* codes, void* scales, void* la, float gs, hipStream_t st) {
   const dim3 grid((M + 15) / 16), block(64 * WAVES);
@@ -393,25 +391,25 @@ static hipError_t launch_qws(int M, int K, const void* X, const float* si, const
     static std::atomic<int> raised{0};
     if (!raised.load(std::memory_order_acquire)) {
       const hipError_t e = hipFuncSetAttribute(
-          reinterpret_cast<const void*>(&quantize_act_kernel<FMT, NCB, WAVES, SLDS>),
+          reinterpret_cast<const void*>(&quantize_act_kernel<IO, FMT, NCB, WAVES, SLDS>),
           hipFuncAttributeMaxDynamicSharedMemorySize, kQuantLdsMax);
       if (e != hipSuccess) return e;
       raised.store(1, std::memory_order_release);
     }
   }
-  hipLaunchKernelGGL((quantize_act_kernel<FMT, NCB, WAVES, SLDS>), grid, block, lds, st,
-                     (const __half*)X, si, (const __half*)ld, codes, scales, (__half*)la, M, K, gs,
+  hipLaunchKernelGGL((quantize_act_kernel<IO, FMT, NCB, WAVES, SLDS>), grid, block, lds, st,
+                     (const uint16_t*)X, si, (const uint16_t*)ld, codes, scales, (uint16_t*)la, M, K, gs,
                      6.0f * gs);
   return hipGetLastError();
 }
 
 // smooth_inv goes to LDS when it fits beside the low-rank partials
-template <int FMT, int NCB, int WAVES>
+template <int IO, int FMT, int NCB, int WAVES>
 static hipError_t launch_qw(int M, int K, const void* X, const float* si, const void* ld,
                             uint8_t* codes, void* scales, void* la, float gs, hipStream_t st) {
   if (quant_lds_bytes<WAVES>(NCB) + (size_t)K * sizeof(float) <= (size_t)kQuantLdsMax)
-    return launch_qws<FMT, NCB, WAVES, true>(M, K, X, si, ld, codes, scales, la, gs, st);
-  return launch_qws<FMT, NCB, WAVES, false>(M, K, X, si, ld, codes, scales, la, gs, st);
+    return launch_qws<IO, FMT, NCB, WAVES, true>(M, K, X, si, ld, codes, scales, la, gs, st);
+  return launch_qws<IO, FMT, NCB, WAVES, false>(M, K, X, si, ld, codes, scales, la, gs, st);
 }
 
 // 16 rows per workgroup. With at least one workgroup per CU, 8 waves (2 per
@@ -419,41 +417,49 @@ static hipError_t launch_qw(int M, int K, const void* X, const float* si, const 
 // a small rank, 16 waves so that each busy CU keeps more loads in flight; for
 // ranks of 112 and more, 4 waves (the lora_down operands of a step take
 // 8 * r / 16 VGPRs per set).
-template <int FMT, int NCB>
+template <int IO, int FMT, int NCB>
 static hipError_t launch_q(int M, int K, const void* X, const float* si, const void* ld,
                            uint8_t* codes, void* scales, void* la, float gs, hipStream_t st) {
   if constexpr (NCB >= 7) {
-    return launch_qw<FMT, NCB, 4>(M, K, X, si, ld, codes, scales, la, gs, st);
+    return launch_qw<IO, FMT, NCB, 4>(M, K, X, si, ld, codes, scales, la, gs, st);
   } else if constexpr (NCB > 2) {
-    return launch_qw<FMT, NCB, 8>(M, K, X, si, ld, codes, scales, la, gs, st);
+    return launch_qw<IO, FMT, NCB, 8>(M, K, X, si, ld, codes, scales, la, gs, st);
   } else {
-    if ((M + 15) / 16 >= 256) return launch_qw<FMT, NCB, 8>(M, K, X, si, ld, codes, scales, la, gs, st);
-    return launch_qw<FMT, NCB, 16>(M, K, X, si, ld, codes, scales, la, gs, st);
+    if ((M + 15) / 16 >= 256) return launch_qw<IO, FMT, NCB, 8>(M, K, X, si, ld, codes, scales, la, gs, st);
+    return launch_qw<IO, FMT, NCB, 16>(M, K, X, si, ld, codes, scales, la, gs, st);
   }
 }
 
-template <int FMT>
+template <int IO, int FMT>
 static hipError_t launch_q_r(int M, int K, int r, const void* X, const float* si, const void* ld,
                              uint8_t* codes, void* scales, void* la, float gs, hipStream_t st) {
   switch (r / 16) {
-    case 0: return launch_q<FMT, 0>(M, K, X, si, ld, codes, scales, la, gs, st);
-    case 1: return launch_q<FMT, 1>(M, K, X, si, ld, codes, scales, la, gs, st);
-    case 2: return launch_q<FMT, 2>(M, K, X, si, ld, codes, scales, la, gs, st);
-    case 3: return launch_q<FMT, 3>(M, K, X, si, ld, codes, scales, la, gs, st);
-    case 4: return launch_q<FMT, 4>(M, K, X, si, ld, codes, scales, la, gs, st);
-    case 5: return launch_q<FMT, 5>(M, K, X, si, ld, codes, scales, la, gs, st);
-    case 6: return launch_q<FMT, 6>(M, K, X, si, ld, codes, scales, la, gs, st);
-    case 7: return launch_q<FMT, 7>(M, K, X, si, ld, codes, scales, la, gs, st);
-    default: return launch_q<FMT, 8>(M, K, X, si, ld, codes, scales, la, gs, st);
+    case 0: return launch_q<IO, FMT, 0>(M, K, X, si, ld, codes, scales, la, gs, st);
+    case 1: return launch_q<IO, FMT, 1>(M, K, X, si, ld, codes, scales, la, gs, st);
+    case 2: return launch_q<IO, FMT, 2>(M, K, X, si, ld, codes, scales, la, gs, st);
+    case 3: return launch_q<IO, FMT, 3>(M, K, X, si, ld, codes, scales, la, gs, st);
+    case 4: return launch_q<IO, FMT, 4>(M, K, X, si, ld, codes, scales, la, gs, st);
+    case 5: return launch_q<IO, FMT, 5>(M, K, X, si, ld, codes, scales, la, gs, st);
+    case 6: return launch_q<IO, FMT, 6>(M, K, X, si, ld, codes, scales, la, gs, st);
+    case 7: return launch_q<IO, FMT, 7>(M, K, X, si, ld, codes, scales, la, gs, st);
+    default: return launch_q<IO, FMT, 8>(M, K, X, si, ld, codes, scales, la, gs, st);
   }
 }
 
-hipError_t launch_quantize_act(int fmt, int M, int K, int r, const void* X, const float* si,
+template <int IO>
+static hipError_t launch_q_io(int fmt, int M, int K, int r, const void* X, const float* si,
+                              const void* ld, uint8_t* codes, void* scales, void* la,
+                              hipStream_t st, float gscale) {
+  if (fmt == 0) return launch_q_r<IO, 0>(M, K, r, X, si, ld, codes, scales, la, 1.0f, st);
+  if (fmt == 2) return launch_q_r<IO, 2>(M, K, r, X, si, ld, codes, scales, la, gscale, st);
+  return launch_q_r<IO, 1>(M, K, r, X, si, ld, codes, scales, la, 1.0f, st);
+}
+
+hipError_t launch_quantize_act(int fmt, int io, int M, int K, int r, const void* X, const float* si,
                                const void* ld, uint8_t* codes, void* scales, void* la,
                                hipStream_t st, float gscale) {
-  if (fmt == 0) return launch_q_r<0>(M, K, r, X, si, ld, codes, scales, la, 1.0f, st);
-  if (fmt == 2) return launch_q_r<2>(M, K, r, X, si, ld, codes, scales, la, gscale, st);
-  return launch_q_r<1>(M, K, r, X, si, ld, codes, scales, la, 1.0f, st);
+  if (io == 1) return launch_q_io<1>(fmt, M, K, r, X, si, ld, codes, scales, la, st, gscale);
+  return launch_q_io<0>(fmt, M, K, r, X, si, ld, codes, scales, la, st, gscale);
 }
 
 }  // namespace svdq

@@ -22,7 +22,8 @@ The linears run on the library's kernels once quantize_model /
 fuse_qkv_norm_rope have swapped them in. The rest of the block (LayerNorm,
 modulation arithmetic, attention, residuals) is plain torch arithmetic in
 fp32 (fp64 for fp64 inputs): it is not part of the 4-bit linear layers. The
-inputs of a 4-bit layer are rounded to fp16, which those layers take.
+inputs of a 4-bit layer are rounded to its 16-bit compute type (fp16 or
+bf16), which those layers take.
 """
 from __future__ import annotations
 
@@ -44,7 +45,7 @@ def _glue_dtype(t: torch.Tensor):
 def _linear(mod: nn.Module, x: torch.Tensor) -> torch.Tensor:
     """Apply a dense or 4-bit linear; the result comes back in x's dtype."""
     if isinstance(mod, (SVDQLinear, AWQLinear)):
-        return mod(x.to(torch.float16)).to(x.dtype)
+        return mod(x.to(mod.io_dtype)).to(x.dtype)
     return mod(x.to(mod.weight.dtype)).to(x.dtype)
 
 
@@ -88,7 +89,7 @@ class SelfAttention(nn.Module):
         H = self.heads
         if isinstance(getattr(self, "to_qkv", None), SVDQLinearQKV):
             q, k, v = (t.to(h.dtype).reshape(B, T, H, HEAD_DIM)
-                       for t in self.to_qkv(h.to(torch.float16), rope))
+                       for t in self.to_qkv(h.to(self.to_qkv.io_dtype), rope))
         else:
             q, k, v = (_linear(m, h).reshape(B, T, H, HEAD_DIM)
                        for m in (self.to_q, self.to_k, self.to_v))

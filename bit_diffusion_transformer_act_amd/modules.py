@@ -25,11 +25,11 @@ from . import ops
 from .config import QuantConfig, parse_quantization_config
 
 
-def _as_rows(x: torch.Tensor, K: int, name: str) -> torch.Tensor:
+def _as_rows(x: torch.Tensor, K: int, name: str, dtype=torch.float16) -> torch.Tensor:
     if x.device.type != "cuda":
         raise RuntimeError(f"{name}: input is on {x.device}; the 4-bit kernels run only on a HIP device")
-    if x.dtype != torch.float16:
-        raise TypeError(f"{name}: input dtype {x.dtype}, expected torch.float16")
+    if x.dtype != dtype:
+        raise TypeError(f"{name}: input dtype {x.dtype}, expected {dtype}")
     if x.shape[-1] != K:
         raise ValueError(f"{name}: input has {x.shape[-1]} channels, expected {K}")
     return x.reshape(-1, K).contiguous()
@@ -38,12 +38,13 @@ def _as_rows(x: torch.Tensor, K: int, name: str) -> torch.Tensor:
 class SVDQLinear(nn.Module):
     """y = x W^T + b with W held as smoothing + low-rank branch + 4-bit residual.
 
-    Buffers (the layout the C ABI takes, N = out_features, K = in_features):
-      smooth_inv fp32 [K]; lora_down fp16 [r][K]; lora_up fp16 [N][r];
+    Buffers (the layout the C ABI takes, N = out_features, K = in_features;
+    16-bit ones in the layer's compute dtype, float16 or bfloat16):
+      smooth_inv fp32 [K]; lora_down [r][K]; lora_up [N][r];
       w_codes u8 [N][K/2] (even-k code in the low nibble);
       w_scales fp16 [N][K/64] (int4_g64), E8M0 u8 [N][K/32] (fp4_b32) or
       E4M3 u8 [N][K/16] (nvfp4_g16);
-      bias fp16 [N] when bias=True;
+      bias [N] when bias=True;
       nvfp4_g16 only: act_gscale and w_gscale, fp32 scalars (the per-tensor
       scales of the activations, fixed from calibration, and of the weight).
     epilogue "gelu_tanh" applies the tanh-approximated GELU inside the GEMM.
@@ -51,8 +52,11 @@ class SVDQLinear(nn.Module):
 
     def __init__(self, in_features: int, out_features: int, rank: int = 32,
                  fmt: str = "int4_g64", bias: bool = True, epilogue: str = "none",
-                 device=None):
+                 device=None, dtype=torch.float16):
         super().__init__()
+        if dtype not in (torch.float16, torch.bfloat16):
+            raise ValueError("the compute dtype is torch.float16 or torch.bfloat16")
+        self.io_dtype = dtype
         if fmt not in ops.ALL_FORMATS:
             raise ValueError(f"unknown format {fmt!r}")
         if epilogue not in ops.EPILOGUES:
@@ -70,12 +74,12 @@ class SVDQLinear(nn.Module):
                    "nvfp4_g16": (torch.uint8, 16)}[fmt]
         kw = {"device": device}
         self.register_buffer("smooth_inv", torch.ones(K, dtype=torch.float32, **kw))
-        self.register_buffer("lora_down", torch.zeros(rank, K, dtype=torch.float16, **kw))
-        self.register_buffer("lora_up", torch.zeros(N, rank, dtype=torch.float16, **kw))
+        self.register_buffer("lora_down", torch.zeros(rank, K, dtype=dtype, **kw))
+        self.register_buffer("lora_up", torch.zeros(N, rank, dtype=dtype, **kw))
         self.register_buffer("w_codes", torch.zeros(N, K // 2, dtype=torch.uint8, **kw))
         self.register_buffer("w_scales", torch.zeros(N, K // sg, dtype=sdt, **kw))
         if bias:
-            self.register_buffer("bias", torch.zeros(N, dtype=torch.float16, **kw))
+            self.register_buffer("bias", torch.zeros(N, dtype=dtype, **kw))
         else:
             self.bias = None
         if fmt == "nvfp4_g16":
@@ -102,11 +106,11 @@ class SVDQLinear(nn.Module):
 
     def extra_repr(self) -> str:
         return (f"in_features={self.in_features}, out_features={self.out_features}, "
-                f"rank={self.rank}, fmt={self.fmt}, epilogue={self.epilogue}")
+                f"rank={self.rank}, fmt={self.fmt}, epilogue={self.epilogue}, dtype={self.io_dtype}")
 
     def quantize_input(self, x: torch.Tensor):
         """The first fused call: 4-bit codes, scales and the low-rank activation."""
-        X = _as_rows(x, self.in_features, "SVDQLinear")
+        X = _as_rows(x, self.in_features, "SVDQLinear", self.io_dtype)
         ld = self.lora_down if self.rank else None
         if self.fmt == "nvfp4_g16":
             return ops.svdq_quantize_act_nvfp4(X, self.smooth_inv, ld, self._gs[0])
@@ -117,10 +121,10 @@ class SVDQLinear(nn.Module):
         lu = self.lora_up if self.rank else None
         if self.fmt == "nvfp4_g16":
             y = ops.svdq_gemm_nvfp4(codes, scales, la, self.w_codes, self.w_scales, lu, self.bias,
-                                    self._alpha, self.epilogue)
+                                    self._alpha, self.epilogue, dtype=self.io_dtype)
         else:
             y = ops.svdq_gemm_w4a4(codes, scales, la, self.w_codes, self.w_scales, lu, self.bias,
-                                   self.fmt, self.epilogue)
+                                   self.fmt, self.epilogue, dtype=self.io_dtype)
         return y.reshape(*x.shape[:-1], self.out_features)
 
 
@@ -136,14 +140,14 @@ class SVDQLinearQKV(SVDQLinear):
     Only the int4_g64 format has the fused epilogue."""
 
     def __init__(self, dim: int, rank: int = 32, fmt: str = "int4_g64", bias: bool = True,
-                 eps: float = 1e-6, device=None):
+                 eps: float = 1e-6, device=None, dtype=torch.float16):
         if fmt != "int4_g64":
             raise ValueError("the fused QKV epilogue is built for int4_g64 only")
         if dim % 128:
             raise ValueError("dim must be a whole number of 128-channel heads")
-        super().__init__(dim, 3 * dim, rank, fmt, bias, "none", device)
+        super().__init__(dim, 3 * dim, rank, fmt, bias, "none", device, dtype)
         self.dim, self.eps = dim, float(eps)
-        self.register_buffer("qk_norm_w", torch.ones(2, 128, dtype=torch.float16, device=device))
+        self.register_buffer("qk_norm_w", torch.ones(2, 128, dtype=dtype, device=device))
 
     def forward(self, x: torch.Tensor, rope: torch.Tensor):
         codes, scales, la = self.quantize_input(x)
@@ -155,7 +159,8 @@ class SVDQLinearQKV(SVDQLinear):
             rope = rope.repeat(M // rope.shape[0], 1, 1)
         y = ops.svdq_gemm_w4a4_qkv(codes, scales, la, self.w_codes, self.w_scales,
                                    self.lora_up if self.rank else None, self.bias,
-                                   self.qk_norm_w, rope.contiguous(), self.eps, self.fmt)
+                                   self.qk_norm_w, rope.contiguous(), self.eps, self.fmt,
+                                   dtype=self.io_dtype)
         y = y.reshape(*x.shape[:-1], 3 * self.dim)
         return y.split(self.dim, dim=-1)
 
@@ -163,15 +168,19 @@ class SVDQLinearQKV(SVDQLinear):
 class AWQLinear(nn.Module):
     """y = x W^T + b with W held as AWQ 4-bit codes: w = (q - z) s per group of
     64 along K. Buffers: w_codes u8 [N][K/2] (unsigned, even-k code in the low
-    nibble), scales and zeros fp16 [N][K/64], bias fp16 [N]. For the
+    nibble), scales and zeros fp16 [N][K/64], bias [N] in the compute dtype
+    (float16 or bfloat16, that of the input). For the
     memory-bound modulation projections: at most 8 rows per call of the GEMV,
     larger inputs go through it 8 rows at a time."""
 
     MAX_ROWS = 8
 
     def __init__(self, in_features: int, out_features: int, group_size: int = 64,
-                 bias: bool = True, device=None):
+                 bias: bool = True, device=None, dtype=torch.float16):
         super().__init__()
+        if dtype not in (torch.float16, torch.bfloat16):
+            raise ValueError("the compute dtype is torch.float16 or torch.bfloat16")
+        self.io_dtype = dtype
         if group_size != 64:
             raise ValueError("AWQLinear supports group_size 64")
         if in_features % 64:
@@ -183,18 +192,19 @@ class AWQLinear(nn.Module):
         self.register_buffer("scales", torch.zeros(N, K // 64, dtype=torch.float16, **kw))
         self.register_buffer("zeros", torch.zeros(N, K // 64, dtype=torch.float16, **kw))
         if bias:
-            self.register_buffer("bias", torch.zeros(N, dtype=torch.float16, **kw))
+            self.register_buffer("bias", torch.zeros(N, dtype=dtype, **kw))
         else:
             self.bias = None
 
     def extra_repr(self) -> str:
-        return f"in_features={self.in_features}, out_features={self.out_features}, group_size=64"
+        return (f"in_features={self.in_features}, out_features={self.out_features}, group_size=64, "
+                f"dtype={self.io_dtype}")
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
-        X = _as_rows(x, self.in_features, "AWQLinear")
+        X = _as_rows(x, self.in_features, "AWQLinear", self.io_dtype)
         M, N = X.shape[0], self.out_features
         rows = max(1, min(self.MAX_ROWS, 32768 // self.in_features))
-        y = torch.empty((M, N), dtype=torch.float16, device=X.device)
+        y = torch.empty((M, N), dtype=self.io_dtype, device=X.device)
         for m0 in range(0, M, rows):
             ops.awq_gemv_w4a16(X[m0:m0 + rows], self.w_codes, self.scales, self.zeros, 64,
                                out=y[m0:m0 + rows], bias=self.bias)
@@ -219,6 +229,7 @@ def quantize_model(model: nn.Module, config, device=None, fuse_gelu: bool = True
     empty: fill them with load_state_dict.
     """
     q = config if isinstance(config, QuantConfig) else parse_quantization_config(config)
+    io = torch.bfloat16 if q.compute_dtype == "bfloat16" else torch.float16
     done = []
     for name, mod in list(model.named_modules()):
         if not isinstance(mod, nn.Linear):
@@ -230,10 +241,10 @@ def quantize_model(model: nn.Module, config, device=None, fuse_gelu: bool = True
         has_bias = mod.bias is not None
         if how == "svdq":
             new = SVDQLinear(mod.in_features, mod.out_features, q.svdq.rank, q.svdq.fmt,
-                             has_bias, device=dev)
+                             has_bias, device=dev, dtype=io)
         else:
             new = AWQLinear(mod.in_features, mod.out_features, q.awq.group_size, has_bias,
-                            device=dev)
+                            device=dev, dtype=io)
         _set_child(model, name, new)
         done.append(name)
     if fuse_gelu:
@@ -256,8 +267,8 @@ def _norm_pair_hook(module, state_dict, prefix, local_metadata, strict, missing,
     kq, kk = prefix + "norm_q.weight", prefix + "norm_k.weight"
     if kq in state_dict and kk in state_dict:
         wq, wk = state_dict.pop(kq), state_dict.pop(kk)
-        state_dict.setdefault(prefix + "to_qkv.qk_norm_w",
-                              torch.stack([wq.reshape(-1), wk.reshape(-1)]).to(torch.float16))
+        # load_state_dict converts to the buffer's own dtype
+        state_dict.setdefault(prefix + "to_qkv.qk_norm_w", torch.stack([wq.reshape(-1), wk.reshape(-1)]))
 
 
 def fuse_qkv_norm_rope(model: nn.Module) -> list:
@@ -280,13 +291,14 @@ def fuse_qkv_norm_rope(model: nn.Module) -> list:
             continue
         q = parts[0]
         if any(p.fmt != "int4_g64" or p.in_features != q.in_features or p.out_features != q.in_features
-               or p.rank != q.rank or (p.bias is None) != (q.bias is None) for p in parts):
+               or p.rank != q.rank or (p.bias is None) != (q.bias is None) or p.io_dtype != q.io_dtype
+               for p in parts):
             continue
         if getattr(nq, "weight", None) is None or nq.weight.numel() != 128 or nk.weight.numel() != 128:
             continue
         eps = float(getattr(nq, "eps", 1e-6) or 1e-6)
         fused = SVDQLinearQKV(q.in_features, q.rank, q.fmt, q.bias is not None, eps,
-                              device=q.w_codes.device)
+                              device=q.w_codes.device, dtype=q.io_dtype)
         with torch.no_grad():
             fused.qk_norm_w.copy_(torch.stack([nq.weight.reshape(-1), nk.weight.reshape(-1)]))
         for a in ("to_q", "to_k", "to_v", "norm_q", "norm_k"):

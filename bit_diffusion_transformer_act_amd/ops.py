@@ -26,6 +26,9 @@ EPI_NONE = 0
 EPI_GELU_TANH = 1
 EPILOGUES = {"none": EPI_NONE, "gelu_tanh": EPI_GELU_TANH}
 
+# the layer's 16-bit compute type (activations, low-rank branch, biases, outputs)
+DTYPES = {torch.float16: 0, torch.bfloat16: 1}
+
 SVDQ_OK = 0
 SVDQ_ERR_INVALID_ARG = -1
 SVDQ_ERR_SHAPE = -2
@@ -64,19 +67,19 @@ def lib() -> ctypes.CDLL:
             h.svdq_status_str.restype = ctypes.c_char_p
             h.svdq_version.argtypes = []
             h.svdq_version.restype = i32
-            h.svdq_quantize_act.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
+            h.svdq_quantize_act.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
             h.svdq_quantize_act.restype = i32
-            h.svdq_gemm_w4a4.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp]
+            h.svdq_gemm_w4a4.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp]
             h.svdq_gemm_w4a4.restype = i32
-            h.svdq_gemm_w4a4_qkv.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+            h.svdq_gemm_w4a4_qkv.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                              ctypes.c_float, vp, vp]
             h.svdq_gemm_w4a4_qkv.restype = i32
             f32 = ctypes.c_float
-            h.svdq_quantize_act_nvfp4.argtypes = [i32, i32, i32, vp, vp, vp, f32, vp, vp, vp, vp]
+            h.svdq_quantize_act_nvfp4.argtypes = [i32, i32, i32, i32, vp, vp, vp, f32, vp, vp, vp, vp]
             h.svdq_quantize_act_nvfp4.restype = i32
-            h.svdq_gemm_nvfp4.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, f32, i32, vp, vp]
+            h.svdq_gemm_nvfp4.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, f32, i32, vp, vp]
             h.svdq_gemm_nvfp4.restype = i32
-            h.awq_gemv_w4a16.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
+            h.awq_gemv_w4a16.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
             h.awq_gemv_w4a16.restype = i32
             _handle = h
         return _handle
@@ -115,6 +118,22 @@ def _check(t: torch.Tensor, name: str, dtype, shape, dev):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _io(t: torch.Tensor, name: str) -> int:
+    if t.dtype not in DTYPES:
+        raise TypeError(f"{name} has dtype {t.dtype}; the layer's 16-bit type is float16 or bfloat16")
+    return DTYPES[t.dtype]
+
+
+def _pick_dtype(dtype, *tensors):
+    """The GEMM's 16-bit type: given, else that of the first 16-bit tensor passed, else fp16."""
+    if dtype is not None:
+        return dtype
+    for t in tensors:
+        if t is not None:
+            return t.dtype
+    return torch.float16
+
+
 def _fmt(fmt) -> int:
     if isinstance(fmt, str):
         if fmt not in FORMATS:
@@ -133,33 +152,36 @@ def svdq_quantize_act(X: torch.Tensor, smooth_inv: torch.Tensor, lora_down, fmt=
                       act_codes=None, act_scales=None, lora_act=None):
     """Smoothing + low-rank down-projection + 4-bit activation quantization.
 
-    X fp16 [M][K]; smooth_inv fp32 [K]; lora_down fp16 [r][K] or None.
-    Returns (act_codes u8 [M][K/2], act_scales fp16 [M][K/64] | u8 [M][K/32],
-    lora_act fp16 [M][r] or None). Output tensors may be passed in.
+    X [M][K] in the layer's 16-bit type (float16 or bfloat16); smooth_inv fp32
+    [K]; lora_down [r][K] (same 16-bit type) or None. Returns (act_codes u8
+    [M][K/2], act_scales fp16 [M][K/64] | u8 [M][K/32], lora_act [M][r] or
+    None). Output tensors may be passed in.
     """
     f = _fmt(fmt)
     dev = X.device
     if dev.type != "cuda":
         raise ValueError("X must be a HIP device tensor")
     M, K = X.shape
+    io = _io(X, "X")
+    h = X.dtype
     r = 0 if lora_down is None else lora_down.shape[0]
-    _check(X, "X", torch.float16, (M, K), dev)
+    _check(X, "X", h, (M, K), dev)
     _check(smooth_inv, "smooth_inv", torch.float32, (K,), dev)
     if lora_down is not None:
-        _check(lora_down, "lora_down", torch.float16, (r, K), dev)
+        _check(lora_down, "lora_down", h, (r, K), dev)
     sdt, sshape = _scale_spec(f, M, K)
     if act_codes is None:
         act_codes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
     if act_scales is None:
         act_scales = torch.empty(sshape, dtype=sdt, device=dev)
     if r > 0 and lora_act is None:
-        lora_act = torch.empty((M, r), dtype=torch.float16, device=dev)
+        lora_act = torch.empty((M, r), dtype=h, device=dev)
     _check(act_codes, "act_codes", torch.uint8, (M, K // 2), dev)
     _check(act_scales, "act_scales", sdt, sshape, dev)
     if r > 0:
-        _check(lora_act, "lora_act", torch.float16, (M, r), dev)
+        _check(lora_act, "lora_act", h, (M, r), dev)
     with torch.cuda.device(dev):
-        st = lib().svdq_quantize_act(f, M, K, r, _ptr(X), _ptr(smooth_inv), _ptr(lora_down),
+        st = lib().svdq_quantize_act(f, io, M, K, r, _ptr(X), _ptr(smooth_inv), _ptr(lora_down),
                                      _ptr(act_codes), _ptr(act_scales),
                                      _ptr(lora_act) if r > 0 else None, _stream(dev))
     if st != SVDQ_OK:
@@ -168,9 +190,13 @@ def svdq_quantize_act(X: torch.Tensor, smooth_inv: torch.Tensor, lora_down, fmt=
 
 
 def svdq_gemm_w4a4(act_codes, act_scales, lora_act, w_codes, w_scales, lora_up, bias,
-                   fmt="int4_g64", epilogue="none", out=None):
-    """Fused 4-bit GEMM + low-rank up-projection + bias (+ GELU) -> Y fp16 [M][N]."""
+                   fmt="int4_g64", epilogue="none", out=None, dtype=None):
+    """Fused 4-bit GEMM + low-rank up-projection + bias (+ GELU) -> Y [M][N] in
+    the layer's 16-bit type (dtype, else that of lora_act / lora_up / bias /
+    out, else float16)."""
     f = _fmt(fmt)
+    h = _pick_dtype(dtype, lora_act, lora_up, bias, out)
+    io = DTYPES[h]
     e = EPILOGUES[epilogue] if isinstance(epilogue, str) else int(epilogue)
     dev = act_codes.device
     if dev.type != "cuda":
@@ -186,15 +212,15 @@ def svdq_gemm_w4a4(act_codes, act_scales, lora_act, w_codes, w_scales, lora_up, 
     _check(w_codes, "w_codes", torch.uint8, (N, KB), dev)
     _check(w_scales, "w_scales", sdt, sw_shape, dev)
     if r > 0:
-        _check(lora_act, "lora_act", torch.float16, (M, r), dev)
-        _check(lora_up, "lora_up", torch.float16, (N, r), dev)
+        _check(lora_act, "lora_act", h, (M, r), dev)
+        _check(lora_up, "lora_up", h, (N, r), dev)
     if bias is not None:
-        _check(bias, "bias", torch.float16, (N,), dev)
+        _check(bias, "bias", h, (N,), dev)
     if out is None:
-        out = torch.empty((M, N), dtype=torch.float16, device=dev)
-    _check(out, "out", torch.float16, (M, N), dev)
+        out = torch.empty((M, N), dtype=h, device=dev)
+    _check(out, "out", h, (M, N), dev)
     with torch.cuda.device(dev):
-        st = lib().svdq_gemm_w4a4(f, M, N, K, r, _ptr(act_codes), _ptr(act_scales),
+        st = lib().svdq_gemm_w4a4(f, io, M, N, K, r, _ptr(act_codes), _ptr(act_scales),
                                   _ptr(lora_act) if r > 0 else None, _ptr(w_codes), _ptr(w_scales),
                                   _ptr(lora_up) if r > 0 else None, _ptr(bias), e, _ptr(out),
                                   _stream(dev))
@@ -204,11 +230,14 @@ def svdq_gemm_w4a4(act_codes, act_scales, lora_act, w_codes, w_scales, lora_up, 
 
 
 def svdq_gemm_w4a4_qkv(act_codes, act_scales, lora_act, w_codes, w_scales, lora_up, bias,
-                       qk_norm_w, rope, eps: float = 1e-6, fmt="int4_g64", out=None):
+                       qk_norm_w, rope, eps: float = 1e-6, fmt="int4_g64", out=None, dtype=None):
     """Fused Q|K|V projection: the 4-bit GEMM, then per-head (128-channel)
     RMSNorm of the Q and K thirds and the rotation of channel pairs by rope
-    (fp32 [M][64][2] cos, sin); V unchanged -> Y fp16 [M][N], N % 384 == 0."""
+    (fp32 [M][64][2] cos, sin); V unchanged -> Y [M][N], N % 384 == 0, in the
+    layer's 16-bit type (that of qk_norm_w)."""
     f = _fmt(fmt)
+    h = _pick_dtype(dtype, qk_norm_w)
+    io = DTYPES[h]
     dev = act_codes.device
     if dev.type != "cuda":
         raise ValueError("act_codes must be a HIP device tensor")
@@ -223,17 +252,17 @@ def svdq_gemm_w4a4_qkv(act_codes, act_scales, lora_act, w_codes, w_scales, lora_
     _check(w_codes, "w_codes", torch.uint8, (N, KB), dev)
     _check(w_scales, "w_scales", sdt, sw_shape, dev)
     if r > 0:
-        _check(lora_act, "lora_act", torch.float16, (M, r), dev)
-        _check(lora_up, "lora_up", torch.float16, (N, r), dev)
+        _check(lora_act, "lora_act", h, (M, r), dev)
+        _check(lora_up, "lora_up", h, (N, r), dev)
     if bias is not None:
-        _check(bias, "bias", torch.float16, (N,), dev)
-    _check(qk_norm_w, "qk_norm_w", torch.float16, (2, 128), dev)
+        _check(bias, "bias", h, (N,), dev)
+    _check(qk_norm_w, "qk_norm_w", h, (2, 128), dev)
     _check(rope, "rope", torch.float32, (M, 64, 2), dev)
     if out is None:
-        out = torch.empty((M, N), dtype=torch.float16, device=dev)
-    _check(out, "out", torch.float16, (M, N), dev)
+        out = torch.empty((M, N), dtype=h, device=dev)
+    _check(out, "out", h, (M, N), dev)
     with torch.cuda.device(dev):
-        st = lib().svdq_gemm_w4a4_qkv(f, M, N, K, r, _ptr(act_codes), _ptr(act_scales),
+        st = lib().svdq_gemm_w4a4_qkv(f, io, M, N, K, r, _ptr(act_codes), _ptr(act_scales),
                                       _ptr(lora_act) if r > 0 else None, _ptr(w_codes), _ptr(w_scales),
                                       _ptr(lora_up) if r > 0 else None, _ptr(bias), _ptr(qk_norm_w),
                                       _ptr(rope), ctypes.c_float(eps), _ptr(out), _stream(dev))
@@ -246,28 +275,31 @@ def svdq_quantize_act_nvfp4(X: torch.Tensor, smooth_inv: torch.Tensor, lora_down
                             act_codes=None, act_scales=None, lora_act=None):
     """NVFP4 activation quantizer (E2M1 codes, E4M3 scale per 16, per-tensor
     scale act_gscale) + smoothing + low-rank down-projection.
-    Returns (act_codes u8 [M][K/2], act_scales u8 [M][K/16], lora_act fp16 [M][r] or None)."""
+    Returns (act_codes u8 [M][K/2], act_scales u8 [M][K/16], lora_act [M][r] or
+    None); X, lora_down and lora_act share the layer's 16-bit type."""
     dev = X.device
     if dev.type != "cuda":
         raise ValueError("X must be a HIP device tensor")
     M, K = X.shape
+    io = _io(X, "X")
+    h = X.dtype
     r = 0 if lora_down is None else lora_down.shape[0]
-    _check(X, "X", torch.float16, (M, K), dev)
+    _check(X, "X", h, (M, K), dev)
     _check(smooth_inv, "smooth_inv", torch.float32, (K,), dev)
     if lora_down is not None:
-        _check(lora_down, "lora_down", torch.float16, (r, K), dev)
+        _check(lora_down, "lora_down", h, (r, K), dev)
     if act_codes is None:
         act_codes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
     if act_scales is None:
         act_scales = torch.empty((M, K // 16), dtype=torch.uint8, device=dev)
     if r > 0 and lora_act is None:
-        lora_act = torch.empty((M, r), dtype=torch.float16, device=dev)
+        lora_act = torch.empty((M, r), dtype=h, device=dev)
     _check(act_codes, "act_codes", torch.uint8, (M, K // 2), dev)
     _check(act_scales, "act_scales", torch.uint8, (M, K // 16), dev)
     if r > 0:
-        _check(lora_act, "lora_act", torch.float16, (M, r), dev)
+        _check(lora_act, "lora_act", h, (M, r), dev)
     with torch.cuda.device(dev):
-        st = lib().svdq_quantize_act_nvfp4(M, K, r, _ptr(X), _ptr(smooth_inv), _ptr(lora_down),
+        st = lib().svdq_quantize_act_nvfp4(io, M, K, r, _ptr(X), _ptr(smooth_inv), _ptr(lora_down),
                                            ctypes.c_float(act_gscale), _ptr(act_codes), _ptr(act_scales),
                                            _ptr(lora_act) if r > 0 else None, _stream(dev))
     if st != SVDQ_OK:
@@ -276,10 +308,12 @@ def svdq_quantize_act_nvfp4(X: torch.Tensor, smooth_inv: torch.Tensor, lora_down
 
 
 def svdq_gemm_nvfp4(act_codes, act_scales, lora_act, w_codes, w_scales, lora_up, bias, alpha: float,
-                    epilogue="none", out=None):
-    """NVFP4 GEMM + low-rank up-projection + bias (+ GELU) -> Y fp16 [M][N];
-    alpha = act_gscale * w_gscale scales the 4-bit sum."""
+                    epilogue="none", out=None, dtype=None):
+    """NVFP4 GEMM + low-rank up-projection + bias (+ GELU) -> Y [M][N] in the
+    layer's 16-bit type; alpha = act_gscale * w_gscale scales the 4-bit sum."""
     e = EPILOGUES[epilogue] if isinstance(epilogue, str) else int(epilogue)
+    h = _pick_dtype(dtype, lora_act, lora_up, bias, out)
+    io = DTYPES[h]
     dev = act_codes.device
     if dev.type != "cuda":
         raise ValueError("act_codes must be a HIP device tensor")
@@ -292,15 +326,15 @@ def svdq_gemm_nvfp4(act_codes, act_scales, lora_act, w_codes, w_scales, lora_up,
     _check(w_codes, "w_codes", torch.uint8, (N, KB), dev)
     _check(w_scales, "w_scales", torch.uint8, (N, K // 16), dev)
     if r > 0:
-        _check(lora_act, "lora_act", torch.float16, (M, r), dev)
-        _check(lora_up, "lora_up", torch.float16, (N, r), dev)
+        _check(lora_act, "lora_act", h, (M, r), dev)
+        _check(lora_up, "lora_up", h, (N, r), dev)
     if bias is not None:
-        _check(bias, "bias", torch.float16, (N,), dev)
+        _check(bias, "bias", h, (N,), dev)
     if out is None:
-        out = torch.empty((M, N), dtype=torch.float16, device=dev)
-    _check(out, "out", torch.float16, (M, N), dev)
+        out = torch.empty((M, N), dtype=h, device=dev)
+    _check(out, "out", h, (M, N), dev)
     with torch.cuda.device(dev):
-        st = lib().svdq_gemm_nvfp4(M, N, K, r, _ptr(act_codes), _ptr(act_scales),
+        st = lib().svdq_gemm_nvfp4(io, M, N, K, r, _ptr(act_codes), _ptr(act_scales),
                                    _ptr(lora_act) if r > 0 else None, _ptr(w_codes), _ptr(w_scales),
                                    _ptr(lora_up) if r > 0 else None, _ptr(bias), ctypes.c_float(alpha), e,
                                    _ptr(out), _stream(dev))
@@ -310,23 +344,26 @@ def svdq_gemm_nvfp4(act_codes, act_scales, lora_act, w_codes, w_scales, lora_up,
 
 
 def awq_gemv_w4a16(x, w_codes, scales, zeros, group: int = 64, out=None, bias=None):
-    """AWQ W4A16 GEMV: y[m,n] = sum_k x[m,k] (q[n,k] - z) s + bias[n] -> fp16 [M][N]."""
+    """AWQ W4A16 GEMV: y[m,n] = sum_k x[m,k] (q[n,k] - z) s + bias[n] -> y [M][N];
+    x, bias and y share the layer's 16-bit type, scales and zeros are fp16."""
     dev = x.device
     if dev.type != "cuda":
         raise ValueError("x must be a HIP device tensor")
     M, K = x.shape
     N = w_codes.shape[0]
-    _check(x, "x", torch.float16, (M, K), dev)
+    io = _io(x, "x")
+    h = x.dtype
+    _check(x, "x", h, (M, K), dev)
     _check(w_codes, "w_codes", torch.uint8, (N, K // 2), dev)
     _check(scales, "scales", torch.float16, (N, K // group), dev)
     _check(zeros, "zeros", torch.float16, (N, K // group), dev)
     if bias is not None:
-        _check(bias, "bias", torch.float16, (N,), dev)
+        _check(bias, "bias", h, (N,), dev)
     if out is None:
-        out = torch.empty((M, N), dtype=torch.float16, device=dev)
-    _check(out, "out", torch.float16, (M, N), dev)
+        out = torch.empty((M, N), dtype=h, device=dev)
+    _check(out, "out", h, (M, N), dev)
     with torch.cuda.device(dev):
-        st = lib().awq_gemv_w4a16(M, N, K, group, _ptr(x), _ptr(w_codes), _ptr(scales),
+        st = lib().awq_gemv_w4a16(io, M, N, K, group, _ptr(x), _ptr(w_codes), _ptr(scales),
                                   _ptr(zeros), _ptr(bias), _ptr(out), _stream(dev))
     if st != SVDQ_OK:
         raise SvdqError(st, "awq_gemv_w4a16")

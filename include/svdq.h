@@ -76,6 +76,16 @@ typedef enum { SVDQ_INT4_G64 = 0, SVDQ_FP4_E2M1_B32 = 1, SVDQ_NVFP4_G16 = 2 } sv
  * model-specific fused paths). */
 typedef enum { SVDQ_EPI_NONE = 0, SVDQ_EPI_GELU_TANH = 1 } svdq_epilogue;
 
+/* The layer's 16-bit compute type (the quantization_config's compute_dtype,
+ * dothoosh.com article, quantization_config block; "bfloat16" in the pages'
+ * example). Below, "h16" is this type: it is the type of X, lora_down,
+ * lora_act, lora_up, bias, qk_norm_w and Y, and of the GEMV's x, bias and y.
+ * Conversions to h16 round to nearest, ties to even; the low-rank products
+ * run on the h16 matrix instructions with fp32 accumulation. Stored scales
+ * keep their format's own type whatever dtype is (INT4 and AWQ: fp16). A value
+ * outside this enum is SVDQ_ERR_INVALID_ARG. */
+typedef enum { SVDQ_F16 = 0, SVDQ_BF16 = 1 } svdq_dtype;
+
 /* Returns SVDQ_OK iff HIP device `hip_device` exists and is a gfx950 part.
  * This is the library's capability check: a clear error instead of wrong
  * output on hardware the kernels were not built for (dothoosh.com article,
@@ -93,7 +103,7 @@ int svdq_version(void);
  * and per-group 4-bit activation quantization (one pass over X).
  *
  *   x_hat[m,k]   = fl32(fp32(X[m,k]) * smooth_inv[k])          (IEEE multiply)
- *   lora_act[m,j]= fp16_rne(sum_k X[m,k] * lora_down[j,k])   (fp16 inputs, fp32 accumulate)
+ *   lora_act[m,j]= h16_rne(sum_k X[m,k] * lora_down[j,k])    (h16 inputs, fp32 accumulate)
  *   INT4_G64, per row m and group g of 64 along K:
  *     amax = max |x_hat|;  s = fp16_rne(min(fl32(amax / 7), 65504));
  *     q = s == 0 ? 0 : clamp(rint_even(fl32(x_hat / s)), -7, 7)   (IEEE division)
@@ -103,23 +113,24 @@ int svdq_version(void);
  *     code = E2M1 nearest to x_hat / 2^e (ties to even mantissa), sign bit
  *     from x_hat's sign.
  * Codes and scales are bit-exact functions of (X, smooth_inv); lora_act is a
- * float result (fp32 accumulation in unspecified order, stored as fp16 -- the
- * 16-bit low-rank branch -- which is what the GEMM's fp16 matrix product takes).
+ * float result (fp32 accumulation in unspecified order, stored as h16 -- the
+ * 16-bit low-rank branch -- which is what the GEMM's h16 matrix product takes).
  *
  * Arguments:
  *   fmt         svdq_format.
+ *   dtype       svdq_dtype.
  *   M           rows (tokens), M >= 0.
  *   K           input channels; K % 128 == 0, 128 <= K <= 65536.
  *   r           low-rank width; r % 16 == 0, 0 <= r <= 128.
- *   X           fp16 [M][K].
+ *   X           h16 [M][K].
  *   smooth_inv  fp32 [K], the smoothing multiplier (1/lambda).
- *   lora_down   fp16 [r][K] (carries diag(smooth_inv)); may be NULL iff r == 0.
+ *   lora_down   h16 [r][K] (carries diag(smooth_inv)); may be NULL iff r == 0.
  *   act_codes   out, u8 [M][K/2].
  *   act_scales  out, fp16 [M][K/64] (INT4_G64) or u8 [M][K/32] (FP4_E2M1_B32).
- *   lora_act    out, fp16 [M][r]; may be NULL iff r == 0.
+ *   lora_act    out, h16 [M][r]; may be NULL iff r == 0.
  *   stream      hipStream_t.
  */
-int svdq_quantize_act(int fmt, int M, int K, int r,
+int svdq_quantize_act(int fmt, int dtype, int M, int K, int r,
                       const void* X, const float* smooth_inv, const void* lora_down,
                       uint8_t* act_codes, void* act_scales, void* lora_act,
                       void* stream);
@@ -130,12 +141,12 @@ int svdq_quantize_act(int fmt, int M, int K, int r,
  *
  *   Y[m,n] = act( sum_j lora_act[m,j] lora_up[n,j]
  *               + sum_g s_x[m,g] s_w[n,g] sum_{k in g} q_x[m,k] q_w[n,k]
- *               + bias[n] )                                 -> fp16 (RNE)
+ *               + bias[n] )                                 -> h16 (RNE)
  *
  * INT4_G64 multiplies the codes exactly (int8 matrix cores, int32 per
  * group) and applies s_x s_w in fp32; FP4_E2M1_B32 uses the block-scaled
  * FP4 matrix instruction with the E8M0 scales applied in hardware and fp32
- * accumulation. lora_act is rounded to fp16 for the low-rank product
+ * accumulation. lora_act is the h16 value the quantizer stored, for the low-rank product
  * (fp32 accumulation).
  *
  * Arguments:
@@ -146,16 +157,16 @@ int svdq_quantize_act(int fmt, int M, int K, int r,
  *   r           low-rank width; r % 16 == 0, 0 <= r <= 128.
  *   act_codes   u8 [M][K/2] (from svdq_quantize_act).
  *   act_scales  fp16 [M][K/64] or u8 [M][K/32].
- *   lora_act    fp16 [M][r]; may be NULL iff r == 0.
+ *   lora_act    h16 [M][r]; may be NULL iff r == 0.
  *   w_codes     u8 [N][K/2].
  *   w_scales    fp16 [N][K/64] or u8 [N][K/32].
- *   lora_up     fp16 [N][r]; may be NULL iff r == 0.
- *   bias        fp16 [N], or NULL for no bias.
+ *   lora_up     h16 [N][r]; may be NULL iff r == 0.
+ *   bias        h16 [N], or NULL for no bias.
  *   epi         svdq_epilogue.
- *   Y           out, fp16 [M][N].
+ *   Y           out, h16 [M][N].
  *   stream      hipStream_t.
  */
-int svdq_gemm_w4a4(int fmt, int M, int N, int K, int r,
+int svdq_gemm_w4a4(int fmt, int dtype, int M, int N, int K, int r,
                    const uint8_t* act_codes, const void* act_scales, const void* lora_act,
                    const uint8_t* w_codes, const void* w_scales, const void* lora_up,
                    const void* bias, int epi, void* Y, void* stream);
@@ -173,19 +184,19 @@ int svdq_gemm_w4a4(int fmt, int M, int N, int K, int r,
  *   Q, K      (per head):    u[d] = lin[d] / sqrt(mean_d lin^2 + eps) * w[d]
  *                            Y[2i]   = u[2i] cos[m,i] - u[2i+1] sin[m,i]
  *                            Y[2i+1] = u[2i] sin[m,i] + u[2i+1] cos[m,i]
- *                                                         -> fp16 (RNE)
+ *                                                         -> h16 (RNE)
  *
  * Float results (fp32 arithmetic, hardware rsqrt); INT4_G64 only.
  *
  * Arguments as svdq_gemm_w4a4 (fmt must be SVDQ_INT4_G64, no activation), and
  *   N           output channels; N % 384 == 0 (Q, K, V thirds of 128-channel heads).
- *   qk_norm_w   fp16 [2][128]: the RMSNorm weights of Q, then of K.
+ *   qk_norm_w   h16 [2][128]: the RMSNorm weights of Q, then of K.
  *   rope        fp32 [M][64][2]: (cos, sin) of token m for channel pair i.
  *   eps         RMSNorm epsilon, 0 <= eps <= 1.
  * Errors: SVDQ_ERR_INVALID_ARG for another format, a bad eps or a NULL
  * qk_norm_w / rope; otherwise as svdq_gemm_w4a4.
  */
-int svdq_gemm_w4a4_qkv(int fmt, int M, int N, int K, int r,
+int svdq_gemm_w4a4_qkv(int fmt, int dtype, int M, int N, int K, int r,
                        const uint8_t* act_codes, const void* act_scales, const void* lora_act,
                        const uint8_t* w_codes, const void* w_scales, const void* lora_up,
                        const void* bias, const void* qk_norm_w, const float* rope, float eps,
@@ -211,7 +222,7 @@ int svdq_gemm_w4a4_qkv(int fmt, int M, int N, int K, int r,
  *   act_gscale  g, finite and > 0 (else SVDQ_ERR_INVALID_ARG).
  *   act_scales  out, u8 [M][K/16] E4M3 bytes (sign bit 0).
  */
-int svdq_quantize_act_nvfp4(int M, int K, int r,
+int svdq_quantize_act_nvfp4(int dtype, int M, int K, int r,
                             const void* X, const float* smooth_inv, const void* lora_down,
                             float act_gscale, uint8_t* act_codes, uint8_t* act_scales,
                             void* lora_act, void* stream);
@@ -221,7 +232,7 @@ int svdq_quantize_act_nvfp4(int M, int K, int r,
  *
  *   Y[m,n] = act( alpha * sum_k (E2M1(q_x[m,k]) E4M3(s_x[m,k/16]))
  *                               (E2M1(q_w[n,k]) E4M3(s_w[n,k/16]))
- *               + sum_j lora_act[m,j] lora_up[n,j] + bias[n] )     -> fp16 (RNE)
+ *               + sum_j lora_act[m,j] lora_up[n,j] + bias[n] )     -> h16 (RNE)
  *
  * with alpha = act_gscale * w_gscale (the two per-tensor scales; the caller
  * forms the product). gfx950 has no matrix instruction for E4M3 scales per
@@ -234,7 +245,7 @@ int svdq_quantize_act_nvfp4(int M, int K, int r,
  *               is ignored (scales are magnitudes).
  *   alpha       finite (else SVDQ_ERR_INVALID_ARG).
  */
-int svdq_gemm_nvfp4(int M, int N, int K, int r,
+int svdq_gemm_nvfp4(int dtype, int M, int N, int K, int r,
                     const uint8_t* act_codes, const uint8_t* act_scales, const void* lora_act,
                     const uint8_t* w_codes, const uint8_t* w_scales, const void* lora_up,
                     const void* bias, float alpha, int epilogue, void* Y, void* stream);
@@ -244,10 +255,10 @@ int svdq_gemm_nvfp4(int M, int N, int K, int r,
  * the modulation / adaptive-norm projections (dothoosh.com article,
  * kernel-family list: awq_w4a16; quantization_config block: int4, group 64):
  *
- *   y[m,n] = sum_k x[m,k] * (q[n,k] - z[n,k/G]) * s[n,k/G] + bias[n]   -> fp16 (RNE)
+ *   y[m,n] = sum_k x[m,k] * (q[n,k] - z[n,k/G]) * s[n,k/G] + bias[n]   -> h16 (RNE)
  *
  * with fp32 accumulation; the bias is added to the fp32 total before the one
- * rounding to fp16.
+ * rounding to h16.
  *
  * Arguments:
  *   M       rows of x, 0 <= M <= 8.
@@ -255,15 +266,16 @@ int svdq_gemm_nvfp4(int M, int N, int K, int r,
  *   K       input channels; K % 64 == 0, K >= 64, M * K <= 32768 (x is staged
  *           in LDS).
  *   group   group size along K; must be 64.
- *   x       fp16 [M][K].
+ *   dtype   svdq_dtype (x, bias and y).
+ *   x       h16 [M][K].
  *   w_codes u8 [N][K/2], unsigned nibbles, even k in the low nibble.
  *   scales  fp16 [N][K/64].
  *   zeros   fp16 [N][K/64], in code units (any fp16 value).
- *   bias    fp16 [N], or NULL for none.
- *   y       out, fp16 [M][N].
+ *   bias    h16 [N], or NULL for none.
+ *   y       out, h16 [M][N].
  *   stream  hipStream_t.
  */
-int awq_gemv_w4a16(int M, int N, int K, int group,
+int awq_gemv_w4a16(int dtype, int M, int N, int K, int group,
                    const void* x, const uint8_t* w_codes, const void* scales,
                    const void* zeros, const void* bias, void* y, void* stream);
 

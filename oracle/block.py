@@ -29,9 +29,10 @@ Each linear is an entry of `params`:
   {"kind": "svdq_qkv", "layer": ..., "b": ..., "qk_norm_w": fp16 [2][128], "eps": float}
   {"kind": "awq", "awq": awq_prep(...), "b": fp16 [N] | None}
 plus "self_attention.norm_q" / "self_attention.norm_k" weight arrays when Q,
-K and V are separate. A 4-bit layer takes its input rounded to fp16 and
-returns its output rounded to fp16 (the storage types of the layers); the
-rest is float64.
+K and V are separate. A 4-bit entry may carry "dtype": "bfloat16" (default
+"float16"): the layer's 16-bit type. A 4-bit layer takes its input rounded to
+that type and returns its output rounded to it (the storage types of the
+layers); the rest is float64.
 """
 from __future__ import annotations
 
@@ -39,13 +40,17 @@ import numpy as np
 
 from .awq import gemv_ref
 from .qkv import qkv_epilogue_ref, rms_norm_heads, rope_pairs
-from .svdq import forward_ref, gelu_tanh, quantize_act_ref
+from .svdq import bf16_round, forward_ref, gelu_tanh, quantize_act_ref
 
 HEAD_DIM = 128
 
 
-def _f16(a) -> np.ndarray:
-    return np.asarray(a, dtype=np.float64).astype(np.float16)
+def _r16(a, dtype: str = "float16") -> np.ndarray:
+    """Round to the layer's 16-bit type: fp16 array, or float32 holding bf16 values."""
+    a = np.asarray(a, dtype=np.float64)
+    if dtype == "bfloat16":
+        return bf16_round(a.astype(np.float32))
+    return a.astype(np.float16)
 
 
 def layer_norm(x: np.ndarray, eps: float = 1e-6) -> np.ndarray:
@@ -80,18 +85,19 @@ def linear(x: np.ndarray, e: dict, rope=None) -> np.ndarray:
     if kind == "dense":
         y = np.asarray(x, dtype=np.float64) @ np.asarray(e["W"], dtype=np.float64).T
         return y if e.get("b") is None else y + np.asarray(e["b"], dtype=np.float64)
-    X16 = _f16(x)
+    dt = e.get("dtype", "float16")
+    X16 = _r16(x, dt)
     if kind == "awq":
         a = e["awq"]
-        return _f16(gemv_ref(X16, a["codes"], a["scales"], a["zeros"], a["group"], bias=e.get("b")))
+        return _r16(gemv_ref(X16, a["codes"], a["scales"], a["zeros"], a["group"], bias=e.get("b")), dt)
     layer = e["layer"]
-    codes, _, scales = quantize_act_ref(X16, layer["smooth_inv"], layer["fmt"])
+    codes, _, scales = quantize_act_ref(X16, layer["smooth_inv"], layer["fmt"], layer.get("act_gscale"))
     if kind == "svdq":
-        return _f16(forward_ref(X16, layer, codes, scales, e.get("b"), e.get("epilogue", "none")))
+        return _r16(forward_ref(X16, layer, codes, scales, e.get("b"), e.get("epilogue", "none")), dt)
     if kind == "svdq_qkv":
         y = forward_ref(X16, layer, codes, scales, e.get("b"))
         w = np.asarray(e["qk_norm_w"])
-        return _f16(qkv_epilogue_ref(y, HEAD_DIM, w[0], w[1], rope[..., 0], rope[..., 1], e["eps"]))
+        return _r16(qkv_epilogue_ref(y, HEAD_DIM, w[0], w[1], rope[..., 0], rope[..., 1], e["eps"]), dt)
     raise ValueError(kind)
 
 
@@ -120,7 +126,8 @@ def dit_block_ref(x, c, rope, params: dict, eps: float = 1e-6, capture: dict | N
         if outputs is not None and name in outputs:
             y = np.array(outputs[name], dtype=np.float64).reshape(rows.shape[0], -1)
         else:
-            y = linear(rows, params[name], **kw)
+            # the layer's 16-bit values, carried on in float64 like the rest of the block
+            y = np.asarray(linear(rows, params[name], **kw), dtype=np.float64)
         if capture is not None:
             capture[name] = (np.array(rows, dtype=np.float64), y)
         return y

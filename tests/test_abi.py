@@ -42,19 +42,26 @@ def test_status_strings_and_version():
     for st in (0, -1, -2, -3, -4, -5):
         assert P.svdq_status_str(st)
     assert "unknown" in P.svdq_status_str(17)
-    assert P.svdq_version() == 100
+    assert P.svdq_version() == 200
 
 
-def q(fmt=0, M=4, K=128, r=16, X=A, si=A, ld=A, codes=A, scales=A, la=A):
-    return P.lib().svdq_quantize_act(fmt, M, K, r, X, si, ld, codes, scales, la, None)
+def q(fmt=0, M=4, K=128, r=16, X=A, si=A, ld=A, codes=A, scales=A, la=A, dt=0):
+    return P.lib().svdq_quantize_act(fmt, dt, M, K, r, X, si, ld, codes, scales, la, None)
 
 
-def g(fmt=0, M=4, N=128, K=128, r=16, ac=A, sa=A, la=A, wc=A, ws=A, lu=A, b=None, epi=0, Y=A):
-    return P.lib().svdq_gemm_w4a4(fmt, M, N, K, r, ac, sa, la, wc, ws, lu, b, epi, Y, None)
+def g(fmt=0, M=4, N=128, K=128, r=16, ac=A, sa=A, la=A, wc=A, ws=A, lu=A, b=None, epi=0, Y=A, dt=0):
+    return P.lib().svdq_gemm_w4a4(fmt, dt, M, N, K, r, ac, sa, la, wc, ws, lu, b, epi, Y, None)
 
 
-def v(M=1, N=64, K=128, G=64, x=A, c=A, s=A, z=A, b=None, y=A):
-    return P.lib().awq_gemv_w4a16(M, N, K, G, x, c, s, z, b, y, None)
+def v(M=1, N=64, K=128, G=64, x=A, c=A, s=A, z=A, b=None, y=A, dt=0):
+    return P.lib().awq_gemv_w4a16(dt, M, N, K, G, x, c, s, z, b, y, None)
+
+
+def test_dtype_argument():
+    for f in (q, g, v, qn, gn):
+        assert f(dt=2) == ops.SVDQ_ERR_INVALID_ARG
+        assert f(dt=-1) == ops.SVDQ_ERR_INVALID_ARG
+        assert f(dt=1) == ops.SVDQ_ERR_UNSUPPORTED_DEVICE   # bf16 is accepted
 
 
 def test_quantize_act_argument_errors():
@@ -105,12 +112,13 @@ def test_gemv_argument_errors():
     assert v(b=A) == ops.SVDQ_ERR_UNSUPPORTED_DEVICE
 
 
-def qn(M=4, K=256, r=16, X=A, si=A, ld=A, g=0.5, codes=A, scales=A, la=A):
-    return P.lib().svdq_quantize_act_nvfp4(M, K, r, X, si, ld, ctypes.c_float(g), codes, scales, la, None)
+def qn(M=4, K=256, r=16, X=A, si=A, ld=A, g=0.5, codes=A, scales=A, la=A, dt=0):
+    return P.lib().svdq_quantize_act_nvfp4(dt, M, K, r, X, si, ld, ctypes.c_float(g), codes, scales, la, None)
 
 
-def gn(M=4, N=128, K=256, r=16, ac=A, sa=A, la=A, wc=A, ws=A, lu=A, b=None, alpha=1.0, epi=0, Y=A):
-    return P.lib().svdq_gemm_nvfp4(M, N, K, r, ac, sa, la, wc, ws, lu, b, ctypes.c_float(alpha), epi, Y, None)
+def gn(M=4, N=128, K=256, r=16, ac=A, sa=A, la=A, wc=A, ws=A, lu=A, b=None, alpha=1.0, epi=0, Y=A, dt=0):
+    return P.lib().svdq_gemm_nvfp4(dt, M, N, K, r, ac, sa, la, wc, ws, lu, b, ctypes.c_float(alpha), epi, Y,
+                                   None)
 
 
 def test_nvfp4_argument_errors():

@@ -8,8 +8,9 @@ layer on the module's own fp16 input). The block, in three parts:
   - the composition: the oracle block's float64 arithmetic around the layers
     (modulation, LayerNorm, Q/K norm and rotation when unfused, attention,
     residuals), run on the GPU's own layer outputs, must give every layer
-    input and the block output within GLUE_TOL (fp16 storage of the GPU's
-    values, relative L2 about 1.4e-4, plus its fp32 arithmetic);
+    input (rounded to the layer's 16-bit type on both sides) and the block
+    output within GLUE_TOL (the GPU's fp32 arithmetic and the rare last-bit
+    rounding differences it causes);
   - free running, GPU block against oracle block from the same x, c, rope:
     4-bit activation quantization is not continuous at fp16 resolution (a
     last-bit change of a layer input moves a code by a whole step), so the
@@ -85,13 +86,13 @@ def test_awq_linear_module(M):
     assert rel_l2(host(y), ref) <= Y_TOL
 
 
-def _run_block(fmt, fuse, D=1024, C=768, B=2, T=200, rank=32):
+def _run_block(fmt, fuse, D=1024, C=768, B=2, T=200, rank=32, dtype="float16"):
     w = synth.dit_block_params(D, C, seed=11)
     cal = synth.dit_block_inputs(2, 256, D, C, seed=12)
     inp = synth.dit_block_inputs(B, T, D, C, seed=13)
-    P, sd = quantized_params(w, cal, fmt=fmt, rank=rank, fuse_qkv=fuse)
+    P, sd = quantized_params(w, cal, fmt=fmt, rank=rank, fuse_qkv=fuse, dtype=dtype)
     blk = DiTBlock(D, C)
-    quantize_model(blk, quant_config(fmt, rank), device=DEV)
+    quantize_model(blk, quant_config(fmt, rank, dtype), device=DEV)
     if fuse:
         assert fuse_qkv_norm_rope(blk) == ["self_attention"]
     blk.load_state_dict(to_torch(sd, DEV), strict=True)
@@ -101,7 +102,8 @@ def _run_block(fmt, fuse, D=1024, C=768, B=2, T=200, rank=32):
     def hook(name):
         def f(mod, args, out):
             y = torch.cat(out, -1) if isinstance(out, tuple) else out
-            seen[name] = (host(args[0]).reshape(-1, args[0].shape[-1]), host(y).reshape(-1, y.shape[-1]))
+            seen[name] = (host(args[0].float()).reshape(-1, args[0].shape[-1]),
+                          host(y.float()).reshape(-1, y.shape[-1]))
         return f
     for name, mod in blk.named_modules():
         if isinstance(mod, (SVDQLinear, AWQLinear)):
@@ -112,9 +114,11 @@ def _run_block(fmt, fuse, D=1024, C=768, B=2, T=200, rank=32):
     return w, inp, P, seen, host(out)
 
 
-@pytest.mark.parametrize("fmt,fuse", [("int4_g64", True), ("fp4_b32", False)])
-def test_dit_block_end_to_end(fmt, fuse, monkeypatch):
-    w, inp, P, seen, out = _run_block(fmt, fuse)
+@pytest.mark.parametrize("fmt,fuse,dtype", [("int4_g64", True, "float16"), ("fp4_b32", False, "float16"),
+                                            ("nvfp4_g16", False, "bfloat16"),     # the pages' own config
+                                            ("int4_g64", True, "bfloat16")])
+def test_dit_block_end_to_end(fmt, fuse, dtype, monkeypatch):
+    w, inp, P, seen, out = _run_block(fmt, fuse, dtype=dtype)
     expect = {"adaLN_modulation.1", "self_attention.to_out", "mlp.0", "mlp.2"} | (
         {"self_attention.to_qkv"} if fuse else {f"self_attention.to_{p}" for p in "qkv"})
     assert set(seen) == expect
@@ -130,11 +134,12 @@ def test_dit_block_end_to_end(fmt, fuse, monkeypatch):
     forced = oracle.dit_block_ref(inp["x"], inp["c"], inp["rope"], P, capture=fcap,
                                   outputs={n: y for n, (_, y) in seen.items()})
     for name, (xin, _) in seen.items():
-        err = rel_l2(xin, fcap[name][0])
+        # the GPU stored the input in the layer's 16-bit type: round the oracle's alike
+        err = rel_l2(xin, oracle.block._r16(fcap[name][0], P[name].get("dtype", "float16")))
         print(f"{fmt} input of {name}: rel_l2 vs oracle glue {err:.2e}")
         assert err <= GLUE_TOL, name
     err = rel_l2(out, forced)
-    print(f"{fmt} block output, teacher-forced: rel_l2 {err:.2e}")
+    print(f"{fmt} {dtype} block output, teacher-forced: rel_l2 {err:.2e}")
     assert np.isfinite(out).all() and err <= GLUE_TOL
 
     # free running, against the oracle's own sensitivity
@@ -143,14 +148,19 @@ def test_dit_block_end_to_end(fmt, fuse, monkeypatch):
     err = rel_l2(out - x64, ref - x64)
     rng = np.random.default_rng(17)
 
+    # up to one ulp of the layer's 16-bit type (2^-10 fp16, 2^-7 bf16, relative),
+    # then its rounding: last-bit changes in a share of the outputs comparable
+    # to the GPU's (whose per-layer difference is about a quarter ulp RMS)
     def noisy(xr, e, rope=None):
-        y = oracle_linear(xr, e, rope)
-        return (y * (1 + 1e-5 * rng.standard_normal(y.shape))).astype(np.float16).astype(np.float64)
+        dt = e.get("dtype", "float16")
+        y = oracle_linear(xr, e, rope).astype(np.float64)
+        eps = 2.0 ** -10 if dt == "float16" else 2.0 ** -7
+        return oracle.block._r16(y * (1 + eps * rng.uniform(-1, 1, y.shape)), dt)
     monkeypatch.setattr(oracle.block, "linear", noisy)
     floor = rel_l2(oracle.dit_block_ref(inp["x"], inp["c"], inp["rope"], P) - x64, ref - x64)
     monkeypatch.undo()
     dense = oracle.dit_block_ref(inp["x"], inp["c"], inp["rope"], dense_params(w))
     qerr = rel_l2(ref - x64, dense - x64)
-    print(f"{fmt} block increment: GPU vs oracle {err:.2e}, oracle vs itself under 1e-5 noise "
+    print(f"{fmt} {dtype} block increment: GPU vs oracle {err:.2e}, oracle vs itself under 1-ulp noise "
           f"{floor:.2e}, 4-bit vs dense {qerr:.2e} (T={T})")
     assert err <= 2 * floor + 1e-3

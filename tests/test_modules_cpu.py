@@ -25,11 +25,23 @@ PAGES_EXAMPLE = {
 }
 
 
-def test_pages_example_compute_dtype_is_rejected_with_a_reason():
-    with pytest.raises(UnsupportedQuantConfig, match="bfloat16"):
-        parse_quantization_config({"quantization_config": PAGES_EXAMPLE})
-    q = parse_quantization_config(dict(PAGES_EXAMPLE, compute_dtype="float16"))
+def test_pages_example_parses():
+    q = parse_quantization_config({"quantization_config": PAGES_EXAMPLE})
+    assert q.compute_dtype == "bfloat16"
     assert q.svdq.fmt == "nvfp4_g16" and q.svdq.rank == 32
+    q = parse_quantization_config(dict(PAGES_EXAMPLE, compute_dtype="float16"))
+    assert q.compute_dtype == "float16"
+
+
+def test_bf16_patching_makes_bf16_buffers():
+    blk = DiTBlock(256)
+    cfg = dict(PAGES_EXAMPLE, svdq_w4a4=dict(PAGES_EXAMPLE["svdq_w4a4"], targets=["self_attention.*", "mlp.*"]))
+    quantize_model(blk, cfg)
+    m = blk.self_attention.to_q
+    assert m.fmt == "nvfp4_g16" and m.io_dtype == torch.bfloat16
+    assert m.lora_down.dtype == torch.bfloat16 and m.bias.dtype == torch.bfloat16
+    assert blk.adaLN_modulation[1].bias.dtype == torch.bfloat16
+    assert fuse_qkv_norm_rope(blk) == []      # the fused QKV epilogue is INT4 only
 
 
 @pytest.mark.parametrize("prec,gs,fmt", [("int4", 64, "int4_g64"), ("mxfp4", 32, "fp4_b32"),
@@ -52,6 +64,7 @@ def test_config_errors_and_wildcards():
     q = parse_quantization_config(base)
     assert q.method_for("layers.17.mlp.0") == "svdq" and q.awq is None
     for bad, exc in [({"quant_method": "gptq"}, ValueError),
+                     ({"compute_dtype": "float32"}, ValueError),
                      ({"compute_dtype": "float8"}, ValueError),
                      ({"svdq_w4a4": {"precision": "int4", "group_size": 128, "rank": 32}}, UnsupportedQuantConfig),
                      ({"svdq_w4a4": {"precision": "nvfp4", "group_size": 32, "rank": 32}}, UnsupportedQuantConfig),
