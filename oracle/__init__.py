@@ -52,3 +52,4 @@ from .svdq import (  # noqa: F401
 from .awq import awq_prep, awq_dequantize, gemv_ref  # noqa: F401
 from .qkv import rms_norm_heads, rope_pairs, qkv_epilogue_ref  # noqa: F401
 from .block import layer_norm, silu, attention, dit_block_ref  # noqa: F401
+from .mlp import mlp_chain_ref  # noqa: F401

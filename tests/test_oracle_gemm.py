@@ -170,3 +170,22 @@ def test_awq_prep_error_bound():
     assert (err <= s * 1.0 + 1e-12).all()
     assert (err <= s / 2 * (1 + 1e-3)).mean() > 0.99
     assert set(np.unique(p["zeros"]).tolist()) <= set(range(16))
+
+
+def test_mlp_chain_is_the_composition_and_pins_hold():
+    """The chain adds no arithmetic of its own: with all-zero up-projection codes
+    and rank 0 the up-projection is the bias, so U = GELU(bias) in every row, and
+    the chain's quantizer sees exactly that (closed form through the pinned GELU
+    and quantizer)."""
+    M, K, N = 3, 128, 128
+    b = (np.arange(N) / 16.0 - 4.0).astype(np.float16)
+    z = np.zeros((M, K), np.int64)
+    s1 = np.ones((M, K // 64), np.float16)
+    U16, codes, packed, scales, la2 = oracle.mlp_chain_ref(
+        z, s1, np.zeros((M, 0)), np.zeros((N, K), np.int64), np.ones((N, K // 64), np.float16),
+        np.zeros((N, 0)), b, "int4_g64", np.ones(N, np.float32), np.zeros((0, N), np.float16))
+    want = oracle.gelu_tanh(b.astype(np.float64)).astype(np.float16)
+    assert np.array_equal(U16, np.broadcast_to(want, (M, N)))
+    c2, _, s2 = oracle.quantize_act_ref(np.broadcast_to(want, (M, N)), np.ones(N, np.float32), "int4_g64")
+    assert np.array_equal(codes, c2) and np.array_equal(scales.view(np.uint16), s2.view(np.uint16))
+    assert la2.shape == (M, 0)
