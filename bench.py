@@ -55,7 +55,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="qkv",
                     choices=["qkv", "qkv_normrope", "mlp_up", "mlp_up_nvfp4", "mlp_down",
-                             "mlp_down_m1024", "attn_out", "mlp_up_int4", "block"])
+                             "mlp_down_m1024", "attn_out", "mlp_up_int4", "block", "mlp_pair",
+                             "mlp_chain"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--warm", action="store_true", help="no buffer rotation (cache-warm)")
     ap.add_argument("--rank", type=int, default=None, help="override the low-rank width")
@@ -121,7 +122,13 @@ def main():
         print("cuda:0 is not a gfx950 (MI355X) device", file=sys.stderr)
         sys.exit(3)
 
-    names = list(synth.BLOCK_STREAM) if args.workload == "block" else [args.workload]
+    chain = args.workload == "mlp_chain"
+    if args.workload == "block":
+        names = list(synth.BLOCK_STREAM)
+    elif args.workload in ("mlp_pair", "mlp_chain"):
+        names = ["mlp_up_int4", "mlp_down"]      # the DiT MLP: INT4 up-projection + GELU, INT4 down
+    else:
+        names = [args.workload]
     cfgs = [synth.CONFIGS[n] for n in names]
     gcfg = synth.CONFIGS["gemv"]
 
@@ -165,16 +172,42 @@ def main():
                 e = synth.qkv_epilogue_inputs(cfg.M, seed=0)
                 L["qk_norm_w"], L["rope"], L["eps"] = t(e["qk_norm_w"]), t(e["rope"]), e["eps"]
             layers.append(L)
+        if chain:
+            # the fused chain writes the down-projection's codes, scales and lora_act
+            # directly; its fp32 partials live in a caller-owned workspace
+            Lu, Ld = layers
+            wsb = P.lib().svdq_gemm_w4a4_mlp_workspace(Lu["cfg"].M, Lu["cfg"].N, Ld["r"])
+            Lu["workspace"] = torch.empty(max(1, wsb // 4), dtype=torch.float32, device=dev)
         G = {"x": t(gp["x"]), "codes": t(gp["codes"]), "scales": t(gp["scales"]),
              "zeros": t(gp["zeros"]), "y": torch.empty((1, gcfg.N), dtype=torch.float16, device=dev)}
         sets.append((layers, G))
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)
-    nk = sum(2 for _ in cfgs) + 1   # launches per step
+    nk = 4 if chain else sum(2 for _ in cfgs) + 1   # timed calls per step
+
+    def step_chain(layers, G, events):
+        Lu, Ld = layers
+        ev = (lambda k: events[k].record(stream)) if events is not None else (lambda k: None)
+        ev(0)
+        P.svdq_quantize_act(Lu["X"], Lu["smooth_inv"], Lu["lora_down"], "int4_g64",
+                            Lu["codes"], Lu["scales"], Lu["lora_act"])
+        ev(1)
+        P.svdq_gemm_w4a4_mlp(Lu["codes"], Lu["scales"], Lu["lora_act"], Lu["w_codes"], Lu["w_scales"],
+                             Lu["lora_up"], Lu["bias"], Ld["smooth_inv"], Ld["lora_down"], "int4_g64",
+                             Ld["codes"], Ld["scales"], Ld["lora_act"], Lu["workspace"])
+        ev(2)
+        P.svdq_gemm_w4a4(Ld["codes"], Ld["scales"], Ld["lora_act"], Ld["w_codes"], Ld["w_scales"],
+                         Ld["lora_up"], Ld["bias"], "int4_g64", "none", out=Ld["Y"])
+        ev(3)
+        P.awq_gemv_w4a16(G["x"], G["codes"], G["scales"], G["zeros"], out=G["y"])
+        ev(4)
 
     def step(i, events=None):
         layers, G = sets[i % nsets]
+        if chain:
+            step_chain(layers, G, events)
+            return
         j = 0
         for L in layers:
             cfg = L["cfg"]
@@ -252,7 +285,25 @@ def main():
     kernels = {}
     gemm_ms_sum = 0.0
     dominant = None
-    for li, (cfg, r, _) in enumerate(host_sets):
+    if chain:
+        (cu, ru, _), (cd, rd, _) = host_sets
+        qb, _ = layer_bytes(cu, ru)
+        kernels[f"{cu.name}.svdq_quantize_act"] = {
+            "avg_us": round(mean_ms[0] * 1e3, 2), "median_us": round(med_ms[0] * 1e3, 2),
+            "alg_bytes": qb, "GB/s": round(qb / (mean_ms[0] * 1e-3) / 1e9, 1)}
+        for k, (cfg, r, name) in ((1, (cu, ru, "svdq_gemm_w4a4_mlp")), (2, (cd, rd, "svdq_gemm_w4a4"))):
+            ops = 2.0 * cfg.M * cfg.N * cfg.K
+            tops = ops / (mean_ms[k] * 1e-3) / 1e12
+            kernels[f"{cfg.name}.{name}"] = {
+                "avg_us": round(mean_ms[k] * 1e3, 2), "median_us": round(med_ms[k] * 1e3, 2),
+                "alg_ops": ops, "TOPS": round(tops, 1), "frac_peak": round(tops / PEAK_TOPS[cfg.fmt], 4),
+                "format": cfg.fmt, "rank": r,
+                "note": "GEMM + GELU + the next layer's quantizer, then the fixed-order sum of the "
+                        "low-rank partials (two launches)" if k == 1 else "reads the chain's codes"}
+            gemm_ms_sum += mean_ms[k]
+            if dominant is None or mean_ms[k] > dominant[1]:
+                dominant = (cfg, mean_ms[k], ops, r)
+    for li, (cfg, r, _) in enumerate([] if chain else host_sets):
         qb, gb = layer_bytes(cfg, r)
         qms, gms = mean_ms[2 * li], mean_ms[2 * li + 1]
         gemm_ms_sum += gms
@@ -292,6 +343,10 @@ def main():
 
     wl = ("DiT block linear stream (QKV, out-proj, MLP-up GELU, MLP-down; all W4A4 INT4 g64 r32)"
           if args.workload == "block" else
+          "DiT MLP (M4096: up K3072 N12288 + GELU, down K12288 N3072; INT4 g64 r32)"
+          + (", fused chain: the up-projection's epilogue quantizes for the down-projection"
+             if chain else ", unfused")
+          if args.workload in ("mlp_pair", "mlp_chain") else
           f"SVDQ W4A4 {cfgs[0].name} M={cfgs[0].M} K={cfgs[0].K} N={cfgs[0].N} r={host_sets[0][1]} "
           f"{cfgs[0].fmt} epilogue={cfgs[0].epilogue}")
     wl += f" + AWQ W4A16 modulation GEMV M=1 K={gcfg.K} N={gcfg.N} g{gcfg.group}"

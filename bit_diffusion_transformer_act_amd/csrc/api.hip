@@ -152,6 +152,48 @@ int svdq_gemm_w4a4_qkv(int fmt, int dtype, int M, int N, int K, int r, const uin
                                        w_scales, lora_up, bias, 2, Y, (hipStream_t)stream, &qe));
 }
 
+size_t svdq_gemm_w4a4_mlp_workspace(int M, int N, int r2) {
+  if (M < 0 || N < 0 || r2 < 0) return 0;
+  return (size_t)(N / 128) * (size_t)M * (size_t)r2 * sizeof(float);
+}
+
+int svdq_gemm_w4a4_mlp(int fmt, int dtype, int M, int N, int K, int r, const uint8_t* act_codes,
+                       const void* act_scales, const void* lora_act, const uint8_t* w_codes,
+                       const void* w_scales, const void* lora_up, const void* bias,
+                       const float* smooth_inv2, const void* lora_down2, int r2, uint8_t* act_codes2,
+                       void* act_scales2, void* lora_act2, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  if (fmt != SVDQ_INT4_G64) return SVDQ_ERR_INVALID_ARG;
+  if (!dtype_ok(dtype)) return SVDQ_ERR_INVALID_ARG;
+  if (M < 0 || M > (1 << 23) || N < 128 || N > 65536 || (N % 128) != 0 || !k_ok(K) || !rank_ok(r) ||
+      !rank_ok(r2))
+    return SVDQ_ERR_SHAPE;
+  if (M == 0) return SVDQ_OK;
+  if (!act_codes || !act_scales || !w_codes || !w_scales || !smooth_inv2 || !act_codes2 || !act_scales2)
+    return SVDQ_ERR_INVALID_ARG;
+  if (r > 0 && (!lora_act || !lora_up)) return SVDQ_ERR_INVALID_ARG;
+  if (r2 > 0 && (!lora_down2 || !lora_act2 || !workspace)) return SVDQ_ERR_INVALID_ARG;
+  if (r2 > 0 && workspace_bytes < svdq_gemm_w4a4_mlp_workspace(M, N, r2)) return SVDQ_ERR_SHAPE;
+  if (!aligned16(act_codes) || !aligned16(act_scales) || !aligned16(w_codes) || !aligned16(w_scales) ||
+      (bias && !aligned16(bias)) || !aligned16(smooth_inv2) || !aligned16(act_codes2) ||
+      !aligned16(act_scales2))
+    return SVDQ_ERR_ALIGN;
+  if (r > 0 && (!aligned16(lora_act) || !aligned16(lora_up))) return SVDQ_ERR_ALIGN;
+  if (r2 > 0 && (!aligned16(lora_down2) || !aligned16(lora_act2) || !aligned16(workspace)))
+    return SVDQ_ERR_ALIGN;
+  const int dc = check_current_device();
+  if (dc != SVDQ_OK) return dc;
+  (void)hipGetLastError();
+  const svdq::ChainEpilogue ce{smooth_inv2, lora_down2, r2, act_codes2, act_scales2,
+                               static_cast<float*>(workspace)};
+  hipError_t e = svdq::launch_gemm_w4a4(fmt, dtype, M, N, K, r, act_codes, act_scales, lora_act, w_codes,
+                                        w_scales, lora_up, bias, 3, nullptr, (hipStream_t)stream, nullptr, &ce);
+  if (e == hipSuccess && r2 > 0)
+    e = svdq::launch_chain_reduce(dtype, M, r2, N / 128, static_cast<const float*>(workspace), lora_act2,
+                                  (hipStream_t)stream);
+  return finish(e);
+}
+
 int svdq_quantize_act_nvfp4(int dtype, int M, int K, int r, const void* X, const float* smooth_inv,
                             const void* lora_down, float act_gscale, uint8_t* act_codes,
                             uint8_t* act_scales, void* lora_act, void* stream) {

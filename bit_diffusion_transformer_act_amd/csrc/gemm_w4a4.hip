@@ -41,6 +41,7 @@
 // v_mfma_scale_f32_32x32x64_f8f6f4 as they are (lane l: row l%32, k
 // 32 (l/32) .. +32), with the E8M0 byte of (row, 32-block) as the lane's
 // scale; the hardware applies both scales and accumulates in fp32.
+#include <algorithm>
 #include <atomic>
 
 #include "common.hpp"
@@ -83,7 +84,7 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restr
                       const uint16_t* __restrict__ lora_act, const uint8_t* __restrict__ w_codes,
                       const void* __restrict__ w_scales, const uint16_t* __restrict__ lora_up,
                       const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y,
-                      int M, int N, int K, int r, QkvEpilogue qe) {
+                      int M, int N, int K, int r, QkvEpilogue qe, ChainEpilogue ce) {
   using S = GemmShape<WM, WN, STAGES>;
   constexpr int BM = S::BM, BN = S::BN;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -356,6 +357,7 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restr
   static_assert(BM * TP * 2 <= S::LDS, "staging tile must fit in the ring");
   __syncthreads();
   uint16_t* tile = reinterpret_cast<uint16_t*>(smem);
+  uint2 ce_pre[EPI == 3 ? 2 : 1][EPI == 3 ? BN / 16 : 1];   // lora_down operands of the chain's partial
   if constexpr (FMT == 0) {
     const int l16 = lane & 15, lq = lane >> 4;
     // the fused QKV epilogue applies to the Q and K thirds (a tile is one head:
@@ -375,7 +377,7 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restr
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float v = fmaf(acc4[rb][cb][i], 0.00390625f, bn);   // exact 2^-8, then + bias
-          if (EPI == 1) v = gelu_tanh_f32(v);
+          if (EPI == 1 || EPI == 3) v = gelu_tanh_f32(v);
           yv[rb][cb][i] = v;
         }
     }
@@ -429,6 +431,73 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restr
         for (int i = 0; i < 4; ++i)
           tile[(wm * 32 * WM + rb * 16 + lq * 4 + i) * TP + nl] = Io<IO>::from_f(yv[rb][cb][i]);
     }
+    if constexpr (EPI == 3) {
+      // The fused MLP chain: U (the 16-bit values just staged) is the input of the
+      // down-projection's quantizer, exactly as if it had gone through memory.
+      // This wave's 64 columns are one INT4 group of the down-projection's K, so
+      // a row's group max is a max over this lane's 4 columns and the 16 lanes of
+      // its DPP row. Codes and scales are staged in LDS, then stored as lines.
+      static_assert(WN == 2 && 32 * WN == 64, "one INT4 group per wave");
+      static_assert(BM * TP * 2 + BM * (BN / 2) + BM * 4 <= S::LDS, "chain staging must fit in the ring");
+      uint8_t* cst = smem + BM * TP * 2;                                // [BM][BN / 2] code bytes
+      __half* sst = reinterpret_cast<__half*>(cst + BM * (BN / 2));     // [BM][2] scales
+      // the low-rank partial's first 32 ranks of lora_down go out now, so their
+      // latency hides behind the quantization below
+      if (ce.r > 0) {
+        const uint16_t* ldn = reinterpret_cast<const uint16_t*>(ce.lora_down);
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+          for (int k = 0; k < BN / 16; ++k)
+            ce_pre[jb][k] = *reinterpret_cast<const uint2*>(
+                ldn + (size_t)(min(jb * 16, ce.r - 16) + l16) * N + n0 + k * 16 + lq * 4);
+      }
+      float sv[CB4];
+#pragma unroll
+      for (int cb = 0; cb < CB4; ++cb) sv[cb] = ce.smooth_inv[n0 + wn * 64 + cb * 16 + l16];
+#pragma unroll
+      for (int rb = 0; rb < RB4; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = wm * 32 * WM + rb * 16 + lq * 4 + i;
+          float x[CB4];
+          float amax = 0.f;
+#pragma unroll
+          for (int cb = 0; cb < CB4; ++cb) {
+            // x_hat = fl32(u * smooth_inv): one multiply, -0 addend keeps the sign of zero
+            x[cb] = fmaf(Io<IO>::to_f(Io<IO>::from_f(yv[rb][cb][i])), sv[cb], -0.0f);
+            amax = fmaxf(amax, fabsf(x[cb]));
+          }
+          amax = row16_max(amax);
+          const __half s16 = __float2half_rn(fminf(amax / 7.0f, 65504.0f));   // IEEE division
+          const float sf = __half2float(s16);
+          // q = clamp(rint(fl32(x / s)), -7, 7): x * rcp(s) rounded inside
+          // fma(x, rcp(s), 1.5 * 2^23) gives the same integer unless the product
+          // lies within 2^-16 of a half-integer (rcp is within an ulp, so it is
+          // within 2^-19 |y| of the quotient); such lanes redo the IEEE division
+          constexpr float kM = 12582912.0f;   // 1.5 * 2^23
+          const float rs = sf != 0.0f ? __builtin_amdgcn_rcpf(sf) : 0.0f;
+          int qn[CB4];
+          bool near_tie = false;
+#pragma unroll
+          for (int cb = 0; cb < CB4; ++cb) {
+            const float y = __builtin_amdgcn_fmed3f(fmaf(x[cb], rs, kM), kM - 7.0f, kM + 7.0f);
+            near_tie |= fabsf(fmaf(x[cb], rs, -(y - kM))) > 0.4999847412109375f;
+            qn[cb] = (int)(__float_as_uint(y) & 0xFu);
+          }
+          if (near_tie && sf != 0.0f) {
+#pragma unroll
+            for (int cb = 0; cb < CB4; ++cb)
+              qn[cb] = (int)fminf(fmaxf(rintf(x[cb] / sf), -7.0f), 7.0f) & 0xF;   // IEEE division
+          }
+#pragma unroll
+          for (int cb = 0; cb < CB4; ++cb) {
+            const int qo = __builtin_amdgcn_update_dpp(0, qn[cb], 0xB1, 0xF, 0xF, false);   // column + 1
+            if ((l16 & 1) == 0) cst[row * (BN / 2) + wn * 32 + cb * 8 + (l16 >> 1)] = (uint8_t)(qn[cb] | (qo << 4));
+          }
+          if (l16 == 0) sst[row * 2 + wn] = s16;
+        }
+    }
   } else {
 #pragma unroll
     for (int cb = 0; cb < CB32; ++cb) {
@@ -445,18 +514,85 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restr
     }
   }
   __syncthreads();
-  for (int c = tid; c < BM * (BN / 8); c += 256) {
-    const int row = c / (BN / 8), c8 = c - row * (BN / 8);
-    if (m0 + row < M)
-      *reinterpret_cast<uint4*>(Y + (size_t)(m0 + row) * N + n0 + c8 * 8) =
-          *reinterpret_cast<const uint4*>(tile + row * TP + c8 * 8);
+  if constexpr (EPI != 3) {
+    for (int c = tid; c < BM * (BN / 8); c += 256) {
+      const int row = c / (BN / 8), c8 = c - row * (BN / 8);
+      if (m0 + row < M)
+        *reinterpret_cast<uint4*>(Y + (size_t)(m0 + row) * N + n0 + c8 * 8) =
+            *reinterpret_cast<const uint4*>(tile + row * TP + c8 * 8);
+    }
+  } else {
+    const uint8_t* cst = smem + BM * TP * 2;
+    const uint32_t* sst = reinterpret_cast<const uint32_t*>(cst + BM * (BN / 2));
+    for (int c = tid; c < BM * (BN / 32); c += 256) {          // codes: 64 bytes per row
+      const int row = c / (BN / 32), c16 = c - row * (BN / 32);
+      if (m0 + row < M)
+        *reinterpret_cast<uint4*>(ce.codes + (size_t)(m0 + row) * (N >> 1) + (n0 >> 1) + c16 * 16) =
+            *reinterpret_cast<const uint4*>(cst + row * (BN / 2) + c16 * 16);
+    }
+    for (int row = tid; row < BM; row += 256)                  // scales: the tile's 2 groups per row
+      if (m0 + row < M)
+        *reinterpret_cast<uint32_t*>(reinterpret_cast<__half*>(ce.scales) + (size_t)(m0 + row) * (N >> 6) +
+                                     (n0 >> 6)) = sst[row];
+    // low-rank partial of the down-projection over this tile's 128 columns:
+    // P[m][j] = sum_n U[m][n] lora_down[j][n0 + n], v_mfma 16x16x16 (lane l: row or
+    // rank l % 16, k 4 (l / 16) .. +4; result: rank l % 16, rows 4 (l / 16) + i).
+    // Wave w takes rows 32 w .. +32; written in full to the tile's slice.
+    const int l16 = lane & 15, lq = lane >> 4;
+    const uint16_t* ldn = reinterpret_cast<const uint16_t*>(ce.lora_down);
+    float* part = ce.partial + ((size_t)(n0 / BN) * M) * ce.r;
+    for (int jb = 0; jb < ce.r; jb += 16) {
+      v4f pacc[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int k0 = 0; k0 < BN; k0 += 16) {
+        const uint2 bw = jb < 32 ? ce_pre[jb >> 4][k0 >> 4]
+                                 : *reinterpret_cast<const uint2*>(ldn + (size_t)(jb + l16) * N + n0 + k0 + lq * 4);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint2 aw = *reinterpret_cast<const uint2*>(tile + (wave * 32 + h * 16 + l16) * TP + k0 + lq * 4);
+          pacc[h] = Io<IO>::mma16x16x16(aw, bw, pacc[h]);
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = m0 + wave * 32 + h * 16 + lq * 4 + i;
+          if (m < M) part[(size_t)m * ce.r + jb + l16] = pacc[h][i];
+        }
+    }
   }
+}
+
+// lora_act[m][j] = h16( sum_t partial[t][m][j] ), summed in the order t = 0, 1, ...
+template <int IO>
+__global__ __launch_bounds__(256)
+void chain_reduce_kernel(const float* __restrict__ partial, uint16_t* __restrict__ lora_act, int M, int r,
+                         int tiles) {
+  const size_t n = (size_t)M * r;
+  for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (size_t)gridDim.x * 256) {
+    float s = 0.f;
+    for (int t = 0; t < tiles; ++t) s += partial[(size_t)t * n + e];
+    lora_act[e] = Io<IO>::from_f(s);
+  }
+}
+
+hipError_t launch_chain_reduce(int io, int M, int r, int tiles, const float* partial, void* lora_act,
+                               hipStream_t st) {
+  const size_t n = (size_t)M * r;
+  const int grid = (int)std::min<size_t>((n + 255) / 256, 2048);
+  if (io == 1)
+    hipLaunchKernelGGL(chain_reduce_kernel<1>, dim3(grid), dim3(256), 0, st, partial, (uint16_t*)lora_act, M, r, tiles);
+  else
+    hipLaunchKernelGGL(chain_reduce_kernel<0>, dim3(grid), dim3(256), 0, st, partial, (uint16_t*)lora_act, M, r, tiles);
+  return hipGetLastError();
 }
 
 template <int IO, int FMT, int EPI, int WM, int WN, int STAGES>
 static hipError_t launch_cfg(int M, int N, int K, int r, const uint8_t* ac, const void* as,
                              const void* la, const uint8_t* wc, const void* ws, const void* lu,
-                             const void* bias, void* Y, hipStream_t st, const QkvEpilogue& qe) {
+                             const void* bias, void* Y, hipStream_t st, const QkvEpilogue& qe,
+                             const ChainEpilogue& ce) {
   using S = GemmShape<WM, WN, STAGES>;
   auto kern = gemm_w4a4_kernel<IO, FMT, EPI, WM, WN, STAGES>;
   if (S::LDS > 65536) {
@@ -470,7 +606,7 @@ static hipError_t launch_cfg(int M, int N, int K, int r, const uint8_t* ac, cons
   }
   const int ntiles = ((M + S::BM - 1) / S::BM) * (N / S::BN);
   hipLaunchKernelGGL(kern, dim3(ntiles), dim3(256), S::LDS, st, ac, as, (const uint16_t*)la, wc, ws,
-                     (const uint16_t*)lu, (const uint16_t*)bias, (uint16_t*)Y, M, N, K, r, qe);
+                     (const uint16_t*)lu, (const uint16_t*)bias, (uint16_t*)Y, M, N, K, r, qe, ce);
   return hipGetLastError();
 }
 
@@ -478,13 +614,18 @@ template <int IO>
 static hipError_t launch_gemm_io(int fmt, int M, int N, int K, int r, const uint8_t* ac, const void* as,
                                  const void* la, const uint8_t* wc, const void* ws, const void* lu,
                                  const void* bias, int epi, void* Y, hipStream_t st,
-                                 const QkvEpilogue* qkv) {
+                                 const QkvEpilogue* qkv, const ChainEpilogue* chain) {
   const QkvEpilogue qe = qkv ? *qkv : QkvEpilogue{nullptr, nullptr, 0.f, 1};
+  const ChainEpilogue ce = chain ? *chain : ChainEpilogue{nullptr, nullptr, 0, nullptr, nullptr, nullptr};
 #define SVDQ_GO(F, E, WM_, WN_, ST_) \
-  return launch_cfg<IO, F, E, WM_, WN_, ST_>(M, N, K, r, ac, as, la, wc, ws, lu, bias, Y, st, qe)
+  return launch_cfg<IO, F, E, WM_, WN_, ST_>(M, N, K, r, ac, as, la, wc, ws, lu, bias, Y, st, qe, ce)
   if (epi == 2) {   // fused QKV epilogue: INT4 only
     if (fmt != 0 || !qkv) return hipErrorInvalidValue;
     SVDQ_GO(0, 2, 2, 2, 3);
+  }
+  if (epi == 3) {   // fused MLP chain: INT4 only
+    if (fmt != 0 || !chain) return hipErrorInvalidValue;
+    SVDQ_GO(0, 3, 2, 2, 3);
   }
   if (fmt == 0) {
     if (epi == 0) SVDQ_GO(0, 0, 2, 2, 3); else SVDQ_GO(0, 1, 2, 2, 3);
@@ -498,9 +639,10 @@ static hipError_t launch_gemm_io(int fmt, int M, int N, int K, int r, const uint
 
 hipError_t launch_gemm_w4a4(int fmt, int io, int M, int N, int K, int r, const uint8_t* ac, const void* as,
                             const void* la, const uint8_t* wc, const void* ws, const void* lu,
-                            const void* bias, int epi, void* Y, hipStream_t st, const QkvEpilogue* qkv) {
-  if (io == 1) return launch_gemm_io<1>(fmt, M, N, K, r, ac, as, la, wc, ws, lu, bias, epi, Y, st, qkv);
-  return launch_gemm_io<0>(fmt, M, N, K, r, ac, as, la, wc, ws, lu, bias, epi, Y, st, qkv);
+                            const void* bias, int epi, void* Y, hipStream_t st, const QkvEpilogue* qkv,
+                            const ChainEpilogue* chain) {
+  if (io == 1) return launch_gemm_io<1>(fmt, M, N, K, r, ac, as, la, wc, ws, lu, bias, epi, Y, st, qkv, chain);
+  return launch_gemm_io<0>(fmt, M, N, K, r, ac, as, la, wc, ws, lu, bias, epi, Y, st, qkv, chain);
 }
 
 }  // namespace svdq

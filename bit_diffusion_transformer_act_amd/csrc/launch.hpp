@@ -23,10 +23,28 @@ struct QkvEpilogue {
   int heads;
 };
 
+// Parameters of the fused MLP chain (epi == 3, INT4 only): GELU, then the
+// down-projection's quantizer on the 16-bit result U: smoothing by
+// smooth_inv [N], INT4 g64 codes [M][N/2] and fp16 scales [M][N/64], and the
+// per-tile fp32 partials of U lora_down^T ([N/128][M][r], summed by
+// launch_chain_reduce into lora_act).
+struct ChainEpilogue {
+  const float* smooth_inv;
+  const void* lora_down;
+  int r;
+  uint8_t* codes;
+  void* scales;
+  float* partial;
+};
+
+hipError_t launch_chain_reduce(int io, int M, int r, int tiles, const float* partial, void* lora_act,
+                               hipStream_t stream);
+
 hipError_t launch_gemm_w4a4(int fmt, int io, int M, int N, int K, int r, const uint8_t* act_codes,
                             const void* act_scales, const void* lora_act, const uint8_t* w_codes,
                             const void* w_scales, const void* lora_up, const void* bias, int epi,
-                            void* Y, hipStream_t stream, const QkvEpilogue* qkv = nullptr);
+                            void* Y, hipStream_t stream, const QkvEpilogue* qkv = nullptr,
+                            const ChainEpilogue* chain = nullptr);
 
 hipError_t launch_gemm_fp4_big(int io, int M, int N, int K, int r, const uint8_t* act_codes,
                                const void* act_scales, const void* lora_act, const uint8_t* w_codes,

@@ -38,7 +38,8 @@ SVDQ_ERR_HIP = -5
 
 EXPORTED_SYMBOLS = ("svdq_device_check", "svdq_status_str", "svdq_version",
                     "svdq_quantize_act", "svdq_gemm_w4a4", "svdq_gemm_w4a4_qkv",
-                    "svdq_quantize_act_nvfp4", "svdq_gemm_nvfp4", "awq_gemv_w4a16")
+                    "svdq_quantize_act_nvfp4", "svdq_gemm_nvfp4", "awq_gemv_w4a16",
+                    "svdq_gemm_w4a4_mlp", "svdq_gemm_w4a4_mlp_workspace")
 
 _lock = threading.Lock()
 _handle = None
@@ -79,6 +80,12 @@ def lib() -> ctypes.CDLL:
             h.svdq_quantize_act_nvfp4.restype = i32
             h.svdq_gemm_nvfp4.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, f32, i32, vp, vp]
             h.svdq_gemm_nvfp4.restype = i32
+            sz = ctypes.c_size_t
+            h.svdq_gemm_w4a4_mlp_workspace.argtypes = [i32, i32, i32]
+            h.svdq_gemm_w4a4_mlp_workspace.restype = sz
+            h.svdq_gemm_w4a4_mlp.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp,
+                                             vp, vp, i32, vp, vp, vp, vp, sz, vp]
+            h.svdq_gemm_w4a4_mlp.restype = i32
             h.awq_gemv_w4a16.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
             h.awq_gemv_w4a16.restype = i32
             _handle = h
@@ -269,6 +276,66 @@ def svdq_gemm_w4a4_qkv(act_codes, act_scales, lora_act, w_codes, w_scales, lora_
     if st != SVDQ_OK:
         raise SvdqError(st, "svdq_gemm_w4a4_qkv")
     return out
+
+
+def svdq_gemm_w4a4_mlp(act_codes, act_scales, lora_act, w_codes, w_scales, lora_up, bias,
+                       smooth_inv2, lora_down2, fmt="int4_g64", act_codes2=None, act_scales2=None,
+                       lora_act2=None, workspace=None, dtype=None):
+    """The fused MLP chain: the up-projection with GELU, straight into the
+    down-projection's INT4 quantizer. Returns (act_codes2 u8 [M][N/2],
+    act_scales2 fp16 [M][N/64], lora_act2 [M][r2] or None), what
+    svdq_quantize_act would give on the up-projection's output. workspace:
+    fp32 device memory of svdq_gemm_w4a4_mlp_workspace(M, N, r2) bytes (taken
+    from torch's allocator when not given)."""
+    f = _fmt(fmt)
+    h = _pick_dtype(dtype, lora_act, lora_up, bias, lora_down2)
+    io = DTYPES[h]
+    dev = act_codes.device
+    if dev.type != "cuda":
+        raise ValueError("act_codes must be a HIP device tensor")
+    M, KB = act_codes.shape
+    K = 2 * KB
+    N = w_codes.shape[0]
+    r = 0 if lora_up is None else lora_up.shape[1]
+    r2 = 0 if lora_down2 is None else lora_down2.shape[0]
+    sdt, sa_shape = _scale_spec(f, M, K)
+    _, sw_shape = _scale_spec(f, N, K)
+    _check(act_codes, "act_codes", torch.uint8, (M, KB), dev)
+    _check(act_scales, "act_scales", sdt, sa_shape, dev)
+    _check(w_codes, "w_codes", torch.uint8, (N, KB), dev)
+    _check(w_scales, "w_scales", sdt, sw_shape, dev)
+    if r > 0:
+        _check(lora_act, "lora_act", h, (M, r), dev)
+        _check(lora_up, "lora_up", h, (N, r), dev)
+    if bias is not None:
+        _check(bias, "bias", h, (N,), dev)
+    _check(smooth_inv2, "smooth_inv2", torch.float32, (N,), dev)
+    if r2 > 0:
+        _check(lora_down2, "lora_down2", h, (r2, N), dev)
+    if act_codes2 is None:
+        act_codes2 = torch.empty((M, N // 2), dtype=torch.uint8, device=dev)
+    if act_scales2 is None:
+        act_scales2 = torch.empty((M, N // 64), dtype=torch.float16, device=dev)
+    if r2 > 0 and lora_act2 is None:
+        lora_act2 = torch.empty((M, r2), dtype=h, device=dev)
+    _check(act_codes2, "act_codes2", torch.uint8, (M, N // 2), dev)
+    _check(act_scales2, "act_scales2", torch.float16, (M, N // 64), dev)
+    if r2 > 0:
+        _check(lora_act2, "lora_act2", h, (M, r2), dev)
+    need = lib().svdq_gemm_w4a4_mlp_workspace(M, N, r2)
+    if r2 > 0 and workspace is None:
+        workspace = torch.empty(need // 4, dtype=torch.float32, device=dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    with torch.cuda.device(dev):
+        st = lib().svdq_gemm_w4a4_mlp(f, io, M, N, K, r, _ptr(act_codes), _ptr(act_scales),
+                                      _ptr(lora_act) if r > 0 else None, _ptr(w_codes), _ptr(w_scales),
+                                      _ptr(lora_up) if r > 0 else None, _ptr(bias), _ptr(smooth_inv2),
+                                      _ptr(lora_down2) if r2 > 0 else None, r2, _ptr(act_codes2),
+                                      _ptr(act_scales2), _ptr(lora_act2) if r2 > 0 else None,
+                                      _ptr(workspace) if r2 > 0 else None, wbytes, _stream(dev))
+    if st != SVDQ_OK:
+        raise SvdqError(st, "svdq_gemm_w4a4_mlp")
+    return act_codes2, act_scales2, (lora_act2 if r2 > 0 else None)
 
 
 def svdq_quantize_act_nvfp4(X: torch.Tensor, smooth_inv: torch.Tensor, lora_down, act_gscale: float,

@@ -44,6 +44,7 @@
 #ifndef SVDQ_MI355X_H
 #define SVDQ_MI355X_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -201,6 +202,43 @@ int svdq_gemm_w4a4_qkv(int fmt, int dtype, int M, int N, int K, int r,
                        const uint8_t* w_codes, const void* w_scales, const void* lora_up,
                        const void* bias, const void* qk_norm_w, const float* rope, float eps,
                        void* Y, void* stream);
+
+/*
+ * svdq_gemm_w4a4_mlp -- the fused MLP chain: an MLP up-projection with GELU
+ * whose output never reaches memory; its 16-bit result U goes straight into
+ * the down-projection's activation quantizer (the pages' GELU / MLP fused
+ * kernels of the full engine: dothoosh.com article, generic-path paragraph).
+ * Exactly the composition of the unfused calls, without Y:
+ *
+ *   U = h16_rne( svdq_gemm_w4a4(..., SVDQ_EPI_GELU_TANH) )      (not stored)
+ *   act_codes2, act_scales2, lora_act2 = svdq_quantize_act(INT4_G64, U,
+ *                                          smooth_inv2, lora_down2)
+ *
+ * The codes and scales equal the unfused path's bit for bit (the same U, the
+ * same quantizer rule); lora_act2 is summed over the up-projection's tiles of
+ * 128 columns in fp32, in a fixed order (deterministic), then rounded to h16.
+ * Two kernels: the GEMM with the quantizer in its epilogue, and the sum of the
+ * per-tile partials of the low-rank down-projection, kept in `workspace`.
+ *
+ * Arguments as svdq_gemm_w4a4 for the up-projection (fmt must be
+ * SVDQ_INT4_G64; GELU is implied; there is no Y), and
+ *   smooth_inv2      fp32 [N], the down-projection's smoothing multiplier.
+ *   lora_down2       h16 [r2][N], its low-rank down factor; NULL iff r2 == 0.
+ *   r2               its low-rank width; r2 % 16 == 0, 0 <= r2 <= 128.
+ *   act_codes2       out, u8 [M][N/2]   (INT4 codes of U, the down-projection's K = N).
+ *   act_scales2      out, fp16 [M][N/64].
+ *   lora_act2        out, h16 [M][r2]; NULL iff r2 == 0.
+ *   workspace        device memory of at least svdq_gemm_w4a4_mlp_workspace(M, N, r2)
+ *                    bytes (fp32 partials), owned by the caller; NULL iff r2 == 0.
+ *   workspace_bytes  its size (SVDQ_ERR_SHAPE if too small).
+ */
+size_t svdq_gemm_w4a4_mlp_workspace(int M, int N, int r2);
+int svdq_gemm_w4a4_mlp(int fmt, int dtype, int M, int N, int K, int r,
+                       const uint8_t* act_codes, const void* act_scales, const void* lora_act,
+                       const uint8_t* w_codes, const void* w_scales, const void* lora_up,
+                       const void* bias, const float* smooth_inv2, const void* lora_down2, int r2,
+                       uint8_t* act_codes2, void* act_scales2, void* lora_act2,
+                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * svdq_quantize_act_nvfp4 -- svdq_quantize_act for NVFP4 (the pages' svdq_w4a4

@@ -24,7 +24,7 @@ U = 4099  # unaligned fake address
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(\w+)\s*\(", src, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(\w+)\s*\(", src, flags=re.M)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -145,6 +145,27 @@ def test_nvfp4_argument_errors():
     assert gn(Y=U) == ops.SVDQ_ERR_ALIGN
     assert gn(b=U) == ops.SVDQ_ERR_ALIGN
     assert gn() == ops.SVDQ_ERR_UNSUPPORTED_DEVICE
+
+
+def gm(M=4, N=128, K=128, r=16, r2=16, ac=A, sa=A, la=A, wc=A, ws=A, lu=A, b=None, si2=A, ld2=A,
+       c2=A, s2=A, la2=A, wk=A, wkb=1 << 20, dt=0, fmt=0):
+    return P.lib().svdq_gemm_w4a4_mlp(fmt, dt, M, N, K, r, ac, sa, la, wc, ws, lu, b, si2, ld2, r2, c2, s2, la2,
+                                      wk, wkb, None)
+
+
+def test_mlp_chain_argument_errors():
+    assert P.lib().svdq_gemm_w4a4_mlp_workspace(4096, 12288, 32) == 96 * 4096 * 32 * 4
+    assert gm(fmt=1) == ops.SVDQ_ERR_INVALID_ARG          # INT4 only
+    assert gm(dt=3) == ops.SVDQ_ERR_INVALID_ARG
+    assert gm(N=192) == ops.SVDQ_ERR_SHAPE
+    assert gm(r2=24) == ops.SVDQ_ERR_SHAPE
+    assert gm(wkb=4 * 16 * 4 - 1) == ops.SVDQ_ERR_SHAPE   # one tile x 4 rows x 16 ranks x 4 bytes needed
+    assert gm(wk=None) == ops.SVDQ_ERR_INVALID_ARG
+    assert gm(r2=0, ld2=None, la2=None, wk=None, wkb=0) == ops.SVDQ_ERR_UNSUPPORTED_DEVICE
+    assert gm(c2=U) == ops.SVDQ_ERR_ALIGN
+    assert gm(M=0, ac=None, sa=None, la=None, wc=None, ws=None, lu=None, si2=None, ld2=None, c2=None,
+              s2=None, la2=None, wk=None) == ops.SVDQ_OK
+    assert gm() == ops.SVDQ_ERR_UNSUPPORTED_DEVICE
 
 
 def test_device_check_without_gpu():

@@ -1,0 +1,131 @@
+"""The fused MLP chain (svdq_gemm_w4a4_mlp): the up-projection with GELU whose
+16-bit output goes straight into the down-projection's INT4 quantizer.
+
+Two bars. (1) It equals the unfused path on the GPU (svdq_gemm_w4a4 with
+GELU, then svdq_quantize_act on its output): codes and scales bit for bit,
+lora_act2 within relative L2 1e-3 (a different fp32 summation order). (2) The
+whole MLP against the oracle chain (oracle.mlp_chain_ref, then the
+down-projection's gemm_ref): relative L2 2e-3 on the down-projection's
+output. The oracle's own U differs from the GPU's in last bits, so the
+4-bit codes of the two may differ where a value sits at a rounding edge; the
+down-projection's output is where that difference has to stay inside the bar.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+Y_TOL = 2e-3
+LORA_TOL = 1e-3
+DEV = torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def P():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    import bit_diffusion_transformer_act_amd as pkg
+    assert pkg.svdq_device_check(0) == 0, "cuda:0 is not gfx950"
+    return pkg
+
+
+def dev(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    return t.to(dtype) if dtype is not None else t
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.float().cpu().numpy() if t.dtype == torch.bfloat16 else t.cpu().numpy()
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300)
+
+
+def chain_inputs(M, K, N, r, r2, seed=0):
+    """Up-projection in storage format (INT4), and the down-projection's
+    smoothing vector and low-rank down factor (fp16)."""
+    cfg = synth.LayerConfig(f"chain_{M}_{K}_{N}", 70, M, K, N, r, "int4_g64", "gelu_tanh", "normal", 0.005, 30.0)
+    up = synth.random_quantized_layer(cfg, seed=seed)
+    g = synth.rng_for(seed, 71, 7)
+    si2 = np.exp(g.normal(0.0, 0.3, N)).astype(np.float32)
+    ld2 = (g.standard_normal((r2, N)) * 0.02).astype(np.float16)
+    return up, si2, ld2
+
+
+def run_unfused(P, codes, scales, la, up, si2, ld2, h):
+    y = P.svdq_gemm_w4a4(codes, scales, la, dev(up["w_codes"]), dev(up["w_scales"]),
+                         dev(up["lora_up"], h) if la is not None else None, dev(up["bias"], h), "int4_g64",
+                         "gelu_tanh", dtype=h)
+    return P.svdq_quantize_act(y, dev(si2), dev(ld2, h) if ld2.shape[0] else None, "int4_g64")
+
+
+def run_fused(P, codes, scales, la, up, si2, ld2, h):
+    return P.svdq_gemm_w4a4_mlp(codes, scales, la, dev(up["w_codes"]), dev(up["w_scales"]),
+                                dev(up["lora_up"], h) if la is not None else None, dev(up["bias"], h), dev(si2),
+                                dev(ld2, h) if ld2.shape[0] else None, dtype=h)
+
+
+@pytest.mark.parametrize("M,K,N,r,r2,h", [(200, 512, 1024, 16, 16, torch.float16),
+                                          (37, 256, 384, 16, 32, torch.float16),
+                                          (256, 512, 512, 0, 0, torch.float16),
+                                          (130, 512, 768, 32, 16, torch.bfloat16),
+                                          (4096, 3072, 12288, 32, 32, torch.float16)])
+def test_chain_equals_unfused(P, M, K, N, r, r2, h):
+    up, si2, ld2 = chain_inputs(M, K, N, r, r2)
+    X = dev(up["X"], h)
+    codes, scales, la = P.svdq_quantize_act(X, dev(up["smooth_inv"]), dev(up["lora_down"][:r], h) if r else None,
+                                            "int4_g64")
+    c1, s1, l1 = run_unfused(P, codes, scales, la, up, si2, ld2, h)
+    c2, s2, l2 = run_fused(P, codes, scales, la, up, si2, ld2, h)
+    assert np.array_equal(host(c2), host(c1))
+    assert np.array_equal(host(s2).view(np.uint16), host(s1).view(np.uint16))
+    if r2:
+        assert l2.dtype == h
+        assert rel_l2(host(l2), host(l1)) <= LORA_TOL
+    else:
+        assert l2 is None
+
+
+def test_chain_is_deterministic(P):
+    up, si2, ld2 = chain_inputs(200, 512, 1024, 16, 32, seed=2)
+    X = dev(up["X"])
+    codes, scales, la = P.svdq_quantize_act(X, dev(up["smooth_inv"]), dev(up["lora_down"][:16]), "int4_g64")
+    a = [host(t) for t in run_fused(P, codes, scales, la, up, si2, ld2, torch.float16)]
+    b = [host(t) for t in run_fused(P, codes, scales, la, up, si2, ld2, torch.float16)]
+    for x, y in zip(a, b):
+        assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
+
+
+def test_mlp_against_oracle_chain(P):
+    M, K, N, N2, r, r2 = 200, 512, 1024, 384, 16, 16
+    up, si2, ld2 = chain_inputs(M, K, N, r, r2, seed=3)
+    cfg2 = synth.LayerConfig("chain_down", 72, M, N, N2, r2, "int4_g64", "none", "gelu_normal", 0.005, 30.0)
+    down = synth.random_quantized_layer(cfg2, seed=3)
+    # the oracle: quantize X, the up-projection with GELU, the chain's quantizer, the down-projection
+    cu, packed, scales = oracle.quantize_act_ref(up["X"], up["smooth_inv"], "int4_g64")
+    la = oracle.lora_act_ref(up["X"], up["lora_down"][:r]).astype(np.float16)
+    wu = oracle.unpack_nibbles(up["w_codes"], signed=True)
+    U16, c2u, c2p, s2, la2 = oracle.mlp_chain_ref(cu, scales, la, wu, up["w_scales"], up["lora_up"][:, :r],
+                                                 up["bias"], "int4_g64", si2, ld2)
+    w2u = oracle.unpack_nibbles(down["w_codes"], signed=True)
+    y_ref = oracle.gemm_ref(c2u, s2, la2.astype(np.float16), w2u, down["w_scales"], down["lora_up"][:, :r2],
+                            down["bias"], "int4_g64")
+    # the GPU: the same quantized X (bit-exact, checked), the fused chain, the down-projection
+    codes, sc, la_g = P.svdq_quantize_act(dev(up["X"]), dev(up["smooth_inv"]), dev(up["lora_down"][:r]), "int4_g64")
+    assert np.array_equal(host(codes), packed)
+    c2, sc2, l2 = P.svdq_gemm_w4a4_mlp(codes, sc, dev(la), dev(up["w_codes"]), dev(up["w_scales"]),
+                                       dev(up["lora_up"][:, :r]), dev(up["bias"]), dev(si2), dev(ld2))
+    assert rel_l2(host(l2), la2) <= LORA_TOL
+    mismatch = np.mean(host(c2) != c2p)
+    print(f"chain codes differing from the oracle's (last-bit differences of U): {mismatch:.2e}")
+    assert mismatch < 0.01
+    y = P.svdq_gemm_w4a4(c2, sc2, l2, dev(down["w_codes"]), dev(down["w_scales"]), dev(down["lora_up"][:, :r2]),
+                         dev(down["bias"]), "int4_g64")
+    assert rel_l2(host(y), y_ref) <= Y_TOL
