@@ -95,7 +95,7 @@ def main():
                                "source_sha": source_sha(src)}
         lines.append(f"| {api} | {fk:.0f} | {wk:.0f} | {rd / 1e6:.1f} | {wr / 1e6:.1f} | "
                      f"{(rd + wr) / 1e6:.1f} |")
-    g = out["kernels"].get("svdq_gemm_w4a4")
+    g = out["kernels"].get("svdq_gemm_w4a4") or out["kernels"].get("svdq_gemm_nvfp4")
     if g:
         out["source"] = g["source"]
         out["source_sha"] = g["source_sha"]
