@@ -105,9 +105,9 @@ def stored_traffic(workload):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build runs the layer on a single MI355X "
-              "(token-parallel sharding across GPUs is described in DESIGN.md, not run). "
-              "Use --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the layer runs on a single MI355X; splitting the "
+              "tokens across GPUs needs no exchange and is not run here. Use --gpus 1.",
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
