@@ -412,9 +412,10 @@ static hipError_t launch_qw(int M, int K, const void* X, const float* si, const 
   return launch_qws<IO, FMT, NCB, WAVES, false>(M, K, X, si, ld, codes, scales, la, gs, st);
 }
 
-// 16 rows per workgroup. With at least one workgroup per CU, 8 waves (2 per
-// SIMD, up to 256 VGPRs for the load ring); with fewer workgroups than CUs and
-// a small rank, 16 waves so that each busy CU keeps more loads in flight; for
+// 16 rows per workgroup. For ranks up to 32, 16 waves (4 per SIMD): more waves
+// keep more loads in flight per CU and measured faster than 8 at every M (e.g.
+// 17.2 -> 15.3 us at M4096 K3072, 51.2 -> 46.6 us at M4096 K12288); for ranks
+// 48 to 96, 8 waves (the ring's lora_down operands need the registers); for
 // ranks of 112 and more, 4 waves (the lora_down operands of a step take
 // 8 * r / 16 VGPRs per set).
 template <int IO, int FMT, int NCB>
@@ -425,7 +426,6 @@ static hipError_t launch_q(int M, int K, const void* X, const float* si, const v
   } else if constexpr (NCB > 2) {
     return launch_qw<IO, FMT, NCB, 8>(M, K, X, si, ld, codes, scales, la, gs, st);
   } else {
-    if ((M + 15) / 16 >= 256) return launch_qw<IO, FMT, NCB, 8>(M, K, X, si, ld, codes, scales, la, gs, st);
     return launch_qw<IO, FMT, NCB, 16>(M, K, X, si, ld, codes, scales, la, gs, st);
   }
 }
