@@ -72,6 +72,37 @@ void awq_gemv_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__
   uint32_t* xs = lds;
   float* xc = reinterpret_cast<float*>(lds + (size_t)MR * nch * 16);
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const long long W = (long long)gridDim.x * kGemvWaves;
+  const long long wg = (long long)blockIdx.x * kGemvWaves + wave;
+  const int r0 = (int)(wg * N / W), r1 = (int)((wg + 1) * N / W);
+  const int nseg = (nch + 63) >> 6;       // units per row
+  const int nunits = max(r1 - r0, 0) * nseg;
+
+  struct Unit {
+    uint4 w;
+    __half s, z;
+  };
+  // Loads are unconditional: past the wave's last unit they re-read it (never
+  // processed), so the compiler's count of loads in flight stays exact.
+  int lrow = r0, lseg = 0;
+  auto load_next = [&](Unit& d) {
+    const int row = max(min(lrow, r1 - 1), 0);   // a wave with no rows re-reads row 0
+    const int c = min(lseg * 64 + lane, nch - 1);
+    d.w = *reinterpret_cast<const uint4*>(codes + (size_t)row * (K >> 1) + (size_t)c * 16);
+    d.s = scales[(size_t)row * G + (c >> 1)];
+    d.z = zeros[(size_t)row * G + (c >> 1)];
+    if (++lseg == nseg) {
+      lseg = 0;
+      ++lrow;
+    }
+  };
+
+  // the weight stream starts before x is staged, so its first latency overlaps the staging
+  Unit d[kGemvRing];
+#pragma unroll
+  for (int i = 0; i < kGemvRing - 1; ++i) load_next(d[i]);
+
   for (int idx = tid; idx < MR * nch * 4; idx += 64 * kGemvWaves) {
     // idx = (m nch + c) 4 + e: segment e of chunk c = channels 32 c + 8 e .. +8
     const int e = idx & 3, mc = idx >> 2;
@@ -96,32 +127,7 @@ void awq_gemv_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__
   }
   __syncthreads();
 
-  const int lane = tid & 63, wave = tid >> 6;
-  const long long W = (long long)gridDim.x * kGemvWaves;
-  const long long wg = (long long)blockIdx.x * kGemvWaves + wave;
-  const int r0 = (int)(wg * N / W), r1 = (int)((wg + 1) * N / W);
   if (r1 <= r0) return;
-  const int nseg = (nch + 63) >> 6;       // units per row
-  const int nunits = (r1 - r0) * nseg;
-
-  struct Unit {
-    uint4 w;
-    __half s, z;
-  };
-  // Loads are unconditional: past the wave's last unit they re-read it (never
-  // processed), so the compiler's count of loads in flight stays exact.
-  int lrow = r0, lseg = 0;
-  auto load_next = [&](Unit& d) {
-    const int row = min(lrow, r1 - 1);
-    const int c = min(lseg * 64 + lane, nch - 1);
-    d.w = *reinterpret_cast<const uint4*>(codes + (size_t)row * (K >> 1) + (size_t)c * 16);
-    d.s = scales[(size_t)row * G + (c >> 1)];
-    d.z = zeros[(size_t)row * G + (c >> 1)];
-    if (++lseg == nseg) {
-      lseg = 0;
-      ++lrow;
-    }
-  };
 
   // Row totals are collected in registers (row i of the wave in lane i; the
   // grid gives no wave more than 64 rows) and written after the loop: a store
@@ -166,9 +172,6 @@ void awq_gemv_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__
     }
   };
 
-  Unit d[kGemvRing];
-#pragma unroll
-  for (int i = 0; i < kGemvRing - 1; ++i) load_next(d[i]);
   for (int u0 = 0; u0 < nunits; u0 += kGemvRing) {
 #pragma unroll
     for (int i = 0; i < kGemvRing; ++i) {
