@@ -39,10 +39,12 @@ template <> struct Io<0> {
 };
 template <> struct Io<1> {
   static __device__ __forceinline__ float to_f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+  // gfx950's v_cvt_pk_bf16_f32: round to nearest even, NaN -> quiet NaN with
+  // the upper payload bits kept, denormals kept; equal bit for bit, over all
+  // 2^32 inputs, to (u + 0x7FFF + lsb) >> 16 with NaN -> (u >> 16) | 0x40.
+  // One instruction and no branch.
   static __device__ __forceinline__ uint16_t from_f(float v) {
-    const uint32_t u = __float_as_uint(v);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);   // NaN stays NaN
-    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+    return __builtin_bit_cast(uint16_t, (__bf16)v);
   }
   static __device__ __forceinline__ v4f mma16x16x16(uint2 a, uint2 b, v4f c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4s, a), __builtin_bit_cast(v4s, b), c, 0, 0, 0);

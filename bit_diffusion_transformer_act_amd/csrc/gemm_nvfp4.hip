@@ -14,8 +14,9 @@
 // scale 2^8 (E2M1 pair -> fp16 pair x 256; the instruction applies a
 // power-of-two scale), then v_pk_mul_f16 by the E4M3 scale read as fp16 bits
 // (byte << 7 is the fp16 pattern of the E4M3 value x 2^-8, subnormals
-// included). The per-tensor scales are applied once, as alpha, to the fp32
-// sum.
+// included; op_sel broadcasts one half of a row's two-block scale word, so
+// the pair needs no shuffle of its own). The per-tensor scales are applied
+// once, as alpha, to the fp32 sum.
 //
 // Tiling as in the large FP4 kernel: 256 x BN per workgroup, 4 waves of
 // 128 x BN/2 (32 x 32 blocks, fp32 accumulators in AGPRs), one workgroup per
@@ -49,17 +50,18 @@ __device__ __forceinline__ int nv_swz8(int row) { return (row >> 1) & 7; }
 
 // fp16 pair (s_lo, s_lo) and (s_hi, s_hi) from two E4M3 scale bytes (each
 // value x 2^-8; the sign bit of a scale byte is ignored: scales are magnitudes)
-__device__ __forceinline__ void nv_scale_pairs(uint32_t two, uint32_t& lo, uint32_t& hi) {
+__device__ __forceinline__ uint32_t nv_scale_pair(uint32_t two) {
   const uint32_t w = __builtin_amdgcn_perm(two, two, 0x0c010c00u);   // [b0, 0, b1, 0]
-  const uint32_t f = (w << 7) & 0x3F803F80u;                          // [fp16(b0), fp16(b1)]
-  lo = __builtin_amdgcn_perm(f, f, 0x01000100u);
-  hi = __builtin_amdgcn_perm(f, f, 0x03020302u);
+  return (w << 7) & 0x3F803F80u;                                      // [fp16(b0), fp16(b1)]
 }
 
 // 8 E2M1 codes (one dword, even code in the low nibble) times the scale pair
 // -> the 8 fp16 values of an MFMA operand, in k order
+template <int HI>
 __device__ __forceinline__ v8h nv_dequant8(uint32_t w, uint32_t spair) {
-  const v2h s = __builtin_bit_cast(v2h, spair);
+  // both halves of the multiplier from one half of the pair (op_sel of v_pk_mul_f16)
+  const v2h f = __builtin_bit_cast(v2h, spair);
+  const v2h s = __builtin_shufflevector(f, f, HI, HI);
   const v2h h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 0) * s;
   const v2h h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 1) * s;
   const v2h h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 2) * s;
@@ -152,19 +154,27 @@ void gemm_nvfp4_kernel(const uint8_t* __restrict__ act_codes, const uint8_t* __r
     uint4 a[RB], b[CB];
     uint32_t sa[RB], sb[CB];
   };
+  // one lane base per operand and half-step; the 32-row blocks are immediate
+  // offsets of the LDS reads
+  const int a_lane = (wm * 128 + l32) * ROW, b_lane = (BM + wn * (BN / 2) + l32) * ROW;
+  const int sa_lane = CODES + (wm * 128 + l32) * SROW + 2 * lh;
+  const int sb_lane = CODES + (256 + wn * (BN / 2) + l32) * SROW + 2 * lh;
   auto load_ops = [&](Ops& o, int pp, int hs) {
     const uint8_t* st = smem + (pp & 1) * SLOT;
     const int ch = ((2 * hs + lh) ^ s8) << 4;
-    const int so = 4 * hs + 2 * lh;
+    const uint8_t* pa = st + (a_lane + ch);
+    const uint8_t* pb = st + (b_lane + ch);
+    const uint8_t* psa = st + sa_lane + 4 * hs;
+    const uint8_t* psb = st + sb_lane + 4 * hs;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      o.a[rb] = *reinterpret_cast<const uint4*>(st + arow[rb] * ROW + ch);
-      o.sa[rb] = *reinterpret_cast<const uint16_t*>(st + CODES + arow[rb] * SROW + so);
+      o.a[rb] = *reinterpret_cast<const uint4*>(pa + rb * 32 * ROW);
+      o.sa[rb] = *reinterpret_cast<const uint16_t*>(psa + rb * 32 * SROW);
     }
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-      o.b[cb] = *reinterpret_cast<const uint4*>(st + (BM + brow[cb]) * ROW + ch);
-      o.sb[cb] = *reinterpret_cast<const uint16_t*>(st + CODES + (256 + brow[cb]) * SROW + so);
+      o.b[cb] = *reinterpret_cast<const uint4*>(pb + cb * 32 * ROW);
+      o.sb[cb] = *reinterpret_cast<const uint16_t*>(psb + cb * 32 * SROW);
     }
   };
   // Dequantization runs one K block ahead of the MFMAs: while the 16 MFMAs of
@@ -172,23 +182,23 @@ void gemm_nvfp4_kernel(const uint8_t* __restrict__ act_codes, const uint8_t* __r
   // 0) into fp16 operands, 1 MFMA : 4 VALU in the issue order. K block j of a
   // half-step uses dword j of each fragment and scale byte j / 2.
   v8h A0[RB], B0[CB], A1[RB], B1[CB];
-  uint32_t pa[RB][2], pb[CB][2];
+  uint32_t pa[RB], pb[CB];
   auto pairs = [&](const Ops& o) {
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) nv_scale_pairs(o.sa[rb], pa[rb][0], pa[rb][1]);
+    for (int rb = 0; rb < RB; ++rb) pa[rb] = nv_scale_pair(o.sa[rb]);
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) nv_scale_pairs(o.sb[cb], pb[cb][0], pb[cb][1]);
+    for (int cb = 0; cb < CB; ++cb) pb[cb] = nv_scale_pair(o.sb[cb]);
   };
   auto deq = [&](v8h (&A)[RB], v8h (&B)[CB], const Ops& o, int j) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const uint32_t w = j == 0 ? o.a[rb].x : j == 1 ? o.a[rb].y : j == 2 ? o.a[rb].z : o.a[rb].w;
-      A[rb] = nv_dequant8(w, pa[rb][j >> 1]);
+      A[rb] = (j >> 1) ? nv_dequant8<1>(w, pa[rb]) : nv_dequant8<0>(w, pa[rb]);
     }
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
       const uint32_t w = j == 0 ? o.b[cb].x : j == 1 ? o.b[cb].y : j == 2 ? o.b[cb].z : o.b[cb].w;
-      B[cb] = nv_dequant8(w, pb[cb][j >> 1]);
+      B[cb] = (j >> 1) ? nv_dequant8<1>(w, pb[cb]) : nv_dequant8<0>(w, pb[cb]);
     }
   };
   auto mm = [&](const v8h (&A)[RB], const v8h (&B)[CB]) {
