@@ -19,7 +19,9 @@
 // the same number of bytes. The rows of a wave are contiguous in memory and
 // are read as a stream of units of 64 chunks of 16 bytes (lane l takes chunk
 // l of the unit): each load instruction covers 1 KB of whole cache lines, and
-// a ring of units keeps several in flight. x and its chunk sums sit in LDS. A
+// a ring of units keeps several in flight. Where a row is an odd number of
+// 32-chunk halves (K = 3072, for one), rows go in pairs, one per half-wave, so
+// that no unit is half empty. x and its chunk sums sit in LDS. A
 // row's lane partials are summed with lane swaps and DPP at its last unit.
 #include <atomic>
 
@@ -45,6 +47,18 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Sum over each 32-lane half; every lane gets its half's total (the xor-16
+// partner, then the DPP steps of wave_sum).
+__device__ __forceinline__ float half_sum(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));  // row_mirror
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+  return v;
+}
+
 // dot2 of packed 16-bit pairs in the activations' type, fp32 accumulation
 template <int IO>
 __device__ __forceinline__ float dot2_io(uint32_t a, uint32_t b, float c) {
@@ -54,7 +68,11 @@ __device__ __forceinline__ float dot2_io(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(v2h, a), __builtin_bit_cast(v2h, b), c, false);
 }
 
-template <int IO, int MR>
+// PAIRS: a row is an odd number of 32-chunk halves (K = 1024 x odd), so
+// 64-chunk units would leave every other load half empty. The wave's rows then
+// go in pairs, the even row of a pair in lanes 0-31 and the odd one in lanes
+// 32-63, in units of 32 chunks per half: every load is a whole 1 KB.
+template <int IO, int MR, bool PAIRS>
 __global__ __launch_bounds__(64 * kGemvWaves)
 void awq_gemv_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
                      const __half* __restrict__ scales, const __half* __restrict__ zeros,
@@ -76,19 +94,25 @@ void awq_gemv_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__
   const long long W = (long long)gridDim.x * kGemvWaves;
   const long long wg = (long long)blockIdx.x * kGemvWaves + wave;
   const int r0 = (int)(wg * N / W), r1 = (int)((wg + 1) * N / W);
-  const int nseg = (nch + 63) >> 6;       // units per row
-  const int nunits = max(r1 - r0, 0) * nseg;
+  constexpr int UL = PAIRS ? 32 : 64;      // chunks of a row per unit
+  const int ul = PAIRS ? (lane & 31) : lane;
+  const int hl = PAIRS ? (lane >> 5) : 0;   // PAIRS: the half's row within its pair
+  const int nseg = (nch + UL - 1) / UL;     // units per row (per pair of rows)
+  const int nrow = max(r1 - r0, 0);
+  const int nunits = (PAIRS ? (nrow + 1) >> 1 : nrow) * nseg;
 
   struct Unit {
     uint4 w;
     __half s, z;
   };
   // Loads are unconditional: past the wave's last unit they re-read it (never
-  // processed), so the compiler's count of loads in flight stays exact.
-  int lrow = r0, lseg = 0;
+  // processed), so the compiler's count of loads in flight stays exact; the odd
+  // half of a last pair with one row re-reads that row (its total is never stored).
+  int lrow = 0, lseg = 0;   // row (PAIRS: pair) of the wave and unit within it
   auto load_next = [&](Unit& d) {
-    const int row = max(min(lrow, r1 - 1), 0);   // a wave with no rows re-reads row 0
-    const int c = min(lseg * 64 + lane, nch - 1);
+    // a wave with no rows re-reads row 0
+    const int row = max(min(r0 + (PAIRS ? 2 * lrow + hl : lrow), r1 - 1), 0);
+    const int c = min(lseg * UL + ul, nch - 1);
     d.w = *reinterpret_cast<const uint4*>(codes + (size_t)row * (K >> 1) + (size_t)c * 16);
     d.s = scales[(size_t)row * G + (c >> 1)];
     d.z = zeros[(size_t)row * G + (c >> 1)];
@@ -136,9 +160,9 @@ void awq_gemv_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__
   float acc[MR], out[MR];
 #pragma unroll
   for (int m = 0; m < MR; ++m) acc[m] = out[m] = 0.f;
-  int prow = r0, pseg = 0;
+  int prow = 0, pseg = 0;   // row (PAIRS: pair) of the wave and unit within it
   auto process = [&](const Unit& d) {
-    const int c = pseg * 64 + lane;
+    const int c = pseg * UL + ul;
     if (c < nch) {
       const uint32_t w[4] = {d.w.x, d.w.y, d.w.z, d.w.w};
       const float s = __half2float(d.s);
@@ -159,12 +183,20 @@ void awq_gemv_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__
         acc[m] = fmaf(s, fmaf(-zb, xc[m * nch + c], part), acc[m]);
       }
     }
-    if (++pseg == nseg) {   // the row is complete
-      const int slot = prow - r0;
+    if (++pseg == nseg) {   // the row (PAIRS: the pair) is complete
 #pragma unroll
       for (int m = 0; m < MR; ++m) {
-        const float t = wave_sum(acc[m]);
-        out[m] = (lane == slot) ? t : out[m];
+        if constexpr (PAIRS) {
+          // each half's total, then both in every lane: the even row's from the
+          // low half, the odd row's from the high half
+          const float t = half_sum(acc[m]);
+          const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(t), __float_as_uint(t), false, false);
+          const int slot = 2 * prow;
+          out[m] = (lane == slot) ? __uint_as_float(h[0]) : (lane == slot + 1) ? __uint_as_float(h[1]) : out[m];
+        } else {
+          const float t = wave_sum(acc[m]);
+          out[m] = (lane == prow) ? t : out[m];
+        }
         acc[m] = 0.f;
       }
       pseg = 0;
@@ -186,9 +218,9 @@ void awq_gemv_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__
   }
 }
 
-template <int IO, int MR>
-static hipError_t launch_mr(int N, int K, const void* x, const uint8_t* q, const void* s,
-                            const void* z, const void* b, void* y, hipStream_t st) {
+template <int IO, int MR, bool PAIRS>
+static hipError_t launch_k(int N, int K, const void* x, const uint8_t* q, const void* s,
+                           const void* z, const void* b, void* y, hipStream_t st) {
   // about one workgroup per CU for large N, at least ~4 rows per wave for small
   // N, and never more than 64 rows per wave (the kernel keeps one row per lane)
   const int rows_cap = kGemvWaves * 64;
@@ -197,15 +229,24 @@ static hipError_t launch_mr(int N, int K, const void* x, const uint8_t* q, const
   if (lds > 65536) {   // M K = 32768 needs 68 KB
     static std::atomic<int> raised{0};
     if (!raised.load(std::memory_order_acquire)) {
-      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&awq_gemv_kernel<IO, MR>),
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&awq_gemv_kernel<IO, MR, PAIRS>),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, 72 * 1024);
       if (e != hipSuccess) return e;
       raised.store(1, std::memory_order_release);
     }
   }
-  hipLaunchKernelGGL((awq_gemv_kernel<IO, MR>), dim3(grid), dim3(64 * kGemvWaves), lds, st, (const uint16_t*)x, q,
-                     (const __half*)s, (const __half*)z, (const uint16_t*)b, (uint16_t*)y, N, K);
+  hipLaunchKernelGGL((awq_gemv_kernel<IO, MR, PAIRS>), dim3(grid), dim3(64 * kGemvWaves), lds, st,
+                     (const uint16_t*)x, q, (const __half*)s, (const __half*)z, (const uint16_t*)b, (uint16_t*)y,
+                     N, K);
   return hipGetLastError();
+}
+
+template <int IO, int MR>
+static hipError_t launch_mr(int N, int K, const void* x, const uint8_t* q, const void* s,
+                            const void* z, const void* b, void* y, hipStream_t st) {
+  // rows of an odd number of 32-chunk halves go in pairs (whole 1 KB loads)
+  if (((K >> 5) & 63) == 32) return launch_k<IO, MR, true>(N, K, x, q, s, z, b, y, st);
+  return launch_k<IO, MR, false>(N, K, x, q, s, z, b, y, st);
 }
 
 template <int IO>
