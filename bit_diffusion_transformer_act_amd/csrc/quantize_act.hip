@@ -87,11 +87,15 @@ void quantize_act_kernel(const uint16_t* __restrict__ X, const float* __restrict
   // the load's destination would make every prefetch wait for the previous one.
   const size_t xrow = (size_t)min(row, M - 1) * (size_t)K;
 
-  if constexpr (SLDS) {
-    for (int i = threadIdx.x * 4; i < K; i += 64 * WAVES * 4)
-      *reinterpret_cast<float4*>(s_si + i) = *reinterpret_cast<const float4*>(smooth_inv + i);
-    __syncthreads();
-  }
+  // smooth_inv into LDS; called after the first loads of X are out, so the two
+  // latencies overlap
+  auto stage_si = [&]() {
+    if constexpr (SLDS) {
+      for (int i = threadIdx.x * 4; i < K; i += 64 * WAVES * 4)
+        *reinterpret_cast<float4*>(s_si + i) = *reinterpret_cast<const float4*>(smooth_inv + i);
+      __syncthreads();
+    }
+  };
 
   v4f lacc[NL];
 #pragma unroll
@@ -341,6 +345,7 @@ void quantize_act_kernel(const uint16_t* __restrict__ X, const float* __restrict
     Step d0, d1, d2;
     load(d0, wave);
     load(d1, wave + WAVES);
+    stage_si();
     for (int p = 0; p < nrounds; p += 3) {
       load(d2, (p + 2) * WAVES + wave);
       round(d0, p);
@@ -354,6 +359,7 @@ void quantize_act_kernel(const uint16_t* __restrict__ X, const float* __restrict
   } else {
     Step d0, d1;
     load(d0, wave);
+    stage_si();
     for (int p = 0; p < nrounds; p += 2) {
       load(d1, (p + 1) * WAVES + wave);
       round(d0, p);
