@@ -41,7 +41,7 @@ METRIC = "W4A4+lowrank GEMM effective TOPS & % MFMA peak; W4A16 GEMV HBM GB/s"
 PEAK_TOPS = {"int4_g64": 5000.0, "fp4_b32": 10100.0, "nvfp4_g16": 2500.0}
 PEAK_NOTE = {"int4_g64": "INT4 runs on int8 MFMA: tera-ops against the 5.0 POP/s int8 peak",
              "fp4_b32": "FP4 against the 10.1 PFLOP/s MXFP4 peak",
-             "nvfp4_g16": "NVFP4 operands dequantized exactly to fp16: against the 2.5 PFLOP/s fp16 peak"}
+             "nvfp4_g16": "NVFP4 operands dequantized exactly to fp16 (bf16 inputs and outputs, the pages' compute dtype): against the 2.5 PFLOP/s fp16 peak"}
 SCALE_BYTES_PER_ROW = {"int4_g64": lambda K: (K // 64) * 2, "fp4_b32": lambda K: K // 32,
                        "nvfp4_g16": lambda K: K // 16}
 PEAK_HBM_GBS = 8000.0
@@ -118,6 +118,7 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    IO_DTYPE = {"int4_g64": torch.float16, "fp4_b32": torch.float16, "nvfp4_g16": torch.bfloat16}
     if P.svdq_device_check(0) != 0:
         print("cuda:0 is not a gfx950 (MI355X) device", file=sys.stderr)
         sys.exit(3)
@@ -154,11 +155,13 @@ def main():
     for _ in range(nsets):
         layers = []
         for cfg, r, p in host_sets:
-            L = {"cfg": cfg, "r": r, "X": t(p["X"]), "smooth_inv": t(p["smooth_inv"]),
-                 "lora_down": t(p["lora_down"][:r]) if r else None,
+            # NVFP4 runs in bf16, the compute dtype the pages pair it with; the rest in fp16
+            h = IO_DTYPE[cfg.fmt]
+            L = {"cfg": cfg, "r": r, "X": t(p["X"]).to(h), "smooth_inv": t(p["smooth_inv"]),
+                 "lora_down": t(p["lora_down"][:r]).to(h) if r else None,
                  "w_codes": t(p["w_codes"]), "w_scales": t(p["w_scales"]),
-                 "lora_up": t(np.ascontiguousarray(p["lora_up"][:, :r])) if r else None,
-                 "bias": t(p["bias"])}
+                 "lora_up": t(np.ascontiguousarray(p["lora_up"][:, :r])).to(h) if r else None,
+                 "bias": t(p["bias"]).to(h)}
             sdt = torch.float16 if cfg.fmt == "int4_g64" else torch.uint8
             scols = SCALE_BYTES_PER_ROW[cfg.fmt](cfg.K) // (2 if cfg.fmt == "int4_g64" else 1)
             if cfg.fmt == "nvfp4_g16":
@@ -166,8 +169,8 @@ def main():
                 L["alpha"] = float(np.float32(p["act_gscale"]) * np.float32(p["w_gscale"]))
             L["codes"] = torch.empty((cfg.M, cfg.K // 2), dtype=torch.uint8, device=dev)
             L["scales"] = torch.empty((cfg.M, scols), dtype=sdt, device=dev)
-            L["lora_act"] = torch.empty((cfg.M, r), dtype=torch.float16, device=dev) if r else None
-            L["Y"] = torch.empty((cfg.M, cfg.N), dtype=torch.float16, device=dev)
+            L["lora_act"] = torch.empty((cfg.M, r), dtype=h, device=dev) if r else None
+            L["Y"] = torch.empty((cfg.M, cfg.N), dtype=h, device=dev)
             if cfg.epilogue == "qkv_norm_rope":
                 e = synth.qkv_epilogue_inputs(cfg.M, seed=0)
                 L["qk_norm_w"], L["rope"], L["eps"] = t(e["qk_norm_w"]), t(e["rope"]), e["eps"]
@@ -277,6 +280,11 @@ def main():
             durs[s, k] = e[k].elapsed_time(e[k + 1])
     mean_ms = durs.mean(axis=0)
     med_ms = np.median(durs, axis=0)
+    p10_ms = np.percentile(durs, 10, axis=0)
+    p90_ms = np.percentile(durs, 90, axis=0)
+
+    def spread(k):
+        return {"p10_us": round(p10_ms[k] * 1e3, 2), "p90_us": round(p90_ms[k] * 1e3, 2)}
     ms_per_step = wall * 1e3 / args.steps
 
     total_ops = sum(2.0 * c.M * c.N * c.K for c in cfgs)
@@ -289,13 +297,13 @@ def main():
         (cu, ru, _), (cd, rd, _) = host_sets
         qb, _ = layer_bytes(cu, ru)
         kernels[f"{cu.name}.svdq_quantize_act"] = {
-            "avg_us": round(mean_ms[0] * 1e3, 2), "median_us": round(med_ms[0] * 1e3, 2),
+            "avg_us": round(mean_ms[0] * 1e3, 2), "median_us": round(med_ms[0] * 1e3, 2), **spread(0),
             "alg_bytes": qb, "GB/s": round(qb / (mean_ms[0] * 1e-3) / 1e9, 1)}
         for k, (cfg, r, name) in ((1, (cu, ru, "svdq_gemm_w4a4_mlp")), (2, (cd, rd, "svdq_gemm_w4a4"))):
             ops = 2.0 * cfg.M * cfg.N * cfg.K
             tops = ops / (mean_ms[k] * 1e-3) / 1e12
             kernels[f"{cfg.name}.{name}"] = {
-                "avg_us": round(mean_ms[k] * 1e3, 2), "median_us": round(med_ms[k] * 1e3, 2),
+                "avg_us": round(mean_ms[k] * 1e3, 2), "median_us": round(med_ms[k] * 1e3, 2), **spread(k),
                 "alg_ops": ops, "TOPS": round(tops, 1), "frac_peak": round(tops / PEAK_TOPS[cfg.fmt], 4),
                 "format": cfg.fmt, "rank": r,
                 "note": "GEMM + GELU + the next layer's quantizer, then the fixed-order sum of the "
@@ -309,13 +317,13 @@ def main():
         gemm_ms_sum += gms
         ops = 2.0 * cfg.M * cfg.N * cfg.K
         kernels[f"{cfg.name}.svdq_quantize_act"] = {
-            "avg_us": round(qms * 1e3, 2), "median_us": round(med_ms[2 * li] * 1e3, 2),
+            "avg_us": round(qms * 1e3, 2), "median_us": round(med_ms[2 * li] * 1e3, 2), **spread(2 * li),
             "alg_bytes": qb, "GB/s": round(qb / (qms * 1e-3) / 1e9, 1),
             "frac_hbm": round(qb / (qms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
         tops = ops / (gms * 1e-3) / 1e12
         gname = gemm_name(cfg)
         kernels[f"{cfg.name}.{gname}"] = {
-            "avg_us": round(gms * 1e3, 2), "median_us": round(med_ms[2 * li + 1] * 1e3, 2),
+            "avg_us": round(gms * 1e3, 2), "median_us": round(med_ms[2 * li + 1] * 1e3, 2), **spread(2 * li + 1),
             "alg_ops": ops, "lowrank_ops": 2.0 * cfg.M * cfg.N * r + 2.0 * cfg.M * cfg.K * r,
             "TOPS": round(tops, 1), "frac_peak": round(tops / PEAK_TOPS[cfg.fmt], 4),
             "format": cfg.fmt, "epilogue": cfg.epilogue, "rank": r}
@@ -324,7 +332,7 @@ def main():
     gvb = gemv_bytes(gcfg)
     gvms = mean_ms[-1]
     kernels["gemv.awq_gemv_w4a16"] = {
-        "avg_us": round(gvms * 1e3, 2), "median_us": round(med_ms[-1] * 1e3, 2),
+        "avg_us": round(gvms * 1e3, 2), "median_us": round(med_ms[-1] * 1e3, 2), **spread(nk - 1),
         "alg_bytes": gvb, "GB/s": round(gvb / (gvms * 1e-3) / 1e9, 1),
         "frac_hbm": round(gvb / (gvms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
 

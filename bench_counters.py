@@ -13,6 +13,11 @@ by those factors.
 Writes profiles/traffic_<workload>.json (read by bench.py, which reports the
 figure only while the GEMM source hash recorded here still matches) and prints
 a short text summary.
+
+With --util instead: the counter_collection.csv of one
+`rocprofv3 --pmc MfmaUtil VALUBusy SQ_INSTS_VALU SQ_INSTS_MFMA` pass, summarised
+per library kernel into profiles/util_<workload>.md (MFMA busy %, VALU busy %,
+instruction counts per launch).
 """
 from __future__ import annotations
 
@@ -51,11 +56,17 @@ def per_dispatch(path: str, counter: str):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", required=True)
-    ap.add_argument("--fetch", required=True, help="counter_collection.csv of the FETCH_SIZE pass")
-    ap.add_argument("--write", required=True, help="counter_collection.csv of the WRITE_SIZE pass")
-    ap.add_argument("--calib-mib", type=int, required=True)
+    ap.add_argument("--fetch", help="counter_collection.csv of the FETCH_SIZE pass")
+    ap.add_argument("--write", help="counter_collection.csv of the WRITE_SIZE pass")
+    ap.add_argument("--calib-mib", type=int)
+    ap.add_argument("--util", help="counter_collection.csv of the MfmaUtil / VALUBusy pass")
     ap.add_argument("--command", default="", help="the profiled command, recorded verbatim")
     args = ap.parse_args()
+    if args.util:
+        util(args)
+        return
+    if not (args.fetch and args.write and args.calib_mib):
+        raise SystemExit("--fetch, --write and --calib-mib are required (or --util)")
 
     fetch = per_dispatch(args.fetch, "FETCH_SIZE")
     write = per_dispatch(args.write, "WRITE_SIZE")
@@ -103,6 +114,37 @@ def main():
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     with open(os.path.join(ROOT, "profiles", f"traffic_{args.workload}.json"), "w") as f:
         json.dump(out, f, indent=1)
+    print("\n".join(lines))
+
+
+UTIL_COUNTERS = ("MfmaUtil", "VALUBusy", "SQ_INSTS_MFMA", "SQ_INSTS_VALU")
+
+
+def util(args):
+    """Per library kernel: the average over its launches of each counter."""
+    acc = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in csv.DictReader(open(args.util)):
+        if r["Counter_Name"] in UTIL_COUNTERS:
+            acc[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    lines = [f"# MFMA and VALU utilisation per launch, workload {args.workload}", "",
+             f"command: {args.command}", "",
+             "MfmaUtil = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMDs); VALUBusy = "
+             "SQ_ACTIVE_INST_VALU / (CUs x GRBM_GUI_ACTIVE) (rocprofv3's derived counters, percent of "
+             "the dispatch's active time); instruction counts are per launch, all waves.", "",
+             "| kernel | launches | MFMA busy % | VALU busy % | MFMA instr | VALU instr | VALU per MFMA |",
+             "|---|---|---|---|---|---|---|"]
+    for name, c in acc.items():
+        short = name.split("(")[0].replace("void ", "")
+        if not short.startswith("svdq::"):
+            continue
+        mean = {k: (sum(v) / len(v) if v else 0.0) for k, v in c.items()}
+        nm, nv = mean.get("SQ_INSTS_MFMA", 0.0), mean.get("SQ_INSTS_VALU", 0.0)
+        ratio = f"{nv / nm:.1f}" if nm else "-"
+        lines.append(f"| `{short}` | {len(c.get('MfmaUtil', []))} | {mean.get('MfmaUtil', 0.0):.1f} | "
+                     f"{mean.get('VALUBusy', 0.0):.1f} | {nm:.0f} | {nv:.0f} | {ratio} |")
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", f"util_{args.workload}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
 
