@@ -7,7 +7,7 @@
 // Lite to Diffusers", section "Why W4A4 differs from weight-only backends").
 //
 // Tiling: a workgroup of 4 waves (2 x 2) owns a BM x BN output tile, each wave
-// (32 WM) x (32 WN) built from 32 x 32 MFMA blocks. The K loop walks steps of
+// (32 WM) x (32 WN): 16 x 16 MFMA blocks for INT4, 32 x 32 for FP4. The K loop walks steps of
 // 128 codes (64 packed bytes per row). Each step (A codes, B codes and both
 // operands' scale words) is brought into an LDS ring of STAGES buffers by
 // LDS-DMA loads (global_load_lds_dwordx4 / _dword): no register staging, and
@@ -23,16 +23,17 @@
 // Accumulators start from the low-rank product: lora_act (fp16) times lora_up
 // on fp16 MFMAs (16 ranks per instruction), loads for 32 ranks in one batch.
 //
-// INT4_G64: each lane reads 16 packed bytes (32 codes) per 32-row block and
-// group; nibbles become int8 bytes holding 16 q with two ALU ops per word
-// (hi = w & 0xF0F0F0F0, lo = (w << 4) & 0xF0F0F0F0), so the int32 result is
-// 256 sum q_x q_w exactly. Two v_mfma_i32_32x32x32_i8 give one group's
-// partial P. The int32 accumulation starts from the bit pattern of 1.5 * 2^23,
-// so the result read as fp32 is exactly 1.5*2^23 + 256 P; one fma with the
-// fp16 s_w (read as is by v_fma_mix) and the exact constant -1.5*2^23 s_w
-// yields fl(256 P s_w) = 256 fl(P s_w) with no int-to-float convert, and a
-// second fma adds s_x times that to the fp32 accumulator: two VALU ops per
-// output and group. The accumulators therefore hold 256 times the sum (the
+// INT4_G64: each lane reads 8 packed bytes (16 codes) per 16-row block and
+// group; nibbles become int8 bytes holding 16 q (hi = w & 0xF0F0F0F0,
+// lo = (w << 4) & 0xF0F0F0F0), so the int32 result is 256 sum q_x q_w exactly.
+// One v_mfma_i32_16x16x64_i8 gives a 16 x 16 block's partial P of one group.
+// The int32 accumulation starts from the bit pattern of 1.5 * 2^23, so the
+// result read as fp32 is exactly 1.5*2^23 + 256 P; one fma with s_w and the
+// exact constant -1.5*2^23 s_w yields fl(256 P s_w) = 256 fl(P s_w) with no
+// int-to-float convert, and a second fma adds s_x times that to the fp32
+// accumulator: two VALU ops per output and group, plain fp32 fmas on scales
+// converted once per step (gfx950 issues v_fma_mix with a 16-bit operand
+// slower than v_fma_f32). The accumulators therefore hold 256 times the sum (the
 // low-rank start is scaled to match); the epilogue's multiply by 2^-8 is exact.
 // A and B use the same permutation of k inside the instruction, which a dot
 // product does not see.
