@@ -633,8 +633,16 @@ static hipError_t launch_gemm_io(int fmt, int M, int N, int K, int r, const uint
   const ChainEpilogue ce = chain ? *chain : ChainEpilogue{nullptr, nullptr, 0, nullptr, nullptr, nullptr};
 #define SVDQ_GO(F, E, WM_, WN_, ST_) \
   return launch_cfg<IO, F, E, WM_, WN_, ST_>(M, N, K, r, ac, as, la, wc, ws, lu, bias, Y, st, qe, ce)
-  if (epi == 2) {   // fused QKV epilogue: INT4 only
+  // INT4 tile size by how many 128 x 128 tiles the problem has: with fewer than
+  // one per CU, 64 x 64 tiles; with fewer than two, 64 x 128; else 128 x 128 (up
+  // to three workgroups per CU run at once). The arithmetic of an output is the
+  // same in every shape. (The 4-bit float path keeps 128 x 128: its smaller
+  // tiles measured slower.)
+  const int t128 = ((M + 127) / 128) * (N / 128);
+  const int small = t128 < 256 ? 2 : t128 < 512 ? 1 : 0;
+  if (epi == 2) {   // fused QKV epilogue: INT4 only, one 128-channel head per tile
     if (fmt != 0 || !qkv) return hipErrorInvalidValue;
+    if (small) SVDQ_GO(0, 2, 1, 2, 3);
     SVDQ_GO(0, 2, 2, 2, 3);
   }
   if (epi == 3) {   // fused MLP chain: INT4 only
@@ -642,6 +650,12 @@ static hipError_t launch_gemm_io(int fmt, int M, int N, int K, int r, const uint
     SVDQ_GO(0, 3, 2, 2, 3);
   }
   if (fmt == 0) {
+    if (small == 2) {
+      if (epi == 0) SVDQ_GO(0, 0, 1, 1, 3); else SVDQ_GO(0, 1, 1, 1, 3);
+    }
+    if (small == 1) {
+      if (epi == 0) SVDQ_GO(0, 0, 1, 2, 3); else SVDQ_GO(0, 1, 1, 2, 3);
+    }
     if (epi == 0) SVDQ_GO(0, 0, 2, 2, 3); else SVDQ_GO(0, 1, 2, 2, 3);
   } else {
     const hipError_t e = launch_gemm_fp4_big(IO, M, N, K, r, ac, as, la, wc, ws, lu, bias, epi, Y, st);

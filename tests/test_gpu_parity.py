@@ -223,6 +223,31 @@ def test_gemm_full_size_sampled(P, name):
     assert np.isfinite(y).all()
 
 
+@pytest.mark.parametrize("fmt", ["int4_g64", "fp4_b32"])
+@pytest.mark.parametrize("M,N,epi", [
+    (2000, 3072, "none"),        # 16 x 24 tiles of 128: the INT4 path's 64 x 128 tiles, ragged M
+    (2048, 3072, "gelu_tanh"),   # same band, whole tiles, GELU
+    (1000, 1536, "none"),        # 8 x 12 tiles of 128: 64 x 64 tiles, ragged M
+])
+def test_gemm_tile_bands(P, fmt, M, N, epi):
+    """The GEMM picks its INT4 tile size from the number of 128 x 128 tiles;
+    each band against the oracle on sampled rows (first and last included)."""
+    cfg = synth.LayerConfig(f"band_{M}_{N}", 52, M, 512, N, 32, fmt, epi, "normal", 0.005, 30.0)
+    p = synth.random_quantized_layer(cfg, seed=3)
+    codes_u, packed, scales = oracle.quantize_act_ref(p["X"], p["smooth_inv"], fmt)
+    la = oracle.lora_act_ref(p["X"], p["lora_down"]).astype(np.float16)
+    Y = P.svdq_gemm_w4a4(dev(packed), dev(scales), dev(la), dev(p["w_codes"]), dev(p["w_scales"]),
+                         dev(p["lora_up"]), dev(p["bias"]), fmt, epi)
+    y = host(Y)
+    rng = np.random.default_rng(12)
+    rows = np.unique(np.concatenate([rng.choice(M, 48, replace=False), [0, 63, 64, 127, 128, M - 1]]))
+    wu = oracle.unpack_nibbles(p["w_codes"], signed=(fmt == "int4_g64"))
+    y_ref = oracle.gemm_ref(codes_u, scales, la, wu, p["w_scales"], p["lora_up"], p["bias"], fmt, epi,
+                            rows=rows)
+    assert rel_l2(y[rows], y_ref) <= Y_TOL
+    assert np.isfinite(y).all()
+
+
 # ------------------------------------------------ fused QKV epilogue --
 
 def _qkv_case(P, cfg, seed, rows=None):
