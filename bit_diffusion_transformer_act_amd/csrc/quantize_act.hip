@@ -56,12 +56,23 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
   return c < 8u ? (float)c * 0.001953125f : __uint_as_float((((c >> 3) + 120u) << 23) | ((c & 7u) << 20));
 }
 
-template <int IO, int FMT, int NCB, int WAVES, bool SLDS>
+// gridDim.y = S > 1 splits K: workgroup (b, y) takes rows 16 b .. +16 over the
+// y-th of S slices of whole 64-channel steps. Then
+//  - LORA_ONLY: the slice's low-rank partial sums (fp32) go to the tail of each
+//    row of `codes` (S r 4 bytes before the row's end, slice y at y r 4), no
+//    codes or scales;
+//  - NCB = 0: codes and scales of the slice; with rq > 0, the workgroup of the
+//    last slice first adds the S partials of its rows in slice order and stores
+//    lora_act (rq wide), before it writes the codes that overwrite them (the
+//    tail lies inside its own slice, and the partials were written by an
+//    earlier launch on the same stream).
+// LORA_ONLY with S = 1: lora_act alone, in the fused kernel's summation order.
+template <int IO, int FMT, int NCB, int WAVES, bool SLDS, bool LORA_ONLY>
 __global__ __launch_bounds__(64 * WAVES)
 void quantize_act_kernel(const uint16_t* __restrict__ X, const float* __restrict__ smooth_inv,
                          const uint16_t* __restrict__ lora_down, uint8_t* __restrict__ codes,
                          void* __restrict__ scales, uint16_t* __restrict__ lora_act,
-                         int M, int K, float gs, float gs6) {
+                         int M, int K, float gs, float gs6, int rq) {
 #pragma clang fp contract(off)
   // LDS: two round buffers (codes, then scales, of 16 rows x WAVES steps),
   // [WAVES][16 rows][16 * NCB] low-rank partials, then smooth_inv[K] if SLDS
@@ -81,7 +92,11 @@ void quantize_act_kernel(const uint16_t* __restrict__ X, const float* __restrict
   const int row = m0 + (lane & 15);
   const int q4 = lane >> 4;
   const bool row_ok = row < M;
-  const int steps = K >> 6;
+  // this workgroup's slice of the 64-channel steps (all of them when gridDim.y == 1)
+  const int steps_all = K >> 6;
+  const int sps = (steps_all + (int)gridDim.y - 1) / (int)gridDim.y;
+  const int sbeg = (int)blockIdx.y * sps;
+  const int steps = max(min(sps, steps_all - sbeg), 0);
   // rows past M read row M - 1 (never stored; rows are independent in the
   // MFMA and in the amax groups). An unconditional load matters: a select on
   // the load's destination would make every prefetch wait for the previous one.
@@ -90,7 +105,7 @@ void quantize_act_kernel(const uint16_t* __restrict__ X, const float* __restrict
   // smooth_inv into LDS; called after the first loads of X are out, so the two
   // latencies overlap
   auto stage_si = [&]() {
-    if constexpr (SLDS) {
+    if constexpr (SLDS && !LORA_ONLY) {
       for (int i = threadIdx.x * 4; i < K; i += 64 * WAVES * 4)
         *reinterpret_cast<float4*>(s_si + i) = *reinterpret_cast<const float4*>(smooth_inv + i);
       __syncthreads();
@@ -100,6 +115,26 @@ void quantize_act_kernel(const uint16_t* __restrict__ X, const float* __restrict
   v4f lacc[NL];
 #pragma unroll
   for (int c = 0; c < NL; ++c) lacc[c] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // NCB = 0, rq > 0, last slice: lora_act from the partials at the rows' tails
+  auto lora_from_partials = [&]() {
+    if constexpr (NCB == 0 && !LORA_ONLY) {
+      if (rq > 0 && blockIdx.y == gridDim.y - 1) {
+        const int S = (int)gridDim.y;
+        for (int t = threadIdx.x; t < 16 * rq; t += blockDim.x) {
+          const int rr = t / rq, cc = t - rr * rq;
+          if (m0 + rr < M) {
+            const float* pp = reinterpret_cast<const float*>(codes + (size_t)(m0 + rr) * (K >> 1) + (K >> 1) -
+                                                             (size_t)S * rq * 4);
+            float sum = 0.f;
+            for (int y = 0; y < S; ++y) sum += pp[y * rq + cc];
+            lora_act[(size_t)(m0 + rr) * rq + cc] = Io<IO>::from_f(sum);
+          }
+        }
+        __syncthreads();   // every partial is read before this workgroup writes codes
+      }
+    }
+  };
 
   // One step's loads: this lane's two 8-channel chunks of X and the matching
   // lora_down operands. Register sets rotate so that the loads of the next one
@@ -113,7 +148,7 @@ void quantize_act_kernel(const uint16_t* __restrict__ X, const float* __restrict
   // vmcnt bookkeeping unsure how many are in flight, and every use would then
   // wait for all of them.
   auto load = [&](Step& d, int s) {
-    const int k0 = min(s, steps - 1) * 64 + q4 * 8;
+    const int k0 = (sbeg + min(s, steps - 1)) * 64 + q4 * 8;
     d.xa = *reinterpret_cast<const uint4*>(X + xrow + k0);
     d.xb = *reinterpret_cast<const uint4*>(X + xrow + k0 + 32);
     if constexpr (NCB > 0) {
@@ -184,7 +219,7 @@ void quantize_act_kernel(const uint16_t* __restrict__ X, const float* __restrict
 
   // process step s into round buffer rb (its column is this wave's index)
   auto process = [&](const Step& d, int s, uint8_t* rb) {
-    const int k0 = s * 64 + q4 * 8;
+    const int k0 = (sbeg + s) * 64 + q4 * 8;
     if constexpr (NCB > 0) {
 #pragma unroll
       for (int c = 0; c < NCB; ++c) {
@@ -192,6 +227,7 @@ void quantize_act_kernel(const uint16_t* __restrict__ X, const float* __restrict
         lacc[c] = Io<IO>::mma16x16x32(d.xb, d.lb[c][1], lacc[c]);
       }
     }
+    if constexpr (LORA_ONLY) return;
     // smoothing: x_hat = fl32(fp32(x) * smooth_inv), a plain IEEE multiply.
     // xh[0..7]: channels k0 .. k0+7, xh[8..15]: channels k0+32 .. k0+39.
     float xh[16];
@@ -313,13 +349,14 @@ void quantize_act_kernel(const uint16_t* __restrict__ X, const float* __restrict
     uint8_t* rb = rbuf + (p & 1) * RBUF;
     const int s = p * WAVES + wave;
     if (s < steps) process(d, s, rb);
+    if constexpr (LORA_ONLY) return;   // nothing to write out, no round barrier
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS writes are done
     __builtin_amdgcn_s_barrier();
     const int vs = min(WAVES, steps - p * WAVES);   // steps in this round
     for (int c = threadIdx.x; c < 16 * 2 * WAVES; c += 64 * WAVES) {
       const int rl = c / (2 * WAVES), ch = c - rl * (2 * WAVES);
       if (ch < 2 * vs && m0 + rl < M)
-        *reinterpret_cast<uint4*>(codes + (size_t)(m0 + rl) * (K >> 1) + p * WAVES * 32 + ch * 16) =
+        *reinterpret_cast<uint4*>(codes + (size_t)(m0 + rl) * (K >> 1) + (size_t)(sbeg + p * WAVES) * 32 + ch * 16) =
             *reinterpret_cast<const uint4*>(rb + rl * CROW + ch * 16);
     }
     for (int c = threadIdx.x; c < 16 * WAVES; c += 64 * WAVES) {
@@ -327,7 +364,7 @@ void quantize_act_kernel(const uint16_t* __restrict__ X, const float* __restrict
       if (j < vs && m0 + rl < M) {
         // a row holds SB scale bytes per 64-channel step
         uint8_t* dst = reinterpret_cast<uint8_t*>(scales) + (size_t)(m0 + rl) * (size_t)((K >> 6) * SB) +
-                       (size_t)(p * WAVES + j) * SB;
+                       (size_t)(sbeg + p * WAVES + j) * SB;
         if constexpr (SB == 4)
           *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(rb + 16 * CROW + rl * SROW + j * 4);
         else
@@ -346,6 +383,7 @@ void quantize_act_kernel(const uint16_t* __restrict__ X, const float* __restrict
     load(d0, wave);
     load(d1, wave + WAVES);
     stage_si();
+    lora_from_partials();
     for (int p = 0; p < nrounds; p += 3) {
       load(d2, (p + 2) * WAVES + wave);
       round(d0, p);
@@ -360,6 +398,7 @@ void quantize_act_kernel(const uint16_t* __restrict__ X, const float* __restrict
     Step d0, d1;
     load(d0, wave);
     stage_si();
+    lora_from_partials();
     for (int p = 0; p < nrounds; p += 2) {
       load(d1, (p + 1) * WAVES + wave);
       round(d0, p);
@@ -382,40 +421,49 @@ void quantize_act_kernel(const uint16_t* __restrict__ X, const float* __restrict
       float sum = 0.f;
 #pragma unroll
       for (int w = 0; w < WAVES; ++w) sum += red[(w * 16 + rr) * R + cc];
-      if (m0 + rr < M) lora_act[(size_t)(m0 + rr) * R + cc] = Io<IO>::from_f(sum);
+      if (m0 + rr < M) {
+        if (gridDim.y > 1)   // the slice's partial, at the row's tail in codes
+          reinterpret_cast<float*>(codes + (size_t)(m0 + rr) * (K >> 1) + (K >> 1) -
+                                   (size_t)gridDim.y * R * 4)[blockIdx.y * R + cc] = sum;
+        else
+          lora_act[(size_t)(m0 + rr) * R + cc] = Io<IO>::from_f(sum);
+      }
     }
   }
 }
 
-template <int IO, int FMT, int NCB, int WAVES, bool SLDS>
-static hipError_t launch_qws(int M, int K, const void* X, const float* si, const void* ld,
-                             uint8_t* codes, void* scales, void* la, float gs, hipStream_t st) {
-  const dim3 grid((M + 15) / 16), block(64 * WAVES);
+template <int IO, int FMT, int NCB, int WAVES, bool SLDS, bool LO>
+static hipError_t launch_qws(int M, int K, int slices, const void* X, const float* si, const void* ld,
+                             uint8_t* codes, void* scales, void* la, float gs, hipStream_t st, int rq) {
+  const dim3 grid((M + 15) / 16, slices), block(64 * WAVES);
   const size_t lds = quant_lds_bytes<WAVES>(NCB) + (SLDS ? (size_t)K * sizeof(float) : 0);
   if (lds > 65536) {
     // the attribute is raised once per instantiation to the largest size it may need
     static std::atomic<int> raised{0};
     if (!raised.load(std::memory_order_acquire)) {
       const hipError_t e = hipFuncSetAttribute(
-          reinterpret_cast<const void*>(&quantize_act_kernel<IO, FMT, NCB, WAVES, SLDS>),
+          reinterpret_cast<const void*>(&quantize_act_kernel<IO, FMT, NCB, WAVES, SLDS, LO>),
           hipFuncAttributeMaxDynamicSharedMemorySize, kQuantLdsMax);
       if (e != hipSuccess) return e;
       raised.store(1, std::memory_order_release);
     }
   }
-  hipLaunchKernelGGL((quantize_act_kernel<IO, FMT, NCB, WAVES, SLDS>), grid, block, lds, st,
+  hipLaunchKernelGGL((quantize_act_kernel<IO, FMT, NCB, WAVES, SLDS, LO>), grid, block, lds, st,
                      (const uint16_t*)X, si, (const uint16_t*)ld, codes, scales, (uint16_t*)la, M, K, gs,
-                     6.0f * gs);
+                     6.0f * gs, rq);
   return hipGetLastError();
 }
 
-// smooth_inv goes to LDS when it fits beside the low-rank partials
-template <int IO, int FMT, int NCB, int WAVES>
-static hipError_t launch_qw(int M, int K, const void* X, const float* si, const void* ld,
-                            uint8_t* codes, void* scales, void* la, float gs, hipStream_t st) {
-  if (quant_lds_bytes<WAVES>(NCB) + (size_t)K * sizeof(float) <= (size_t)kQuantLdsMax)
-    return launch_qws<IO, FMT, NCB, WAVES, true>(M, K, X, si, ld, codes, scales, la, gs, st);
-  return launch_qws<IO, FMT, NCB, WAVES, false>(M, K, X, si, ld, codes, scales, la, gs, st);
+// smooth_inv goes to LDS when it fits beside the low-rank partials (the
+// low-rank-only pass does not read it)
+template <int IO, int FMT, int NCB, int WAVES, bool LO>
+static hipError_t launch_qw(int M, int K, int slices, const void* X, const float* si, const void* ld,
+                            uint8_t* codes, void* scales, void* la, float gs, hipStream_t st, int rq) {
+  if constexpr (!LO) {
+    if (quant_lds_bytes<WAVES>(NCB) + (size_t)K * sizeof(float) <= (size_t)kQuantLdsMax)
+      return launch_qws<IO, FMT, NCB, WAVES, true, LO>(M, K, slices, X, si, ld, codes, scales, la, gs, st, rq);
+  }
+  return launch_qws<IO, FMT, NCB, WAVES, false, LO>(M, K, slices, X, si, ld, codes, scales, la, gs, st, rq);
 }
 
 // 16 rows per workgroup. For ranks up to 32, 16 waves (4 per SIMD): more waves
@@ -424,31 +472,73 @@ static hipError_t launch_qw(int M, int K, const void* X, const float* si, const 
 // 48 to 96, 8 waves (the ring's lora_down operands need the registers); for
 // ranks of 112 and more, 4 waves (the lora_down operands of a step take
 // 8 * r / 16 VGPRs per set).
-template <int IO, int FMT, int NCB>
-static hipError_t launch_q(int M, int K, const void* X, const float* si, const void* ld,
-                           uint8_t* codes, void* scales, void* la, float gs, hipStream_t st) {
+template <int IO, int FMT, int NCB, bool LO>
+static hipError_t launch_q(int M, int K, int slices, const void* X, const float* si, const void* ld,
+                           uint8_t* codes, void* scales, void* la, float gs, hipStream_t st, int rq = 0) {
   if constexpr (NCB >= 7) {
-    return launch_qw<IO, FMT, NCB, 4>(M, K, X, si, ld, codes, scales, la, gs, st);
+    return launch_qw<IO, FMT, NCB, 4, LO>(M, K, slices, X, si, ld, codes, scales, la, gs, st, rq);
   } else if constexpr (NCB > 2) {
-    return launch_qw<IO, FMT, NCB, 8>(M, K, X, si, ld, codes, scales, la, gs, st);
+    return launch_qw<IO, FMT, NCB, 8, LO>(M, K, slices, X, si, ld, codes, scales, la, gs, st, rq);
   } else {
-    return launch_qw<IO, FMT, NCB, 16>(M, K, X, si, ld, codes, scales, la, gs, st);
+    return launch_qw<IO, FMT, NCB, 16, LO>(M, K, slices, X, si, ld, codes, scales, la, gs, st, rq);
+  }
+}
+
+// the low-rank down-projection alone: over all of K into lora_act (S = 1, the
+// fused kernel's summation order), or per K slice into the tails of the code
+// rows (S > 1)
+template <int IO>
+static hipError_t launch_lora_only(int M, int K, int r, int S, const void* X, const void* ld, uint8_t* codes,
+                                   void* la, hipStream_t st) {
+  switch (r / 16) {
+    case 1: return launch_q<IO, 0, 1, true>(M, K, S, X, nullptr, ld, codes, nullptr, la, 1.0f, st);
+    case 2: return launch_q<IO, 0, 2, true>(M, K, S, X, nullptr, ld, codes, nullptr, la, 1.0f, st);
+    case 3: return launch_q<IO, 0, 3, true>(M, K, S, X, nullptr, ld, codes, nullptr, la, 1.0f, st);
+    case 4: return launch_q<IO, 0, 4, true>(M, K, S, X, nullptr, ld, codes, nullptr, la, 1.0f, st);
+    case 5: return launch_q<IO, 0, 5, true>(M, K, S, X, nullptr, ld, codes, nullptr, la, 1.0f, st);
+    case 6: return launch_q<IO, 0, 6, true>(M, K, S, X, nullptr, ld, codes, nullptr, la, 1.0f, st);
+    case 7: return launch_q<IO, 0, 7, true>(M, K, S, X, nullptr, ld, codes, nullptr, la, 1.0f, st);
+    default: return launch_q<IO, 0, 8, true>(M, K, S, X, nullptr, ld, codes, nullptr, la, 1.0f, st);
   }
 }
 
 template <int IO, int FMT>
 static hipError_t launch_q_r(int M, int K, int r, const void* X, const float* si, const void* ld,
                              uint8_t* codes, void* scales, void* la, float gs, hipStream_t st) {
+  // A workgroup walks all of K for its 16 rows, so with few row blocks most CUs
+  // would idle. Then K is cut into S slices of whole steps, S doubling while the
+  // row blocks fill fewer than 256 workgroups and each slice keeps at least 8
+  // steps (32 with a low-rank pass): a first launch leaves each slice's low-rank partial sums in the
+  // tails of the code rows, a second quantizes the slices (codes and scales are
+  // independent per group), its last-slice workgroups summing the partials into
+  // lora_act before their codes overwrite them. S stays below the point where
+  // the partials (S r 4 bytes per row) would not fit in the last slice's codes.
+  const int nb = (M + 15) / 16, steps = K >> 6;
+  int S = 1;
+  while (nb * S < 256 && S < 8 && steps >= 16 * S) {
+    const int S2 = 2 * S, last = steps - (S2 - 1) * ((steps + S2 - 1) / S2);
+    // with a low-rank pass, slices of fewer than 32 steps lose to the fused
+    // kernel (two short launches: M1024 K3072 r32 13 -> 18 us, K12288 43 -> 26 us)
+    if (r > 0 && (steps < 32 * S2 || S2 * r * 4 > last * 32)) break;
+    S = S2;
+  }
+  if (S > 1) {
+    if (r > 0) {
+      const hipError_t e = launch_lora_only<IO>(M, K, r, S, X, ld, codes, nullptr, st);
+      if (e != hipSuccess) return e;
+    }
+    return launch_q<IO, FMT, 0, false>(M, K, S, X, si, ld, codes, scales, la, gs, st, r);
+  }
   switch (r / 16) {
-    case 0: return launch_q<IO, FMT, 0>(M, K, X, si, ld, codes, scales, la, gs, st);
-    case 1: return launch_q<IO, FMT, 1>(M, K, X, si, ld, codes, scales, la, gs, st);
-    case 2: return launch_q<IO, FMT, 2>(M, K, X, si, ld, codes, scales, la, gs, st);
-    case 3: return launch_q<IO, FMT, 3>(M, K, X, si, ld, codes, scales, la, gs, st);
-    case 4: return launch_q<IO, FMT, 4>(M, K, X, si, ld, codes, scales, la, gs, st);
-    case 5: return launch_q<IO, FMT, 5>(M, K, X, si, ld, codes, scales, la, gs, st);
-    case 6: return launch_q<IO, FMT, 6>(M, K, X, si, ld, codes, scales, la, gs, st);
-    case 7: return launch_q<IO, FMT, 7>(M, K, X, si, ld, codes, scales, la, gs, st);
-    default: return launch_q<IO, FMT, 8>(M, K, X, si, ld, codes, scales, la, gs, st);
+    case 0: return launch_q<IO, FMT, 0, false>(M, K, 1, X, si, ld, codes, scales, la, gs, st);
+    case 1: return launch_q<IO, FMT, 1, false>(M, K, 1, X, si, ld, codes, scales, la, gs, st);
+    case 2: return launch_q<IO, FMT, 2, false>(M, K, 1, X, si, ld, codes, scales, la, gs, st);
+    case 3: return launch_q<IO, FMT, 3, false>(M, K, 1, X, si, ld, codes, scales, la, gs, st);
+    case 4: return launch_q<IO, FMT, 4, false>(M, K, 1, X, si, ld, codes, scales, la, gs, st);
+    case 5: return launch_q<IO, FMT, 5, false>(M, K, 1, X, si, ld, codes, scales, la, gs, st);
+    case 6: return launch_q<IO, FMT, 6, false>(M, K, 1, X, si, ld, codes, scales, la, gs, st);
+    case 7: return launch_q<IO, FMT, 7, false>(M, K, 1, X, si, ld, codes, scales, la, gs, st);
+    default: return launch_q<IO, FMT, 8, false>(M, K, 1, X, si, ld, codes, scales, la, gs, st);
   }
 }
 

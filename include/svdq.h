@@ -126,7 +126,10 @@ int svdq_version(void);
  *   X           h16 [M][K].
  *   smooth_inv  fp32 [K], the smoothing multiplier (1/lambda).
  *   lora_down   h16 [r][K] (carries diag(smooth_inv)); may be NULL iff r == 0.
- *   act_codes   out, u8 [M][K/2].
+ *   act_codes   out, u8 [M][K/2]. With few rows and a long K the call splits K
+ *               across workgroups and first parks fp32 low-rank partial sums in
+ *               the tails of these rows (scratch owned by the call until its
+ *               work on `stream` completes; the final content is the codes).
  *   act_scales  out, fp16 [M][K/64] (INT4_G64) or u8 [M][K/32] (FP4_E2M1_B32).
  *   lora_act    out, h16 [M][r]; may be NULL iff r == 0.
  *   stream      hipStream_t.
