@@ -579,22 +579,46 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restr
 }
 
 // lora_act[m][j] = h16( sum_t partial[t][m][j] ), summed in the order t = 0, 1, ...
+// Each thread takes 4 consecutive elements (16-byte loads) and keeps the loads
+// of 8 tiles in flight ahead of the adds (the order of the adds is unchanged).
 template <int IO>
 __global__ __launch_bounds__(256)
 void chain_reduce_kernel(const float* __restrict__ partial, uint16_t* __restrict__ lora_act, int M, int r,
                          int tiles) {
-  const size_t n = (size_t)M * r;
-  for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (size_t)gridDim.x * 256) {
-    float s = 0.f;
-    for (int t = 0; t < tiles; ++t) s += partial[(size_t)t * n + e];
-    lora_act[e] = Io<IO>::from_f(s);
+  const size_t n = (size_t)M * r;   // a multiple of 16 (r % 16 == 0)
+  for (size_t e = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4; e < n; e += (size_t)gridDim.x * 256 * 4) {
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    int t = 0;
+    for (; t + 8 <= tiles; t += 8) {
+      float4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const float4*>(partial + (size_t)(t + u) * n + e);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        s.x += v[u].x;
+        s.y += v[u].y;
+        s.z += v[u].z;
+        s.w += v[u].w;
+      }
+    }
+    for (; t < tiles; ++t) {
+      const float4 v = *reinterpret_cast<const float4*>(partial + (size_t)t * n + e);
+      s.x += v.x;
+      s.y += v.y;
+      s.z += v.z;
+      s.w += v.w;
+    }
+    lora_act[e] = Io<IO>::from_f(s.x);
+    lora_act[e + 1] = Io<IO>::from_f(s.y);
+    lora_act[e + 2] = Io<IO>::from_f(s.z);
+    lora_act[e + 3] = Io<IO>::from_f(s.w);
   }
 }
 
 hipError_t launch_chain_reduce(int io, int M, int r, int tiles, const float* partial, void* lora_act,
                                hipStream_t st) {
-  const size_t n = (size_t)M * r;
-  const int grid = (int)std::min<size_t>((n + 255) / 256, 2048);
+  const size_t n4 = (size_t)M * r / 4;
+  const int grid = (int)std::min<size_t>((n4 + 255) / 256, 2048);
   if (io == 1)
     hipLaunchKernelGGL(chain_reduce_kernel<1>, dim3(grid), dim3(256), 0, st, partial, (uint16_t*)lora_act, M, r, tiles);
   else
