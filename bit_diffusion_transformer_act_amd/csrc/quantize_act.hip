@@ -8,7 +8,8 @@
 // section "Why W4A4 differs from weight-only backends").
 //
 // Work split (gfx950, wave64): a workgroup of W waves (4, 8 or 16) owns 16 rows
-// of X and all of K; wave w handles 64-wide K steps w, w+W, w+2W, ..., with the
+// of X and all of K (or, with few rows and a long K, one slice of K: see
+// launch_q_r); wave w handles 64-wide K steps w, w+W, w+2W, ..., with the
 // loads of its next one or two steps in flight. In a step, lane l holds row
 // (l % 16) and two 8-channel chunks: q*8 .. +8 and 32 + q*8 .. +8 of the step
 // (q = l / 16), so each load instruction reads 16 rows x 64 contiguous bytes
@@ -22,8 +23,8 @@
 //     shuffle reduction.
 // smooth_inv is staged in LDS once per workgroup (a global-load variant serves
 // K beyond the LDS budget). Partial low-rank sums of the W waves meet in LDS
-// and are added in a fixed order, so lora_act (stored as fp16) is
-// deterministic.
+// and are added in a fixed order (then the slices', in slice order, when K is
+// split), so lora_act (stored in the 16-bit type) is deterministic.
 #include <atomic>
 
 #include "common.hpp"
