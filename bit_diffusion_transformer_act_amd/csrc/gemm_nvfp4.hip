@@ -340,7 +340,10 @@ template <int IO>
 static hipError_t launch_nv_io(int M, int N, int K, int r, const uint8_t* ac, const uint8_t* as,
                                const void* la, const uint8_t* wc, const uint8_t* ws, const void* lu,
                                const void* bias, float alpha, int epi, void* Y, hipStream_t st) {
-  if (N % 256 == 0) {
+  // 256 x 256 tiles unless that grid would fill at most half the CUs: then
+  // 256 x 128 tiles, twice as many in one round (M1024 K12288 N3072: 48 tiles,
+  // 243 -> 159 us; with 144 or 192 tiles the second round costs more, 77 -> 97 us)
+  if (N % 256 == 0 && ((M + 255) / 256) * (N / 256) > 128) {
     return epi ? launch_nv<IO, 1, 256>(M, N, K, r, ac, as, la, wc, ws, lu, bias, alpha, Y, st)
                : launch_nv<IO, 0, 256>(M, N, K, r, ac, as, la, wc, ws, lu, bias, alpha, Y, st);
   }

@@ -105,7 +105,7 @@ def _gemm_case(P, M, K, N, r, epi, seed=1):
 
 
 @pytest.mark.parametrize("M,K,N,r,epi", [(200, 512, 384, 16, "none"),      # 128-wide tiles
-                                         (256, 512, 512, 16, "gelu_tanh"),  # 256-wide tiles
+                                         (256, 512, 512, 16, "gelu_tanh"),  # few tiles: 128-wide
                                          (300, 1024, 768, 32, "none"),
                                          (17, 256, 256, 0, "gelu_tanh"),
                                          (520, 768, 1280, 128, "none")])
@@ -132,6 +132,31 @@ def test_gemm_nvfp4_full_size_sampled(P):
     c_ref_u, c_ref, s_ref = oracle.quantize_act_ref(p["X"][rows], p["smooth_inv"], "nvfp4_g16", ga)
     assert np.array_equal(host(codes)[rows], c_ref)
     assert np.array_equal(host(scales)[rows], s_ref)
+    la_h = host(la)[rows]
+    wu = oracle.unpack_nibbles(p["w_codes"][cols], signed=False)
+    y_ref = oracle.gemm_ref(c_ref_u, s_ref, la_h, wu, p["w_scales"][cols], p["lora_up"][cols],
+                            p["bias"][cols], "nvfp4_g16", "gelu_tanh", act_gscale=ga, w_gscale=gw)
+    yh = host(y)
+    assert np.isfinite(yh).all()
+    assert rel_l2(yh[np.ix_(rows, cols)], y_ref) <= Y_TOL
+
+
+def test_gemm_nvfp4_wide_tiles_ragged_sampled(P):
+    """256-wide tiles (more than 128 of them) with a ragged last row tile:
+    M 1000, N 8448 (4 x 33 tiles); sampled rows (the last ones included) and
+    columns against the oracle."""
+    cfg = synth.LayerConfig("nv_wide", 62, 1000, 512, 8448, 32, "nvfp4_g16", "gelu_tanh", "normal", 0.005, 30.0)
+    p = synth.random_quantized_layer(cfg, seed=4)
+    ga, gw = p["act_gscale"], p["w_gscale"]
+    codes, scales, la = P.svdq_quantize_act_nvfp4(dev(p["X"]), dev(p["smooth_inv"]), dev(p["lora_down"]),
+                                                  float(ga))
+    y = P.svdq_gemm_nvfp4(codes, scales, la, dev(p["w_codes"]), dev(p["w_scales"]), dev(p["lora_up"]),
+                          dev(p["bias"]), float(np.float32(ga) * np.float32(gw)), "gelu_tanh")
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([rng.choice(cfg.M, 20, replace=False), [0, 767, 768, 999]]))
+    cols = np.unique(np.concatenate([rng.choice(cfg.N, 80, replace=False), [0, 255, 256, 8447]]))
+    c_ref_u, c_ref, s_ref = oracle.quantize_act_ref(p["X"][rows], p["smooth_inv"], "nvfp4_g16", ga)
+    assert np.array_equal(host(codes)[rows], c_ref)
     la_h = host(la)[rows]
     wu = oracle.unpack_nibbles(p["w_codes"][cols], signed=False)
     y_ref = oracle.gemm_ref(c_ref_u, s_ref, la_h, wu, p["w_scales"][cols], p["lora_up"][cols],
