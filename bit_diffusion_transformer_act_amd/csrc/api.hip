@@ -89,7 +89,7 @@ int svdq_quantize_act(int fmt, int dtype, int M, int K, int r, const void* X, co
                       void* stream) {
   if (fmt != SVDQ_INT4_G64 && fmt != SVDQ_FP4_E2M1_B32) return SVDQ_ERR_INVALID_ARG;
   if (!dtype_ok(dtype)) return SVDQ_ERR_INVALID_ARG;
-  if (M < 0 || !k_ok(K) || !rank_ok(r)) return SVDQ_ERR_SHAPE;
+  if (M < 0 || M > (1 << 23) || !k_ok(K) || !rank_ok(r)) return SVDQ_ERR_SHAPE;
   if (M == 0) return SVDQ_OK;
   if (!X || !smooth_inv || !act_codes || !act_scales) return SVDQ_ERR_INVALID_ARG;
   if (r > 0 && (!lora_down || !lora_act)) return SVDQ_ERR_INVALID_ARG;
@@ -198,7 +198,7 @@ int svdq_quantize_act_nvfp4(int dtype, int M, int K, int r, const void* X, const
                             const void* lora_down, float act_gscale, uint8_t* act_codes,
                             uint8_t* act_scales, void* lora_act, void* stream) {
   if (!dtype_ok(dtype)) return SVDQ_ERR_INVALID_ARG;
-  if (M < 0 || !k_nv_ok(K) || !rank_ok(r)) return SVDQ_ERR_SHAPE;
+  if (M < 0 || M > (1 << 23) || !k_nv_ok(K) || !rank_ok(r)) return SVDQ_ERR_SHAPE;
   if (!positive_finite(act_gscale) || !positive_finite(6.0f * act_gscale)) return SVDQ_ERR_INVALID_ARG;
   if (M == 0) return SVDQ_OK;
   if (!X || !smooth_inv || !act_codes || !act_scales) return SVDQ_ERR_INVALID_ARG;
@@ -220,7 +220,8 @@ int svdq_gemm_nvfp4(int dtype, int M, int N, int K, int r, const uint8_t* act_co
   if (!dtype_ok(dtype)) return SVDQ_ERR_INVALID_ARG;
   if (epilogue != SVDQ_EPI_NONE && epilogue != SVDQ_EPI_GELU_TANH) return SVDQ_ERR_INVALID_ARG;
   if (!std::isfinite(alpha)) return SVDQ_ERR_INVALID_ARG;
-  if (M < 0 || N < 128 || N > 65536 || (N % 128) != 0 || !k_nv_ok(K) || !rank_ok(r)) return SVDQ_ERR_SHAPE;
+  if (M < 0 || M > (1 << 23) || N < 128 || N > 65536 || (N % 128) != 0 || !k_nv_ok(K) || !rank_ok(r))
+    return SVDQ_ERR_SHAPE;
   if (M == 0) return SVDQ_OK;
   if (!act_codes || !act_scales || !w_codes || !w_scales || !Y) return SVDQ_ERR_INVALID_ARG;
   if (r > 0 && (!lora_act || !lora_up)) return SVDQ_ERR_INVALID_ARG;

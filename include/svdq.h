@@ -120,7 +120,7 @@ int svdq_version(void);
  * Arguments:
  *   fmt         svdq_format.
  *   dtype       svdq_dtype.
- *   M           rows (tokens), M >= 0.
+ *   M           rows (tokens), 0 <= M <= 2^23.
  *   K           input channels; K % 128 == 0, 128 <= K <= 65536.
  *   r           low-rank width; r % 16 == 0, 0 <= r <= 128.
  *   X           h16 [M][K].

@@ -71,6 +71,8 @@ def test_quantize_act_argument_errors():
     assert q(r=8) == ops.SVDQ_ERR_SHAPE
     assert q(r=144) == ops.SVDQ_ERR_SHAPE
     assert q(M=-1) == ops.SVDQ_ERR_SHAPE
+    assert q(M=(1 << 23) + 1) == ops.SVDQ_ERR_SHAPE
+    assert q(M=1 << 23) == ops.SVDQ_ERR_UNSUPPORTED_DEVICE   # the largest M is accepted
     assert q(M=0, X=None, si=None, ld=None, codes=None, scales=None, la=None) == ops.SVDQ_OK
     assert q(X=None) == ops.SVDQ_ERR_INVALID_ARG
     assert q(la=None) == ops.SVDQ_ERR_INVALID_ARG
@@ -89,6 +91,9 @@ def test_gemm_argument_errors():
     assert g(K=320) == ops.SVDQ_ERR_SHAPE
     assert g(r=40) == ops.SVDQ_ERR_SHAPE
     assert g(M=(1 << 23) + 1) == ops.SVDQ_ERR_SHAPE
+    assert g(N=65536 + 128) == ops.SVDQ_ERR_SHAPE
+    assert g(K=65536 + 128) == ops.SVDQ_ERR_SHAPE
+    assert g(M=1 << 23, N=65536, K=65536, r=128) == ops.SVDQ_ERR_UNSUPPORTED_DEVICE
     assert g(M=0, ac=None, sa=None, la=None, wc=None, ws=None, lu=None, Y=None) == ops.SVDQ_OK
     assert g(wc=None) == ops.SVDQ_ERR_INVALID_ARG
     assert g(lu=None) == ops.SVDQ_ERR_INVALID_ARG
@@ -104,6 +109,8 @@ def test_gemv_argument_errors():
     assert v(K=96) == ops.SVDQ_ERR_SHAPE
     assert v(M=2, K=32768) == ops.SVDQ_ERR_SHAPE
     assert v(N=0) == ops.SVDQ_ERR_SHAPE
+    assert v(N=(1 << 20) + 1) == ops.SVDQ_ERR_SHAPE
+    assert v(M=8, K=4096, N=1 << 20) == ops.SVDQ_ERR_UNSUPPORTED_DEVICE   # the limits themselves pass
     assert v(M=0, x=None, c=None, s=None, z=None, y=None) == ops.SVDQ_OK
     assert v(z=None) == ops.SVDQ_ERR_INVALID_ARG
     assert v(y=U) == ops.SVDQ_ERR_ALIGN
@@ -125,6 +132,7 @@ def test_nvfp4_argument_errors():
     assert qn(K=128) == ops.SVDQ_ERR_SHAPE          # K % 256
     assert qn(K=384) == ops.SVDQ_ERR_SHAPE
     assert qn(r=8) == ops.SVDQ_ERR_SHAPE
+    assert qn(M=(1 << 23) + 1) == ops.SVDQ_ERR_SHAPE
     assert qn(g=0.0) == ops.SVDQ_ERR_INVALID_ARG
     assert qn(g=-1.0) == ops.SVDQ_ERR_INVALID_ARG
     assert qn(g=float("inf")) == ops.SVDQ_ERR_INVALID_ARG
@@ -139,6 +147,9 @@ def test_nvfp4_argument_errors():
     assert gn(N=64) == ops.SVDQ_ERR_SHAPE
     assert gn(N=200) == ops.SVDQ_ERR_SHAPE
     assert gn(r=144) == ops.SVDQ_ERR_SHAPE
+    assert gn(M=(1 << 23) + 1) == ops.SVDQ_ERR_SHAPE
+    assert gn(N=65536 + 128) == ops.SVDQ_ERR_SHAPE
+    assert gn(K=65536 + 256) == ops.SVDQ_ERR_SHAPE
     assert gn(M=0, ac=None, sa=None, la=None, wc=None, ws=None, lu=None, Y=None) == ops.SVDQ_OK
     assert gn(ws=None) == ops.SVDQ_ERR_INVALID_ARG
     assert gn(lu=None) == ops.SVDQ_ERR_INVALID_ARG

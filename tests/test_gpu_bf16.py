@@ -124,7 +124,10 @@ def test_gemm_fp4_large_tile_bf16(P):
     X = bf(p["X"].astype(np.float32))
     ld, lu, b = bf(p["lora_down"].astype(np.float32)), bf(p["lora_up"].astype(np.float32)), bf(p["bias"].astype(np.float32))
     codes, scales, la = P.svdq_quantize_act(dbf(X), dev(p["smooth_inv"]), dbf(ld), "fp4_b32")
-    y = P.svdq_gemm_w4a4(codes, scales, la, dev(p["w_codes"]), dev(p["w_scales"]), dbf(lu), dbf(b),
+    # the GEMM takes the oracle's low-rank activations, the GPU's checked against them
+    la_o = oracle.bf16_round(oracle.lora_act_ref(X, ld).astype(np.float32))
+    assert rel_l2(host(la), la_o) <= LORA_TOL
+    y = P.svdq_gemm_w4a4(codes, scales, dbf(la_o), dev(p["w_codes"]), dev(p["w_scales"]), dbf(lu), dbf(b),
                          "fp4_b32", "gelu_tanh")
     rng = np.random.default_rng(5)
     rows = np.sort(rng.choice(cfg.M, 16, replace=False))
@@ -132,7 +135,7 @@ def test_gemm_fp4_large_tile_bf16(P):
     cu, c_ref, s_ref = oracle.quantize_act_ref(X[rows], p["smooth_inv"], "fp4_b32")
     assert np.array_equal(host(codes)[rows], c_ref)
     wu = oracle.unpack_nibbles(p["w_codes"][cols], signed=False)
-    y_ref = oracle.gemm_ref(cu, s_ref, host(la)[rows], wu, p["w_scales"][cols], lu[cols], b[cols], "fp4_b32",
+    y_ref = oracle.gemm_ref(cu, s_ref, la_o[rows], wu, p["w_scales"][cols], lu[cols], b[cols], "fp4_b32",
                             "gelu_tanh")
     assert rel_l2(host(y)[np.ix_(rows, cols)], oracle.bf16_round(y_ref.astype(np.float32))) <= Y_TOL
 

@@ -76,7 +76,9 @@ def run_fused(P, codes, scales, la, up, si2, ld2, h):
                                           (37, 256, 384, 16, 32, torch.float16),
                                           (256, 512, 512, 0, 0, torch.float16),
                                           (130, 512, 768, 32, 16, torch.bfloat16),
-                                          (4096, 3072, 12288, 32, 32, torch.float16)])
+                                          (4096, 3072, 12288, 32, 32, torch.float16),
+                                          (200, 512, 1024, 16, 48, torch.bfloat16),   # ranks past the prefetched 32
+                                          (130, 128, 65536, 16, 128, torch.float16)])  # the largest N and rank
 def test_chain_equals_unfused(P, M, K, N, r, r2, h):
     up, si2, ld2 = chain_inputs(M, K, N, r, r2)
     X = dev(up["X"], h)

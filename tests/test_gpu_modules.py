@@ -3,14 +3,17 @@ AWQLinear at a time, and the synthetic DiT block with every linear patched
 to the 4-bit kernels.
 
 Bars. A module: the layer bar (relative L2 2e-3 against the oracle's float64
-layer on the module's own fp16 input). The block, in three parts:
-  - each 4-bit layer on the input the GPU block actually fed it: the layer bar;
-  - the composition: the oracle block's float64 arithmetic around the layers
-    (modulation, LayerNorm, Q/K norm and rotation when unfused, attention,
-    residuals), run on the GPU's own layer outputs, must give every layer
-    input (rounded to the layer's 16-bit type on both sides) and the block
-    output within GLUE_TOL (the GPU's fp32 arithmetic and the rare last-bit
-    rounding differences it causes);
+layer on the module's own fp16 input). The block, in three parts, with values
+flowing only from the oracle to the GPU, never back:
+  - each 4-bit GPU layer on the oracle block's own input to that layer
+    (rounded to the layer's 16-bit type), against the oracle's output of that
+    layer: the layer bar;
+  - the composition: the GPU block with every layer's output replaced by the
+    oracle's output of that layer, so that only the block's arithmetic around
+    the layers (modulation, LayerNorm, Q/K norm and rotation when unfused,
+    attention, residuals) differs; the layer inputs it forms (16-bit on both
+    sides) and its output must match the oracle block's within GLUE_TOL (the
+    GPU's fp32 arithmetic and the rare last-bit rounding differences it causes);
   - free running, GPU block against oracle block from the same x, c, rope:
     4-bit activation quantization is not continuous at fp16 resolution (a
     last-bit change of a layer input moves a code by a whole step), so the
@@ -36,6 +39,7 @@ pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 Y_TOL = 2e-3
 GLUE_TOL = 1e-3
+H16 = {"float16": torch.float16, "bfloat16": torch.bfloat16}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -86,7 +90,7 @@ def test_awq_linear_module(M):
     assert rel_l2(host(y), ref) <= Y_TOL
 
 
-def _run_block(fmt, fuse, D=1024, C=768, B=2, T=200, rank=32, dtype="float16"):
+def _block(fmt, fuse, D=1024, C=768, B=2, T=200, rank=32, dtype="float16"):
     w = synth.dit_block_params(D, C, seed=11)
     cal = synth.dit_block_inputs(2, 256, D, C, seed=12)
     inp = synth.dit_block_inputs(B, T, D, C, seed=13)
@@ -97,54 +101,83 @@ def _run_block(fmt, fuse, D=1024, C=768, B=2, T=200, rank=32, dtype="float16"):
         assert fuse_qkv_norm_rope(blk) == ["self_attention"]
     blk.load_state_dict(to_torch(sd, DEV), strict=True)
     blk.to(DEV)
-    seen = {}
+    return w, inp, P, blk
+
+
+def _layers(blk):
+    return {n: m for n, m in blk.named_modules() if isinstance(m, (SVDQLinear, SVDQLinearQKV, AWQLinear))}
+
+
+def _run(blk, inp, forced=None):
+    """The GPU block on (x, c, rope). Returns its output and, per 4-bit layer,
+    the 16-bit input the block fed it (rows). With forced (name -> the
+    oracle's output rows of that layer), each layer's output is replaced by
+    the oracle's before the block goes on: the block's own arithmetic then
+    runs on the oracle's layer values."""
+    seen, hooks = {}, []
 
     def hook(name):
         def f(mod, args, out):
-            y = torch.cat(out, -1) if isinstance(out, tuple) else out
-            seen[name] = (host(args[0].float()).reshape(-1, args[0].shape[-1]),
-                          host(y.float()).reshape(-1, y.shape[-1]))
+            seen[name] = host(args[0].float()).reshape(-1, args[0].shape[-1])
+            if forced is None:
+                return None
+            like = out[0] if isinstance(out, tuple) else out
+            y = torch.from_numpy(np.asarray(forced[name], np.float32)).to(DEV, like.dtype)
+            if isinstance(out, tuple):
+                return y.reshape(*args[0].shape[:-1], -1).split(like.shape[-1], dim=-1)
+            return y.reshape(out.shape)
         return f
-    for name, mod in blk.named_modules():
-        if isinstance(mod, (SVDQLinear, AWQLinear)):
-            mod.register_forward_hook(hook(name))
-    x = torch.from_numpy(inp["x"]).to(DEV)
-    with torch.no_grad():
-        out = blk(x, torch.from_numpy(inp["c"]).to(DEV), torch.from_numpy(inp["rope"]).to(DEV))
-    return w, inp, P, seen, host(out)
+    for name, mod in _layers(blk).items():
+        hooks.append(mod.register_forward_hook(hook(name)))
+    try:
+        with torch.no_grad():
+            out = blk(torch.from_numpy(inp["x"]).to(DEV), torch.from_numpy(inp["c"]).to(DEV),
+                      torch.from_numpy(inp["rope"]).to(DEV))
+    finally:
+        for h in hooks:
+            h.remove()
+    return host(out), seen
 
 
 @pytest.mark.parametrize("fmt,fuse,dtype", [("int4_g64", True, "float16"), ("fp4_b32", False, "float16"),
                                             ("nvfp4_g16", False, "bfloat16"),     # the pages' own config
                                             ("int4_g64", True, "bfloat16")])
 def test_dit_block_end_to_end(fmt, fuse, dtype, monkeypatch):
-    w, inp, P, seen, out = _run_block(fmt, fuse, dtype=dtype)
+    w, inp, P, blk = _block(fmt, fuse, dtype=dtype)
     expect = {"adaLN_modulation.1", "self_attention.to_out", "mlp.0", "mlp.2"} | (
         {"self_attention.to_qkv"} if fuse else {f"self_attention.to_{p}" for p in "qkv"})
-    assert set(seen) == expect
-    T = inp["x"].shape[1]
-    rope_rows = np.tile(inp["rope"].astype(np.float64), (inp["x"].shape[0], 1, 1))
-    for name, (xin, y) in seen.items():
-        ref = oracle_linear(xin, P[name], rope=rope_rows if name.endswith("to_qkv") else None)
-        err = rel_l2(y, ref)
+    layers = _layers(blk)
+    assert set(layers) == expect
+    # the oracle block, free running; cap holds each layer's input and output rows
+    cap = {}
+    ref = oracle.dit_block_ref(inp["x"], inp["c"], inp["rope"], P, capture=cap)
+    assert set(cap) == expect
+
+    # each 4-bit layer on the GPU, fed the oracle's own input to that layer
+    for name, mod in layers.items():
+        dt = P[name].get("dtype", "float16")
+        xin = torch.from_numpy(np.asarray(oracle.block._r16(cap[name][0], dt), np.float32)).to(DEV, H16[dt])
+        with torch.no_grad():
+            y = mod(xin, torch.from_numpy(inp["rope"]).to(DEV)) if name.endswith("to_qkv") else mod(xin)
+        y = torch.cat(y, -1) if isinstance(y, tuple) else y
+        err = rel_l2(host(y.float()), cap[name][1])
         print(f"{fmt} {name}: rows {xin.shape[0]} rel_l2 {err:.2e}")
         assert err <= Y_TOL, name
-    # composition: the oracle's block arithmetic on the GPU's layer outputs
-    fcap = {}
-    forced = oracle.dit_block_ref(inp["x"], inp["c"], inp["rope"], P, capture=fcap,
-                                  outputs={n: y for n, (_, y) in seen.items()})
-    for name, (xin, _) in seen.items():
-        # the GPU stored the input in the layer's 16-bit type: round the oracle's alike
-        err = rel_l2(xin, oracle.block._r16(fcap[name][0], P[name].get("dtype", "float16")))
-        print(f"{fmt} input of {name}: rel_l2 vs oracle glue {err:.2e}")
+
+    # the composition: the GPU block with every layer output replaced by the
+    # oracle's; the inputs it then feeds the layers, and its output, against the oracle's
+    out_f, seen_f = _run(blk, inp, forced={n: cap[n][1] for n in expect})
+    for name in expect:
+        err = rel_l2(seen_f[name], oracle.block._r16(cap[name][0], P[name].get("dtype", "float16")))
+        print(f"{fmt} input of {name}, oracle layer outputs forced: rel_l2 {err:.2e}")
         assert err <= GLUE_TOL, name
-    err = rel_l2(out, forced)
-    print(f"{fmt} {dtype} block output, teacher-forced: rel_l2 {err:.2e}")
-    assert np.isfinite(out).all() and err <= GLUE_TOL
+    err = rel_l2(out_f, ref)
+    print(f"{fmt} {dtype} block output, oracle layer outputs forced: rel_l2 {err:.2e}")
+    assert np.isfinite(out_f).all() and err <= GLUE_TOL
 
     # free running, against the oracle's own sensitivity
+    out, _ = _run(blk, inp)
     x64 = inp["x"].astype(np.float64)
-    ref = oracle.dit_block_ref(inp["x"], inp["c"], inp["rope"], P)
     err = rel_l2(out - x64, ref - x64)
     rng = np.random.default_rng(17)
 
@@ -162,5 +195,5 @@ def test_dit_block_end_to_end(fmt, fuse, dtype, monkeypatch):
     dense = oracle.dit_block_ref(inp["x"], inp["c"], inp["rope"], dense_params(w))
     qerr = rel_l2(ref - x64, dense - x64)
     print(f"{fmt} {dtype} block increment: GPU vs oracle {err:.2e}, oracle vs itself under 1-ulp noise "
-          f"{floor:.2e}, 4-bit vs dense {qerr:.2e} (T={T})")
+          f"{floor:.2e}, 4-bit vs dense {qerr:.2e} (T={inp['x'].shape[1]})")
     assert err <= 2 * floor + 1e-3

@@ -124,7 +124,10 @@ def test_gemm_nvfp4_full_size_sampled(P):
     ga, gw = p["act_gscale"], p["w_gscale"]
     codes, scales, la = P.svdq_quantize_act_nvfp4(dev(p["X"]), dev(p["smooth_inv"]), dev(p["lora_down"]),
                                                   float(ga))
-    y = P.svdq_gemm_nvfp4(codes, scales, la, dev(p["w_codes"]), dev(p["w_scales"]), dev(p["lora_up"]),
+    # the GEMM takes the oracle's low-rank activations (all rows), the GPU's checked against them
+    la_o = oracle.lora_act_ref(p["X"], p["lora_down"]).astype(np.float16)
+    assert rel_l2(host(la), la_o) <= LORA_TOL
+    y = P.svdq_gemm_nvfp4(codes, scales, dev(la_o), dev(p["w_codes"]), dev(p["w_scales"]), dev(p["lora_up"]),
                           dev(p["bias"]), float(np.float32(ga) * np.float32(gw)), "gelu_tanh")
     rng = np.random.default_rng(3)
     rows = np.sort(rng.choice(cfg.M, 24, replace=False))
@@ -132,9 +135,8 @@ def test_gemm_nvfp4_full_size_sampled(P):
     c_ref_u, c_ref, s_ref = oracle.quantize_act_ref(p["X"][rows], p["smooth_inv"], "nvfp4_g16", ga)
     assert np.array_equal(host(codes)[rows], c_ref)
     assert np.array_equal(host(scales)[rows], s_ref)
-    la_h = host(la)[rows]
     wu = oracle.unpack_nibbles(p["w_codes"][cols], signed=False)
-    y_ref = oracle.gemm_ref(c_ref_u, s_ref, la_h, wu, p["w_scales"][cols], p["lora_up"][cols],
+    y_ref = oracle.gemm_ref(c_ref_u, s_ref, la_o[rows], wu, p["w_scales"][cols], p["lora_up"][cols],
                             p["bias"][cols], "nvfp4_g16", "gelu_tanh", act_gscale=ga, w_gscale=gw)
     yh = host(y)
     assert np.isfinite(yh).all()
@@ -150,16 +152,17 @@ def test_gemm_nvfp4_wide_tiles_ragged_sampled(P):
     ga, gw = p["act_gscale"], p["w_gscale"]
     codes, scales, la = P.svdq_quantize_act_nvfp4(dev(p["X"]), dev(p["smooth_inv"]), dev(p["lora_down"]),
                                                   float(ga))
-    y = P.svdq_gemm_nvfp4(codes, scales, la, dev(p["w_codes"]), dev(p["w_scales"]), dev(p["lora_up"]),
+    la_o = oracle.lora_act_ref(p["X"], p["lora_down"]).astype(np.float16)
+    assert rel_l2(host(la), la_o) <= LORA_TOL
+    y = P.svdq_gemm_nvfp4(codes, scales, dev(la_o), dev(p["w_codes"]), dev(p["w_scales"]), dev(p["lora_up"]),
                           dev(p["bias"]), float(np.float32(ga) * np.float32(gw)), "gelu_tanh")
     rng = np.random.default_rng(5)
     rows = np.unique(np.concatenate([rng.choice(cfg.M, 20, replace=False), [0, 767, 768, 999]]))
     cols = np.unique(np.concatenate([rng.choice(cfg.N, 80, replace=False), [0, 255, 256, 8447]]))
     c_ref_u, c_ref, s_ref = oracle.quantize_act_ref(p["X"][rows], p["smooth_inv"], "nvfp4_g16", ga)
     assert np.array_equal(host(codes)[rows], c_ref)
-    la_h = host(la)[rows]
     wu = oracle.unpack_nibbles(p["w_codes"][cols], signed=False)
-    y_ref = oracle.gemm_ref(c_ref_u, s_ref, la_h, wu, p["w_scales"][cols], p["lora_up"][cols],
+    y_ref = oracle.gemm_ref(c_ref_u, s_ref, la_o[rows], wu, p["w_scales"][cols], p["lora_up"][cols],
                             p["bias"][cols], "nvfp4_g16", "gelu_tanh", act_gscale=ga, w_gscale=gw)
     yh = host(y)
     assert np.isfinite(yh).all()
