@@ -26,6 +26,7 @@
 #include <atomic>
 
 #include "common.hpp"
+#include "launch.hpp"
 
 namespace svdq {
 
@@ -227,13 +228,10 @@ static hipError_t launch_k(int N, int K, const void* x, const uint8_t* q, const 
   const int grid = max(max(1, min(256, (N + 8 * 4 - 1) / (8 * 4))), (N + rows_cap - 1) / rows_cap);
   const size_t lds = (size_t)MR * (K >> 5) * 16 * sizeof(uint32_t) + (size_t)MR * (K >> 5) * sizeof(float);
   if (lds > 65536) {   // M K = 32768 needs 68 KB
-    static std::atomic<int> raised{0};
-    if (!raised.load(std::memory_order_acquire)) {
-      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&awq_gemv_kernel<IO, MR, PAIRS>),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, 72 * 1024);
-      if (e != hipSuccess) return e;
-      raised.store(1, std::memory_order_release);
-    }
+    static std::atomic<uint64_t> raised{0};
+    const hipError_t e =
+        raise_lds_limit(raised, reinterpret_cast<const void*>(&awq_gemv_kernel<IO, MR, PAIRS>), 72 * 1024);
+    if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((awq_gemv_kernel<IO, MR, PAIRS>), dim3(grid), dim3(64 * kGemvWaves), lds, st,
                      (const uint16_t*)x, q, (const __half*)s, (const __half*)z, (const uint16_t*)b, (uint16_t*)y,

@@ -26,6 +26,7 @@
 #include <type_traits>
 
 #include "common.hpp"
+#include "launch.hpp"
 #include "pipeline.hpp"
 
 namespace svdq {
@@ -310,13 +311,9 @@ hipError_t launch_gemm_fp4_big(int io, int M, int N, int K, int r, const uint8_t
   const int v = 2 * (io == 1) + (epi != 0);
   auto kern = v == 3 ? gemm_fp4_big_kernel<1, 1> : v == 2 ? gemm_fp4_big_kernel<1, 0>
             : v == 1 ? gemm_fp4_big_kernel<0, 1> : gemm_fp4_big_kernel<0, 0>;
-  static std::atomic<int> raised[4] = {0, 0, 0, 0};
-  if (!raised[v].load(std::memory_order_acquire)) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
-    if (e != hipSuccess) return e;
-    raised[v].store(1, std::memory_order_release);
-  }
+  static std::atomic<uint64_t> raised[4] = {};
+  const hipError_t e = raise_lds_limit(raised[v], reinterpret_cast<const void*>(kern), LDS);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(ntiles), dim3(256), LDS, st, ac, (const uint8_t*)as, (const uint16_t*)la, wc,
                      (const uint8_t*)ws, (const uint16_t*)lu, (const uint16_t*)bias, (uint16_t*)Y, M, N, K, r);
   return hipGetLastError();

@@ -323,13 +323,9 @@ static hipError_t launch_nv(int M, int N, int K, int r, const uint8_t* ac, const
                             const void* bias, float alpha, void* Y, hipStream_t st) {
   using namespace nvfp4;
   auto kern = gemm_nvfp4_kernel<IO, EPI, BN>;
-  static std::atomic<int> raised{0};
-  if (!raised.load(std::memory_order_acquire)) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
-    if (e != hipSuccess) return e;
-    raised.store(1, std::memory_order_release);
-  }
+  static std::atomic<uint64_t> raised{0};
+  const hipError_t e = raise_lds_limit(raised, reinterpret_cast<const void*>(kern), LDS);
+  if (e != hipSuccess) return e;
   const int ntiles = ((M + BM - 1) / BM) * (N / BN);
   hipLaunchKernelGGL(kern, dim3(ntiles), dim3(256), LDS, st, ac, as, (const uint16_t*)la, wc, ws,
                      (const uint16_t*)lu, (const uint16_t*)bias, (uint16_t*)Y, alpha, M, N, K, r);

@@ -634,13 +634,9 @@ static hipError_t launch_cfg(int M, int N, int K, int r, const uint8_t* ac, cons
   using S = GemmShape<WM, WN, STAGES>;
   auto kern = gemm_w4a4_kernel<IO, FMT, EPI, WM, WN, STAGES>;
   if (S::LDS > 65536) {
-    static std::atomic<int> raised{0};
-    if (!raised.load(std::memory_order_acquire)) {
-      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS);
-      if (e != hipSuccess) return e;
-      raised.store(1, std::memory_order_release);
-    }
+    static std::atomic<uint64_t> raised{0};
+    const hipError_t e = raise_lds_limit(raised, reinterpret_cast<const void*>(kern), S::LDS);
+    if (e != hipSuccess) return e;
   }
   const int ntiles = ((M + S::BM - 1) / S::BM) * (N / S::BN);
   hipLaunchKernelGGL(kern, dim3(ntiles), dim3(256), S::LDS, st, ac, as, (const uint16_t*)la, wc, ws,

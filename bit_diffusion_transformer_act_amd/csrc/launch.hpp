@@ -4,7 +4,24 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace svdq {
+
+// Raises a kernel's dynamic LDS limit to `bytes` on the current device, once
+// per device and call site: the attribute belongs to the device that is
+// current when it is set, so `done` keeps one bit per device id (ids past 63
+// set it on every call).
+inline hipError_t raise_lds_limit(std::atomic<uint64_t>& done, const void* kern, int bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t{1} << dev) : 0;
+  if (bit != 0 && (done.load(std::memory_order_acquire) & bit) != 0) return hipSuccess;
+  e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit != 0) done.fetch_or(bit, std::memory_order_acq_rel);
+  return e;
+}
 
 // io: 16-bit type of activations, low-rank branch, biases and outputs (0 fp16, 1 bf16)
 // fmt 0 INT4 g64, 1 FP4 E2M1 b32, 2 NVFP4 (gscale: the per-tensor scale)

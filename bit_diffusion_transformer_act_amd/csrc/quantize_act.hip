@@ -28,6 +28,7 @@
 #include <atomic>
 
 #include "common.hpp"
+#include "launch.hpp"
 
 namespace svdq {
 
@@ -439,15 +440,11 @@ static hipError_t launch_qws(int M, int K, int slices, const void* X, const floa
   const dim3 grid((M + 15) / 16, slices), block(64 * WAVES);
   const size_t lds = quant_lds_bytes<WAVES>(NCB) + (SLDS ? (size_t)K * sizeof(float) : 0);
   if (lds > 65536) {
-    // the attribute is raised once per instantiation to the largest size it may need
-    static std::atomic<int> raised{0};
-    if (!raised.load(std::memory_order_acquire)) {
-      const hipError_t e = hipFuncSetAttribute(
-          reinterpret_cast<const void*>(&quantize_act_kernel<IO, FMT, NCB, WAVES, SLDS, LO>),
-          hipFuncAttributeMaxDynamicSharedMemorySize, kQuantLdsMax);
-      if (e != hipSuccess) return e;
-      raised.store(1, std::memory_order_release);
-    }
+    // raised once per instantiation and device to the largest size it may need
+    static std::atomic<uint64_t> raised{0};
+    const hipError_t e = raise_lds_limit(
+        raised, reinterpret_cast<const void*>(&quantize_act_kernel<IO, FMT, NCB, WAVES, SLDS, LO>), kQuantLdsMax);
+    if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((quantize_act_kernel<IO, FMT, NCB, WAVES, SLDS, LO>), grid, block, lds, st,
                      (const uint16_t*)X, si, (const uint16_t*)ld, codes, scales, (uint16_t*)la, M, K, gs,
