@@ -10,11 +10,14 @@
 // Work split (gfx950, wave64): a workgroup of W waves (4, 8 or 16) owns 16 rows
 // of X and all of K (or, with few rows and a long K, one slice of K: see
 // launch_q_r); wave w handles 64-wide K steps w, w+W, w+2W, ..., with the
-// loads of its next one or two steps in flight. In a step, lane l holds row
+// loads of its next one or two steps in flight. The loads are the kernel's
+// bottleneck: the vector memory unit spends about 50 cycles on an instruction
+// that touches 16 half lines and about 17 on one that covers 8 whole lines, so
+// with a low-rank pass (X plus two 16-rank blocks of lora_down per step at
+// rank 32) every load covers 8 whole 128-byte lines and a per-wave LDS
+// scratch turns them into the layout below. In a step, lane l holds row
 // (l % 16) and two 8-channel chunks: q*8 .. +8 and 32 + q*8 .. +8 of the step
-// (q = l / 16), so each load instruction reads 16 rows x 64 contiguous bytes
-// (the vector memory unit's cost grows with the number of 64-byte sectors an
-// instruction touches). That register tile is at the same time
+// (q = l / 16). That register tile is at the same time
 //   - the A operands of two v_mfma_f32_16x16x32_f16 against lora_down, in the
 //     instruction's own layout (lane l: row l % 16, k 8 (l / 16) .. +8), one
 //     call per 32-channel half, and
@@ -34,11 +37,19 @@ namespace svdq {
 
 constexpr int kQuantLdsMax = 144 * 1024;   // LDS budget per workgroup (gfx950 has 160 KB)
 
-// LDS bytes besides smooth_inv: two round buffers (sized for the 4 scale
-// bytes per step of NVFP4) and the low-rank partials
+// LDS bytes besides smooth_inv: per wave a re-layout scratch of two blocks of
+// 16 rows x 128 bytes (X, and the 16-rank blocks of lora_down one after the
+// other), which the low-rank partials reuse after the main loop, then two
+// round buffers (sized for the 4 scale bytes per step of NVFP4)
+template <int WAVES>
+constexpr size_t quant_scratch_bytes(int ncb) {
+  const size_t scr = ncb > 0 ? (size_t)WAVES * 2 * 2048 : 0;   // none without a low-rank pass
+  const size_t part = (size_t)WAVES * 16 * 16 * ncb * sizeof(float);
+  return scr > part ? scr : part;
+}
 template <int WAVES>
 constexpr size_t quant_lds_bytes(int ncb) {
-  return 2 * (size_t)(16 * (WAVES * 32 + 16) + 16 * WAVES * 4) + (size_t)WAVES * 16 * 16 * ncb * sizeof(float);
+  return quant_scratch_bytes<WAVES>(ncb) + 2 * (size_t)(16 * (WAVES * 32 + 16) + 16 * WAVES * 4);
 }
 
 // E4M3 (OCP FP8, bias 7) byte of a non-negative fp32 value: round to nearest,
@@ -76,8 +87,9 @@ void quantize_act_kernel(const uint16_t* __restrict__ X, const float* __restrict
                          void* __restrict__ scales, uint16_t* __restrict__ lora_act,
                          int M, int K, float gs, float gs6, int rq) {
 #pragma clang fp contract(off)
-  // LDS: two round buffers (codes, then scales, of 16 rows x WAVES steps),
-  // [WAVES][16 rows][16 * NCB] low-rank partials, then smooth_inv[K] if SLDS
+  // LDS: the waves' re-layout scratch (reused after the main loop for the
+  // [WAVES][16 rows][16 * NCB] low-rank partials), two round buffers (codes,
+  // then scales, of 16 rows x WAVES steps), then smooth_inv[K] if SLDS
   extern __shared__ float lds_f[];
   constexpr int R = 16 * NCB;
   constexpr int NL = NCB > 0 ? NCB : 1;
@@ -85,11 +97,12 @@ void quantize_act_kernel(const uint16_t* __restrict__ X, const float* __restrict
   constexpr int SB = FMT == 2 ? 4 : 2;          // scale bytes per row and step
   constexpr int SROW = WAVES * SB;              // scale row of a round (bytes)
   constexpr int RBUF = 16 * CROW + 16 * SROW;   // one round buffer (bytes, multiple of 16)
-  uint8_t* rbuf = reinterpret_cast<uint8_t*>(lds_f);
-  float* red = lds_f + 2 * RBUF / 4;
-  float* s_si = red + WAVES * 16 * R;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  float* red = lds_f;
+  uint4* scr = reinterpret_cast<uint4*>(lds_f) + (size_t)wave * 2 * 128;   // this wave's scratch (NCB > 0)
+  uint8_t* rbuf = reinterpret_cast<uint8_t*>(lds_f) + quant_scratch_bytes<WAVES>(NCB);
+  float* s_si = reinterpret_cast<float*>(rbuf + 2 * RBUF);
   const int m0 = blockIdx.x * 16;
   const int row = m0 + (lane & 15);
   const int q4 = lane >> 4;
@@ -99,10 +112,22 @@ void quantize_act_kernel(const uint16_t* __restrict__ X, const float* __restrict
   const int sps = (steps_all + (int)gridDim.y - 1) / (int)gridDim.y;
   const int sbeg = (int)blockIdx.y * sps;
   const int steps = max(min(sps, steps_all - sbeg), 0);
-  // rows past M read row M - 1 (never stored; rows are independent in the
-  // MFMA and in the amax groups). An unconditional load matters: a select on
-  // the load's destination would make every prefetch wait for the previous one.
+  // With a low-rank pass (six or more loads per step) the loads read whole
+  // lines: lane l reads 16 bytes (chunk l % 8) of row l / 8 and of row 8 + l / 8
+  // of the 16-row block, so one instruction covers 8 128-byte lines (the vector
+  // memory unit's time per instruction grows with the number of lines it
+  // touches: 16 half lines cost about three times as much), and relayout()
+  // moves the values to the MFMA layout. Without one (two loads per step) that
+  // detour costs more than it saves, and lane l reads its own chunks of row
+  // l % 16 directly. Rows past M read row M - 1 (never stored; rows are
+  // independent in the MFMA and in the amax groups). An unconditional load
+  // matters: a select on the load's destination would make every prefetch wait
+  // for the previous one.
+  constexpr bool kLines = NCB > 0;
+  const int r8 = lane >> 3, c8 = lane & 7;
   const size_t xrow = (size_t)min(row, M - 1) * (size_t)K;
+  const size_t xrow_a = (size_t)min(m0 + r8, M - 1) * (size_t)K;
+  const size_t xrow_b = (size_t)min(m0 + 8 + r8, M - 1) * (size_t)K;
 
   // smooth_inv into LDS; called after the first loads of X are out, so the two
   // latencies overlap
@@ -138,9 +163,11 @@ void quantize_act_kernel(const uint16_t* __restrict__ X, const float* __restrict
     }
   };
 
-  // One step's loads: this lane's two 8-channel chunks of X and the matching
-  // lora_down operands. Register sets rotate so that the loads of the next one
-  // or two steps of the wave are in flight while a step is processed.
+  // One step's loads: X's 16 rows x 64 channels and each 16-rank block of
+  // lora_down over the same channels, as whole lines (rows r8 and 8 + r8, chunk
+  // c8); relayout() turns them into the MFMA operand layout. Register sets rotate
+  // so that the loads of the next one or two steps of the wave are in flight
+  // while a step is processed.
   struct Step {
     uint4 xa, xb;
     uint4 lb[NL][2];
@@ -150,15 +177,61 @@ void quantize_act_kernel(const uint16_t* __restrict__ X, const float* __restrict
   // vmcnt bookkeeping unsure how many are in flight, and every use would then
   // wait for all of them.
   auto load = [&](Step& d, int s) {
-    const int k0 = (sbeg + min(s, steps - 1)) * 64 + q4 * 8;
-    d.xa = *reinterpret_cast<const uint4*>(X + xrow + k0);
-    d.xb = *reinterpret_cast<const uint4*>(X + xrow + k0 + 32);
+    if constexpr (!kLines) {
+      const int k0 = (sbeg + min(s, steps - 1)) * 64 + q4 * 8;
+      d.xa = *reinterpret_cast<const uint4*>(X + xrow + k0);
+      d.xb = *reinterpret_cast<const uint4*>(X + xrow + k0 + 32);
+      return;
+    }
+    const int k0 = (sbeg + min(s, steps - 1)) * 64 + c8 * 8;
+    d.xa = *reinterpret_cast<const uint4*>(X + xrow_a + k0);
+    d.xb = *reinterpret_cast<const uint4*>(X + xrow_b + k0);
     if constexpr (NCB > 0) {
 #pragma unroll
       for (int c = 0; c < NCB; ++c) {
-        const uint16_t* pb = lora_down + (size_t)(c * 16 + (lane & 15)) * K + k0;
-        d.lb[c][0] = *reinterpret_cast<const uint4*>(pb);
-        d.lb[c][1] = *reinterpret_cast<const uint4*>(pb + 32);
+        d.lb[c][0] = *reinterpret_cast<const uint4*>(lora_down + (size_t)(c * 16 + r8) * K + k0);
+        d.lb[c][1] = *reinterpret_cast<const uint4*>(lora_down + (size_t)(c * 16 + 8 + r8) * K + k0);
+      }
+    }
+  };
+
+  // Through this wave's scratch, [block][16 rows][8 chunks of 16 bytes] with the
+  // chunk slot XOR-ed with the row (conflict-free 16-byte accesses both ways),
+  // into the MFMA operand layout: lane l then holds row (rank) l % 16 and chunks
+  // q4 and 4 + q4, i.e. channels 8 q4 .. +8 and 32 + 8 q4 .. +8 of the step.
+  // Block 0 takes X, block 1 the rank blocks in turn. One wave's LDS accesses
+  // complete in order; the fences only keep the compiler from moving them
+  // across each other.
+  auto wave_fence = [&]() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  auto relayout = [&](Step& d) {
+    const int r16 = lane & 15;
+    auto put = [&](int blk, int rr, const uint4& v) { scr[blk * 128 + rr * 8 + (c8 ^ (rr & 7))] = v; };
+    auto get = [&](int blk, int h) { return scr[blk * 128 + r16 * 8 + ((4 * h + q4) ^ (r16 & 7))]; };
+    wave_fence();   // the previous step's reads are done
+    put(0, r8, d.xa);
+    put(0, 8 + r8, d.xb);
+    {
+      put(1, r8, d.lb[0][0]);
+      put(1, 8 + r8, d.lb[0][1]);
+    }
+    wave_fence();
+    d.xa = get(0, 0);
+    d.xb = get(0, 1);
+    {
+      d.lb[0][0] = get(1, 0);
+      d.lb[0][1] = get(1, 1);
+#pragma unroll
+      for (int c = 1; c < NCB; ++c) {
+        wave_fence();
+        put(1, r8, d.lb[c][0]);
+        put(1, 8 + r8, d.lb[c][1]);
+        wave_fence();
+        d.lb[c][0] = get(1, 0);
+        d.lb[c][1] = get(1, 1);
       }
     }
   };
@@ -220,7 +293,9 @@ void quantize_act_kernel(const uint16_t* __restrict__ X, const float* __restrict
   };
 
   // process step s into round buffer rb (its column is this wave's index)
-  auto process = [&](const Step& d, int s, uint8_t* rb) {
+  auto process = [&](const Step& dl, int s, uint8_t* rb) {
+    Step d = dl;
+    if constexpr (kLines) relayout(d);
     const int k0 = (sbeg + s) * 64 + q4 * 8;
     if constexpr (NCB > 0) {
 #pragma unroll
@@ -411,6 +486,7 @@ void quantize_act_kernel(const uint16_t* __restrict__ X, const float* __restrict
   }
 
   if constexpr (NCB > 0) {
+    __syncthreads();   // every wave is done with its scratch, which the partials reuse
     // lane l holds rows (l/16)*4 + i, column c*16 + l%16 of the wave's partial
 #pragma unroll
     for (int c = 0; c < NCB; ++c)
