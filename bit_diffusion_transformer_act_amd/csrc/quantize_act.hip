@@ -382,10 +382,33 @@ void quantize_act_kernel(const uint16_t* __restrict__ X, const float* __restrict
         const float d = e4m3_to_f32(sc[h]) * gs;
         w[h] = 0;
         if (d != 0.0f) {
-          w[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[h], v[0] / d, v[1] / d, 1.0f, 0);
-          w[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[h], v[2] / d, v[3] / d, 1.0f, 1);
-          w[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[h], v[4] / d, v[5] / d, 1.0f, 2);
-          w[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[h], v[6] / d, v[7] / d, 1.0f, 3);
+          // u = fl32(x_hat / d) without a division per value: y = x_hat * rcp(d)
+          // (rcp within 1 ulp, one rounding of the product) is within 3.5 ulp of
+          // u, so the two convert to the same E2M1 code unless a rounding
+          // boundary of E2M1 (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5; ties to even)
+          // lies between them or on one. Every boundary has its low 21 mantissa
+          // bits zero, so y is then within 8 units of 0 mod 2^21 in its low bits
+          // (below a power-of-two boundary the mantissa is near all ones): such
+          // blocks, and divisors near either end of the fp32 range (whose
+          // reciprocal would leave the normal range), take the IEEE division.
+          float u[8];
+          bool exact = !(d >= 0x1p-125f && d <= 0x1p125f);
+          if (!exact) {
+            const float rd = __builtin_amdgcn_rcpf(d);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              u[i] = v[i] * rd;
+              exact |= ((__float_as_uint(u[i]) + 8u) & 0x1FFFFFu) <= 16u;
+            }
+          }
+          if (exact) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) u[i] = v[i] / d;
+          }
+          w[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[h], u[0], u[1], 1.0f, 0);
+          w[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[h], u[2], u[3], 1.0f, 1);
+          w[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[h], u[4], u[5], 1.0f, 2);
+          w[h] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w[h], u[6], u[7], 1.0f, 3);
         }
       }
       *reinterpret_cast<uint32_t*>(crow) = w[0];

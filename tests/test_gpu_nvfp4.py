@@ -90,6 +90,34 @@ def test_quantize_act_nvfp4_extremes(P):
         assert np.array_equal(host(scales), scales_ref), ga
 
 
+def test_quantize_act_nvfp4_ties(P):
+    """Quotients on an E2M1 rounding boundary (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5)
+    or a few fp16 ulps from one, with block divisors that are not powers of two
+    (1.25, 1.5, 1.75 at a per-tensor scale of 1): where a reciprocal multiply
+    would land on the other side of a tie, the codes must still be those of the
+    correctly rounded quotient."""
+    M, K = 48, 512
+    rng = np.random.default_rng(41)
+    bounds = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    X = np.zeros((M, K), np.float16)
+    for m in range(M):
+        for j in range(K // 16):
+            dv = (1.25, 1.5, 1.75)[(m + j) % 3]
+            blk = (rng.choice(bounds, 16) * dv).astype(np.float16)
+            for t in range(16):                      # a third exact, the rest 1-3 ulps off
+                for _ in range(int(rng.integers(0, 4)) if t % 3 else 0):
+                    blk[t] = np.nextafter(blk[t], np.float16(np.inf if rng.integers(2) else -np.inf),
+                                          dtype=np.float16)
+            blk[0] = np.float16(6.0 * dv)            # amax: the block scale is exactly dv
+            blk = np.minimum(blk, np.float16(6.0 * dv))
+            X[m, 16 * j:16 * j + 16] = blk * rng.choice(np.array([-1, 1], np.float16), 16)
+    si = np.ones(K, np.float32)
+    _, packed_ref, scales_ref = oracle.quantize_act_ref(X, si, "nvfp4_g16", np.float32(1.0))
+    codes, scales, _ = P.svdq_quantize_act_nvfp4(dev(X), dev(si), None, 1.0)
+    assert np.array_equal(host(scales), scales_ref)
+    assert np.array_equal(host(codes), packed_ref)
+
+
 def _gemm_case(P, M, K, N, r, epi, seed=1):
     d, si, ga, layer = nv_layer(M, K, N, r, seed)
     codes_u, packed, scales = oracle.quantize_act_ref(d["X"], si, "nvfp4_g16", ga)
