@@ -214,25 +214,21 @@ void quantize_act_kernel(const uint16_t* __restrict__ X, const float* __restrict
     wave_fence();   // the previous step's reads are done
     put(0, r8, d.xa);
     put(0, 8 + r8, d.xb);
-    {
-      put(1, r8, d.lb[0][0]);
-      put(1, 8 + r8, d.lb[0][1]);
-    }
+    put(1, r8, d.lb[0][0]);
+    put(1, 8 + r8, d.lb[0][1]);
     wave_fence();
     d.xa = get(0, 0);
     d.xb = get(0, 1);
-    {
-      d.lb[0][0] = get(1, 0);
-      d.lb[0][1] = get(1, 1);
+    d.lb[0][0] = get(1, 0);
+    d.lb[0][1] = get(1, 1);
 #pragma unroll
-      for (int c = 1; c < NCB; ++c) {
-        wave_fence();
-        put(1, r8, d.lb[c][0]);
-        put(1, 8 + r8, d.lb[c][1]);
-        wave_fence();
-        d.lb[c][0] = get(1, 0);
-        d.lb[c][1] = get(1, 1);
-      }
+    for (int c = 1; c < NCB; ++c) {   // the next rank block through the same slot
+      wave_fence();
+      put(1, r8, d.lb[c][0]);
+      put(1, 8 + r8, d.lb[c][1]);
+      wave_fence();
+      d.lb[c][0] = get(1, 0);
+      d.lb[c][1] = get(1, 1);
     }
   };
 
