@@ -110,3 +110,50 @@ def test_gemv_largest_n(P):
     yh = host(y)
     assert yh.shape == (3, 1 << 20) and np.isfinite(yh).all()
     assert rel_l2(yh, y_ref) <= Y_TOL
+
+
+def _bf(a):
+    """host values -> float32 array of bf16 values (torch's CPU rounding)"""
+    return torch.from_numpy(np.asarray(a, np.float32)).to(torch.bfloat16).float().numpy()
+
+
+def _dbf(a):
+    return torch.from_numpy(np.ascontiguousarray(_bf(a))).to(torch.bfloat16).to(DEV)
+
+
+@pytest.mark.parametrize("fmt", ["int4_g64", "nvfp4_g16"])
+def test_largest_k_and_rank_bf16(P, fmt):
+    """The same K 65536 / rank 128 layer in the bf16 compute dtype: inputs are
+    the seeded draws rounded to bf16, outputs against the oracle's float64
+    result rounded to bf16."""
+    M, K, N, r = 130, 65536, 256, 128
+    cfg = synth.LayerConfig(f"limit_bf_{fmt}", 82, M, K, N, r, fmt, "none", "normal", 0.005, 30.0)
+    p = synth.random_quantized_layer(cfg, seed=3)
+    X, ld, lu, b = (_bf(p[k].astype(np.float32)) for k in ("X", "lora_down", "lora_up", "bias"))
+    ga = oracle.nvfp4_act_global_scale(X, p["smooth_inv"]) if fmt == "nvfp4_g16" else None
+    cu, c_ref, s_ref = oracle.quantize_act_ref(X, p["smooth_inv"], fmt, ga)
+    la_o = oracle.bf16_round(oracle.lora_act_ref(X, ld).astype(np.float32))
+    if fmt == "nvfp4_g16":
+        codes, scales, la = P.svdq_quantize_act_nvfp4(_dbf(X), dev(p["smooth_inv"]), _dbf(ld), float(ga))
+    else:
+        codes, scales, la = P.svdq_quantize_act(_dbf(X), dev(p["smooth_inv"]), _dbf(ld), fmt)
+    assert np.array_equal(host(codes), c_ref)
+    s = host(scales)
+    if fmt == "int4_g64":
+        assert np.array_equal(s.view(np.uint16), np.asarray(s_ref, np.float16).view(np.uint16))
+    else:
+        assert np.array_equal(s, s_ref)
+    assert rel_l2(la.float().cpu().numpy(), la_o) <= LORA_TOL
+    if fmt == "nvfp4_g16":
+        Y = P.svdq_gemm_nvfp4(codes, scales, _dbf(la_o), dev(p["w_codes"]), dev(p["w_scales"]), _dbf(lu), _dbf(b),
+                              float(np.float32(ga) * np.float32(p["w_gscale"])), "none")
+        kw = dict(act_gscale=ga, w_gscale=p["w_gscale"])
+    else:
+        Y = P.svdq_gemm_w4a4(codes, scales, _dbf(la_o), dev(p["w_codes"]), dev(p["w_scales"]), _dbf(lu), _dbf(b),
+                             fmt, "none")
+        kw = {}
+    assert Y.dtype == torch.bfloat16
+    y = Y.float().cpu().numpy()
+    wu = oracle.unpack_nibbles(p["w_codes"], signed=(fmt == "int4_g64"))
+    y_ref = oracle.gemm_ref(cu, s_ref, la_o, wu, p["w_scales"], lu, b, fmt, "none", **kw)
+    assert rel_l2(y, oracle.bf16_round(y_ref.astype(np.float32))) <= Y_TOL
