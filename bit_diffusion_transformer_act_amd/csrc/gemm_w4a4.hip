@@ -70,11 +70,18 @@ template <int WM, int WN, int STAGES>
 struct GemmShape {
   static constexpr int BM = 64 * WM, BN = 64 * WN;
   static constexpr int A_BYTES = BM * 64, B_BYTES = BN * 64;
-  static constexpr int SC_INSTR = (BM + BN + 255) / 256;     // scale DMAs per wave per step
-  static constexpr int SC_ROWS = SC_INSTR * 256;
-  static constexpr int STAGE = A_BYTES + B_BYTES + SC_ROWS * 4;
-  static constexpr int LDS = STAGES * STAGE;
-  static constexpr int DMA_PER_STEP = BM / 64 + BN / 64 + SC_INSTR;  // per thread
+  static constexpr int SC_ROWS = (BM + BN + 255) / 256 * 256;   // scale rows (A, B, padding)
+  static constexpr int STAGE = A_BYTES + B_BYTES;                 // one step's codes
+  // Scales go in groups of two steps, [SC_ROWS][2] 4-byte words (a row's words of
+  // steps 2g and 2g + 1 are adjacent in memory, so two lanes per row read one
+  // line where one lane per row and step would read two). A group is loaded with
+  // the codes of its first step; STAGES / 2 + 1 slots keep a slot from being
+  // refilled while its steps are still read.
+  static constexpr int SC_SLOTS = STAGES / 2 + 1;
+  static constexpr int SC_GROUP = SC_ROWS * 8;
+  static constexpr int SC_GINSTR = SC_GROUP / 1024;               // dword DMAs per wave per group
+  static constexpr int LDS = STAGES * STAGE + SC_SLOTS * SC_GROUP;
+  static constexpr int NC = BM / 64 + BN / 64;                    // code DMAs per thread per step
 };
 
 // 3 waves per SIMD (at most 168 VGPRs): the INT4 inner loop is VALU-bound and
@@ -118,8 +125,8 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restr
   // ---- DMA source pointers (per lane) for step 0; advance by 64 B (codes) / 4 B (scales)
   const uint8_t* ga[BM / 64];
   const uint8_t* gb[BN / 64];
-  const uint8_t* gs[S::SC_INSTR];
-  uint32_t la_off[BM / 64], lb_off[BN / 64], ls_off[S::SC_INSTR];
+  const uint8_t* gs[S::SC_GINSTR];
+  uint32_t la_off[BM / 64], lb_off[BN / 64], ls_off[S::SC_GINSTR];
   const uint32_t lds0 = lds_addr(smem);
 #pragma unroll
   for (int i = 0; i < BM / 64; ++i) {
@@ -140,15 +147,16 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restr
     lb_off[i] = S::A_BYTES + rloc * 64;
   }
 #pragma unroll
-  for (int i = 0; i < S::SC_INSTR; ++i) {
-    const int rloc = (wave * S::SC_INSTR + i) * 64;
-    const int row = rloc + lane;   // rows [0, BM) are A, [BM, BM + BN) are B, beyond: padding
+  for (int i = 0; i < S::SC_GINSTR; ++i) {
+    // 32 rows per instruction, lanes 2 j and 2 j + 1 on row rloc + j (its words of the group's two steps)
+    const int rloc = (wave * S::SC_GINSTR + i) * 32;
+    const int row = rloc + (lane >> 1);   // rows [0, BM) are A, [BM, BM + BN) are B, beyond: padding
     const uint8_t* p;
     if (row < BM) p = reinterpret_cast<const uint8_t*>(act_scales) + (size_t)min(m0 + row, M - 1) * sstride;
     else if (row < BM + BN) p = reinterpret_cast<const uint8_t*>(w_scales) + (size_t)(n0 + row - BM) * sstride;
     else p = reinterpret_cast<const uint8_t*>(w_scales) + (size_t)n0 * sstride;
     gs[i] = p;
-    ls_off[i] = S::A_BYTES + S::B_BYTES + rloc * 4;
+    ls_off[i] = rloc * 8;
   }
 
   auto issue = [&](int ks) {
@@ -157,8 +165,12 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restr
     for (int i = 0; i < BM / 64; ++i) dma16(ga[i] + ks * 64, base + la_off[i]);
 #pragma unroll
     for (int i = 0; i < BN / 64; ++i) dma16(gb[i] + ks * 64, base + lb_off[i]);
+    if ((ks & 1) == 0) {   // the scale group of steps ks and ks + 1 (the last step again past nk)
+      const uint32_t sb = lds0 + (uint32_t)(STAGES * S::STAGE + ((ks >> 1) % S::SC_SLOTS) * S::SC_GROUP);
+      const int sst = min(ks + (lane & 1), nk - 1);
 #pragma unroll
-    for (int i = 0; i < S::SC_INSTR; ++i) dma4(gs[i] + ks * 4, base + ls_off[i]);
+      for (int i = 0; i < S::SC_GINSTR; ++i) dma4(gs[i] + sst * 4, sb + ls_off[i]);
+    }
   };
 
   // prologue loads go out before the low-rank product so they overlap it
@@ -256,15 +268,36 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restr
   for (int cb = 0; cb < WN; ++cb) brow[cb] = wn * 32 * WN + cb * 32 + l32;
 
   for (int ks = 0; ks < nk; ++ks) {
-    if (ks + STAGES - 2 < nk) waitvm<S::DMA_PER_STEP * (STAGES - 2)>();
-    else waitvm<0>();
+    // issue(j) puts NC code DMAs in flight, and SC_GINSTR scale DMAs more when j is
+    // even; the batches of the STAGES - 2 steps after ks may stay outstanding
+    constexpr int NC = S::NC, NG = S::SC_GINSTR;
+    static_assert(STAGES == 3 || STAGES == 4, "wait counts are written out for 3 and 4 stages");
+    if constexpr (STAGES == 3) {
+      if (ks + 1 < nk) {
+        if (ks & 1) waitvm<NC + NG>();
+        else waitvm<NC>();
+      } else {
+        waitvm<0>();
+      }
+    } else {
+      if (ks + 2 < nk) {
+        waitvm<2 * NC + NG>();
+      } else if (ks + 1 < nk) {
+        if (ks & 1) waitvm<NC + NG>();
+        else waitvm<NC>();
+      } else {
+        waitvm<0>();
+      }
+    }
     __syncthreads();
     if (ks + STAGES - 1 < nk) issue(ks + STAGES - 1);
 
     const uint8_t* st = smem + (ks % STAGES) * S::STAGE;
     const uint8_t* sA = st;
     const uint8_t* sB = st + S::A_BYTES;
-    const uint32_t* sS = reinterpret_cast<const uint32_t*>(st + S::A_BYTES + S::B_BYTES);
+    // this step's scale words: word ks & 1 of each row in the slot of group ks / 2
+    const uint32_t* sS = reinterpret_cast<const uint32_t*>(smem + STAGES * S::STAGE +
+                                                           ((ks >> 1) % S::SC_SLOTS) * S::SC_GROUP) + (ks & 1);
 
     if constexpr (FMT == 0) {
       // INT4 on v_mfma_i32_16x16x64_i8: the wave tile is (2 WM) x (2 WN) blocks
@@ -277,10 +310,13 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restr
       uint4 sxw[RB];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
-        sxw[rb] = *reinterpret_cast<const uint4*>(sS + wm * 32 * WM + rb * 16 + lq * 4);
+      {
+        const uint32_t* q = sS + 2 * (wm * 32 * WM + rb * 16 + lq * 4);
+        sxw[rb] = make_uint4(q[0], q[2], q[4], q[6]);
+      }
       uint32_t sww[CB];
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) sww[cb] = sS[BM + wn * 32 * WN + cb * 16 + l16];
+      for (int cb = 0; cb < CB; ++cb) sww[cb] = sS[2 * (BM + wn * 32 * WN + cb * 16 + l16)];
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
         v4i av[RB], bv[CB];
@@ -335,9 +371,9 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restr
     } else {
       uint32_t ea[WM], eb[WN];
 #pragma unroll
-      for (int rb = 0; rb < WM; ++rb) ea[rb] = sS[arow[rb]];
+      for (int rb = 0; rb < WM; ++rb) ea[rb] = sS[2 * arow[rb]];
 #pragma unroll
-      for (int cb = 0; cb < WN; ++cb) eb[cb] = sS[BM + brow[cb]];
+      for (int cb = 0; cb < WN; ++cb) eb[cb] = sS[2 * (BM + brow[cb])];
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
         const int sh = 8 * (2 * g + lh);
