@@ -72,8 +72,8 @@ def parse():
 def layer_bytes(cfg, r):
     M, K, N = cfg.M, cfg.K, cfg.N
     sbytes = SCALE_BYTES_PER_ROW[cfg.fmt](K)
-    q = M * K * 2 + K * 4 + r * K * 2 + M * K // 2 + M * sbytes + M * r * 2
-    g = (M * K // 2 + M * sbytes + M * r * 2 + N * K // 2 + N * sbytes + N * r * 2 + N * 2
+    q = M * K * 2 + K * 4 + r * K * 2 + M * K // 2 + M * sbytes + M * r * 4   # lora_act is fp32
+    g = (M * K // 2 + M * sbytes + M * r * 4 + N * K // 2 + N * sbytes + N * r * 2 + N * 2
          + M * N * 2)
     return q, g
 
@@ -169,7 +169,7 @@ def main():
                 L["alpha"] = float(np.float32(p["act_gscale"]) * np.float32(p["w_gscale"]))
             L["codes"] = torch.empty((cfg.M, cfg.K // 2), dtype=torch.uint8, device=dev)
             L["scales"] = torch.empty((cfg.M, scols), dtype=sdt, device=dev)
-            L["lora_act"] = torch.empty((cfg.M, r), dtype=h, device=dev) if r else None
+            L["lora_act"] = torch.empty((cfg.M, r), dtype=torch.float32, device=dev) if r else None
             L["Y"] = torch.empty((cfg.M, cfg.N), dtype=h, device=dev)
             if cfg.epilogue == "qkv_norm_rope":
                 e = synth.qkv_epilogue_inputs(cfg.M, seed=0)

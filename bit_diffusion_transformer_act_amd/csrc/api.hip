@@ -85,7 +85,7 @@ const char* svdq_status_str(int status) {
 int svdq_device_check(int hip_device) { return check_device(hip_device); }
 
 int svdq_quantize_act(int fmt, int dtype, int M, int K, int r, const void* X, const float* smooth_inv,
-                      const void* lora_down, uint8_t* act_codes, void* act_scales, void* lora_act,
+                      const void* lora_down, uint8_t* act_codes, void* act_scales, float* lora_act,
                       void* stream) {
   if (fmt != SVDQ_INT4_G64 && fmt != SVDQ_FP4_E2M1_B32) return SVDQ_ERR_INVALID_ARG;
   if (!dtype_ok(dtype)) return SVDQ_ERR_INVALID_ARG;
@@ -104,7 +104,7 @@ int svdq_quantize_act(int fmt, int dtype, int M, int K, int r, const void* X, co
 }
 
 int svdq_gemm_w4a4(int fmt, int dtype, int M, int N, int K, int r, const uint8_t* act_codes,
-                   const void* act_scales, const void* lora_act, const uint8_t* w_codes,
+                   const void* act_scales, const float* lora_act, const uint8_t* w_codes,
                    const void* w_scales, const void* lora_up, const void* bias, int epi, void* Y,
                    void* stream) {
   if (fmt != SVDQ_INT4_G64 && fmt != SVDQ_FP4_E2M1_B32) return SVDQ_ERR_INVALID_ARG;
@@ -127,7 +127,7 @@ int svdq_gemm_w4a4(int fmt, int dtype, int M, int N, int K, int r, const uint8_t
 }
 
 int svdq_gemm_w4a4_qkv(int fmt, int dtype, int M, int N, int K, int r, const uint8_t* act_codes,
-                       const void* act_scales, const void* lora_act, const uint8_t* w_codes,
+                       const void* act_scales, const float* lora_act, const uint8_t* w_codes,
                        const void* w_scales, const void* lora_up, const void* bias,
                        const void* qk_norm_w, const float* rope, float eps, void* Y, void* stream) {
   if (fmt != SVDQ_INT4_G64) return SVDQ_ERR_INVALID_ARG;
@@ -158,10 +158,10 @@ size_t svdq_gemm_w4a4_mlp_workspace(int M, int N, int r2) {
 }
 
 int svdq_gemm_w4a4_mlp(int fmt, int dtype, int M, int N, int K, int r, const uint8_t* act_codes,
-                       const void* act_scales, const void* lora_act, const uint8_t* w_codes,
+                       const void* act_scales, const float* lora_act, const uint8_t* w_codes,
                        const void* w_scales, const void* lora_up, const void* bias,
                        const float* smooth_inv2, const void* lora_down2, int r2, uint8_t* act_codes2,
-                       void* act_scales2, void* lora_act2, void* workspace, size_t workspace_bytes,
+                       void* act_scales2, float* lora_act2, void* workspace, size_t workspace_bytes,
                        void* stream) {
   if (fmt != SVDQ_INT4_G64) return SVDQ_ERR_INVALID_ARG;
   if (!dtype_ok(dtype)) return SVDQ_ERR_INVALID_ARG;
@@ -189,14 +189,14 @@ int svdq_gemm_w4a4_mlp(int fmt, int dtype, int M, int N, int K, int r, const uin
   hipError_t e = svdq::launch_gemm_w4a4(fmt, dtype, M, N, K, r, act_codes, act_scales, lora_act, w_codes,
                                         w_scales, lora_up, bias, 3, nullptr, (hipStream_t)stream, nullptr, &ce);
   if (e == hipSuccess && r2 > 0)
-    e = svdq::launch_chain_reduce(dtype, M, r2, N / 128, static_cast<const float*>(workspace), lora_act2,
-                                  (hipStream_t)stream);
+    e = svdq::launch_chain_reduce(M, r2, N / 128, static_cast<const float*>(workspace),
+                                  lora_act2, (hipStream_t)stream);
   return finish(e);
 }
 
 int svdq_quantize_act_nvfp4(int dtype, int M, int K, int r, const void* X, const float* smooth_inv,
                             const void* lora_down, float act_gscale, uint8_t* act_codes,
-                            uint8_t* act_scales, void* lora_act, void* stream) {
+                            uint8_t* act_scales, float* lora_act, void* stream) {
   if (!dtype_ok(dtype)) return SVDQ_ERR_INVALID_ARG;
   if (M < 0 || M > (1 << 23) || !k_nv_ok(K) || !rank_ok(r)) return SVDQ_ERR_SHAPE;
   if (!positive_finite(act_gscale) || !positive_finite(6.0f * act_gscale)) return SVDQ_ERR_INVALID_ARG;
@@ -214,7 +214,7 @@ int svdq_quantize_act_nvfp4(int dtype, int M, int K, int r, const void* X, const
 }
 
 int svdq_gemm_nvfp4(int dtype, int M, int N, int K, int r, const uint8_t* act_codes,
-                    const uint8_t* act_scales, const void* lora_act, const uint8_t* w_codes,
+                    const uint8_t* act_scales, const float* lora_act, const uint8_t* w_codes,
                     const uint8_t* w_scales, const void* lora_up, const void* bias, float alpha,
                     int epilogue, void* Y, void* stream) {
   if (!dtype_ok(dtype)) return SVDQ_ERR_INVALID_ARG;

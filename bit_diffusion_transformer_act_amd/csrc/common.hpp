@@ -57,6 +57,40 @@ template <> struct Io<1> {
   }
 };
 
+// lora_act is fp32; the low-rank up-projection runs on the 16-bit matrix
+// instructions, so each value v enters as a pair of 16-bit operands hi =
+// h16(v), lo = h16(v - hi) (v - hi is exact in fp32) and the pair goes through
+// two MFMAs against the same lora_up operand. hi + lo equals v within
+// 2^-22 |v| for fp16 (plus 2^-25 absolute where lo is subnormal) and 2^-18 |v|
+// for bf16, where one 16-bit value alone would be off by up to 2^-11 |v| or
+// 2^-8 |v|.
+template <int IO>
+__device__ __forceinline__ void split_h16(float v, uint32_t& hi, uint32_t& lo) {
+  const uint16_t h = Io<IO>::from_f(v);
+  hi = h;
+  lo = Io<IO>::from_f(v - Io<IO>::to_f(h));
+}
+// four consecutive values -> (hi, lo) as two packed 4 x h16 operands
+template <int IO>
+__device__ __forceinline__ void split4_h16(float4 v, uint2& hi, uint2& lo) {
+  uint32_t h[4], l[4];
+  split_h16<IO>(v.x, h[0], l[0]);
+  split_h16<IO>(v.y, h[1], l[1]);
+  split_h16<IO>(v.z, h[2], l[2]);
+  split_h16<IO>(v.w, h[3], l[3]);
+  hi = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+  lo = make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
+}
+// eight consecutive values -> (hi, lo) as two packed 8 x h16 operands
+template <int IO>
+__device__ __forceinline__ void split8_h16(float4 a, float4 b, uint4& hi, uint4& lo) {
+  uint2 h0, l0, h1, l1;
+  split4_h16<IO>(a, h0, l0);
+  split4_h16<IO>(b, h1, l1);
+  hi = make_uint4(h0.x, h0.y, h1.x, h1.y);
+  lo = make_uint4(l0.x, l0.y, l1.x, l1.y);
+}
+
 constexpr int kWave = 64;
 
 __device__ __forceinline__ float lane_max_xor(float v, int mask) {

@@ -50,7 +50,7 @@ __device__ __forceinline__ int swz8(int row) { return (row >> 1) & 7; }
 template <int IO, int EPI>
 __global__ __launch_bounds__(256, 1)
 void gemm_fp4_big_kernel(const uint8_t* __restrict__ act_codes, const uint8_t* __restrict__ act_scales,
-                         const uint16_t* __restrict__ lora_act, const uint8_t* __restrict__ w_codes,
+                         const float* __restrict__ lora_act, const uint8_t* __restrict__ w_codes,
                          const uint8_t* __restrict__ w_scales, const uint16_t* __restrict__ lora_up,
                          const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y,
                          int M, int N, int K, int r) {
@@ -227,20 +227,22 @@ void gemm_fp4_big_kernel(const uint8_t* __restrict__ act_codes, const uint8_t* _
   }
   pair(2 * q, T_{}, F_{}, F_{});
 
-  // ---- low-rank up-projection: lora_act (fp16) times lora_up (fp16) into the
-  // same accumulators, v_mfma_f32_32x32x16_f16 (lane l: row l%32, ranks
-  // j0 + 8 (l/32) .. +8). The loads go out before the last pair's MFMAs.
-  constexpr int LR = 2;   // 16-rank blocks per round trip
-  auto lora_load = [&](uint4 (&ua)[RB][LR], uint4 (&ub)[CB][LR], int j0) {
+  // ---- low-rank up-projection: lora_act (fp32, as a hi + lo pair of 16-bit
+  // operands) times lora_up into the same accumulators, v_mfma_f32_32x32x16_f16
+  // (lane l: row l%32, ranks j0 + 8 (l/32) .. +8). The loads go out before the
+  // last pair's MFMAs.
+  constexpr int LR = 1;   // 16-rank blocks per round trip
+  auto lora_load = [&](float4 (&fa)[RB][LR][2], uint4 (&ub)[CB][LR], int j0) {
     const int nj = min(r - j0, 16 * LR) >> 4;
 #pragma unroll
     for (int h = 0; h < LR; ++h) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         const int m = m0 + arow[rb];
-        ua[rb][h] = (m < M && h < nj)
-                        ? *reinterpret_cast<const uint4*>(lora_act + (size_t)m * r + j0 + 16 * h + lh * 8)
-                        : make_uint4(0, 0, 0, 0);
+        const bool ok = m < M && h < nj;
+        const float* src = lora_act + (size_t)min(m, M - 1) * r + j0 + 16 * h + lh * 8;
+        fa[rb][h][0] = ok ? *reinterpret_cast<const float4*>(src) : make_float4(0.f, 0.f, 0.f, 0.f);
+        fa[rb][h][1] = ok ? *reinterpret_cast<const float4*>(src + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
       }
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
@@ -250,16 +252,22 @@ void gemm_fp4_big_kernel(const uint8_t* __restrict__ act_codes, const uint8_t* _
       }
     }
   };
-  auto lora_mma = [&](const uint4 (&ua)[RB][LR], const uint4 (&ub)[CB][LR]) {
+  auto lora_mma = [&](const float4 (&fa)[RB][LR][2], const uint4 (&ub)[CB][LR]) {
 #pragma unroll
     for (int h = 0; h < LR; ++h)
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
+      for (int rb = 0; rb < RB; ++rb) {
+        uint4 hi, lo;
+        split8_h16<IO>(fa[rb][h][0], fa[rb][h][1], hi, lo);
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
-          acc[rb][cb] = Io<IO>::mma32x32x16(ua[rb][h], ub[cb][h], acc[rb][cb]);
+        for (int cb = 0; cb < CB; ++cb) {
+          acc[rb][cb] = Io<IO>::mma32x32x16(hi, ub[cb][h], acc[rb][cb]);
+          acc[rb][cb] = Io<IO>::mma32x32x16(lo, ub[cb][h], acc[rb][cb]);
+        }
+      }
   };
-  uint4 ua[RB][LR], ub[CB][LR];
+  float4 ua[RB][LR][2];
+  uint4 ub[CB][LR];
   if (r > 0) lora_load(ua, ub, 0);
   pair(2 * q + 1, F_{}, F_{}, F_{});
   if (r > 0) {
@@ -314,7 +322,7 @@ hipError_t launch_gemm_fp4_big(int io, int M, int N, int K, int r, const uint8_t
   static std::atomic<uint64_t> raised[4] = {};
   const hipError_t e = raise_lds_limit(raised[v], reinterpret_cast<const void*>(kern), LDS);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(ntiles), dim3(256), LDS, st, ac, (const uint8_t*)as, (const uint16_t*)la, wc,
+  hipLaunchKernelGGL(kern, dim3(ntiles), dim3(256), LDS, st, ac, (const uint8_t*)as, (const float*)la, wc,
                      (const uint8_t*)ws, (const uint16_t*)lu, (const uint16_t*)bias, (uint16_t*)Y, M, N, K, r);
   return hipGetLastError();
 }

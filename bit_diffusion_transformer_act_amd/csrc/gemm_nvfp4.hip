@@ -72,7 +72,7 @@ __device__ __forceinline__ v8h nv_dequant8(uint32_t w, uint32_t spair) {
 template <int IO, int EPI, int BN>
 __global__ __launch_bounds__(256, 1)
 void gemm_nvfp4_kernel(const uint8_t* __restrict__ act_codes, const uint8_t* __restrict__ act_scales,
-                       const uint16_t* __restrict__ lora_act, const uint8_t* __restrict__ w_codes,
+                       const float* __restrict__ lora_act, const uint8_t* __restrict__ w_codes,
                        const uint8_t* __restrict__ w_scales, const uint16_t* __restrict__ lora_up,
                        const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, float alpha,
                        int M, int N, int K, int r) {
@@ -266,26 +266,35 @@ void gemm_nvfp4_kernel(const uint8_t* __restrict__ act_codes, const uint8_t* __r
   }
 
   // ---- per-tensor scales, then the low-rank up-projection into the same
-  // accumulators (v_mfma_f32_32x32x16_f16, lane l: row l%32, ranks 8 (l/32) .. +8)
+  // accumulators (v_mfma_f32_32x32x16_f16, lane l: row l%32, ranks 8 (l/32) .. +8;
+  // lora_act is fp32 and enters as a hi + lo pair of 16-bit operands)
 #pragma unroll
   for (int i = 0; i < RB; ++i)
 #pragma unroll
     for (int j = 0; j < CB; ++j) acc[i][j] *= alpha;
   for (int j0 = 0; j0 < r; j0 += 16) {
-    uint4 ua[RB], ub[CB];
+    float4 fa[RB][2];
+    uint4 ub[CB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const int m = min(m0 + arow[rb], M - 1);
-      ua[rb] = *reinterpret_cast<const uint4*>(lora_act + (size_t)m * r + j0 + lh * 8);
+      const float* src = lora_act + (size_t)m * r + j0 + lh * 8;
+      fa[rb][0] = *reinterpret_cast<const float4*>(src);
+      fa[rb][1] = *reinterpret_cast<const float4*>(src + 4);
     }
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
       ub[cb] = *reinterpret_cast<const uint4*>(lora_up + (size_t)(n0 + brow[cb]) * r + j0 + lh * 8);
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
+    for (int rb = 0; rb < RB; ++rb) {
+      uint4 hi, lo;
+      split8_h16<IO>(fa[rb][0], fa[rb][1], hi, lo);
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb)
-        acc[rb][cb] = Io<IO>::mma32x32x16(ua[rb], ub[cb], acc[rb][cb]);
+      for (int cb = 0; cb < CB; ++cb) {
+        acc[rb][cb] = Io<IO>::mma32x32x16(hi, ub[cb], acc[rb][cb]);
+        acc[rb][cb] = Io<IO>::mma32x32x16(lo, ub[cb], acc[rb][cb]);
+      }
+    }
   }
 
   // ---- epilogue: bias and activation, staged through LDS so that Y is written
@@ -327,7 +336,7 @@ static hipError_t launch_nv(int M, int N, int K, int r, const uint8_t* ac, const
   const hipError_t e = raise_lds_limit(raised, reinterpret_cast<const void*>(kern), LDS);
   if (e != hipSuccess) return e;
   const int ntiles = ((M + BM - 1) / BM) * (N / BN);
-  hipLaunchKernelGGL(kern, dim3(ntiles), dim3(256), LDS, st, ac, as, (const uint16_t*)la, wc, ws,
+  hipLaunchKernelGGL(kern, dim3(ntiles), dim3(256), LDS, st, ac, as, (const float*)la, wc, ws,
                      (const uint16_t*)lu, (const uint16_t*)bias, (uint16_t*)Y, alpha, M, N, K, r);
   return hipGetLastError();
 }

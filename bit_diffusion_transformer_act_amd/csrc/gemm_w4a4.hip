@@ -20,8 +20,8 @@
 // works on a contiguous range of tiles in 8-M-tile groups, which keeps the A
 // and B rows of concurrently running tiles in that XCD's L2.
 //
-// Accumulators start from the low-rank product: lora_act (fp16) times lora_up
-// on fp16 MFMAs (16 ranks per instruction), loads for 32 ranks in one batch.
+// Accumulators start from the low-rank product: lora_act (fp32, entering as a
+// hi + lo pair of 16-bit operands) times lora_up on 16-bit MFMAs.
 //
 // INT4_G64: each lane reads 8 packed bytes (16 codes) per 16-row block and
 // group; nibbles become int8 bytes holding 16 q (hi = w & 0xF0F0F0F0,
@@ -89,12 +89,15 @@ struct GemmShape {
 template <int IO, int FMT, int EPI, int WM, int WN, int STAGES>
 __global__ __launch_bounds__(256, 3)
 void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restrict__ act_scales,
-                      const uint16_t* __restrict__ lora_act, const uint8_t* __restrict__ w_codes,
+                      const float* __restrict__ lora_act, const uint8_t* __restrict__ w_codes,
                       const void* __restrict__ w_scales, const uint16_t* __restrict__ lora_up,
                       const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y,
                       int M, int N, int K, int r, QkvEpilogue qe, ChainEpilogue ce) {
   using S = GemmShape<WM, WN, STAGES>;
   constexpr int BM = S::BM, BN = S::BN;
+  // the 3-stage tiles rely on three workgroups per CU (the launch bound): their
+  // LDS must fit three times in the CU's 160 KB, or occupancy drops silently
+  static_assert(STAGES != 3 || 3 * S::LDS <= 160 * 1024, "three 3-stage workgroups must fit in a CU's LDS");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   const int tid = threadIdx.x;
@@ -196,59 +199,63 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restr
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
   if constexpr (FMT == 0) {
-    // v_mfma_f32_16x16x16_f16: lane l supplies row l%16, ranks j0 + 4 (l/16) .. +4.
+    // v_mfma_f32_16x16x16_f16: lane l supplies row l%16, ranks j0 + 4 (l/16) .. +4,
+    // as the hi and the lo halves of lora_act (two MFMAs per block and 16 ranks).
     // Loads for 16 ranks go out together (more would raise the register peak).
     const int l16 = lane & 15, lq = lane >> 4;
     for (int j0 = 0; j0 < r; j0 += 16) {
-      uint2 ua[RB4], ub[CB4];
-      {
+      float4 fa[RB4];
+      uint2 ub[CB4];
 #pragma unroll
-        for (int rb = 0; rb < RB4; ++rb) {
-          const int m = m0 + wm * 32 * WM + rb * 16 + l16;
-          ua[rb] = (m < M) ? *reinterpret_cast<const uint2*>(lora_act + (size_t)m * r + j0 + lq * 4)
-                           : make_uint2(0, 0);
-        }
+      for (int rb = 0; rb < RB4; ++rb) {
+        const int m = m0 + wm * 32 * WM + rb * 16 + l16;
+        fa[rb] = (m < M) ? *reinterpret_cast<const float4*>(lora_act + (size_t)m * r + j0 + lq * 4)
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int cb = 0; cb < CB4; ++cb) {
+        const int n = n0 + wn * 32 * WN + cb * 16 + l16;
+        ub[cb] = *reinterpret_cast<const uint2*>(lora_up + (size_t)n * r + j0 + lq * 4);
+      }
+#pragma unroll
+      for (int rb = 0; rb < RB4; ++rb) {
+        uint2 hi, lo;
+        split4_h16<IO>(fa[rb], hi, lo);
 #pragma unroll
         for (int cb = 0; cb < CB4; ++cb) {
-          const int n = n0 + wn * 32 * WN + cb * 16 + l16;
-          ub[cb] = *reinterpret_cast<const uint2*>(lora_up + (size_t)n * r + j0 + lq * 4);
+          acc4[rb][cb] = Io<IO>::mma16x16x16(hi, ub[cb], acc4[rb][cb]);
+          acc4[rb][cb] = Io<IO>::mma16x16x16(lo, ub[cb], acc4[rb][cb]);
         }
       }
-#pragma unroll
-      for (int rb = 0; rb < RB4; ++rb)
-#pragma unroll
-        for (int cb = 0; cb < CB4; ++cb)
-          acc4[rb][cb] = Io<IO>::mma16x16x16(ua[rb], ub[cb], acc4[rb][cb]);
     }
   } else {
-    // v_mfma_f32_32x32x16_f16: lane l supplies row l%32, ranks j0 + 8 (l/32) .. +8.
-    // Loads for 32 ranks are issued together so a tile pays one round trip.
-    for (int j0 = 0; j0 < r; j0 += 32) {
-      const int nj = min(r - j0, 32) >> 4;
-      uint4 ua[RB32][2], ub[CB32][2];
+    // v_mfma_f32_32x32x16_f16: lane l supplies row l%32, ranks j0 + 8 (l/32) .. +8,
+    // as the hi and the lo halves of lora_act.
+    for (int j0 = 0; j0 < r; j0 += 16) {
+      float4 fa[RB32][2];
+      uint4 ub[CB32];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-#pragma unroll
-        for (int rb = 0; rb < RB32; ++rb) {
-          const int m = m0 + wm * 32 * WM + rb * 32 + l32;
-          ua[rb][h] = (m < M && h < nj)
-                          ? *reinterpret_cast<const uint4*>(lora_act + (size_t)m * r + j0 + 16 * h + lh * 8)
-                          : make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int cb = 0; cb < CB32; ++cb) {
-          const int n = n0 + wn * 32 * WN + cb * 32 + l32;
-          ub[cb][h] = (h < nj) ? *reinterpret_cast<const uint4*>(lora_up + (size_t)n * r + j0 + 16 * h + lh * 8)
-                               : make_uint4(0, 0, 0, 0);
-        }
+      for (int rb = 0; rb < RB32; ++rb) {
+        const int m = m0 + wm * 32 * WM + rb * 32 + l32;
+        const float* src = lora_act + (size_t)m * r + j0 + lh * 8;
+        fa[rb][0] = (m < M) ? *reinterpret_cast<const float4*>(src) : make_float4(0.f, 0.f, 0.f, 0.f);
+        fa[rb][1] = (m < M) ? *reinterpret_cast<const float4*>(src + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
       }
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int cb = 0; cb < CB32; ++cb) {
+        const int n = n0 + wn * 32 * WN + cb * 32 + l32;
+        ub[cb] = *reinterpret_cast<const uint4*>(lora_up + (size_t)n * r + j0 + lh * 8);
+      }
 #pragma unroll
-        for (int rb = 0; rb < RB32; ++rb)
+      for (int rb = 0; rb < RB32; ++rb) {
+        uint4 hi, lo;
+        split8_h16<IO>(fa[rb][0], fa[rb][1], hi, lo);
 #pragma unroll
-          for (int cb = 0; cb < CB32; ++cb)
-            acc[rb][cb] = Io<IO>::mma32x32x16(ua[rb][h], ub[cb][h], acc[rb][cb]);
+        for (int cb = 0; cb < CB32; ++cb) {
+          acc[rb][cb] = Io<IO>::mma32x32x16(hi, ub[cb], acc[rb][cb]);
+          acc[rb][cb] = Io<IO>::mma32x32x16(lo, ub[cb], acc[rb][cb]);
+        }
+      }
     }
   }
 
@@ -614,12 +621,11 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restr
   }
 }
 
-// lora_act[m][j] = h16( sum_t partial[t][m][j] ), summed in the order t = 0, 1, ...
+// lora_act[m][j] = sum_t partial[t][m][j] (fp32), summed in the order t = 0, 1, ...
 // Each thread takes 4 consecutive elements (16-byte loads) and keeps the loads
 // of 8 tiles in flight ahead of the adds (the order of the adds is unchanged).
-template <int IO>
 __global__ __launch_bounds__(256)
-void chain_reduce_kernel(const float* __restrict__ partial, uint16_t* __restrict__ lora_act, int M, int r,
+void chain_reduce_kernel(const float* __restrict__ partial, float* __restrict__ lora_act, int M, int r,
                          int tiles) {
   const size_t n = (size_t)M * r;   // a multiple of 16 (r % 16 == 0)
   for (size_t e = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4; e < n; e += (size_t)gridDim.x * 256 * 4) {
@@ -644,21 +650,15 @@ void chain_reduce_kernel(const float* __restrict__ partial, uint16_t* __restrict
       s.z += v.z;
       s.w += v.w;
     }
-    lora_act[e] = Io<IO>::from_f(s.x);
-    lora_act[e + 1] = Io<IO>::from_f(s.y);
-    lora_act[e + 2] = Io<IO>::from_f(s.z);
-    lora_act[e + 3] = Io<IO>::from_f(s.w);
+    *reinterpret_cast<float4*>(lora_act + e) = s;
   }
 }
 
-hipError_t launch_chain_reduce(int io, int M, int r, int tiles, const float* partial, void* lora_act,
+hipError_t launch_chain_reduce(int M, int r, int tiles, const float* partial, float* lora_act,
                                hipStream_t st) {
   const size_t n4 = (size_t)M * r / 4;
   const int grid = (int)std::min<size_t>((n4 + 255) / 256, 2048);
-  if (io == 1)
-    hipLaunchKernelGGL(chain_reduce_kernel<1>, dim3(grid), dim3(256), 0, st, partial, (uint16_t*)lora_act, M, r, tiles);
-  else
-    hipLaunchKernelGGL(chain_reduce_kernel<0>, dim3(grid), dim3(256), 0, st, partial, (uint16_t*)lora_act, M, r, tiles);
+  hipLaunchKernelGGL(chain_reduce_kernel, dim3(grid), dim3(256), 0, st, partial, lora_act, M, r, tiles);
   return hipGetLastError();
 }
 
@@ -675,7 +675,7 @@ static hipError_t launch_cfg(int M, int N, int K, int r, const uint8_t* ac, cons
     if (e != hipSuccess) return e;
   }
   const int ntiles = ((M + S::BM - 1) / S::BM) * (N / S::BN);
-  hipLaunchKernelGGL(kern, dim3(ntiles), dim3(256), S::LDS, st, ac, as, (const uint16_t*)la, wc, ws,
+  hipLaunchKernelGGL(kern, dim3(ntiles), dim3(256), S::LDS, st, ac, as, (const float*)la, wc, ws,
                      (const uint16_t*)lu, (const uint16_t*)bias, (uint16_t*)Y, M, N, K, r, qe, ce);
   return hipGetLastError();
 }

@@ -44,7 +44,7 @@ struct QkvEpilogue {
 // down-projection's quantizer on the 16-bit result U: smoothing by
 // smooth_inv [N], INT4 g64 codes [M][N/2] and fp16 scales [M][N/64], and the
 // per-tile fp32 partials of U lora_down^T ([N/128][M][r], summed by
-// launch_chain_reduce into lora_act).
+// launch_chain_reduce into the fp32 lora_act).
 struct ChainEpilogue {
   const float* smooth_inv;
   const void* lora_down;
@@ -54,7 +54,7 @@ struct ChainEpilogue {
   float* partial;
 };
 
-hipError_t launch_chain_reduce(int io, int M, int r, int tiles, const float* partial, void* lora_act,
+hipError_t launch_chain_reduce(int M, int r, int tiles, const float* partial, float* lora_act,
                                hipStream_t stream);
 
 hipError_t launch_gemm_w4a4(int fmt, int io, int M, int N, int K, int r, const uint8_t* act_codes,

@@ -27,7 +27,7 @@
 // smooth_inv is staged in LDS once per workgroup (a global-load variant serves
 // K beyond the LDS budget). Partial low-rank sums of the W waves meet in LDS
 // and are added in a fixed order (then the slices', in slice order, when K is
-// split), so lora_act (stored in the 16-bit type) is deterministic.
+// split), so lora_act (stored in fp32) is deterministic.
 #include <atomic>
 
 #include "common.hpp"
@@ -84,7 +84,7 @@ template <int IO, int FMT, int NCB, int WAVES, bool SLDS, bool LORA_ONLY>
 __global__ __launch_bounds__(64 * WAVES)
 void quantize_act_kernel(const uint16_t* __restrict__ X, const float* __restrict__ smooth_inv,
                          const uint16_t* __restrict__ lora_down, uint8_t* __restrict__ codes,
-                         void* __restrict__ scales, uint16_t* __restrict__ lora_act,
+                         void* __restrict__ scales, float* __restrict__ lora_act,
                          int M, int K, float gs, float gs6, int rq) {
 #pragma clang fp contract(off)
   // LDS: the waves' re-layout scratch (reused after the main loop for the
@@ -155,7 +155,7 @@ void quantize_act_kernel(const uint16_t* __restrict__ X, const float* __restrict
                                                              (size_t)S * rq * 4);
             float sum = 0.f;
             for (int y = 0; y < S; ++y) sum += pp[y * rq + cc];
-            lora_act[(size_t)(m0 + rr) * rq + cc] = Io<IO>::from_f(sum);
+            lora_act[(size_t)(m0 + rr) * rq + cc] = sum;
           }
         }
         __syncthreads();   // every partial is read before this workgroup writes codes
@@ -523,7 +523,7 @@ void quantize_act_kernel(const uint16_t* __restrict__ X, const float* __restrict
           reinterpret_cast<float*>(codes + (size_t)(m0 + rr) * (K >> 1) + (K >> 1) -
                                    (size_t)gridDim.y * R * 4)[blockIdx.y * R + cc] = sum;
         else
-          lora_act[(size_t)(m0 + rr) * R + cc] = Io<IO>::from_f(sum);
+          lora_act[(size_t)(m0 + rr) * R + cc] = sum;
       }
     }
   }
@@ -542,7 +542,7 @@ static hipError_t launch_qws(int M, int K, int slices, const void* X, const floa
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((quantize_act_kernel<IO, FMT, NCB, WAVES, SLDS, LO>), grid, block, lds, st,
-                     (const uint16_t*)X, si, (const uint16_t*)ld, codes, scales, (uint16_t*)la, M, K, gs,
+                     (const uint16_t*)X, si, (const uint16_t*)ld, codes, scales, (float*)la, M, K, gs,
                      6.0f * gs, rq);
   return hipGetLastError();
 }

@@ -161,7 +161,7 @@ def svdq_quantize_act(X: torch.Tensor, smooth_inv: torch.Tensor, lora_down, fmt=
 
     X [M][K] in the layer's 16-bit type (float16 or bfloat16); smooth_inv fp32
     [K]; lora_down [r][K] (same 16-bit type) or None. Returns (act_codes u8
-    [M][K/2], act_scales fp16 [M][K/64] | u8 [M][K/32], lora_act [M][r] or
+    [M][K/2], act_scales fp16 [M][K/64] | u8 [M][K/32], lora_act fp32 [M][r] or
     None). Output tensors may be passed in.
     """
     f = _fmt(fmt)
@@ -182,11 +182,11 @@ def svdq_quantize_act(X: torch.Tensor, smooth_inv: torch.Tensor, lora_down, fmt=
     if act_scales is None:
         act_scales = torch.empty(sshape, dtype=sdt, device=dev)
     if r > 0 and lora_act is None:
-        lora_act = torch.empty((M, r), dtype=h, device=dev)
+        lora_act = torch.empty((M, r), dtype=torch.float32, device=dev)
     _check(act_codes, "act_codes", torch.uint8, (M, K // 2), dev)
     _check(act_scales, "act_scales", sdt, sshape, dev)
     if r > 0:
-        _check(lora_act, "lora_act", h, (M, r), dev)
+        _check(lora_act, "lora_act", torch.float32, (M, r), dev)
     with torch.cuda.device(dev):
         st = lib().svdq_quantize_act(f, io, M, K, r, _ptr(X), _ptr(smooth_inv), _ptr(lora_down),
                                      _ptr(act_codes), _ptr(act_scales),
@@ -199,10 +199,10 @@ def svdq_quantize_act(X: torch.Tensor, smooth_inv: torch.Tensor, lora_down, fmt=
 def svdq_gemm_w4a4(act_codes, act_scales, lora_act, w_codes, w_scales, lora_up, bias,
                    fmt="int4_g64", epilogue="none", out=None, dtype=None):
     """Fused 4-bit GEMM + low-rank up-projection + bias (+ GELU) -> Y [M][N] in
-    the layer's 16-bit type (dtype, else that of lora_act / lora_up / bias /
-    out, else float16)."""
+    the layer's 16-bit type (dtype, else that of lora_up / bias / out, else
+    float16); lora_act is fp32 [M][r]."""
     f = _fmt(fmt)
-    h = _pick_dtype(dtype, lora_act, lora_up, bias, out)
+    h = _pick_dtype(dtype, lora_up, bias, out)
     io = DTYPES[h]
     e = EPILOGUES[epilogue] if isinstance(epilogue, str) else int(epilogue)
     dev = act_codes.device
@@ -219,7 +219,7 @@ def svdq_gemm_w4a4(act_codes, act_scales, lora_act, w_codes, w_scales, lora_up, 
     _check(w_codes, "w_codes", torch.uint8, (N, KB), dev)
     _check(w_scales, "w_scales", sdt, sw_shape, dev)
     if r > 0:
-        _check(lora_act, "lora_act", h, (M, r), dev)
+        _check(lora_act, "lora_act", torch.float32, (M, r), dev)
         _check(lora_up, "lora_up", h, (N, r), dev)
     if bias is not None:
         _check(bias, "bias", h, (N,), dev)
@@ -259,7 +259,7 @@ def svdq_gemm_w4a4_qkv(act_codes, act_scales, lora_act, w_codes, w_scales, lora_
     _check(w_codes, "w_codes", torch.uint8, (N, KB), dev)
     _check(w_scales, "w_scales", sdt, sw_shape, dev)
     if r > 0:
-        _check(lora_act, "lora_act", h, (M, r), dev)
+        _check(lora_act, "lora_act", torch.float32, (M, r), dev)
         _check(lora_up, "lora_up", h, (N, r), dev)
     if bias is not None:
         _check(bias, "bias", h, (N,), dev)
@@ -283,12 +283,12 @@ def svdq_gemm_w4a4_mlp(act_codes, act_scales, lora_act, w_codes, w_scales, lora_
                        lora_act2=None, workspace=None, dtype=None):
     """The fused MLP chain: the up-projection with GELU, straight into the
     down-projection's INT4 quantizer. Returns (act_codes2 u8 [M][N/2],
-    act_scales2 fp16 [M][N/64], lora_act2 [M][r2] or None), what
+    act_scales2 fp16 [M][N/64], lora_act2 fp32 [M][r2] or None), what
     svdq_quantize_act would give on the up-projection's output. workspace:
     fp32 device memory of svdq_gemm_w4a4_mlp_workspace(M, N, r2) bytes (taken
     from torch's allocator when not given)."""
     f = _fmt(fmt)
-    h = _pick_dtype(dtype, lora_act, lora_up, bias, lora_down2)
+    h = _pick_dtype(dtype, lora_up, bias, lora_down2)
     io = DTYPES[h]
     dev = act_codes.device
     if dev.type != "cuda":
@@ -305,7 +305,7 @@ def svdq_gemm_w4a4_mlp(act_codes, act_scales, lora_act, w_codes, w_scales, lora_
     _check(w_codes, "w_codes", torch.uint8, (N, KB), dev)
     _check(w_scales, "w_scales", sdt, sw_shape, dev)
     if r > 0:
-        _check(lora_act, "lora_act", h, (M, r), dev)
+        _check(lora_act, "lora_act", torch.float32, (M, r), dev)
         _check(lora_up, "lora_up", h, (N, r), dev)
     if bias is not None:
         _check(bias, "bias", h, (N,), dev)
@@ -317,11 +317,11 @@ def svdq_gemm_w4a4_mlp(act_codes, act_scales, lora_act, w_codes, w_scales, lora_
     if act_scales2 is None:
         act_scales2 = torch.empty((M, N // 64), dtype=torch.float16, device=dev)
     if r2 > 0 and lora_act2 is None:
-        lora_act2 = torch.empty((M, r2), dtype=h, device=dev)
+        lora_act2 = torch.empty((M, r2), dtype=torch.float32, device=dev)
     _check(act_codes2, "act_codes2", torch.uint8, (M, N // 2), dev)
     _check(act_scales2, "act_scales2", torch.float16, (M, N // 64), dev)
     if r2 > 0:
-        _check(lora_act2, "lora_act2", h, (M, r2), dev)
+        _check(lora_act2, "lora_act2", torch.float32, (M, r2), dev)
     need = lib().svdq_gemm_w4a4_mlp_workspace(M, N, r2)
     if r2 > 0 and workspace is None:
         workspace = torch.empty(need // 4, dtype=torch.float32, device=dev)
@@ -342,8 +342,8 @@ def svdq_quantize_act_nvfp4(X: torch.Tensor, smooth_inv: torch.Tensor, lora_down
                             act_codes=None, act_scales=None, lora_act=None):
     """NVFP4 activation quantizer (E2M1 codes, E4M3 scale per 16, per-tensor
     scale act_gscale) + smoothing + low-rank down-projection.
-    Returns (act_codes u8 [M][K/2], act_scales u8 [M][K/16], lora_act [M][r] or
-    None); X, lora_down and lora_act share the layer's 16-bit type."""
+    Returns (act_codes u8 [M][K/2], act_scales u8 [M][K/16], lora_act fp32
+    [M][r] or None); X and lora_down share the layer's 16-bit type."""
     dev = X.device
     if dev.type != "cuda":
         raise ValueError("X must be a HIP device tensor")
@@ -360,11 +360,11 @@ def svdq_quantize_act_nvfp4(X: torch.Tensor, smooth_inv: torch.Tensor, lora_down
     if act_scales is None:
         act_scales = torch.empty((M, K // 16), dtype=torch.uint8, device=dev)
     if r > 0 and lora_act is None:
-        lora_act = torch.empty((M, r), dtype=h, device=dev)
+        lora_act = torch.empty((M, r), dtype=torch.float32, device=dev)
     _check(act_codes, "act_codes", torch.uint8, (M, K // 2), dev)
     _check(act_scales, "act_scales", torch.uint8, (M, K // 16), dev)
     if r > 0:
-        _check(lora_act, "lora_act", h, (M, r), dev)
+        _check(lora_act, "lora_act", torch.float32, (M, r), dev)
     with torch.cuda.device(dev):
         st = lib().svdq_quantize_act_nvfp4(io, M, K, r, _ptr(X), _ptr(smooth_inv), _ptr(lora_down),
                                            ctypes.c_float(act_gscale), _ptr(act_codes), _ptr(act_scales),
@@ -377,9 +377,10 @@ def svdq_quantize_act_nvfp4(X: torch.Tensor, smooth_inv: torch.Tensor, lora_down
 def svdq_gemm_nvfp4(act_codes, act_scales, lora_act, w_codes, w_scales, lora_up, bias, alpha: float,
                     epilogue="none", out=None, dtype=None):
     """NVFP4 GEMM + low-rank up-projection + bias (+ GELU) -> Y [M][N] in the
-    layer's 16-bit type; alpha = act_gscale * w_gscale scales the 4-bit sum."""
+    layer's 16-bit type; alpha = act_gscale * w_gscale scales the 4-bit sum;
+    lora_act is fp32 [M][r]."""
     e = EPILOGUES[epilogue] if isinstance(epilogue, str) else int(epilogue)
-    h = _pick_dtype(dtype, lora_act, lora_up, bias, out)
+    h = _pick_dtype(dtype, lora_up, bias, out)
     io = DTYPES[h]
     dev = act_codes.device
     if dev.type != "cuda":
@@ -393,7 +394,7 @@ def svdq_gemm_nvfp4(act_codes, act_scales, lora_act, w_codes, w_scales, lora_up,
     _check(w_codes, "w_codes", torch.uint8, (N, KB), dev)
     _check(w_scales, "w_scales", torch.uint8, (N, K // 16), dev)
     if r > 0:
-        _check(lora_act, "lora_act", h, (M, r), dev)
+        _check(lora_act, "lora_act", torch.float32, (M, r), dev)
         _check(lora_up, "lora_up", h, (N, r), dev)
     if bias is not None:
         _check(bias, "bias", h, (N,), dev)

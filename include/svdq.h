@@ -80,11 +80,12 @@ typedef enum { SVDQ_EPI_NONE = 0, SVDQ_EPI_GELU_TANH = 1 } svdq_epilogue;
 /* The layer's 16-bit compute type (the quantization_config's compute_dtype,
  * dothoosh.com article, quantization_config block; "bfloat16" in the pages'
  * example). Below, "h16" is this type: it is the type of X, lora_down,
- * lora_act, lora_up, bias, qk_norm_w and Y, and of the GEMV's x, bias and y.
+ * lora_up, bias, qk_norm_w and Y, and of the GEMV's x, bias and y.
  * Conversions to h16 round to nearest, ties to even; the low-rank products
- * run on the h16 matrix instructions with fp32 accumulation. Stored scales
- * keep their format's own type whatever dtype is (INT4 and AWQ: fp16). A value
- * outside this enum is SVDQ_ERR_INVALID_ARG. */
+ * run on the h16 matrix instructions with fp32 accumulation. lora_act, the
+ * low-rank activations between the two calls, is fp32 whatever dtype is.
+ * Stored scales keep their format's own type whatever dtype is (INT4 and AWQ:
+ * fp16). A value outside this enum is SVDQ_ERR_INVALID_ARG. */
 typedef enum { SVDQ_F16 = 0, SVDQ_BF16 = 1 } svdq_dtype;
 
 /* Returns SVDQ_OK iff HIP device `hip_device` exists and is a gfx950 part.
@@ -104,7 +105,7 @@ int svdq_version(void);
  * and per-group 4-bit activation quantization (one pass over X).
  *
  *   x_hat[m,k]   = fl32(fp32(X[m,k]) * smooth_inv[k])          (IEEE multiply)
- *   lora_act[m,j]= h16_rne(sum_k X[m,k] * lora_down[j,k])    (h16 inputs, fp32 accumulate)
+ *   lora_act[m,j]= sum_k X[m,k] * lora_down[j,k]             (h16 inputs, fp32 accumulate)
  *   INT4_G64, per row m and group g of 64 along K:
  *     amax = max |x_hat|;  s = fp16_rne(min(fl32(amax / 7), 65504));
  *     q = s == 0 ? 0 : clamp(rint_even(fl32(x_hat / s)), -7, 7)   (IEEE division)
@@ -114,8 +115,8 @@ int svdq_version(void);
  *     code = E2M1 nearest to x_hat / 2^e (ties to even mantissa), sign bit
  *     from x_hat's sign.
  * Codes and scales are bit-exact functions of (X, smooth_inv); lora_act is a
- * float result (fp32 accumulation in unspecified order, stored as h16 -- the
- * 16-bit low-rank branch -- which is what the GEMM's h16 matrix product takes).
+ * float result (fp32 accumulation in a fixed but unspecified order, stored in
+ * fp32).
  *
  * Arguments:
  *   fmt         svdq_format.
@@ -131,12 +132,12 @@ int svdq_version(void);
  *               the tails of these rows (scratch owned by the call until its
  *               work on `stream` completes; the final content is the codes).
  *   act_scales  out, fp16 [M][K/64] (INT4_G64) or u8 [M][K/32] (FP4_E2M1_B32).
- *   lora_act    out, h16 [M][r]; may be NULL iff r == 0.
+ *   lora_act    out, fp32 [M][r]; may be NULL iff r == 0.
  *   stream      hipStream_t.
  */
 int svdq_quantize_act(int fmt, int dtype, int M, int K, int r,
                       const void* X, const float* smooth_inv, const void* lora_down,
-                      uint8_t* act_codes, void* act_scales, void* lora_act,
+                      uint8_t* act_codes, void* act_scales, float* lora_act,
                       void* stream);
 
 /*
@@ -150,8 +151,11 @@ int svdq_quantize_act(int fmt, int dtype, int M, int K, int r,
  * INT4_G64 multiplies the codes exactly (int8 matrix cores, int32 per
  * group) and applies s_x s_w in fp32; FP4_E2M1_B32 uses the block-scaled
  * FP4 matrix instruction with the E8M0 scales applied in hardware and fp32
- * accumulation. lora_act is the h16 value the quantizer stored, for the low-rank product
- * (fp32 accumulation).
+ * accumulation. The low-rank product takes each fp32 lora_act value as a pair
+ * of h16 operands, hi = h16(v) and lo = h16(v - hi), on two matrix
+ * instructions with fp32 accumulation: hi + lo is v within 2^-22 |v| for fp16
+ * (2^-18 |v| for bf16), where one h16 value would be off by up to 2^-11 |v|
+ * (2^-8 |v|). |lora_act| must stay below the h16 maximum.
  *
  * Arguments:
  *   fmt         svdq_format.
@@ -161,7 +165,7 @@ int svdq_quantize_act(int fmt, int dtype, int M, int K, int r,
  *   r           low-rank width; r % 16 == 0, 0 <= r <= 128.
  *   act_codes   u8 [M][K/2] (from svdq_quantize_act).
  *   act_scales  fp16 [M][K/64] or u8 [M][K/32].
- *   lora_act    h16 [M][r]; may be NULL iff r == 0.
+ *   lora_act    fp32 [M][r] (from svdq_quantize_act); may be NULL iff r == 0.
  *   w_codes     u8 [N][K/2].
  *   w_scales    fp16 [N][K/64] or u8 [N][K/32].
  *   lora_up     h16 [N][r]; may be NULL iff r == 0.
@@ -171,7 +175,7 @@ int svdq_quantize_act(int fmt, int dtype, int M, int K, int r,
  *   stream      hipStream_t.
  */
 int svdq_gemm_w4a4(int fmt, int dtype, int M, int N, int K, int r,
-                   const uint8_t* act_codes, const void* act_scales, const void* lora_act,
+                   const uint8_t* act_codes, const void* act_scales, const float* lora_act,
                    const uint8_t* w_codes, const void* w_scales, const void* lora_up,
                    const void* bias, int epi, void* Y, void* stream);
 
@@ -201,7 +205,7 @@ int svdq_gemm_w4a4(int fmt, int dtype, int M, int N, int K, int r,
  * qk_norm_w / rope; otherwise as svdq_gemm_w4a4.
  */
 int svdq_gemm_w4a4_qkv(int fmt, int dtype, int M, int N, int K, int r,
-                       const uint8_t* act_codes, const void* act_scales, const void* lora_act,
+                       const uint8_t* act_codes, const void* act_scales, const float* lora_act,
                        const uint8_t* w_codes, const void* w_scales, const void* lora_up,
                        const void* bias, const void* qk_norm_w, const float* rope, float eps,
                        void* Y, void* stream);
@@ -219,7 +223,7 @@ int svdq_gemm_w4a4_qkv(int fmt, int dtype, int M, int N, int K, int r,
  *
  * The codes and scales equal the unfused path's bit for bit (the same U, the
  * same quantizer rule); lora_act2 is summed over the up-projection's tiles of
- * 128 columns in fp32, in a fixed order (deterministic), then rounded to h16.
+ * 128 columns in fp32, in a fixed order (deterministic), and stored in fp32.
  * Two kernels: the GEMM with the quantizer in its epilogue, and the sum of the
  * per-tile partials of the low-rank down-projection, kept in `workspace`.
  *
@@ -230,17 +234,17 @@ int svdq_gemm_w4a4_qkv(int fmt, int dtype, int M, int N, int K, int r,
  *   r2               its low-rank width; r2 % 16 == 0, 0 <= r2 <= 128.
  *   act_codes2       out, u8 [M][N/2]   (INT4 codes of U, the down-projection's K = N).
  *   act_scales2      out, fp16 [M][N/64].
- *   lora_act2        out, h16 [M][r2]; NULL iff r2 == 0.
+ *   lora_act2        out, fp32 [M][r2]; NULL iff r2 == 0.
  *   workspace        device memory of at least svdq_gemm_w4a4_mlp_workspace(M, N, r2)
  *                    bytes (fp32 partials), owned by the caller; NULL iff r2 == 0.
  *   workspace_bytes  its size (SVDQ_ERR_SHAPE if too small).
  */
 size_t svdq_gemm_w4a4_mlp_workspace(int M, int N, int r2);
 int svdq_gemm_w4a4_mlp(int fmt, int dtype, int M, int N, int K, int r,
-                       const uint8_t* act_codes, const void* act_scales, const void* lora_act,
+                       const uint8_t* act_codes, const void* act_scales, const float* lora_act,
                        const uint8_t* w_codes, const void* w_scales, const void* lora_up,
                        const void* bias, const float* smooth_inv2, const void* lora_down2, int r2,
-                       uint8_t* act_codes2, void* act_scales2, void* lora_act2,
+                       uint8_t* act_codes2, void* act_scales2, float* lora_act2,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -266,7 +270,7 @@ int svdq_gemm_w4a4_mlp(int fmt, int dtype, int M, int N, int K, int r,
 int svdq_quantize_act_nvfp4(int dtype, int M, int K, int r,
                             const void* X, const float* smooth_inv, const void* lora_down,
                             float act_gscale, uint8_t* act_codes, uint8_t* act_scales,
-                            void* lora_act, void* stream);
+                            float* lora_act, void* stream);
 
 /*
  * svdq_gemm_nvfp4 -- svdq_gemm_w4a4 for NVFP4 operands:
@@ -287,7 +291,7 @@ int svdq_quantize_act_nvfp4(int dtype, int M, int K, int r,
  *   alpha       finite (else SVDQ_ERR_INVALID_ARG).
  */
 int svdq_gemm_nvfp4(int dtype, int M, int N, int K, int r,
-                    const uint8_t* act_codes, const uint8_t* act_scales, const void* lora_act,
+                    const uint8_t* act_codes, const uint8_t* act_scales, const float* lora_act,
                     const uint8_t* w_codes, const uint8_t* w_scales, const void* lora_up,
                     const void* bias, float alpha, int epilogue, void* Y, void* stream);
 

@@ -175,8 +175,10 @@ def random_quantized_layer(cfg: LayerConfig, seed: int = 0, M: int | None = None
     lora_up = (g.standard_normal((N, r)) * 0.1).astype(np.float16)
     bias = (g.standard_normal(N) * cfg.bias_std).astype(np.float16)
     if cfg.fmt == "int4_g64":
-        lo = g.integers(-7, 8, (N, K // 2))
-        hi = g.integers(-7, 8, (N, K // 2))
+        # the whole two's-complement range: -8 is a valid weight code for the GEMM
+        # even though the symmetric quantizer never produces it
+        lo = g.integers(-8, 8, (N, K // 2))
+        hi = g.integers(-8, 8, (N, K // 2))
         w_scales = (g.uniform(0.004, 0.01, (N, K // 64))).astype(np.float16)
     elif cfg.fmt == "fp4_b32":
         lo = g.integers(0, 16, (N, K // 2))

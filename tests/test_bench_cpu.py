@@ -32,8 +32,8 @@ def test_layer_bytes_qkv():
     lora_down = 32 * 3072 * 2               # fp16, once
     codes = 4096 * 3072 // 2                # two codes per byte
     scales = 4096 * (3072 // 64) * 2        # one fp16 scale per 64
-    lora_act = 4096 * 32 * 2
-    assert q == x_read + smooth + lora_down + codes + scales + lora_act == 32_321_536
+    lora_act = 4096 * 32 * 4                # fp32
+    assert q == x_read + smooth + lora_down + codes + scales + lora_act == 32_583_680
     w = 9216 * 3072 // 2 + 9216 * (3072 // 64) * 2 + 9216 * 32 * 2 + 9216 * 2
     assert g == codes + scales + lora_act + w + 4096 * 9216 * 2
 

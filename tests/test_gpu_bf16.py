@@ -10,11 +10,10 @@ import torch
 
 import oracle
 import synth
+from tests.parity import LORA_TOL, Y_TOL, assert_close, band_rows, rel_l2  # noqa: F401
 
 pytestmark = pytest.mark.gpu
 
-Y_TOL = 2e-3
-LORA_TOL = 1e-3
 DEV = torch.device("cuda:0")
 
 
@@ -42,12 +41,6 @@ def dev(a):
 def host(t):
     torch.cuda.synchronize()
     return t.float().cpu().numpy() if t.dtype == torch.bfloat16 else t.cpu().numpy()
-
-
-def rel_l2(a, b):
-    a = np.asarray(a, np.float64)
-    b = np.asarray(b, np.float64)
-    return np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300)
 
 
 _cache = {}
@@ -86,14 +79,14 @@ def test_quantize_act_bf16(P, fmt, M, r):
     else:
         assert np.array_equal(sc, scales_ref)
     if r:
-        assert la.dtype == torch.bfloat16
-        la_ref = oracle.bf16_round(oracle.lora_act_ref(X, layer["lora_down"]).astype(np.float32))
-        assert rel_l2(host(la), la_ref) <= LORA_TOL
+        assert la.dtype == torch.float32
+        la_ref = oracle.lora_act_ref(X, layer["lora_down"])
+        assert_close(host(la), la_ref, LORA_TOL)
 
 
 def _gemm(P, fmt, layer, packed, scales, la, b, epi, alpha=None):
     lu = dbf(layer["lora_up"]) if layer["rank"] else None
-    la_t = dbf(la) if layer["rank"] else None
+    la_t = dev(la) if layer["rank"] else None
     if fmt == "nvfp4_g16":
         return P.svdq_gemm_nvfp4(dev(packed), dev(scales), la_t, dev(layer["w_codes"]), dev(layer["w_scales"]),
                                  lu, dbf(b), alpha, epi, dtype=torch.bfloat16)
@@ -107,13 +100,13 @@ def _gemm(P, fmt, layer, packed, scales, la, b, epi, alpha=None):
 def test_gemm_bf16(P, fmt, M, N, epi):
     X, b, si, ga, layer, _ = bf_layer(fmt, M=M, N=N, r=16)
     cu, packed, scales = oracle.quantize_act_ref(X, si, fmt, ga)
-    la = oracle.bf16_round(oracle.lora_act_ref(X, layer["lora_down"]).astype(np.float32))
+    la = oracle.lora_act_ref(X, layer["lora_down"]).astype(np.float32)
     alpha = float(np.float32(ga) * np.float32(layer["w_gscale"])) if fmt == "nvfp4_g16" else None
     y = _gemm(P, fmt, layer, packed, scales, la, b, epi, alpha)
     assert y.dtype == torch.bfloat16
     y_ref = oracle.gemm_ref(cu, scales, la, layer["w_codes_unpacked"], layer["w_scales"], layer["lora_up"], b,
                             fmt, epi, act_gscale=ga, w_gscale=layer.get("w_gscale"))
-    assert rel_l2(host(y), oracle.bf16_round(y_ref.astype(np.float32))) <= Y_TOL
+    assert_close(host(y), oracle.bf16_round(y_ref.astype(np.float32)))
 
 
 def test_gemm_fp4_large_tile_bf16(P):
@@ -125,9 +118,9 @@ def test_gemm_fp4_large_tile_bf16(P):
     ld, lu, b = bf(p["lora_down"].astype(np.float32)), bf(p["lora_up"].astype(np.float32)), bf(p["bias"].astype(np.float32))
     codes, scales, la = P.svdq_quantize_act(dbf(X), dev(p["smooth_inv"]), dbf(ld), "fp4_b32")
     # the GEMM takes the oracle's low-rank activations, the GPU's checked against them
-    la_o = oracle.bf16_round(oracle.lora_act_ref(X, ld).astype(np.float32))
-    assert rel_l2(host(la), la_o) <= LORA_TOL
-    y = P.svdq_gemm_w4a4(codes, scales, dbf(la_o), dev(p["w_codes"]), dev(p["w_scales"]), dbf(lu), dbf(b),
+    la_o = oracle.lora_act_ref(X, ld).astype(np.float32)
+    assert_close(host(la), la_o, LORA_TOL)
+    y = P.svdq_gemm_w4a4(codes, scales, dev(la_o), dev(p["w_codes"]), dev(p["w_scales"]), dbf(lu), dbf(b),
                          "fp4_b32", "gelu_tanh")
     rng = np.random.default_rng(5)
     rows = np.sort(rng.choice(cfg.M, 16, replace=False))
@@ -137,7 +130,7 @@ def test_gemm_fp4_large_tile_bf16(P):
     wu = oracle.unpack_nibbles(p["w_codes"][cols], signed=False)
     y_ref = oracle.gemm_ref(cu, s_ref, la_o[rows], wu, p["w_scales"][cols], lu[cols], b[cols], "fp4_b32",
                             "gelu_tanh")
-    assert rel_l2(host(y)[np.ix_(rows, cols)], oracle.bf16_round(y_ref.astype(np.float32))) <= Y_TOL
+    assert_close(host(y)[np.ix_(rows, cols)], oracle.bf16_round(y_ref.astype(np.float32)))
 
 
 def test_gemm_qkv_bf16(P):
@@ -147,14 +140,14 @@ def test_gemm_qkv_bf16(P):
     e = synth.qkv_epilogue_inputs(M, seed=3)
     qkw = bf(e["qk_norm_w"].astype(np.float32))
     cu, packed, scales = oracle.quantize_act_ref(X, si, "int4_g64")
-    la = oracle.bf16_round(oracle.lora_act_ref(X, layer["lora_down"]).astype(np.float32))
-    y = P.svdq_gemm_w4a4_qkv(dev(packed), dev(scales), dbf(la), dev(layer["w_codes"]), dev(layer["w_scales"]),
+    la = oracle.lora_act_ref(X, layer["lora_down"]).astype(np.float32)
+    y = P.svdq_gemm_w4a4_qkv(dev(packed), dev(scales), dev(la), dev(layer["w_codes"]), dev(layer["w_scales"]),
                              dbf(layer["lora_up"]), dbf(b), dbf(qkw), dev(e["rope"]), e["eps"])
     assert y.dtype == torch.bfloat16
     lin = oracle.gemm_ref(cu, scales, la, layer["w_codes_unpacked"], layer["w_scales"], layer["lora_up"], b,
                           "int4_g64")
     y_ref = oracle.qkv_epilogue_ref(lin, 128, qkw[0], qkw[1], e["rope"][..., 0], e["rope"][..., 1], e["eps"])
-    assert rel_l2(host(y), oracle.bf16_round(y_ref.astype(np.float32))) <= Y_TOL
+    assert_close(host(y), oracle.bf16_round(y_ref.astype(np.float32)))
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 3072, 18432), (6, 2048, 333)])
@@ -166,7 +159,7 @@ def test_awq_gemv_bf16(P, M, K, N):
     y = P.awq_gemv_w4a16(dbf(x), dev(p["codes"]), dev(p["scales"]), dev(p["zeros"]), bias=dbf(b))
     assert y.dtype == torch.bfloat16
     y_ref = oracle.gemv_ref(x, p["codes"], p["scales"], p["zeros"], bias=b)
-    assert rel_l2(host(y), oracle.bf16_round(y_ref.astype(np.float32))) <= Y_TOL
+    assert_close(host(y), oracle.bf16_round(y_ref.astype(np.float32)))
 
 
 def test_mixed_dtypes_rejected(P):

@@ -13,11 +13,10 @@ import torch
 
 import oracle
 import synth
+from tests.parity import LORA_TOL, Y_TOL, assert_close, band_rows, rel_l2  # noqa: F401
 
 pytestmark = pytest.mark.gpu
 
-Y_TOL = 2e-3
-LORA_TOL = 1e-3
 DEV = torch.device("cuda:0")
 
 
@@ -38,12 +37,6 @@ def host(t):
     return t.cpu().numpy()
 
 
-def rel_l2(a, b):
-    a = np.asarray(a, np.float64)
-    b = np.asarray(b, np.float64)
-    return np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300)
-
-
 def _layer_at(P, fmt, M, K, N, r, epi, cols):
     """Quantize X on the GPU (codes and scales checked on every row, lora_act
     against the oracle's), run the GEMM on the GPU's codes and the oracle's
@@ -53,7 +46,7 @@ def _layer_at(P, fmt, M, K, N, r, epi, cols):
     p = synth.random_quantized_layer(cfg, seed=1)
     ga = p.get("act_gscale")
     cu, c_ref, s_ref = oracle.quantize_act_ref(p["X"], p["smooth_inv"], fmt, ga)
-    la_o = oracle.lora_act_ref(p["X"], p["lora_down"]).astype(np.float16)
+    la_o = oracle.lora_act_ref(p["X"], p["lora_down"]).astype(np.float32)
     if fmt == "nvfp4_g16":
         codes, scales, la = P.svdq_quantize_act_nvfp4(dev(p["X"]), dev(p["smooth_inv"]), dev(p["lora_down"]),
                                                       float(ga))
@@ -65,7 +58,7 @@ def _layer_at(P, fmt, M, K, N, r, epi, cols):
         assert np.array_equal(s.view(np.uint16), np.asarray(s_ref, np.float16).view(np.uint16))
     else:
         assert np.array_equal(s, s_ref)
-    assert rel_l2(host(la), la_o) <= LORA_TOL
+    assert_close(host(la), la_o, LORA_TOL)
     if fmt == "nvfp4_g16":
         Y = P.svdq_gemm_nvfp4(codes, scales, dev(la_o), dev(p["w_codes"]), dev(p["w_scales"]), dev(p["lora_up"]),
                               dev(p["bias"]), float(np.float32(ga) * np.float32(p["w_gscale"])), epi)
@@ -87,7 +80,7 @@ def test_largest_k_and_rank(P, fmt):
     """K 65536, rank 128, M 130 (9 row blocks, the last ragged), N 256: all
     outputs."""
     y, y_ref = _layer_at(P, fmt, 130, 65536, 256, 128, "gelu_tanh", np.arange(256))
-    assert rel_l2(y, y_ref) <= Y_TOL
+    assert_close(y, y_ref)
 
 
 @pytest.mark.parametrize("fmt,K", [("int4_g64", 128), ("fp4_b32", 512), ("nvfp4_g16", 256)])
@@ -97,7 +90,7 @@ def test_largest_n(P, fmt, K):
     (first and last of each 256 included where sampled)."""
     cols = np.unique(np.concatenate([np.arange(0, 65536, 32), [65535]]))
     y, y_ref = _layer_at(P, fmt, 300, K, 65536, 16, "none", cols)
-    assert rel_l2(y, y_ref) <= Y_TOL
+    assert_close(y, y_ref)
 
 
 def test_gemv_largest_n(P):
@@ -109,7 +102,7 @@ def test_gemv_largest_n(P):
     y_ref = oracle.gemv_ref(p["x"], p["codes"], p["scales"], p["zeros"], bias=b)
     yh = host(y)
     assert yh.shape == (3, 1 << 20) and np.isfinite(yh).all()
-    assert rel_l2(yh, y_ref) <= Y_TOL
+    assert_close(yh, y_ref)
 
 
 def _bf(a):
@@ -132,7 +125,7 @@ def test_largest_k_and_rank_bf16(P, fmt):
     X, ld, lu, b = (_bf(p[k].astype(np.float32)) for k in ("X", "lora_down", "lora_up", "bias"))
     ga = oracle.nvfp4_act_global_scale(X, p["smooth_inv"]) if fmt == "nvfp4_g16" else None
     cu, c_ref, s_ref = oracle.quantize_act_ref(X, p["smooth_inv"], fmt, ga)
-    la_o = oracle.bf16_round(oracle.lora_act_ref(X, ld).astype(np.float32))
+    la_o = oracle.lora_act_ref(X, ld).astype(np.float32)
     if fmt == "nvfp4_g16":
         codes, scales, la = P.svdq_quantize_act_nvfp4(_dbf(X), dev(p["smooth_inv"]), _dbf(ld), float(ga))
     else:
@@ -143,17 +136,17 @@ def test_largest_k_and_rank_bf16(P, fmt):
         assert np.array_equal(s.view(np.uint16), np.asarray(s_ref, np.float16).view(np.uint16))
     else:
         assert np.array_equal(s, s_ref)
-    assert rel_l2(la.float().cpu().numpy(), la_o) <= LORA_TOL
+    assert_close(la.float().cpu().numpy(), la_o, LORA_TOL)
     if fmt == "nvfp4_g16":
-        Y = P.svdq_gemm_nvfp4(codes, scales, _dbf(la_o), dev(p["w_codes"]), dev(p["w_scales"]), _dbf(lu), _dbf(b),
+        Y = P.svdq_gemm_nvfp4(codes, scales, dev(la_o), dev(p["w_codes"]), dev(p["w_scales"]), _dbf(lu), _dbf(b),
                               float(np.float32(ga) * np.float32(p["w_gscale"])), "none")
         kw = dict(act_gscale=ga, w_gscale=p["w_gscale"])
     else:
-        Y = P.svdq_gemm_w4a4(codes, scales, _dbf(la_o), dev(p["w_codes"]), dev(p["w_scales"]), _dbf(lu), _dbf(b),
+        Y = P.svdq_gemm_w4a4(codes, scales, dev(la_o), dev(p["w_codes"]), dev(p["w_scales"]), _dbf(lu), _dbf(b),
                              fmt, "none")
         kw = {}
     assert Y.dtype == torch.bfloat16
     y = Y.float().cpu().numpy()
     wu = oracle.unpack_nibbles(p["w_codes"], signed=(fmt == "int4_g64"))
     y_ref = oracle.gemm_ref(cu, s_ref, la_o, wu, p["w_scales"], lu, b, fmt, "none", **kw)
-    assert rel_l2(y, oracle.bf16_round(y_ref.astype(np.float32))) <= Y_TOL
+    assert_close(y, oracle.bf16_round(y_ref.astype(np.float32)))

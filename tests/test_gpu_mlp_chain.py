@@ -3,12 +3,16 @@
 
 Two bars. (1) It equals the unfused path on the GPU (svdq_gemm_w4a4 with
 GELU, then svdq_quantize_act on its output): codes and scales bit for bit,
-lora_act2 within relative L2 1e-3 (a different fp32 summation order). (2) The
-whole MLP against the oracle chain (oracle.mlp_chain_ref, then the
-down-projection's gemm_ref): relative L2 2e-3 on the down-projection's
-output. The oracle's own U differs from the GPU's in last bits, so the
-4-bit codes of the two may differ where a value sits at a rounding edge; the
-down-projection's output is where that difference has to stay inside the bar.
+lora_act2 within the lora_act bar (a different fp32 summation order).
+(2) Against the oracle chain (oracle.mlp_chain_ref), on every row at a small
+size and on one row from every band of 64 at the DiT MLP size: U is a float
+result and the oracle's differs from the GPU's in the last bit now and then,
+so the 4-bit codes may differ where a value sits at a rounding edge. Fewer
+than 1 in 1000 code bytes and scales may differ, a differing scale is one
+fp16 ulp from the oracle's, every code dequantizes to within half a step
+(plus that one-ulp slack) of the oracle's smoothed U, and lora_act2 meets the
+lora_act bar. The down-projection then runs on the oracle chain's codes and
+meets the layer bar against the oracle's.
 """
 import numpy as np
 import pytest
@@ -16,11 +20,10 @@ import torch
 
 import oracle
 import synth
+from tests.parity import LORA_TOL, Y_TOL, assert_close, band_rows, rel_l2  # noqa: F401
 
 pytestmark = pytest.mark.gpu
 
-Y_TOL = 2e-3
-LORA_TOL = 1e-3
 DEV = torch.device("cuda:0")
 
 
@@ -40,12 +43,6 @@ def dev(a, dtype=None):
 def host(t):
     torch.cuda.synchronize()
     return t.float().cpu().numpy() if t.dtype == torch.bfloat16 else t.cpu().numpy()
-
-
-def rel_l2(a, b):
-    a = np.asarray(a, np.float64)
-    b = np.asarray(b, np.float64)
-    return np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300)
 
 
 def chain_inputs(M, K, N, r, r2, seed=0):
@@ -89,8 +86,8 @@ def test_chain_equals_unfused(P, M, K, N, r, r2, h):
     assert np.array_equal(host(c2), host(c1))
     assert np.array_equal(host(s2).view(np.uint16), host(s1).view(np.uint16))
     if r2:
-        assert l2.dtype == h
-        assert rel_l2(host(l2), host(l1)) <= LORA_TOL
+        assert l2.dtype == torch.float32
+        assert_close(host(l2), host(l1), LORA_TOL)
     else:
         assert l2 is None
 
@@ -105,29 +102,70 @@ def test_chain_is_deterministic(P):
         assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
 
 
+def _check_chain_codes(cg, sg, c2p_ref, s2_ref, U16, si2):
+    """The chain's codes and scales against the oracle's: U is a float result,
+    so where the GPU's U and the oracle's differ in the last bit a group's scale
+    or a code may differ. Fewer than 1 in 1000 code bytes and scales may, a
+    differing scale is one fp16 ulp from the oracle's, and every GPU code
+    dequantizes to within half a step (plus the one-ulp slack of U) of the
+    oracle's smoothed value."""
+    code_diff = np.mean(cg != c2p_ref)
+    sc_diff = np.mean(sg.view(np.uint16) != s2_ref.view(np.uint16))
+    print(f"chain codes differing from the oracle's: bytes {code_diff:.2e}, scales {sc_diff:.2e}")
+    assert code_diff < 1e-3 and sc_diff < 1e-3
+    ulp_gap = np.abs(sg.view(np.uint16).astype(np.int32) - s2_ref.view(np.uint16).astype(np.int32))
+    assert ulp_gap.max() <= 1
+    qg = oracle.unpack_nibbles(cg, signed=True).astype(np.float64)
+    sgx = np.repeat(sg.astype(np.float64), 64, axis=1)
+    xhat = oracle.smooth_act(U16, si2).astype(np.float64)
+    err = np.abs(qg * sgx - xhat)
+    assert (err <= 0.5 * sgx + 2.0 ** -8 * sgx + 2.0 ** -9 * np.abs(xhat) + 1e-30).all()
+
+
 def test_mlp_against_oracle_chain(P):
+    """The whole MLP at a small size: the chain's outputs against the oracle
+    chain, then the GPU down-projection on the oracle chain's codes against the
+    oracle's down-projection (values flow from the oracle to the GPU only)."""
     M, K, N, N2, r, r2 = 200, 512, 1024, 384, 16, 16
     up, si2, ld2 = chain_inputs(M, K, N, r, r2, seed=3)
     cfg2 = synth.LayerConfig("chain_down", 72, M, N, N2, r2, "int4_g64", "none", "gelu_normal", 0.005, 30.0)
     down = synth.random_quantized_layer(cfg2, seed=3)
     # the oracle: quantize X, the up-projection with GELU, the chain's quantizer, the down-projection
     cu, packed, scales = oracle.quantize_act_ref(up["X"], up["smooth_inv"], "int4_g64")
-    la = oracle.lora_act_ref(up["X"], up["lora_down"][:r]).astype(np.float16)
+    la = oracle.lora_act_ref(up["X"], up["lora_down"][:r]).astype(np.float32)
     wu = oracle.unpack_nibbles(up["w_codes"], signed=True)
     U16, c2u, c2p, s2, la2 = oracle.mlp_chain_ref(cu, scales, la, wu, up["w_scales"], up["lora_up"][:, :r],
                                                  up["bias"], "int4_g64", si2, ld2)
     w2u = oracle.unpack_nibbles(down["w_codes"], signed=True)
-    y_ref = oracle.gemm_ref(c2u, s2, la2.astype(np.float16), w2u, down["w_scales"], down["lora_up"][:, :r2],
-                            down["bias"], "int4_g64")
-    # the GPU: the same quantized X (bit-exact, checked), the fused chain, the down-projection
+    la2_32 = la2.astype(np.float32)
+    y_ref = oracle.gemm_ref(c2u, s2, la2_32, w2u, down["w_scales"], down["lora_up"][:, :r2], down["bias"],
+                            "int4_g64")
+    # the GPU: the same quantized X (bit-exact, checked), then the fused chain
     codes, sc, la_g = P.svdq_quantize_act(dev(up["X"]), dev(up["smooth_inv"]), dev(up["lora_down"][:r]), "int4_g64")
     assert np.array_equal(host(codes), packed)
     c2, sc2, l2 = P.svdq_gemm_w4a4_mlp(codes, sc, dev(la), dev(up["w_codes"]), dev(up["w_scales"]),
                                        dev(up["lora_up"][:, :r]), dev(up["bias"]), dev(si2), dev(ld2))
-    assert rel_l2(host(l2), la2) <= LORA_TOL
-    mismatch = np.mean(host(c2) != c2p)
-    print(f"chain codes differing from the oracle's (last-bit differences of U): {mismatch:.2e}")
-    assert mismatch < 0.01
-    y = P.svdq_gemm_w4a4(c2, sc2, l2, dev(down["w_codes"]), dev(down["w_scales"]), dev(down["lora_up"][:, :r2]),
-                         dev(down["bias"]), "int4_g64")
-    assert rel_l2(host(y), y_ref) <= Y_TOL
+    assert_close(host(l2), la2, LORA_TOL, what="lora_act2")
+    _check_chain_codes(host(c2), host(sc2), c2p, s2, U16, si2)
+    y = P.svdq_gemm_w4a4(dev(c2p), dev(s2), dev(la2_32), dev(down["w_codes"]), dev(down["w_scales"]),
+                         dev(down["lora_up"][:, :r2]), dev(down["bias"]), "int4_g64")
+    assert_close(host(y), y_ref, what="down-projection")
+
+
+def test_chain_full_size_against_oracle(P):
+    """The DiT MLP up-projection (M 4096, K 3072, N 12288, rank 32) through the
+    fused chain, against the oracle chain on one row from every band of 64 (all
+    12288 columns): codes and scales as _check_chain_codes states, lora_act2
+    against the oracle's."""
+    M, K, N, r, r2 = 4096, 3072, 12288, 32, 32
+    up, si2, ld2 = chain_inputs(M, K, N, r, r2, seed=5)
+    cu, packed, scales = oracle.quantize_act_ref(up["X"], up["smooth_inv"], "int4_g64")
+    la = oracle.lora_act_ref(up["X"], up["lora_down"][:r]).astype(np.float32)
+    c2, s2, l2 = P.svdq_gemm_w4a4_mlp(dev(packed), dev(scales), dev(la), dev(up["w_codes"]), dev(up["w_scales"]),
+                                      dev(up["lora_up"][:, :r]), dev(up["bias"]), dev(si2), dev(ld2))
+    rows = band_rows(M, seed=14)
+    wu = oracle.unpack_nibbles(up["w_codes"], signed=True)
+    U16, c2u_ref, c2p_ref, s2_ref, la2_ref = oracle.mlp_chain_ref(
+        cu, scales, la, wu, up["w_scales"], up["lora_up"][:, :r], up["bias"], "int4_g64", si2, ld2, rows=rows)
+    _check_chain_codes(host(c2)[rows], host(s2)[rows], c2p_ref, s2_ref, U16, si2)
+    assert_close(host(l2)[rows], la2_ref, LORA_TOL, what="lora_act2")

@@ -33,11 +33,11 @@ from bit_diffusion_transformer_act_amd.modules import (AWQLinear, SVDQLinear, SV
                                                        fuse_qkv_norm_rope, quantize_model)
 from oracle.block import linear as oracle_linear
 from tests.dit_support import dense_params, quant_config, quantized_params, to_torch
+from tests.parity import Y_TOL, assert_close, rel_l2
 
 pytestmark = pytest.mark.gpu
 
 DEV = torch.device("cuda:0")
-Y_TOL = 2e-3
 GLUE_TOL = 1e-3
 H16 = {"float16": torch.float16, "bfloat16": torch.bfloat16}
 
@@ -47,12 +47,6 @@ def gpu():
     assert torch.cuda.is_available(), "GPU tests need a HIP device"
     import bit_diffusion_transformer_act_amd as pkg
     assert pkg.svdq_device_check(0) == 0, "cuda:0 is not gfx950"
-
-
-def rel_l2(a, b):
-    a = np.asarray(a, np.float64)
-    b = np.asarray(b, np.float64)
-    return np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300)
 
 
 def host(t):
@@ -73,7 +67,7 @@ def test_svdq_linear_module(fmt, epi):
     y = m(torch.from_numpy(X.reshape(3, 50, cfg.K)).to(DEV))
     assert tuple(y.shape) == (3, 50, cfg.N) and y.dtype == torch.float16
     ref = oracle_linear(X, {"kind": "svdq", "layer": layer, "b": d["bias"], "epilogue": epi})
-    assert rel_l2(host(y).reshape(150, cfg.N), ref) <= Y_TOL
+    assert_close(host(y).reshape(150, cfg.N), ref)
 
 
 @pytest.mark.parametrize("M", [1, 11])
@@ -87,7 +81,7 @@ def test_awq_linear_module(M):
     m.load_state_dict(to_torch({"w_codes": a["codes"], "scales": a["scales"], "zeros": a["zeros"], "bias": b}, DEV))
     y = m(torch.from_numpy(x).to(DEV))
     ref = oracle.gemv_ref(x, a["codes"], a["scales"], a["zeros"], bias=b)
-    assert rel_l2(host(y), ref) <= Y_TOL
+    assert_close(host(y), ref)
 
 
 def _block(fmt, fuse, D=1024, C=768, B=2, T=200, rank=32, dtype="float16"):
@@ -160,9 +154,8 @@ def test_dit_block_end_to_end(fmt, fuse, dtype, monkeypatch):
         with torch.no_grad():
             y = mod(xin, torch.from_numpy(inp["rope"]).to(DEV)) if name.endswith("to_qkv") else mod(xin)
         y = torch.cat(y, -1) if isinstance(y, tuple) else y
-        err = rel_l2(host(y.float()), cap[name][1])
+        err = assert_close(host(y.float()), cap[name][1], Y_TOL, kind=dt, what=name)
         print(f"{fmt} {name}: rows {xin.shape[0]} rel_l2 {err:.2e}")
-        assert err <= Y_TOL, name
 
     # the composition: the GPU block with every layer output replaced by the
     # oracle's; the inputs it then feeds the layers, and its output, against the oracle's

@@ -9,11 +9,10 @@ import torch
 
 import oracle
 import synth
+from tests.parity import LORA_TOL, Y_TOL, assert_close, band_rows, rel_l2  # noqa: F401
 
 pytestmark = pytest.mark.gpu
 
-Y_TOL = 2e-3
-LORA_TOL = 1e-3
 DEV = torch.device("cuda:0")
 
 
@@ -32,12 +31,6 @@ def dev(a):
 def host(t):
     torch.cuda.synchronize()
     return t.cpu().numpy()
-
-
-def rel_l2(a, b):
-    a = np.asarray(a, np.float64)
-    b = np.asarray(b, np.float64)
-    return np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300)
 
 
 _cache = {}
@@ -68,7 +61,7 @@ def test_quantize_act_nvfp4(P, M, K, r):
     assert np.array_equal(host(scales), scales_ref)
     if r:
         la_ref = oracle.lora_act_ref(X, layer["lora_down"])
-        assert rel_l2(host(la), la_ref) <= LORA_TOL
+        assert_close(host(la), la_ref, LORA_TOL)
     else:
         assert la is None
 
@@ -121,7 +114,7 @@ def test_quantize_act_nvfp4_ties(P):
 def _gemm_case(P, M, K, N, r, epi, seed=1):
     d, si, ga, layer = nv_layer(M, K, N, r, seed)
     codes_u, packed, scales = oracle.quantize_act_ref(d["X"], si, "nvfp4_g16", ga)
-    la16 = oracle.lora_act_ref(d["X"], layer["lora_down"]).astype(np.float16)
+    la16 = oracle.lora_act_ref(d["X"], layer["lora_down"]).astype(np.float32)
     y_ref = oracle.gemm_ref(codes_u, scales, la16, layer["w_codes_unpacked"], layer["w_scales"],
                             layer["lora_up"], d["bias"], "nvfp4_g16", epi,
                             act_gscale=ga, w_gscale=layer["w_gscale"])
@@ -140,7 +133,7 @@ def _gemm_case(P, M, K, N, r, epi, seed=1):
 def test_gemm_nvfp4(P, M, K, N, r, epi):
     y, y_ref = _gemm_case(P, M, K, N, r, epi)
     assert np.isfinite(y).all()
-    assert rel_l2(y, y_ref) <= Y_TOL
+    assert_close(y, y_ref)
 
 
 def test_gemm_nvfp4_full_size_sampled(P):
@@ -153,8 +146,8 @@ def test_gemm_nvfp4_full_size_sampled(P):
     codes, scales, la = P.svdq_quantize_act_nvfp4(dev(p["X"]), dev(p["smooth_inv"]), dev(p["lora_down"]),
                                                   float(ga))
     # the GEMM takes the oracle's low-rank activations (all rows), the GPU's checked against them
-    la_o = oracle.lora_act_ref(p["X"], p["lora_down"]).astype(np.float16)
-    assert rel_l2(host(la), la_o) <= LORA_TOL
+    la_o = oracle.lora_act_ref(p["X"], p["lora_down"]).astype(np.float32)
+    assert_close(host(la), la_o, LORA_TOL)
     y = P.svdq_gemm_nvfp4(codes, scales, dev(la_o), dev(p["w_codes"]), dev(p["w_scales"]), dev(p["lora_up"]),
                           dev(p["bias"]), float(np.float32(ga) * np.float32(gw)), "gelu_tanh")
     rng = np.random.default_rng(3)
@@ -168,7 +161,7 @@ def test_gemm_nvfp4_full_size_sampled(P):
                             p["bias"][cols], "nvfp4_g16", "gelu_tanh", act_gscale=ga, w_gscale=gw)
     yh = host(y)
     assert np.isfinite(yh).all()
-    assert rel_l2(yh[np.ix_(rows, cols)], y_ref) <= Y_TOL
+    assert_close(yh[np.ix_(rows, cols)], y_ref)
 
 
 def test_gemm_nvfp4_wide_tiles_ragged_sampled(P):
@@ -180,8 +173,8 @@ def test_gemm_nvfp4_wide_tiles_ragged_sampled(P):
     ga, gw = p["act_gscale"], p["w_gscale"]
     codes, scales, la = P.svdq_quantize_act_nvfp4(dev(p["X"]), dev(p["smooth_inv"]), dev(p["lora_down"]),
                                                   float(ga))
-    la_o = oracle.lora_act_ref(p["X"], p["lora_down"]).astype(np.float16)
-    assert rel_l2(host(la), la_o) <= LORA_TOL
+    la_o = oracle.lora_act_ref(p["X"], p["lora_down"]).astype(np.float32)
+    assert_close(host(la), la_o, LORA_TOL)
     y = P.svdq_gemm_nvfp4(codes, scales, dev(la_o), dev(p["w_codes"]), dev(p["w_scales"]), dev(p["lora_up"]),
                           dev(p["bias"]), float(np.float32(ga) * np.float32(gw)), "gelu_tanh")
     rng = np.random.default_rng(5)
@@ -194,7 +187,7 @@ def test_gemm_nvfp4_wide_tiles_ragged_sampled(P):
                             p["bias"][cols], "nvfp4_g16", "gelu_tanh", act_gscale=ga, w_gscale=gw)
     yh = host(y)
     assert np.isfinite(yh).all()
-    assert rel_l2(yh[np.ix_(rows, cols)], y_ref) <= Y_TOL
+    assert_close(yh[np.ix_(rows, cols)], y_ref)
 
 
 def test_nvfp4_layer_module(P):
@@ -209,7 +202,7 @@ def test_nvfp4_layer_module(P):
     y = m(dev(d["X"]))
     codes_u, _, scales = oracle.quantize_act_ref(d["X"], si, "nvfp4_g16", ga)
     y_ref = oracle.forward_ref(d["X"], layer, codes_u, scales, d["bias"], "gelu_tanh")
-    assert rel_l2(host(y), y_ref) <= Y_TOL
+    assert_close(host(y), y_ref)
     # the method's point, on this calibrated layer: close to the dense layer
     dense = oracle.dense_ref(d["X"], d["W"], d["bias"], "gelu_tanh")
     assert rel_l2(host(y), dense) < 0.1

@@ -10,11 +10,10 @@ import torch
 
 import oracle
 import synth
+from tests.parity import LORA_TOL, Y_TOL, assert_close, band_rows, rel_l2  # noqa: F401
 
 pytestmark = pytest.mark.gpu
 
-Y_TOL = 2e-3
-LORA_TOL = 1e-3
 DEV = torch.device("cuda:0")
 
 
@@ -35,17 +34,11 @@ def host(t):
     return t.cpu().numpy()
 
 
-def rel_l2(a, b):
-    a = np.asarray(a, np.float64)
-    b = np.asarray(b, np.float64)
-    return np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300)
-
-
 def _case(fmt, M, K, N, r, epi, seed):
     cfg = synth.LayerConfig(f"opt_{fmt}_{M}_{N}_{r}", 90, M, K, N, r, fmt, epi, "normal", 0.005, 30.0)
     p = synth.random_quantized_layer(cfg, seed=seed)
     cu, packed, scales = oracle.quantize_act_ref(p["X"], p["smooth_inv"], fmt, p.get("act_gscale"))
-    la = oracle.lora_act_ref(p["X"], p["lora_down"]).astype(np.float16)
+    la = oracle.lora_act_ref(p["X"], p["lora_down"]).astype(np.float32)
     return p, cu, packed, scales, la
 
 
@@ -84,7 +77,7 @@ def test_gemm_without_optional_operands(P, fmt, M, K, N, r, use_bias):
     assert y.dtype == np.float16 and np.isfinite(y).all()
     rng = np.random.default_rng(7)
     rows = np.unique(np.concatenate([rng.choice(M, min(M, 48), replace=False), [0, M - 1]]))
-    assert rel_l2(y[rows], _ref(p, cu, scales, la, fmt, epi, r, use_bias, rows=rows)) <= Y_TOL
+    assert_close(y[rows], _ref(p, cu, scales, la, fmt, epi, r, use_bias, rows=rows))
 
 
 @pytest.mark.parametrize("r,use_bias", [(0, False), (16, False), (0, True)])
@@ -103,7 +96,7 @@ def test_qkv_epilogue_without_optional_operands(P, r, use_bias):
     assert np.isfinite(y).all()
     for third in range(3):
         sl = slice(third * N // 3, (third + 1) * N // 3)
-        assert rel_l2(y[:, sl], y_ref[:, sl]) <= Y_TOL, third
+        assert_close(y[:, sl], y_ref[:, sl], what=third)
 
 
 @pytest.mark.parametrize("r,r2", [(0, 16), (16, 0), (0, 0)])
@@ -123,8 +116,8 @@ def test_chain_without_bias(P, r, r2):
     assert np.array_equal(host(c2), host(c1))
     assert np.array_equal(host(s2).view(np.uint16), host(s1).view(np.uint16))
     if r2:
-        assert rel_l2(host(l2), host(l1)) <= LORA_TOL
+        assert_close(host(l2), host(l1), LORA_TOL)
     else:
         assert l2 is None
     # and the up-projection it quantized is the oracle's
-    assert rel_l2(host(y), _ref(p, cu, scales, la, "int4_g64", "gelu_tanh", r, False)) <= Y_TOL
+    assert_close(host(y), _ref(p, cu, scales, la, "int4_g64", "gelu_tanh", r, False))

@@ -12,11 +12,9 @@ import torch
 
 import oracle
 import synth
+from tests.parity import LORA_TOL, Y_TOL, assert_close, band_rows, rel_l2  # noqa: F401
 
 pytestmark = pytest.mark.gpu
-
-Y_TOL = 2e-3
-LORA_TOL = 1e-3
 
 
 @pytest.fixture(scope="module")
@@ -37,12 +35,6 @@ def dev(a):
 def host(t):
     torch.cuda.synchronize()
     return t.cpu().numpy()
-
-
-def rel_l2(a, b):
-    a = np.asarray(a, np.float64)
-    b = np.asarray(b, np.float64)
-    return np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300)
 
 
 def scales_equal(gpu, ref, fmt):
@@ -77,7 +69,7 @@ def test_quantize_act_tiny(P, fmt, M):
     assert np.array_equal(host(codes), packed_ref)
     assert scales_equal(host(scales), scales_ref, fmt)
     la_ref = oracle.lora_act_ref(X, layer["lora_down"])
-    assert rel_l2(host(la), la_ref) <= LORA_TOL
+    assert_close(host(la), la_ref, LORA_TOL)
 
 
 @pytest.mark.parametrize("name,fmt", [("qkv", "int4_g64"), ("mlp_up", "fp4_b32"),
@@ -91,7 +83,7 @@ def test_quantize_act_full_size(P, name, fmt):
     mism = int((c != packed_ref).sum())
     assert mism == 0, f"{mism} code bytes differ"
     assert scales_equal(host(scales), scales_ref, fmt)
-    assert rel_l2(host(la), oracle.lora_act_ref(p["X"], p["lora_down"])) <= LORA_TOL
+    assert_close(host(la), oracle.lora_act_ref(p["X"], p["lora_down"]), LORA_TOL)
 
 
 @pytest.mark.parametrize("fmt", ["int4_g64", "fp4_b32"])
@@ -110,7 +102,7 @@ def test_quantize_act_shapes(P, fmt, M, K, r):
     codes, scales, la = P.svdq_quantize_act(dev(X), dev(si), dev(ld), fmt)
     assert np.array_equal(host(codes), packed_ref)
     assert scales_equal(host(scales), scales_ref, fmt)
-    assert rel_l2(host(la), oracle.lora_act_ref(X, ld)) <= LORA_TOL
+    assert_close(host(la), oracle.lora_act_ref(X, ld), LORA_TOL)
 
 
 def _adversarial_x(fmt, K=512, M=64, seed=3):
@@ -176,14 +168,14 @@ def test_gemm_tiny(P, fmt, M, rank, use_bias, epi):
     cfg, d, si, layer = tiny_layer(fmt, rank)
     X = d["X"][:M]
     codes_u, packed, scales = oracle.quantize_act_ref(X, si, fmt)
-    la = oracle.lora_act_ref(X, layer["lora_down"]).astype(np.float16)
+    la = oracle.lora_act_ref(X, layer["lora_down"]).astype(np.float32)
     bias = d["bias"] if use_bias else None
     wu = layer["w_codes_unpacked"]
     y_ref = oracle.gemm_ref(codes_u, scales, la, wu, layer["w_scales"], layer["lora_up"], bias, fmt, epi)
     Y = P.svdq_gemm_w4a4(dev(packed), dev(scales), dev(la) if rank else None, dev(layer["w_codes"]),
                          dev(layer["w_scales"]), dev(layer["lora_up"]) if rank else None,
                          None if bias is None else dev(bias), fmt, epi)
-    assert rel_l2(host(Y), y_ref) <= Y_TOL
+    assert_close(host(Y), y_ref)
 
 
 @pytest.mark.parametrize("fmt", ["int4_g64", "fp4_b32"])
@@ -196,30 +188,33 @@ def test_layer_end_to_end_tiny(P, fmt):
          "w_codes": dev(layer["w_codes"]), "w_scales": dev(layer["w_scales"]),
          "lora_up": dev(layer["lora_up"])}
     Y = P.svdq_linear(dev(d["X"]), L, dev(d["bias"]))
-    assert rel_l2(host(Y), y_ref) <= Y_TOL
+    assert_close(host(Y), y_ref)
     # and the method's accuracy claim holds on the GPU output as well
     y_dense = oracle.dense_ref(d["X"], d["W"], d["bias"])
     print(f"{fmt}: GPU layer vs dense fp64 rel err {rel_l2(host(Y), y_dense):.3e}")
 
 
-@pytest.mark.parametrize("name", ["qkv", "mlp_up", "mlp_down", "mlp_down_m1024", "attn_out"])
+@pytest.mark.parametrize("name", ["qkv", "mlp_up", "mlp_down", "mlp_down_m1024", "attn_out", "mlp_up_int4"])
 def test_gemm_full_size_sampled(P, name):
     """Full DiT shapes in the benchmark's launch configuration; outputs
-    checked on sampled rows (all columns) against the oracle."""
+    checked against the oracle on one row from every band of 64 (every M-tile
+    of the remapped grid) plus the first and last rows, all columns. INT4
+    weight codes span -8..7."""
     cfg = synth.CONFIGS[name]
     fmt = cfg.fmt
     p = synth.random_quantized_layer(cfg, seed=2)
     codes_u, packed, scales = oracle.quantize_act_ref(p["X"], p["smooth_inv"], fmt)
-    la = oracle.lora_act_ref(p["X"], p["lora_down"]).astype(np.float16)
+    la = oracle.lora_act_ref(p["X"], p["lora_down"]).astype(np.float32)
     Y = P.svdq_gemm_w4a4(dev(packed), dev(scales), dev(la), dev(p["w_codes"]), dev(p["w_scales"]),
                          dev(p["lora_up"]), dev(p["bias"]), fmt, cfg.epilogue)
     y = host(Y)
-    rng = np.random.default_rng(11)
-    rows = np.unique(np.concatenate([rng.choice(cfg.M, 40, replace=False), [0, cfg.M - 1]]))
+    rows = band_rows(cfg.M, seed=11)
     wu = oracle.unpack_nibbles(p["w_codes"], signed=(fmt == "int4_g64"))
+    if fmt == "int4_g64":
+        assert wu.min() == -8
     y_ref = oracle.gemm_ref(codes_u, scales, la, wu, p["w_scales"], p["lora_up"], p["bias"], fmt,
                             cfg.epilogue, rows=rows)
-    assert rel_l2(y[rows], y_ref) <= Y_TOL
+    assert_close(y[rows], y_ref, what=name)
     assert np.isfinite(y).all()
 
 
@@ -235,17 +230,74 @@ def test_gemm_tile_bands(P, fmt, M, N, epi):
     cfg = synth.LayerConfig(f"band_{M}_{N}", 52, M, 512, N, 32, fmt, epi, "normal", 0.005, 30.0)
     p = synth.random_quantized_layer(cfg, seed=3)
     codes_u, packed, scales = oracle.quantize_act_ref(p["X"], p["smooth_inv"], fmt)
-    la = oracle.lora_act_ref(p["X"], p["lora_down"]).astype(np.float16)
+    la = oracle.lora_act_ref(p["X"], p["lora_down"]).astype(np.float32)
     Y = P.svdq_gemm_w4a4(dev(packed), dev(scales), dev(la), dev(p["w_codes"]), dev(p["w_scales"]),
                          dev(p["lora_up"]), dev(p["bias"]), fmt, epi)
     y = host(Y)
-    rng = np.random.default_rng(12)
-    rows = np.unique(np.concatenate([rng.choice(M, 48, replace=False), [0, 63, 64, 127, 128, M - 1]]))
+    rows = band_rows(M, seed=12, extra=(63, 64, 127, 128))
     wu = oracle.unpack_nibbles(p["w_codes"], signed=(fmt == "int4_g64"))
     y_ref = oracle.gemm_ref(codes_u, scales, la, wu, p["w_scales"], p["lora_up"], p["bias"], fmt, epi,
                             rows=rows)
-    assert rel_l2(y[rows], y_ref) <= Y_TOL
+    assert_close(y[rows], y_ref)
     assert np.isfinite(y).all()
+
+
+@pytest.mark.parametrize("fmt", ["int4_g64", "fp4_b32"])
+@pytest.mark.parametrize("M,K,N", [(200, 384, 512), (200, 640, 512), (4096, 384, 4096)])
+def test_gemm_odd_k_steps(P, fmt, M, K, N):
+    """K / 128 odd (3 and 5 steps of 128): the last two-step scale group holds
+    one step, and the pipelines' wait schedule ends on an odd step. Small M puts
+    INT4 on its 64 x 64 tiles and FP4 on the 4-stage 128 x 128 path; M 4096 N 4096
+    puts INT4 on its 3-stage 128 x 128 tiles."""
+    cfg = synth.LayerConfig(f"oddk_{M}_{K}_{N}", 53, M, K, N, 16, fmt, "none", "normal", 0.005, 30.0)
+    p = synth.random_quantized_layer(cfg, seed=4)
+    codes_u, packed, scales = oracle.quantize_act_ref(p["X"], p["smooth_inv"], fmt)
+    codes, sc, la = P.svdq_quantize_act(dev(p["X"]), dev(p["smooth_inv"]), dev(p["lora_down"]), fmt)
+    assert np.array_equal(host(codes), packed)
+    assert scales_equal(host(sc), scales, fmt)
+    la_o = oracle.lora_act_ref(p["X"], p["lora_down"]).astype(np.float32)
+    Y = P.svdq_gemm_w4a4(codes, sc, dev(la_o), dev(p["w_codes"]), dev(p["w_scales"]), dev(p["lora_up"]),
+                         dev(p["bias"]), fmt, "none")
+    y = host(Y)
+    rows = np.arange(M) if M <= 256 else band_rows(M, seed=13)
+    wu = oracle.unpack_nibbles(p["w_codes"], signed=(fmt == "int4_g64"))
+    y_ref = oracle.gemm_ref(codes_u, scales, la_o, wu, p["w_scales"], p["lora_up"], p["bias"], fmt, "none",
+                            rows=rows)
+    assert_close(y[rows], y_ref, what=f"{fmt} K{K}")
+
+
+def test_gemm_int4_extreme_codes(P):
+    """INT4 code -8 on both operands: groups of all -8 against all -8 (the
+    largest group product, 64 * 64, i.e. 2^20 in the kernel's 256 P accumulation),
+    all -8 against all 7, alternating -8 / 7, and random codes, with random fp16
+    scales; no low-rank branch, with and without bias."""
+    M, K, N = 192, 512, 256
+    rng = np.random.default_rng(21)
+    G = K // 64
+    a = rng.integers(-8, 8, (M, K))
+    w = rng.integers(-8, 8, (N, K))
+    for g in range(G):
+        sl = slice(64 * g, 64 * g + 64)
+        kind = g % 4
+        if kind == 0:
+            a[: M // 2, sl] = -8
+            w[: N // 2, sl] = -8
+        elif kind == 1:
+            a[:, sl] = -8
+            w[:, sl] = 7
+        elif kind == 2:
+            a[:, sl] = np.where(np.arange(64) % 2 == 0, -8, 7)
+            w[:, sl] = np.where(np.arange(64) % 3 == 0, 7, -8)
+    sa = rng.uniform(0.01, 0.1, (M, G)).astype(np.float16)
+    sw = rng.uniform(0.001, 0.01, (N, G)).astype(np.float16)
+    bias = (rng.standard_normal(N) * 0.1).astype(np.float16)
+    ap, wp = oracle.pack_nibbles(a), oracle.pack_nibbles(w)
+    for b in (None, bias):
+        Y = P.svdq_gemm_w4a4(dev(ap), dev(sa), None, dev(wp), dev(sw), None, None if b is None else dev(b),
+                             "int4_g64", "none")
+        y_ref = oracle.gemm_ref(a.astype(np.int8), sa, np.zeros((M, 0)), w.astype(np.int8), sw, np.zeros((N, 0)),
+                                b, "int4_g64")
+        assert_close(host(Y), y_ref, what="extreme codes")
 
 
 # ------------------------------------------------ fused QKV epilogue --
@@ -254,7 +306,7 @@ def _qkv_case(P, cfg, seed, rows=None):
     p = synth.random_quantized_layer(cfg, seed=seed)
     e = synth.qkv_epilogue_inputs(cfg.M, seed=seed)
     codes_u, packed, scales = oracle.quantize_act_ref(p["X"], p["smooth_inv"], "int4_g64")
-    la = oracle.lora_act_ref(p["X"], p["lora_down"]).astype(np.float16)
+    la = oracle.lora_act_ref(p["X"], p["lora_down"]).astype(np.float32)
     args = (dev(packed), dev(scales), dev(la), dev(p["w_codes"]), dev(p["w_scales"]), dev(p["lora_up"]),
             dev(p["bias"]))
     Y = P.svdq_gemm_w4a4_qkv(*args, dev(e["qk_norm_w"]), dev(e["rope"]), e["eps"])
@@ -284,20 +336,20 @@ def test_gemm_qkv_epilogue_small(P):
     cfg = synth.LayerConfig("qkv_small", 51, 200, 512, 768, 16, "int4_g64", "none", "normal", 0.005, 30.0)
     y, y_plain, y_ref, _ = _qkv_case(P, cfg, seed=6)
     n3 = cfg.N // 3
-    assert rel_l2(y[:, :n3], y_ref[:, :n3]) <= Y_TOL
-    assert rel_l2(y[:, n3:2 * n3], y_ref[:, n3:2 * n3]) <= Y_TOL
+    assert_close(y[:, :n3], y_ref[:, :n3])
+    assert_close(y[:, n3:2 * n3], y_ref[:, n3:2 * n3])
     assert _within_one_ulp(y[:, 2 * n3:], y_plain[:, 2 * n3:])
-    assert rel_l2(y[:, 2 * n3:], y_ref[:, 2 * n3:]) <= Y_TOL
+    assert_close(y[:, 2 * n3:], y_ref[:, 2 * n3:])
 
 
 def test_gemm_qkv_epilogue_full_size_sampled(P):
     """The DiT QKV projection (24 heads of 128 per third) in the benchmark's
-    launch configuration, checked on sampled rows."""
+    launch configuration, checked on one row from every band of 64 (all
+    columns: every head of Q, K and V)."""
     cfg = synth.CONFIGS["qkv"]
-    rng = np.random.default_rng(12)
-    rows = np.unique(np.concatenate([rng.choice(cfg.M, 24, replace=False), [0, cfg.M - 1]]))
+    rows = band_rows(cfg.M, seed=12)
     y, y_plain, y_ref, sel = _qkv_case(P, cfg, seed=3, rows=rows)
-    assert rel_l2(y[sel], y_ref) <= Y_TOL
+    assert_close(y[sel], y_ref)
     n3 = cfg.N // 3
     assert _within_one_ulp(y[:, 2 * n3:], y_plain[:, 2 * n3:])
     assert np.isfinite(y).all()
@@ -327,7 +379,7 @@ def test_awq_gemv(P, M, N):
     aw = oracle.awq_prep(d["W"][:N])
     y_ref = oracle.gemv_ref(d["x"], aw["codes"], aw["scales"], aw["zeros"])
     y = P.awq_gemv_w4a16(dev(d["x"]), dev(aw["codes"]), dev(aw["scales"]), dev(aw["zeros"]))
-    assert rel_l2(host(y), y_ref) <= Y_TOL
+    assert_close(host(y), y_ref)
 
 
 @pytest.mark.parametrize("M,K,N", [(4, 4096, 512), (1, 12288, 3072), (2, 16384, 300),
@@ -339,7 +391,7 @@ def test_awq_gemv_random_params_other_k(P, M, K, N):
     p = synth.random_awq_layer(g, seed=5, M=M)
     y_ref = oracle.gemv_ref(p["x"], p["codes"], p["scales"], p["zeros"])
     y = P.awq_gemv_w4a16(dev(p["x"]), dev(p["codes"]), dev(p["scales"]), dev(p["zeros"]))
-    assert rel_l2(host(y), y_ref) <= Y_TOL
+    assert_close(host(y), y_ref)
 
 
 @pytest.mark.parametrize("M", [1, 8])
@@ -349,7 +401,7 @@ def test_awq_gemv_fractional_zeros(P, M):
     z = (p["zeros"].astype(np.float32) + np.random.default_rng(1).uniform(-0.5, 0.5, p["zeros"].shape)).astype(np.float16)
     y_ref = oracle.gemv_ref(p["x"], p["codes"], p["scales"], z)
     y = P.awq_gemv_w4a16(dev(p["x"]), dev(p["codes"]), dev(p["scales"]), dev(z))
-    assert rel_l2(host(y), y_ref) <= Y_TOL
+    assert_close(host(y), y_ref)
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 3072, 18432), (5, 2048, 333)])
@@ -360,7 +412,7 @@ def test_awq_gemv_bias(P, M, K, N):
     b = np.random.default_rng(2).normal(0, 2.0, N).astype(np.float16)
     y_ref = oracle.gemv_ref(p["x"], p["codes"], p["scales"], p["zeros"], bias=b)
     y = P.awq_gemv_w4a16(dev(p["x"]), dev(p["codes"]), dev(p["scales"]), dev(p["zeros"]), bias=dev(b))
-    assert rel_l2(host(y), y_ref) <= Y_TOL
+    assert_close(host(y), y_ref)
 
 
 # ------------------------------------------------------------ semantics --

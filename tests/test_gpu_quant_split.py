@@ -10,10 +10,10 @@ import pytest
 import torch
 
 import oracle
+from tests.parity import LORA_TOL, assert_close  # noqa: F401
 
 pytestmark = pytest.mark.gpu
 
-LORA_TOL = 1e-3
 DEV = torch.device("cuda:0")
 H16 = {"float16": torch.float16, "bfloat16": torch.bfloat16}
 
@@ -32,12 +32,6 @@ def to16(a, dtype):
     t = torch.from_numpy(np.asarray(a, np.float32)).to(H16[dtype])
     host = t.numpy() if dtype == "float16" else t.float().numpy()
     return host, t.to(DEV)
-
-
-def rel_l2(a, b):
-    a = np.asarray(a, np.float64)
-    b = np.asarray(b, np.float64)
-    return np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300)
 
 
 @pytest.mark.parametrize("fmt", ["int4_g64", "fp4_b32", "nvfp4_g16"])
@@ -66,8 +60,8 @@ def test_quantize_act_k_split(P, fmt, dtype, M, r):
     else:
         assert np.array_equal(s, scales_ref)
     if r:
-        la_ref, _ = to16(oracle.lora_act_ref(Xh, ld_h), dtype)
-        assert rel_l2(la.float().cpu().numpy(), la_ref) <= LORA_TOL
+        assert la.dtype == torch.float32
+        assert_close(la.cpu().numpy(), oracle.lora_act_ref(Xh, ld_h), LORA_TOL)
         # deterministic: the slices' partials are added in a fixed order
         if fmt == "nvfp4_g16":
             _, _, la2 = P.svdq_quantize_act_nvfp4(Xd, torch.from_numpy(si).to(DEV), ld_d, float(ga))

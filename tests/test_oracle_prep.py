@@ -126,3 +126,18 @@ def test_nvfp4_residual_within_half_step(tiny):
     err = np.abs(deq - R)
     assert (err <= unit + 1e-6 * np.abs(R)).all()
     assert np.linalg.norm(deq - R) / np.linalg.norm(R) < 0.15
+
+
+@pytest.mark.parametrize("alpha", ["0.5", "0.25"])
+def test_smoothing_factors_hand_worked(alpha):
+    """tests/golden/smoothing.txt: the alpha rule (alpha 0.25 tells a^alpha /
+    w^(1 - alpha) from the rule with the exponents exchanged), and lambda = 1
+    for an all-zero calibration column and for an all-zero weight column."""
+    from tests.golden_io import read_golden
+    g = read_golden("smoothing.txt")
+    X_cal = np.array([[float(v) for v in row] for row in g["xcal"]], np.float16)
+    W = np.array([[float(v) for v in row] for row in g["w"]], np.float16)
+    want = np.array([int(h, 16) for h in g[f"si_a{alpha}"][0]], np.uint32)
+    si = oracle.smoothing_factors(X_cal, W, float(alpha))
+    assert si.dtype == np.float32
+    assert np.array_equal(si.view(np.uint32), want), [hex(v) for v in si.view(np.uint32)]
