@@ -1,26 +1,33 @@
 #!/usr/bin/env python3
-"""Benchmark of the SVDQuant W4A4 + low-rank linear layer and the AWQ W4A16
+"""Benchmark of the SVDQuant W4A4 + low-rank linear layers and the AWQ W4A16
 GEMV on one MI355X.
 
-A step is one pass of the whole hot path over one batch of synthetic input:
-svdq_quantize_act (smoothing + low-rank down + 4-bit activation quantizer),
-svdq_gemm_w4a4 (4-bit GEMM + low-rank up + scales + bias [+ GELU]) on the
-DiT QKV projection (M=4096 tokens, K=3072, N=9216, rank 32, INT4 group 64),
-then awq_gemv_w4a16 on the modulation projection (M=1, K=3072, N=18432,
-group 64). Inputs are resident in HBM before the timed region; R sets of
-inputs and outputs are rotated so the working set (> 512 MB) cannot live in
-the 256 MB Infinity Cache.
+A step is one pass of the whole hot path over one batch of synthetic input.
+The default workload is one DiT block's linear stream at 4096 tokens, hidden
+3072: for each of QKV (3072 -> 9216), out-projection (3072 -> 3072), MLP-up
+(3072 -> 12288, GELU) and MLP-down (12288 -> 3072), all W4A4 INT4 group 64
+rank 32, the fused quantizer (svdq_quantize_act: smoothing + low-rank down +
+4-bit activation codes) then the fused GEMM (svdq_gemm_w4a4: 4-bit GEMM +
+low-rank up + scales + bias [+ GELU]); then the AWQ W4A16 modulation GEMV
+(M 1, K 3072, N 18432, group 64). `--workload` selects a single layer or the
+MLP pair / fused chain instead. Inputs are resident in HBM before the timed
+region; R sets of inputs and outputs rotate so the working set (> 600 MB)
+cannot live in the 256 MB Infinity Cache.
 
-Prints ONE JSON line (rank 0). `value` is the layer's effective throughput
-2*M*N*K / step time in TOPS (the GEMV's time is inside the step).
-Per-kernel durations come from HIP events recorded on the launch stream
-around every launch in the timed region.
+Prints ONE JSON line. `value` is the stream's effective throughput
+sum(2 M N K) / step time in TOPS (the quantizers' and the GEMV's time is
+inside the step). Per-launch durations come from HIP events recorded on the
+launch stream around every launch in the timed region (median, p10, p90 over
+the steps). The low-rank overhead t(rank r) / t(rank 0) - 1 is measured by a
+second timed pass with the low-rank branch off. GPU clocks are sampled with
+amdsmi on a host thread during the timed region.
 
-Options: --gpus N (only 1 is supported: one GPU), --steps K, --warmup W,
---workload {qkv,qkv_normrope,mlp_up,mlp_down,mlp_down_m1024,attn_out,mlp_up_int4,block},
---no-cpu-baseline, --warm (no buffer rotation), --prewarm-ms T (untimed steps
-for T ms before the W warm-up steps, default 150: after idle the clocks need
-tens of ms of load to settle, and a short warm-up would time the ramp).
+Options: --gpus N (only 1: one GPU), --steps K (default 100), --warmup W
+(default 20), --workload NAME, --no-cpu-baseline, --no-lowrank-overhead,
+--warm (no buffer rotation), --rank R, --prewarm-ms T (untimed steps for T ms
+before the warm-up steps, default 150: after idle the clocks need tens of ms
+of load to settle), --calib-copy-mib N (a plain fill and add of N MiB after
+the timed region: the reference kernels for scaling HBM byte counters).
 """
 from __future__ import annotations
 
@@ -29,6 +36,7 @@ import hashlib
 import json
 import os
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -41,35 +49,46 @@ METRIC = "W4A4+lowrank GEMM effective TOPS & % MFMA peak; W4A16 GEMV HBM GB/s"
 PEAK_TOPS = {"int4_g64": 5000.0, "fp4_b32": 10100.0, "nvfp4_g16": 2500.0}
 PEAK_NOTE = {"int4_g64": "INT4 runs on int8 MFMA: tera-ops against the 5.0 POP/s int8 peak",
              "fp4_b32": "FP4 against the 10.1 PFLOP/s MXFP4 peak",
-             "nvfp4_g16": "NVFP4 operands dequantized exactly to fp16 (bf16 inputs and outputs, the pages' compute dtype): against the 2.5 PFLOP/s fp16 peak"}
+             "nvfp4_g16": "NVFP4 operands dequantized exactly to fp16 (bf16 inputs and outputs, the pages' "
+                          "compute dtype): against the 2.5 PFLOP/s fp16 peak"}
+MFMA_DTYPE = {"int4_g64": "int8", "fp4_b32": "fp4", "nvfp4_g16": "f16"}
 SCALE_BYTES_PER_ROW = {"int4_g64": lambda K: (K // 64) * 2, "fp4_b32": lambda K: K // 32,
                        "nvfp4_g16": lambda K: K // 16}
 PEAK_HBM_GBS = 8000.0
 ROTATE_BYTES = 600 << 20
 
+# workloads of several layers, in stream order
+WORKLOADS = {
+    "block": ("qkv", "attn_out", "mlp_up_int4", "mlp_down"),
+    "mlp_pair": ("mlp_up_int4", "mlp_down"),
+    "mlp_chain": ("mlp_up_int4", "mlp_down"),
+}
+SINGLE = ("qkv", "qkv_normrope", "mlp_up", "mlp_up_nvfp4", "mlp_down", "mlp_down_m1024", "attn_out",
+          "mlp_up_int4")
+CHAINED = ("mlp_chain",)
 
-def parse():
+
+def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="qkv",
-                    choices=["qkv", "qkv_normrope", "mlp_up", "mlp_up_nvfp4", "mlp_down",
-                             "mlp_down_m1024", "attn_out", "mlp_up_int4", "block", "mlp_pair",
-                             "mlp_chain"])
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="block", choices=list(WORKLOADS) + list(SINGLE))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-lowrank-overhead", action="store_true")
     ap.add_argument("--warm", action="store_true", help="no buffer rotation (cache-warm)")
     ap.add_argument("--rank", type=int, default=None, help="override the low-rank width")
     ap.add_argument("--prewarm-ms", type=float, default=150.0,
                     help="untimed steps for this long before the warm-up steps: the GPU's clocks "
                          "take tens of ms of sustained load to settle after idle")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
-                    help="after the timed region, run one plain device copy of this many MiB "
-                         "(the reference kernel for scaling HBM byte counters)")
-    return ap.parse_args()
+                    help="after the timed region, run one plain device fill and add of this many MiB "
+                         "(the reference kernels for scaling HBM byte counters)")
+    return ap.parse_args(argv)
 
 
 def layer_bytes(cfg, r):
+    """Algorithmic HBM bytes of the quantizer and of the GEMM of one layer."""
     M, K, N = cfg.M, cfg.K, cfg.N
     sbytes = SCALE_BYTES_PER_ROW[cfg.fmt](K)
     q = M * K * 2 + K * 4 + r * K * 2 + M * K // 2 + M * sbytes + M * r * 4   # lora_act is fp32
@@ -87,23 +106,110 @@ def kernel_source_hash(name):
     return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
 
 
-def stored_traffic(workload):
-    """HBM bytes per launch of the GEMM from committed rocprofv3 --pmc counters,
-    only if the kernel's source file is unchanged since they were taken."""
+def stored_traffic(workload, layer=None):
+    """HBM bytes per launch of a GEMM from committed rocprofv3 --pmc counters,
+    only if the kernel's source file is unchanged since they were taken. A
+    record holds one GEMM (top-level fields) or, for a stream of layers, one
+    entry per layer under "layers"."""
     p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(p):
         return None
     try:
         d = json.load(open(p))
+        if layer is not None and "layers" in d:
+            d = d["layers"][layer]
         if d.get("source_sha") != kernel_source_hash(d["source"]):
             return None
-    except (OSError, ValueError, KeyError):
+    except (OSError, ValueError, KeyError, TypeError):
         return None
     return d.get("hbm_bytes_per_launch")
 
 
-def main():
-    args = parse()
+def gemm_name(cfg):
+    if cfg.fmt == "nvfp4_g16":
+        return "svdq_gemm_nvfp4"
+    return "svdq_gemm_w4a4_qkv" if cfg.epilogue == "qkv_norm_rope" else "svdq_gemm_w4a4"
+
+
+class ClockSampler:
+    """The GPU's graphics clock, sampled on a host thread every `period`
+    seconds between start() and stop(): amdsmi's GPU metrics (the current
+    clock of each XCD, averaged over the XCDs, and the firmware's own running
+    average), falling back to amdsmi_get_clock_info."""
+
+    def __init__(self, pci_bus=None, period=0.005):
+        self.period, self.samples, self.err, self.h, self.max_gfx = period, [], None, None, None
+        try:
+            import amdsmi
+            self.amdsmi = amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            h = handles[0]
+            if pci_bus is not None and len(handles) > 1:
+                for c in handles:
+                    if int(amdsmi.amdsmi_get_gpu_device_bdf(c).split(":")[1], 16) == pci_bus:
+                        h = c
+            self.h = h
+            self.max_gfx = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX).get("max_clk")
+        except Exception as e:  # no amdsmi, no permission: report why
+            self.err = f"{type(e).__name__}: {e}"
+        self._stop = threading.Event()
+        self._t = None
+
+    @staticmethod
+    def _num(v):
+        return float(v) if isinstance(v, (int, float)) and 0 < v < 100000 else None
+
+    def _sample(self):
+        a = self.amdsmi
+        try:
+            m = a.amdsmi_get_gpu_metrics_info(self.h)
+            xcd = [self._num(v) for v in (m.get("current_gfxclks") or [])]
+            xcd = [v for v in xcd if v is not None]
+            cur = sum(xcd) / len(xcd) if xcd else self._num(m.get("current_gfxclk"))
+            avg = self._num(m.get("average_gfxclk_frequency"))
+            if cur is not None:
+                return cur, avg
+        except Exception:
+            pass
+        return float(a.amdsmi_get_clock_info(self.h, a.AmdSmiClkType.GFX)["clk"]), None
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                self.samples.append(self._sample())
+            except Exception as e:
+                self.err = f"{type(e).__name__}: {e}"
+                return
+            time.sleep(self.period)
+
+    def start(self):
+        if self.h is not None:
+            self._t = threading.Thread(target=self._run, daemon=True)
+            self._t.start()
+
+    def stop(self):
+        if self._t is not None:
+            self._stop.set()
+            self._t.join()
+
+    def summary(self):
+        if not self.samples:
+            return {"source": "amdsmi", "error": self.err or "no samples"}
+        import numpy as np
+        g = np.array([s[0] for s in self.samples], float)
+        avg = [s[1] for s in self.samples if s[1] is not None]
+        out = {"source": f"amdsmi GPU metrics (current graphics clock, mean over the XCDs), every "
+                         f"{self.period * 1e3:.0f} ms over the timed steps",
+               "samples": len(g), "gfx_mhz_median": float(np.median(g)), "gfx_mhz_min": float(g.min()),
+               "gfx_mhz_max": float(g.max()), "gfx_mhz_limit": self.max_gfx}
+        if avg:
+            out["gfx_mhz_firmware_average"] = float(np.median(avg))
+        return out
+
+
+def main(argv=None):
+    args = parse(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the layer runs on a single MI355X; splitting the "
               "tokens across GPUs needs no exchange and is not run here. Use --gpus 1.",
@@ -123,13 +229,8 @@ def main():
         print("cuda:0 is not a gfx950 (MI355X) device", file=sys.stderr)
         sys.exit(3)
 
-    chain = args.workload == "mlp_chain"
-    if args.workload == "block":
-        names = list(synth.BLOCK_STREAM)
-    elif args.workload in ("mlp_pair", "mlp_chain"):
-        names = ["mlp_up_int4", "mlp_down"]      # the DiT MLP: INT4 up-projection + GELU, INT4 down
-    else:
-        names = [args.workload]
+    chain = args.workload in CHAINED
+    names = list(WORKLOADS.get(args.workload, (args.workload,)))
     cfgs = [synth.CONFIGS[n] for n in names]
     gcfg = synth.CONFIGS["gemv"]
 
@@ -144,11 +245,7 @@ def main():
         host_sets.append((cfg, r, p))
     gp = synth.random_awq_layer(gcfg, seed=0)
 
-    per_set = 0
-    for cfg, r, _ in host_sets:
-        qb, gb = layer_bytes(cfg, r)
-        per_set += qb + gb
-    per_set += gemv_bytes(gcfg)
+    per_set = gemv_bytes(gcfg) + sum(sum(layer_bytes(cfg, r)) for cfg, r, _ in host_sets)
     nsets = 1 if args.warm else max(2, -(-ROTATE_BYTES // per_set))
 
     sets = []
@@ -185,84 +282,98 @@ def main():
              "zeros": t(gp["zeros"]), "y": torch.empty((1, gcfg.N), dtype=torch.float16, device=dev)}
         sets.append((layers, G))
     torch.cuda.synchronize()
-
     stream = torch.cuda.current_stream(dev)
-    nk = 4 if chain else sum(2 for _ in cfgs) + 1   # timed calls per step
 
-    def step_chain(layers, G, events):
-        Lu, Ld = layers
-        ev = (lambda k: events[k].record(stream)) if events is not None else (lambda k: None)
-        ev(0)
-        P.svdq_quantize_act(Lu["X"], Lu["smooth_inv"], Lu["lora_down"], "int4_g64",
-                            Lu["codes"], Lu["scales"], Lu["lora_act"])
-        ev(1)
-        P.svdq_gemm_w4a4_mlp(Lu["codes"], Lu["scales"], Lu["lora_act"], Lu["w_codes"], Lu["w_scales"],
-                             Lu["lora_up"], Lu["bias"], Ld["smooth_inv"], Ld["lora_down"], "int4_g64",
-                             Ld["codes"], Ld["scales"], Ld["lora_act"], Lu["workspace"])
-        ev(2)
-        P.svdq_gemm_w4a4(Ld["codes"], Ld["scales"], Ld["lora_act"], Ld["w_codes"], Ld["w_scales"],
-                         Ld["lora_up"], Ld["bias"], "int4_g64", "none", out=Ld["Y"])
-        ev(3)
+    # ---- the launches of one step, in order: (label, kind, cfg, rank, fn(layers, G, lowrank))
+    def quant(L, lr):
+        cfg = L["cfg"]
+        ld, la = (L["lora_down"], L["lora_act"]) if lr else (None, None)
+        if cfg.fmt == "nvfp4_g16":
+            P.svdq_quantize_act_nvfp4(L["X"], L["smooth_inv"], ld, L["act_gscale"], L["codes"], L["scales"], la)
+        else:
+            P.svdq_quantize_act(L["X"], L["smooth_inv"], ld, cfg.fmt, L["codes"], L["scales"], la)
+
+    def gemm(L, lr):
+        cfg = L["cfg"]
+        la, lu = (L["lora_act"], L["lora_up"]) if lr else (None, None)
+        h = IO_DTYPE[cfg.fmt]
+        if cfg.fmt == "nvfp4_g16":
+            P.svdq_gemm_nvfp4(L["codes"], L["scales"], la, L["w_codes"], L["w_scales"], lu, L["bias"],
+                              L["alpha"], cfg.epilogue, out=L["Y"], dtype=h)
+        elif cfg.epilogue == "qkv_norm_rope":
+            P.svdq_gemm_w4a4_qkv(L["codes"], L["scales"], la, L["w_codes"], L["w_scales"], lu, L["bias"],
+                                 L["qk_norm_w"], L["rope"], L["eps"], out=L["Y"], dtype=h)
+        else:
+            P.svdq_gemm_w4a4(L["codes"], L["scales"], la, L["w_codes"], L["w_scales"], lu, L["bias"],
+                             cfg.fmt, cfg.epilogue, out=L["Y"], dtype=h)
+
+    def fused_chain(Lu, Ld, lr):
+        la, lu = (Lu["lora_act"], Lu["lora_up"]) if lr else (None, None)
+        ld2, la2 = (Ld["lora_down"], Ld["lora_act"]) if lr else (None, None)
+        P.svdq_gemm_w4a4_mlp(Lu["codes"], Lu["scales"], la, Lu["w_codes"], Lu["w_scales"], lu, Lu["bias"],
+                             Ld["smooth_inv"], ld2, "int4_g64", Ld["codes"], Ld["scales"], la2,
+                             Lu["workspace"] if lr else None, dtype=torch.float16)
+
+    def gemv(G):
         P.awq_gemv_w4a16(G["x"], G["codes"], G["scales"], G["zeros"], out=G["y"])
-        ev(4)
 
-    def step(i, events=None):
+    plan = []
+    if chain:
+        (cu, ru, _), (cd, rd, _) = host_sets
+        plan.append((f"{cu.name}.svdq_quantize_act", "quantize", cu, ru, lambda Ls, G, lr: quant(Ls[0], lr)))
+        plan.append((f"{cu.name}.svdq_gemm_w4a4_mlp", "chain", cu, ru,
+                     lambda Ls, G, lr: fused_chain(Ls[0], Ls[1], lr)))
+        plan.append((f"{cd.name}.svdq_gemm_w4a4", "gemm", cd, rd, lambda Ls, G, lr: gemm(Ls[1], lr)))
+    else:
+        for li, (cfg, r, _) in enumerate(host_sets):
+            plan.append((f"{cfg.name}.svdq_quantize_act", "quantize", cfg, r,
+                         lambda Ls, G, lr, li=li: quant(Ls[li], lr)))
+            plan.append((f"{cfg.name}.{gemm_name(cfg)}", "gemm", cfg, r,
+                         lambda Ls, G, lr, li=li: gemm(Ls[li], lr)))
+    plan.append(("gemv.awq_gemv_w4a16", "gemv", gcfg, 0, lambda Ls, G, lr: gemv(G)))
+    nk = len(plan)
+
+    def step(i, events=None, lowrank=True):
         layers, G = sets[i % nsets]
-        if chain:
-            step_chain(layers, G, events)
-            return
-        j = 0
-        for L in layers:
-            cfg = L["cfg"]
+        for k, (_, _, _, _, fn) in enumerate(plan):
             if events is not None:
-                events[j].record(stream)
-            if cfg.fmt == "nvfp4_g16":
-                P.svdq_quantize_act_nvfp4(L["X"], L["smooth_inv"], L["lora_down"], L["act_gscale"],
-                                          L["codes"], L["scales"], L["lora_act"])
-            else:
-                P.svdq_quantize_act(L["X"], L["smooth_inv"], L["lora_down"], cfg.fmt,
-                                    L["codes"], L["scales"], L["lora_act"])
-            if events is not None:
-                events[j + 1].record(stream)
-            if cfg.fmt == "nvfp4_g16":
-                P.svdq_gemm_nvfp4(L["codes"], L["scales"], L["lora_act"], L["w_codes"], L["w_scales"],
-                                  L["lora_up"], L["bias"], L["alpha"], cfg.epilogue, out=L["Y"])
-            elif cfg.epilogue == "qkv_norm_rope":
-                P.svdq_gemm_w4a4_qkv(L["codes"], L["scales"], L["lora_act"], L["w_codes"], L["w_scales"],
-                                     L["lora_up"], L["bias"], L["qk_norm_w"], L["rope"], L["eps"],
-                                     out=L["Y"])
-            else:
-                P.svdq_gemm_w4a4(L["codes"], L["scales"], L["lora_act"], L["w_codes"], L["w_scales"],
-                                 L["lora_up"], L["bias"], cfg.fmt, cfg.epilogue, out=L["Y"])
-            j += 2
+                events[k].record(stream)
+            fn(layers, G, lowrank)
         if events is not None:
-            events[j].record(stream)
-        P.awq_gemv_w4a16(G["x"], G["codes"], G["scales"], G["zeros"], out=G["y"])
-        if events is not None:
-            events[j + 1].record(stream)
+            events[nk].record(stream)
 
-    # clocks ramp for tens of ms under load after idle: run untimed steps for
-    # --prewarm-ms of wall time (synchronizing every 8 steps so the host clock
-    # follows the GPU), then the W warm-up steps
-    t_end = time.perf_counter() + args.prewarm_ms * 1e-3
-    i = 0
-    while time.perf_counter() < t_end:
-        step(i)
-        i += 1
-        if i % 8 == 0:
-            torch.cuda.synchronize()
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    def timed(lowrank, sampler=None):
+        # clocks ramp for tens of ms under load after idle: untimed steps for
+        # --prewarm-ms of wall time (synchronizing every 8 steps so the host
+        # clock follows the GPU), then the W warm-up steps
+        t_end = time.perf_counter() + args.prewarm_ms * 1e-3
+        i = 0
+        while time.perf_counter() < t_end:
+            step(i, lowrank=lowrank)
+            i += 1
+            if i % 8 == 0:
+                torch.cuda.synchronize()
+        for i in range(args.warmup):
+            step(i, lowrank=lowrank)
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        if sampler is not None:
+            sampler.start()
+        t0 = time.perf_counter()
+        for s in range(args.steps):
+            step(args.warmup + s, evs[s], lowrank=lowrank)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        if sampler is not None:
+            sampler.stop()
+        # launch k spans events[k] -> events[k + 1] (ms)
+        durs = np.array([[e[k].elapsed_time(e[k + 1]) for k in range(nk)] for e in evs])
+        return wall * 1e3 / args.steps, durs
 
-    # event pairs per launch: quantize_l, gemm_l ..., gemv
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        step(args.warmup + s, evs[s])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    props = torch.cuda.get_device_properties(dev)
+    sampler = ClockSampler(getattr(props, "pci_bus_id", None))
+    ms_per_step, durs = timed(True, sampler)
 
     if args.calib_copy_mib:
         n = args.calib_copy_mib << 20
@@ -272,20 +383,22 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # per-launch durations (ms): launch k spans events[k] -> events[k+1]
-    durs = np.zeros((args.steps, nk))
-    for s in range(args.steps):
-        e = evs[s]
-        for k in range(nk):
-            durs[s, k] = e[k].elapsed_time(e[k + 1])
+    any_rank = any(r > 0 for _, _, _, r, _ in plan)
+    lr_over = None
+    if any_rank and not args.no_lowrank_overhead:
+        ms0, durs0 = timed(False)
+        mean0 = durs0.mean(axis=0)
+        lr_over = {"step": round(ms_per_step / ms0 - 1, 4), "rank": max(r for _, _, _, r, _ in plan),
+                   "ms_per_step_rank0": round(ms0, 4),
+                   "per_launch": {plan[k][0]: round(float(durs[:, k].mean() / mean0[k] - 1), 4)
+                                  for k in range(nk) if plan[k][1] != "gemv"},
+                   "note": "t(rank r) / t(rank 0) - 1, same inputs with the low-rank branch off "
+                           "(second timed pass)"}
+
     mean_ms = durs.mean(axis=0)
     med_ms = np.median(durs, axis=0)
     p10_ms = np.percentile(durs, 10, axis=0)
     p90_ms = np.percentile(durs, 90, axis=0)
-
-    def spread(k):
-        return {"p10_us": round(p10_ms[k] * 1e3, 2), "p90_us": round(p90_ms[k] * 1e3, 2)}
-    ms_per_step = wall * 1e3 / args.steps
 
     total_ops = sum(2.0 * c.M * c.N * c.K for c in cfgs)
     value = total_ops / (ms_per_step * 1e-3) / 1e12
@@ -293,70 +406,53 @@ def main():
     kernels = {}
     gemm_ms_sum = 0.0
     dominant = None
-    if chain:
-        (cu, ru, _), (cd, rd, _) = host_sets
-        qb, _ = layer_bytes(cu, ru)
-        kernels[f"{cu.name}.svdq_quantize_act"] = {
-            "avg_us": round(mean_ms[0] * 1e3, 2), "median_us": round(med_ms[0] * 1e3, 2), **spread(0),
-            "alg_bytes": qb, "GB/s": round(qb / (mean_ms[0] * 1e-3) / 1e9, 1)}
-        for k, (cfg, r, name) in ((1, (cu, ru, "svdq_gemm_w4a4_mlp")), (2, (cd, rd, "svdq_gemm_w4a4"))):
-            ops = 2.0 * cfg.M * cfg.N * cfg.K
-            tops = ops / (mean_ms[k] * 1e-3) / 1e12
-            kernels[f"{cfg.name}.{name}"] = {
-                "avg_us": round(mean_ms[k] * 1e3, 2), "median_us": round(med_ms[k] * 1e3, 2), **spread(k),
-                "alg_ops": ops, "TOPS": round(tops, 1), "frac_peak": round(tops / PEAK_TOPS[cfg.fmt], 4),
-                "format": cfg.fmt, "rank": r,
-                "note": "GEMM + GELU + the next layer's quantizer, then the fixed-order sum of the "
-                        "low-rank partials (two launches)" if k == 1 else "reads the chain's codes"}
-            gemm_ms_sum += mean_ms[k]
-            if dominant is None or mean_ms[k] > dominant[1]:
-                dominant = (cfg, mean_ms[k], ops, r)
-    for li, (cfg, r, _) in enumerate([] if chain else host_sets):
-        qb, gb = layer_bytes(cfg, r)
-        qms, gms = mean_ms[2 * li], mean_ms[2 * li + 1]
-        gemm_ms_sum += gms
+    for k, (label, kind, cfg, r, _) in enumerate(plan):
+        base = {"avg_us": round(mean_ms[k] * 1e3, 2), "median_us": round(med_ms[k] * 1e3, 2),
+                "p10_us": round(p10_ms[k] * 1e3, 2), "p90_us": round(p90_ms[k] * 1e3, 2)}
+        if kind in ("quantize", "gemv"):
+            b = layer_bytes(cfg, r)[0] if kind == "quantize" else gemv_bytes(cfg)
+            gbs = b / (mean_ms[k] * 1e-3) / 1e9
+            kernels[label] = {**base, "alg_bytes": b, "GB/s": round(gbs, 1),
+                              "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+            continue
         ops = 2.0 * cfg.M * cfg.N * cfg.K
-        kernels[f"{cfg.name}.svdq_quantize_act"] = {
-            "avg_us": round(qms * 1e3, 2), "median_us": round(med_ms[2 * li] * 1e3, 2), **spread(2 * li),
-            "alg_bytes": qb, "GB/s": round(qb / (qms * 1e-3) / 1e9, 1),
-            "frac_hbm": round(qb / (qms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
-        tops = ops / (gms * 1e-3) / 1e12
-        gname = gemm_name(cfg)
-        kernels[f"{cfg.name}.{gname}"] = {
-            "avg_us": round(gms * 1e3, 2), "median_us": round(med_ms[2 * li + 1] * 1e3, 2), **spread(2 * li + 1),
-            "alg_ops": ops, "lowrank_ops": 2.0 * cfg.M * cfg.N * r + 2.0 * cfg.M * cfg.K * r,
-            "TOPS": round(tops, 1), "frac_peak": round(tops / PEAK_TOPS[cfg.fmt], 4),
-            "format": cfg.fmt, "epilogue": cfg.epilogue, "rank": r}
-        if dominant is None or gms > dominant[1]:
-            dominant = (cfg, gms, ops, r)
-    gvb = gemv_bytes(gcfg)
-    gvms = mean_ms[-1]
-    kernels["gemv.awq_gemv_w4a16"] = {
-        "avg_us": round(gvms * 1e3, 2), "median_us": round(med_ms[-1] * 1e3, 2), **spread(nk - 1),
-        "alg_bytes": gvb, "GB/s": round(gvb / (gvms * 1e-3) / 1e9, 1),
-        "frac_hbm": round(gvb / (gvms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        tops = ops / (mean_ms[k] * 1e-3) / 1e12
+        gemm_ms_sum += mean_ms[k]
+        kernels[label] = {**base, "alg_ops": ops,
+                          "lowrank_ops": 2.0 * cfg.M * cfg.N * r + 2.0 * cfg.M * cfg.K * r,
+                          "TOPS": round(tops, 1), "frac_peak": round(tops / PEAK_TOPS[cfg.fmt], 4),
+                          "format": cfg.fmt, "epilogue": cfg.epilogue, "rank": r}
+        if kind == "chain":
+            kernels[label]["note"] = ("GEMM + GELU + the next layer's quantizer, then the fixed-order sum "
+                                      "of the low-rank partials (two launches)")
+        if dominant is None or mean_ms[k] > dominant[1]:
+            dominant = (label, mean_ms[k], ops, cfg, kind)
 
-    dcfg, dms, dops, dr = dominant
+    dlabel, dms, dops, dcfg, dkind = dominant
     achieved = dops / (dms * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "kernel": gemm_name(dcfg), "workload": dcfg.name,
+    multi = len(names) > 1
+    roofline = {"bound": "mfma", "kernel": dlabel.split(".", 1)[1], "layer": dcfg.name,
                 "achieved": round(achieved, 1), "peak": PEAK_TOPS[dcfg.fmt], "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_TOPS[dcfg.fmt], 4),
-                "traffic": stored_traffic(dcfg.name),
+                "traffic": stored_traffic(args.workload, dcfg.name if multi else None),
                 "ops_per_launch": dops,
-                "note": PEAK_NOTE[dcfg.fmt]}
+                "note": PEAK_NOTE[dcfg.fmt] + "; the dominant kernel is the launch with the longest "
+                        "mean event time, its algorithmic ops 2 M N K per launch"}
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfgs[0], gcfg, host_sets[0][2], gp, host_sets[0][1])
+        cpu = cpu_baseline([(c, r, p) for c, r, p in host_sets], gcfg, gp)
 
-    wl = ("DiT block linear stream (QKV, out-proj, MLP-up GELU, MLP-down; all W4A4 INT4 g64 r32)"
-          if args.workload == "block" else
-          "DiT MLP (M4096: up K3072 N12288 + GELU, down K12288 N3072; INT4 g64 r32)"
-          + (", fused chain: the up-projection's epilogue quantizes for the down-projection"
-             if chain else ", unfused")
-          if args.workload in ("mlp_pair", "mlp_chain") else
-          f"SVDQ W4A4 {cfgs[0].name} M={cfgs[0].M} K={cfgs[0].K} N={cfgs[0].N} r={host_sets[0][1]} "
-          f"{cfgs[0].fmt} epilogue={cfgs[0].epilogue}")
+    if args.workload == "block":
+        wl = "DiT block linear stream at M=4096, hidden 3072 (QKV 3072->9216, out-proj 3072->3072, " \
+             "MLP-up 3072->12288 GELU, MLP-down 12288->3072; all W4A4 INT4 g64 r32)"
+    elif args.workload in WORKLOADS:
+        wl = "DiT MLP at M=4096 (up K3072 N12288 + GELU, down K12288 N3072; INT4 g64 r32)" + (
+            ", fused chain: the up-projection's epilogue quantizes for the down-projection"
+            if chain else ", unfused")
+    else:
+        c = cfgs[0]
+        wl = f"SVDQ W4A4 {c.name} M={c.M} K={c.K} N={c.N} r={host_sets[0][1]} {c.fmt} epilogue={c.epilogue}"
     wl += f" + AWQ W4A16 modulation GEMV M=1 K={gcfg.K} N={gcfg.N} g{gcfg.group}"
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "TOPS", "n_gpus": 1,
@@ -364,60 +460,57 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "+".join(sorted({MFMA_DTYPE[c.fmt] for c in cfgs})),
         "data": "synthetic",
-        "config": {"workload": wl, "layers": names, "rotating_sets": nsets,
+        "config": {"workload": wl, "name": args.workload, "layers": names, "rotating_sets": nsets,
                    "cache": "warm" if args.warm else "cold (rotated > Infinity Cache)"},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": kernels,
-        "gemm_TOPS": round(sum(2.0 * c.M * c.N * c.K for c in cfgs) / (gemm_ms_sum * 1e-3) / 1e12, 1),
+        "lowrank_overhead": lr_over,
+        "clocks": sampler.summary(),
+        "gemm_TOPS": round(total_ops / (gemm_ms_sum * 1e-3) / 1e12, 1),
         "gemv_GBps": kernels["gemv.awq_gemv_w4a16"]["GB/s"],
-        "device": torch.cuda.get_device_properties(dev).gcnArchName,
+        "device": props.gcnArchName,
     }
     print(json.dumps(out), flush=True)
 
 
-MFMA_DTYPE = {"int4_g64": "int8", "fp4_b32": "fp4", "nvfp4_g16": "f16"}
-
-
-def gemm_name(cfg):
-    if cfg.fmt == "nvfp4_g16":
-        return "svdq_gemm_nvfp4"
-    return "svdq_gemm_w4a4_qkv" if cfg.epilogue == "qkv_norm_rope" else "svdq_gemm_w4a4"
-
-
-def cpu_baseline(cfg, gcfg, p, gp, r, min_seconds=10.0, max_passes=200):
-    """The oracle's run-time steps, as they stand, on the same workload:
-    quantizer + fp64 group-scaled GEMM + low-rank + bias over all tokens,
-    repeated until at least min_seconds of host time (a bounded sample), and
-    the fp64 AWQ GEMV. Scaled to TOPS over the passes' own 2*M*N*K."""
-    import numpy as np
-
+def cpu_baseline(layers, gcfg, gp, min_seconds=10.0, max_passes=50):
+    """The oracle's run-time steps, as they stand, on the same workload: per
+    layer of the stream, the quantizer (fp32 emulation) and the fp64 forward
+    (group-scaled GEMM + low-rank + bias [+ GELU]) over all of the layer's
+    tokens; whole passes over the stream until at least min_seconds of host
+    time (a bounded sample), then the fp64 AWQ GEMV once. Scaled to TOPS over
+    the passes' own 2 M N K."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count()
-    X = p["X"]
-    wu = oracle.unpack_nibbles(p["w_codes"], signed=(cfg.fmt == "int4_g64"))
+    unpacked = [oracle.unpack_nibbles(p["w_codes"], signed=(cfg.fmt == "int4_g64")) for cfg, _, p in layers]
     t0 = time.perf_counter()
     passes = 0
     while passes < max_passes and (passes == 0 or time.perf_counter() - t0 < min_seconds):
-        codes_u, _, scales = oracle.quantize_act_ref(X, p["smooth_inv"], cfg.fmt, p.get("act_gscale"))
-        la = oracle.lora_act_ref(X, p["lora_down"][:r])
-        oracle.gemm_ref(codes_u, scales, la, wu, p["w_scales"], p["lora_up"][:, :r], p["bias"], cfg.fmt,
-                        cfg.epilogue, act_gscale=p.get("act_gscale"), w_gscale=p.get("w_gscale"))
+        for (cfg, r, p), wu in zip(layers, unpacked):
+            codes_u, _, scales = oracle.quantize_act_ref(p["X"], p["smooth_inv"], cfg.fmt, p.get("act_gscale"))
+            la = oracle.lora_act_ref(p["X"], p["lora_down"][:r])
+            oracle.gemm_ref(codes_u, scales, la, wu, p["w_scales"], p["lora_up"][:, :r], p["bias"], cfg.fmt,
+                            "gelu_tanh" if cfg.epilogue == "gelu_tanh" else "none",
+                            act_gscale=p.get("act_gscale"), w_gscale=p.get("w_gscale"))
         passes += 1
-    t_layer = time.perf_counter() - t0
+    t_layers = time.perf_counter() - t0
     t1 = time.perf_counter()
     oracle.gemv_ref(gp["x"], gp["codes"], gp["scales"], gp["zeros"], gcfg.group)
     t_gemv = time.perf_counter() - t1
-    ops = 2.0 * cfg.M * cfg.N * cfg.K * passes
-    return {"value": round(ops / t_layer / 1e12, 5), "unit": "TOPS", "cores": int(threads),
+    ops = sum(2.0 * cfg.M * cfg.N * cfg.K for cfg, _, _ in layers) * passes
+    names = ", ".join(cfg.name for cfg, _, _ in layers)
+    return {"value": round(ops / t_layers / 1e12, 5), "unit": "TOPS", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"{passes} passes over all {cfg.M} tokens of the {cfg.name} layer (quantizer + "
-                      f"fp64 forward), {t_layer:.1f} s; full AWQ GEMV fp64 {t_gemv * 1e3:.0f} ms "
-                      f"({gemv_bytes(gcfg) / t_gemv / 1e9:.2f} GB/s)"}
+            "sample": f"{passes} pass(es) over all tokens of every layer ({names}): quantizer + fp64 "
+                      f"forward, {t_layers:.1f} s; the fp64 AWQ GEMV once, {t_gemv * 1e3:.0f} ms "
+                      f"({gemv_bytes(gcfg) / t_gemv / 1e9:.2f} GB/s)"
+                      + ("; the QKV epilogue's norm and rotation are not in the sample"
+                         if any(cfg.epilogue == "qkv_norm_rope" for cfg, _, _ in layers) else "")}
 
 
 if __name__ == "__main__":

@@ -72,15 +72,69 @@ def test_stored_traffic_follows_the_source(tmp_path, monkeypatch):
     assert bench.stored_traffic("w") is None
 
 
-@pytest.mark.parametrize("w", ["qkv", "mlp_up", "mlp_down", "mlp_up_nvfp4", "qkv_normrope"])
-def test_committed_traffic_records_are_well_formed(w):
+def test_stored_traffic_per_layer(tmp_path, monkeypatch):
+    """A stream's record holds one GEMM per layer; each is used only while its
+    source is unchanged."""
+    csrc = tmp_path / "bit_diffusion_transformer_act_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    (tmp_path / "profiles").mkdir()
+    (csrc / "k.hip").write_text("// kernel as profiled\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    sha = bench.kernel_source_hash("k.hip")
+    rec = {"layers": {"a": {"source": "k.hip", "source_sha": sha, "hbm_bytes_per_launch": 11},
+                      "b": {"source": "k.hip", "source_sha": "0" * 16, "hbm_bytes_per_launch": 22}}}
+    (tmp_path / "profiles" / "traffic_s.json").write_text(json.dumps(rec))
+    assert bench.stored_traffic("s", "a") == 11
+    assert bench.stored_traffic("s", "b") is None      # taken with another source
+    assert bench.stored_traffic("s", "c") is None      # no such layer
+
+
+def test_default_workload_is_the_block_stream():
+    """The default run is the DiT block's linear stream (QKV, out-projection,
+    MLP-up, MLP-down) with at least 100 timed and 20 warm-up steps."""
+    a = bench.parse([])
+    assert a.workload == "block" and a.steps >= 100 and a.warmup >= 20
+    assert bench.WORKLOADS["block"] == ("qkv", "attn_out", "mlp_up_int4", "mlp_down")
+    cfgs = [synth.CONFIGS[n] for n in bench.WORKLOADS["block"]]
+    assert [(c.K, c.N) for c in cfgs] == [(3072, 9216), (3072, 3072), (3072, 12288), (12288, 3072)]
+    assert all(c.M == 4096 and c.rank == 32 and c.fmt == "int4_g64" for c in cfgs)
+
+
+def test_step_pattern_labels_the_block():
+    """bench_counters labels every library dispatch by its slot in the step and
+    keeps a multi-dispatch launch (the quantizer's K split) together."""
+    import bench_counters as bc
+    pat = bc.step_pattern("block")
+    assert [p[0] for p in pat] == ["qkv", "qkv", "attn_out", "attn_out", "mlp_up_int4", "mlp_up_int4",
+                                   "mlp_down", "mlp_down", "gemv"]
+    names = ["quantize_act_kernel<0>", "gemm_w4a4_kernel<0>"] * 4 + ["awq_gemv_kernel<0>"]
+    rows = [{"Kernel_Name": "void svdq::" + n} for n in names * 3]
+    lab = bc.label(rows, pat)
+    assert len(lab) == 27 and [l[0] for l, _ in lab[:9]] == [p[0] for p in pat]
+    split = [{"Kernel_Name": "svdq::" + n} for n in ["quantize_act_kernel<a>", "quantize_act_kernel<b>",
+                                                     "gemm_w4a4_kernel<0>", "awq_gemv_kernel<0>"]]
+    lab = bc.label(split * 2, bc.step_pattern("mlp_down_m1024"))
+    assert [len(rs) for _, rs in lab] == [2, 1, 1, 2, 1, 1]
+    with pytest.raises(SystemExit):
+        bc.label([{"Kernel_Name": "svdq::awq_gemv_kernel<0>"}], pat)
+
+
+def _traffic_records():
+    d = os.path.join(ROOT, "profiles")
+    return sorted(f for f in os.listdir(d) if f.startswith("traffic_") and f.endswith(".json"))
+
+
+@pytest.mark.parametrize("fname", _traffic_records())
+def test_committed_traffic_records_are_well_formed(fname):
     """Each committed record names an existing kernel source, a 16-hex-digit hash
     and a per-launch byte count per kernel (bench.py reports the GEMM's only while
-    that hash matches, else null)."""
-    d = json.load(open(os.path.join(ROOT, "profiles", f"traffic_{w}.json")))
-    assert os.path.exists(os.path.join(ROOT, "bit_diffusion_transformer_act_amd", "csrc", d["source"]))
-    assert len(d["source_sha"]) == 16 and int(d["source_sha"], 16) >= 0
-    assert d["hbm_bytes_per_launch"] > 0
-    for k in d["kernels"].values():
-        # each of the three is rounded to whole bytes on its own
-        assert abs(k["hbm_bytes_per_launch"] - k["hbm_read_bytes"] - k["hbm_write_bytes"]) <= 1
+    that hash matches, else null); a stream's record does so per layer."""
+    d = json.load(open(os.path.join(ROOT, "profiles", fname)))
+    entries = list(d["layers"].values()) if "layers" in d else [d]
+    for e in entries:
+        assert os.path.exists(os.path.join(ROOT, "bit_diffusion_transformer_act_amd", "csrc", e["source"]))
+        assert len(e["source_sha"]) == 16 and int(e["source_sha"], 16) >= 0
+        assert e["hbm_bytes_per_launch"] > 0
+        for k in e["kernels"].values():
+            # each of the three is rounded to whole bytes on its own
+            assert abs(k["hbm_bytes_per_launch"] - k["hbm_read_bytes"] - k["hbm_write_bytes"]) <= 1
