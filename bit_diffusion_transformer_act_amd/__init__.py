@@ -15,6 +15,7 @@ from .ops import (  # noqa: F401
     svdq_gemm_w4a4,
     svdq_gemm_w4a4_qkv,
     svdq_gemm_w4a4_mlp,
+    svdq_gemm_w4a4_mlp_noalloc,
     svdq_gemm_nvfp4,
     svdq_quantize_act_nvfp4,
     svdq_linear,

@@ -9,9 +9,16 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "launch.hpp"
 #include "svdq.h"
+
+namespace svdq {
+// 64 MiB: the chain's partials at M 4096, N 12288, rank 32 take 50 MB
+constexpr size_t kChainScratchBytes = size_t{64} << 20;
+__device__ __align__(256) uint8_t scratch[kChainScratchBytes];
+}  // namespace svdq
 
 namespace {
 
@@ -63,6 +70,87 @@ bool k_ok(int K) { return K >= 128 && K <= 65536 && (K % 128) == 0; }
 bool k_nv_ok(int K) { return K >= 256 && K <= 65536 && (K % 256) == 0; }
 bool positive_finite(float v) { return std::isfinite(v) && v > 0.0f; }
 bool dtype_ok(int d) { return d == SVDQ_F16 || d == SVDQ_BF16; }
+
+// Device scratch of svdq_gemm_w4a4_mlp_noalloc: the fused MLP chain's fp32
+// low-rank partials live here instead of in a caller workspace. One copy per
+// GPU, held until the process ends; every call on a GPU shares it. Host code
+// never names `scratch` as a device address: scratch_address() takes the
+// device's own address from hipGetSymbolAddress, once per device, with that
+// device current.
+constexpr size_t kScratchBytes = svdq::kChainScratchBytes;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return SVDQ_ERR_UNSUPPORTED_DEVICE;
+  }
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(svdq::scratch));
+      if (e != hipSuccess || p == nullptr) {
+        (void)hipGetLastError();
+        return SVDQ_ERR_HIP;
+      }
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return SVDQ_OK;
+}
+
+size_t mlp_partial_bytes(int M, int N, int r2) {
+  if (M < 0 || N < 0 || r2 < 0) return 0;
+  return (size_t)(N / 128) * (size_t)M * (size_t)r2 * sizeof(float);
+}
+
+// The fused MLP chain behind both entry points. workspace: NULL means the
+// device scratch above (then the partials must fit in it).
+int mlp_chain(int fmt, int dtype, int M, int N, int K, int r, const uint8_t* act_codes, const void* act_scales,
+              const float* lora_act, const uint8_t* w_codes, const void* w_scales, const void* lora_up,
+              const void* bias, const float* smooth_inv2, const void* lora_down2, int r2,
+              uint8_t* act_codes2, void* act_scales2, float* lora_act2, void* workspace,
+              size_t workspace_bytes, bool use_scratch, void* stream) {
+  if (fmt != SVDQ_INT4_G64) return SVDQ_ERR_INVALID_ARG;
+  if (!dtype_ok(dtype)) return SVDQ_ERR_INVALID_ARG;
+  if (M < 0 || M > (1 << 23) || N < 128 || N > 65536 || (N % 128) != 0 || !k_ok(K) || !rank_ok(r) ||
+      !rank_ok(r2))
+    return SVDQ_ERR_SHAPE;
+  if (use_scratch && r2 > 0 && mlp_partial_bytes(M, N, r2) > kScratchBytes) return SVDQ_ERR_SHAPE;
+  if (M == 0) return SVDQ_OK;
+  if (!act_codes || !act_scales || !w_codes || !w_scales || !smooth_inv2 || !act_codes2 || !act_scales2)
+    return SVDQ_ERR_INVALID_ARG;
+  if (r > 0 && (!lora_act || !lora_up)) return SVDQ_ERR_INVALID_ARG;
+  if (r2 > 0 && (!lora_down2 || !lora_act2 || (!use_scratch && !workspace))) return SVDQ_ERR_INVALID_ARG;
+  if (!use_scratch && r2 > 0 && workspace_bytes < mlp_partial_bytes(M, N, r2)) return SVDQ_ERR_SHAPE;
+  if (!aligned16(act_codes) || !aligned16(act_scales) || !aligned16(w_codes) || !aligned16(w_scales) ||
+      (bias && !aligned16(bias)) || !aligned16(smooth_inv2) || !aligned16(act_codes2) ||
+      !aligned16(act_scales2))
+    return SVDQ_ERR_ALIGN;
+  if (r > 0 && (!aligned16(lora_act) || !aligned16(lora_up))) return SVDQ_ERR_ALIGN;
+  if (r2 > 0 && (!aligned16(lora_down2) || !aligned16(lora_act2) || (!use_scratch && !aligned16(workspace))))
+    return SVDQ_ERR_ALIGN;
+  const int dc = check_current_device();
+  if (dc != SVDQ_OK) return dc;
+  (void)hipGetLastError();
+  if (use_scratch && r2 > 0) {
+    const int sc = scratch_address(&workspace);
+    if (sc != SVDQ_OK) return sc;
+  }
+  const svdq::ChainEpilogue ce{smooth_inv2, lora_down2, r2, act_codes2, act_scales2,
+                               static_cast<float*>(workspace)};
+  hipError_t e = svdq::launch_gemm_w4a4(fmt, dtype, M, N, K, r, act_codes, act_scales, lora_act, w_codes,
+                                        w_scales, lora_up, bias, 3, nullptr, (hipStream_t)stream, nullptr, &ce);
+  if (e == hipSuccess && r2 > 0)
+    e = svdq::launch_chain_reduce(M, r2, N / 128, static_cast<const float*>(workspace), lora_act2,
+                                  (hipStream_t)stream);
+  return finish(e);
+}
 
 }  // namespace
 
@@ -152,10 +240,7 @@ int svdq_gemm_w4a4_qkv(int fmt, int dtype, int M, int N, int K, int r, const uin
                                        w_scales, lora_up, bias, 2, Y, (hipStream_t)stream, &qe));
 }
 
-size_t svdq_gemm_w4a4_mlp_workspace(int M, int N, int r2) {
-  if (M < 0 || N < 0 || r2 < 0) return 0;
-  return (size_t)(N / 128) * (size_t)M * (size_t)r2 * sizeof(float);
-}
+size_t svdq_gemm_w4a4_mlp_workspace(int M, int N, int r2) { return mlp_partial_bytes(M, N, r2); }
 
 int svdq_gemm_w4a4_mlp(int fmt, int dtype, int M, int N, int K, int r, const uint8_t* act_codes,
                        const void* act_scales, const float* lora_act, const uint8_t* w_codes,
@@ -163,35 +248,18 @@ int svdq_gemm_w4a4_mlp(int fmt, int dtype, int M, int N, int K, int r, const uin
                        const float* smooth_inv2, const void* lora_down2, int r2, uint8_t* act_codes2,
                        void* act_scales2, float* lora_act2, void* workspace, size_t workspace_bytes,
                        void* stream) {
-  if (fmt != SVDQ_INT4_G64) return SVDQ_ERR_INVALID_ARG;
-  if (!dtype_ok(dtype)) return SVDQ_ERR_INVALID_ARG;
-  if (M < 0 || M > (1 << 23) || N < 128 || N > 65536 || (N % 128) != 0 || !k_ok(K) || !rank_ok(r) ||
-      !rank_ok(r2))
-    return SVDQ_ERR_SHAPE;
-  if (M == 0) return SVDQ_OK;
-  if (!act_codes || !act_scales || !w_codes || !w_scales || !smooth_inv2 || !act_codes2 || !act_scales2)
-    return SVDQ_ERR_INVALID_ARG;
-  if (r > 0 && (!lora_act || !lora_up)) return SVDQ_ERR_INVALID_ARG;
-  if (r2 > 0 && (!lora_down2 || !lora_act2 || !workspace)) return SVDQ_ERR_INVALID_ARG;
-  if (r2 > 0 && workspace_bytes < svdq_gemm_w4a4_mlp_workspace(M, N, r2)) return SVDQ_ERR_SHAPE;
-  if (!aligned16(act_codes) || !aligned16(act_scales) || !aligned16(w_codes) || !aligned16(w_scales) ||
-      (bias && !aligned16(bias)) || !aligned16(smooth_inv2) || !aligned16(act_codes2) ||
-      !aligned16(act_scales2))
-    return SVDQ_ERR_ALIGN;
-  if (r > 0 && (!aligned16(lora_act) || !aligned16(lora_up))) return SVDQ_ERR_ALIGN;
-  if (r2 > 0 && (!aligned16(lora_down2) || !aligned16(lora_act2) || !aligned16(workspace)))
-    return SVDQ_ERR_ALIGN;
-  const int dc = check_current_device();
-  if (dc != SVDQ_OK) return dc;
-  (void)hipGetLastError();
-  const svdq::ChainEpilogue ce{smooth_inv2, lora_down2, r2, act_codes2, act_scales2,
-                               static_cast<float*>(workspace)};
-  hipError_t e = svdq::launch_gemm_w4a4(fmt, dtype, M, N, K, r, act_codes, act_scales, lora_act, w_codes,
-                                        w_scales, lora_up, bias, 3, nullptr, (hipStream_t)stream, nullptr, &ce);
-  if (e == hipSuccess && r2 > 0)
-    e = svdq::launch_chain_reduce(M, r2, N / 128, static_cast<const float*>(workspace),
-                                  lora_act2, (hipStream_t)stream);
-  return finish(e);
+  return mlp_chain(fmt, dtype, M, N, K, r, act_codes, act_scales, lora_act, w_codes, w_scales, lora_up, bias,
+                   smooth_inv2, lora_down2, r2, act_codes2, act_scales2, lora_act2, workspace, workspace_bytes,
+                   false, stream);
+}
+
+int svdq_gemm_w4a4_mlp_noalloc(int fmt, int dtype, int M, int N, int K, int r, const uint8_t* act_codes,
+                               const void* act_scales, const float* lora_act, const uint8_t* w_codes,
+                               const void* w_scales, const void* lora_up, const void* bias,
+                               const float* smooth_inv2, const void* lora_down2, int r2, uint8_t* act_codes2,
+                               void* act_scales2, float* lora_act2, void* stream) {
+  return mlp_chain(fmt, dtype, M, N, K, r, act_codes, act_scales, lora_act, w_codes, w_scales, lora_up, bias,
+                   smooth_inv2, lora_down2, r2, act_codes2, act_scales2, lora_act2, nullptr, 0, true, stream);
 }
 
 int svdq_quantize_act_nvfp4(int dtype, int M, int K, int r, const void* X, const float* smooth_inv,

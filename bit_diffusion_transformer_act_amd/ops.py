@@ -39,7 +39,7 @@ SVDQ_ERR_HIP = -5
 EXPORTED_SYMBOLS = ("svdq_device_check", "svdq_status_str", "svdq_version",
                     "svdq_quantize_act", "svdq_gemm_w4a4", "svdq_gemm_w4a4_qkv",
                     "svdq_quantize_act_nvfp4", "svdq_gemm_nvfp4", "awq_gemv_w4a16",
-                    "svdq_gemm_w4a4_mlp", "svdq_gemm_w4a4_mlp_workspace")
+                    "svdq_gemm_w4a4_mlp", "svdq_gemm_w4a4_mlp_workspace", "svdq_gemm_w4a4_mlp_noalloc")
 
 _lock = threading.Lock()
 _handle = None
@@ -86,6 +86,9 @@ def lib() -> ctypes.CDLL:
             h.svdq_gemm_w4a4_mlp.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp,
                                              vp, vp, i32, vp, vp, vp, vp, sz, vp]
             h.svdq_gemm_w4a4_mlp.restype = i32
+            h.svdq_gemm_w4a4_mlp_noalloc.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp,
+                                                     vp, vp, i32, vp, vp, vp, vp]
+            h.svdq_gemm_w4a4_mlp_noalloc.restype = i32
             h.awq_gemv_w4a16.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
             h.awq_gemv_w4a16.restype = i32
             _handle = h
@@ -335,6 +338,57 @@ def svdq_gemm_w4a4_mlp(act_codes, act_scales, lora_act, w_codes, w_scales, lora_
                                       _ptr(workspace) if r2 > 0 else None, wbytes, _stream(dev))
     if st != SVDQ_OK:
         raise SvdqError(st, "svdq_gemm_w4a4_mlp")
+    return act_codes2, act_scales2, (lora_act2 if r2 > 0 else None)
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # the library's device scratch of the allocation-free chain
+
+
+def svdq_gemm_w4a4_mlp_noalloc(act_codes, act_scales, lora_act, w_codes, w_scales, lora_up, bias,
+                               smooth_inv2, lora_down2, act_codes2, act_scales2, lora_act2, fmt="int4_g64",
+                               dtype=None):
+    """svdq_gemm_w4a4_mlp without a workspace and without any allocation: the
+    fp32 partials live in the library's per-GPU device scratch (64 MiB; calls
+    that overlap on one GPU race). The outputs act_codes2 u8 [M][N/2],
+    act_scales2 fp16 [M][N/64] and lora_act2 fp32 [M][r2] (None when r2 == 0)
+    must be passed; nothing is allocated here either. Returns them."""
+    f = _fmt(fmt)
+    h = _pick_dtype(dtype, lora_up, bias, lora_down2)
+    io = DTYPES[h]
+    dev = act_codes.device
+    if dev.type != "cuda":
+        raise ValueError("act_codes must be a HIP device tensor")
+    M, KB = act_codes.shape
+    K = 2 * KB
+    N = w_codes.shape[0]
+    r = 0 if lora_up is None else lora_up.shape[1]
+    r2 = 0 if lora_down2 is None else lora_down2.shape[0]
+    sdt, sa_shape = _scale_spec(f, M, K)
+    _, sw_shape = _scale_spec(f, N, K)
+    _check(act_codes, "act_codes", torch.uint8, (M, KB), dev)
+    _check(act_scales, "act_scales", sdt, sa_shape, dev)
+    _check(w_codes, "w_codes", torch.uint8, (N, KB), dev)
+    _check(w_scales, "w_scales", sdt, sw_shape, dev)
+    if r > 0:
+        _check(lora_act, "lora_act", torch.float32, (M, r), dev)
+        _check(lora_up, "lora_up", h, (N, r), dev)
+    if bias is not None:
+        _check(bias, "bias", h, (N,), dev)
+    _check(smooth_inv2, "smooth_inv2", torch.float32, (N,), dev)
+    _check(act_codes2, "act_codes2", torch.uint8, (M, N // 2), dev)
+    _check(act_scales2, "act_scales2", torch.float16, (M, N // 64), dev)
+    if r2 > 0:
+        _check(lora_down2, "lora_down2", h, (r2, N), dev)
+        _check(lora_act2, "lora_act2", torch.float32, (M, r2), dev)
+    with torch.cuda.device(dev):
+        st = lib().svdq_gemm_w4a4_mlp_noalloc(f, io, M, N, K, r, _ptr(act_codes), _ptr(act_scales),
+                                              _ptr(lora_act) if r > 0 else None, _ptr(w_codes),
+                                              _ptr(w_scales), _ptr(lora_up) if r > 0 else None, _ptr(bias),
+                                              _ptr(smooth_inv2), _ptr(lora_down2) if r2 > 0 else None, r2,
+                                              _ptr(act_codes2), _ptr(act_scales2),
+                                              _ptr(lora_act2) if r2 > 0 else None, _stream(dev))
+    if st != SVDQ_OK:
+        raise SvdqError(st, "svdq_gemm_w4a4_mlp_noalloc")
     return act_codes2, act_scales2, (lora_act2 if r2 > 0 else None)
 
 

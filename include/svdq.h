@@ -248,6 +248,30 @@ int svdq_gemm_w4a4_mlp(int fmt, int dtype, int M, int N, int K, int r,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * svdq_gemm_w4a4_mlp_noalloc -- svdq_gemm_w4a4_mlp for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same computation, the same arguments
+ * without `workspace` / `workspace_bytes`, bit-identical results. The fp32
+ * partials live in a device array of the library instead: 64 MiB
+ * (67108864 bytes), one copy per GPU, created when the library's code is
+ * loaded on that GPU and held until the process ends. The call allocates
+ * nothing and calls no allocating routine.
+ *
+ * Limit: svdq_gemm_w4a4_mlp_workspace(M, N, r2) <= 67108864 (e.g. M 4096,
+ * N 12288, r2 32 needs 50331648), else SVDQ_ERR_SHAPE; r2 == 0 uses no scratch.
+ * Every call on one GPU shares the array and overwrites it (the partials are
+ * written in full before they are read, so nothing needs clearing): calls
+ * that overlap on one GPU -- on two streams, or from two threads without
+ * ordering -- race and give wrong results. Calls on one stream are ordered
+ * and safe.
+ */
+int svdq_gemm_w4a4_mlp_noalloc(int fmt, int dtype, int M, int N, int K, int r,
+                               const uint8_t* act_codes, const void* act_scales, const float* lora_act,
+                               const uint8_t* w_codes, const void* w_scales, const void* lora_up,
+                               const void* bias, const float* smooth_inv2, const void* lora_down2, int r2,
+                               uint8_t* act_codes2, void* act_scales2, float* lora_act2, void* stream);
+
+/*
  * svdq_quantize_act_nvfp4 -- svdq_quantize_act for NVFP4 (the pages' svdq_w4a4
  * precision "nvfp4" with group size 16: dothoosh.com article,
  * quantization_config block). Smoothing and the low-rank down-projection as

@@ -179,6 +179,29 @@ def test_mlp_chain_argument_errors():
     assert gm() == ops.SVDQ_ERR_UNSUPPORTED_DEVICE
 
 
+def gz(M=4, N=128, K=128, r=16, r2=16, ac=A, sa=A, la=A, wc=A, ws=A, lu=A, b=None, si2=A, ld2=A,
+       c2=A, s2=A, la2=A, dt=0, fmt=0):
+    return P.lib().svdq_gemm_w4a4_mlp_noalloc(fmt, dt, M, N, K, r, ac, sa, la, wc, ws, lu, b, si2, ld2, r2, c2, s2,
+                                              la2, None)
+
+
+def test_mlp_chain_noalloc_argument_errors():
+    """The allocation-free chain: the chain's checks, no workspace, and the
+    64 MiB limit of the library's device scratch (partials M (N/128) r2 fp32)."""
+    assert gz(fmt=1) == ops.SVDQ_ERR_INVALID_ARG
+    assert gz(N=192) == ops.SVDQ_ERR_SHAPE
+    assert gz(c2=U) == ops.SVDQ_ERR_ALIGN
+    assert gz(la2=None) == ops.SVDQ_ERR_INVALID_ARG
+    assert gz() == ops.SVDQ_ERR_UNSUPPORTED_DEVICE
+    # the DiT MLP (M 4096, N 12288, rank 32: 50331648 bytes) fits; exactly 64 MiB fits; more does not
+    assert gz(M=4096, N=12288, K=3072, r2=32) == ops.SVDQ_ERR_UNSUPPORTED_DEVICE
+    assert gz(M=4096, N=16384, K=3072, r2=32) == ops.SVDQ_ERR_UNSUPPORTED_DEVICE
+    assert gz(M=4096, N=16384, K=3072, r2=48) == ops.SVDQ_ERR_SHAPE
+    assert gz(M=8192, N=12288, K=3072, r2=32) == ops.SVDQ_ERR_SHAPE
+    assert gz(M=8192, N=12288, K=3072, r2=0, ld2=None, la2=None) == ops.SVDQ_ERR_UNSUPPORTED_DEVICE
+    assert ops.NOALLOC_SCRATCH_BYTES == 64 << 20
+
+
 def test_device_check_without_gpu():
     assert P.svdq_device_check(0) == ops.SVDQ_ERR_UNSUPPORTED_DEVICE
     assert P.svdq_device_check(-1) == ops.SVDQ_ERR_UNSUPPORTED_DEVICE
