@@ -57,15 +57,25 @@ SCALE_BYTES_PER_ROW = {"int4_g64": lambda K: (K // 64) * 2, "fp4_b32": lambda K:
 PEAK_HBM_GBS = 8000.0
 ROTATE_BYTES = 600 << 20
 
-# workloads of several layers, in stream order
+# workloads of several layers, in stream order; CHAINS names the layers whose
+# output feeds the next layer through the fused MLP chain (the next layer's
+# quantizer runs in their epilogue)
+BLOCK_INT4 = ("qkv", "attn_out", "mlp_up_int4", "mlp_down")
+BLOCK_FP4 = ("qkv", "attn_out", "mlp_up", "mlp_down")   # MLP-up in FP4 E2M1, as its own workload has it
 WORKLOADS = {
-    "block": ("qkv", "attn_out", "mlp_up_int4", "mlp_down"),
+    "block": BLOCK_INT4,
+    "block_chain": BLOCK_INT4,
+    "block_fp4": BLOCK_FP4,
+    "block_fp4_chain": BLOCK_FP4,
     "mlp_pair": ("mlp_up_int4", "mlp_down"),
     "mlp_chain": ("mlp_up_int4", "mlp_down"),
+    "mlp_pair_fp4": ("mlp_up", "mlp_down"),
+    "mlp_chain_fp4": ("mlp_up", "mlp_down"),
 }
+CHAINS = {"block_chain": ("mlp_up_int4",), "block_fp4_chain": ("mlp_up",), "mlp_chain": ("mlp_up_int4",),
+          "mlp_chain_fp4": ("mlp_up",)}
 SINGLE = ("qkv", "qkv_normrope", "mlp_up", "mlp_up_nvfp4", "mlp_down", "mlp_down_m1024", "attn_out",
           "mlp_up_int4")
-CHAINED = ("mlp_chain",)
 
 
 def parse(argv=None):
@@ -229,7 +239,7 @@ def main(argv=None):
         print("cuda:0 is not a gfx950 (MI355X) device", file=sys.stderr)
         sys.exit(3)
 
-    chain = args.workload in CHAINED
+    chained = CHAINS.get(args.workload, ())
     names = list(WORKLOADS.get(args.workload, (args.workload,)))
     cfgs = [synth.CONFIGS[n] for n in names]
     gcfg = synth.CONFIGS["gemv"]
@@ -272,12 +282,12 @@ def main(argv=None):
                 e = synth.qkv_epilogue_inputs(cfg.M, seed=0)
                 L["qk_norm_w"], L["rope"], L["eps"] = t(e["qk_norm_w"]), t(e["rope"]), e["eps"]
             layers.append(L)
-        if chain:
-            # the fused chain writes the down-projection's codes, scales and lora_act
-            # directly; its fp32 partials live in a caller-owned workspace
-            Lu, Ld = layers
-            wsb = P.lib().svdq_gemm_w4a4_mlp_workspace(Lu["cfg"].M, Lu["cfg"].N, Ld["r"])
-            Lu["workspace"] = torch.empty(max(1, wsb // 4), dtype=torch.float32, device=dev)
+        for li, L in enumerate(layers):
+            if L["cfg"].name in chained:
+                # the fused chain writes the next layer's codes, scales and lora_act
+                # directly; its fp32 partials live in a caller-owned workspace
+                wsb = P.lib().svdq_gemm_w4a4_mlp_workspace(L["cfg"].M, L["cfg"].N, layers[li + 1]["r"])
+                L["workspace"] = torch.empty(max(1, wsb // 4), dtype=torch.float32, device=dev)
         G = {"x": t(gp["x"]), "codes": t(gp["codes"]), "scales": t(gp["scales"]),
              "zeros": t(gp["zeros"]), "y": torch.empty((1, gcfg.N), dtype=torch.float16, device=dev)}
         sets.append((layers, G))
@@ -311,23 +321,21 @@ def main(argv=None):
         la, lu = (Lu["lora_act"], Lu["lora_up"]) if lr else (None, None)
         ld2, la2 = (Ld["lora_down"], Ld["lora_act"]) if lr else (None, None)
         P.svdq_gemm_w4a4_mlp(Lu["codes"], Lu["scales"], la, Lu["w_codes"], Lu["w_scales"], lu, Lu["bias"],
-                             Ld["smooth_inv"], ld2, "int4_g64", Ld["codes"], Ld["scales"], la2,
+                             Ld["smooth_inv"], ld2, Lu["cfg"].fmt, Ld["codes"], Ld["scales"], la2,
                              Lu["workspace"] if lr else None, dtype=torch.float16)
 
     def gemv(G):
         P.awq_gemv_w4a16(G["x"], G["codes"], G["scales"], G["zeros"], out=G["y"])
 
     plan = []
-    if chain:
-        (cu, ru, _), (cd, rd, _) = host_sets
-        plan.append((f"{cu.name}.svdq_quantize_act", "quantize", cu, ru, lambda Ls, G, lr: quant(Ls[0], lr)))
-        plan.append((f"{cu.name}.svdq_gemm_w4a4_mlp", "chain", cu, ru,
-                     lambda Ls, G, lr: fused_chain(Ls[0], Ls[1], lr)))
-        plan.append((f"{cd.name}.svdq_gemm_w4a4", "gemm", cd, rd, lambda Ls, G, lr: gemm(Ls[1], lr)))
-    else:
-        for li, (cfg, r, _) in enumerate(host_sets):
+    for li, (cfg, r, _) in enumerate(host_sets):
+        if li == 0 or host_sets[li - 1][0].name not in chained:   # else the chain quantized for it
             plan.append((f"{cfg.name}.svdq_quantize_act", "quantize", cfg, r,
                          lambda Ls, G, lr, li=li: quant(Ls[li], lr)))
+        if cfg.name in chained:
+            plan.append((f"{cfg.name}.svdq_gemm_w4a4_mlp", "chain", cfg, r,
+                         lambda Ls, G, lr, li=li: fused_chain(Ls[li], Ls[li + 1], lr)))
+        else:
             plan.append((f"{cfg.name}.{gemm_name(cfg)}", "gemm", cfg, r,
                          lambda Ls, G, lr, li=li: gemm(Ls[li], lr)))
     plan.append(("gemv.awq_gemv_w4a16", "gemv", gcfg, 0, lambda Ls, G, lr: gemv(G)))
@@ -443,13 +451,16 @@ def main(argv=None):
     if not args.no_cpu_baseline:
         cpu = cpu_baseline([(c, r, p) for c, r, p in host_sets], gcfg, gp)
 
-    if args.workload == "block":
-        wl = "DiT block linear stream at M=4096, hidden 3072 (QKV 3072->9216, out-proj 3072->3072, " \
-             "MLP-up 3072->12288 GELU, MLP-down 12288->3072; all W4A4 INT4 g64 r32)"
+    fused = (", fused chain: the MLP up-projection's epilogue quantizes for the down-projection"
+             if chained else "")
+    up_fmt = "FP4 E2M1 b32" if "mlp_up" in names else "INT4 g64"
+    if args.workload.startswith("block"):
+        wl = ("DiT block linear stream at M=4096, hidden 3072 (QKV 3072->9216, out-proj 3072->3072, "
+              f"MLP-up 3072->12288 GELU, MLP-down 12288->3072; W4A4 r32, INT4 g64 except MLP-up {up_fmt})"
+              + fused)
     elif args.workload in WORKLOADS:
-        wl = "DiT MLP at M=4096 (up K3072 N12288 + GELU, down K12288 N3072; INT4 g64 r32)" + (
-            ", fused chain: the up-projection's epilogue quantizes for the down-projection"
-            if chain else ", unfused")
+        wl = (f"DiT MLP at M=4096 (up K3072 N12288 + GELU in {up_fmt}, down K12288 N3072 INT4 g64; r32)"
+              + (fused or ", unfused"))
     else:
         c = cfgs[0]
         wl = f"SVDQ W4A4 {c.name} M={c.M} K={c.K} N={c.N} r={host_sets[0][1]} {c.fmt} epilogue={c.epilogue}"

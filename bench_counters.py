@@ -48,21 +48,25 @@ SOURCES = [("gemm_fp4_big_kernel", "gemm_fp4.hip"), ("gemm_w4a4_kernel", "gemm_w
 
 def step_pattern(workload: str):
     """Labels of the library dispatches of one bench.py step, in order:
-    (layer, entry point, kernel-name substring that must match)."""
+    (layer, entry point, kernel-name substring that must match). A fused MLP
+    chain is the up-projection's GEMM (INT4 or FP4 kernel) and the reduce of
+    its low-rank partials; the next layer then has no quantizer launch."""
     import bench
-    if workload in bench.CHAINED:
-        up, down = bench.WORKLOADS[workload]
-        pat = [(up, "svdq_quantize_act", "quantize_act_kernel"),
-               (up, "svdq_gemm_w4a4_mlp", "gemm_w4a4_kernel"),
-               (up, "svdq_gemm_w4a4_mlp.reduce", "chain_reduce_kernel"),
-               (down, "svdq_gemm_w4a4", "gemm_w4a4_kernel")]
-    else:
-        import synth
-        pat = []
-        for name in bench.WORKLOADS.get(workload, (workload,)):
-            cfg = synth.CONFIGS[name]
+    import synth
+    names = bench.WORKLOADS.get(workload, (workload,))
+    chained = bench.CHAINS.get(workload, ())
+    pat = []
+    for i, name in enumerate(names):
+        cfg = synth.CONFIGS[name]
+        if i == 0 or names[i - 1] not in chained:
+            pat.append((name, "svdq_quantize_act", "quantize_act_kernel"))
+        if name in chained:
+            pat.append((name, "svdq_gemm_w4a4_mlp", "gemm_"))
+            if synth.CONFIGS[names[i + 1]].rank > 0:
+                pat.append((name, "svdq_gemm_w4a4_mlp.reduce", "chain_reduce_kernel"))
+        else:
             gk = "gemm_nvfp4_kernel" if cfg.fmt == "nvfp4_g16" else "gemm_"
-            pat += [(name, "svdq_quantize_act", "quantize_act_kernel"), (name, bench.gemm_name(cfg), gk)]
+            pat.append((name, bench.gemm_name(cfg), gk))
     return pat + [("gemv", "awq_gemv_w4a16", "awq_gemv")]
 
 

@@ -116,7 +116,7 @@ int mlp_chain(int fmt, int dtype, int M, int N, int K, int r, const uint8_t* act
               const void* bias, const float* smooth_inv2, const void* lora_down2, int r2,
               uint8_t* act_codes2, void* act_scales2, float* lora_act2, void* workspace,
               size_t workspace_bytes, bool use_scratch, void* stream) {
-  if (fmt != SVDQ_INT4_G64) return SVDQ_ERR_INVALID_ARG;
+  if (fmt != SVDQ_INT4_G64 && fmt != SVDQ_FP4_E2M1_B32) return SVDQ_ERR_INVALID_ARG;
   if (!dtype_ok(dtype)) return SVDQ_ERR_INVALID_ARG;
   if (M < 0 || M > (1 << 23) || N < 128 || N > 65536 || (N % 128) != 0 || !k_ok(K) || !rank_ok(r) ||
       !rank_ok(r2))
@@ -147,8 +147,8 @@ int mlp_chain(int fmt, int dtype, int M, int N, int K, int r, const uint8_t* act
   hipError_t e = svdq::launch_gemm_w4a4(fmt, dtype, M, N, K, r, act_codes, act_scales, lora_act, w_codes,
                                         w_scales, lora_up, bias, 3, nullptr, (hipStream_t)stream, nullptr, &ce);
   if (e == hipSuccess && r2 > 0)
-    e = svdq::launch_chain_reduce(M, r2, N / 128, static_cast<const float*>(workspace), lora_act2,
-                                  (hipStream_t)stream);
+    e = svdq::launch_chain_reduce(M, r2, N / svdq::chain_tile_n(fmt, M, N, K),
+                                  static_cast<const float*>(workspace), lora_act2, (hipStream_t)stream);
   return finish(e);
 }
 

@@ -25,6 +25,7 @@
 #include <atomic>
 #include <type_traits>
 
+#include "chain.hpp"
 #include "common.hpp"
 #include "launch.hpp"
 #include "pipeline.hpp"
@@ -53,7 +54,7 @@ void gemm_fp4_big_kernel(const uint8_t* __restrict__ act_codes, const uint8_t* _
                          const float* __restrict__ lora_act, const uint8_t* __restrict__ w_codes,
                          const uint8_t* __restrict__ w_scales, const uint16_t* __restrict__ lora_up,
                          const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y,
-                         int M, int N, int K, int r) {
+                         int M, int N, int K, int r, ChainEpilogue ce) {
   using namespace fp4big;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
@@ -279,12 +280,15 @@ void gemm_fp4_big_kernel(const uint8_t* __restrict__ act_codes, const uint8_t* _
   }
 
   // ---- epilogue: bias and activation, then the tile goes through LDS (the ring
-  // is free now) so that Y is written as whole rows with 16-byte stores.
+  // is free now) so that Y is written as whole rows with 16-byte stores; in the
+  // fused MLP chain (EPI 3: GELU, then the down-projection's quantizer) the
+  // staged tile is quantized and multiplied by lora_down2 there instead.
   constexpr int TP = BN + 8;   // padded row (halves) of the staging tile
-  static_assert(BM * TP * 2 <= LDS, "staging tile must fit in the ring");
+  static_assert(BM * TP * 2 + BN * 4 <= LDS, "staging tile (and the chain's smooth_inv) must fit in the ring");
   waitvm<0>();   // no DMA outstanding
   __syncthreads();
   uint16_t* tile = reinterpret_cast<uint16_t*>(smem);
+  float* si_lds = reinterpret_cast<float*>(smem + BM * TP * 2);
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
     const int nl = brow[cb];
@@ -294,36 +298,58 @@ void gemm_fp4_big_kernel(const uint8_t* __restrict__ act_codes, const uint8_t* _
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         float yv = acc[rb][cb][v] + bn;
-        if (EPI == 1) yv = gelu_tanh_f32(yv);
+        if (EPI == 1 || EPI == 3) yv = gelu_tanh_f32(yv);
         tile[(wm * 128 + rb * 32 + (v >> 2) * 8 + lh * 4 + (v & 3)) * TP + nl] = Io<IO>::from_f(yv);
       }
   }
-  __syncthreads();
-  for (int c = tid; c < BM * (BN / 8); c += 256) {
-    const int row = c / (BN / 8), c8 = c - row * (BN / 8);
-    if (m0 + row < M)
-      *reinterpret_cast<uint4*>(Y + (size_t)(m0 + row) * N + n0 + c8 * 8) =
-          *reinterpret_cast<const uint4*>(tile + row * TP + c8 * 8);
+  if constexpr (EPI == 3) {
+    if (tid < BN / 4)
+      *reinterpret_cast<float4*>(si_lds + 4 * tid) = *reinterpret_cast<const float4*>(ce.smooth_inv + n0 + 4 * tid);
   }
+  __syncthreads();
+  if constexpr (EPI != 3) {
+    for (int c = tid; c < BM * (BN / 8); c += 256) {
+      const int row = c / (BN / 8), c8 = c - row * (BN / 8);
+      if (m0 + row < M)
+        *reinterpret_cast<uint4*>(Y + (size_t)(m0 + row) * N + n0 + c8 * 8) =
+            *reinterpret_cast<const uint4*>(tile + row * TP + c8 * 8);
+    }
+  } else {
+    chain_quantize_tile<IO, BM, BN, TP>(tile, si_lds, m0, n0, M, N, ce, tid);
+    if (ce.r > 0)
+      chain_lowrank_partial<IO, BM, BN, TP>(tile, m0, n0, M, N, ce, ce.partial + (size_t)(n0 / BN) * M * ce.r,
+                                            wave, lane);
+  }
+}
+
+bool fp4_big_fits(int M, int N, int K) {
+  using namespace fp4big;
+  if (N % BN != 0 || K % 512 != 0) return false;                      // whole scale groups
+  return ((M + BM - 1) / BM) * (N / BN) >= 256;                       // enough tiles to fill 256 CUs
 }
 
 // Large-tile FP4 launch; returns hipErrorNotSupported (without launching) when
 // the shape does not suit it, so the caller can fall back to the 128 x 128 kernel.
 hipError_t launch_gemm_fp4_big(int io, int M, int N, int K, int r, const uint8_t* ac, const void* as,
                                const void* la, const uint8_t* wc, const void* ws, const void* lu,
-                               const void* bias, int epi, void* Y, hipStream_t st) {
+                               const void* bias, int epi, void* Y, hipStream_t st, const ChainEpilogue* chain) {
   using namespace fp4big;
-  if (N % BN != 0 || K % 512 != 0) return hipErrorNotSupported;   // whole scale groups
+  if (!fp4_big_fits(M, N, K)) return hipErrorNotSupported;
+  if (epi == 3 && !chain) return hipErrorInvalidValue;
   const int ntiles = ((M + BM - 1) / BM) * (N / BN);
-  if (ntiles < 256) return hipErrorNotSupported;   // too few tiles to fill 256 CUs
-  const int v = 2 * (io == 1) + (epi != 0);
-  auto kern = v == 3 ? gemm_fp4_big_kernel<1, 1> : v == 2 ? gemm_fp4_big_kernel<1, 0>
-            : v == 1 ? gemm_fp4_big_kernel<0, 1> : gemm_fp4_big_kernel<0, 0>;
-  static std::atomic<uint64_t> raised[4] = {};
+  const int e3 = epi == 3 ? 2 : epi != 0 ? 1 : 0;
+  const int v = 3 * (io == 1) + e3;
+  using K_t = void (*)(const uint8_t*, const uint8_t*, const float*, const uint8_t*, const uint8_t*,
+                       const uint16_t*, const uint16_t*, uint16_t*, int, int, int, int, ChainEpilogue);
+  static const K_t kerns[6] = {gemm_fp4_big_kernel<0, 0>, gemm_fp4_big_kernel<0, 1>, gemm_fp4_big_kernel<0, 3>,
+                               gemm_fp4_big_kernel<1, 0>, gemm_fp4_big_kernel<1, 1>, gemm_fp4_big_kernel<1, 3>};
+  const K_t kern = kerns[v];
+  static std::atomic<uint64_t> raised[6] = {};
   const hipError_t e = raise_lds_limit(raised[v], reinterpret_cast<const void*>(kern), LDS);
   if (e != hipSuccess) return e;
+  const ChainEpilogue ce = chain ? *chain : ChainEpilogue{nullptr, nullptr, 0, nullptr, nullptr, nullptr};
   hipLaunchKernelGGL(kern, dim3(ntiles), dim3(256), LDS, st, ac, (const uint8_t*)as, (const float*)la, wc,
-                     (const uint8_t*)ws, (const uint16_t*)lu, (const uint16_t*)bias, (uint16_t*)Y, M, N, K, r);
+                     (const uint8_t*)ws, (const uint16_t*)lu, (const uint16_t*)bias, (uint16_t*)Y, M, N, K, r, ce);
   return hipGetLastError();
 }
 

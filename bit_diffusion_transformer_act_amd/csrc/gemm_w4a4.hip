@@ -45,6 +45,7 @@
 #include <algorithm>
 #include <atomic>
 
+#include "chain.hpp"
 #include "common.hpp"
 #include "launch.hpp"
 #include "pipeline.hpp"
@@ -565,13 +566,28 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restr
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           float yv = acc[rb][cb][v] + bn;
-          if (EPI == 1) yv = gelu_tanh_f32(yv);
+          if (EPI == 1 || EPI == 3) yv = gelu_tanh_f32(yv);
           tile[(wm * 32 * WM + rb * 32 + (v >> 2) * 8 + lh * 4 + (v & 3)) * TP + nl] = Io<IO>::from_f(yv);
         }
     }
+    if constexpr (EPI == 3) {
+      // the fused MLP chain on a 4-bit float up-projection: the down-projection's
+      // smoothing vector for the tile's columns, next to the staged tile
+      static_assert(BM * TP * 2 + BN * 4 <= S::LDS, "chain staging must fit in the ring");
+      float* si_lds = reinterpret_cast<float*>(smem + BM * TP * 2);
+      if (tid < BN / 4)
+        *reinterpret_cast<float4*>(si_lds + 4 * tid) = *reinterpret_cast<const float4*>(ce.smooth_inv + n0 + 4 * tid);
+    }
   }
   __syncthreads();
-  if constexpr (EPI != 3) {
+  if constexpr (EPI == 3 && FMT != 0) {
+    // the staged U tile through the down-projection's quantizer, and its low-rank partial
+    const float* si_lds = reinterpret_cast<const float*>(smem + BM * TP * 2);
+    chain_quantize_tile<IO, BM, BN, TP>(tile, si_lds, m0, n0, M, N, ce, tid);
+    if (ce.r > 0)
+      chain_lowrank_partial<IO, BM, BN, TP>(tile, m0, n0, M, N, ce, ce.partial + (size_t)(n0 / BN) * M * ce.r,
+                                            wave, lane);
+  } else if constexpr (EPI != 3) {
     for (int c = tid; c < BM * (BN / 8); c += 256) {
       const int row = c / (BN / 8), c8 = c - row * (BN / 8);
       if (m0 + row < M)
@@ -701,9 +717,12 @@ static hipError_t launch_gemm_io(int fmt, int M, int N, int K, int r, const uint
     if (small) SVDQ_GO(0, 2, 1, 2, 3);
     SVDQ_GO(0, 2, 2, 2, 3);
   }
-  if (epi == 3) {   // fused MLP chain: INT4 only
-    if (fmt != 0 || !chain) return hipErrorInvalidValue;
-    SVDQ_GO(0, 3, 2, 2, 3);
+  if (epi == 3) {   // fused MLP chain
+    if (!chain) return hipErrorInvalidValue;
+    if (fmt == 0) SVDQ_GO(0, 3, 2, 2, 3);
+    const hipError_t e = launch_gemm_fp4_big(IO, M, N, K, r, ac, as, la, wc, ws, lu, bias, 3, Y, st, chain);
+    if (e != hipErrorNotSupported) return e;
+    SVDQ_GO(1, 3, 2, 2, 4);
   }
   if (fmt == 0) {
     if (small == 2) {
@@ -720,6 +739,8 @@ static hipError_t launch_gemm_io(int fmt, int M, int N, int K, int r, const uint
   }
 #undef SVDQ_GO
 }
+
+int chain_tile_n(int fmt, int M, int N, int K) { return (fmt != 0 && fp4_big_fits(M, N, K)) ? 256 : 128; }
 
 hipError_t launch_gemm_w4a4(int fmt, int io, int M, int N, int K, int r, const uint8_t* ac, const void* as,
                             const void* la, const uint8_t* wc, const void* ws, const void* lu,

@@ -40,11 +40,12 @@ struct QkvEpilogue {
   int heads;
 };
 
-// Parameters of the fused MLP chain (epi == 3, INT4 only): GELU, then the
-// down-projection's quantizer on the 16-bit result U: smoothing by
-// smooth_inv [N], INT4 g64 codes [M][N/2] and fp16 scales [M][N/64], and the
-// per-tile fp32 partials of U lora_down^T ([N/128][M][r], summed by
-// launch_chain_reduce into the fp32 lora_act).
+// Parameters of the fused MLP chain (epi == 3, INT4 or FP4 up-projection):
+// GELU, then the down-projection's INT4 quantizer on the 16-bit result U:
+// smoothing by smooth_inv [N], INT4 g64 codes [M][N/2] and fp16 scales
+// [M][N/64], and the per-tile fp32 partials of U lora_down^T ([N/BN][M][r]
+// with BN = chain_tile_n(...), summed by launch_chain_reduce into the fp32
+// lora_act).
 struct ChainEpilogue {
   const float* smooth_inv;
   const void* lora_down;
@@ -63,10 +64,17 @@ hipError_t launch_gemm_w4a4(int fmt, int io, int M, int N, int K, int r, const u
                             void* Y, hipStream_t stream, const QkvEpilogue* qkv = nullptr,
                             const ChainEpilogue* chain = nullptr);
 
+// whether the 256 x 256 FP4 kernel takes the shape (else the 128 x 128 one does)
+bool fp4_big_fits(int M, int N, int K);
+
 hipError_t launch_gemm_fp4_big(int io, int M, int N, int K, int r, const uint8_t* act_codes,
                                const void* act_scales, const void* lora_act, const uint8_t* w_codes,
                                const void* w_scales, const void* lora_up, const void* bias, int epi,
-                               void* Y, hipStream_t stream);
+                               void* Y, hipStream_t stream, const ChainEpilogue* chain = nullptr);
+
+// columns per slice of the fused chain's low-rank partials: the up-projection
+// GEMM's tile width for this format and shape
+int chain_tile_n(int fmt, int M, int N, int K);
 
 // NVFP4 GEMM: Y = act(alpha * sum (q_x s_x)(q_w s_w) + lora_act lora_up^T + bias)
 hipError_t launch_gemm_nvfp4(int io, int M, int N, int K, int r, const uint8_t* act_codes,

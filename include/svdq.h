@@ -223,12 +223,14 @@ int svdq_gemm_w4a4_qkv(int fmt, int dtype, int M, int N, int K, int r,
  *
  * The codes and scales equal the unfused path's bit for bit (the same U, the
  * same quantizer rule); lora_act2 is summed over the up-projection's tiles of
- * 128 columns in fp32, in a fixed order (deterministic), and stored in fp32.
- * Two kernels: the GEMM with the quantizer in its epilogue, and the sum of the
- * per-tile partials of the low-rank down-projection, kept in `workspace`.
+ * columns (128, or 256 for the large FP4 tile) in fp32, in a fixed order
+ * (deterministic), and stored in fp32. Two kernels: the GEMM with the
+ * quantizer in its epilogue, and the sum of the per-tile partials of the
+ * low-rank down-projection, kept in `workspace`.
  *
- * Arguments as svdq_gemm_w4a4 for the up-projection (fmt must be
- * SVDQ_INT4_G64; GELU is implied; there is no Y), and
+ * Arguments as svdq_gemm_w4a4 for the up-projection (fmt: SVDQ_INT4_G64 or
+ * SVDQ_FP4_E2M1_B32, the up-projection's own format; the down-projection's
+ * codes are INT4 g64 either way; GELU is implied; there is no Y), and
  *   smooth_inv2      fp32 [N], the down-projection's smoothing multiplier.
  *   lora_down2       h16 [r2][N], its low-rank down factor; NULL iff r2 == 0.
  *   r2               its low-rank width; r2 % 16 == 0, 0 <= r2 <= 128.

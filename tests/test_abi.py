@@ -166,7 +166,8 @@ def gm(M=4, N=128, K=128, r=16, r2=16, ac=A, sa=A, la=A, wc=A, ws=A, lu=A, b=Non
 
 def test_mlp_chain_argument_errors():
     assert P.lib().svdq_gemm_w4a4_mlp_workspace(4096, 12288, 32) == 96 * 4096 * 32 * 4
-    assert gm(fmt=1) == ops.SVDQ_ERR_INVALID_ARG          # INT4 only
+    assert gm(fmt=2) == ops.SVDQ_ERR_INVALID_ARG          # INT4 or FP4 up-projections only
+    assert gm(fmt=1, sa=A) == ops.SVDQ_ERR_UNSUPPORTED_DEVICE
     assert gm(dt=3) == ops.SVDQ_ERR_INVALID_ARG
     assert gm(N=192) == ops.SVDQ_ERR_SHAPE
     assert gm(r2=24) == ops.SVDQ_ERR_SHAPE
@@ -188,7 +189,7 @@ def gz(M=4, N=128, K=128, r=16, r2=16, ac=A, sa=A, la=A, wc=A, ws=A, lu=A, b=Non
 def test_mlp_chain_noalloc_argument_errors():
     """The allocation-free chain: the chain's checks, no workspace, and the
     64 MiB limit of the library's device scratch (partials M (N/128) r2 fp32)."""
-    assert gz(fmt=1) == ops.SVDQ_ERR_INVALID_ARG
+    assert gz(fmt=2) == ops.SVDQ_ERR_INVALID_ARG
     assert gz(N=192) == ops.SVDQ_ERR_SHAPE
     assert gz(c2=U) == ops.SVDQ_ERR_ALIGN
     assert gz(la2=None) == ops.SVDQ_ERR_INVALID_ARG

@@ -45,10 +45,11 @@ def host(t):
     return t.float().cpu().numpy() if t.dtype == torch.bfloat16 else t.cpu().numpy()
 
 
-def chain_inputs(M, K, N, r, r2, seed=0):
-    """Up-projection in storage format (INT4), and the down-projection's
-    smoothing vector and low-rank down factor (fp16)."""
-    cfg = synth.LayerConfig(f"chain_{M}_{K}_{N}", 70, M, K, N, r, "int4_g64", "gelu_tanh", "normal", 0.005, 30.0)
+def chain_inputs(M, K, N, r, r2, seed=0, fmt="int4_g64"):
+    """Up-projection in storage format (INT4, or FP4 E2M1 with E8M0 block-32
+    scales), and the down-projection's smoothing vector and low-rank down
+    factor (fp16)."""
+    cfg = synth.LayerConfig(f"chain_{M}_{K}_{N}", 70, M, K, N, r, fmt, "gelu_tanh", "normal", 0.005, 30.0)
     up = synth.random_quantized_layer(cfg, seed=seed)
     g = synth.rng_for(seed, 71, 7)
     si2 = np.exp(g.normal(0.0, 0.3, N)).astype(np.float32)
@@ -56,17 +57,33 @@ def chain_inputs(M, K, N, r, r2, seed=0):
     return up, si2, ld2
 
 
-def run_unfused(P, codes, scales, la, up, si2, ld2, h):
+def run_unfused(P, codes, scales, la, up, si2, ld2, h, fmt="int4_g64"):
     y = P.svdq_gemm_w4a4(codes, scales, la, dev(up["w_codes"]), dev(up["w_scales"]),
-                         dev(up["lora_up"], h) if la is not None else None, dev(up["bias"], h), "int4_g64",
+                         dev(up["lora_up"], h) if la is not None else None, dev(up["bias"], h), fmt,
                          "gelu_tanh", dtype=h)
     return P.svdq_quantize_act(y, dev(si2), dev(ld2, h) if ld2.shape[0] else None, "int4_g64")
 
 
-def run_fused(P, codes, scales, la, up, si2, ld2, h):
+def run_fused(P, codes, scales, la, up, si2, ld2, h, fmt="int4_g64"):
     return P.svdq_gemm_w4a4_mlp(codes, scales, la, dev(up["w_codes"]), dev(up["w_scales"]),
                                 dev(up["lora_up"], h) if la is not None else None, dev(up["bias"], h), dev(si2),
-                                dev(ld2, h) if ld2.shape[0] else None, dtype=h)
+                                dev(ld2, h) if ld2.shape[0] else None, fmt=fmt, dtype=h)
+
+
+def _equals_unfused(P, M, K, N, r, r2, h, fmt, seed=0):
+    up, si2, ld2 = chain_inputs(M, K, N, r, r2, seed=seed, fmt=fmt)
+    X = dev(up["X"], h)
+    codes, scales, la = P.svdq_quantize_act(X, dev(up["smooth_inv"]), dev(up["lora_down"][:r], h) if r else None,
+                                            fmt)
+    c1, s1, l1 = run_unfused(P, codes, scales, la, up, si2, ld2, h, fmt)
+    c2, s2, l2 = run_fused(P, codes, scales, la, up, si2, ld2, h, fmt)
+    assert np.array_equal(host(c2), host(c1))
+    assert np.array_equal(host(s2).view(np.uint16), host(s1).view(np.uint16))
+    if r2:
+        assert l2.dtype == torch.float32
+        assert_close(host(l2), host(l1), LORA_TOL)
+    else:
+        assert l2 is None
 
 
 @pytest.mark.parametrize("M,K,N,r,r2,h", [(200, 512, 1024, 16, 16, torch.float16),
@@ -77,19 +94,21 @@ def run_fused(P, codes, scales, la, up, si2, ld2, h):
                                           (200, 512, 1024, 16, 48, torch.bfloat16),   # ranks past the prefetched 32
                                           (130, 128, 65536, 16, 128, torch.float16)])  # the largest N and rank
 def test_chain_equals_unfused(P, M, K, N, r, r2, h):
-    up, si2, ld2 = chain_inputs(M, K, N, r, r2)
-    X = dev(up["X"], h)
-    codes, scales, la = P.svdq_quantize_act(X, dev(up["smooth_inv"]), dev(up["lora_down"][:r], h) if r else None,
-                                            "int4_g64")
-    c1, s1, l1 = run_unfused(P, codes, scales, la, up, si2, ld2, h)
-    c2, s2, l2 = run_fused(P, codes, scales, la, up, si2, ld2, h)
-    assert np.array_equal(host(c2), host(c1))
-    assert np.array_equal(host(s2).view(np.uint16), host(s1).view(np.uint16))
-    if r2:
-        assert l2.dtype == torch.float32
-        assert_close(host(l2), host(l1), LORA_TOL)
-    else:
-        assert l2 is None
+    _equals_unfused(P, M, K, N, r, r2, h, "int4_g64")
+
+
+@pytest.mark.parametrize("M,K,N,r,r2,h", [
+    (4096, 3072, 12288, 32, 32, torch.float16),   # the DiT MLP: the 256 x 256 FP4 kernel
+    (2000, 1024, 8192, 16, 128, torch.float16),   # 256 x 256 tiles, ragged M, the largest rank
+    (2048, 512, 8192, 0, 0, torch.bfloat16),      # 256 x 256 tiles without low-rank branches
+    (200, 512, 1024, 16, 16, torch.float16),      # too few tiles: the 128 x 128 FP4 path
+    (130, 384, 768, 32, 48, torch.bfloat16),      # 128 x 128, ragged M, K not a multiple of 512
+])
+def test_fp4_chain_equals_unfused(P, M, K, N, r, r2, h):
+    """The chain on an FP4 E2M1 up-projection (its GELU output quantized to the
+    down-projection's INT4 in the epilogue of either FP4 kernel) equals the
+    unfused FP4 GEMM followed by the quantizer."""
+    _equals_unfused(P, M, K, N, r, r2, h, "fp4_b32", seed=7)
 
 
 def test_chain_is_deterministic(P):
@@ -152,20 +171,21 @@ def test_mlp_against_oracle_chain(P):
     assert_close(host(y), y_ref, what="down-projection")
 
 
-def test_chain_full_size_against_oracle(P):
-    """The DiT MLP up-projection (M 4096, K 3072, N 12288, rank 32) through the
-    fused chain, against the oracle chain on one row from every band of 64 (all
-    12288 columns): codes and scales as _check_chain_codes states, lora_act2
-    against the oracle's."""
+@pytest.mark.parametrize("fmt", ["int4_g64", "fp4_b32"])
+def test_chain_full_size_against_oracle(P, fmt):
+    """The DiT MLP up-projection (M 4096, K 3072, N 12288, rank 32; INT4, or
+    FP4 E2M1 as in the MLP-up workload) through the fused chain, against the
+    oracle chain on one row from every band of 64 (all 12288 columns): codes
+    and scales as _check_chain_codes states, lora_act2 against the oracle's."""
     M, K, N, r, r2 = 4096, 3072, 12288, 32, 32
-    up, si2, ld2 = chain_inputs(M, K, N, r, r2, seed=5)
-    cu, packed, scales = oracle.quantize_act_ref(up["X"], up["smooth_inv"], "int4_g64")
+    up, si2, ld2 = chain_inputs(M, K, N, r, r2, seed=5, fmt=fmt)
+    cu, packed, scales = oracle.quantize_act_ref(up["X"], up["smooth_inv"], fmt)
     la = oracle.lora_act_ref(up["X"], up["lora_down"][:r]).astype(np.float32)
     c2, s2, l2 = P.svdq_gemm_w4a4_mlp(dev(packed), dev(scales), dev(la), dev(up["w_codes"]), dev(up["w_scales"]),
-                                      dev(up["lora_up"][:, :r]), dev(up["bias"]), dev(si2), dev(ld2))
+                                      dev(up["lora_up"][:, :r]), dev(up["bias"]), dev(si2), dev(ld2), fmt=fmt)
     rows = band_rows(M, seed=14)
-    wu = oracle.unpack_nibbles(up["w_codes"], signed=True)
+    wu = oracle.unpack_nibbles(up["w_codes"], signed=(fmt == "int4_g64"))
     U16, c2u_ref, c2p_ref, s2_ref, la2_ref = oracle.mlp_chain_ref(
-        cu, scales, la, wu, up["w_scales"], up["lora_up"][:, :r], up["bias"], "int4_g64", si2, ld2, rows=rows)
+        cu, scales, la, wu, up["w_scales"], up["lora_up"][:, :r], up["bias"], fmt, si2, ld2, rows=rows)
     _check_chain_codes(host(c2)[rows], host(s2)[rows], c2p_ref, s2_ref, U16, si2)
     assert_close(host(l2)[rows], la2_ref, LORA_TOL, what="lora_act2")

@@ -300,6 +300,29 @@ def test_gemm_int4_extreme_codes(P):
         assert_close(host(Y), y_ref, what="extreme codes")
 
 
+@pytest.mark.parametrize("M,K,N", [(256, 1024, 512), (2048, 512, 8192)])
+def test_gemm_fp4_extreme_scales(P, M, K, N):
+    """FP4 E8M0 scale bytes far from 127 on both operands (2^-63 .. 2^63 per
+    block), the pairs' exponents summing to about -16 so the outputs stay in
+    fp16 range: the hardware's scaling against the oracle's exact dequantized
+    product. Random E2M1 codes (all 16 nibbles); the 128 x 128 FP4 path and the
+    256 x 256 kernel."""
+    rng = np.random.default_rng(31)
+    nb = K // 32
+    ea = rng.integers(64, 191, nb)                      # per block, shared by the rows
+    eb = 254 - 16 - ea                                  # per block, shared by the columns
+    sa = (ea[None, :] + rng.integers(-2, 3, (M, nb))).astype(np.uint8)
+    sw = (eb[None, :] + rng.integers(-2, 3, (N, nb))).astype(np.uint8)
+    a = rng.integers(0, 16, (M, K)).astype(np.uint8)
+    w = rng.integers(0, 16, (N, K)).astype(np.uint8)
+    Y = P.svdq_gemm_w4a4(dev(oracle.pack_nibbles(a)), dev(sa), None, dev(oracle.pack_nibbles(w)), dev(sw), None,
+                         None, "fp4_b32", "none")
+    y = host(Y)
+    rows = np.arange(M) if M <= 256 else band_rows(M, seed=15)
+    y_ref = oracle.gemm_ref(a, sa, np.zeros((M, 0)), w, sw, np.zeros((N, 0)), None, "fp4_b32", rows=rows)
+    assert_close(y[rows], y_ref, what="FP4 extreme scales")
+
+
 # ------------------------------------------------ fused QKV epilogue --
 
 def _qkv_case(P, cfg, seed, rows=None):
