@@ -23,21 +23,21 @@
 
 namespace svdq {
 
-// INT4 codes of 8 values against scale sf (nonzero), rs = rcp(sf); sets
-// near_tie when a value may round differently from the IEEE quotient. The
-// product v * rs is rounded to an integer (ties to even) inside
-// fma(v, rs, 1.5 * 2^23) and clamped to +-7 by a med3 in that domain; it is
-// within 2^-19 |y| of fl32(v / sf) (rcp is within an ulp), so the two round to
-// the same integer unless y lies within 2^-16 of a half-integer, which
-// fma(v, rs, -q) detects (one rounding). Such a group is recomputed with the
-// IEEE division by the caller. Nibbles: even k low.
-__device__ __forceinline__ uint32_t chain_int4_codes8(const float* v, float rs, bool& near_tie) {
+// INT4 codes of 8 values against scale sf (nonzero), rs = rcp(sf); raises
+// tmax to the largest |v * rs - q|. The product v * rs is rounded to an integer
+// (ties to even) inside fma(v, rs, 1.5 * 2^23) and clamped to +-7 by a med3 in
+// that domain; it is within 2^-19 |y| of fl32(v / sf) (rcp is within an ulp),
+// so the two round to the same integer unless y lies within 2^-16 of a
+// half-integer, which fma(v, rs, -q) shows (one rounding): a group with
+// tmax > 0.5 - 2^-16 is recomputed with the IEEE division by the caller.
+// Nibbles: even k low.
+__device__ __forceinline__ uint32_t chain_int4_codes8(const float* v, float rs, float& tmax) {
   constexpr float kM = 12582912.0f;   // 1.5 * 2^23
   uint32_t w = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const float y = __builtin_amdgcn_fmed3f(fmaf(v[i], rs, kM), kM - 7.0f, kM + 7.0f);
-    near_tie |= fabsf(fmaf(v[i], rs, -(y - kM))) > 0.4999847412109375f;   // 0.5 - 2^-16
+    tmax = __builtin_fmaxf(tmax, fabsf(fmaf(v[i], rs, -(y - kM))));
     w |= (__float_as_uint(y) & 0xFu) << (4 * i);
   }
   return w;
@@ -83,15 +83,15 @@ __device__ __forceinline__ void chain_quantize_tile(const uint16_t* tile, const 
         amax = fmaxf(amax, fabsf(x[8 * c + i]));
       }
     }
-    const __half s16 = __float2half_rn(fminf(amax / 7.0f, 65504.0f));   // IEEE division
+    const __half s16 = __float2half_rn(fminf(div7_rn(amax), 65504.0f));   // fl32(amax / 7), as IEEE division
     const float sf = __half2float(s16);
     uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     if (sf != 0.0f) {
       const float rs = __builtin_amdgcn_rcpf(sf);
-      bool near_tie = false;
+      float tmax = 0.0f;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) w[c] = chain_int4_codes8(x + 8 * c, rs, near_tie);
-      if (near_tie) {
+      for (int c = 0; c < 8; ++c) w[c] = chain_int4_codes8(x + 8 * c, rs, tmax);
+      if (tmax > 0.4999847412109375f) {   // 0.5 - 2^-16
 #pragma unroll
         for (int c = 0; c < 8; ++c) w[c] = chain_int4_codes8_exact(x + 8 * c, sf);
       }

@@ -106,9 +106,12 @@ __device__ __forceinline__ float lane_sum_xor(float v, int mask) {
 // with the lower 32 of its second (so with two copies of v each lane ends up
 // holding v[l] and v[l ^ 32]); v_permlane16_swap does the same between the odd
 // and even 16-lane rows (v[l] and v[l ^ 16]). All 64 lanes must be active.
+// For NON-NEGATIVE values only (the group maxima of |x|): their bit patterns
+// order as unsigned integers the way the values do, so an integer max takes
+// the place of a float max (which would canonicalize both swapped operands).
 __device__ __forceinline__ float lane_max_xor32(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return __uint_as_float(max((uint32_t)r[0], (uint32_t)r[1]));
 }
 // Sum over each 16-lane row with DPP (mirror, half-mirror, then the two quad
 // exchanges); every lane of the row gets the same total.
@@ -120,18 +123,32 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
-// max over the 16 lanes of a DPP row (same exchange pattern as row16_sum)
+// max over the 16 lanes of a DPP row (same exchange pattern as row16_sum), for
+// NON-NEGATIVE values (compared as unsigned bit patterns, as in lane_max_xor32)
 __device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
-  return v;
+  uint32_t u = __float_as_uint(v);
+  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x140, 0xF, 0xF, false));   // row_mirror
+  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x141, 0xF, 0xF, false));   // row_half_mirror
+  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0xB1, 0xF, 0xF, false));    // quad_perm 1,0,3,2
+  u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x4E, 0xF, 0xF, false));    // quad_perm 2,3,0,1
+  return __uint_as_float(u);
 }
 
-__device__ __forceinline__ float lane_max_xor16(float v) {
+__device__ __forceinline__ float lane_max_xor16(float v) {   // non-negative values, as above
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return __uint_as_float(max((uint32_t)r[0], (uint32_t)r[1]));
+}
+
+// fl32(a / 7), correctly rounded, in three instructions: q = RN(a z) with
+// z = RN(1/7), the residual r = a - 7 q (exact in one fma), then RN(q + r z).
+// Equal to the IEEE quotient for every fp32 a: checked exhaustively over the
+// significands of the subnormals and of the lowest 40 and highest 55 binades
+// (the sequence scales exactly by powers of two in between).
+__device__ __forceinline__ float div7_rn(float a) {
+#pragma clang fp contract(off)
+  const float z = 0.142857149243354797363281250f;   // RN(1/7) = 0x3E124925
+  const float q = a * z;
+  return fmaf(fmaf(-7.0f, q, a), z, q);
 }
 
 // GELU, tanh form, in fp32: y/2 * (1 + tanh(u)), u = sqrt(2/pi) (y + 0.044715 y^3).

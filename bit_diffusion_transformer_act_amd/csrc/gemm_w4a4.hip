@@ -527,7 +527,7 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restr
             amax = fmaxf(amax, fabsf(x[cb]));
           }
           amax = row16_max(amax);
-          const __half s16 = __float2half_rn(fminf(amax / 7.0f, 65504.0f));   // IEEE division
+          const __half s16 = __float2half_rn(fminf(div7_rn(amax), 65504.0f));   // fl32(amax / 7)
           const float sf = __half2float(s16);
           // q = clamp(rint(fl32(x / s)), -7, 7): x * rcp(s) rounded inside
           // fma(x, rcp(s), 1.5 * 2^23) gives the same integer unless the product
@@ -536,13 +536,14 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restr
           constexpr float kM = 12582912.0f;   // 1.5 * 2^23
           const float rs = sf != 0.0f ? __builtin_amdgcn_rcpf(sf) : 0.0f;
           int qn[CB4];
-          bool near_tie = false;
+          float tmax = 0.0f;
 #pragma unroll
           for (int cb = 0; cb < CB4; ++cb) {
             const float y = __builtin_amdgcn_fmed3f(fmaf(x[cb], rs, kM), kM - 7.0f, kM + 7.0f);
-            near_tie |= fabsf(fmaf(x[cb], rs, -(y - kM))) > 0.4999847412109375f;
+            tmax = __builtin_fmaxf(tmax, fabsf(fmaf(x[cb], rs, -(y - kM))));
             qn[cb] = (int)(__float_as_uint(y) & 0xFu);
           }
+          const bool near_tie = tmax > 0.4999847412109375f;   // 0.5 - 2^-16
           if (near_tie && sf != 0.0f) {
 #pragma unroll
             for (int cb = 0; cb < CB4; ++cb)

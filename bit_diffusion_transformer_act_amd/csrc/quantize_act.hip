@@ -232,23 +232,28 @@ void quantize_act_kernel(const uint16_t* __restrict__ X, const float* __restrict
     }
   };
 
-  // INT4 codes of 8 values against scale sf (nonzero), rs = rcp(sf); sets
-  // near_tie when a value may round differently from the IEEE quotient.
+  // INT4 codes of 8 values against scale sf (nonzero), rs = rcp(sf); raises
+  // tmax to the largest |v * rs - q|, which tells whether a value may round
+  // differently from the IEEE quotient (tmax > 0.5 - 2^-16, tested once per
+  // group: cheaper than a flag per value).
   // y = v * rs is formed exactly inside fma(v, rs, 1.5 * 2^23), which rounds it
   // to an integer (ties to even) in the low mantissa bits; the clamp to +-7 is
   // a med3 in that domain, and fma(v, rs, -q) is y - q with one rounding. The
   // low byte of the clamped value is q as a two's-complement int8, and byte
   // permutes gather the eight low nibbles (even k in the low nibble).
-  auto int4_codes = [&](const float* v, float rs, bool& near_tie) {
+  auto int4_codes = [&](const float* v, float rs, float& tmax) {
     constexpr float kM = 12582912.0f;   // 1.5 * 2^23
     uint32_t b[8];
+    float t[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float yv = __builtin_amdgcn_fmed3f(fmaf(v[i], rs, kM), kM - 7.0f, kM + 7.0f);
-      const float t = fmaf(v[i], rs, -(yv - kM));
-      near_tie |= fabsf(t) > 0.4999847412109375f;   // 0.5 - 2^-16
+      t[i] = fmaf(v[i], rs, -(yv - kM));
       b[i] = __float_as_uint(yv);
     }
+#pragma unroll
+    for (int i = 0; i < 8; i += 2)
+      tmax = __builtin_fmaxf(tmax, __builtin_fmaxf(fabsf(t[i]), fabsf(t[i + 1])));
     const uint32_t e = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[6], b[4], 0x0c0c0400u),
                                              __builtin_amdgcn_perm(b[2], b[0], 0x0c0c0400u), 0x05040100u);
     const uint32_t o = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[7], b[5], 0x0c0c0400u),
@@ -332,7 +337,7 @@ void quantize_act_kernel(const uint16_t* __restrict__ X, const float* __restrict
       for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(xh[i]));
       amax = lane_max_xor16(amax);
       amax = lane_max_xor32(amax);
-      const float s32 = amax / 7.0f;                    // IEEE division
+      const float s32 = div7_rn(amax);                  // = fl32(amax / 7)
       const __half s16 = __float2half_rn(fminf(s32, 65504.0f));
       const float sf = __half2float(s16);
       uint32_t w0 = 0, w1 = 0;
@@ -345,10 +350,10 @@ void quantize_act_kernel(const uint16_t* __restrict__ X, const float* __restrict
         // and a value beyond +-7.5 (possible only with a saturated scale) is
         // flagged and recomputed.
         const float rs = __builtin_amdgcn_rcpf(sf);
-        bool near_tie = false;
-        w0 = int4_codes(xh, rs, near_tie);
-        w1 = int4_codes(xh + 8, rs, near_tie);
-        if (near_tie) {
+        float tmax = 0.0f;
+        w0 = int4_codes(xh, rs, tmax);
+        w1 = int4_codes(xh + 8, rs, tmax);
+        if (tmax > 0.4999847412109375f) {   // 0.5 - 2^-16
           w0 = int4_codes_exact(xh, sf);
           w1 = int4_codes_exact(xh + 8, sf);
         }
