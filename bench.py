@@ -19,8 +19,9 @@ sum(2 M N K) / step time in TOPS (the quantizers' and the GEMV's time is
 inside the step). Per-launch durations come from HIP events recorded on the
 launch stream around every launch in the timed region (median, p10, p90 over
 the steps). The low-rank overhead t(rank r) / t(rank 0) - 1 is measured by a
-second timed pass with the low-rank branch off. GPU clocks are sampled with
-amdsmi on a host thread during the timed region.
+second timed pass with the low-rank branch off. The shader clock is measured
+on the GPU just before and just after the timed steps (cycles against the
+real-time counter), and amdsmi's reported clock is sampled during them.
 
 Options: --gpus N (only 1: one GPU), --steps K (default 100), --warmup W
 (default 20), --workload NAME, --no-cpu-baseline, --no-lowrank-overhead,
@@ -142,10 +143,10 @@ def gemm_name(cfg):
 
 
 class ClockSampler:
-    """The GPU's graphics clock, sampled on a host thread every `period`
-    seconds between start() and stop(): amdsmi's GPU metrics (the current
-    clock of each XCD, averaged over the XCDs, and the firmware's own running
-    average), falling back to amdsmi_get_clock_info."""
+    """The graphics clock that amdsmi reports (amdsmi_get_clock_info), sampled
+    on a host thread every `period` seconds between start() and stop(). The
+    driver refreshes this reading slowly, so it is kept as a secondary record
+    next to the clock measured on the GPU (svdq_clock_probe)."""
 
     def __init__(self, pci_bus=None, period=0.005):
         self.period, self.samples, self.err, self.h, self.max_gfx = period, [], None, None, None
@@ -166,28 +167,11 @@ class ClockSampler:
         self._stop = threading.Event()
         self._t = None
 
-    @staticmethod
-    def _num(v):
-        return float(v) if isinstance(v, (int, float)) and 0 < v < 100000 else None
-
-    def _sample(self):
-        a = self.amdsmi
-        try:
-            m = a.amdsmi_get_gpu_metrics_info(self.h)
-            xcd = [self._num(v) for v in (m.get("current_gfxclks") or [])]
-            xcd = [v for v in xcd if v is not None]
-            cur = sum(xcd) / len(xcd) if xcd else self._num(m.get("current_gfxclk"))
-            avg = self._num(m.get("average_gfxclk_frequency"))
-            if cur is not None:
-                return cur, avg
-        except Exception:
-            pass
-        return float(a.amdsmi_get_clock_info(self.h, a.AmdSmiClkType.GFX)["clk"]), None
-
     def _run(self):
+        a = self.amdsmi
         while not self._stop.is_set():
             try:
-                self.samples.append(self._sample())
+                self.samples.append(float(a.amdsmi_get_clock_info(self.h, a.AmdSmiClkType.GFX)["clk"]))
             except Exception as e:
                 self.err = f"{type(e).__name__}: {e}"
                 return
@@ -205,17 +189,18 @@ class ClockSampler:
 
     def summary(self):
         if not self.samples:
-            return {"source": "amdsmi", "error": self.err or "no samples"}
+            return {"amdsmi_error": self.err or "no samples"}
         import numpy as np
-        g = np.array([s[0] for s in self.samples], float)
-        avg = [s[1] for s in self.samples if s[1] is not None]
-        out = {"source": f"amdsmi GPU metrics (current graphics clock, mean over the XCDs), every "
-                         f"{self.period * 1e3:.0f} ms over the timed steps",
-               "samples": len(g), "gfx_mhz_median": float(np.median(g)), "gfx_mhz_min": float(g.min()),
-               "gfx_mhz_max": float(g.max()), "gfx_mhz_limit": self.max_gfx}
-        if avg:
-            out["gfx_mhz_firmware_average"] = float(np.median(avg))
-        return out
+        g = np.array(self.samples, float)
+        return {"amdsmi_gfx_mhz_median": float(np.median(g)), "amdsmi_samples": len(g),
+                "gfx_mhz_limit": self.max_gfx}
+
+
+def probe_clock(P):
+    """Median over ~one workgroup per CU of the shader clock (MHz) measured on
+    the GPU over 2 ms: shader cycles against the real-time counter."""
+    import numpy as np
+    return round(float(np.median(P.svdq_clock_probe(0, workgroups=256, ticks=200_000))), 1)
 
 
 def main(argv=None):
@@ -350,6 +335,8 @@ def main(argv=None):
         if events is not None:
             events[nk].record(stream)
 
+    clock = {}
+
     def timed(lowrank, sampler=None):
         # clocks ramp for tens of ms under load after idle: untimed steps for
         # --prewarm-ms of wall time (synchronizing every 8 steps so the host
@@ -364,6 +351,8 @@ def main(argv=None):
         for i in range(args.warmup):
             step(i, lowrank=lowrank)
         torch.cuda.synchronize()
+        if sampler is not None:
+            clock["gfx_mhz_before"] = probe_clock(P)
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(args.steps)]
         torch.cuda.synchronize()
         if sampler is not None:
@@ -374,6 +363,7 @@ def main(argv=None):
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         if sampler is not None:
+            clock["gfx_mhz_after"] = probe_clock(P)
             sampler.stop()
         # launch k spans events[k] -> events[k + 1] (ms)
         durs = np.array([[e[k].elapsed_time(e[k + 1]) for k in range(nk)] for e in evs])
@@ -477,7 +467,10 @@ def main(argv=None):
         "cpu_baseline": cpu,
         "kernels": kernels,
         "lowrank_overhead": lr_over,
-        "clocks": sampler.summary(),
+        "clocks": {"source": "shader cycles (s_memtime) over the real-time counter (s_memrealtime), "
+                             "2 ms on ~every CU just before and just after the timed steps; amdsmi's "
+                             "reported clock sampled every 5 ms during them",
+                   **clock, **sampler.summary()},
         "gemm_TOPS": round(total_ops / (gemm_ms_sum * 1e-3) / 1e12, 1),
         "gemv_GBps": kernels["gemv.awq_gemv_w4a16"]["GB/s"],
         "device": props.gcnArchName,

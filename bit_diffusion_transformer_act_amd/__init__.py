@@ -11,6 +11,7 @@ from .ops import (  # noqa: F401
     SvdqError,
     awq_gemv_w4a16,
     lib,
+    svdq_clock_probe,
     svdq_device_check,
     svdq_gemm_w4a4,
     svdq_gemm_w4a4_qkv,

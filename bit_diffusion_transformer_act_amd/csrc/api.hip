@@ -154,6 +154,26 @@ int mlp_chain(int fmt, int dtype, int M, int N, int K, int r, const uint8_t* act
 
 }  // namespace
 
+
+// Shader-clock probe. Each one-wave workgroup reads the constant-rate
+// real-time counter (s_memrealtime) and the shader-clock cycle counter
+// (s_memtime), polls the real-time counter until `ticks` of it have passed
+// (at most 2^24 polls, so the loop always ends), then reads both again; lane 0
+// stores (cycles, real-time ticks). The cycle interval lies inside the
+// real-time one.
+__global__ __launch_bounds__(64) void clock_probe_kernel(unsigned long long* out, unsigned long long ticks) {
+  const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
+  const unsigned long long c0 = __builtin_amdgcn_s_memtime();
+  unsigned long long r1 = r0;
+  for (int i = 0; i < (1 << 24) && r1 - r0 < ticks; ++i) r1 = __builtin_amdgcn_s_memrealtime();
+  const unsigned long long c1 = __builtin_amdgcn_s_memtime();
+  r1 = __builtin_amdgcn_s_memrealtime();
+  if (threadIdx.x == 0) {
+    out[2 * blockIdx.x] = c1 - c0;
+    out[2 * blockIdx.x + 1] = r1 - r0;
+  }
+}
+
 extern "C" {
 
 int svdq_version(void) { return 10000 * 0 + 100 * 2 + 0; }
@@ -320,6 +340,22 @@ int awq_gemv_w4a16(int dtype, int M, int N, int K, int group, const void* x, con
   (void)hipGetLastError();
   return finish(svdq::launch_awq_gemv(dtype, M, N, K, x, w_codes, scales, zeros, bias, y,
                                       (hipStream_t)stream));
+}
+
+int svdq_clock_probe(int workgroups, unsigned long long ticks, unsigned long long* out, int* wall_khz,
+                     void* stream) {
+  if (workgroups < 1 || workgroups > 4096 || ticks < 1 || ticks > 100000000ull) return SVDQ_ERR_SHAPE;
+  if (!out || !wall_khz) return SVDQ_ERR_INVALID_ARG;
+  if (!aligned16(out)) return SVDQ_ERR_ALIGN;
+  const int dc = check_current_device();
+  if (dc != SVDQ_OK) return dc;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(wall_khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess)
+    return SVDQ_ERR_HIP;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(clock_probe_kernel, dim3(workgroups), dim3(64), 0, (hipStream_t)stream, out, ticks);
+  return finish(hipGetLastError());
 }
 
 }  // extern "C"

@@ -39,7 +39,8 @@ SVDQ_ERR_HIP = -5
 EXPORTED_SYMBOLS = ("svdq_device_check", "svdq_status_str", "svdq_version",
                     "svdq_quantize_act", "svdq_gemm_w4a4", "svdq_gemm_w4a4_qkv",
                     "svdq_quantize_act_nvfp4", "svdq_gemm_nvfp4", "awq_gemv_w4a16",
-                    "svdq_gemm_w4a4_mlp", "svdq_gemm_w4a4_mlp_workspace", "svdq_gemm_w4a4_mlp_noalloc")
+                    "svdq_gemm_w4a4_mlp", "svdq_gemm_w4a4_mlp_workspace", "svdq_gemm_w4a4_mlp_noalloc",
+                    "svdq_clock_probe")
 
 _lock = threading.Lock()
 _handle = None
@@ -91,6 +92,8 @@ def lib() -> ctypes.CDLL:
             h.svdq_gemm_w4a4_mlp_noalloc.restype = i32
             h.awq_gemv_w4a16.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
             h.awq_gemv_w4a16.restype = i32
+            h.svdq_clock_probe.argtypes = [i32, ctypes.c_ulonglong, vp, ctypes.POINTER(i32), vp]
+            h.svdq_clock_probe.restype = i32
             _handle = h
         return _handle
 
@@ -499,3 +502,18 @@ def svdq_linear(X, layer: dict, bias=None, epilogue: str = "none"):
     codes, scales, la = svdq_quantize_act(X, layer["smooth_inv"], layer.get("lora_down"), layer["fmt"])
     return svdq_gemm_w4a4(codes, scales, la, layer["w_codes"], layer["w_scales"],
                           layer.get("lora_up"), bias, layer["fmt"], epilogue)
+
+
+def svdq_clock_probe(device=0, workgroups=256, ticks=200_000):
+    """The shader clock in MHz, one value per workgroup (numpy float64): each
+    workgroup counts shader cycles while the real-time counter advances by
+    `ticks`. Synchronizes the device's current stream."""
+    dev = torch.device("cuda", device) if isinstance(device, int) else torch.device(device)
+    with torch.cuda.device(dev):
+        out = torch.empty((workgroups, 2), dtype=torch.int64, device=dev)
+        khz = ctypes.c_int(0)
+        st = lib().svdq_clock_probe(int(workgroups), int(ticks), _ptr(out), ctypes.byref(khz), _stream(dev))
+        if st != 0:
+            raise SvdqError(st, "svdq_clock_probe")
+        cyc = out.cpu().numpy().astype("float64")
+    return cyc[:, 0] / cyc[:, 1] * khz.value / 1000.0

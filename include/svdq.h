@@ -350,6 +350,23 @@ int awq_gemv_w4a16(int dtype, int M, int N, int K, int group,
                    const void* x, const uint8_t* w_codes, const void* scales,
                    const void* zeros, const void* bias, void* y, void* stream);
 
+/*
+ * svdq_clock_probe -- measures the shader clock, for reporting next to
+ * timings (the clock a kernel ran at decides its share of the chip's peak).
+ * Each of `workgroups` one-wave workgroups counts shader cycles (s_memtime)
+ * while the constant-rate real-time counter (s_memrealtime) advances by
+ * `ticks`; the clock in MHz is cycles / ticks * wall_khz / 1000.
+ *
+ * Arguments:
+ *   workgroups  1 .. 4096 (256 puts about one on every CU).
+ *   ticks       real-time ticks to wait, 1 .. 10^8.
+ *   out         out, device u64 [workgroups][2]: (cycles, ticks) per workgroup.
+ *   wall_khz    out, HOST int: the real-time counter's rate in kHz.
+ *   stream      hipStream_t.
+ */
+int svdq_clock_probe(int workgroups, unsigned long long ticks, unsigned long long* out, int* wall_khz,
+                     void* stream);
+
 #ifdef __cplusplus
 }
 #endif

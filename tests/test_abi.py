@@ -203,6 +203,19 @@ def test_mlp_chain_noalloc_argument_errors():
     assert ops.NOALLOC_SCRATCH_BYTES == 64 << 20
 
 
+def test_clock_probe_argument_errors():
+    khz = ctypes.c_int(0)
+    probe = lambda wg=4, ticks=1000, out=A, k=ctypes.byref(khz): P.lib().svdq_clock_probe(wg, ticks, out, k, None)
+    assert probe(wg=0) == ops.SVDQ_ERR_SHAPE
+    assert probe(wg=4097) == ops.SVDQ_ERR_SHAPE
+    assert probe(ticks=0) == ops.SVDQ_ERR_SHAPE
+    assert probe(ticks=100_000_001) == ops.SVDQ_ERR_SHAPE
+    assert probe(out=None) == ops.SVDQ_ERR_INVALID_ARG
+    assert probe(k=None) == ops.SVDQ_ERR_INVALID_ARG
+    assert probe(out=U) == ops.SVDQ_ERR_ALIGN
+    assert probe() == ops.SVDQ_ERR_UNSUPPORTED_DEVICE
+
+
 def test_device_check_without_gpu():
     assert P.svdq_device_check(0) == ops.SVDQ_ERR_UNSUPPORTED_DEVICE
     assert P.svdq_device_check(-1) == ops.SVDQ_ERR_UNSUPPORTED_DEVICE
