@@ -82,23 +82,30 @@ void awq_gemv_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__
   constexpr uint32_t kOne = IO == 1 ? 0x3F803F80u : 0x3C003C00u;
   constexpr uint32_t kMagic = IO == 1 ? 0x43004300u : 0x64006400u;
   constexpr float kB = IO == 1 ? 128.0f : 1024.0f;
-  // LDS: x pairs as [m][4 segments of a chunk][chunk][4 pairs] (for a fixed
-  // segment, consecutive chunks are 16 bytes apart: conflict-free reads), then
-  // the chunk sums of x [m][chunk]
+  // LDS: x pairs as [m][chunk group of 16][4 segments of a chunk][16 chunks][4
+  // pairs] (for a fixed segment, the 16 chunks of a group are 16 bytes apart:
+  // conflict-free 16-byte reads; a lane's four segments are 256 bytes apart, one
+  // address and three immediate offsets), then the chunk sums of x [m][chunk].
+  // Both are padded to whole units of the row (npad chunks; the padding holds
+  // zeros and only feeds results that are discarded).
   extern __shared__ uint32_t lds[];
   const int nch = K >> 5;                 // 32-code chunks per row (16 bytes each)
   const int G = K >> 6;
+  const int KB = K >> 1;                  // code bytes per row
+  constexpr int UL = PAIRS ? 32 : 64;     // chunks of a row per unit
+  const int nseg = (nch + UL - 1) / UL;   // units per row (per pair of rows)
+  const int npad = nseg * UL;             // chunks per row in LDS
+  const bool full = npad == nch;          // no unit reaches past the row's end
   uint32_t* xs = lds;
-  float* xc = reinterpret_cast<float*>(lds + (size_t)MR * nch * 16);
+  float* xc = reinterpret_cast<float*>(lds + (size_t)MR * npad * 16);
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const long long W = (long long)gridDim.x * kGemvWaves;
   const long long wg = (long long)blockIdx.x * kGemvWaves + wave;
   const int r0 = (int)(wg * N / W), r1 = (int)((wg + 1) * N / W);
-  constexpr int UL = PAIRS ? 32 : 64;      // chunks of a row per unit
   const int ul = PAIRS ? (lane & 31) : lane;
-  const int hl = PAIRS ? (lane >> 5) : 0;   // PAIRS: the half's row within its pair
-  const int nseg = (nch + UL - 1) / UL;     // units per row (per pair of rows)
+  const bool hl = PAIRS && lane >= 32;    // PAIRS: the odd row of the pair
   const int nrow = max(r1 - r0, 0);
   const int nunits = (PAIRS ? (nrow + 1) >> 1 : nrow) * nseg;
 
@@ -108,15 +115,24 @@ void awq_gemv_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__
   };
   // Loads are unconditional: past the wave's last unit they re-read it (never
   // processed), so the compiler's count of loads in flight stays exact; the odd
-  // half of a last pair with one row re-reads that row (its total is never stored).
+  // half of a last pair with one row re-reads that row (its total is never
+  // stored). The row and unit offsets are wave-uniform (scalar base address);
+  // a lane adds its chunk and, for the odd half of a pair, one row.
   int lrow = 0, lseg = 0;   // row (PAIRS: pair) of the wave and unit within it
   auto load_next = [&](Unit& d) {
     // a wave with no rows re-reads row 0
-    const int row = max(min(r0 + (PAIRS ? 2 * lrow + hl : lrow), r1 - 1), 0);
-    const int c = min(lseg * UL + ul, nch - 1);
-    d.w = *reinterpret_cast<const uint4*>(codes + (size_t)row * (K >> 1) + (size_t)c * 16);
-    d.s = scales[(size_t)row * G + (c >> 1)];
-    d.z = zeros[(size_t)row * G + (c >> 1)];
+    const int ra = max(min(r0 + (PAIRS ? 2 * lrow : lrow), r1 - 1), 0);
+    const int rb = PAIRS ? max(min(r0 + 2 * lrow + 1, r1 - 1), 0) : ra;
+    const int c0 = lseg * UL;
+    const int cl = full ? ul : min(ul, nch - 1 - c0);   // the lane's chunk within the unit
+    const bool odd = hl && rb != ra;
+    const uint8_t* cb = codes + (size_t)ra * KB + (size_t)c0 * 16;
+    const __half* sb = scales + (size_t)ra * G + (c0 >> 1);
+    const __half* zb = zeros + (size_t)ra * G + (c0 >> 1);
+    d.w = *reinterpret_cast<const uint4*>(cb + (uint32_t)((odd ? KB : 0) + cl * 16));
+    const uint32_t so = (uint32_t)((odd ? G : 0) + (cl >> 1)) * 2u;   // byte offset
+    d.s = *reinterpret_cast<const __half*>(reinterpret_cast<const uint8_t*>(sb) + so);
+    d.z = *reinterpret_cast<const __half*>(reinterpret_cast<const uint8_t*>(zb) + so);
     if (++lseg == nseg) {
       lseg = 0;
       ++lrow;
@@ -128,26 +144,27 @@ void awq_gemv_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__
 #pragma unroll
   for (int i = 0; i < kGemvRing - 1; ++i) load_next(d[i]);
 
-  for (int idx = tid; idx < MR * nch * 4; idx += 64 * kGemvWaves) {
-    // idx = (m nch + c) 4 + e: segment e of chunk c = channels 32 c + 8 e .. +8
+  for (int idx = tid; idx < MR * npad * 4; idx += 64 * kGemvWaves) {
+    // idx = (m npad + c) 4 + e: segment e of chunk c = channels 32 c + 8 e .. +8
     const int e = idx & 3, mc = idx >> 2;
-    const int m = mc / nch, c = mc - m * nch;
-    const uint4 v = *reinterpret_cast<const uint4*>(x + (size_t)m * K + (size_t)c * 32 + e * 8);
-    uint32_t* o = xs + (((size_t)m * 4 + e) * nch + c) * 4;
+    const int m = mc / npad, c = mc - m * npad;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (c < nch) v = *reinterpret_cast<const uint4*>(x + (size_t)m * K + (size_t)c * 32 + e * 8);
+    uint32_t* o = xs + (((size_t)m * npad + (c & ~15)) * 4 + e * 16 + (c & 15)) * 4;
     o[0] = (v.x & 0xFFFFu) | (v.z << 16);          // (x_0, x_4)
     o[1] = (v.x >> 16) | (v.z & 0xFFFF0000u);      // (x_1, x_5)
     o[2] = (v.y & 0xFFFFu) | (v.w << 16);          // (x_2, x_6)
     o[3] = (v.y >> 16) | (v.w & 0xFFFF0000u);      // (x_3, x_7)
   }
   __syncthreads();
-  for (int mc = tid; mc < MR * nch; mc += 64 * kGemvWaves) {
-    const int m = mc / nch, c = mc - m * nch;
+  for (int mc = tid; mc < MR * npad; mc += 64 * kGemvWaves) {
+    const int m = mc / npad, c = mc - m * npad;
     float sum = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        sum = dot2_io<IO>(xs[(((size_t)m * 4 + e) * nch + c) * 4 + j], kOne, sum);
+        sum = dot2_io<IO>(xs[(((size_t)m * npad + (c & ~15)) * 4 + e * 16 + (c & 15)) * 4 + j], kOne, sum);
     xc[mc] = sum;
   }
   __syncthreads();
@@ -161,28 +178,36 @@ void awq_gemv_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__
   float acc[MR], out[MR];
 #pragma unroll
   for (int m = 0; m < MR; ++m) acc[m] = out[m] = 0.f;
+  // the dequantization constants live in registers, so that (w & mask) | magic
+  // is one v_and_or_b32
+  uint32_t kmask = 0x000F000Fu, kmag = kMagic;
+  asm volatile("" : "+v"(kmask), "+v"(kmag));
+  // this lane's LDS words: x pairs of chunk ul (segment e at +64 e words), its chunk sum
+  const uint32_t* xl = xs + ((size_t)(ul & ~15) * 4 + (ul & 15)) * 4;
+  const float* xcl = xc + ul;
   int prow = 0, pseg = 0;   // row (PAIRS: pair) of the wave and unit within it
   auto process = [&](const Unit& d) {
-    const int c = pseg * UL + ul;
-    if (c < nch) {
-      const uint32_t w[4] = {d.w.x, d.w.y, d.w.z, d.w.w};
-      const float s = __half2float(d.s);
-      const float zb = kB + __half2float(d.z);
+    const int c0 = pseg * UL;
+    const bool valid = full || c0 + ul < nch;
+    const uint32_t w[4] = {d.w.x, d.w.y, d.w.z, d.w.w};
+    const float s = __half2float(d.s);
+    const float zb = kB + __half2float(d.z);
 #pragma unroll
-      for (int m = 0; m < MR; ++m) {
-        float part = 0.f;
+    for (int m = 0; m < MR; ++m) {
+      const uint32_t* xm = xl + ((size_t)m * npad + c0) * 16;
+      float part = 0.f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint4 xp = *reinterpret_cast<const uint4*>(xs + (((size_t)m * 4 + e) * nch + c) * 4);
-          const uint32_t xv[4] = {xp.x, xp.y, xp.z, xp.w};
+      for (int e = 0; e < 4; ++e) {
+        const uint4 xp = *reinterpret_cast<const uint4*>(xm + e * 64);
+        const uint32_t xv[4] = {xp.x, xp.y, xp.z, xp.w};
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const uint32_t hb = ((w[e] >> (4 * j)) & 0x000F000Fu) | kMagic;
-            part = dot2_io<IO>(hb, xv[j], part);
-          }
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t hb = ((w[e] >> (4 * j)) & kmask) | kmag;
+          part = dot2_io<IO>(hb, xv[j], part);
         }
-        acc[m] = fmaf(s, fmaf(-zb, xc[m * nch + c], part), acc[m]);
       }
+      const float t = fmaf(s, fmaf(-zb, xcl[(size_t)m * npad + c0], part), acc[m]);
+      acc[m] = valid ? t : acc[m];
     }
     if (++pseg == nseg) {   // the row (PAIRS: the pair) is complete
 #pragma unroll
@@ -226,11 +251,13 @@ static hipError_t launch_k(int N, int K, const void* x, const uint8_t* q, const 
   // N, and never more than 64 rows per wave (the kernel keeps one row per lane)
   const int rows_cap = kGemvWaves * 64;
   const int grid = max(max(1, min(256, (N + 8 * 4 - 1) / (8 * 4))), (N + rows_cap - 1) / rows_cap);
-  const size_t lds = (size_t)MR * (K >> 5) * 16 * sizeof(uint32_t) + (size_t)MR * (K >> 5) * sizeof(float);
-  if (lds > 65536) {   // M K = 32768 needs 68 KB
+  constexpr int UL = PAIRS ? 32 : 64;
+  const size_t npad = (size_t)((K >> 5) + UL - 1) / UL * UL;   // chunks per row in LDS, whole units
+  const size_t lds = (size_t)MR * npad * 16 * sizeof(uint32_t) + (size_t)MR * npad * sizeof(float);
+  if (lds > 65536) {   // at most 91392 bytes (M 7, K 4160: 130 chunks padded to 192)
     static std::atomic<uint64_t> raised{0};
     const hipError_t e =
-        raise_lds_limit(raised, reinterpret_cast<const void*>(&awq_gemv_kernel<IO, MR, PAIRS>), 72 * 1024);
+        raise_lds_limit(raised, reinterpret_cast<const void*>(&awq_gemv_kernel<IO, MR, PAIRS>), 96 * 1024);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((awq_gemv_kernel<IO, MR, PAIRS>), dim3(grid), dim3(64 * kGemvWaves), lds, st,

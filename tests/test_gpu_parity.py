@@ -406,10 +406,14 @@ def test_awq_gemv(P, M, N):
 
 
 @pytest.mark.parametrize("M,K,N", [(4, 4096, 512), (1, 12288, 3072), (2, 16384, 300),
-                                   (1, 16448, 77), (8, 4096, 130), (1, 64, 5)])
+                                   (1, 16448, 77), (8, 4096, 130), (1, 64, 5),
+                                   (7, 4160, 1000), (3, 10880, 200), (2, 1088, 4099),
+                                   (1, 3072, 2049), (6, 5440, 64)])
 def test_awq_gemv_random_params_other_k(P, M, K, N):
     """Batched x (M up to 8), ragged N (including fewer rows than waves), K
-    not a multiple of 64 chunks per unit, up to the LDS limit M K = 32768."""
+    not a multiple of 64 chunks per unit (the last unit of a row reaches past
+    its end; x is staged padded to whole units, up to 91392 bytes of LDS at M 7,
+    K 4160), rows in pairs with an odd count, up to the LDS limit M K = 32768."""
     g = synth.GemvConfig(f"gemv_k{K}", 40, 1, K, N, 64)
     p = synth.random_awq_layer(g, seed=5, M=M)
     y_ref = oracle.gemv_ref(p["x"], p["codes"], p["scales"], p["zeros"])
