@@ -136,10 +136,21 @@ def stored_traffic(workload, layer=None):
     return d.get("hbm_bytes_per_launch")
 
 
+def splitk_bytes(cfg):
+    """Workspace of the split-K GEMM for this layer (0: it runs unsplit): INT4
+    layers with too few 128 x 128 output tiles to fill the GPU."""
+    if cfg.fmt != "int4_g64" or cfg.epilogue not in ("none", "gelu_tanh"):
+        return 0
+    import bit_diffusion_transformer_act_amd as P
+    return P.svdq_gemm_w4a4_splitk_workspace(cfg.M, cfg.N, cfg.K, cfg.fmt)
+
+
 def gemm_name(cfg):
     if cfg.fmt == "nvfp4_g16":
         return "svdq_gemm_nvfp4"
-    return "svdq_gemm_w4a4_qkv" if cfg.epilogue == "qkv_norm_rope" else "svdq_gemm_w4a4"
+    if cfg.epilogue == "qkv_norm_rope":
+        return "svdq_gemm_w4a4_qkv"
+    return "svdq_gemm_w4a4_splitk" if splitk_bytes(cfg) else "svdq_gemm_w4a4"
 
 
 class ClockSampler:
@@ -263,6 +274,8 @@ def main(argv=None):
             L["scales"] = torch.empty((cfg.M, scols), dtype=sdt, device=dev)
             L["lora_act"] = torch.empty((cfg.M, r), dtype=torch.float32, device=dev) if r else None
             L["Y"] = torch.empty((cfg.M, cfg.N), dtype=h, device=dev)
+            if splitk_bytes(cfg):
+                L["splitk_ws"] = torch.empty((splitk_bytes(cfg),), dtype=torch.uint8, device=dev)
             if cfg.epilogue == "qkv_norm_rope":
                 e = synth.qkv_epilogue_inputs(cfg.M, seed=0)
                 L["qk_norm_w"], L["rope"], L["eps"] = t(e["qk_norm_w"]), t(e["rope"]), e["eps"]
@@ -298,6 +311,9 @@ def main(argv=None):
         elif cfg.epilogue == "qkv_norm_rope":
             P.svdq_gemm_w4a4_qkv(L["codes"], L["scales"], la, L["w_codes"], L["w_scales"], lu, L["bias"],
                                  L["qk_norm_w"], L["rope"], L["eps"], out=L["Y"], dtype=h)
+        elif "splitk_ws" in L:
+            P.svdq_gemm_w4a4_splitk(L["codes"], L["scales"], la, L["w_codes"], L["w_scales"], lu, L["bias"],
+                                    cfg.fmt, cfg.epilogue, out=L["Y"], dtype=h, workspace=L["splitk_ws"])
         else:
             P.svdq_gemm_w4a4(L["codes"], L["scales"], la, L["w_codes"], L["w_scales"], lu, L["bias"],
                              cfg.fmt, cfg.epilogue, out=L["Y"], dtype=h)

@@ -67,6 +67,8 @@ def step_pattern(workload: str):
         else:
             gk = "gemm_nvfp4_kernel" if cfg.fmt == "nvfp4_g16" else "gemm_"
             pat.append((name, bench.gemm_name(cfg), gk))
+            if bench.splitk_bytes(cfg):   # the split-K GEMM adds its partials in a second kernel
+                pat.append((name, "svdq_gemm_w4a4_splitk.reduce", "splitk_reduce_kernel"))
     return pat + [("gemv", "awq_gemv_w4a16", "awq_gemv")]
 
 

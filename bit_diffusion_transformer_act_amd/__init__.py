@@ -15,6 +15,8 @@ from .ops import (  # noqa: F401
     svdq_device_check,
     svdq_gemm_w4a4,
     svdq_gemm_w4a4_qkv,
+    svdq_gemm_w4a4_splitk,
+    svdq_gemm_w4a4_splitk_workspace,
     svdq_gemm_w4a4_mlp,
     svdq_gemm_w4a4_mlp_noalloc,
     svdq_gemm_nvfp4,

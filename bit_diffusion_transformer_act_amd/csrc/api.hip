@@ -234,6 +234,37 @@ int svdq_gemm_w4a4(int fmt, int dtype, int M, int N, int K, int r, const uint8_t
                                        w_scales, lora_up, bias, epi, Y, (hipStream_t)stream));
 }
 
+size_t svdq_gemm_w4a4_splitk_workspace(int fmt, int M, int N, int K) {
+  if ((fmt != SVDQ_INT4_G64 && fmt != SVDQ_FP4_E2M1_B32) || M < 1 || M > (1 << 23) || N < 128 || N > 65536 ||
+      (N % 128) != 0 || !k_ok(K))
+    return 0;
+  return svdq::splitk_bytes(fmt, M, N, K);
+}
+
+int svdq_gemm_w4a4_splitk(int fmt, int dtype, int M, int N, int K, int r, const uint8_t* act_codes,
+                          const void* act_scales, const float* lora_act, const uint8_t* w_codes,
+                          const void* w_scales, const void* lora_up, const void* bias, int epi, void* Y,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (fmt != SVDQ_INT4_G64 && fmt != SVDQ_FP4_E2M1_B32) return SVDQ_ERR_INVALID_ARG;
+  if (!dtype_ok(dtype)) return SVDQ_ERR_INVALID_ARG;
+  if (epi != SVDQ_EPI_NONE && epi != SVDQ_EPI_GELU_TANH) return SVDQ_ERR_INVALID_ARG;
+  if (M < 0 || M > (1 << 23) || N < 128 || N > 65536 || (N % 128) != 0 || !k_ok(K) || !rank_ok(r))
+    return SVDQ_ERR_SHAPE;
+  if (M == 0) return SVDQ_OK;
+  if (!act_codes || !act_scales || !w_codes || !w_scales || !Y) return SVDQ_ERR_INVALID_ARG;
+  if (r > 0 && (!lora_act || !lora_up)) return SVDQ_ERR_INVALID_ARG;
+  if (!aligned16(act_codes) || !aligned16(act_scales) || !aligned16(w_codes) ||
+      !aligned16(w_scales) || !aligned16(Y) || (bias && !aligned16(bias)) || (workspace && !aligned16(workspace)))
+    return SVDQ_ERR_ALIGN;
+  if (r > 0 && (!aligned16(lora_act) || !aligned16(lora_up))) return SVDQ_ERR_ALIGN;
+  const int dc = check_current_device();
+  if (dc != SVDQ_OK) return dc;
+  (void)hipGetLastError();
+  return finish(svdq::launch_gemm_w4a4_split(fmt, dtype, M, N, K, r, act_codes, act_scales, lora_act, w_codes,
+                                             w_scales, lora_up, bias, epi, Y, workspace, workspace_bytes,
+                                             (hipStream_t)stream));
+}
+
 int svdq_gemm_w4a4_qkv(int fmt, int dtype, int M, int N, int K, int r, const uint8_t* act_codes,
                        const void* act_scales, const float* lora_act, const uint8_t* w_codes,
                        const void* w_scales, const void* lora_up, const void* bias,

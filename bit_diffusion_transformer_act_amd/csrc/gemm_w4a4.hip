@@ -93,7 +93,7 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restr
                       const float* __restrict__ lora_act, const uint8_t* __restrict__ w_codes,
                       const void* __restrict__ w_scales, const uint16_t* __restrict__ lora_up,
                       const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y,
-                      int M, int N, int K, int r, QkvEpilogue qe, ChainEpilogue ce) {
+                      int M, int N, int K, int r, QkvEpilogue qe, ChainEpilogue ce, SplitK sk) {
   using S = GemmShape<WM, WN, STAGES>;
   constexpr int BM = S::BM, BN = S::BN;
   // the 3-stage tiles rely on three workgroups per CU (the launch bound): their
@@ -114,15 +114,24 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restr
   const int ntm = (M + BM - 1) / BM;
   const int ntn = N / BN;
   const int ntiles = ntm * ntn;
+  // EPI 4 (split K): workgroup ids run over (split, tile); the XCD remap over all
+  // of them keeps the tiles of one split, which share A and B rows, on one XCD
+  const int nsplit = EPI == 4 ? sk.splits : 1;
+  const int total = ntiles * nsplit;
   int pid = blockIdx.x;
-  if ((ntiles & 7) == 0) pid = (pid & 7) * (ntiles >> 3) + (pid >> 3);
+  if ((total & 7) == 0) pid = (pid & 7) * (total >> 3) + (pid >> 3);
+  const int split = EPI == 4 ? pid / ntiles : 0;
+  pid -= split * ntiles;
   constexpr int GROUP_M = 8;
   const int gsz = GROUP_M * ntn;
   const int first_m = (pid / gsz) * GROUP_M;
   const int gm = min(ntm - first_m, GROUP_M);
   const int m0 = (first_m + (pid % gsz) % gm) * BM;
   const int n0 = ((pid % gsz) / gm) * BN;
-  const int nk = K >> 7;
+  // this workgroup's K steps: all of them, or split `split` of nsplit near-equal runs
+  const int nk_all = K >> 7;
+  const int ks0 = (int)((long long)split * nk_all / nsplit);
+  const int nk = (int)((long long)(split + 1) * nk_all / nsplit) - ks0;
   const int KB = K >> 1;  // bytes per packed row
   const int sstride = (FMT == 0) ? (K >> 6) * 2 : (K >> 5);  // scale bytes per row
 
@@ -139,7 +148,7 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restr
     const int row = rloc + (lane >> 2);
     const int chunk = (lane & 3) ^ swz(row);
     const int grow = min(m0 + row, M - 1);
-    ga[i] = act_codes + (size_t)grow * KB + chunk * 16;
+    ga[i] = act_codes + (size_t)grow * KB + chunk * 16 + (size_t)ks0 * 64;
     la_off[i] = rloc * 64;
   }
 #pragma unroll
@@ -147,7 +156,7 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restr
     const int rloc = wave * (BN / 4) + 16 * i;
     const int row = rloc + (lane >> 2);
     const int chunk = (lane & 3) ^ swz(row);
-    gb[i] = w_codes + (size_t)(n0 + row) * KB + chunk * 16;
+    gb[i] = w_codes + (size_t)(n0 + row) * KB + chunk * 16 + (size_t)ks0 * 64;
     lb_off[i] = S::A_BYTES + rloc * 64;
   }
 #pragma unroll
@@ -159,7 +168,7 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restr
     if (row < BM) p = reinterpret_cast<const uint8_t*>(act_scales) + (size_t)min(m0 + row, M - 1) * sstride;
     else if (row < BM + BN) p = reinterpret_cast<const uint8_t*>(w_scales) + (size_t)(n0 + row - BM) * sstride;
     else p = reinterpret_cast<const uint8_t*>(w_scales) + (size_t)n0 * sstride;
-    gs[i] = p;
+    gs[i] = p + (size_t)ks0 * 4;   // 4 scale bytes per row and step in both formats
     ls_off[i] = rloc * 8;
   }
 
@@ -199,12 +208,13 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restr
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
+  const int rl = split == 0 ? r : 0;   // split K: the low-rank product joins split 0 only
   if constexpr (FMT == 0) {
     // v_mfma_f32_16x16x16_f16: lane l supplies row l%16, ranks j0 + 4 (l/16) .. +4,
     // as the hi and the lo halves of lora_act (two MFMAs per block and 16 ranks).
     // Loads for 16 ranks go out together (more would raise the register peak).
     const int l16 = lane & 15, lq = lane >> 4;
-    for (int j0 = 0; j0 < r; j0 += 16) {
+    for (int j0 = 0; j0 < rl; j0 += 16) {
       float4 fa[RB4];
       uint2 ub[CB4];
 #pragma unroll
@@ -232,7 +242,7 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restr
   } else {
     // v_mfma_f32_32x32x16_f16: lane l supplies row l%32, ranks j0 + 8 (l/32) .. +8,
     // as the hi and the lo halves of lora_act.
-    for (int j0 = 0; j0 < r; j0 += 16) {
+    for (int j0 = 0; j0 < rl; j0 += 16) {
       float4 fa[RB32][2];
       uint4 ub[CB32];
 #pragma unroll
@@ -409,6 +419,25 @@ void gemm_w4a4_kernel(const uint8_t* __restrict__ act_codes, const void* __restr
     }
   }
 
+  if constexpr (EPI == 4) {
+    // split K: this split's fp32 partial of the tile (256 times the sum, as the
+    // accumulators hold it) goes to its slice [split][M][N]; the reduce kernel
+    // adds the slices in split order and applies the epilogue
+    static_assert(FMT == 0, "split K runs the INT4 kernel");
+    const int l16 = lane & 15, lq = lane >> 4;
+    float* part = sk.part + (size_t)split * M * N;
+#pragma unroll
+    for (int rb = 0; rb < RB4; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + wm * 32 * WM + rb * 16 + lq * 4 + i;
+        if (m < M) {
+#pragma unroll
+          for (int cb = 0; cb < CB4; ++cb) part[(size_t)m * N + n0 + wn * 32 * WN + cb * 16 + l16] = acc4[rb][cb][i];
+        }
+      }
+    return;
+  }
   // ---- epilogue: bias and activation, then the tile goes through LDS (the ring
   // is free now) so that Y is written as whole rows with 16-byte stores.
   constexpr int TP = BN + 8;   // padded row (halves) of the staging tile
@@ -683,7 +712,7 @@ template <int IO, int FMT, int EPI, int WM, int WN, int STAGES>
 static hipError_t launch_cfg(int M, int N, int K, int r, const uint8_t* ac, const void* as,
                              const void* la, const uint8_t* wc, const void* ws, const void* lu,
                              const void* bias, void* Y, hipStream_t st, const QkvEpilogue& qe,
-                             const ChainEpilogue& ce) {
+                             const ChainEpilogue& ce, const SplitK& sk = SplitK{nullptr, 1}) {
   using S = GemmShape<WM, WN, STAGES>;
   auto kern = gemm_w4a4_kernel<IO, FMT, EPI, WM, WN, STAGES>;
   if (S::LDS > 65536) {
@@ -692,8 +721,9 @@ static hipError_t launch_cfg(int M, int N, int K, int r, const uint8_t* ac, cons
     if (e != hipSuccess) return e;
   }
   const int ntiles = ((M + S::BM - 1) / S::BM) * (N / S::BN);
-  hipLaunchKernelGGL(kern, dim3(ntiles), dim3(256), S::LDS, st, ac, as, (const float*)la, wc, ws,
-                     (const uint16_t*)lu, (const uint16_t*)bias, (uint16_t*)Y, M, N, K, r, qe, ce);
+  hipLaunchKernelGGL(kern, dim3(ntiles * (EPI == 4 ? sk.splits : 1)), dim3(256), S::LDS, st, ac, as,
+                     (const float*)la, wc, ws, (const uint16_t*)lu, (const uint16_t*)bias, (uint16_t*)Y, M, N,
+                     K, r, qe, ce, sk);
   return hipGetLastError();
 }
 
@@ -739,6 +769,87 @@ static hipError_t launch_gemm_io(int fmt, int M, int N, int K, int r, const uint
     if (epi == 0) SVDQ_GO(1, 0, 2, 2, 4); else SVDQ_GO(1, 1, 2, 2, 4);
   }
 #undef SVDQ_GO
+}
+
+// Y[m][n] = act(sum_s part[s][m][n] * 2^-8 + bias[n]), the slices added in
+// split order (deterministic); the same epilogue arithmetic as the unsplit
+// kernel. 8 consecutive outputs per thread (16-byte loads and stores).
+template <int IO, int ACT>
+__global__ __launch_bounds__(256)
+void splitk_reduce_kernel(const float* __restrict__ part, int S, const uint16_t* __restrict__ bias,
+                          uint16_t* __restrict__ Y, int M, int N) {
+  const size_t mn = (size_t)M * N;
+  for (size_t e = ((size_t)blockIdx.x * 256 + threadIdx.x) * 8; e < mn; e += (size_t)gridDim.x * 256 * 8) {
+    float4 a = *reinterpret_cast<const float4*>(part + e);
+    float4 b = *reinterpret_cast<const float4*>(part + e + 4);
+    for (int t = 1; t < S; ++t) {
+      const float4 c = *reinterpret_cast<const float4*>(part + (size_t)t * mn + e);
+      const float4 d = *reinterpret_cast<const float4*>(part + (size_t)t * mn + e + 4);
+      a.x += c.x; a.y += c.y; a.z += c.z; a.w += c.w;
+      b.x += d.x; b.y += d.y; b.z += d.z; b.w += d.w;
+    }
+    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    const int n = (int)(e % (size_t)N);
+    uint16_t o[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float y = fmaf(v[j], 0.00390625f, bias ? Io<IO>::to_f(bias[n + j]) : 0.f);   // exact 2^-8, then + bias
+      if (ACT) y = gelu_tanh_f32(y);
+      o[j] = Io<IO>::from_f(y);
+    }
+    *reinterpret_cast<uint4*>(Y + e) = make_uint4(o[0] | ((uint32_t)o[1] << 16), o[2] | ((uint32_t)o[3] << 16),
+                                                  o[4] | ((uint32_t)o[5] << 16), o[6] | ((uint32_t)o[7] << 16));
+  }
+}
+
+int splitk_splits(int fmt, int M, int N, int K) {
+  // INT4 only, and only where 128 x 128 tiles fill fewer than 256 workgroups:
+  // K is cut into S (a power of two) runs while S tiles' worth of workgroups
+  // fit in the 768 slots (three per CU) and each run keeps at least 8 steps
+  if (fmt != 0 || N % 128 != 0) return 1;
+  const long long t128 = (long long)((M + 127) / 128) * (N / 128);
+  if (t128 >= 256) return 1;
+  const int nk = K >> 7;
+  int S = 1;
+  while (t128 * S * 2 <= 768 && nk / (S * 2) >= 8) S *= 2;
+  return S;
+}
+
+size_t splitk_bytes(int fmt, int M, int N, int K) {
+  const int S = splitk_splits(fmt, M, N, K);
+  return S > 1 ? (size_t)S * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
+
+template <int IO>
+static hipError_t launch_split_io(int M, int N, int K, int r, int S, const uint8_t* ac, const void* as,
+                                  const void* la, const uint8_t* wc, const void* ws, const void* lu,
+                                  const void* bias, int epi, void* Y, float* part, hipStream_t st) {
+  const QkvEpilogue qe{nullptr, nullptr, 0.f, 1};
+  const ChainEpilogue ce{nullptr, nullptr, 0, nullptr, nullptr, nullptr};
+  hipError_t e = launch_cfg<IO, 0, 4, 2, 2, 3>(M, N, K, r, ac, as, la, wc, ws, lu, bias, Y, st, qe, ce,
+                                              SplitK{part, S});
+  if (e != hipSuccess) return e;
+  const size_t n8 = (size_t)M * N / 8;
+  const int grid = (int)std::min<size_t>((n8 + 255) / 256, 4096);
+  if (epi == 1)
+    hipLaunchKernelGGL((splitk_reduce_kernel<IO, 1>), dim3(grid), dim3(256), 0, st, part, S,
+                       (const uint16_t*)bias, (uint16_t*)Y, M, N);
+  else
+    hipLaunchKernelGGL((splitk_reduce_kernel<IO, 0>), dim3(grid), dim3(256), 0, st, part, S,
+                       (const uint16_t*)bias, (uint16_t*)Y, M, N);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_w4a4_split(int fmt, int io, int M, int N, int K, int r, const uint8_t* ac, const void* as,
+                                  const void* la, const uint8_t* wc, const void* ws, const void* lu,
+                                  const void* bias, int epi, void* Y, void* workspace, size_t workspace_bytes,
+                                  hipStream_t st) {
+  const int S = splitk_splits(fmt, M, N, K);
+  if (S <= 1 || workspace == nullptr || workspace_bytes < splitk_bytes(fmt, M, N, K))
+    return launch_gemm_w4a4(fmt, io, M, N, K, r, ac, as, la, wc, ws, lu, bias, epi, Y, st);
+  float* part = static_cast<float*>(workspace);
+  if (io == 1) return launch_split_io<1>(M, N, K, r, S, ac, as, la, wc, ws, lu, bias, epi, Y, part, st);
+  return launch_split_io<0>(M, N, K, r, S, ac, as, la, wc, ws, lu, bias, epi, Y, part, st);
 }
 
 int chain_tile_n(int fmt, int M, int N, int K) { return (fmt != 0 && fp4_big_fits(M, N, K)) ? 256 : 128; }

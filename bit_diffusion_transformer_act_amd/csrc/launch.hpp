@@ -58,6 +58,27 @@ struct ChainEpilogue {
 hipError_t launch_chain_reduce(int M, int r, int tiles, const float* partial, float* lora_act,
                                hipStream_t stream);
 
+// Split K (epi == 4 of the INT4 kernel): `splits` workgroups per output tile,
+// each over a contiguous run of K steps, write fp32 partials [splits][M][N]
+// (256 times the sum, the low-rank start in split 0) to `part`.
+struct SplitK {
+  float* part;
+  int splits;
+};
+
+// splits the split-K path uses for this shape (1: it does not split), and the
+// bytes of fp32 partials it needs
+int splitk_splits(int fmt, int M, int N, int K);
+size_t splitk_bytes(int fmt, int M, int N, int K);
+
+// launch_gemm_w4a4 (epi 0 or 1) with K split across workgroups where the shape
+// has too few output tiles for the GPU; falls back to the unsplit kernel when
+// the shape does not split or the workspace is smaller than splitk_bytes()
+hipError_t launch_gemm_w4a4_split(int fmt, int io, int M, int N, int K, int r, const uint8_t* act_codes,
+                                  const void* act_scales, const void* lora_act, const uint8_t* w_codes,
+                                  const void* w_scales, const void* lora_up, const void* bias, int epi,
+                                  void* Y, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 hipError_t launch_gemm_w4a4(int fmt, int io, int M, int N, int K, int r, const uint8_t* act_codes,
                             const void* act_scales, const void* lora_act, const uint8_t* w_codes,
                             const void* w_scales, const void* lora_up, const void* bias, int epi,

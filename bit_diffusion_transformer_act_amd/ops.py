@@ -40,7 +40,7 @@ EXPORTED_SYMBOLS = ("svdq_device_check", "svdq_status_str", "svdq_version",
                     "svdq_quantize_act", "svdq_gemm_w4a4", "svdq_gemm_w4a4_qkv",
                     "svdq_quantize_act_nvfp4", "svdq_gemm_nvfp4", "awq_gemv_w4a16",
                     "svdq_gemm_w4a4_mlp", "svdq_gemm_w4a4_mlp_workspace", "svdq_gemm_w4a4_mlp_noalloc",
-                    "svdq_clock_probe")
+                    "svdq_clock_probe", "svdq_gemm_w4a4_splitk", "svdq_gemm_w4a4_splitk_workspace")
 
 _lock = threading.Lock()
 _handle = None
@@ -92,6 +92,11 @@ def lib() -> ctypes.CDLL:
             h.svdq_gemm_w4a4_mlp_noalloc.restype = i32
             h.awq_gemv_w4a16.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
             h.awq_gemv_w4a16.restype = i32
+            h.svdq_gemm_w4a4_splitk.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, i32, vp,
+                                                vp, sz, vp]
+            h.svdq_gemm_w4a4_splitk.restype = i32
+            h.svdq_gemm_w4a4_splitk_workspace.argtypes = [i32, i32, i32, i32]
+            h.svdq_gemm_w4a4_splitk_workspace.restype = sz
             h.svdq_clock_probe.argtypes = [i32, ctypes.c_ulonglong, vp, ctypes.POINTER(i32), vp]
             h.svdq_clock_probe.restype = i32
             _handle = h
@@ -202,11 +207,8 @@ def svdq_quantize_act(X: torch.Tensor, smooth_inv: torch.Tensor, lora_down, fmt=
     return act_codes, act_scales, (lora_act if r > 0 else None)
 
 
-def svdq_gemm_w4a4(act_codes, act_scales, lora_act, w_codes, w_scales, lora_up, bias,
-                   fmt="int4_g64", epilogue="none", out=None, dtype=None):
-    """Fused 4-bit GEMM + low-rank up-projection + bias (+ GELU) -> Y [M][N] in
-    the layer's 16-bit type (dtype, else that of lora_up / bias / out, else
-    float16); lora_act is fp32 [M][r]."""
+def _gemm_call(name, act_codes, act_scales, lora_act, w_codes, w_scales, lora_up, bias, fmt, epilogue, out,
+               dtype, extra):
     f = _fmt(fmt)
     h = _pick_dtype(dtype, lora_up, bias, out)
     io = DTYPES[h]
@@ -233,13 +235,44 @@ def svdq_gemm_w4a4(act_codes, act_scales, lora_act, w_codes, w_scales, lora_up, 
         out = torch.empty((M, N), dtype=h, device=dev)
     _check(out, "out", h, (M, N), dev)
     with torch.cuda.device(dev):
-        st = lib().svdq_gemm_w4a4(f, io, M, N, K, r, _ptr(act_codes), _ptr(act_scales),
+        st = getattr(lib(), name)(f, io, M, N, K, r, _ptr(act_codes), _ptr(act_scales),
                                   _ptr(lora_act) if r > 0 else None, _ptr(w_codes), _ptr(w_scales),
                                   _ptr(lora_up) if r > 0 else None, _ptr(bias), e, _ptr(out),
-                                  _stream(dev))
+                                  *extra(f, M, N, K, dev), _stream(dev))
     if st != SVDQ_OK:
-        raise SvdqError(st, "svdq_gemm_w4a4")
+        raise SvdqError(st, name)
     return out
+
+
+def svdq_gemm_w4a4(act_codes, act_scales, lora_act, w_codes, w_scales, lora_up, bias,
+                   fmt="int4_g64", epilogue="none", out=None, dtype=None):
+    """Fused 4-bit GEMM + low-rank up-projection + bias (+ GELU) -> Y [M][N] in
+    the layer's 16-bit type (dtype, else that of lora_up / bias / out, else
+    float16); lora_act is fp32 [M][r]."""
+    return _gemm_call("svdq_gemm_w4a4", act_codes, act_scales, lora_act, w_codes, w_scales, lora_up, bias, fmt,
+                      epilogue, out, dtype, lambda f, M, N, K, dev: ())
+
+
+def svdq_gemm_w4a4_splitk_workspace(M: int, N: int, K: int, fmt="int4_g64") -> int:
+    """Bytes of workspace svdq_gemm_w4a4_splitk splits K with (0: no split)."""
+    return int(lib().svdq_gemm_w4a4_splitk_workspace(_fmt(fmt), int(M), int(N), int(K)))
+
+
+def svdq_gemm_w4a4_splitk(act_codes, act_scales, lora_act, w_codes, w_scales, lora_up, bias,
+                          fmt="int4_g64", epilogue="none", out=None, dtype=None, workspace=None):
+    """svdq_gemm_w4a4 with K split across workgroups for shapes with few output
+    tiles; `workspace` is a device uint8 tensor of at least
+    svdq_gemm_w4a4_splitk_workspace(M, N, K) bytes (allocated here when None;
+    a smaller one runs the unsplit kernel)."""
+    def extra(f, M, N, K, dev):
+        nonlocal workspace
+        if workspace is None:
+            n = int(lib().svdq_gemm_w4a4_splitk_workspace(f, M, N, K))
+            workspace = torch.empty((max(n, 16),), dtype=torch.uint8, device=dev)
+        _check(workspace, "workspace", torch.uint8, (workspace.numel(),), dev)
+        return (_ptr(workspace), ctypes.c_size_t(workspace.numel()))
+    return _gemm_call("svdq_gemm_w4a4_splitk", act_codes, act_scales, lora_act, w_codes, w_scales, lora_up, bias,
+                      fmt, epilogue, out, dtype, extra)
 
 
 def svdq_gemm_w4a4_qkv(act_codes, act_scales, lora_act, w_codes, w_scales, lora_up, bias,

@@ -180,6 +180,34 @@ int svdq_gemm_w4a4(int fmt, int dtype, int M, int N, int K, int r,
                    const void* bias, int epi, void* Y, void* stream);
 
 /*
+ * svdq_gemm_w4a4_splitk -- svdq_gemm_w4a4 (epi NONE or GELU_TANH) for shapes
+ * with too few output tiles to fill the GPU (few tokens, long K, e.g. an MLP
+ * down-projection at M 1024): K is cut into S near-equal runs of whole 128-code
+ * steps, S (a power of two, at most 8) workgroups per output tile each write
+ * the fp32 partial sum of their run into `workspace` ([S][M][N]; the low-rank
+ * product joins the first run), and a second kernel adds the S partials in
+ * run order and applies bias and epilogue as svdq_gemm_w4a4 does. The same
+ * float result up to the order of the fp32 additions (deterministic). INT4
+ * only: with SVDQ_FP4_E2M1_B32, with a shape that does not split, with a NULL
+ * workspace or with workspace_bytes below
+ * svdq_gemm_w4a4_splitk_workspace(...), the call runs svdq_gemm_w4a4 itself.
+ *
+ * Arguments as svdq_gemm_w4a4, and
+ *   workspace        device memory (16-byte aligned) owned by the call until its
+ *                    work on `stream` completes; contents on entry do not matter.
+ *   workspace_bytes  its size.
+ */
+int svdq_gemm_w4a4_splitk(int fmt, int dtype, int M, int N, int K, int r,
+                          const uint8_t* act_codes, const void* act_scales, const float* lora_act,
+                          const uint8_t* w_codes, const void* w_scales, const void* lora_up,
+                          const void* bias, int epi, void* Y, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* Workspace bytes svdq_gemm_w4a4_splitk splits K with for this shape:
+ * S M N 4, or 0 when the shape (or format) does not split or is invalid. */
+size_t svdq_gemm_w4a4_splitk_workspace(int fmt, int M, int N, int K);
+
+/*
  * svdq_gemm_w4a4_qkv -- svdq_gemm_w4a4 for a fused Q|K|V projection, with the
  * per-head RMSNorm of Q and K and the rotary position embedding applied in the
  * same epilogue (the pages' structural rewrite that fuses the QKV projection

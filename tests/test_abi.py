@@ -203,6 +203,32 @@ def test_mlp_chain_noalloc_argument_errors():
     assert ops.NOALLOC_SCRATCH_BYTES == 64 << 20
 
 
+def test_splitk_workspace_and_argument_errors():
+    """The split rule through its workspace size: K is split only for INT4 and
+    fewer than 256 output tiles of 128 x 128, into the largest power of two S
+    with S tiles' workgroups within 768 and at least 8 K steps per split."""
+    ws = P.lib().svdq_gemm_w4a4_splitk_workspace
+    assert ws(0, 1024, 3072, 12288) == 4 * 1024 * 3072 * 4     # 192 tiles, 96 steps: S 4
+    assert ws(0, 256, 3072, 12288) == 8 * 256 * 3072 * 4       # 48 tiles: S 8 (12 steps each)
+    assert ws(0, 200, 512, 4096) == 4 * 200 * 512 * 4          # 8 tiles, 32 steps: S 4 (8 each)
+    assert ws(0, 64, 1024, 2048) == 2 * 64 * 1024 * 4          # 16 steps: S 2
+    assert ws(0, 2048, 3072, 12288) == 0                        # 384 tiles: no split
+    assert ws(0, 1024, 3072, 1024) == 0                         # 8 steps: too short to split
+    assert ws(1, 1024, 3072, 12288) == 0                        # FP4 does not split
+    assert ws(0, 1024, 3000, 12288) == 0 and ws(0, 0, 3072, 12288) == 0 and ws(2, 1024, 3072, 12288) == 0
+
+    def sk(fmt=0, M=4, N=128, K=128, r=16, epi=0, w=A, n=1 << 20, Y=A, dt=0):
+        return P.lib().svdq_gemm_w4a4_splitk(fmt, dt, M, N, K, r, A, A, A, A, A, A, None, epi, Y, w, n, None)
+    assert sk(fmt=2) == ops.SVDQ_ERR_INVALID_ARG
+    assert sk(epi=2) == ops.SVDQ_ERR_INVALID_ARG
+    assert sk(N=192) == ops.SVDQ_ERR_SHAPE
+    assert sk(w=U) == ops.SVDQ_ERR_ALIGN
+    assert sk(Y=None) == ops.SVDQ_ERR_INVALID_ARG
+    assert sk(M=0, Y=None) == ops.SVDQ_OK
+    assert sk() == ops.SVDQ_ERR_UNSUPPORTED_DEVICE
+    assert sk(w=None, n=0) == ops.SVDQ_ERR_UNSUPPORTED_DEVICE   # no workspace: the unsplit kernel
+
+
 def test_clock_probe_argument_errors():
     khz = ctypes.c_int(0)
     probe = lambda wg=4, ticks=1000, out=A, k=ctypes.byref(khz): P.lib().svdq_clock_probe(wg, ticks, out, k, None)

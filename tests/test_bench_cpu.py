@@ -111,10 +111,15 @@ def test_step_pattern_labels_the_block():
     rows = [{"Kernel_Name": "void svdq::" + n} for n in names * 3]
     lab = bc.label(rows, pat)
     assert len(lab) == 27 and [l[0] for l, _ in lab[:9]] == [p[0] for p in pat]
+    # M 1024: the quantizer splits K (two dispatches, one launch), the GEMM splits
+    # K (its kernel, then the reduce of the partials as a slot of its own)
     split = [{"Kernel_Name": "svdq::" + n} for n in ["quantize_act_kernel<a>", "quantize_act_kernel<b>",
-                                                     "gemm_w4a4_kernel<0>", "awq_gemv_kernel<0>"]]
+                                                     "gemm_w4a4_kernel<0>", "splitk_reduce_kernel<0>",
+                                                     "awq_gemv_kernel<0>"]]
     lab = bc.label(split * 2, bc.step_pattern("mlp_down_m1024"))
-    assert [len(rs) for _, rs in lab] == [2, 1, 1, 2, 1, 1]
+    assert [len(rs) for _, rs in lab] == [2, 1, 1, 1, 2, 1, 1, 1]
+    assert [l[1] for l, _ in lab[:4]] == ["svdq_quantize_act", "svdq_gemm_w4a4_splitk",
+                                          "svdq_gemm_w4a4_splitk.reduce", "awq_gemv_w4a16"]
     with pytest.raises(SystemExit):
         bc.label([{"Kernel_Name": "svdq::awq_gemv_kernel<0>"}], pat)
 
