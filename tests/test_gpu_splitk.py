@@ -89,7 +89,8 @@ def test_splitk_small_against_oracle(P, M, K, N, r, epi, dt, splits):
 def test_splitk_deterministic_and_close_to_unsplit(P):
     """Two calls give the same bits; against the unsplit kernel only the order
     of the fp32 additions differs, so the outputs agree to an ulp or two of
-    fp16 (the checks against the oracle above are the bar)."""
+    fp16 plus a floor far below the oracle bar's (the checks against the
+    oracle above are the bar)."""
     cfg = synth.LayerConfig("splitk_det", 55, 512, 8192, 768, 32, "int4_g64", "none", "normal", 0.005, 30.0)
     p, codes_u, packed, scales, la = layer(cfg, seed=6)
     args = gemm_args(p, packed, scales, la, torch.float16)
@@ -99,7 +100,10 @@ def test_splitk_deterministic_and_close_to_unsplit(P):
     assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16))
     y0 = host(P.svdq_gemm_w4a4(*args)).astype(np.float64)
     ulp = np.spacing(np.abs(y0).astype(np.float16)).astype(np.float64)
-    assert np.all(np.abs(y1.astype(np.float64) - y0) <= 2 * ulp + 1e-6)
+    # outputs near zero come from cancelling sums, where the fp32 order shows
+    # at a tiny fraction of the outputs' rms rather than in fp16 ulps
+    rms = np.sqrt(np.mean(y0 ** 2))
+    assert np.all(np.abs(y1.astype(np.float64) - y0) <= 2 * ulp + 1e-4 * rms)
 
 
 @pytest.mark.parametrize("case", ["too_small", "no_split_shape", "fp4"])
