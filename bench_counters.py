@@ -42,7 +42,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 
 # kernel-name substring -> source file
 SOURCES = [("gemm_fp4_big_kernel", "gemm_fp4.hip"), ("gemm_w4a4_kernel", "gemm_w4a4.hip"),
-           ("chain_reduce_kernel", "gemm_w4a4.hip"), ("gemm_nvfp4_kernel", "gemm_nvfp4.hip"),
+           ("chain_reduce_kernel", "gemm_w4a4.hip"), ("splitk_reduce_kernel", "gemm_w4a4.hip"),
+           ("gemm_nvfp4_kernel", "gemm_nvfp4.hip"),
            ("quantize_act_kernel", "quantize_act.hip"), ("awq_gemv", "awq_gemv.hip")]
 
 

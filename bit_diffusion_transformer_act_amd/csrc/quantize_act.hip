@@ -319,13 +319,18 @@ void quantize_act_kernel(const uint16_t* __restrict__ X, const float* __restrict
         sv[8 * h + 0] = u0.x; sv[8 * h + 1] = u0.y; sv[8 * h + 2] = u0.z; sv[8 * h + 3] = u0.w;
         sv[8 * h + 4] = u1.x; sv[8 * h + 5] = u1.y; sv[8 * h + 6] = u1.z; sv[8 * h + 7] = u1.w;
       }
-      // one fma with a -0 addend: the product rounded once, sign of zero kept
+      // one fma with a -0 addend: the product rounded once, sign of zero kept.
+      // The -0 sits in a register, so that with fp16 input each product is one
+      // v_fma_mix_f32 reading the 16-bit half in place (no separate convert;
+      // an fp32 literal cannot be an operand of that instruction).
       const uint16_t* ha = reinterpret_cast<const uint16_t*>(&d.xa);
       const uint16_t* hb = reinterpret_cast<const uint16_t*>(&d.xb);
+      float nz = -0.0f;
+      asm volatile("" : "+s"(nz));
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        xh[i] = fmaf(Io<IO>::to_f(ha[i]), sv[i], -0.0f);
-        xh[8 + i] = fmaf(Io<IO>::to_f(hb[i]), sv[8 + i], -0.0f);
+        xh[i] = fmaf(Io<IO>::to_f(ha[i]), sv[i], nz);
+        xh[8 + i] = fmaf(Io<IO>::to_f(hb[i]), sv[8 + i], nz);
       }
     }
     uint8_t* crow = rb + (lane & 15) * CROW + wave * 32 + q4 * 4;
