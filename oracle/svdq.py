@@ -430,7 +430,7 @@ def gemm_ref(act_codes, act_scales, lora_act, w_codes, w_scales, lora_up, bias,
     Y = act(lora_act . lora_up^T + sum_g s_x[m,g] s_w[n,g] (q_x[m,g,:] . q_w[n,g,:]) + bias).
 
     act_codes / w_codes are unpacked ([M][K], [N][K]); lora_act [M][r] is the
-    value handed to the GEMM (the quantizer's fp16 output). rows / cols pick a
+    value handed to the GEMM (the quantizer's fp32 output). rows / cols pick a
     subset of outputs for spot checks at full size. act_gscale / w_gscale are
     NVFP4's per-tensor scales (each dequantized value carries its own).
     """

@@ -1,10 +1,11 @@
 """Parity of the HIP library (through the C ABI binding) with the CPU oracle.
 
 Bar: activation codes and scales bit-exact; layer / GEMM / GEMV outputs
-within relative L2 2e-3 of the oracle's float64 result on the same codes;
-lora_act (fp16) within 1e-3 of the float64 low-rank down-projection. Every oracle
-input comes from the seeded generators or from the oracle itself, never from
-the GPU.
+within relative L2 2e-3 of the oracle's float64 result on the same codes, and
+every compared element within 2 ulp of its type plus 1e-3 rms
+(tests/parity.py); lora_act (fp32) within 1e-3 of the float64 low-rank
+down-projection under the same element bound. Every oracle input comes from
+the seeded generators or from the oracle itself, never from the GPU.
 """
 import numpy as np
 import pytest
