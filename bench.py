@@ -16,15 +16,18 @@ cannot live in the 256 MB Infinity Cache.
 
 Prints ONE JSON line. `value` is the stream's effective throughput
 sum(2 M N K) / step time in TOPS (the quantizers' and the GEMV's time is
-inside the step). Per-launch durations come from HIP events recorded on the
-launch stream around every launch in the timed region (median, p10, p90 over
-the steps). The low-rank overhead t(rank r) / t(rank 0) - 1 is measured by a
+inside the step). The timed steps are eager launches with HIP events recorded
+on the launch stream around every launch, which give the per-launch
+durations (mean, median, p10, p90 over the steps); --graph times HIP graph
+replays instead (one graph per rotating input set, captured after the warm-up
+and checked bit for bit against an eager step), with the per-launch durations
+from an eager pass. The low-rank overhead t(rank r) / t(rank 0) - 1 is measured by a
 second timed pass with the low-rank branch off. The shader clock is measured
 on the GPU just before and just after the timed steps (cycles against the
 real-time counter), and amdsmi's reported clock is sampled during them.
 
 Options: --gpus N (only 1: one GPU), --steps K (default 100), --warmup W
-(default 20), --workload NAME, --no-cpu-baseline, --no-lowrank-overhead,
+(default 20), --workload NAME, --graph, --no-cpu-baseline, --no-lowrank-overhead,
 --warm (no buffer rotation), --rank R, --prewarm-ms T (untimed steps for T ms
 before the warm-up steps, default 150: after idle the clocks need tens of ms
 of load to settle), --calib-copy-mib N (a plain fill and add of N MiB after
@@ -87,6 +90,10 @@ def parse(argv=None):
     ap.add_argument("--workload", default="block", choices=list(WORKLOADS) + list(SINGLE))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-lowrank-overhead", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the steps as HIP graph replays: each rotating input set's step captured "
+                         "once (checked bit for bit against an eager step) and replayed (default: eager "
+                         "launches; the two measured within 0.1 %% of each other on the block stream)")
     ap.add_argument("--warm", action="store_true", help="no buffer rotation (cache-warm)")
     ap.add_argument("--rank", type=int, default=None, help="override the low-rank width")
     ap.add_argument("--prewarm-ms", type=float, default=150.0,
@@ -353,20 +360,25 @@ def main(argv=None):
 
     clock = {}
 
-    def timed(lowrank, sampler=None):
+    def settle(run):
         # clocks ramp for tens of ms under load after idle: untimed steps for
         # --prewarm-ms of wall time (synchronizing every 8 steps so the host
         # clock follows the GPU), then the W warm-up steps
         t_end = time.perf_counter() + args.prewarm_ms * 1e-3
         i = 0
         while time.perf_counter() < t_end:
-            step(i, lowrank=lowrank)
+            run(i)
             i += 1
             if i % 8 == 0:
                 torch.cuda.synchronize()
         for i in range(args.warmup):
-            step(i, lowrank=lowrank)
+            run(i)
         torch.cuda.synchronize()
+
+    def timed(lowrank, sampler=None):
+        """Eager launches with HIP events around every launch: per-launch
+        durations (and the eager step time)."""
+        settle(lambda i: step(i, lowrank=lowrank))
         if sampler is not None:
             clock["gfx_mhz_before"] = probe_clock(P)
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(args.steps)]
@@ -385,9 +397,56 @@ def main(argv=None):
         durs = np.array([[e[k].elapsed_time(e[k + 1]) for k in range(nk)] for e in evs])
         return wall * 1e3 / args.steps, durs
 
+    def capture(lowrank):
+        """One HIP graph per rotating input set holding that set's whole step
+        (the same launches, on torch's capture stream); checked against an
+        eager step on the same set, output for output, bit for bit."""
+        graphs = []
+        for i in range(nsets):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(i, lowrank=lowrank)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        layers, G = sets[0]
+        outs = [L[k] for L in layers for k in ("Y", "codes", "scales") if L.get(k) is not None] + [G["y"]]
+        step(0, lowrank=lowrank)
+        torch.cuda.synchronize()
+        ref = [o.clone() for o in outs]
+        for o in outs:
+            o.fill_(0)
+        graphs[0].replay()
+        torch.cuda.synchronize()
+        for o, r in zip(outs, ref):
+            if not torch.equal(o.view(torch.uint8), r.view(torch.uint8)):
+                raise RuntimeError("a graph replay differs from the eager step")
+        return graphs
+
+    def timed_graph(graphs, sampler=None):
+        """The steps as graph replays: the step time without per-launch events
+        or per-launch host overhead."""
+        settle(lambda i: graphs[i % nsets].replay())
+        if sampler is not None:
+            clock["gfx_mhz_before"] = probe_clock(P)
+            sampler.start()
+        t0 = time.perf_counter()
+        for s in range(args.steps):
+            graphs[(args.warmup + s) % nsets].replay()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        if sampler is not None:
+            clock["gfx_mhz_after"] = probe_clock(P)
+            sampler.stop()
+        return wall * 1e3 / args.steps
+
     props = torch.cuda.get_device_properties(dev)
     sampler = ClockSampler(getattr(props, "pci_bus_id", None))
-    ms_per_step, durs = timed(True, sampler)
+    if not args.graph:
+        ms_per_step, durs = timed(True, sampler)
+        ms_eager = ms_per_step
+    else:
+        ms_eager, durs = timed(True)
+        ms_per_step = timed_graph(capture(True), sampler)
 
     if args.calib_copy_mib:
         n = args.calib_copy_mib << 20
@@ -401,13 +460,15 @@ def main(argv=None):
     lr_over = None
     if any_rank and not args.no_lowrank_overhead:
         ms0, durs0 = timed(False)
+        if args.graph:
+            ms0 = timed_graph(capture(False))
         mean0 = durs0.mean(axis=0)
         lr_over = {"step": round(ms_per_step / ms0 - 1, 4), "rank": max(r for _, _, _, r, _ in plan),
                    "ms_per_step_rank0": round(ms0, 4),
                    "per_launch": {plan[k][0]: round(float(durs[:, k].mean() / mean0[k] - 1), 4)
                                   for k in range(nk) if plan[k][1] != "gemv"},
                    "note": "t(rank r) / t(rank 0) - 1, same inputs with the low-rank branch off "
-                           "(second timed pass)"}
+                           "(second timed pass; the step in the timed mode, per launch from events)"}
 
     mean_ms = durs.mean(axis=0)
     med_ms = np.median(durs, axis=0)
@@ -483,6 +544,10 @@ def main(argv=None):
         "cpu_baseline": cpu,
         "kernels": kernels,
         "lowrank_overhead": lr_over,
+        "launch": {"mode": "hip graph per rotating input set, replayed" if args.graph else "eager",
+                   "ms_per_step_eager_with_events": round(ms_eager, 4),
+                   "note": "kernels and roofline come from the eager pass (HIP events around every "
+                           "launch); ms_per_step and value from the timed steps of this mode"},
         "clocks": {"source": "shader cycles (s_memtime) over the real-time counter (s_memrealtime), "
                              "2 ms on ~every CU just before and just after the timed steps; amdsmi's "
                              "reported clock sampled every 5 ms during them",
