@@ -31,7 +31,10 @@
 namespace svdq {
 
 constexpr int kGemvWaves = 8;   // waves per workgroup
-constexpr int kGemvRing = 6;    // units in flight per wave
+// units in the register ring of a wave (two in flight while one is processed):
+// the fastest of the depths 2 to 10 measured (K3072 N18432: 3 -> 11.9 us,
+// 4 -> 12.3, 6 -> 13.3, 8 -> 14.3; at M4 18.8 against 23.1 with 6)
+constexpr int kGemvRing = 3;
 
 // Sum over the 64 lanes; every lane gets the same total (a fixed order: the
 // xor-32 and xor-16 partners via v_permlane32/16_swap, then within each 16-lane
