@@ -19,7 +19,7 @@
 // the same number of bytes. The rows of a wave are contiguous in memory and
 // are read as a stream of units of 64 chunks of 16 bytes (lane l takes chunk
 // l of the unit): each load instruction covers 1 KB of whole cache lines, and
-// a ring of units keeps several in flight. Where a row is an odd number of
+// a ring of three units keeps two in flight. Where a row is an odd number of
 // 32-chunk halves (K = 3072, for one), rows go in pairs, one per half-wave, so
 // that no unit is half empty. x and its chunk sums sit in LDS. A
 // row's lane partials are summed with lane swaps and DPP at its last unit.
