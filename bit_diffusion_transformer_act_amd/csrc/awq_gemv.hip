@@ -9,20 +9,26 @@
 // in the activations' 16-bit type: (word >> 4j) & 0x000F000F | 0x64006400 is
 // the packed fp16 pair (1024 + q_j, 1024 + q_{j+4}) and | 0x43004300 the bf16
 // pair (128 + q_j, 128 + q_{j+4}), both exact, and v_dot2_f32_f16 / _bf16
-// accumulates x (B + q) in fp32 against x stored as pairs (x_j, x_{j+4}). Per
-// 32-code chunk, sum x (q - z) = sum x (B + q) - (B + z) sum x, with the second
-// term one fma from the precomputed chunk sum of x, so any fp16 zero point
-// works. Scales and zero points are fp16 in both cases (the stored format).
+// accumulates x (B + q) in fp32 against x stored as pairs (x_j, x_{j+4}). In
+// fp16 the odd pairs skip the shift: word & 0x00F000F0 | 0x64006400 is
+// (1024 + 16 q_j, 1024 + 16 q_{j+4}), exact, and their products go to a second
+// accumulator that enters at 1/16 (exact). Per 32-code chunk,
+// sum x (q - z) = P - D - z S, with P the accumulators' total, D the chunk's
+// share of the offsets (1024 x for the even pairs and 64 x for the odd ones in
+// fp16; 128 x in bf16) and S = sum x, both precomputed once per chunk; so any
+// fp16 zero point works. Scales and zero points are fp16 in both cases (the
+// stored format).
 //
-// Work split: one 8-wave workgroup per CU; wave w of the grid owns the
-// contiguous rows [w N / W, (w + 1) N / W) (W waves in all), so every CU streams
-// the same number of bytes. The rows of a wave are contiguous in memory and
-// are read as a stream of units of 64 chunks of 16 bytes (lane l takes chunk
-// l of the unit): each load instruction covers 1 KB of whole cache lines, and
-// a ring of three units keeps two in flight. Where a row is an odd number of
-// 32-chunk halves (K = 3072, for one), rows go in pairs, one per half-wave, so
-// that no unit is half empty. x and its chunk sums sit in LDS. A
-// row's lane partials are summed with lane swaps and DPP at its last unit.
+// Work split: one 8-wave workgroup per CU; wave w of the grid (W waves in all)
+// owns rows w, w + W, w + 2W, ... (in pairs: see below), so at any moment the
+// grid reads one contiguous window of the matrix, and every CU streams the
+// same number of bytes. A row is read as a stream of units of 64 chunks of 16
+// bytes (lane l takes chunk l of the unit): each load instruction covers 1 KB
+// of whole cache lines, and a ring of three units keeps two in flight. Where a
+// row is an odd number of 32-chunk halves (K = 3072, for one), rows go in
+// pairs, one per half-wave, so that no unit is half empty. x and its chunk sums
+// sit in LDS. A row's lane partials are summed with lane swaps and DPP at its
+// last unit.
 #include <atomic>
 
 #include "common.hpp"
@@ -81,14 +87,13 @@ __global__ __launch_bounds__(64 * kGemvWaves)
 void awq_gemv_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
                      const __half* __restrict__ scales, const __half* __restrict__ zeros,
                      const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int N, int K) {
-  // 1.0 as a pair, and the exact offset B of the dequantization trick with its bit pattern
+  // 1.0 as a pair, and the pair (B, B) of the dequantization trick's exact offset
   constexpr uint32_t kOne = IO == 1 ? 0x3F803F80u : 0x3C003C00u;
   constexpr uint32_t kMagic = IO == 1 ? 0x43004300u : 0x64006400u;
-  constexpr float kB = IO == 1 ? 128.0f : 1024.0f;
   // LDS: x pairs as [m][chunk group of 16][4 segments of a chunk][16 chunks][4
   // pairs] (for a fixed segment, the 16 chunks of a group are 16 bytes apart:
   // conflict-free 16-byte reads; a lane's four segments are 256 bytes apart, one
-  // address and three immediate offsets), then the chunk sums of x [m][chunk].
+  // address and three immediate offsets), then each chunk's (D, S) [m][chunk][2].
   // Both are padded to whole units of the row (npad chunks; the padding holds
   // zeros and only feeds results that are discarded).
   extern __shared__ uint32_t lds[];
@@ -106,11 +111,13 @@ void awq_gemv_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const long long W = (long long)gridDim.x * kGemvWaves;
   const long long wg = (long long)blockIdx.x * kGemvWaves + wave;
-  const int r0 = (int)(wg * N / W), r1 = (int)((wg + 1) * N / W);
   const int ul = PAIRS ? (lane & 31) : lane;
   const bool hl = PAIRS && lane >= 32;    // PAIRS: the odd row of the pair
-  const int nrow = max(r1 - r0, 0);
-  const int nunits = (PAIRS ? (nrow + 1) >> 1 : nrow) * nseg;
+  // the wave's row groups (PAIRS: pairs of rows) are wg, wg + W, wg + 2W, ...
+  constexpr int RG = PAIRS ? 2 : 1;
+  const long long ngrp = ((long long)N + RG - 1) / RG;
+  const int ng = wg < ngrp ? (int)((ngrp - wg + W - 1) / W) : 0;
+  const int nunits = ng * nseg;
 
   struct Unit {
     uint4 w;
@@ -121,11 +128,12 @@ void awq_gemv_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__
   // half of a last pair with one row re-reads that row (its total is never
   // stored). The row and unit offsets are wave-uniform (scalar base address);
   // a lane adds its chunk and, for the odd half of a pair, one row.
-  int lrow = 0, lseg = 0;   // row (PAIRS: pair) of the wave and unit within it
+  int lrow = 0, lseg = 0;   // row group of the wave and unit within it
   auto load_next = [&](Unit& d) {
     // a wave with no rows re-reads row 0
-    const int ra = max(min(r0 + (PAIRS ? 2 * lrow : lrow), r1 - 1), 0);
-    const int rb = PAIRS ? max(min(r0 + 2 * lrow + 1, r1 - 1), 0) : ra;
+    const int gi = max(min(lrow, ng - 1), 0);
+    const int ra = ng > 0 ? (int)(((long long)gi * W + wg) * RG) : 0;
+    const int rb = PAIRS ? min(ra + 1, N - 1) : ra;
     const int c0 = lseg * UL;
     const int cl = full ? ul : min(ul, nch - 1 - c0);   // the lane's chunk within the unit
     const bool odd = hl && rb != ra;
@@ -161,20 +169,27 @@ void awq_gemv_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__
   }
   __syncthreads();
   for (int mc = tid; mc < MR * npad; mc += 64 * kGemvWaves) {
+    // the chunk's D (the offsets' share: B x, or (B / 16) x for fp16's odd
+    // pairs, which enter at 1/16) and S = sum x
     const int m = mc / npad, c = mc - m * npad;
-    float sum = 0.f;
+    constexpr uint32_t k64 = 0x54005400u;   // (64, 64) in fp16
+    float dsum = 0.f, ssum = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        sum = dot2_io<IO>(xs[(((size_t)m * npad + (c & ~15)) * 4 + e * 16 + (c & 15)) * 4 + j], kOne, sum);
-    xc[mc] = sum;
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t pr = xs[(((size_t)m * npad + (c & ~15)) * 4 + e * 16 + (c & 15)) * 4 + j];
+        dsum = dot2_io<IO>(pr, (IO == 0 && (j & 1)) ? k64 : kMagic, dsum);
+        ssum = dot2_io<IO>(pr, kOne, ssum);
+      }
+    xc[2 * mc] = dsum;
+    xc[2 * mc + 1] = ssum;
   }
   __syncthreads();
 
-  if (r1 <= r0) return;
+  if (ng == 0) return;
 
-  // Row totals are collected in registers (row i of the wave in lane i; the
+  // Row totals are collected in registers (the wave's i-th row in lane i; the
   // grid gives no wave more than 64 rows) and written after the loop: a store
   // on one path only would leave the compiler unsure how many loads are in
   // flight and drain the ring at every row.
@@ -183,33 +198,41 @@ void awq_gemv_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__
   for (int m = 0; m < MR; ++m) acc[m] = out[m] = 0.f;
   // the dequantization constants live in registers, so that (w & mask) | magic
   // is one v_and_or_b32
-  uint32_t kmask = 0x000F000Fu, kmag = kMagic;
-  asm volatile("" : "+v"(kmask), "+v"(kmag));
-  // this lane's LDS words: x pairs of chunk ul (segment e at +64 e words), its chunk sum
+  uint32_t kmask = 0x000F000Fu, kmask1 = 0x00F000F0u, kmag = kMagic;
+  asm volatile("" : "+v"(kmask), "+v"(kmask1), "+v"(kmag));
+  // this lane's LDS words: x pairs of chunk ul (segment e at +64 e words), its (D, S)
   const uint32_t* xl = xs + ((size_t)(ul & ~15) * 4 + (ul & 15)) * 4;
-  const float* xcl = xc + ul;
-  int prow = 0, pseg = 0;   // row (PAIRS: pair) of the wave and unit within it
+  const float2* xcl = reinterpret_cast<const float2*>(xc) + ul;
+  int prow = 0, pseg = 0;   // row group of the wave and unit within it
   auto process = [&](const Unit& d) {
     const int c0 = pseg * UL;
     const bool valid = full || c0 + ul < nch;
     const uint32_t w[4] = {d.w.x, d.w.y, d.w.z, d.w.w};
     const float s = __half2float(d.s);
-    const float zb = kB + __half2float(d.z);
+    const float z = __half2float(d.z);
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
       const uint32_t* xm = xl + ((size_t)m * npad + c0) * 16;
-      float part = 0.f;
+      float part = 0.f, part16 = 0.f;   // part16: fp16's odd pairs, at 16 times their weight
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint4 xp = *reinterpret_cast<const uint4*>(xm + e * 64);
         const uint32_t xv[4] = {xp.x, xp.y, xp.z, xp.w};
+        if constexpr (IO == 0) {
+          // pairs 1 and 3 keep their codes at bits 4-7 of each half: 1024 + 16 q
+          const uint32_t w8 = w[e] >> 8;
+          part = dot2_io<IO>((w[e] & kmask) | kmag, xv[0], part);
+          part16 = dot2_io<IO>((w[e] & kmask1) | kmag, xv[1], part16);
+          part = dot2_io<IO>((w8 & kmask) | kmag, xv[2], part);
+          part16 = dot2_io<IO>((w8 & kmask1) | kmag, xv[3], part16);
+        } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t hb = ((w[e] >> (4 * j)) & kmask) | kmag;
-          part = dot2_io<IO>(hb, xv[j], part);
+          for (int j = 0; j < 4; ++j) part = dot2_io<IO>(((w[e] >> (4 * j)) & kmask) | kmag, xv[j], part);
         }
       }
-      const float t = fmaf(s, fmaf(-zb, xcl[(size_t)m * npad + c0], part), acc[m]);
+      const float2 ds = xcl[(size_t)m * npad + c0];
+      const float tot = IO == 0 ? fmaf(part16, 0.0625f, part) : part;
+      const float t = fmaf(s, fmaf(-z, ds.y, tot - ds.x), acc[m]);
       acc[m] = valid ? t : acc[m];
     }
     if (++pseg == nseg) {   // the row (PAIRS: the pair) is complete
@@ -240,10 +263,15 @@ void awq_gemv_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__
       if (u0 + i < nunits) process(d[i]);
     }
   }
-  if (lane < r1 - r0) {
-    const float b = bias ? Io<IO>::to_f(bias[r0 + lane]) : 0.f;
+  {
+    // lane i holds the total of the wave's i-th row (PAIRS: lanes 2i, 2i + 1 the rows of its i-th pair)
+    const int gi = PAIRS ? (lane >> 1) : lane;
+    const long long row = ((long long)gi * W + wg) * RG + (PAIRS ? (lane & 1) : 0);
+    if (gi < ng && row < N) {
+      const float b = bias ? Io<IO>::to_f(bias[row]) : 0.f;
 #pragma unroll
-    for (int m = 0; m < MR; ++m) y[(size_t)m * N + r0 + lane] = Io<IO>::from_f(out[m] + b);
+      for (int m = 0; m < MR; ++m) y[(size_t)m * N + row] = Io<IO>::from_f(out[m] + b);
+    }
   }
 }
 
@@ -256,8 +284,8 @@ static hipError_t launch_k(int N, int K, const void* x, const uint8_t* q, const 
   const int grid = max(max(1, min(256, (N + 8 * 4 - 1) / (8 * 4))), (N + rows_cap - 1) / rows_cap);
   constexpr int UL = PAIRS ? 32 : 64;
   const size_t npad = (size_t)((K >> 5) + UL - 1) / UL * UL;   // chunks per row in LDS, whole units
-  const size_t lds = (size_t)MR * npad * 16 * sizeof(uint32_t) + (size_t)MR * npad * sizeof(float);
-  if (lds > 65536) {   // at most 91392 bytes (M 7, K 4160: 130 chunks padded to 192)
+  const size_t lds = (size_t)MR * npad * 16 * sizeof(uint32_t) + (size_t)MR * npad * 2 * sizeof(float);
+  if (lds > 65536) {   // at most 96768 bytes (M 7, K 4160: 130 chunks padded to 192)
     static std::atomic<uint64_t> raised{0};
     const hipError_t e =
         raise_lds_limit(raised, reinterpret_cast<const void*>(&awq_gemv_kernel<IO, MR, PAIRS>), 96 * 1024);

@@ -413,13 +413,37 @@ def test_awq_gemv(P, M, N):
 def test_awq_gemv_random_params_other_k(P, M, K, N):
     """Batched x (M up to 8), ragged N (including fewer rows than waves), K
     not a multiple of 64 chunks per unit (the last unit of a row reaches past
-    its end; x is staged padded to whole units, up to 91392 bytes of LDS at M 7,
+    its end; x is staged padded to whole units, up to 96768 bytes of LDS at M 7,
     K 4160), rows in pairs with an odd count, up to the LDS limit M K = 32768."""
     g = synth.GemvConfig(f"gemv_k{K}", 40, 1, K, N, 64)
     p = synth.random_awq_layer(g, seed=5, M=M)
     y_ref = oracle.gemv_ref(p["x"], p["codes"], p["scales"], p["zeros"])
     y = P.awq_gemv_w4a16(dev(p["x"]), dev(p["codes"]), dev(p["scales"]), dev(p["zeros"]))
     assert_close(host(y), y_ref)
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 3072, 2048), (3, 2048, 333)])
+@pytest.mark.parametrize("dtype", ["float16", "bfloat16"])
+def test_awq_gemv_small_activations(P, M, K, N, dtype):
+    """x scaled by 2^-12 (input preparation), so that |x| < 2^-10 almost
+    everywhere and many values are fp16 subnormals: the accuracy must not depend
+    on the scale of x."""
+    g = synth.GemvConfig(f"gemv_s{K}", 43, 1, K, N, 64)
+    p = synth.random_awq_layer(g, seed=8, M=M)
+    x = (p["x"].astype(np.float32) * np.float32(2.0 ** -12)).astype(np.float16)
+    if dtype == "bfloat16":
+        xt = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16)
+        x = xt.float().numpy()
+        xd = xt.to(DEV)
+    else:
+        xd = dev(x)
+    y_ref = oracle.gemv_ref(x, p["codes"], p["scales"], p["zeros"])
+    y = P.awq_gemv_w4a16(xd, dev(p["codes"]), dev(p["scales"]), dev(p["zeros"]))
+    if dtype == "bfloat16":
+        torch.cuda.synchronize()
+        assert_close(y.float().cpu().numpy(), oracle.bf16_round(y_ref.astype(np.float32)))
+    else:
+        assert_close(host(y), y_ref)
 
 
 @pytest.mark.parametrize("M", [1, 8])
