@@ -82,7 +82,11 @@ __device__ __forceinline__ float dot2_io(uint32_t a, uint32_t b, float c) {
 // 64-chunk units would leave every other load half empty. The wave's rows then
 // go in pairs, the even row of a pair in lanes 0-31 and the odd one in lanes
 // 32-63, in units of 32 chunks per half: every load is a whole 1 KB.
-template <int IO, int MR, bool PAIRS>
+// XR (M 1, K 3072: rows in pairs, three units per pair, as many as the ring
+// holds): ring slot i always carries unit i of a pair, so each lane keeps the x
+// pairs and (D, S) of its three chunks in registers instead of reading them
+// from LDS per unit.
+template <int IO, int MR, bool PAIRS, bool XR>
 __global__ __launch_bounds__(64 * kGemvWaves)
 void awq_gemv_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ codes,
                      const __half* __restrict__ scales, const __half* __restrict__ zeros,
@@ -204,7 +208,19 @@ void awq_gemv_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__
   const uint32_t* xl = xs + ((size_t)(ul & ~15) * 4 + (ul & 15)) * 4;
   const float2* xcl = reinterpret_cast<const float2*>(xc) + ul;
   int prow = 0, pseg = 0;   // row group of the wave and unit within it
-  auto process = [&](const Unit& d) {
+  static_assert(!XR || (MR == 1 && PAIRS && kGemvRing == 3), "XR: one row of x, pairs, three ring slots");
+  uint4 xr[XR ? 3 : 1][4];
+  float2 dsr[XR ? 3 : 1];
+  if constexpr (XR) {
+#pragma unroll
+    for (int u = 0; u < 3; ++u) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) xr[u][e] = *reinterpret_cast<const uint4*>(xl + (size_t)u * UL * 16 + e * 64);
+      dsr[u] = xcl[u * UL];
+    }
+  }
+  // slot: the ring slot of the unit (XR: its unit within the pair)
+  auto process = [&](const Unit& d, int slot) {
     const int c0 = pseg * UL;
     const bool valid = full || c0 + ul < nch;
     const uint32_t w[4] = {d.w.x, d.w.y, d.w.z, d.w.w};
@@ -216,7 +232,7 @@ void awq_gemv_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__
       float part = 0.f, part16 = 0.f;   // part16: fp16's odd pairs, at 16 times their weight
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint4 xp = *reinterpret_cast<const uint4*>(xm + e * 64);
+        const uint4 xp = XR ? xr[slot][e] : *reinterpret_cast<const uint4*>(xm + e * 64);
         const uint32_t xv[4] = {xp.x, xp.y, xp.z, xp.w};
         if constexpr (IO == 0) {
           // pairs 1 and 3 keep their codes at bits 4-7 of each half: 1024 + 16 q
@@ -230,7 +246,7 @@ void awq_gemv_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__
           for (int j = 0; j < 4; ++j) part = dot2_io<IO>(((w[e] >> (4 * j)) & kmask) | kmag, xv[j], part);
         }
       }
-      const float2 ds = xcl[(size_t)m * npad + c0];
+      const float2 ds = XR ? dsr[slot] : xcl[(size_t)m * npad + c0];
       const float tot = IO == 0 ? fmaf(part16, 0.0625f, part) : part;
       const float t = fmaf(s, fmaf(-z, ds.y, tot - ds.x), acc[m]);
       acc[m] = valid ? t : acc[m];
@@ -260,7 +276,7 @@ void awq_gemv_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__
 #pragma unroll
     for (int i = 0; i < kGemvRing; ++i) {
       load_next(d[(i + kGemvRing - 1) % kGemvRing]);
-      if (u0 + i < nunits) process(d[i]);
+      if (u0 + i < nunits) process(d[i], i);
     }
   }
   {
@@ -275,7 +291,7 @@ void awq_gemv_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__
   }
 }
 
-template <int IO, int MR, bool PAIRS>
+template <int IO, int MR, bool PAIRS, bool XR = false>
 static hipError_t launch_k(int N, int K, const void* x, const uint8_t* q, const void* s,
                            const void* z, const void* b, void* y, hipStream_t st) {
   // about one workgroup per CU for large N, at least ~4 rows per wave for small
@@ -288,10 +304,10 @@ static hipError_t launch_k(int N, int K, const void* x, const uint8_t* q, const 
   if (lds > 65536) {   // at most 96768 bytes (M 7, K 4160: 130 chunks padded to 192)
     static std::atomic<uint64_t> raised{0};
     const hipError_t e =
-        raise_lds_limit(raised, reinterpret_cast<const void*>(&awq_gemv_kernel<IO, MR, PAIRS>), 96 * 1024);
+        raise_lds_limit(raised, reinterpret_cast<const void*>(&awq_gemv_kernel<IO, MR, PAIRS, XR>), 96 * 1024);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((awq_gemv_kernel<IO, MR, PAIRS>), dim3(grid), dim3(64 * kGemvWaves), lds, st,
+  hipLaunchKernelGGL((awq_gemv_kernel<IO, MR, PAIRS, XR>), dim3(grid), dim3(64 * kGemvWaves), lds, st,
                      (const uint16_t*)x, q, (const __half*)s, (const __half*)z, (const uint16_t*)b, (uint16_t*)y,
                      N, K);
   return hipGetLastError();
@@ -300,7 +316,10 @@ static hipError_t launch_k(int N, int K, const void* x, const uint8_t* q, const 
 template <int IO, int MR>
 static hipError_t launch_mr(int N, int K, const void* x, const uint8_t* q, const void* s,
                             const void* z, const void* b, void* y, hipStream_t st) {
-  // rows of an odd number of 32-chunk halves go in pairs (whole 1 KB loads)
+  // rows of an odd number of 32-chunk halves go in pairs (whole 1 KB loads);
+  // one row of x at K 3072 keeps x in registers
+  if constexpr (MR == 1)
+    if (K == 3072) return launch_k<IO, 1, true, true>(N, K, x, q, s, z, b, y, st);
   if (((K >> 5) & 63) == 32) return launch_k<IO, MR, true>(N, K, x, q, s, z, b, y, st);
   return launch_k<IO, MR, false>(N, K, x, q, s, z, b, y, st);
 }
