@@ -162,9 +162,11 @@ def gemm_name(cfg):
 
 class ClockSampler:
     """The graphics clock that amdsmi reports (amdsmi_get_clock_info), sampled
-    on a host thread every `period` seconds between start() and stop(). The
-    driver refreshes this reading slowly, so it is kept as a secondary record
-    next to the clock measured on the GPU (svdq_clock_probe)."""
+    on a host thread every `period` seconds between start() and stop(). On the
+    MI355X boxes measured this reading does not follow the shader clock (it
+    read 157 to 1719 MHz while svdq_clock_probe measured 2.38 to 2.43 GHz on
+    the CUs over the same steps), so it is recorded only as the driver's own
+    report; the clock of the run is the one measured on the GPU."""
 
     def __init__(self, pci_bus=None, period=0.005):
         self.period, self.samples, self.err, self.h, self.max_gfx = period, [], None, None, None
@@ -210,7 +212,7 @@ class ClockSampler:
             return {"amdsmi_error": self.err or "no samples"}
         import numpy as np
         g = np.array(self.samples, float)
-        return {"amdsmi_gfx_mhz_median": float(np.median(g)), "amdsmi_samples": len(g),
+        return {"amdsmi_reported_gfx_mhz_median": float(np.median(g)), "amdsmi_samples": len(g),
                 "gfx_mhz_limit": self.max_gfx}
 
 
