@@ -409,17 +409,34 @@ def test_awq_gemv(P, M, N):
 @pytest.mark.parametrize("M,K,N", [(4, 4096, 512), (1, 12288, 3072), (2, 16384, 300),
                                    (1, 16448, 77), (8, 4096, 130), (1, 64, 5),
                                    (7, 4160, 1000), (3, 10880, 200), (2, 1088, 4099),
-                                   (1, 3072, 2049), (6, 5440, 64)])
+                                   (1, 3072, 2049), (6, 5440, 64), (1, 3072, 1), (1, 3072, 3),
+                                   (2, 3072, 1)])
 def test_awq_gemv_random_params_other_k(P, M, K, N):
     """Batched x (M up to 8), ragged N (including fewer rows than waves), K
     not a multiple of 64 chunks per unit (the last unit of a row reaches past
     its end; x is staged padded to whole units, up to 96768 bytes of LDS at M 7,
-    K 4160), rows in pairs with an odd count, up to the LDS limit M K = 32768."""
+    K 4160), rows in pairs with an odd count, up to the LDS limit M K = 32768;
+    at M 1 K 3072 (x in registers) one row and a lone odd row."""
     g = synth.GemvConfig(f"gemv_k{K}", 40, 1, K, N, 64)
     p = synth.random_awq_layer(g, seed=5, M=M)
     y_ref = oracle.gemv_ref(p["x"], p["codes"], p["scales"], p["zeros"])
     y = P.awq_gemv_w4a16(dev(p["x"]), dev(p["codes"]), dev(p["scales"]), dev(p["zeros"]))
     assert_close(host(y), y_ref)
+
+
+@pytest.mark.parametrize("M,K", [(1, 3072), (2, 3072), (1, 4096)])
+def test_awq_gemv_grid_beyond_one_workgroup_per_cu(P, M, K):
+    """N 140 001: more rows than 256 workgroups of 8 waves hold at 64 rows a
+    wave, so the grid grows (274 workgroups); checked on every 61st row and the
+    last 130 rows (each wave's rows are spread over the matrix, row w, w + W,
+    ...), including the lone last row of an odd count."""
+    N = 140001
+    g = synth.GemvConfig(f"gemv_bigN{K}", 45, 1, K, N, 64)
+    p = synth.random_awq_layer(g, seed=9, M=M)
+    y = host(P.awq_gemv_w4a16(dev(p["x"]), dev(p["codes"]), dev(p["scales"]), dev(p["zeros"])))
+    rows = np.unique(np.concatenate([np.arange(0, N, 61), np.arange(N - 130, N)]))
+    y_ref = oracle.gemv_ref(p["x"], p["codes"][rows], p["scales"][rows], p["zeros"][rows])
+    assert_close(y[:, rows], y_ref)
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 3072, 2048), (3, 2048, 333)])
