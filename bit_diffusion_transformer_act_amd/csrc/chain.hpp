@@ -54,15 +54,15 @@ __device__ __forceinline__ uint32_t chain_int4_codes8_exact(const float* v, floa
 }
 
 // tile: U [BM][TP] in LDS (h16 bits), columns n0 .. n0 + BN of the up-projection's
-// output; si: smooth_inv2[n0 .. n0 + BN) in LDS. Thread t takes the (row, group)
-// items t, t + 256, ...; the four (or two) threads of one row write its
-// BN / 2 code bytes as consecutive 32-byte pieces.
-template <int IO, int BM, int BN, int TP>
+// output; si: smooth_inv2[n0 .. n0 + BN) in LDS. Thread t of the NT takes the
+// (row, group) items t, t + NT, ...; the four (or two) threads of one row write
+// its BN / 2 code bytes as consecutive 32-byte pieces.
+template <int IO, int BM, int BN, int TP, int NT = 256>
 __device__ __forceinline__ void chain_quantize_tile(const uint16_t* tile, const float* si, int m0, int n0, int M,
                                                     int N, const ChainEpilogue& ce, int tid) {
 #pragma clang fp contract(off)
   constexpr int G = BN / 64;
-  for (int it = tid; it < BM * G; it += 256) {
+  for (int it = tid; it < BM * G; it += NT) {
     const int row = it / G, g = it - row * G;
     if (m0 + row >= M) break;   // items run row by row, so every later one is past M too
     const uint16_t* src = tile + row * TP + g * 64;
@@ -105,13 +105,15 @@ __device__ __forceinline__ void chain_quantize_tile(const uint16_t* tile, const 
 
 // P[m][j] = sum_n U[m][n] lora_down2[j][n0 + n] over the tile's BN columns, on
 // v_mfma_f32_16x16x16 (lane l: row or rank l % 16, k 4 (l / 16) .. +4; result:
-// rank l % 16, rows 4 (l / 16) + i). Wave w takes rows w BM/4 .. +BM/4; the
-// slice `part` ([M][r2] fp32, this tile's) is written in full for rows < M.
-template <int IO, int BM, int BN, int TP>
+// rank l % 16, rows 4 (l / 16) + i). Wave w of the NT / 64 takes rows w WR .. +WR
+// (WR = BM / (NT / 64)); the slice `part` ([M][r2] fp32, this tile's) is
+// written in full for rows < M.
+template <int IO, int BM, int BN, int TP, int NT = 256>
 __device__ __forceinline__ void chain_lowrank_partial(const uint16_t* tile, int m0, int n0, int M, int N,
                                                       const ChainEpilogue& ce, float* part, int wave,
                                                       int lane) {
-  constexpr int WR = BM / 4, HB = WR / 16;   // rows per wave, 16-row blocks per wave
+  constexpr int WR = BM / (NT / 64), HB = WR / 16;   // rows per wave, 16-row blocks per wave
+  static_assert(WR % 16 == 0, "whole 16-row blocks per wave");
   const int l16 = lane & 15, lq = lane >> 4;
   const uint16_t* ldn = reinterpret_cast<const uint16_t*>(ce.lora_down);
   for (int jb = 0; jb < ce.r; jb += 16) {

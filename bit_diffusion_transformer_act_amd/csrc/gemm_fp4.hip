@@ -9,14 +9,16 @@
 // as the lane's scale, and accumulates in fp32.
 //
 // With no VALU work the bound is the matrix core, so the tile is sized for
-// operand reuse: 256 x 256 per workgroup, 4 waves of 128 x 128 (4 x 4 blocks
-// of 32 x 32, 256 fp32 accumulators per lane held in AGPRs), one workgroup per
-// CU. Operands reach LDS by LDS-DMA in units that keep the memory pipeline's
-// request count low (each request costs about as much as the bytes it moves):
+// operand reuse: 256 x 256 per workgroup, one workgroup per CU, 8 waves of
+// 128 x 64 (4 x 2 blocks of 32 x 32, 128 fp32 accumulators per lane held in
+// AGPRs), two per SIMD, so that one wave's LDS reads, DMA issue and barrier
+// waits overlap the other's MFMAs. Operands reach LDS by LDS-DMA in units that
+// keep the memory pipeline's request count low (each request costs about as
+// much as the bytes it moves):
 //  - codes in stage pairs of 256 codes: whole 128-byte row lines, 8 rows per
 //    instruction, two 64 KB pair slots (the pair in use and the next one);
 //  - scales in groups of 4 steps: 16 bytes per row, two 8 KB group slots.
-// The 16 MFMAs of each half-step (64 codes) run while the next half-step's
+// The 8 MFMAs of each half-step (64 codes) run while the next half-step's
 // operands are read from LDS; the DMA of the pair after next is threaded
 // between the MFMAs of the last half-step of a pair, after the one barrier per
 // pair. The low-rank up-projection is added after the main loop, so its global
@@ -34,13 +36,27 @@ namespace svdq {
 
 namespace fp4big {
 constexpr int BM = 256, BN = 256;
-constexpr int RB = 4, CB = 4;                 // 32 x 32 blocks per wave
+constexpr int RB = 4;                         // 32-row blocks per wave
 constexpr int ROW = 128;                      // bytes of a code row per stage pair
-constexpr int PAIR = (BM + BN) * ROW;         // 64 KB pair slot: A rows, then B rows
+constexpr int PAIR = (BM + BN) * ROW;         // 64 KB: one pair of A rows and B rows
+// The ring holds A slot 0, A slot 1, B slot 0, B slot 1 (32 KB each), so that
+// the slot and the 32-row block of an operand read are immediate offsets
+// (under 64 KB) from one lane address per half-step.
+constexpr int SLOT = BM * ROW;                // 32 KB
+constexpr int BOFF = 2 * SLOT;                // B slots after both A slots
 constexpr int SROW = 16;                      // bytes of a scale row per group of 4 steps
 constexpr int SGRP = (BM + BN) * SROW;        // 8 KB group slot
 constexpr int LDS = 2 * PAIR + 2 * SGRP;      // 144 KB
-static_assert(PAIR / 4096 == 16 && SGRP / 4096 == 2, "DMA plan: 16 + 2 instructions per thread");
+// 8 waves in a 2 x 4 grid, each 128 rows x 64 columns (two per SIMD)
+constexpr int NW = 8, NT = 64 * NW;
+constexpr int CB = 2;                         // 32-column blocks per wave
+constexpr int WNC = 32 * CB;                  // columns per wave
+constexpr int CI = PAIR / (1024 * NW);        // code DMA instructions per wave and pair
+constexpr int SI = SGRP / (1024 * NW);        // scale DMA instructions per wave and group
+static_assert((NW / 2) * WNC == BN && 2 * 128 == BM, "the wave grid covers the tile");
+static_assert(CI == RB * CB, "one code DMA per MFMA of the last half-step");
+static_assert(SI == 1, "one scale DMA per wave and group");
+static_assert(BM == BN && SLOT == BN * ROW, "A and B slots of one size");
 }  // namespace fp4big
 
 // The eight 16-byte chunks of a 128-byte code row are XOR-swizzled with
@@ -49,7 +65,7 @@ static_assert(PAIR / 4096 == 16 && SGRP / 4096 == 2, "DMA plan: 16 + 2 instructi
 __device__ __forceinline__ int swz8(int row) { return (row >> 1) & 7; }
 
 template <int IO, int EPI>
-__global__ __launch_bounds__(256, 1)
+__global__ __launch_bounds__(fp4big::NT, 1)
 void gemm_fp4_big_kernel(const uint8_t* __restrict__ act_codes, const uint8_t* __restrict__ act_scales,
                          const float* __restrict__ lora_act, const uint8_t* __restrict__ w_codes,
                          const uint8_t* __restrict__ w_scales, const uint16_t* __restrict__ lora_up,
@@ -61,7 +77,7 @@ void gemm_fp4_big_kernel(const uint8_t* __restrict__ act_codes, const uint8_t* _
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / (NW / 2), wn = wave % (NW / 2);
   const int l32 = lane & 31, lh = lane >> 5;
 
   // XCD-aware grouped tile order (4 M-tiles per group: one 256 x 256 tile per
@@ -83,37 +99,49 @@ void gemm_fp4_big_kernel(const uint8_t* __restrict__ act_codes, const uint8_t* _
   const int KB = K >> 1;
   const int SK = K >> 5;          // scale bytes per row
 
-  // ---- DMA plan. Code instruction j (0..15) of wave w fills slot rows
-  // 32 j + 8 w .. +8 (j < 8: A, else B); lane L takes row + L/8 and chunk L%8.
-  // Scale instruction j (0: A, 1: B) of wave w fills rows 64 w + L of its half.
+  // ---- DMA plan. Code instruction j (0..CI-1) of wave w fills slot rows
+  // 8 NW j + 8 w .. +8 (the first CI/2: A, the rest: B); lane L takes row + L/8
+  // and chunk L%8. Scale instruction j of wave w fills slot rows 64 (NW j + w)
+  // + L (A rows below 256, then B).
   const uint8_t* tA = act_codes + (size_t)m0 * KB;
   const uint8_t* tB = w_codes + (size_t)n0 * KB;
   const uint8_t* tsA = act_scales + (size_t)m0 * SK;
   const uint8_t* tsB = w_scales + (size_t)n0 * SK;
   const int alast = M - 1 - m0;                 // rows past M re-read the last row
   const int rl = 8 * wave + (lane >> 3);
-  const int coff = ((lane & 7) ^ swz8(rl)) * 16;  // swz8(32 j + rl) == swz8(rl)
-  uint32_t aoff[8], boff[8];
+  const int coff = ((lane & 7) ^ swz8(rl)) * 16;  // swz8(8 NW j + rl) == swz8(rl)
+  constexpr int CH = CI / 2;
+  uint32_t aoff[CH], boff[CH];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    aoff[j] = (uint32_t)min(32 * j + rl, alast) * (uint32_t)KB + (uint32_t)coff;
-    boff[j] = (uint32_t)(32 * j + rl) * (uint32_t)KB + (uint32_t)coff;
+  for (int j = 0; j < CH; ++j) {
+    aoff[j] = (uint32_t)min(8 * NW * j + rl, alast) * (uint32_t)KB + (uint32_t)coff;
+    boff[j] = (uint32_t)(8 * NW * j + rl) * (uint32_t)KB + (uint32_t)coff;
   }
-  const uint32_t saoff = (uint32_t)min(64 * wave + lane, alast) * (uint32_t)SK;
-  const uint32_t sboff = (uint32_t)(64 * wave + lane) * (uint32_t)SK;
+  uint32_t soff[SI];
+#pragma unroll
+  for (int j = 0; j < SI; ++j) {
+    const int sr = 64 * (NW * j + wave) + lane;   // slot row
+    soff[j] = (uint32_t)(sr < BM ? min(sr, alast) : sr - BM) * (uint32_t)SK;
+  }
+  const uint8_t* tsW = 64 * wave < BM ? tsA : tsB;   // the half this wave's scale rows lie in
   const uint32_t lds0 = lds_addr(smem);
 
   auto code_dma = [&](int pp, int j) {   // pair pp, instruction j (constant)
-    const uint32_t lds = lds0 + (uint32_t)((pp & 1) * PAIR + (32 * j + 8 * wave) * ROW);
-    if (j < 8) dma16_so(tA, aoff[j] + (uint32_t)(pp * ROW), lds);
-    else dma16_so(tB, boff[j - 8] + (uint32_t)(pp * ROW), lds);
+    const uint32_t lds = lds0 + (uint32_t)((j < CH ? 0 : BOFF) + (pp & 1) * SLOT +
+                                           (8 * NW * (j % CH) + 8 * wave) * ROW);
+    if (j < CH) dma16_so(tA, aoff[j] + (uint32_t)(pp * ROW), lds);
+    else dma16_so(tB, boff[j - CH] + (uint32_t)(pp * ROW), lds);
   };
   auto scale_dma = [&](int q, int j) {   // scale group q, instruction j (constant)
-    const uint32_t lds = lds0 + (uint32_t)(2 * PAIR + (q & 1) * SGRP + (256 * j + 64 * wave) * SROW);
-    if (j == 0) dma16_so(tsA, saoff + (uint32_t)(q * SROW), lds);
-    else dma16_so(tsB, sboff + (uint32_t)(q * SROW), lds);
+    const uint32_t lds = lds0 + (uint32_t)(2 * PAIR + (q & 1) * SGRP + 64 * (NW * j + wave) * SROW);
+    dma16_so(tsW, soff[j] + (uint32_t)(q * SROW), lds);
   };
 
+  // With two waves per SIMD a lane may use at most 256 registers, and the
+  // compiler then selects MFMAs with VGPR results unless the function is seen
+  // to use AGPRs; an empty asm statement with an AGPR operand keeps the 128
+  // accumulators in AGPRs (VGPR results spill).
+  asm volatile("" ::"a"(0));
   v16f acc[RB][CB];
 #pragma unroll
   for (int i = 0; i < RB; ++i)
@@ -126,19 +154,26 @@ void gemm_fp4_big_kernel(const uint8_t* __restrict__ act_codes, const uint8_t* _
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) arow[rb] = wm * 128 + rb * 32 + l32;
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb) brow[cb] = wn * 128 + cb * 32 + l32;
+  for (int cb = 0; cb < CB; ++cb) brow[cb] = wn * WNC + cb * 32 + l32;
   const int s8 = swz8(l32);   // == swz8(arow[rb]) == swz8(brow[cb])
 
   // operands of half-step hs (0..3) of pair pp: step 2 pp + hs / 2, K half hs % 2
   struct Ops { uint4 a[RB], b[CB]; };
-  auto load_ops = [&](Ops& o, int pp, int hs) {
-    const uint8_t* st = smem + (pp & 1) * PAIR;
+  // lane addresses of half-step hs: row block 0 of A and of B in slot 0
+  uint32_t la[4], lb[4];
+#pragma unroll
+  for (int hs = 0; hs < 4; ++hs) {
     const int ch = ((2 * hs + lh) ^ s8) << 4;
+    la[hs] = (uint32_t)(arow[0] * ROW + ch);
+    lb[hs] = (uint32_t)(BOFF + brow[0] * ROW + ch);
+  }
+  auto load_ops = [&](Ops& o, int pp, int hs) {
+    const uint8_t* pa = smem + la[hs] + (pp & 1) * SLOT;
+    const uint8_t* pb = smem + lb[hs] + (pp & 1) * SLOT;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) o.a[rb] = *reinterpret_cast<const uint4*>(st + arow[rb] * ROW + ch);
+    for (int rb = 0; rb < RB; ++rb) o.a[rb] = *reinterpret_cast<const uint4*>(pa + rb * 32 * ROW);
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
-      o.b[cb] = *reinterpret_cast<const uint4*>(st + (BM + brow[cb]) * ROW + ch);
+    for (int cb = 0; cb < CB; ++cb) o.b[cb] = *reinterpret_cast<const uint4*>(pb + cb * 32 * ROW);
   };
   struct Sc { uint32_t a[RB], b[CB]; };
   auto load_sc = [&](Sc& e, int ks) {   // the 4 E8M0 bytes of step ks for this lane's rows
@@ -163,9 +198,9 @@ void gemm_fp4_big_kernel(const uint8_t* __restrict__ act_codes, const uint8_t* _
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) mfma(o, e, g, rb, cb);
   };
-  // the same 16 MFMAs with the DMA of pair dp (and scale group dq) threaded
-  // between them, so that issuing loads never holds up the matrix core of a
-  // SIMD that has one wave
+  // the same 8 MFMAs with the DMA of pair dp (and scale group dq) threaded
+  // between them, one DMA instruction after each MFMA (issuing all DMA first,
+  // or raising the wave priority around the MFMAs, measured no faster)
   auto mma_dma = [&](const Ops& o, const Sc& e, int g, int dp, int dq, auto with_scales) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
@@ -175,7 +210,7 @@ void gemm_fp4_big_kernel(const uint8_t* __restrict__ act_codes, const uint8_t* _
         const int i = rb * CB + cb;
         code_dma(dp, i);
         if constexpr (decltype(with_scales)::value) {
-          if (i < 2) scale_dma(dq, i);
+          if (i < SI) scale_dma(dq, i);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -189,14 +224,23 @@ void gemm_fp4_big_kernel(const uint8_t* __restrict__ act_codes, const uint8_t* _
   // first step. MORE: a pair follows (published at the end of this one); DMA:
   // the pair after that (and, for SDMA, the next scale group) is loaded now.
   // All three are compile-time, so the body is straight-line code.
+  // Scheduling fences keep the reads of a half-step from being hoisted above
+  // the MFMAs before it (which needs more than the 256 registers of a lane).
+  auto fence = [&]() { __builtin_amdgcn_sched_barrier(0); };
   auto pair = [&](int pp, auto more, auto dma, auto sdma) {
     load_ops(P1, pp, 1);
+    fence();
     mma(P0, E0, 0);
+    fence();
     load_ops(P0, pp, 2);
     load_sc(E1, 2 * pp + 1);
+    fence();
     mma(P1, E0, 1);
+    fence();
     load_ops(P1, pp, 3);
+    fence();
     mma(P0, E1, 0);
+    fence();
     if constexpr (decltype(more)::value) {
       // every LDS read of this pair has completed, and so has the DMA of the next
       // pair and scale group; past the barrier no wave reads this pair's slot (nor
@@ -206,18 +250,20 @@ void gemm_fp4_big_kernel(const uint8_t* __restrict__ act_codes, const uint8_t* _
       load_ops(P0, pp + 1, 0);
       load_sc(E0, 2 * pp + 2);
     }
+    fence();
     if constexpr (decltype(dma)::value) mma_dma(P1, E1, 1, pp + 2, (pp >> 1) + 1, sdma);
     else mma(P1, E1, 1);
+    fence();
   };
 
   // prologue: pair 0, scale group 0, pair 1 (nk >= 4, so np >= 2)
 #pragma unroll
-  for (int j = 0; j < 16; ++j) code_dma(0, j);
-  scale_dma(0, 0);
-  scale_dma(0, 1);
+  for (int j = 0; j < CI; ++j) code_dma(0, j);
 #pragma unroll
-  for (int j = 0; j < 16; ++j) code_dma(1, j);
-  waitvm<16>();   // pair 0 and scale group 0 have landed
+  for (int j = 0; j < SI; ++j) scale_dma(0, j);
+#pragma unroll
+  for (int j = 0; j < CI; ++j) code_dma(1, j);
+  waitvm<CI>();   // pair 0 and scale group 0 have landed
   __syncthreads();
   load_ops(P0, 0, 0);
   load_sc(E0, 0);
@@ -308,16 +354,16 @@ void gemm_fp4_big_kernel(const uint8_t* __restrict__ act_codes, const uint8_t* _
   }
   __syncthreads();
   if constexpr (EPI != 3) {
-    for (int c = tid; c < BM * (BN / 8); c += 256) {
+    for (int c = tid; c < BM * (BN / 8); c += NT) {
       const int row = c / (BN / 8), c8 = c - row * (BN / 8);
       if (m0 + row < M)
         *reinterpret_cast<uint4*>(Y + (size_t)(m0 + row) * N + n0 + c8 * 8) =
             *reinterpret_cast<const uint4*>(tile + row * TP + c8 * 8);
     }
   } else {
-    chain_quantize_tile<IO, BM, BN, TP>(tile, si_lds, m0, n0, M, N, ce, tid);
+    chain_quantize_tile<IO, BM, BN, TP, NT>(tile, si_lds, m0, n0, M, N, ce, tid);
     if (ce.r > 0)
-      chain_lowrank_partial<IO, BM, BN, TP>(tile, m0, n0, M, N, ce, ce.partial + (size_t)(n0 / BN) * M * ce.r,
+      chain_lowrank_partial<IO, BM, BN, TP, NT>(tile, m0, n0, M, N, ce, ce.partial + (size_t)(n0 / BN) * M * ce.r,
                                             wave, lane);
   }
 }
@@ -348,7 +394,7 @@ hipError_t launch_gemm_fp4_big(int io, int M, int N, int K, int r, const uint8_t
   const hipError_t e = raise_lds_limit(raised[v], reinterpret_cast<const void*>(kern), LDS);
   if (e != hipSuccess) return e;
   const ChainEpilogue ce = chain ? *chain : ChainEpilogue{nullptr, nullptr, 0, nullptr, nullptr, nullptr};
-  hipLaunchKernelGGL(kern, dim3(ntiles), dim3(256), LDS, st, ac, (const uint8_t*)as, (const float*)la, wc,
+  hipLaunchKernelGGL(kern, dim3(ntiles), dim3(NT), LDS, st, ac, (const uint8_t*)as, (const float*)la, wc,
                      (const uint8_t*)ws, (const uint16_t*)lu, (const uint16_t*)bias, (uint16_t*)Y, M, N, K, r, ce);
   return hipGetLastError();
 }
