@@ -525,7 +525,8 @@ def main(argv=None):
     up_fmt = "FP4 E2M1 b32" if "mlp_up" in names else "INT4 g64"
     if args.workload.startswith("block"):
         wl = ("DiT block linear stream at M=4096, hidden 3072 (QKV 3072->9216, out-proj 3072->3072, "
-              f"MLP-up 3072->12288 GELU, MLP-down 12288->3072; W4A4 r32, INT4 g64 except MLP-up {up_fmt})"
+              "MLP-up 3072->12288 GELU, MLP-down 12288->3072; W4A4 r32, "
+              + ("all INT4 g64)" if up_fmt == "INT4 g64" else f"INT4 g64 except MLP-up {up_fmt})")
               + fused)
     elif args.workload in WORKLOADS:
         wl = (f"DiT MLP at M=4096 (up K3072 N12288 + GELU in {up_fmt}, down K12288 N3072 INT4 g64; r32)"

@@ -243,6 +243,29 @@ def test_gemm_tile_bands(P, fmt, M, N, epi):
     assert np.isfinite(y).all()
 
 
+@pytest.mark.parametrize("M,K,epi", [
+    (2000, 1024, "gelu_tanh"),   # 8 x 32 tiles of 256: the last row tile holds 208 rows
+    (1793, 512, "none"),         # 8 x 32 tiles again: the last row tile holds one row
+])
+def test_gemm_fp4_big_ragged(P, M, K, epi):
+    """The 256 x 256 FP4 kernel (8 waves of 128 x 64) with a ragged last row
+    tile, against the oracle on one row of every 64-row band, all columns."""
+    N = 8192
+    cfg = synth.LayerConfig(f"fp4big_{M}_{K}", 54, M, K, N, 32, "fp4_b32", epi, "normal", 0.005, 30.0)
+    p = synth.random_quantized_layer(cfg, seed=5)
+    codes_u, packed, scales = oracle.quantize_act_ref(p["X"], p["smooth_inv"], "fp4_b32")
+    la = oracle.lora_act_ref(p["X"], p["lora_down"]).astype(np.float32)
+    Y = P.svdq_gemm_w4a4(dev(packed), dev(scales), dev(la), dev(p["w_codes"]), dev(p["w_scales"]),
+                         dev(p["lora_up"]), dev(p["bias"]), "fp4_b32", epi)
+    y = host(Y)
+    rows = band_rows(M, seed=13, extra=(1791, 1792) if M > 1792 else ())
+    wu = oracle.unpack_nibbles(p["w_codes"], signed=False)
+    y_ref = oracle.gemm_ref(codes_u, scales, la, wu, p["w_scales"], p["lora_up"], p["bias"], "fp4_b32", epi,
+                            rows=rows)
+    assert_close(y[rows], y_ref)
+    assert np.isfinite(y).all()
+
+
 @pytest.mark.parametrize("fmt", ["int4_g64", "fp4_b32"])
 @pytest.mark.parametrize("M,K,N", [(200, 384, 512), (200, 640, 512), (4096, 384, 4096)])
 def test_gemm_odd_k_steps(P, fmt, M, K, N):
