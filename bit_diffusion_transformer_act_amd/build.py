@@ -22,7 +22,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 
 # MFMA results stay in VGPRs where VALU post-processes every partial (the INT4
 # group scaling would otherwise pay one AGPR copy per element); the FP4 large
-# tile keeps its 256 accumulators per lane in AGPRs, so it is built without.
+# tile keeps its 128 accumulators per lane in AGPRs, so it is built without.
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 SOURCES = {"api.hip": [], "quantize_act.hip": VGPR_FORM, "gemm_w4a4.hip": VGPR_FORM,
            "gemm_fp4.hip": [], "gemm_nvfp4.hip": [], "awq_gemv.hip": VGPR_FORM}
